@@ -1,0 +1,223 @@
+"""Benchmark of the aggregation hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Prints ONE JSON line.  The default workload is the degree-aware reductions
+at F = 128: an R-MAT(0.57, 0.19, 0.19, 0.05) graph with 1,000,000 nodes and
+16,000,000 edges, X 1,000,000 x 128 float32 ~ N(0, 1); one step runs sum,
+mean, max (+ source index) and min (+ source index) over it.  Inputs are
+resident in HBM before timing; plans (degree bins) are built once, outside
+the timed region, as a training loop would reuse them.
+
+`value` = aggregated edges per second over the step (each op visits every
+edge once).  The roofline entry is for the step's dominant launch, with
+algorithmic bytes from the per-unit model (per edge: 4 B column index +
+one feature row; per row: 4 B row pointer + one output row (+ index row));
+its duration comes from HIP events on the launch stream.  `cpu_baseline`
+times the fp64 oracle on a bounded sample of the same workload on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "aggregation edges/s and achieved HBM GB/s (% of 8 TB/s) at F=128, 1 GPU"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "graph_neural_network_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, kernel: str):
+    """Counter-derived HBM bytes per launch, if a profile of the current
+    kernel sources exists (profiles/traffic_<workload>.json)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+class Op:
+    def __init__(self, name, fn, edges, bytes_alg):
+        self.name, self.fn, self.edges, self.bytes_alg = name, fn, edges, bytes_alg
+
+
+def wl_reduce_f128(args):
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.reduce_rmat()
+    n, m, F = w.n, w.nnz, w.params["F"]
+    X = torch.from_numpy(w.arrays["X"]).cuda()
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    t0 = time.perf_counter()
+    plan = gnn.gnn_plan_create(csr)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    Y = {op: torch.empty((n, F), dtype=torch.float32, device="cuda") for op in ("sum", "mean", "max", "min")}
+    A = {op: torch.empty((n, F), dtype=torch.int32, device="cuda") for op in ("max", "min")}
+    row_b = F * 4
+    ops = []
+    for op in ("sum", "mean", "max", "min"):
+        out_b = row_b + (F * 4 if op in A else 0)
+        b = m * (4 + row_b) + n * (4 + out_b)
+        ops.append(Op(op, (lambda op=op: gnn.gnn_reduce(csr, X, op, Y=Y[op], arg=A.get(op), plan=plan)),
+                      m, b))
+
+    def cpu_sample(budget_s):
+        import oracle
+        Xh = w.arrays["X"]
+        rng = np.random.default_rng(0)
+        k = 2000
+        t_per_edge = None
+        while True:
+            rows = np.sort(rng.choice(n, size=min(k, n), replace=False)).astype(np.int32)
+            e = int(np.diff(w.row_ptr)[rows].sum())
+            t0 = time.perf_counter()
+            for op in ("sum", "mean", "max", "min"):
+                oracle.reduce(w.row_ptr, w.col_idx, Xh, op, rows=rows, want_abs=False)
+            dt = time.perf_counter() - t0
+            if dt > budget_s / 4 or k >= n:
+                break
+            k = min(n, int(k * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+        return {"value": 4 * e / dt, "unit": "edges/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": f"{rows.size} random destination rows ({e} edges) of the same graph, "
+                          f"all four reductions, fp64, {dt:.1f} s"}
+
+    stats = gnn.gnn_plan_stats(plan)
+    cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
+           "F": F, "x_dtype": "f32", "ops": ["sum", "mean", "max+arg", "min+arg"],
+           "plan_build_ms": round(plan_ms, 2), "plan": stats}
+    return {"ops": ops, "dominant": "sum", "kernel": "k_aggregate<float, 32, 4, 0, false>",
+            "config": cfg, "dtype": "f32", "cpu": cpu_sample, "keep": (w, X, csr, plan, Y, A)}
+
+
+def wl_copy(args):
+    """Plain device copy of 4 GiB: the achievable-bandwidth and counter calibration."""
+    import torch
+
+    import graph_neural_network_amd as gnn
+
+    nbytes = 4 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ops = [Op("copy", lambda: gnn.gnn_copy_bytes(src, dst, nbytes), 0, 2 * nbytes)]
+
+    def cpu_sample(budget_s):
+        return None
+
+    return {"ops": ops, "dominant": "copy", "kernel": "k_copy16", "config":
+            {"workload": "copy_4GiB", "bytes": nbytes}, "dtype": "u8", "cpu": cpu_sample,
+            "keep": (src, dst)}
+
+
+WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="reduce_f128", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    torch.cuda.set_device(0)
+    w = WORKLOADS[args.workload](args)
+    ops = w["ops"]
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        for o in ops:
+            o.fn()
+    torch.cuda.synchronize()
+
+    ev = {o.name: [] for o in ops}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for o in ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            o.fn()
+            b.record(stream)
+            ev[o.name].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_op_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    step_ms = wall * 1e3 / args.steps
+    edges = sum(o.edges for o in ops)
+    bytes_alg = sum(o.bytes_alg for o in ops)
+    dom = next(o for o in ops if o.name == w["dominant"])
+    dom_ms = per_op_ms[dom.name]
+    achieved = dom.bytes_alg / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(args.workload, w["kernel"])
+
+    out = {
+        "metric": METRIC,
+        "value": (edges if edges else bytes_alg) / (step_ms * 1e-3),
+        "unit": "edges/s" if edges else "B/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic",
+        "config": w["config"],
+        "hbm_gbps_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9,
+        "hbm_frac_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "per_op_ms": {k: round(v, 4) for k, v in per_op_ms.items()},
+        "roofline": {"bound": "hbm", "kernel": f"{dom.name}: {w['kernel']}", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = w["cpu"](args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,288 @@
+"""Python binding of libgnn (MI355X / gfx950 GNN aggregation kernels).
+
+Thin ctypes layer: it only marshals torch tensors (device memory) and the
+current HIP stream into the C ABI declared in ``include/gnn.h``; every step
+of the computation runs in libgnn's HIP kernels.  The function names are the
+C names.  There is no CPU fallback: if ``libgnn.so`` is missing or cannot be
+loaded, every call raises.
+
+Graph convention: CSR with rows = destinations (row i lists the sources j of
+edges j -> i), int32 indices, on the GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgnn.so")
+
+GNN_OK = 0
+STATUS = {0: "GNN_OK", 1: "GNN_ERR_INVALID_VALUE", 2: "GNN_ERR_UNSUPPORTED",
+          3: "GNN_ERR_OUT_OF_MEMORY", 4: "GNN_ERR_DEVICE", 5: "GNN_ERR_SIZE_OVERFLOW",
+          6: "GNN_ERR_PLAN_MISMATCH"}
+DTYPE = {"f32": 0, "bf16": 1}
+NORM = {"none": 0, "left": 1, "right": 2, "both": 3}
+REDUCE_OP = {"sum": 0, "mean": 1, "max": 2, "min": 3}
+GT_MODE = {"csr": 0, "block16": 1}
+REORDER = {"degree": 0, "rcm": 1}
+
+# every symbol include/gnn.h declares
+EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
+           "gnn_spmm", "gnn_reduce", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
+           "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error")
+
+
+class GnnError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+class _Csr(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int32), ("n_cols", ctypes.c_int32), ("nnz", ctypes.c_int64),
+                ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("edge_val", ctypes.c_void_p)]
+
+
+class _PlanOpts(ctypes.Structure):
+    _fields_ = [("heavy_quantile", ctypes.c_float), ("light_max_deg", ctypes.c_int32),
+                ("chunk_edges", ctypes.c_int32), ("build_wsb", ctypes.c_int32),
+                ("wsb_min_nnz", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libgnn.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libgnn.so not found at {path}; build it with "
+                          "`python -m graph_neural_network_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, ci = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_int)
+    P = ctypes.POINTER
+    sig = {
+        "gnn_plan_create": [P(_Csr), P(_PlanOpts), vp, P(vp)],
+        "gnn_plan_destroy": [vp],
+        "gnn_plan_stats": [vp, P(ctypes.c_int64), i32],
+        "gnn_plan_wsb_export": [vp, vp, vp, vp, vp],
+        "gnn_spmm": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
+        "gnn_reduce": [P(_Csr), vp, ci, i32, i64, ci, vp, i64, vp, vp, vp],
+        "gnn_gatv2_fused": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp],
+        "gnn_gt_fused": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, ci, vp, vp, vp, vp],
+        "gnn_reorder": [P(_Csr), ci, vp, vp, vp, vp],
+        "gnn_permute_rows": [vp, i32, vp, ci, i32, i64, vp, i64, vp],
+        "gnn_copy_bytes": [vp, vp, i64, vp],
+        "gnn_status_string": [ci],
+        "gnn_last_error": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("gnn_status_string", "gnn_last_error") else ci
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str):
+    if rc != GNN_OK:
+        raise GnnError(rc, where, load_library().gnn_last_error().decode())
+
+
+def _stream(stream=None):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE["f32"]
+    if t.dtype == torch.bfloat16:
+        return DTYPE["bf16"]
+    raise TypeError(f"unsupported feature dtype {t.dtype} (float32 or bfloat16)")
+
+
+class Csr:
+    """A device CSR (rows = destinations).  Keeps the tensors alive."""
+
+    def __init__(self, row_ptr: torch.Tensor, col_idx: torch.Tensor, n_cols: int | None = None,
+                 edge_val: torch.Tensor | None = None):
+        for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+            if t.dtype != torch.int32 or not t.is_contiguous():
+                raise TypeError(f"{name} must be a contiguous int32 tensor")
+        self.row_ptr, self.col_idx, self.edge_val = row_ptr, col_idx, edge_val
+        self.n_rows = row_ptr.numel() - 1
+        self.n_cols = self.n_rows if n_cols is None else int(n_cols)
+        self.nnz = col_idx.numel()
+        self._s = _Csr(self.n_rows, self.n_cols, self.nnz, row_ptr.data_ptr(),
+                       col_idx.data_ptr() if self.nnz else None,
+                       edge_val.data_ptr() if edge_val is not None else None)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self._s)
+
+
+class Plan:
+    """Owns a gnn_plan*; destroyed with the object (or explicitly)."""
+
+    def __init__(self, handle: int, csr: Csr):
+        self.handle = ctypes.c_void_p(handle)
+        self.csr = csr
+
+    def destroy(self):
+        if self.handle:
+            _check(load_library().gnn_plan_destroy(self.handle), "gnn_plan_destroy")
+            self.handle = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            if self.handle and _lib is not None:
+                _lib.gnn_plan_destroy(self.handle)
+        except Exception:
+            pass
+
+
+def gnn_plan_create(csr: Csr, heavy_quantile: float = 0.0, light_max_deg: int = 0,
+                    chunk_edges: int = 0, build_wsb: bool = False, wsb_min_nnz: int = 0,
+                    stream=None) -> Plan:
+    o = _PlanOpts(heavy_quantile, light_max_deg, chunk_edges, int(build_wsb), wsb_min_nnz)
+    h = ctypes.c_void_p()
+    _check(load_library().gnn_plan_create(csr.ref, ctypes.byref(o), _stream(stream),
+                                          ctypes.byref(h)), "gnn_plan_create")
+    return Plan(h.value, csr)
+
+
+def gnn_plan_destroy(plan: Plan):
+    plan.destroy()
+
+
+def gnn_plan_stats(plan: Plan) -> dict:
+    c = (ctypes.c_int64 * 9)()
+    _check(load_library().gnn_plan_stats(plan.handle, c, 9), "gnn_plan_stats")
+    keys = ("light_rows", "medium_rows", "heavy_rows", "items", "heavy_threshold",
+            "wsb_windows", "wsb_blocks", "wsb_dense_tiles", "wsb_residual_edges")
+    return dict(zip(keys, list(c)))
+
+
+def gnn_plan_wsb_export(plan: Plan, stream=None):
+    st = gnn_plan_stats(plan)
+    dev = plan.csr.row_ptr.device
+    wp = torch.empty(st["wsb_windows"] + 1, dtype=torch.int32, device=dev)
+    bc = torch.empty((max(st["wsb_blocks"], 1), 8), dtype=torch.int32, device=dev)
+    bb = torch.empty((max(st["wsb_blocks"], 1), 2), dtype=torch.int64, device=dev)
+    _check(load_library().gnn_plan_wsb_export(plan.handle, _ptr(wp), _ptr(bc), _ptr(bb),
+                                              _stream(stream)), "gnn_plan_wsb_export")
+    return wp, bc[:st["wsb_blocks"]], bb[:st["wsb_blocks"]]
+
+
+def _plan_h(plan):
+    return plan.handle if plan is not None else None
+
+
+def gnn_spmm(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | None = None,
+             plan: Plan | None = None, stream=None) -> torch.Tensor:
+    F = X.shape[1]
+    if Y is None:
+        Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    _check(load_library().gnn_spmm(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y),
+                                   Y.stride(0), NORM[norm], _plan_h(plan), _stream(stream)),
+           "gnn_spmm")
+    return Y
+
+
+def gnn_reduce(csr: Csr, X: torch.Tensor, op: str = "sum", Y: torch.Tensor | None = None,
+               arg: torch.Tensor | bool | None = None, plan: Plan | None = None, stream=None):
+    """Returns (Y, arg); arg=True allocates the source-index output (max / min)."""
+    F = X.shape[1]
+    if Y is None:
+        Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    if arg is True:
+        arg = torch.empty((csr.n_rows, F), dtype=torch.int32, device=X.device)
+    elif arg is False:
+        arg = None
+    _check(load_library().gnn_reduce(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0),
+                                     REDUCE_OP[op], _ptr(Y), Y.stride(0), _ptr(arg),
+                                     _plan_h(plan), _stream(stream)), "gnn_reduce")
+    return Y, arg
+
+
+def gnn_gatv2_fused(csr: Csr, xl: torch.Tensor, xr: torch.Tensor, att: torch.Tensor,
+                    neg_slope: float = 0.2, out: torch.Tensor | None = None,
+                    lse: torch.Tensor | bool | None = True, plan: Plan | None = None, stream=None):
+    """xl [n_rows, H, D], xr [n_cols, H, D] (bf16 or f32), att [H, D] f32 -> (out, lse)."""
+    H, D = xl.shape[1], xl.shape[2]
+    if out is None:
+        out = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=xl.device)
+    if lse is True:
+        lse = torch.empty((csr.n_rows, H), dtype=torch.float32, device=xl.device)
+    elif lse is False:
+        lse = None
+    _check(load_library().gnn_gatv2_fused(csr.ref, _ptr(xl), _ptr(xr), _dtype_code(xl), _ptr(att),
+                                          H, D, float(neg_slope), _ptr(out), _ptr(lse),
+                                          _plan_h(plan), _stream(stream)), "gnn_gatv2_fused")
+    return out, lse
+
+
+def gnn_gt_fused(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float = 0.0,
+                 mode: str = "csr", out: torch.Tensor | None = None,
+                 lse: torch.Tensor | bool | None = True, plan: Plan | None = None, stream=None):
+    """q [n_rows, H, D], k, v [n_cols, H, D] -> (out [n_rows, H, D] f32, lse [n_rows, H])."""
+    H, D = q.shape[1], q.shape[2]
+    if out is None:
+        out = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
+    if lse is True:
+        lse = torch.empty((csr.n_rows, H), dtype=torch.float32, device=q.device)
+    elif lse is False:
+        lse = None
+    _check(load_library().gnn_gt_fused(csr.ref, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), H, D,
+                                       float(scale), GT_MODE[mode], _ptr(out), _ptr(lse),
+                                       _plan_h(plan), _stream(stream)), "gnn_gt_fused")
+    return out, lse
+
+
+def gnn_reorder(csr: Csr, kind: str = "degree", apply: bool = True, stream=None):
+    """Returns perm (perm[new] = old) and, if apply, the relabelled (row_ptr, col_idx)."""
+    dev = csr.row_ptr.device
+    perm = torch.empty(csr.n_rows, dtype=torch.int32, device=dev)
+    rp = ci = None
+    if apply:
+        rp = torch.empty(csr.n_rows + 1, dtype=torch.int32, device=dev)
+        ci = torch.empty(max(csr.nnz, 1), dtype=torch.int32, device=dev)
+    _check(load_library().gnn_reorder(csr.ref, REORDER[kind], _ptr(perm), _ptr(rp), _ptr(ci),
+                                      _stream(stream)), "gnn_reorder")
+    if apply:
+        return perm, rp, ci[:csr.nnz]
+    return perm
+
+
+def gnn_permute_rows(perm: torch.Tensor, X: torch.Tensor, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    n, F = perm.numel(), X.shape[1]
+    if out is None:
+        out = torch.empty((n, F), dtype=X.dtype, device=X.device)
+    _check(load_library().gnn_permute_rows(_ptr(perm), n, _ptr(X), _dtype_code(X), F, X.stride(0),
+                                           _ptr(out), out.stride(0), _stream(stream)),
+           "gnn_permute_rows")
+    return out
+
+
+def gnn_copy_bytes(src: torch.Tensor, dst: torch.Tensor, nbytes: int | None = None, stream=None):
+    n = src.numel() * src.element_size() if nbytes is None else int(nbytes)
+    _check(load_library().gnn_copy_bytes(_ptr(src), _ptr(dst), n, _stream(stream)),
+           "gnn_copy_bytes")
+    return dst

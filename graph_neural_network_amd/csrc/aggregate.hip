@@ -1,0 +1,466 @@
+// Neighbourhood aggregation kernels: SpMM (Y = A_norm X) and the segmented
+// reductions sum / mean / max / min.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations": section 2.2 (i) and (ii) define the operators; appendix
+// D.1 gives the degree-aware design (light rows feature-parallel, heavy rows
+// split into edge chunks, partial max / min merged by one 64-bit atomic on a
+// packed (order-preserving key, source index) word, then an unpack kernel);
+// appendix D.4 the normalisation modes.  The forward pass reads about
+// M * F * sizeof(dtype) bytes of neighbour features whatever the mapping.
+//
+// MI355X mapping.  A wave64 gathers neighbour rows with one 16-byte load per
+// lane: a row of F elements spans LPR = F * sizeof(T) / 16 lanes (a "slot"),
+// and a wave holds 64 / LPR slots.  F = 128 float32 or F = 256 bf16 is a
+// 512-byte row: two slots per wave, each slot one dwordx4 wave-half load per
+// edge, 8 edges kept in flight per slot.
+//   light rows  (deg <= light_max): one slot per row, rows in natural order;
+//               the slot loads up to LPR column indices with one coalesced
+//               access and broadcasts them lane to lane (ds_bpermute).
+//   items       (medium rows, and chunks of heavy rows): one workgroup of
+//               four waves per item; each slot takes a contiguous part of the
+//               item's edges, the slots are merged in LDS in slot order.
+//               Single-item rows write Y directly; multi-item rows write
+//               float partials (sum, combined later in item order, so the
+//               sum is deterministic) or packed 64-bit words merged with
+//               atomicMax / atomicMin (max, min) and unpacked afterwards.
+// Both kinds of work run in one launch (items first, then light rows).
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+constexpr int WG = 256;  // 4 waves
+constexpr int U = 8;     // edges in flight per slot
+
+enum Kind { K_SUM = 0, K_MAX = 1, K_MIN = 2 };
+
+struct AggParams {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const float* edge_val;   // nullable
+  const int32_t* deg_out;  // for RIGHT / BOTH
+  const void* X;
+  int64_t ldx;
+  float* Y;
+  int64_t ldy;
+  int32_t* arg;            // nullable, ld = F
+  const int4* items;
+  float* partial;          // [n_items, F]
+  unsigned long long* packed;  // [n_multi, F]
+  int32_t n_rows;
+  int32_t F;
+  int32_t light_max;
+  int32_t n_item_blocks;   // item workgroups in grid.x
+  int32_t n_light_blocks;
+  int32_t norm;            // gnn_norm (SpMM); MEAN is expressed as LEFT
+  int32_t weighted;        // edge_val present or RIGHT / BOTH
+};
+
+// ---------------------------------------------------------------------------
+// vector loads / stores of VE elements per lane
+// ---------------------------------------------------------------------------
+
+template <typename T, int VE>
+__device__ __forceinline__ void loadv(const T* p, float (&o)[VE]);
+
+template <>
+__device__ __forceinline__ void loadv<float, 4>(const float* p, float (&o)[4]) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void loadv<uint16_t, 8>(const uint16_t* p, float (&o)[8]) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x);
+  o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
+  o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z);
+  o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void loadv<float, 1>(const float* p, float (&o)[1]) { o[0] = *p; }
+template <>
+__device__ __forceinline__ void loadv<uint16_t, 1>(const uint16_t* p, float (&o)[1]) {
+  o[0] = __uint_as_float((uint32_t)(*p) << 16);
+}
+
+template <int VE>
+__device__ __forceinline__ void storev(float* p, const float (&v)[VE]) {
+  if constexpr (VE == 1) {
+    *p = v[0];
+  } else {
+#pragma unroll
+    for (int k = 0; k < VE; k += 4)
+      *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  }
+}
+template <int VE>
+__device__ __forceinline__ void storei(int32_t* p, const int (&v)[VE]) {
+  if constexpr (VE == 1) {
+    *p = v[0];
+  } else {
+#pragma unroll
+    for (int k = 0; k < VE; k += 4)
+      *reinterpret_cast<int4*>(p + k) = make_int4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-lane reduction state
+// ---------------------------------------------------------------------------
+
+template <int KIND, int VE, bool ARG>
+struct State {
+  // SUM: acc; MAX / MIN: order keys (+ source index)
+  float acc[VE];
+  uint32_t key[VE];
+  int idx[VE];
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int v = 0; v < VE; ++v) {
+      acc[v] = 0.0f;
+      key[v] = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
+      idx[v] = 0x7FFFFFFF;
+    }
+  }
+  __device__ __forceinline__ void add(const float (&x)[VE], float w, int j) {
+#pragma unroll
+    for (int v = 0; v < VE; ++v) {
+      if constexpr (KIND == K_SUM) {
+        acc[v] = fmaf(w, x[v], acc[v]);
+      } else {
+        uint32_t k = dev::order_key(x[v]);
+        bool better = (KIND == K_MAX) ? (k > key[v]) : (k < key[v]);
+        if constexpr (ARG) better = better || (k == key[v] && j < idx[v]);
+        if (better) {
+          key[v] = k;
+          if constexpr (ARG) idx[v] = j;
+        }
+      }
+    }
+  }
+  // merge another state (used for LDS merges in slot order)
+  __device__ __forceinline__ static void merge1(float& a, uint32_t& k, int& i, float a2, uint32_t k2,
+                                                int i2) {
+    if constexpr (KIND == K_SUM) {
+      a += a2;
+    } else {
+      bool better = (KIND == K_MAX) ? (k2 > k) : (k2 < k);
+      if constexpr (ARG) better = better || (k2 == k && i2 < i);
+      if (better) {
+        k = k2;
+        i = i2;
+      }
+    }
+  }
+};
+
+// Edge weight of SpMM entry e (source j): edge value, times 1/deg_out(j)
+// (RIGHT) or deg_out(j)^-1/2 (BOTH).  The destination's factor is applied
+// once per row at the end.
+__device__ __forceinline__ float edge_weight(const AggParams& p, int e, int j) {
+  float w = p.edge_val ? p.edge_val[e] : 1.0f;
+  if (p.norm == GNN_NORM_RIGHT) w = w / (float)p.deg_out[j];
+  else if (p.norm == GNN_NORM_BOTH) w = w * rsqrtf((float)p.deg_out[j]);
+  return w;
+}
+
+__device__ __forceinline__ float row_factor(const AggParams& p, float acc, int deg) {
+  if (p.norm == GNN_NORM_LEFT) return deg > 0 ? acc / (float)deg : 0.0f;
+  if (p.norm == GNN_NORM_BOTH) return deg > 0 ? acc * rsqrtf((float)deg) : 0.0f;
+  return acc;
+}
+
+// Scan edges [eb, ee) for one slot (LPR lanes, lane sl), accumulating into st.
+// `f_ok` says whether this lane's feature group exists (lanes past F still
+// load column indices for the slot).  slot_base = first lane of the slot.
+template <typename T, int LPR, int VE, int KIND, bool ARG>
+__device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, int sl, int slot_base,
+                                           const T* Xf, bool f_ok, State<KIND, VE, ARG>& st) {
+  for (int e0 = eb; e0 < ee; e0 += LPR) {
+    const int nb = min(LPR, ee - e0);
+    const int my_e = e0 + sl;
+    int my_c = 0;
+    float my_w = 1.0f;
+    if (sl < nb) {
+      my_c = p.col_idx[my_e];
+      if (KIND == K_SUM && p.weighted) my_w = edge_weight(p, my_e, my_c);
+    }
+    for (int u0 = 0; u0 < nb; u0 += U) {
+      int c[U];
+      float w[U];
+      float x[U][VE];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        c[u] = __shfl(my_c, slot_base + u0 + u, 64);
+        if (KIND == K_SUM) w[u] = p.weighted ? __shfl(my_w, slot_base + u0 + u, 64) : 1.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u0 + u < nb && f_ok) loadv<T, VE>(Xf + (int64_t)c[u] * p.ldx, x[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u0 + u < nb && f_ok) st.add(x[u], KIND == K_SUM ? w[u] : 1.0f, c[u]);
+    }
+  }
+}
+
+template <typename T, int LPR, int VE, int KIND, bool ARG>
+__device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg, int f0,
+                                           State<KIND, VE, ARG>& st) {
+  float out[VE];
+  int ai[VE];
+#pragma unroll
+  for (int v = 0; v < VE; ++v) {
+    if constexpr (KIND == K_SUM) {
+      out[v] = row_factor(p, st.acc[v], deg);
+    } else {
+      out[v] = deg > 0 ? dev::key_to_float(st.key[v]) : 0.0f;
+      ai[v] = deg > 0 ? st.idx[v] : -1;
+    }
+  }
+  storev<VE>(p.Y + (int64_t)row * p.ldy + f0, out);
+  if constexpr (ARG) storei<VE>(p.arg + (int64_t)row * p.F + f0, ai);
+}
+
+template <typename T, int LPR, int VE, int KIND, bool ARG>
+__global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
+  constexpr int SPW = 64 / LPR;          // slots per wave
+  constexpr int SPB = SPW * (WG / 64);   // slots per workgroup
+  constexpr int FT = LPR * VE;           // features per tile
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sw = lane / LPR, sl = lane % LPR;
+  const int slot = wave * SPW + sw;
+  const int slot_base = sw * LPR;
+  const int f0 = blockIdx.y * FT + sl * VE;
+  const bool f_ok = f0 < p.F;
+  const T* Xf = reinterpret_cast<const T*>(p.X) + f0;
+
+  // Item workgroups come first (hardware order spreads them over the XCDs);
+  // their count is padded to a multiple of 8 so that the light part starts on
+  // XCD 0 and can be remapped to contiguous row ranges per XCD.
+  const int n_item_pad = (p.n_item_blocks + 7) & ~7;
+  if ((int)blockIdx.x < n_item_pad) {
+    // ---------------- one workgroup per work item ----------------
+    const int lid = blockIdx.x;
+    if (lid >= p.n_item_blocks) return;
+    const int4 it = p.items[lid];
+    const int row = it.x, eb = it.y, ee = it.z, m = it.w;
+    const int len = ee - eb;
+    const int per = (len + SPB - 1) / SPB;
+    const int sb = min(ee, eb + slot * per);
+    const int se = min(ee, sb + per);
+    State<KIND, VE, ARG> st;
+    st.init();
+    scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
+
+    __shared__ float s_acc[(KIND == K_SUM) ? SPB * FT : 1];
+    __shared__ uint32_t s_key[(KIND != K_SUM) ? SPB * FT : 1];
+    __shared__ int s_idx[(KIND != K_SUM && ARG) ? SPB * FT : 1];
+#pragma unroll
+    for (int v = 0; v < VE; ++v) {
+      const int t = sl * VE + v;
+      if constexpr (KIND == K_SUM) s_acc[slot * FT + t] = st.acc[v];
+      else s_key[slot * FT + t] = st.key[v];
+      if constexpr (KIND != K_SUM && ARG) s_idx[slot * FT + t] = st.idx[v];
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < FT; t += WG) {
+      const int f = blockIdx.y * FT + t;
+      if (f >= p.F) continue;
+      float a = 0.0f;
+      uint32_t k = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
+      int ix = 0x7FFFFFFF;
+      for (int s2 = 0; s2 < SPB; ++s2) {
+        float a2 = 0.0f;
+        uint32_t k2 = 0;
+        int i2 = 0x7FFFFFFF;
+        if constexpr (KIND == K_SUM) a2 = s_acc[s2 * FT + t];
+        else k2 = s_key[s2 * FT + t];
+        if constexpr (KIND != K_SUM && ARG) i2 = s_idx[s2 * FT + t];
+        State<KIND, VE, ARG>::merge1(a, k, ix, a2, k2, i2);
+      }
+      if (m < 0) {
+        const int deg = len;  // single item covers the whole row
+        if constexpr (KIND == K_SUM) {
+          p.Y[(int64_t)row * p.ldy + f] = row_factor(p, a, deg);
+        } else {
+          p.Y[(int64_t)row * p.ldy + f] = dev::key_to_float(k);
+          if constexpr (ARG) p.arg[(int64_t)row * p.F + f] = ix;
+        }
+      } else {
+        if constexpr (KIND == K_SUM) {
+          p.partial[(int64_t)lid * p.F + f] = a;
+        } else {
+          unsigned long long w;
+          if constexpr (KIND == K_MAX)
+            w = ((unsigned long long)k << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)ix);
+          else
+            w = ((unsigned long long)k << 32) | (unsigned long long)(uint32_t)ix;
+          unsigned long long* dst = p.packed + (int64_t)m * p.F + f;
+          if constexpr (KIND == K_MAX) atomicMax(dst, w);
+          else atomicMin(dst, w);
+        }
+      }
+    }
+    return;
+  }
+
+  // ---------------- light rows: one slot per row ----------------
+  const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
+  const int64_t row = (int64_t)lb * SPB + slot;
+  if (row >= p.n_rows) return;
+  const int beg = p.row_ptr[row], end = p.row_ptr[row + 1];
+  const int deg = end - beg;
+  if (deg > p.light_max) return;  // handled as an item
+  State<KIND, VE, ARG> st;
+  st.init();
+  scan_edges<T, LPR, VE, KIND, ARG>(p, beg, end, sl, slot_base, Xf, f_ok, st);
+  if (f_ok) finish_row<T, LPR, VE, KIND, ARG>(p, (int)row, deg, f0, st);
+}
+
+// Sum of a heavy row's item partials, in item order (deterministic).
+__global__ __launch_bounds__(256) void k_combine_sum(AggParams p, const int4* multi) {
+  const int4 mr = multi[blockIdx.x];
+  const int row = mr.x, first = mr.y, cnt = mr.z;
+  const int deg = p.row_ptr[row + 1] - p.row_ptr[row];
+  for (int f = threadIdx.x; f < p.F; f += blockDim.x) {
+    float a = 0.0f;
+    for (int c = 0; c < cnt; ++c) a += p.partial[(int64_t)(first + c) * p.F + f];
+    p.Y[(int64_t)row * p.ldy + f] = row_factor(p, a, deg);
+  }
+}
+
+// Packed (key, index) words of heavy rows back to value and source index.
+template <int KIND, bool ARG>
+__global__ __launch_bounds__(256) void k_unpack(AggParams p, const int4* multi) {
+  const int row = multi[blockIdx.x].x;
+  for (int f = threadIdx.x; f < p.F; f += blockDim.x) {
+    unsigned long long w = p.packed[(int64_t)blockIdx.x * p.F + f];
+    uint32_t k = (uint32_t)(w >> 32), lo = (uint32_t)w;
+    p.Y[(int64_t)row * p.ldy + f] = dev::key_to_float(k);
+    if constexpr (ARG) p.arg[(int64_t)row * p.F + f] = (int)(KIND == K_MAX ? 0xFFFFFFFFu - lo : lo);
+  }
+}
+
+__global__ void k_fill_u64(unsigned long long* p, int64_t n, unsigned long long v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// dispatch
+// ---------------------------------------------------------------------------
+
+template <typename T, int LPR, int VE, int KIND, bool ARG>
+int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
+  constexpr int SPB = (64 / LPR) * (WG / 64);
+  constexpr int FT = LPR * VE;
+  const int ftiles = (p.F + FT - 1) / FT;
+  p.n_item_blocks = (int32_t)pl->n_items;
+  p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
+  const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
+  if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "aggregate grid too large");
+  if (KIND != K_SUM && pl->n_multi > 0) {
+    int64_t nw = pl->n_multi * p.F;
+    hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 16384)),
+                       dim3(256), 0, s, p.packed, nw, KIND == K_MAX ? 0ull : ~0ull);
+    GNN_LAUNCH_CHECK("fill packed");
+  }
+  if (gx > 0) {
+    hipLaunchKernelGGL((k_aggregate<T, LPR, VE, KIND, ARG>), dim3((unsigned)gx, (unsigned)ftiles),
+                       dim3(WG), 0, s, p);
+    GNN_LAUNCH_CHECK("aggregate");
+  }
+  if (pl->n_multi > 0) {
+    if constexpr (KIND == K_SUM) {
+      hipLaunchKernelGGL(k_combine_sum, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
+                         (const int4*)pl->multi);
+    } else {
+      hipLaunchKernelGGL((k_unpack<KIND, ARG>), dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
+                         (const int4*)pl->multi);
+    }
+    GNN_LAUNCH_CHECK("merge heavy rows");
+  }
+  return GNN_OK;
+}
+
+template <typename T, int VE, int KIND, bool ARG>
+int pick_lpr(gnn_plan* pl, AggParams& p, int lpr, hipStream_t s) {
+  if constexpr (VE == 1) {
+    return launch_one<T, 64, 1, KIND, ARG>(pl, p, s);
+  } else {
+    switch (lpr) {
+      case 8: return launch_one<T, 8, VE, KIND, ARG>(pl, p, s);
+      case 16: return launch_one<T, 16, VE, KIND, ARG>(pl, p, s);
+      case 32: return launch_one<T, 32, VE, KIND, ARG>(pl, p, s);
+      default: return launch_one<T, 64, VE, KIND, ARG>(pl, p, s);
+    }
+  }
+}
+
+template <typename T, int VE>
+int pick_kind(gnn_plan* pl, AggParams& p, int kind, bool arg, int lpr, hipStream_t s) {
+  if (kind == K_SUM) return pick_lpr<T, VE, K_SUM, false>(pl, p, lpr, s);
+  if (kind == K_MAX)
+    return arg ? pick_lpr<T, VE, K_MAX, true>(pl, p, lpr, s) : pick_lpr<T, VE, K_MAX, false>(pl, p, lpr, s);
+  return arg ? pick_lpr<T, VE, K_MIN, true>(pl, p, lpr, s) : pick_lpr<T, VE, K_MIN, false>(pl, p, lpr, s);
+}
+
+}  // namespace
+
+int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y,
+                     int64_t ldy, int mode, gnn_norm norm, const float* edge_val, int32_t* arg,
+                     hipStream_t s) {
+  AggParams p{};
+  p.row_ptr = pl->row_ptr;
+  p.col_idx = pl->col_idx;
+  p.edge_val = (mode == AGG_SPMM) ? edge_val : nullptr;
+  p.deg_out = pl->deg_out;
+  p.X = X;
+  p.ldx = ldx;
+  p.Y = Y;
+  p.ldy = ldy;
+  p.arg = arg;
+  p.items = pl->items;
+  p.n_rows = pl->n_rows;
+  p.F = F;
+  p.light_max = pl->light_max;
+  p.norm = (mode == AGG_SPMM) ? (int)norm : (mode == AGG_MEAN ? (int)GNN_NORM_LEFT : 0);
+  p.weighted = (p.edge_val != nullptr) || p.norm == GNN_NORM_RIGHT || p.norm == GNN_NORM_BOTH;
+  const int kind = (mode == AGG_MAX) ? K_MAX : (mode == AGG_MIN ? K_MIN : K_SUM);
+
+  // workspace: partials for sums of heavy rows, packed words for max / min
+  if (pl->n_multi > 0) {
+    void* ws = nullptr;
+    size_t need = (kind == K_SUM) ? (size_t)pl->n_items * F * 4 : (size_t)pl->n_multi * F * 8;
+    GNN_TRY(plan_workspace(pl, need, &ws));
+    p.partial = (float*)ws;
+    p.packed = (unsigned long long*)ws;
+  }
+
+  const int esz = (xt == GNN_BF16) ? 2 : 4;
+  const int64_t rowb = (int64_t)F * esz;
+  const bool vec_ok = (rowb % 16 == 0) && ((ldx * esz) % 16 == 0) && ((uintptr_t)X % 16 == 0) &&
+                      ((uintptr_t)Y % 16 == 0) && (ldy % 4 == 0) &&
+                      (arg == nullptr || ((uintptr_t)arg % 16 == 0 && F % 4 == 0));
+  int lpr = 64;
+  if (vec_ok) {
+    int lanes = (int)std::min<int64_t>(rowb / 16, 64);
+    lpr = 8;
+    while (lpr < lanes) lpr <<= 1;
+  }
+  if (xt == GNN_BF16) {
+    return vec_ok ? pick_kind<uint16_t, 8>(pl, p, kind, arg != nullptr, lpr, s)
+                  : pick_kind<uint16_t, 1>(pl, p, kind, arg != nullptr, lpr, s);
+  }
+  return vec_ok ? pick_kind<float, 4>(pl, p, kind, arg != nullptr, lpr, s)
+                : pick_kind<float, 1>(pl, p, kind, arg != nullptr, lpr, s);
+}
+
+}  // namespace gnn

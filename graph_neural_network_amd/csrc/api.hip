@@ -1,0 +1,280 @@
+// C ABI of libgnn: host-side validation, plans, dispatch to the launchers.
+// Declarations and the contract of every entry point are in include/gnn.h.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <new>
+#include <string>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+int fail(int status, const std::string& msg) {
+  g_last_error = msg;
+  return status;
+}
+
+namespace {
+
+int check_csr(const gnn_csr* c, bool need_square) {
+  if (!c) return fail(GNN_ERR_INVALID_VALUE, "csr is NULL");
+  if (c->n_rows < 0 || c->n_cols < 0 || c->nnz < 0)
+    return fail(GNN_ERR_INVALID_VALUE, "negative CSR size");
+  if (c->nnz >= 2147483648LL) return fail(GNN_ERR_SIZE_OVERFLOW, "nnz must be < 2^31");
+  if (!c->row_ptr) return fail(GNN_ERR_INVALID_VALUE, "row_ptr is NULL");
+  if (c->nnz > 0 && !c->col_idx) return fail(GNN_ERR_INVALID_VALUE, "col_idx is NULL");
+  if (c->nnz > 0 && c->n_cols == 0) return fail(GNN_ERR_INVALID_VALUE, "edges but n_cols == 0");
+  if (need_square && c->n_rows != c->n_cols)
+    return fail(GNN_ERR_INVALID_VALUE, "operation needs a square CSR (n_rows == n_cols)");
+  return GNN_OK;
+}
+
+int check_dtype(gnn_dtype t) {
+  if (t != GNN_F32 && t != GNN_BF16) return fail(GNN_ERR_INVALID_VALUE, "unknown dtype");
+  return GNN_OK;
+}
+
+// A plan given by the caller must be bound to this CSR; otherwise build a
+// transient one (synchronises the stream) that the caller of this helper frees.
+int get_plan(const gnn_csr* csr, gnn_plan* given, hipStream_t s, gnn_plan** use, bool* transient,
+             bool need_wsb = false) {
+  *transient = false;
+  if (given) {
+    GNN_TRY(check_plan(given, csr));
+    if (need_wsb && !given->has_wsb)
+      return fail(GNN_ERR_INVALID_VALUE, "plan was built without build_wsb");
+    *use = given;
+    return GNN_OK;
+  }
+  gnn_plan_opts o{};
+  o.build_wsb = need_wsb ? 1 : 0;
+  gnn_plan* p = nullptr;
+  GNN_TRY(gnn_plan_create(csr, &o, s, &p));
+  *use = p;
+  *transient = true;
+  return GNN_OK;
+}
+
+struct PlanGuard {
+  gnn_plan* p;
+  bool own;
+  ~PlanGuard() {
+    if (own && p) gnn_plan_destroy(p);
+  }
+};
+
+}  // namespace
+
+int check_plan(const gnn_plan* p, const gnn_csr* csr) {
+  if (p->n_rows != csr->n_rows || p->n_cols != csr->n_cols || p->nnz != csr->nnz ||
+      p->row_ptr != csr->row_ptr || p->col_idx != csr->col_idx)
+    return fail(GNN_ERR_PLAN_MISMATCH, "plan was built for another CSR");
+  return GNN_OK;
+}
+
+}  // namespace gnn
+
+using namespace gnn;
+
+extern "C" {
+
+const char* gnn_status_string(int status) {
+  switch (status) {
+    case GNN_OK: return "GNN_OK";
+    case GNN_ERR_INVALID_VALUE: return "GNN_ERR_INVALID_VALUE";
+    case GNN_ERR_UNSUPPORTED: return "GNN_ERR_UNSUPPORTED";
+    case GNN_ERR_OUT_OF_MEMORY: return "GNN_ERR_OUT_OF_MEMORY";
+    case GNN_ERR_DEVICE: return "GNN_ERR_DEVICE";
+    case GNN_ERR_SIZE_OVERFLOW: return "GNN_ERR_SIZE_OVERFLOW";
+    case GNN_ERR_PLAN_MISMATCH: return "GNN_ERR_PLAN_MISMATCH";
+    default: return "GNN_ERR_UNKNOWN";
+  }
+}
+
+const char* gnn_last_error(void) { return g_last_error.c_str(); }
+
+int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream, gnn_plan** out) {
+  if (!out) return fail(GNN_ERR_INVALID_VALUE, "out is NULL");
+  *out = nullptr;
+  GNN_TRY(check_csr(csr, false));
+  if (opts) {
+    if (opts->light_max_deg < 0 || opts->chunk_edges < 0 || opts->wsb_min_nnz < 0 ||
+        opts->heavy_quantile > 1.0f)
+      return fail(GNN_ERR_INVALID_VALUE, "invalid plan options");
+    if (opts->build_wsb && csr->n_rows != csr->n_cols)
+      return fail(GNN_ERR_INVALID_VALUE, "WSB tiles need a square CSR");
+  }
+  gnn_plan* p = new (std::nothrow) gnn_plan();
+  if (!p) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
+  int rc = plan_build(csr, opts, (hipStream_t)stream, p);
+  if (rc != GNN_OK) {
+    std::string keep = g_last_error;
+    gnn_plan_destroy(p);
+    g_last_error = keep;
+    return rc;
+  }
+  *out = p;
+  return GNN_OK;
+}
+
+int gnn_plan_destroy(gnn_plan* p) {
+  if (!p) return GNN_OK;
+  int rc = GNN_OK;
+  if (p->n_allocs > 0 || p->ws) {
+    if (hipStreamSynchronize(p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "plan stream sync failed");
+  }
+  for (int k = 0; k < p->n_allocs; ++k) hipFree(p->allocs[k]);
+  if (p->ws) hipFree(p->ws);
+  delete p;
+  return rc;
+}
+
+int gnn_plan_stats(const gnn_plan* p, int64_t* c, int32_t n) {
+  if (!p || !c || n < 9) return fail(GNN_ERR_INVALID_VALUE, "plan_stats: null or n < 9");
+  c[0] = p->n_light;
+  c[1] = p->n_medium;
+  c[2] = p->n_heavy;
+  c[3] = p->n_items;
+  c[4] = p->heavy_thr;
+  c[5] = p->has_wsb ? p->wsb.n_windows : 0;
+  c[6] = p->has_wsb ? p->wsb.n_blocks : 0;
+  c[7] = p->has_wsb ? p->wsb.n_tiles : 0;
+  c[8] = p->has_wsb ? p->wsb.n_resid : 0;
+  for (int32_t k = 9; k < n; ++k) c[k] = 0;
+  return GNN_OK;
+}
+
+int gnn_plan_wsb_export(const gnn_plan* p, int32_t* win_ptr, int32_t* blk_col, uint64_t* blk_bits,
+                        void* stream) {
+  if (!p || !win_ptr || !blk_col || !blk_bits) return fail(GNN_ERR_INVALID_VALUE, "wsb_export: NULL");
+  if (!p->has_wsb) return fail(GNN_ERR_INVALID_VALUE, "plan has no WSB tiles");
+  hipStream_t s = (hipStream_t)stream;
+  GNN_HIP(hipMemcpyAsync(win_ptr, p->wsb.win_ptr, ((size_t)p->wsb.n_windows + 1) * 4,
+                         hipMemcpyDeviceToDevice, s));
+  if (p->wsb.n_blocks > 0) {
+    GNN_HIP(hipMemcpyAsync(blk_col, p->wsb.blk_col, (size_t)p->wsb.n_blocks * 32,
+                           hipMemcpyDeviceToDevice, s));
+    GNN_HIP(hipMemcpyAsync(blk_bits, p->wsb.blk_bits, (size_t)p->wsb.n_blocks * 16,
+                           hipMemcpyDeviceToDevice, s));
+  }
+  return GNN_OK;
+}
+
+int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
+             int64_t ldy, gnn_norm norm, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (norm < GNN_NORM_NONE || norm > GNN_NORM_BOTH) return fail(GNN_ERR_INVALID_VALUE, "unknown norm");
+  if (F <= 0 || ldx < F || ldy < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldx >= F, ldy >= F");
+  if (!Y || (!X && csr->n_cols > 0)) return fail(GNN_ERR_INVALID_VALUE, "X or Y is NULL");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_aggregate(p, X, xtype, F, ldx, Y, ldy, AGG_SPMM, norm, csr->edge_val, nullptr, s);
+}
+
+int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+               gnn_reduce_op op, float* Y, int64_t ldy, int32_t* arg, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (op < GNN_SUM || op > GNN_MIN) return fail(GNN_ERR_INVALID_VALUE, "unknown reduce op");
+  if (F <= 0 || ldx < F || ldy < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldx >= F, ldy >= F");
+  if (!Y || (!X && csr->n_cols > 0)) return fail(GNN_ERR_INVALID_VALUE, "X or Y is NULL");
+  if (arg && (op == GNN_SUM || op == GNN_MEAN))
+    return fail(GNN_ERR_INVALID_VALUE, "arg is only defined for MAX / MIN");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  int mode = op == GNN_SUM ? AGG_SUM : op == GNN_MEAN ? AGG_MEAN : op == GNN_MAX ? AGG_MAX : AGG_MIN;
+  return launch_aggregate(p, X, xtype, F, ldx, Y, ldy, mode, GNN_NORM_NONE, nullptr, arg, s);
+}
+
+int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,
+                    const float* att, int32_t H, int32_t D, float neg_slope, float* out, float* lse,
+                    gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
+  if (!xl || !att || !out || (!xr && csr->n_cols > 0))
+    return fail(GNN_ERR_INVALID_VALUE, "xl, xr, att or out is NULL");
+  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
+  if ((D * esz) % 16 != 0 || H * D * esz > 1024)
+    return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
+  if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out) % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "xl, xr and out must be 16-byte aligned");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_gatv2(p, xl, xr, xtype, att, H, D, neg_slope, out, lse, s);
+}
+
+int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype,
+                 int32_t H, int32_t D, float scale, gnn_gt_mode mode, float* out, float* lse,
+                 gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, mode == GNN_GT_BLOCK16));
+  GNN_TRY(check_dtype(xtype));
+  if (mode != GNN_GT_CSR && mode != GNN_GT_BLOCK16) return fail(GNN_ERR_INVALID_VALUE, "unknown GT mode");
+  if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
+  if (!q || !out || ((!k || !v) && csr->n_cols > 0))
+    return fail(GNN_ERR_INVALID_VALUE, "q, k, v or out is NULL");
+  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
+  if ((D * esz) % 16 != 0 || H * D * esz > 2048)
+    return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  if (mode == GNN_GT_BLOCK16 && (xtype != GNN_BF16 || (D != 32 && D != 64 && D != 128)))
+    return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs bf16 and D in {32, 64, 128}");
+  if (csr->n_rows == 0) return GNN_OK;
+  float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, mode == GNN_GT_BLOCK16));
+  PlanGuard g{p, tr};
+  if (mode == GNN_GT_BLOCK16) return launch_gt_block16(p, q, k, v, H, D, sc, out, lse, s);
+  return launch_gt_csr(p, q, k, v, xtype, H, D, sc, out, lse, s);
+}
+
+int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* row_ptr_out,
+                int32_t* col_idx_out, void* stream) {
+  GNN_TRY(check_csr(csr, true));
+  if (kind != GNN_REORDER_DEGREE && kind != GNN_REORDER_RCM)
+    return fail(GNN_ERR_INVALID_VALUE, "unknown reorder kind");
+  if (!perm) return fail(GNN_ERR_INVALID_VALUE, "perm is NULL");
+  if ((row_ptr_out == nullptr) != (col_idx_out == nullptr))
+    return fail(GNN_ERR_INVALID_VALUE, "give both row_ptr_out and col_idx_out, or neither");
+  if (csr->n_rows == 0) return GNN_OK;
+  return launch_reorder(csr, kind, perm, row_ptr_out, col_idx_out, (hipStream_t)stream);
+}
+
+int gnn_permute_rows(const int32_t* perm, int32_t n, const void* X, gnn_dtype xtype, int32_t F,
+                     int64_t ldx, void* Xout, int64_t ldo, void* stream) {
+  GNN_TRY(check_dtype(xtype));
+  if (n < 0 || F <= 0 || ldx < F || ldo < F) return fail(GNN_ERR_INVALID_VALUE, "bad sizes");
+  if (n == 0) return GNN_OK;
+  if (!perm || !X || !Xout) return fail(GNN_ERR_INVALID_VALUE, "NULL pointer");
+  return launch_permute_rows(perm, n, X, xtype == GNN_BF16 ? 2 : 4, F, ldx, Xout, ldo,
+                             (hipStream_t)stream);
+}
+
+int gnn_copy_bytes(const void* src, void* dst, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return fail(GNN_ERR_INVALID_VALUE, "bad copy arguments");
+  if (n == 0) return GNN_OK;
+  return launch_copy(src, dst, n, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// Internal declarations of libgnn (not installed).  Device helpers shared by
+// the kernels, the plan object, and the host-side error plumbing.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "gnn.h"
+
+namespace gnn {
+
+// ---------------------------------------------------------------------------
+// Host-side error handling
+// ---------------------------------------------------------------------------
+
+void set_error(const std::string& msg);
+int fail(int status, const std::string& msg);
+
+#define GNN_HIP(call)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      return ::gnn::fail(e_ == hipErrorOutOfMemory ? GNN_ERR_OUT_OF_MEMORY         \
+                                                    : GNN_ERR_DEVICE,              \
+                         std::string(#call) + ": " + hipGetErrorString(e_));       \
+    }                                                                              \
+  } while (0)
+
+#define GNN_LAUNCH_CHECK(what)                                                     \
+  do {                                                                             \
+    hipError_t e_ = hipGetLastError();                                             \
+    if (e_ != hipSuccess)                                                          \
+      return ::gnn::fail(GNN_ERR_DEVICE, std::string(what) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+#define GNN_TRY(expr)            \
+  do {                           \
+    int s_ = (expr);             \
+    if (s_ != GNN_OK) return s_; \
+  } while (0)
+
+// Device allocation tracked by the plan (freed in gnn_plan_destroy).
+int dev_alloc(void** p, size_t bytes);
+
+// ---------------------------------------------------------------------------
+// Plan
+// ---------------------------------------------------------------------------
+
+struct WsbLayout {
+  int32_t n_windows = 0;
+  int64_t n_blocks = 0;     // 16x8 blocks
+  int64_t n_tiles = 0;      // dense 16x16 tiles routed to MFMA
+  int64_t n_resid = 0;      // residual CSR edges
+  int32_t* win_ptr = nullptr;     // [n_windows + 1] block offsets
+  int32_t* blk_col = nullptr;     // [n_blocks * 8]
+  uint64_t* blk_bits = nullptr;   // [n_blocks * 2]
+  int32_t* tile_ptr = nullptr;    // [n_windows + 1] dense-tile offsets
+  int32_t* tile_blk = nullptr;    // [n_tiles] first 16x8 block of each dense tile
+  int32_t* res_ptr = nullptr;     // [n_rows + 1] residual CSR
+  int32_t* res_col = nullptr;     // [n_resid]
+};
+
+}  // namespace gnn
+
+struct gnn_plan {
+  int32_t n_rows = 0, n_cols = 0;
+  int64_t nnz = 0;
+  const int32_t* row_ptr = nullptr;
+  const int32_t* col_idx = nullptr;
+  gnn_plan_opts opts{};
+  hipStream_t stream = nullptr;
+
+  // degrees
+  int32_t* deg_out = nullptr;  // [n_cols]
+
+  // degree bins (appendix D.1: light / heavy split by a degree quantile)
+  int32_t light_max = 32;
+  int32_t heavy_thr = 0;     // rows above are split into chunks (INT32_MAX: never)
+  int32_t chunk_edges = 512;
+  int64_t n_light = 0, n_medium = 0, n_heavy = 0;
+  int4* items = nullptr;     // [n_items] (row, e_begin, e_end, multi index or -1)
+  int64_t n_items = 0;
+  int4* multi = nullptr;     // [n_multi] (row, first item, item count, 0)
+  int64_t n_multi = 0;
+  int32_t max_items_per_row = 0;
+
+  // workspace (partials / packed words); grows on demand
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+
+  gnn::WsbLayout wsb;
+  bool has_wsb = false;
+
+  // every device allocation of the plan
+  void* allocs[32] = {};
+  int n_allocs = 0;
+};
+
+namespace gnn {
+
+int plan_alloc(gnn_plan* p, void** ptr, size_t bytes);
+int plan_workspace(gnn_plan* p, size_t bytes, void** out);
+int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p);
+int plan_build_wsb(gnn_plan* p, hipStream_t s);
+int check_plan(const gnn_plan* p, const gnn_csr* csr);
+
+// Launchers (host).  All validate nothing: the entry points did.
+int launch_aggregate(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y,
+                     int64_t ldy, int mode, gnn_norm norm, const float* edge_val, int32_t* arg,
+                     hipStream_t s);
+int launch_gatv2(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, const float* att,
+                 int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s);
+int launch_gt_csr(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
+                  int32_t D, float scale, float* out, float* lse, hipStream_t s);
+int launch_gt_block16(gnn_plan* p, const void* q, const void* k, const void* v, int32_t H,
+                      int32_t D, float scale, float* out, float* lse, hipStream_t s);
+int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* rp_out,
+                   int32_t* ci_out, hipStream_t s);
+int launch_permute_rows(const int32_t* perm, int32_t n, const void* X, int elem_bytes, int32_t F,
+                        int64_t ldx, void* Xout, int64_t ldo, hipStream_t s);
+int launch_copy(const void* src, void* dst, int64_t n, hipStream_t s);
+
+// Device-wide exclusive scan of int32 counts into int32 offsets (out has n+1
+// entries, out[n] = total); scratch is allocated and freed stream-ordered.
+int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s);
+
+// Aggregation modes for launch_aggregate
+enum AggMode { AGG_SUM = 0, AGG_MEAN = 1, AGG_MAX = 2, AGG_MIN = 3, AGG_SPMM = 4 };
+
+}  // namespace gnn
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+namespace gnn {
+namespace dev {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Order-preserving map of IEEE-754 float bits to uint32 (appendix D.1):
+// negative values have every bit inverted, non-negative values get the sign
+// bit set; unsigned order then equals float order with -0.0 < +0.0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X; this
+// maps the hardware workgroup id to a logical one so that each XCD receives
+// a contiguous range of logical ids (neighbouring rows share one L2).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
+  constexpr uint32_t NX = 8;
+  uint32_t per = nblocks / NX, rem = nblocks % NX;
+  uint32_t x = bid % NX, k = bid / NX;
+  // XCD x owns per (+1 for x < rem) consecutive logical ids
+  uint32_t base = x * per + (x < rem ? x : rem);
+  uint32_t lid = base + k;
+  return lid;
+}
+
+}  // namespace dev
+}  // namespace gnn

@@ -1,0 +1,360 @@
+// Plan construction: degrees, the degree-quantile threshold, degree bins and
+// edge-chunk work items.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", appendix D.1: destinations are split into light and heavy
+// sets by a graph-specific degree threshold, the gamma-quantile of the degree
+// distribution (gamma in [0.99, 0.999]); heavy rows are cut into chunks of
+// EDGES_PER_BLOCK edges processed by separate blocks.  Appendix D.4: degrees
+// are precomputed once per graph and cached.
+//
+// Bins used here (the MI355X mapping):
+//   light  : deg <= light_max           one 32-lane slot per row
+//   medium : light_max < deg <= thr     one workgroup per row
+//   heavy  : deg > thr                  ceil(deg / chunk) workgroups, merged
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;                       // per thread
+constexpr int kScanTile = kScanThreads * kScanItems;  // 4096 elements per block
+constexpr int kHistBins = 65536;
+
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Block-wide exclusive scan of one value per thread; returns the block total.
+__device__ int block_excl_scan(int v, int* lds_waves, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NW = kScanThreads / 64;
+  int inc = wave_incl_scan(v);
+  if (lane == 63) lds_waves[wave] = inc;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    int s = lds_waves[w];
+    if (w < wave) off += s;
+    total += s;
+  }
+  __syncthreads();
+  return off + inc - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_block_sums(const int32_t* in, int64_t n,
+                                                                  int32_t* sums) {
+  __shared__ int lw[kScanThreads / 64];
+  int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k)
+    if (base + k < n) s += in[base + k];
+  int total;
+  block_excl_scan(s, lw, total);
+  if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_tiles(const int32_t* in, int64_t n,
+                                                             const int32_t* block_off,
+                                                             int32_t* out) {
+  __shared__ int lw[kScanThreads / 64];
+  int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int v[kScanItems];
+  int s = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    v[k] = (base + k < n) ? in[base + k] : 0;
+    s += v[k];
+  }
+  int total;
+  int run = block_excl_scan(s, lw, total) + (block_off ? block_off[blockIdx.x] : 0);
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    if (base + k < n) out[base + k] = run;
+    run += v[k];
+  }
+  // the last element's successor: out[n] = grand total
+  if (base + kScanItems >= n && base < n) out[n] = run;
+  if (n == 0 && blockIdx.x == 0 && threadIdx.x == 0) out[0] = 0;
+}
+
+// ---------------------------------------------------------------------------
+
+__global__ void k_deg_out(const int32_t* col_idx, int64_t nnz, int32_t* deg_out) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; e < nnz; e += stride) atomicAdd(&deg_out[col_idx[e]], 1);
+}
+
+// Degree histogram.  Low degrees are very common on power-law graphs (most
+// rows have degree 0 or 1), so each workgroup counts bins below kLdsBins in
+// LDS and flushes its non-zero bins once; larger degrees go straight to the
+// global histogram.
+constexpr int kLdsBins = 4096;
+
+__global__ __launch_bounds__(256) void k_deg_hist(const int32_t* row_ptr, int32_t n, int32_t* hist) {
+  __shared__ int32_t lh[kLdsBins];
+  for (int b = threadIdx.x; b < kLdsBins; b += blockDim.x) lh[b] = 0;
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += stride) {
+    const int64_t i = base + threadIdx.x;
+    const bool ok = i < n;
+    const int d = ok ? row_ptr[i + 1] - row_ptr[i] : -1;
+    // degrees 0 and 1 are counted per wave by ballot, the rest by atomics
+    const unsigned long long b0 = __ballot(d == 0), b1 = __ballot(d == 1);
+    if ((threadIdx.x & 63) == 0) {
+      if (b0) atomicAdd(&lh[0], (int)__popcll(b0));
+      if (b1) atomicAdd(&lh[1], (int)__popcll(b1));
+    }
+    if (d >= 2) {
+      if (d < kLdsBins) atomicAdd(&lh[d], 1);
+      else atomicAdd(&hist[d < kHistBins - 1 ? d : kHistBins - 1], 1);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < kLdsBins; b += blockDim.x)
+    if (lh[b]) atomicAdd(&hist[b], lh[b]);
+}
+
+// Smallest degree d with #{rows with deg <= d} >= ceil(gamma * n): the
+// gamma-quantile.  One block; the histogram is scanned serially in chunks.
+__global__ __launch_bounds__(256) void k_quantile(const int32_t* hist, int32_t n, float gamma,
+                                                  int32_t* out) {
+  __shared__ int lw[4];
+  __shared__ int carry;
+  __shared__ int found;
+  if (threadIdx.x == 0) {
+    carry = 0;
+    found = kHistBins - 1;
+  }
+  __syncthreads();
+  int64_t target = (int64_t)ceil((double)gamma * (double)n);
+  if (target < 1) target = 1;
+  for (int base = 0; base < kHistBins; base += 256) {
+    int v = hist[base + threadIdx.x];
+    int total;
+    // reuse the generic block scan (256 threads)
+    int ex = block_excl_scan(v, lw, total);
+    int incl = carry + ex + v;
+    if (incl >= target && (carry + ex) < target) found = base + threadIdx.x;
+    __syncthreads();
+    if (threadIdx.x == 0) carry += total;
+    __syncthreads();
+    if (carry >= target) break;
+  }
+  if (threadIdx.x == 0) *out = found;
+}
+
+__global__ void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max, int32_t thr,
+                           int32_t chunk, int32_t* cnt, int32_t* is_multi,
+                           unsigned long long* stats /* light, medium, heavy, max_chunks */) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int c = 0;
+  if (i < n) {
+    int d = row_ptr[i + 1] - row_ptr[i];
+    if (d <= light_max) c = 0;
+    else if (d <= thr) c = 1;
+    else c = (d + chunk - 1) / chunk;
+    cnt[i] = c;
+    is_multi[i] = c > 1 ? 1 : 0;
+  }
+  // block totals, one atomic each
+  unsigned long long l = (i < n && c == 0), m = (i < n && c == 1), h = (i < n && c > 1);
+  for (int d = 32; d >= 1; d >>= 1) {
+    l += __shfl_xor(l, d);
+    m += __shfl_xor(m, d);
+    h += __shfl_xor(h, d);
+  }
+  int cm = c;
+  for (int d = 32; d >= 1; d >>= 1) cm = max(cm, __shfl_xor(cm, d));
+  if ((threadIdx.x & 63) == 0) {
+    if (l) atomicAdd(&stats[0], l);
+    if (m) atomicAdd(&stats[1], m);
+    if (h) atomicAdd(&stats[2], h);
+    atomicMax(&stats[3], (unsigned long long)cm);
+  }
+}
+
+__global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, const int32_t* cnt,
+                             const int32_t* item_off, const int32_t* multi_off, int4* items,
+                             int4* multi) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int c = cnt[i];
+  if (c == 0) return;
+  int b = row_ptr[i], e = row_ptr[i + 1];
+  int off = item_off[i];
+  int m = c > 1 ? multi_off[i] : -1;
+  if (c == 1) {
+    items[off] = make_int4((int)i, b, e, -1);
+    return;
+  }
+  for (int k = 0; k < c; ++k) {
+    int eb = b + k * chunk;
+    int ee = min(e, eb + chunk);
+    items[off + k] = make_int4((int)i, eb, ee, m);
+  }
+  multi[m] = make_int4((int)i, off, c, 0);
+}
+
+}  // namespace
+
+int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s) {
+  int64_t nb = (n + kScanTile - 1) / kScanTile;
+  if (nb <= 1) {
+    hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kScanThreads), 0, s, in, n, nullptr, out);
+    GNN_LAUNCH_CHECK("scan");
+    return GNN_OK;
+  }
+  int32_t* sums = nullptr;
+  int32_t* offs = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&sums, nb * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&offs, (nb + 1) * 4, s));
+  hipLaunchKernelGGL(k_scan_block_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, sums);
+  GNN_LAUNCH_CHECK("scan sums");
+  int rc = exclusive_scan_i32(sums, offs, nb, s);
+  if (rc == GNN_OK) {
+    hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, offs,
+                       out);
+    GNN_LAUNCH_CHECK("scan tiles");
+  }
+  GNN_HIP(hipFreeAsync(sums, s));
+  GNN_HIP(hipFreeAsync(offs, s));
+  return rc;
+}
+
+int plan_alloc(gnn_plan* p, void** ptr, size_t bytes) {
+  if (p->n_allocs >= (int)(sizeof(p->allocs) / sizeof(p->allocs[0])))
+    return fail(GNN_ERR_DEVICE, "plan: too many allocations");
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
+  if (e != hipSuccess) return fail(GNN_ERR_OUT_OF_MEMORY, std::string("plan alloc: ") + hipGetErrorString(e));
+  p->allocs[p->n_allocs++] = q;
+  *ptr = q;
+  return GNN_OK;
+}
+
+int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
+  if (bytes <= p->ws_bytes && p->ws) {
+    *out = p->ws;
+    return GNN_OK;
+  }
+  if (p->ws) {
+    GNN_HIP(hipStreamSynchronize(p->stream));
+    GNN_HIP(hipFree(p->ws));
+    p->ws = nullptr;
+    p->ws_bytes = 0;
+  }
+  void* q = nullptr;
+  hipError_t e = hipMalloc(&q, bytes);
+  if (e != hipSuccess) return fail(GNN_ERR_OUT_OF_MEMORY, std::string("workspace: ") + hipGetErrorString(e));
+  p->ws = q;
+  p->ws_bytes = bytes;
+  *out = q;
+  return GNN_OK;
+}
+
+int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p) {
+  p->n_rows = csr->n_rows;
+  p->n_cols = csr->n_cols;
+  p->nnz = csr->nnz;
+  p->row_ptr = csr->row_ptr;
+  p->col_idx = csr->col_idx;
+  p->stream = s;
+  if (opts) p->opts = *opts;
+  float gamma = p->opts.heavy_quantile == 0.0f ? 0.99f : p->opts.heavy_quantile;
+  p->light_max = p->opts.light_max_deg > 0 ? p->opts.light_max_deg : 32;
+  p->chunk_edges = p->opts.chunk_edges > 0 ? p->opts.chunk_edges : 512;
+  if (p->opts.wsb_min_nnz <= 0) p->opts.wsb_min_nnz = 32;
+
+  const int32_t n = p->n_rows;
+  GNN_TRY(plan_alloc(p, (void**)&p->deg_out, (size_t)std::max(p->n_cols, 1) * 4));
+  GNN_HIP(hipMemsetAsync(p->deg_out, 0, (size_t)std::max(p->n_cols, 1) * 4, s));
+  if (p->nnz > 0) {
+    int64_t blocks = std::min<int64_t>((p->nnz + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_deg_out, dim3((unsigned)blocks), dim3(256), 0, s, p->col_idx, p->nnz,
+                       p->deg_out);
+    GNN_LAUNCH_CHECK("deg_out");
+  }
+
+  // gamma-quantile degree threshold
+  int32_t* hist = nullptr;
+  int32_t* tmp = nullptr;  // [threshold]
+  GNN_HIP(hipMallocAsync((void**)&hist, kHistBins * 4 + 16, s));
+  tmp = hist + kHistBins;
+  int32_t thr_host = INT32_MAX;
+  if (gamma > 0.0f && n > 0) {
+    GNN_HIP(hipMemsetAsync(hist, 0, kHistBins * 4, s));
+    int64_t blocks = std::min<int64_t>((n + 255) / 256, 512);
+    hipLaunchKernelGGL(k_deg_hist, dim3((unsigned)blocks), dim3(256), 0, s, p->row_ptr, n, hist);
+    GNN_LAUNCH_CHECK("deg_hist");
+    hipLaunchKernelGGL(k_quantile, dim3(1), dim3(256), 0, s, hist, n, std::min(gamma, 1.0f), tmp);
+    GNN_LAUNCH_CHECK("quantile");
+    GNN_HIP(hipMemcpyAsync(&thr_host, tmp, 4, hipMemcpyDeviceToHost, s));
+    GNN_HIP(hipStreamSynchronize(s));
+    // a row is heavy only if it also exceeds one chunk
+    thr_host = std::max(thr_host, p->chunk_edges);
+  }
+  p->heavy_thr = thr_host;
+  GNN_HIP(hipFreeAsync(hist, s));
+
+  // classify rows, scan counts, fill items
+  int32_t *cnt = nullptr, *ism = nullptr, *ioff = nullptr, *moff = nullptr;
+  unsigned long long* stats = nullptr;
+  size_t nn = (size_t)std::max(n, 1);
+  GNN_HIP(hipMallocAsync((void**)&cnt, nn * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&ism, nn * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&ioff, (nn + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&moff, (nn + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&stats, 4 * 8, s));
+  GNN_HIP(hipMemsetAsync(stats, 0, 4 * 8, s));
+  if (n > 0) {
+    hipLaunchKernelGGL(k_classify, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p->row_ptr, n,
+                       p->light_max, p->heavy_thr, p->chunk_edges, cnt, ism, stats);
+    GNN_LAUNCH_CHECK("classify");
+  }
+  GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
+  GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
+  int32_t tot[2] = {0, 0};
+  unsigned long long st[4] = {0, 0, 0, 0};
+  GNN_HIP(hipMemcpyAsync(&tot[0], ioff + n, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipMemcpyAsync(&tot[1], moff + n, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipMemcpyAsync(st, stats, 32, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  p->n_items = tot[0];
+  p->n_multi = tot[1];
+  p->n_light = (int64_t)st[0];
+  p->n_medium = (int64_t)st[1];
+  p->n_heavy = (int64_t)st[2];
+  p->max_items_per_row = (int32_t)st[3];
+  GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(p->n_items, 1) * sizeof(int4)));
+  GNN_TRY(plan_alloc(p, (void**)&p->multi, (size_t)std::max<int64_t>(p->n_multi, 1) * sizeof(int4)));
+  if (n > 0) {
+    hipLaunchKernelGGL(k_fill_items, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p->row_ptr,
+                       n, p->chunk_edges, cnt, ioff, moff, p->items, p->multi);
+    GNN_LAUNCH_CHECK("fill items");
+  }
+  GNN_HIP(hipFreeAsync(cnt, s));
+  GNN_HIP(hipFreeAsync(ism, s));
+  GNN_HIP(hipFreeAsync(ioff, s));
+  GNN_HIP(hipFreeAsync(moff, s));
+  GNN_HIP(hipFreeAsync(stats, s));
+  if (p->opts.build_wsb) GNN_TRY(plan_build_wsb(p, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  return GNN_OK;
+}
+
+}  // namespace gnn

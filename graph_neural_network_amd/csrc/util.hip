@@ -1,0 +1,88 @@
+// Small data-movement kernels: row gather for reordered features and a plain
+// streaming copy used to calibrate bandwidth figures and hardware counters.
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+// One wave per destination row; 16-byte accesses when the row allows it.
+__global__ __launch_bounds__(256) void k_permute_rows16(const int32_t* perm, int32_t n,
+                                                        const uint4* X, int64_t ldx16, uint4* Y,
+                                                        int64_t ldy16, int32_t row16) {
+  int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const uint4* src = X + (int64_t)perm[r] * ldx16;
+  uint4* dst = Y + r * ldy16;
+  for (int c = threadIdx.x & 63; c < row16; c += 64) dst[c] = src[c];
+}
+
+__global__ __launch_bounds__(256) void k_permute_rows_b(const int32_t* perm, int32_t n,
+                                                        const uint8_t* X, int64_t ldxb, uint8_t* Y,
+                                                        int64_t ldyb, int32_t rowb, int esz) {
+  int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const uint8_t* src = X + (int64_t)perm[r] * ldxb;
+  uint8_t* dst = Y + r * ldyb;
+  if (esz == 2) {
+    for (int c = threadIdx.x & 63; c < rowb / 2; c += 64)
+      reinterpret_cast<uint16_t*>(dst)[c] = reinterpret_cast<const uint16_t*>(src)[c];
+  } else {
+    for (int c = threadIdx.x & 63; c < rowb / 4; c += 64)
+      reinterpret_cast<uint32_t*>(dst)[c] = reinterpret_cast<const uint32_t*>(src)[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_copy16(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                int64_t n16) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+__global__ void k_copy_tail(const uint8_t* src, uint8_t* dst, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+}  // namespace
+
+int launch_permute_rows(const int32_t* perm, int32_t n, const void* X, int esz, int32_t F,
+                        int64_t ldx, void* Xout, int64_t ldo, hipStream_t s) {
+  const int64_t rowb = (int64_t)F * esz;
+  const unsigned blocks = (unsigned)((n + 3) / 4);
+  if (rowb % 16 == 0 && (ldx * esz) % 16 == 0 && (ldo * esz) % 16 == 0 &&
+      ((uintptr_t)X | (uintptr_t)Xout) % 16 == 0) {
+    hipLaunchKernelGGL(k_permute_rows16, dim3(blocks), dim3(256), 0, s, perm, n, (const uint4*)X,
+                       ldx * esz / 16, (uint4*)Xout, ldo * esz / 16, (int32_t)(rowb / 16));
+  } else {
+    hipLaunchKernelGGL(k_permute_rows_b, dim3(blocks), dim3(256), 0, s, perm, n, (const uint8_t*)X,
+                       ldx * esz, (uint8_t*)Xout, ldo * esz, (int32_t)rowb, esz);
+  }
+  GNN_LAUNCH_CHECK("permute_rows");
+  return GNN_OK;
+}
+
+int launch_copy(const void* src, void* dst, int64_t n, hipStream_t s) {
+  int64_t head = 0;
+  if (((uintptr_t)src | (uintptr_t)dst) % 16 == 0) {
+    int64_t n16 = n / 16;
+    if (n16 > 0) {
+      int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 256 * 64);
+      hipLaunchKernelGGL(k_copy16, dim3((unsigned)blocks), dim3(256), 0, s, (const uint4*)src,
+                         (uint4*)dst, n16);
+      GNN_LAUNCH_CHECK("copy");
+    }
+    head = n16 * 16;
+  }
+  int64_t rest = n - head;
+  if (rest > 0) {
+    hipLaunchKernelGGL(k_copy_tail, dim3((unsigned)((rest + 255) / 256)), dim3(256), 0, s,
+                       (const uint8_t*)src + head, (uint8_t*)dst + head, rest);
+    GNN_LAUNCH_CHECK("copy tail");
+  }
+  return GNN_OK;
+}
+
+}  // namespace gnn

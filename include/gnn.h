@@ -1,0 +1,226 @@
+/*
+ * gnn.h — C ABI of libgnn: GNN neighbourhood aggregation over a CSR adjacency
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * Operations (Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+ * implementations"; section 2.2 names the three operator families, appendix D
+ * gives the kernels):
+ *   gnn_spmm         SpMM-based convolution Y = A_norm X      (section 2.2 (i), appendix D.4)
+ *   gnn_reduce       segmented sum / mean / max / min          (section 2.2 (ii), appendix D.1)
+ *   gnn_gatv2_fused  GATv2 attention, one pass, online softmax (section 2.2 (iii), appendix D.2)
+ *   gnn_gt_fused     Graph Transformer attention, CSR or 16x16 block-sparse
+ *                                                              (appendix D.2 and D.3)
+ *   gnn_reorder      degree-sort or RCM vertex reordering      (section 2.4; RCM as in
+ *                    Tang et al., "A High-Throughput Solver for Marginalized Graph
+ *                    Kernels on GPU", graph reordering section)
+ *
+ * Conventions for every entry point:
+ *   - Graph: CSR whose rows are DESTINATIONS: row i lists the sources j of the
+ *     edges j -> i in col_idx[row_ptr[i] .. row_ptr[i+1]).  32-bit indices
+ *     (appendix D.4 uses 32-bit CSR indices); nnz < 2^31.  Columns need not be
+ *     sorted except where stated (gnn_reorder output is sorted; the WSB path
+ *     needs no order either).  Duplicate entries count as separate edges.
+ *   - All array pointers are DEVICE pointers, owned by the caller, unless a
+ *     comment says otherwise.  The library never frees caller memory.
+ *   - Dense features are row-major with a row stride (ld*, in elements).
+ *   - Outputs are float32.  bf16 is an input format only; accumulation is
+ *     float32.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream) unless stated.  Validation happens on the host before any
+ *     launch; on an error nothing is launched and no output is touched.
+ *   - Return value: a gnn_status.  gnn_last_error() gives a thread-local
+ *     message for the last failing call on the calling thread.
+ *   - Empty neighbourhoods: sum / mean / SpMM give 0; max / min give 0 with
+ *     arg -1; attention gives out 0 and lse = -inf.
+ */
+#ifndef GNN_H_
+#define GNN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GNN_OK = 0,
+  GNN_ERR_INVALID_VALUE = 1, /* null pointer, negative size, ld < width, bad enum */
+  GNN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head dim for a mode) */
+  GNN_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
+  GNN_ERR_DEVICE = 4,        /* a HIP call failed (launch error, earlier fault) */
+  GNN_ERR_SIZE_OVERFLOW = 5, /* nnz >= 2^31, or a size product overflows */
+  GNN_ERR_PLAN_MISMATCH = 6  /* plan was built for another CSR */
+} gnn_status;
+
+typedef enum { GNN_F32 = 0, GNN_BF16 = 1 } gnn_dtype;
+
+/* Edge weights of gnn_spmm (appendix D.4 names the modes none/left/right/both;
+ * the GCN weight 1/sqrt(deg(i) deg(j)) is in section 2.2):
+ *   NONE  w = 1                  LEFT  w = 1/deg_in(i)
+ *   RIGHT w = 1/deg_out(j)       BOTH  w = 1/sqrt(deg_in(i) deg_out(j))
+ * deg_in(i) = row length, deg_out(j) = number of entries equal to j, both
+ * counting self loops present in the CSR; times edge_val[e] when given. */
+typedef enum { GNN_NORM_NONE = 0, GNN_NORM_LEFT = 1, GNN_NORM_RIGHT = 2, GNN_NORM_BOTH = 3 } gnn_norm;
+
+/* Segmented reductions (section 2.2 (ii), appendix D.1).  MEAN divides the
+ * sum by deg_in.  MAX / MIN follow the IEEE total order on non-NaN values
+ * (-0.0 < +0.0, the order of the order-preserving key of appendix D.1);
+ * on equal values the smallest source index wins.  NaN inputs are not
+ * supported. */
+typedef enum { GNN_SUM = 0, GNN_MEAN = 1, GNN_MAX = 2, GNN_MIN = 3 } gnn_reduce_op;
+
+/* Graph Transformer kernel choice: streaming CSR (appendix D.2) or the
+ * 16x16 block-sparse matrix-core path on WSB tiles (appendix D.3), whose
+ * sparse leftovers are processed by the CSR loop inside the same kernel. */
+typedef enum { GNN_GT_CSR = 0, GNN_GT_BLOCK16 = 1 } gnn_gt_mode;
+
+typedef enum { GNN_REORDER_DEGREE = 0, GNN_REORDER_RCM = 1 } gnn_reorder_kind;
+
+typedef struct gnn_csr {
+  int32_t n_rows;          /* destinations */
+  int32_t n_cols;          /* sources (== n_rows for a square adjacency) */
+  int64_t nnz;             /* == row_ptr[n_rows]; must be < 2^31 */
+  const int32_t* row_ptr;  /* device [n_rows + 1], row_ptr[0] = 0, non-decreasing */
+  const int32_t* col_idx;  /* device [nnz], each in [0, n_cols) */
+  const float* edge_val;   /* device [nnz] or NULL (all ones); gnn_spmm only */
+} gnn_csr;
+
+/* Tuning knobs of a plan (appendix D.1 "degree threshold and autotuning
+ * parameters"; appendix D.3 window and block sizes).  Zero-initialise and set
+ * what you need; zero means the default. */
+typedef struct gnn_plan_opts {
+  float heavy_quantile;    /* gamma: rows above this degree quantile are split
+                              into edge chunks (default 0.99; < 0 = never split) */
+  int32_t light_max_deg;   /* rows up to this degree run one per 32-lane slot (default 32) */
+  int32_t chunk_edges;     /* edges per chunk of a split row (default 512) */
+  int32_t build_wsb;       /* 1 = also build the 16x16 block-sparse tiles (GT BLOCK16) */
+  int32_t wsb_min_nnz;     /* tau: tiles with fewer edges go to the CSR residual (default 32) */
+  int32_t reserved[4];
+} gnn_plan_opts;
+
+/* Opaque plan: the per-graph cache of appendix D.4 made explicit.  It holds
+ * the preprocessing products (degrees, normalisation scales, degree bins,
+ * edge-chunk work items, WSB tiles) in library-owned device memory.  Bound to
+ * one (n_rows, n_cols, nnz, row_ptr, col_idx); using it with another CSR is
+ * GNN_ERR_PLAN_MISMATCH.  One call at a time per plan (its workspace is
+ * shared). */
+typedef struct gnn_plan gnn_plan;
+
+/* Build a plan for `csr` (degree histogram, gamma-quantile threshold, bins,
+ * chunk items; WSB tiles if opts->build_wsb).  opts may be NULL.  Launches on
+ * `stream` and SYNCHRONISES it once (bin sizes are read back).  The CSR
+ * arrays must stay alive and unchanged while the plan is used.
+ * Errors: INVALID_VALUE, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
+int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream, gnn_plan** out);
+
+/* Free a plan and its device memory (the cache reset of appendix D.4).  Waits
+ * for the plan's stream.  NULL is a no-op. */
+int gnn_plan_destroy(gnn_plan* plan);
+
+/* Plan statistics for reports: counts[0] = light rows, [1] = medium rows,
+ * [2] = heavy rows, [3] = chunk work items, [4] = degree threshold used,
+ * [5] = WSB windows, [6] = WSB blocks (16x8), [7] = dense 16x16 tiles,
+ * [8] = residual CSR edges.  Host memory, n >= 9. */
+int gnn_plan_stats(const gnn_plan* plan, int64_t* counts, int32_t n);
+
+/* Copy the plan's WSB layout (appendix D.3: windows of 16 rows, sorted
+ * distinct source columns cut into blocks of 8 zero-padded columns, a 16x8
+ * occupancy bitmap as two 64-bit words with bit r*8+c) into caller DEVICE
+ * buffers: win_ptr [n_windows + 1], blk_col [n_blocks * 8],
+ * blk_bits [n_blocks * 2].  Sizes from gnn_plan_stats.  Asynchronous.
+ * Errors: INVALID_VALUE (null, or the plan has no WSB). */
+int gnn_plan_wsb_export(const gnn_plan* plan, int32_t* win_ptr, int32_t* blk_col,
+                        uint64_t* blk_bits, void* stream);
+
+/* SpMM: Y[i, f] = sum_{e in row i} w_e * X[col_idx[e], f], f < F.
+ * X: device [n_cols, ldx] of `xtype`; Y: device [n_rows, ldy] float32.
+ * plan may be NULL (a transient one is built, which synchronises `stream`).
+ * Errors: INVALID_VALUE (null, F <= 0, ldx < F, ldy < F, bad enum),
+ * PLAN_MISMATCH, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
+int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
+             int64_t ldy, gnn_norm norm, gnn_plan* plan, void* stream);
+
+/* Segmented reduction over each row's sources: Y[i, f] = op_j X[j, f].
+ * arg: device [n_rows, lda = F] int32 or NULL; for MAX / MIN it receives the
+ * winning source index (-1 for an empty row); it must be NULL for SUM / MEAN.
+ * Light rows run one 32-lane slot per row, medium rows one workgroup per row,
+ * heavy rows (above the gamma-quantile) are split into edge chunks merged by a
+ * deterministic partials pass (SUM / MEAN) or by packed 64-bit (key, index)
+ * atomics (MAX / MIN) followed by an unpack kernel (appendix D.1).
+ * Errors as gnn_spmm. */
+int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+               gnn_reduce_op op, float* Y, int64_t ldy, int32_t* arg, gnn_plan* plan, void* stream);
+
+/* Fused GATv2 forward (section 2.2 (iii); appendix D.2 "fused CSR forward
+ * (GATv2)"): for each destination i and head h,
+ *   e_ij = sum_d att[h, d] * LeakyReLU(xl[i, h, d] + xr[j, h, d]),
+ *   LeakyReLU(z) = z > 0 ? z : neg_slope * z,
+ *   out[i, h, :] = sum_j softmax_j(e_ij) * xr[j, h, :],
+ *   lse[i, h] = log sum_j exp(e_ij),
+ * over the CSR row of i (add self loops to the CSR to include j = i).
+ * xl: device [n_rows, H, D], xr: device [n_cols, H, D], both `xtype`, dense
+ * (row stride H*D); att: device [H, D] float32; out: device [n_rows, H, D]
+ * float32; lse: device [n_rows, H] float32 or NULL.  One pass with an online
+ * softmax: no per-edge logits, weights or messages are written to memory.
+ * Supported: xtype BF16 or F32, H*D*sizeof(xtype) a multiple of 16 bytes and
+ * at most 1024 bytes, D*sizeof(xtype) a multiple of 16 bytes.  plan may be
+ * NULL (it then only selects heavy rows for the split-row variant).
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, DEVICE. */
+int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,
+                    const float* att, int32_t H, int32_t D, float neg_slope, float* out, float* lse,
+                    gnn_plan* plan, void* stream);
+
+/* Fused Graph Transformer forward (section 2.2 (iii): q_i = W_Q h_i,
+ * k_j = W_K h_j, v_j = W_V h_j, e_ij = q_i . k_j / sqrt(D); appendix D.2 and
+ * D.3): for each destination i and head h,
+ *   out[i, h, :] = sum_j softmax_j(scale * <q[i,h,:], k[j,h,:]>) * v[j, h, :],
+ *   lse[i, h] = log sum_j exp(scale * <q[i,h,:], k[j,h,:]>).
+ * q: device [n_rows, H, D]; k, v: device [n_cols, H, D]; `xtype` BF16 (or F32
+ * in CSR mode); scale <= 0 means 1/sqrt(D); out: device [n_rows, H, D]
+ * float32; lse: device [n_rows, H] float32 or NULL.
+ * GNN_GT_CSR: streaming online softmax, any supported shape (H*D*sizeof a
+ * multiple of 16 bytes, at most 2048 bytes; D*sizeof a multiple of 16 bytes).
+ * GNN_GT_BLOCK16: needs a plan built with build_wsb = 1, square CSR,
+ * xtype BF16, D in {32, 64, 128}; dense 16x16 tiles run on bf16 MFMA with the
+ * softmax weights rounded to bf16 for the P.V product; the residual edges of
+ * sparse tiles run the CSR loop into the same per-row softmax state.
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, DEVICE. */
+int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype,
+                 int32_t H, int32_t D, float scale, gnn_gt_mode mode, float* out, float* lse,
+                 gnn_plan* plan, void* stream);
+
+/* Vertex reordering of a square CSR (n_rows == n_cols).
+ * DEGREE: perm sorts vertices by descending deg_in, ties by ascending id
+ * (stable).  RCM: reverse Cuthill-McKee on the symmetrised pattern A u A^T
+ * without self loops, each component started at its unvisited vertex of
+ * smallest (degree, id), neighbours visited in increasing (degree, id).
+ * perm: device [n_rows] int32, perm[new] = old (required).
+ * row_ptr_out [n_rows + 1] and col_idx_out [nnz] (device, both or neither):
+ * if given, receive the relabelled CSR P A P^T with each row's columns
+ * sorted ascending.  Synchronises `stream` (RCM runs level by level).
+ * Errors: INVALID_VALUE (null, not square, one of the two outputs missing),
+ * SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
+int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* row_ptr_out,
+                int32_t* col_idx_out, void* stream);
+
+/* Gather rows: Xout[p, :] = X[perm[p], :] for p < n, F elements of `xtype`
+ * per row, strides ldx / ldo (elements).  Used to carry features into a
+ * reordered vertex numbering.  Errors: INVALID_VALUE, DEVICE. */
+int gnn_permute_rows(const int32_t* perm, int32_t n, const void* X, gnn_dtype xtype, int32_t F,
+                     int64_t ldx, void* Xout, int64_t ldo, void* stream);
+
+/* Plain streaming copy of n bytes (device to device), used to calibrate
+ * bandwidth measurements and hardware counters.  Asynchronous. */
+int gnn_copy_bytes(const void* src, void* dst, int64_t n, void* stream);
+
+/* Text of a status code (static storage). */
+const char* gnn_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* gnn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GNN_H_ */

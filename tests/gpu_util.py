@@ -1,0 +1,52 @@
+"""Helpers shared by the GPU parity tests (test-side only)."""
+import numpy as np
+import torch
+
+import graph_neural_network_amd as gnn
+
+
+def cuda_ok() -> bool:
+    return torch.cuda.is_available()
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def dev_bf16(u16: np.ndarray) -> torch.Tensor:
+    """bf16 bit patterns (uint16 numpy) -> torch.bfloat16 on the GPU, bit for bit."""
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_csr(rp, ci, n_cols=None, edge_val=None) -> gnn.Csr:
+    ev = None if edge_val is None else dev(edge_val.astype(np.float32))
+    return gnn.Csr(dev(rp.astype(np.int32)), dev(ci.astype(np.int32)) if ci.size else
+                   torch.zeros(1, dtype=torch.int32, device="cuda"), n_cols=n_cols, edge_val=ev)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def scaled_err(got, ref, mag):
+    """max |got - ref| / mag elementwise; where mag == 0 the result must be exactly ref."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    mag = np.asarray(mag, np.float64)
+    zero = mag == 0
+    if np.any(got[zero] != ref[zero]):
+        return np.inf
+    d = np.abs(got - ref)
+    if (~zero).any():
+        return float((d[~zero] / mag[~zero]).max())
+    return 0.0
+
+
+def bits_equal_f32(got, ref) -> bool:
+    g = np.ascontiguousarray(np.asarray(got, np.float32))
+    r = np.ascontiguousarray(np.asarray(ref, np.float64).astype(np.float32))
+    return bool(np.array_equal(g.view(np.uint32), r.view(np.uint32)))

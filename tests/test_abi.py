@@ -1,0 +1,94 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol that
+include/gnn.h declares, and rejects invalid arguments on the host before any
+launch (no GPU is touched: every call here fails validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import graph_neural_network_amd as gnn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "gnn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(gnn_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = gnn.load_library()
+    names = header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(gnn.EXPORTS)
+
+
+def test_status_strings():
+    lib = gnn.load_library()
+    for code, name in gnn.STATUS.items():
+        assert lib.gnn_status_string(code).decode() == name
+
+
+def fake_csr(n_rows=4, n_cols=4, nnz=4, rp=0x1000, ci=0x2000):
+    return gnn._Csr(n_rows, n_cols, nnz, rp, ci, None)
+
+
+def call(fn, *args):
+    lib = gnn.load_library()
+    rc = getattr(lib, fn)(*args)
+    return rc, lib.gnn_last_error().decode()
+
+
+P = ctypes.c_void_p
+INV, UNS, OVF = 1, 2, 5
+
+
+@pytest.mark.parametrize("case", [
+    ("null csr", lambda: call("gnn_spmm", None, P(8), 0, 4, 4, P(8), 4, 0, None, None), INV),
+    ("F=0", lambda: call("gnn_spmm", ctypes.byref(fake_csr()), P(8), 0, 0, 4, P(8), 4, 0, None, None), INV),
+    ("ldx<F", lambda: call("gnn_spmm", ctypes.byref(fake_csr()), P(8), 0, 8, 4, P(8), 8, 0, None, None), INV),
+    ("bad dtype", lambda: call("gnn_spmm", ctypes.byref(fake_csr()), P(8), 7, 4, 4, P(8), 4, 0, None, None), INV),
+    ("bad norm", lambda: call("gnn_spmm", ctypes.byref(fake_csr()), P(8), 0, 4, 4, P(8), 4, 9, None, None), INV),
+    ("null Y", lambda: call("gnn_spmm", ctypes.byref(fake_csr()), P(8), 0, 4, 4, None, 4, 0, None, None), INV),
+    ("nnz>=2^31", lambda: call("gnn_spmm", ctypes.byref(fake_csr(nnz=2**31)), P(8), 0, 4, 4, P(8), 4, 0, None, None), OVF),
+    ("negative rows", lambda: call("gnn_reduce", ctypes.byref(fake_csr(n_rows=-1)), P(8), 0, 4, 4, 0, P(8), 4, None, None, None), INV),
+    ("arg with sum", lambda: call("gnn_reduce", ctypes.byref(fake_csr()), P(8), 0, 4, 4, 0, P(8), 4, P(8), None, None), INV),
+    ("bad op", lambda: call("gnn_reduce", ctypes.byref(fake_csr()), P(8), 0, 4, 4, 11, P(8), 4, None, None, None), INV),
+    ("gatv2 H=0", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 0, 32, ctypes.c_float(0.2), P(16), None, None, None), INV),
+    ("gatv2 too wide", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gatv2 D*2 % 16", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 12, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gt bad mode", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), 5, P(16), None, None, None), INV),
+    ("gt block16 f32", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 0, 8, 64, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
+    ("gt block16 D=48", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2, 48, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
+    ("gt block16 non-square", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr(n_cols=5)), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), 1, P(16), None, None, None), INV),
+    ("gt misaligned", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(18), P(16), P(16), 1, 8, 64, ctypes.c_float(0), 0, P(16), None, None, None), UNS),
+    ("reorder non-square", lambda: call("gnn_reorder", ctypes.byref(fake_csr(n_cols=3)), 0, P(8), None, None, None), INV),
+    ("reorder null perm", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 0, None, None, None, None), INV),
+    ("reorder one output", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 0, P(8), P(8), None, None), INV),
+    ("reorder bad kind", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 4, P(8), None, None, None), INV),
+    ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
+    ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
+                                   ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),
+    ("plan wsb non-square", lambda: call("gnn_plan_create", ctypes.byref(fake_csr(n_cols=9)),
+                                         ctypes.byref(gnn._PlanOpts(0, 0, 0, 1, 0)), None, ctypes.byref(P())), INV),
+    ("stats null", lambda: call("gnn_plan_stats", None, None, 9), INV),
+    ("permute bad F", lambda: call("gnn_permute_rows", P(8), 4, P(8), 0, 0, 4, P(8), 4, None), INV),
+    ("copy negative", lambda: call("gnn_copy_bytes", P(8), P(8), -1, None), INV),
+], ids=lambda c: c[0])
+def test_validation_errors(case):
+    name, fn, want = case
+    rc, msg = fn()
+    assert rc == want, (name, rc, msg)
+    assert msg, "a message is recorded"
+
+
+def test_empty_calls_are_noops():
+    lib = gnn.load_library()
+    empty = gnn._Csr(0, 0, 0, 0x1000, None, None)
+    assert lib.gnn_spmm(ctypes.byref(empty), None, 0, 4, 4, P(8), 4, 0, None, None) == 0
+    assert lib.gnn_copy_bytes(None, None, 0, None) == 0
+    assert lib.gnn_plan_destroy(None) == 0
