@@ -138,7 +138,100 @@ def wl_copy(args):
             "keep": (src, dst)}
 
 
-WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy}
+def _oracle_rows_rate(w, fn, budget_s, label):
+    """Time an oracle function on growing random row samples until it takes
+    about a quarter of the budget (or covers the graph); edges/s."""
+    import oracle
+    rng = np.random.default_rng(0)
+    n = w.n
+    k = 500
+    while True:
+        rows = np.sort(rng.choice(n, size=min(k, n), replace=False)).astype(np.int32)
+        e = int(np.diff(w.row_ptr)[rows].sum())
+        t0 = time.perf_counter()
+        fn(rows)
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or k >= n:
+            break
+        k = min(n, int(k * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+    return {"value": e / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{rows.size} random destination rows ({e} edges) of the same graph, "
+                      f"{label}, fp64, {dt:.1f} s"}
+
+
+def _to_bf16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def wl_gatv2(args):
+    """Fused GATv2: R-MAT 200,000 nodes, 4,000,000 edges + self loops, H = 4, D = 32 bf16."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gatv2_rmat()
+    n, m = w.n, w.nnz
+    H, D = w.params["H"], w.params["D"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    xl, xr = _to_bf16(w.arrays["xl"]), _to_bf16(w.arrays["xr"])
+    att = torch.from_numpy(w.arrays["att"]).cuda()
+    out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    row_b = H * D * 2
+    b = m * (4 + row_b) + n * (4 + row_b + H * D * 4 + H * 4)
+    ops = [Op("gatv2", lambda: gnn.gnn_gatv2_fused(csr, xl, xr, att, 0.2, out=out, lse=lse, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        return _oracle_rows_rate(w, lambda r: oracle.gatv2(w.row_ptr, w.col_idx, w.arrays["xl"], w.arrays["xr"],
+                                                           w.arrays["att"], 0.2, rows=r), budget_s, "GATv2")
+
+    cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)+self-loops", "nodes": n, "edges": m,
+           "heads": H, "head_dim": D, "x_dtype": "bf16", "plan": gnn.gnn_plan_stats(plan)}
+    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 1, 0>",
+            "config": cfg, "dtype": "bf16", "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse)}
+
+
+def wl_gt(args, mode="csr"):
+    """Graph Transformer: cluster graph 512,000 nodes (64-node clusters, p = 0.5, 1% inter) +
+    self loops, H = 8, D = 64 bf16."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gt_cluster()
+    n, m = w.n, w.nnz
+    H, D = w.params["H"], w.params["D"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    t0 = time.perf_counter()
+    plan = gnn.gnn_plan_create(csr, light_max_deg=64, build_wsb=(mode == "block16"))
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    q, k, v = (_to_bf16(w.arrays[x]) for x in ("q", "k", "v"))
+    out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n, H), dtype=torch.float32, device="cuda")
+    row_b = H * D * 2
+    b = m * (4 + 2 * row_b) + n * (4 + row_b + H * D * 4 + H * 4)
+    ops = [Op("gt", lambda: gnn.gnn_gt_fused(csr, q, k, v, 0.0, mode, out=out, lse=lse, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        return _oracle_rows_rate(w, lambda r: oracle.gt(w.row_ptr, w.col_idx, w.arrays["q"], w.arrays["k"],
+                                                        w.arrays["v"], rows=r), budget_s, "Graph Transformer")
+
+    cfg = {"workload": w.name + ("_block16" if mode == "block16" else "_csr"), "graph": "cluster(64, 0.5, 1%)+self-loops",
+           "nodes": n, "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16", "mode": mode,
+           "plan_build_ms": round(plan_ms, 2), "plan": gnn.gnn_plan_stats(plan)}
+    kern = "k_attention<unsigned short, 64, 1, 1>" if mode == "csr" else "k_gt_block16"
+    return {"ops": ops, "dominant": "gt", "kernel": kern, "config": cfg, "dtype": "bf16", "cpu": cpu,
+            "keep": (w, csr, plan, q, k, v, out, lse)}
+
+
+WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
+             "gt_block16": lambda a: wl_gt(a, "block16")}
 
 
 # ---------------------------------------------------------------------------

@@ -1,0 +1,440 @@
+// Fused CSR attention: GATv2 and Graph Transformer forward in one pass over
+// each destination's neighbours, with an online softmax, so that no per-edge
+// logit, weight or message ever reaches memory.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations":
+//   section 2.2 (iii): h_i' = sum_j alpha_ij v_j, alpha = softmax_j(e_ij);
+//     GATv2 e_ij = a^T LeakyReLU(W_l h_i + W_r h_j), v_j = W_r h_j;
+//     Graph Transformer e_ij = q_i . k_j / sqrt(D);
+//   appendix D.2: fused CSR kernels, online softmax with the running
+//     (max, sum) and the accumulator rescaled by exp(m_old - m_new), partial
+//     states of parallel workers merged by rescaling each with
+//     exp(m_w - m_global), logsumexp kept per (node, head).
+//
+// MI355X mapping.  An edge's feature row (all heads) is spread over a slot of
+// LPE lanes, 16 bytes (NV = 1) or 32 bytes (NV = 2) per lane; the lanes of one
+// head reduce the score with xor shuffles.  Config examples: GATv2 H = 4,
+// D = 32 bf16 is a 256-byte row = 16 lanes, four edges per wave instruction;
+// GT H = 8, D = 64 bf16 is a 1-KB row = one full wave per edge for K and one
+// for V.  Each slot keeps its own (m, l, acc) state over U = 4 edges in
+// flight; slots of a wave, waves of a workgroup and chunks of a split row
+// are merged with the same rescaling rule.  Logits live in the log2 domain
+// (log2 e folded into a or into q * scale) so every exponential is exp2.
+//   light rows : one slot per row (rows in natural order, XCD-contiguous)
+//   items      : one workgroup per medium row or per chunk of a heavy row;
+//                chunks of a heavy row leave partial (m, l, acc) states that a
+//                combine kernel merges in chunk order.
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+constexpr int WG = 256;
+constexpr int U = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+enum { K_GATV2 = 0, K_GT = 1 };
+
+struct AttParams {
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const void* q;     // GATv2: x_l [n_rows, H, D]; GT: q
+  const void* k;     // GATv2: x_r [n_cols, H, D]; GT: k
+  const void* v;     // GT: v (GATv2: same as k)
+  const float* att;  // GATv2: a [H, D]
+  float* out;        // [n_rows, H, D]
+  float* lse;        // [n_rows, H] or null
+  const int4* items;
+  float* pacc;       // [n_items, H * D] partial accumulators of split rows
+  float* pml;        // [n_items, 2, H] partial (m, l) of split rows
+  int32_t n_rows;
+  int32_t H, D;
+  int32_t row_elems;  // H * D
+  int32_t row_lanes;  // lanes holding data (H * D / VEL)
+  int32_t lph;        // lanes per head (power of two)
+  int32_t light_max;
+  int32_t n_item_blocks;
+  int32_t n_light_blocks;
+  float slope;        // GATv2 LeakyReLU slope
+  float qscale;       // GT: scale * log2(e)
+};
+
+template <typename T, int N>
+__device__ __forceinline__ void load_row(const T* p, float (&o)[N]);
+
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 8>(const uint16_t* p, float (&o)[8]) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x); o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
+  o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z); o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
+}
+template <>
+__device__ __forceinline__ void load_row<uint16_t, 16>(const uint16_t* p, float (&o)[16]) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  uint4 w = *reinterpret_cast<const uint4*>(p + 8);
+  o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x); o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
+  o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z); o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
+  o[8] = dev::bf16_lo(w.x); o[9] = dev::bf16_hi(w.x); o[10] = dev::bf16_lo(w.y); o[11] = dev::bf16_hi(w.y);
+  o[12] = dev::bf16_lo(w.z); o[13] = dev::bf16_hi(w.z); o[14] = dev::bf16_lo(w.w); o[15] = dev::bf16_hi(w.w);
+}
+template <>
+__device__ __forceinline__ void load_row<float, 4>(const float* p, float (&o)[4]) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void load_row<float, 8>(const float* p, float (&o)[8]) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  float4 w = *reinterpret_cast<const float4*>(p + 4);
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y; o[6] = w.z; o[7] = w.w;
+}
+
+template <int N>
+__device__ __forceinline__ void store_row(float* p, const float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; k += 4)
+    *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+}
+
+// Online-softmax state of one slot lane: running max m (log2 units), running
+// sum l, accumulator acc over this lane's VEL output elements.
+template <int VEL>
+struct Soft {
+  float m, l;
+  float acc[VEL];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) acc[k] = 0.0f;
+  }
+  // merge another state (m2, l2, acc2) into this one
+  __device__ __forceinline__ void merge(float m2, float l2, const float (&a2)[VEL]) {
+    const float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) return;  // both empty
+    const float c1 = exp2f(m - mn), c2 = exp2f(m2 - mn);
+    l = l * c1 + l2 * c2;
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) acc[k] = acc[k] * c1 + a2[k] * c2;
+    m = mn;
+  }
+};
+
+template <int VEL>
+__device__ __forceinline__ void shfl_merge(Soft<VEL>& s, int lane_xor) {
+  float m2 = __shfl_xor(s.m, lane_xor, 64);
+  float l2 = __shfl_xor(s.l, lane_xor, 64);
+  float a2[VEL];
+#pragma unroll
+  for (int k = 0; k < VEL; ++k) a2[k] = __shfl_xor(s.acc[k], lane_xor, 64);
+  s.merge(m2, l2, a2);
+}
+
+// Process edges [eb, ee) of destination `row` for one slot.
+//   qv  : this lane's slice of the destination-side vector (GATv2: x_l,
+//         GT: q * scale * log2 e)
+//   av  : GATv2 attention-vector slice times log2 e (unused for GT)
+template <typename T, int LPE, int VEL, int KIND>
+__device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, int sl, int slot_base,
+                                           bool d_ok, const float (&qv)[VEL], const float (&av)[VEL],
+                                           Soft<VEL>& st) {
+  const T* K = reinterpret_cast<const T*>(p.k) + sl * VEL;
+  const T* V = reinterpret_cast<const T*>(p.v) + sl * VEL;
+  const int64_t ld = p.row_elems;
+  for (int e0 = eb; e0 < ee; e0 += LPE) {
+    const int nb = min(LPE, ee - e0);
+    const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
+    for (int u0 = 0; u0 < nb; u0 += U) {
+      int c[U];
+      float x[U][VEL];
+      float y[U][VEL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = __shfl(my_c, slot_base + u0 + u, 64);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u0 + u < nb && d_ok) {
+          load_row<T, VEL>(K + (int64_t)c[u] * ld, x[u]);
+          if constexpr (KIND == K_GT) load_row<T, VEL>(V + (int64_t)c[u] * ld, y[u]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) {
+            x[u][k] = 0.0f;
+            if constexpr (KIND == K_GT) y[u][k] = 0.0f;
+          }
+        }
+      }
+      float s[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float t = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VEL; ++k) {
+          if constexpr (KIND == K_GATV2) {
+            const float z = qv[k] + x[u][k];
+            t = fmaf(av[k], z > 0.0f ? z : p.slope * z, t);
+          } else {
+            t = fmaf(qv[k], x[u][k], t);
+          }
+        }
+        for (int o = 1; o < p.lph; o <<= 1) t += __shfl_xor(t, o, 64);
+        s[u] = (u0 + u < nb) ? t : -INFINITY;
+      }
+      float mn = st.m;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mn = fmaxf(mn, s[u]);
+      const float corr = exp2f(st.m - mn);
+      st.l *= corr;
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) st.acc[k] *= corr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pu = exp2f(s[u] - mn);
+        st.l += pu;
+#pragma unroll
+        for (int k = 0; k < VEL; ++k)
+          st.acc[k] = fmaf(pu, (KIND == K_GT) ? y[u][k] : x[u][k], st.acc[k]);
+      }
+      st.m = mn;
+    }
+  }
+}
+
+template <int VEL>
+__device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int sl, int head,
+                                            const Soft<VEL>& st) {
+  float o[VEL];
+  const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+#pragma unroll
+  for (int k = 0; k < VEL; ++k) o[k] = st.acc[k] * inv;
+  store_row<VEL>(p.out + row * p.row_elems + sl * VEL, o);
+  if (p.lse && (sl % p.lph) == 0)
+    p.lse[row * p.H + head] = st.l > 0.0f ? st.m * kLn2 + logf(st.l) : -INFINITY;
+}
+
+template <typename T, int LPE, int NV, int KIND>
+__global__ __launch_bounds__(WG) void k_attention(AttParams p) {
+  constexpr int VEL = (16 / (int)sizeof(T)) * NV;  // elements per lane
+  constexpr int SPW = 64 / LPE;
+  constexpr int NWAVE = WG / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int sw = lane / LPE, sl = lane % LPE;
+  const int slot_base = sw * LPE;
+  const bool d_ok = sl < p.row_lanes;
+  const int head = d_ok ? sl / p.lph : 0;
+
+  const int n_item_pad = (p.n_item_blocks + 7) & ~7;
+  const bool is_item = (int)blockIdx.x < n_item_pad;
+  int64_t row;
+  int eb, ee, m_idx = -1, item = -1;
+  if (is_item) {
+    item = (int)dev::xcd_remap(blockIdx.x, n_item_pad);
+    if (item >= p.n_item_blocks) return;
+    const int4 it = p.items[item];
+    row = it.x;
+    m_idx = it.w;
+    // split the item's edges over all slots of the workgroup
+    const int nslots = SPW * NWAVE;
+    const int slot = wave * SPW + sw;
+    const int len = it.z - it.y;
+    const int per = (len + nslots - 1) / nslots;
+    eb = min(it.z, it.y + slot * per);
+    ee = min(it.z, eb + per);
+  } else {
+    const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
+    row = ((int64_t)lb * NWAVE + wave) * SPW + sw;
+    if (row >= p.n_rows) return;
+    eb = p.row_ptr[row];
+    ee = p.row_ptr[row + 1];
+    if (ee - eb > p.light_max) return;  // processed as an item
+  }
+
+  // destination-side slice (and the attention vector for GATv2)
+  float qv[VEL], av[VEL];
+  if (d_ok) {
+    load_row<T, VEL>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + sl * VEL, qv);
+    if constexpr (KIND == K_GATV2) {
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) av[k] = p.att[sl * VEL + k] * kLog2e;
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) qv[k] *= p.qscale;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) qv[k] = av[k] = 0.0f;
+  }
+
+  Soft<VEL> st;
+  st.init();
+  scan_edges<T, LPE, VEL, KIND>(p, eb, ee, sl, slot_base, d_ok, qv, av, st);
+
+  if (!is_item) {
+    if (d_ok) write_final<VEL>(p, row, sl, head, st);
+    return;
+  }
+
+  // merge the slots of each wave, then the waves through LDS
+#pragma unroll
+  for (int o = LPE; o < 64; o <<= 1) shfl_merge<VEL>(st, o);
+  __shared__ float s_m[NWAVE][LPE], s_l[NWAVE][LPE], s_a[NWAVE][LPE][VEL];
+  if (sw == 0) {
+    s_m[wave][sl] = st.m;
+    s_l[wave][sl] = st.l;
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) s_a[wave][sl][k] = st.acc[k];
+  }
+  __syncthreads();
+  if (wave != 0 || sw != 0) return;
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) {
+    float a2[VEL];
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) a2[k] = s_a[w][sl][k];
+    st.merge(s_m[w][sl], s_l[w][sl], a2);
+  }
+  if (!d_ok) return;
+  if (m_idx < 0) {
+    write_final<VEL>(p, row, sl, head, st);
+  } else {
+    store_row<VEL>(p.pacc + (int64_t)item * p.row_elems + sl * VEL, st.acc);
+    if ((sl % p.lph) == 0) {
+      p.pml[((int64_t)item * 2 + 0) * p.H + head] = st.m;
+      p.pml[((int64_t)item * 2 + 1) * p.H + head] = st.l;
+    }
+  }
+}
+
+// Merge the chunk states of each split row in chunk order (same rule).
+__global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* multi) {
+  const int4 mr = multi[blockIdx.x];
+  const int row = mr.x, first = mr.y, cnt = mr.z;
+  for (int t = threadIdx.x; t < p.row_elems; t += blockDim.x) {
+    const int h = t / p.D;
+    float m = -INFINITY, l = 0.0f, a = 0.0f;
+    for (int c = 0; c < cnt; ++c) {
+      const int64_t it = first + c;
+      const float m2 = p.pml[(it * 2 + 0) * p.H + h];
+      const float l2 = p.pml[(it * 2 + 1) * p.H + h];
+      const float a2 = p.pacc[it * p.row_elems + t];
+      const float mn = fmaxf(m, m2);
+      if (mn == -INFINITY) continue;
+      const float c1 = exp2f(m - mn), c2 = exp2f(m2 - mn);
+      l = l * c1 + l2 * c2;
+      a = a * c1 + a2 * c2;
+      m = mn;
+    }
+    p.out[(int64_t)row * p.row_elems + t] = l > 0.0f ? a / l : 0.0f;
+    if (p.lse && (t % p.D) == 0) p.lse[(int64_t)row * p.H + h] = l > 0.0f ? m * kLn2 + logf(l) : -INFINITY;
+  }
+}
+
+template <typename T, int LPE, int NV, int KIND>
+int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
+  constexpr int SPB = (64 / LPE) * (WG / 64);
+  p.n_item_blocks = (int32_t)pl->n_items;
+  p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
+  const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
+  if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
+  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+  GNN_LAUNCH_CHECK("attention");
+  if (pl->n_multi > 0) {
+    hipLaunchKernelGGL(k_att_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
+                       (const int4*)pl->multi);
+    GNN_LAUNCH_CHECK("attention combine");
+  }
+  return GNN_OK;
+}
+
+template <typename T, int KIND>
+int dispatch(gnn_plan* pl, AttParams& p, int lpe, int nv, hipStream_t s) {
+  if (nv == 2) {
+    switch (lpe) {
+      case 8: return launch_att<T, 8, 2, KIND>(pl, p, s);
+      case 16: return launch_att<T, 16, 2, KIND>(pl, p, s);
+      case 32: return launch_att<T, 32, 2, KIND>(pl, p, s);
+      default: return launch_att<T, 64, 2, KIND>(pl, p, s);
+    }
+  }
+  switch (lpe) {
+    case 8: return launch_att<T, 8, 1, KIND>(pl, p, s);
+    case 16: return launch_att<T, 16, 1, KIND>(pl, p, s);
+    case 32: return launch_att<T, 32, 1, KIND>(pl, p, s);
+    default: return launch_att<T, 64, 1, KIND>(pl, p, s);
+  }
+}
+
+int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* lpe, int* nv,
+          hipStream_t s) {
+  const int esz = xt == GNN_BF16 ? 2 : 4;
+  const int rowb = H * D * esz;
+  *nv = rowb > 1024 ? 2 : 1;
+  const int vb = 16 * *nv;  // bytes per lane
+  if ((D * esz) % vb != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "head dimension does not fill whole lane vectors");
+  const int lph = D * esz / vb;
+  if ((lph & (lph - 1)) != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "lanes per head must be a power of two");
+  const int lanes = rowb / vb;
+  int l = 8;
+  while (l < lanes) l <<= 1;
+  if (l > 64) return fail(GNN_ERR_UNSUPPORTED, "row too wide");
+  *lpe = l;
+  p.row_ptr = pl->row_ptr;
+  p.col_idx = pl->col_idx;
+  p.items = pl->items;
+  p.n_rows = pl->n_rows;
+  p.H = H;
+  p.D = D;
+  p.row_elems = H * D;
+  p.row_lanes = lanes;
+  p.lph = lph;
+  p.light_max = pl->light_max;
+  if (pl->n_multi > 0) {
+    void* ws = nullptr;
+    size_t need = (size_t)pl->n_items * (H * D + 2 * H) * 4;
+    GNN_TRY(plan_workspace(pl, need, &ws));
+    p.pacc = (float*)ws;
+    p.pml = p.pacc + (size_t)pl->n_items * H * D;
+  }
+  return GNN_OK;
+}
+
+}  // namespace
+
+int launch_gatv2(gnn_plan* pl, const void* xl, const void* xr, gnn_dtype xt, const float* att,
+                 int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s) {
+  AttParams p{};
+  int lpe = 0, nv = 1;
+  GNN_TRY(setup(pl, p, xt, H, D, &lpe, &nv, s));
+  p.q = xl;
+  p.k = xr;
+  p.v = xr;
+  p.att = att;
+  p.out = out;
+  p.lse = lse;
+  p.slope = slope;
+  if (xt == GNN_BF16) return dispatch<uint16_t, K_GATV2>(pl, p, lpe, nv, s);
+  return dispatch<float, K_GATV2>(pl, p, lpe, nv, s);
+}
+
+int launch_gt_csr(gnn_plan* pl, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
+                  int32_t D, float scale, float* out, float* lse, hipStream_t s) {
+  AttParams p{};
+  int lpe = 0, nv = 1;
+  GNN_TRY(setup(pl, p, xt, H, D, &lpe, &nv, s));
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.qscale = scale * kLog2e;
+  if (xt == GNN_BF16) return dispatch<uint16_t, K_GT>(pl, p, lpe, nv, s);
+  return dispatch<float, K_GT>(pl, p, lpe, nv, s);
+}
+
+}  // namespace gnn

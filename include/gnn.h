@@ -162,8 +162,9 @@ int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, in
  * (row stride H*D); att: device [H, D] float32; out: device [n_rows, H, D]
  * float32; lse: device [n_rows, H] float32 or NULL.  One pass with an online
  * softmax: no per-edge logits, weights or messages are written to memory.
- * Supported: xtype BF16 or F32, H*D*sizeof(xtype) a multiple of 16 bytes and
- * at most 1024 bytes, D*sizeof(xtype) a multiple of 16 bytes.  plan may be
+ * Supported: xtype BF16 or F32, H*D*sizeof(xtype) at most 1024 bytes,
+ * D*sizeof(xtype) a multiple of 16 bytes with D*sizeof(xtype)/16 (lanes per
+ * head) a power of two.  plan may be
  * NULL (it then only selects heavy rows for the split-row variant).
  * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, DEVICE. */
 int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,
@@ -178,8 +179,9 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
  * q: device [n_rows, H, D]; k, v: device [n_cols, H, D]; `xtype` BF16 (or F32
  * in CSR mode); scale <= 0 means 1/sqrt(D); out: device [n_rows, H, D]
  * float32; lse: device [n_rows, H] float32 or NULL.
- * GNN_GT_CSR: streaming online softmax, any supported shape (H*D*sizeof a
- * multiple of 16 bytes, at most 2048 bytes; D*sizeof a multiple of 16 bytes).
+ * GNN_GT_CSR: streaming online softmax; H*D*sizeof(xtype) at most 2048 bytes;
+ * a lane holds 16 bytes of a row (32 bytes when the row exceeds 1024 bytes),
+ * D*sizeof(xtype) must fill a power-of-two number of lanes.
  * GNN_GT_BLOCK16: needs a plan built with build_wsb = 1, square CSR,
  * xtype BF16, D in {32, 64, 128}; dense 16x16 tiles run on bf16 MFMA with the
  * softmax weights rounded to bf16 for the P.V product; the residual edges of
