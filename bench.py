@@ -214,7 +214,16 @@ def wl_gt(args, mode="csr"):
     out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")
     lse = torch.empty((n, H), dtype=torch.float32, device="cuda")
     row_b = H * D * 2
-    b = m * (4 + 2 * row_b) + n * (4 + row_b + H * D * 4 + H * 4)
+    st = gnn.gnn_plan_stats(plan)
+    per_row = n * (4 + row_b + H * D * 4 + H * 4)
+    if mode == "csr":
+        # per edge: column index + one K row + one V row
+        b = m * (4 + 2 * row_b) + per_row
+    else:
+        # per dense 16x16 tile: 16 K rows + 16 V rows + two 48-byte block descriptors;
+        # per residual edge as in CSR; per window two offsets
+        b = (st["wsb_dense_tiles"] * (2 * 16 * row_b + 96) + st["wsb_residual_edges"] * (4 + 2 * row_b)
+             + st["wsb_windows"] * 8 + per_row)
     ops = [Op("gt", lambda: gnn.gnn_gt_fused(csr, q, k, v, 0.0, mode, out=out, lse=lse, plan=plan), m, b)]
 
     def cpu(budget_s):
@@ -224,8 +233,8 @@ def wl_gt(args, mode="csr"):
 
     cfg = {"workload": w.name + ("_block16" if mode == "block16" else "_csr"), "graph": "cluster(64, 0.5, 1%)+self-loops",
            "nodes": n, "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16", "mode": mode,
-           "plan_build_ms": round(plan_ms, 2), "plan": gnn.gnn_plan_stats(plan)}
-    kern = "k_attention<unsigned short, 64, 1, 1>" if mode == "csr" else "k_gt_block16"
+           "plan_build_ms": round(plan_ms, 2), "plan": st}
+    kern = "k_attention<unsigned short, 64, 1, 1>" if mode == "csr" else "k_gt_block16<64>"
     return {"ops": ops, "dominant": "gt", "kernel": kern, "config": cfg, "dtype": "bf16", "cpu": cpu,
             "keep": (w, csr, plan, q, k, v, out, lse)}
 

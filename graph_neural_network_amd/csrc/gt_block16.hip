@@ -1,0 +1,249 @@
+// Graph Transformer forward on 16 x 16 block-sparse tiles with bf16 MFMA.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", appendix D.3 "Tensor Core attention (Graph Transformer) on
+// WSB": per row window and head, the 16-row query block meets one 16-column
+// key/value block per tile: S = Q_win K_blk^T, entries without an edge set to
+// -inf by the tile bitmap, a per-row online softmax (m, l), and
+// acc <- acc * exp(m_old - m_new) + exp(S - m_new) V_blk; finally acc / l and
+// the logsumexp per row.  Every loaded key then serves 16 queries and every
+// query 16 keys.
+//
+// MI355X mapping.  One workgroup (4 waves) per window; wave w handles heads
+// w, w + 4, ...  For a tile the wave computes the transposed scores
+// S^T = K_blk Q_win^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = the
+// window's queries, both loaded straight from memory in operand layout), so
+// that lane l holds S[row l % 16][cols 4 (l / 16) .. +3]: exactly the B-operand
+// layout of v_mfma_f32_16x16x16_bf16 for O^T += V_blk^T P^T.  The value block
+// is transposed through LDS (V rows are dimension-contiguous, the MFMA needs
+// column-contiguous k).  P is rounded to bf16 for that product; l sums the
+// rounded weights.  Edges of tiles too sparse for the matrix cores (the
+// residual CSR of the plan) are then streamed per row into the same (m, l,
+// acc) state, the four lanes of a row splitting the head dimension.
+// Windows are mapped XCD-contiguously so the windows of one locally dense
+// cluster share an L2.
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int NWAVE = 4;
+
+struct B16Params {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* out;
+  float* lse;
+  const int32_t* win_ptr;
+  const int32_t* blk_col;
+  const unsigned long long* blk_bits;
+  const int32_t* tile_ptr;
+  const int32_t* tile_blk;
+  const int32_t* res_ptr;
+  const int32_t* res_col;
+  int32_t n_rows;
+  int32_t n_windows;
+  int32_t H;
+  float scale_log2;  // scale * log2(e)
+};
+
+__device__ __forceinline__ uint16_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int D>
+__global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
+  constexpr int KC = D / 32;   // k-chunks of the score product
+  constexpr int MB = D / 16;   // 16-dim blocks of the output
+  constexpr int LDV = D + 8;   // padded LDS row (bf16 elements)
+  __shared__ uint16_t s_v[NWAVE][16 * LDV];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const int row = w * 16 + r;
+  const bool row_ok = row < p.n_rows;
+  const int t_beg = p.tile_ptr[w], t_end = p.tile_ptr[w + 1];
+  const int b_end = p.win_ptr[w + 1];
+  const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
+  const int64_t ldr = (int64_t)p.H * D;  // elements per node row
+  uint16_t* lv = s_v[wave];
+
+  for (int h = wave; h < p.H; h += NWAVE) {
+    // queries of the window in B-operand layout: lane l holds Q[row][kc*32 + 8g .. +7]
+    s16x8 qb[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      if (row_ok)
+        qb[kc] = *reinterpret_cast<const s16x8*>(p.q + (int64_t)row * ldr + h * D + kc * 32 + 8 * g);
+      else
+        qb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    float m = -INFINITY, lsum = 0.0f;
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int t = t_beg; t < t_end; ++t) {
+      const int blk0 = p.tile_blk[t];
+      const bool has2 = blk0 + 1 < b_end;
+      // this lane's key / value column (A-operand row m = lane % 16)
+      const int cb = r >> 3;
+      const int col = (cb == 1 && !has2) ? 0 : p.blk_col[(blk0 + cb) * 8 + (r & 7)];
+      const uint16_t* krow = p.k + (int64_t)col * ldr + h * D;
+      const uint16_t* vrow = p.v + (int64_t)col * ldr + h * D;
+      s16x8 ka[KC], va[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        ka[kc] = *reinterpret_cast<const s16x8*>(krow + kc * 32 + 8 * g);
+        va[kc] = *reinterpret_cast<const s16x8*>(vrow + kc * 32 + 8 * g);
+      }
+      // occupancy bits of this lane's four (row, col) entries
+      const int ub = g >> 1;
+      const unsigned long long word =
+          (ub == 1 && !has2) ? 0ull : p.blk_bits[(int64_t)(blk0 + ub) * 2 + (r >> 3)];
+      const int base = (r & 7) * 8 + 4 * (g & 1);
+
+      f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kc]),
+                                                     __builtin_bit_cast(bf16x8, qb[kc]), st, 0, 0, 0);
+      float s[4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = ((word >> (base + i)) & 1ull) ? st[i] * p.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, s[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      float corr = 1.0f;
+      uint16_t pb[4];
+      float rs = 0.0f;
+      if (mn != -INFINITY) {
+        corr = exp2f(m - mn);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = f2bf_rne(exp2f(s[i] - mn));
+          rs += bf(pb[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = 0;
+      }
+      rs += __shfl_xor(rs, 16, 64);
+      rs += __shfl_xor(rs, 32, 64);
+      lsum = lsum * corr + rs;
+      m = mn;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] *= corr;
+
+      // value block -> LDS as [col][dim], then read transposed
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        *reinterpret_cast<s16x8*>(lv + r * LDV + kc * 32 + 8 * g) = va[kc];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const s16x4 pt = s16x4{(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s16x4 vt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vt[i] = (short)lv[(4 * g + i) * LDV + mb * 16 + r];
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, acc[mb], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // residual edges of this row: the row's four lanes split the head dims
+    for (int e = res_b; e < res_e; ++e) {
+      const int j = p.res_col[e];
+      const uint16_t* kr = p.k + (int64_t)j * ldr + h * D;
+      float dot = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const s16x8 kv = *reinterpret_cast<const s16x8*>(kr + kc * 32 + 8 * g);
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) dot = fmaf(bf((uint16_t)qb[kc][t2]), bf((uint16_t)kv[t2]), dot);
+      }
+      dot += __shfl_xor(dot, 16, 64);
+      dot += __shfl_xor(dot, 32, 64);
+      const float sc = dot * p.scale_log2;
+      const float mn = fmaxf(m, sc);
+      const float corr = exp2f(m - mn);
+      const float pe = exp2f(sc - mn);
+      lsum = lsum * corr + pe;
+      m = mn;
+      const uint16_t* vr = p.v + (int64_t)j * ldr + h * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const s16x4 vv = *reinterpret_cast<const s16x4*>(vr + mb * 16 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(pe, bf((uint16_t)vv[i]), acc[mb][i] * corr);
+      }
+    }
+
+    if (row_ok) {
+      const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+      float* orow = p.out + (int64_t)row * ldr + h * D;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        *reinterpret_cast<float4*>(orow + mb * 16 + 4 * g) =
+            make_float4(acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
+      if (p.lse && g == 0)
+        p.lse[(int64_t)row * p.H + h] = lsum > 0.0f ? m * kLn2 + logf(lsum) : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+int launch_gt_block16(gnn_plan* pl, const void* q, const void* k, const void* v, int32_t H,
+                      int32_t D, float scale, float* out, float* lse, hipStream_t s) {
+  B16Params p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.out = out;
+  p.lse = lse;
+  p.win_ptr = pl->wsb.win_ptr;
+  p.blk_col = pl->wsb.blk_col;
+  p.blk_bits = (const unsigned long long*)pl->wsb.blk_bits;
+  p.tile_ptr = pl->wsb.tile_ptr;
+  p.tile_blk = pl->wsb.tile_blk;
+  p.res_ptr = pl->wsb.res_ptr;
+  p.res_col = pl->wsb.res_col;
+  p.n_rows = pl->n_rows;
+  p.n_windows = pl->wsb.n_windows;
+  p.H = H;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const dim3 grid((unsigned)p.n_windows), block(NWAVE * 64);
+  switch (D) {
+    case 32: hipLaunchKernelGGL(k_gt_block16<32>, grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL(k_gt_block16<64>, grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL(k_gt_block16<128>, grid, block, 0, s, p); break;
+    default: return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 head dim must be 32, 64 or 128");
+  }
+  GNN_LAUNCH_CHECK("gt block16");
+  return GNN_OK;
+}
+
+}  // namespace gnn

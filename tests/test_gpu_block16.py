@@ -1,0 +1,136 @@
+"""GPU parity of the WSB builder and the block-sparse (MFMA) Graph
+Transformer kernel.
+
+WSB layout (window offsets, block column lists, bitmaps) is integer work and
+must equal the oracle's bit for bit.  The BLOCK16 kernel computes the same
+function as the CSR kernel; its softmax weights are rounded to bf16 for the
+P.V product, so it is held to the attention bar (2e-2 of sum alpha |v|, and
+2e-2 * max(1, |lse|)), with tau = 0 (every tile on the matrix cores), the
+default tau, and tau beyond any tile (everything on the residual CSR loop).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import graph_neural_network_amd as gnn
+import oracle
+from gpu_util import dev_bf16, dev_csr, host, scaled_err
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def check(out, lse, ro, rl, va, tol=TOL, rows=None):
+    if rows is not None:
+        out, lse = out[rows], lse[rows]
+    err = scaled_err(out, ro, va)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse), fin)
+    lerr = float((np.abs(lse[fin] - rl[fin]) / np.maximum(1, np.abs(rl[fin]))).max()) if fin.any() else 0.0
+    assert err <= tol and lerr <= tol, (err, lerr)
+    return err, lerr
+
+
+def export_layout(csr, **opts):
+    plan = gnn.gnn_plan_create(csr, build_wsb=True, **opts)
+    wp, bc, bb = gnn.gnn_plan_wsb_export(plan)
+    return plan, host(wp), host(bc), host(bb).view(np.uint64)
+
+
+@pytest.mark.parametrize("graph", ["golden", "cluster", "rmat", "partial"])
+def test_wsb_layout_matches_oracle(graph):
+    if graph == "golden":
+        lines = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "wsb_hand.txt"))]
+        lines = [l for l in lines if l]
+        n = int([l for l in lines if l[0] == "n"][0][1])
+        src, dst = [], []
+        for l in lines:
+            if l[0] == "row":
+                for s in l[2:]:
+                    src.append(int(s)); dst.append(int(l[1]))
+        rp, ci = gen.from_edges(n, src, dst)
+    elif graph == "cluster":
+        rp, ci = gen.cluster(0x5EED0300, 64 * 40, 64, 0.5, 0.01)
+    elif graph == "rmat":
+        rp, ci = gen.rmat(0x5EED0301, 30000, 300000, self_loops=True)
+    else:
+        rp, ci = gen.rmat(0x5EED0302, 1000 + 7, 9000)     # last window has 15 rows
+    csr = dev_csr(rp, ci)
+    _, wp, bc, bb = export_layout(csr)
+    owp, obc, obb = oracle.wsb_build(rp, ci)
+    assert np.array_equal(wp, owp)
+    assert np.array_equal(bc, obc)
+    assert np.array_equal(bb, obb)
+
+
+def run_b16(rp, ci, q, k, v, tau=0, scale=0.0):
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, build_wsb=True, wsb_min_nnz=tau) if tau >= 0 else \
+        gnn.gnn_plan_create(csr, build_wsb=True)
+    out, lse = gnn.gnn_gt_fused(csr, dev_bf16(q), dev_bf16(k), dev_bf16(v), scale, "block16", plan=plan)
+    return host(out), host(lse), gnn.gnn_plan_stats(plan)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("tau", [1, 32, 10**6])
+def test_gt_block16_cluster(D, tau):
+    H = 8 if D <= 64 else 4
+    rp, ci = gen.cluster(0x5EED0310, 64 * 30, 64, 0.5, 0.01)
+    n = rp.size - 1
+    q, k, v = (gen.gauss_bf16(0x1000 + i, (n, H, D)) for i in range(3))
+    out, lse, st = run_b16(rp, ci, q, k, v, tau)
+    if tau == 1:
+        assert st["wsb_residual_edges"] == 0
+    if tau == 10**6:
+        assert st["wsb_dense_tiles"] == 0 and st["wsb_residual_edges"] == ci.size
+    ro, rl, va = oracle.gt(rp, ci, q, k, v)
+    err, lerr = check(out, lse, ro, rl, va)
+    if tau == 10**6:
+        assert err < 1e-4, "pure residual path computes in fp32"
+
+
+def test_gt_block16_rmat_partial_window_and_empty_rows():
+    # power-law graph (tiles mostly sparse), n not a multiple of 16, empty rows
+    rp, ci = gen.rmat(0x5EED0320, 5003, 60000)
+    n = rp.size - 1
+    assert (np.diff(rp) == 0).any()
+    H, D = 2, 64
+    q, k, v = (gen.gauss_bf16(0x2000 + i, (n, H, D)) for i in range(3))
+    for tau in (1, 32):
+        out, lse, _ = run_b16(rp, ci, q, k, v, tau)
+        ro, rl, va = oracle.gt(rp, ci, q, k, v)
+        check(out, lse, ro, rl, va)
+        empty = np.diff(rp) == 0
+        assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+
+
+def test_gt_block16_constant_values_and_csr_agreement():
+    rp, ci = gen.cluster(0x5EED0330, 64 * 20, 64, 0.5, 0.01, self_loops=True)
+    n = rp.size - 1
+    H, D = 8, 64
+    q, k, v = (gen.gauss_bf16(0x3000 + i, (n, H, D)) for i in range(3))
+    ones = gen.f32_to_bf16(np.ones((n, H, D), np.float32))
+    out, _, _ = run_b16(rp, ci, q, k, ones, 1)
+    np.testing.assert_allclose(out, 1.0, rtol=1e-5)
+    b16, lb16, _ = run_b16(rp, ci, q, k, v, 32)
+    csr = dev_csr(rp, ci)
+    o2, l2 = gnn.gnn_gt_fused(csr, dev_bf16(q), dev_bf16(k), dev_bf16(v), mode="csr")
+    ro, rl, va = oracle.gt(rp, ci, q, k, v)
+    check(b16, lb16, ro, rl, va)
+    check(host(o2), host(l2), ro, rl, va, tol=1e-4)
+
+
+def test_gt_block16_cluster512k_full():
+    w = gen.gt_cluster()
+    rp, ci = w.row_ptr, w.col_idx
+    q, k, v = w.arrays["q"], w.arrays["k"], w.arrays["v"]
+    out, lse, st = run_b16(rp, ci, q, k, v, -1)
+    assert st["wsb_dense_tiles"] > 0
+    rng = np.random.default_rng(9)
+    rows = np.unique(rng.integers(0, rp.size - 1, 3000)).astype(np.int32)
+    ro, rl, va = oracle.gt(rp, ci, q, k, v, rows=rows)
+    check(out, lse, ro, rl, va, rows=rows)
