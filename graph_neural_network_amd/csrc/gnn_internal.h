@@ -126,9 +126,10 @@ int launch_copy(const void* src, void* dst, int64_t n, hipStream_t s);
 // entries, out[n] = total); scratch is allocated and freed stream-ordered.
 int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s);
 
-// Stable LSD radix sort of 64-bit keys by bits [0, nbits); result in `keys`,
-// `tmp` is scratch of n keys.
-int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int nbits, hipStream_t s);
+// Stable LSD radix sort of 64-bit keys by bits [begin_bit, end_bit); result
+// in `keys`, `tmp` is scratch of n keys.
+int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
+                   hipStream_t s);
 
 // Aggregation modes for launch_aggregate
 enum AggMode { AGG_SUM = 0, AGG_MEAN = 1, AGG_MAX = 2, AGG_MIN = 3, AGG_SPMM = 4 };

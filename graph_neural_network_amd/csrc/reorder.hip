@@ -1,0 +1,491 @@
+// Vertex reordering on the GPU: degree sort and reverse Cuthill-McKee, and the
+// relabelled CSR P A P^T.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", section 2.4 and the reordering discussion of section 4:
+// a permutation that places co-accessed vertices close together helps
+// gather-dominated (neighbour-parallel) kernels.  RCM is named in Tang et
+// al., "A High-Throughput Solver for Marginalized Graph Kernels on GPU",
+// section on graph reordering, as the bandwidth-reduction heuristic; its
+// steps are the textbook Cuthill-McKee ones.
+//
+// Degree sort: perm sorts vertices by descending row length, ties by
+// ascending id; one stable radix sort of ((maxdeg - deg) << idbits | id) on
+// the degree bits only.
+//
+// RCM (readings fixed where the pages are silent): symmetrised pattern
+// A u A^T without self loops; delta(v) its degree; every connected component
+// is started at its vertex of smallest (delta, id), components taken in that
+// order; a FIFO breadth-first search appends each popped vertex's unvisited
+// neighbours in increasing (delta, id); the visit order is reversed.
+// Level-synchronous form computed here, which yields exactly that order:
+//   - rank(v) = position of v in the global (delta, id) order; adjacency lists
+//     sorted by rank;
+//   - component label = smallest rank in the component (min-label
+//     propagation with shortcutting);
+//   - all components advance together, one BFS level per step: every
+//     unvisited neighbour of level L is claimed by its earliest parent
+//     (atomicMin of the parent's position in level L) and emitted in the
+//     parent's rank-sorted adjacency order, so level L+1 is grouped by parent
+//     in parent order, as the queue would produce it;
+//   - a stable sort of the concatenated levels by component label gives
+//     (component, level, position) order = the queue order; then reverse.
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+unsigned nb(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+int bits_for(int64_t v) {
+  int b = 1;
+  while ((1ll << b) <= v) ++b;
+  return b;
+}
+
+__device__ __forceinline__ int row_of(const int32_t* row_ptr, int32_t n, int64_t e) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (row_ptr[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void k_max_deg(const int32_t* row_ptr, int32_t n, int32_t* out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int d = i < n ? row_ptr[i + 1] - row_ptr[i] : 0;
+  for (int o = 32; o >= 1; o >>= 1) d = max(d, __shfl_xor(d, o));
+  if ((threadIdx.x & 63) == 0) atomicMax(out, d);
+}
+
+__global__ void k_deg_keys(const int32_t* row_ptr, int32_t n, int32_t maxdeg, int idbits,
+                           uint64_t* keys) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int d = row_ptr[i + 1] - row_ptr[i];
+  keys[i] = ((uint64_t)(maxdeg - d) << idbits) | (uint64_t)i;
+}
+
+__global__ void k_low_bits(const uint64_t* keys, int64_t n, int idbits, int32_t* out) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = (int32_t)(keys[i] & ((1ull << idbits) - 1));
+}
+
+// ---- relabelled CSR ----
+
+__global__ void k_inverse(const int32_t* perm, int32_t n, int32_t* inv) {
+  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < n) inv[perm[p]] = (int32_t)p;
+}
+
+__global__ void k_new_deg(const int32_t* row_ptr, const int32_t* perm, int32_t n, int32_t* deg) {
+  int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p < n) deg[p] = row_ptr[perm[p] + 1] - row_ptr[perm[p]];
+}
+
+// key = (new row << colbits) | new column, for every entry of P A P^T
+__global__ void k_perm_keys(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
+                            const int32_t* inv, const int32_t* new_ptr, int32_t n, int64_t nnz,
+                            int colbits, uint64_t* keys) {
+  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= nnz) return;
+  const int p = row_of(new_ptr, n, q);
+  const int64_t old_e = row_ptr[perm[p]] + (q - new_ptr[p]);
+  keys[q] = ((uint64_t)p << colbits) | (uint32_t)inv[col_idx[old_e]];
+}
+
+// ---- RCM ----
+
+// both directions of every non-loop edge (compacted by a scan of flags)
+__global__ void k_loop_flags(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
+                             int32_t* flag) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= nnz) return;
+  flag[e] = (col_idx[e] != row_of(row_ptr, n, e)) ? 1 : 0;
+}
+
+__global__ void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
+                           const int32_t* flag, const int32_t* pos, int idbits, uint64_t* keys) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= nnz || !flag[e]) return;
+  const uint64_t i = (uint64_t)row_of(row_ptr, n, e), j = (uint64_t)col_idx[e];
+  keys[2 * (int64_t)pos[e]] = (i << idbits) | j;
+  keys[2 * (int64_t)pos[e] + 1] = (j << idbits) | i;
+}
+
+__global__ void k_uniq_flags(const uint64_t* keys, int64_t m, int32_t* flag) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  flag[e] = (e == 0 || keys[e] != keys[e - 1]) ? 1 : 0;
+}
+
+__global__ void k_sym_fill(const uint64_t* keys, const int32_t* flag, const int32_t* pos, int64_t m,
+                           int idbits, int32_t* adj, int32_t* adj_row, int32_t* cnt) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m || !flag[e]) return;
+  const int r = (int)(keys[e] >> idbits);
+  adj[pos[e]] = (int32_t)(keys[e] & ((1ull << idbits) - 1));
+  adj_row[pos[e]] = r;
+  atomicAdd(&cnt[r], 1);
+}
+
+__global__ void k_rank_keys(const int32_t* sym_ptr, int32_t n, int idbits, uint64_t* keys) {
+  int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  keys[v] = ((uint64_t)(sym_ptr[v + 1] - sym_ptr[v]) << idbits) | (uint64_t)v;
+}
+
+__global__ void k_rank(const uint64_t* keys, int32_t n, int idbits, int32_t* order, int32_t* rank) {
+  int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  const int v = (int)(keys[r] & ((1ull << idbits) - 1));
+  order[r] = v;
+  rank[v] = (int32_t)r;
+}
+
+__global__ void k_adj_keys(const int32_t* adj, const int32_t* adj_row, const int32_t* rank, int64_t m,
+                           int idbits, uint64_t* keys) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  keys[e] = ((uint64_t)adj_row[e] << idbits) | (uint64_t)rank[adj[e]];
+}
+
+__global__ void k_adj_from_keys(const uint64_t* keys, const int32_t* order, int64_t m, int idbits,
+                                int32_t* adj) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  adj[e] = order[keys[e] & ((1ull << idbits) - 1)];
+}
+
+// min-label propagation over edges, then shortcutting through the label's vertex
+__global__ void k_label_edges(const int32_t* adj, const int32_t* adj_row, int64_t m, int32_t* label,
+                              int32_t* changed) {
+  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  const int a = adj_row[e], b = adj[e];
+  const int la = label[a], lb = label[b];
+  if (lb < la) {
+    atomicMin(&label[a], lb);
+    *changed = 1;
+  }
+}
+
+__global__ void k_label_jump(const int32_t* order, int32_t n, int32_t* label, int32_t* changed) {
+  int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  const int l = label[v];
+  const int l2 = label[order[l]];
+  if (l2 < l) {
+    atomicMin(&label[v], l2);
+    *changed = 1;
+  }
+}
+
+__global__ void k_start_flags(const int32_t* order, const int32_t* label, int32_t n, int32_t* flag) {
+  int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n) return;
+  flag[r] = (label[order[r]] == (int32_t)r) ? 1 : 0;
+}
+
+__global__ void k_start_fill(const int32_t* order, const int32_t* flag, const int32_t* pos, int32_t n,
+                             int32_t* level, int32_t* visited) {
+  int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= n || !flag[r]) return;
+  const int v = order[r];
+  level[pos[r]] = v;
+  visited[v] = 1;
+}
+
+__global__ void k_claim(const int32_t* front, int32_t f, const int32_t* sym_ptr, const int32_t* adj,
+                        const int32_t* visited, int32_t* claim) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= f) return;
+  const int u = front[k];
+  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
+    const int w = adj[e];
+    if (!visited[w]) atomicMin(&claim[w], (int32_t)k);
+  }
+}
+
+__global__ void k_child_count(const int32_t* front, int32_t f, const int32_t* sym_ptr,
+                              const int32_t* adj, const int32_t* visited, const int32_t* claim,
+                              int32_t* cnt) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= f) return;
+  const int u = front[k];
+  int c = 0;
+  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
+    const int w = adj[e];
+    c += (!visited[w] && claim[w] == (int32_t)k) ? 1 : 0;
+  }
+  cnt[k] = c;
+}
+
+__global__ void k_child_emit(const int32_t* front, int32_t f, const int32_t* sym_ptr,
+                             const int32_t* adj, const int32_t* visited, const int32_t* claim,
+                             const int32_t* off, int32_t* next) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= f) return;
+  const int u = front[k];
+  int o = off[k];
+  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
+    const int w = adj[e];
+    if (!visited[w] && claim[w] == (int32_t)k) next[o++] = w;
+  }
+}
+
+__global__ void k_mark(const int32_t* next, int32_t f, int32_t* visited) {
+  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k < f) visited[next[k]] = 1;
+}
+
+__global__ void k_final_keys(const int32_t* concat, const int32_t* label, int32_t n, int idbits,
+                             uint64_t* keys) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  keys[i] = ((uint64_t)label[concat[i]] << idbits) | (uint64_t)i;
+}
+
+__global__ void k_final_perm(const uint64_t* keys, const int32_t* concat, int32_t n, int idbits,
+                             int32_t* perm) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  perm[n - 1 - i] = concat[keys[i] & ((1ull << idbits) - 1)];
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+
+int degree_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
+  const int32_t n = c->n_rows;
+  int32_t* mx = nullptr;
+  uint64_t *keys = nullptr, *tmp = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&mx, 4, s));
+  GNN_HIP(hipMemsetAsync(mx, 0, 4, s));
+  hipLaunchKernelGGL(k_max_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, n, mx);
+  GNN_LAUNCH_CHECK("max degree");
+  int32_t maxdeg = 0;
+  GNN_HIP(hipMemcpyAsync(&maxdeg, mx, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  const int idbits = bits_for(n);
+  const int dbits = bits_for(maxdeg);
+  if (idbits + dbits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "degree keys exceed 64 bits");
+  GNN_HIP(hipMallocAsync((void**)&keys, (size_t)n * 8, s));
+  GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)n * 8, s));
+  hipLaunchKernelGGL(k_deg_keys, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, n, maxdeg, idbits, keys);
+  GNN_LAUNCH_CHECK("degree keys");
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + dbits, s));
+  hipLaunchKernelGGL(k_low_bits, dim3(nb(n)), dim3(256), 0, s, keys, (int64_t)n, idbits, perm);
+  GNN_LAUNCH_CHECK("degree perm");
+  GNN_HIP(hipFreeAsync(mx, s));
+  GNN_HIP(hipFreeAsync(keys, s));
+  GNN_HIP(hipFreeAsync(tmp, s));
+  return GNN_OK;
+}
+
+int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
+  const int32_t n = c->n_rows;
+  const int64_t nnz = c->nnz;
+  const int idbits = bits_for(n);
+  if (2 * idbits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM keys exceed 64 bits");
+
+  // 1. symmetrised pattern without loops, as sorted unique (row, col) keys
+  int32_t *flag = nullptr, *pos = nullptr;
+  size_t fl = (size_t)std::max<int64_t>(nnz, 1) + 1;
+  GNN_HIP(hipMallocAsync((void**)&flag, fl * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&pos, fl * 4, s));
+  if (nnz > 0) {
+    hipLaunchKernelGGL(k_loop_flags, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag);
+    GNN_LAUNCH_CHECK("rcm loop flags");
+  }
+  GNN_TRY(exclusive_scan_i32(flag, pos, nnz, s));
+  int32_t nl = 0;
+  GNN_HIP(hipMemcpyAsync(&nl, pos + nnz, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  const int64_t m2 = 2 * (int64_t)nl;
+  if (m2 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM: symmetrised pattern too large");
+  uint64_t *keys = nullptr, *tmp = nullptr;
+  const size_t kb = (size_t)std::max<int64_t>(std::max<int64_t>(m2, n), 1) * 8;
+  GNN_HIP(hipMallocAsync((void**)&keys, kb, s));
+  GNN_HIP(hipMallocAsync((void**)&tmp, kb, s));
+  if (nnz > 0) {
+    hipLaunchKernelGGL(k_sym_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag,
+                       pos, idbits, keys);
+    GNN_LAUNCH_CHECK("rcm sym keys");
+  }
+  GNN_HIP(hipFreeAsync(flag, s));
+  GNN_HIP(hipFreeAsync(pos, s));
+  GNN_TRY(radix_sort_u64(keys, tmp, m2, 0, 2 * idbits, s));
+  int32_t *uf = nullptr, *up = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&uf, ((size_t)m2 + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&up, ((size_t)m2 + 1) * 4, s));
+  if (m2 > 0) {
+    hipLaunchKernelGGL(k_uniq_flags, dim3(nb(m2)), dim3(256), 0, s, keys, m2, uf);
+    GNN_LAUNCH_CHECK("rcm unique");
+  }
+  GNN_TRY(exclusive_scan_i32(uf, up, m2, s));
+  int32_t m32 = 0;
+  GNN_HIP(hipMemcpyAsync(&m32, up + m2, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  const int64_t m = m32;  // entries of the symmetrised pattern
+  int32_t *adj = nullptr, *adj_row = nullptr, *cnt = nullptr, *sym_ptr = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&adj, (size_t)std::max<int64_t>(m, 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&adj_row, (size_t)std::max<int64_t>(m, 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&cnt, ((size_t)n + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&sym_ptr, ((size_t)n + 1) * 4, s));
+  GNN_HIP(hipMemsetAsync(cnt, 0, ((size_t)n + 1) * 4, s));
+  if (m2 > 0) {
+    hipLaunchKernelGGL(k_sym_fill, dim3(nb(m2)), dim3(256), 0, s, keys, uf, up, m2, idbits, adj, adj_row, cnt);
+    GNN_LAUNCH_CHECK("rcm sym fill");
+  }
+  GNN_TRY(exclusive_scan_i32(cnt, sym_ptr, n, s));
+  GNN_HIP(hipFreeAsync(uf, s));
+  GNN_HIP(hipFreeAsync(up, s));
+
+  // 2. global (delta, id) order and ranks
+  int32_t *order = nullptr, *rank = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&order, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&rank, (size_t)n * 4, s));
+  hipLaunchKernelGGL(k_rank_keys, dim3(nb(n)), dim3(256), 0, s, sym_ptr, n, idbits, keys);
+  GNN_LAUNCH_CHECK("rcm rank keys");
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + bits_for(m + 1), s));
+  hipLaunchKernelGGL(k_rank, dim3(nb(n)), dim3(256), 0, s, keys, n, idbits, order, rank);
+  GNN_LAUNCH_CHECK("rcm rank");
+
+  // 3. adjacency lists in rank order
+  if (m > 0) {
+    hipLaunchKernelGGL(k_adj_keys, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, m, idbits, keys);
+    GNN_LAUNCH_CHECK("rcm adj keys");
+    GNN_TRY(radix_sort_u64(keys, tmp, m, 0, 2 * idbits, s));
+    hipLaunchKernelGGL(k_adj_from_keys, dim3(nb(m)), dim3(256), 0, s, keys, order, m, idbits, adj);
+    GNN_LAUNCH_CHECK("rcm adj sort");
+  }
+
+  // 4. component labels: smallest rank in the component
+  int32_t *label = nullptr, *changed = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&label, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&changed, 4, s));
+  GNN_HIP(hipMemcpyAsync(label, rank, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+  for (int it = 0;; ++it) {
+    int32_t ch = 0;
+    GNN_HIP(hipMemsetAsync(changed, 0, 4, s));
+    if (m > 0) {
+      hipLaunchKernelGGL(k_label_edges, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, m, label, changed);
+      GNN_LAUNCH_CHECK("rcm labels");
+    }
+    hipLaunchKernelGGL(k_label_jump, dim3(nb(n)), dim3(256), 0, s, order, n, label, changed);
+    GNN_LAUNCH_CHECK("rcm label jump");
+    GNN_HIP(hipMemcpyAsync(&ch, changed, 4, hipMemcpyDeviceToHost, s));
+    GNN_HIP(hipStreamSynchronize(s));
+    if (!ch) break;
+    if (it > n + 2) return fail(GNN_ERR_DEVICE, "RCM: label propagation did not converge");
+  }
+
+  // 5. level-synchronous BFS of all components at once
+  int32_t *concat = nullptr, *visited = nullptr, *claim = nullptr, *ccnt = nullptr, *coff = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&concat, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&visited, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&claim, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&ccnt, ((size_t)n + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&coff, ((size_t)n + 1) * 4, s));
+  GNN_HIP(hipMemsetAsync(visited, 0, (size_t)n * 4, s));
+  hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
+  GNN_LAUNCH_CHECK("rcm claim init");
+  hipLaunchKernelGGL(k_start_flags, dim3(nb(n)), dim3(256), 0, s, order, label, n, ccnt);
+  GNN_LAUNCH_CHECK("rcm starts");
+  GNN_TRY(exclusive_scan_i32(ccnt, coff, n, s));
+  hipLaunchKernelGGL(k_start_fill, dim3(nb(n)), dim3(256), 0, s, order, ccnt, coff, n, concat, visited);
+  GNN_LAUNCH_CHECK("rcm level 0");
+  int32_t f = 0;
+  GNN_HIP(hipMemcpyAsync(&f, coff + n, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  int64_t base = 0;
+  while (f > 0 && base + f < n) {
+    const int32_t* front = concat + base;
+    int32_t* next = concat + base + f;
+    hipLaunchKernelGGL(k_claim, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited, claim);
+    hipLaunchKernelGGL(k_child_count, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited,
+                       claim, ccnt);
+    GNN_LAUNCH_CHECK("rcm level count");
+    GNN_TRY(exclusive_scan_i32(ccnt, coff, f, s));
+    int32_t nf = 0;
+    GNN_HIP(hipMemcpyAsync(&nf, coff + f, 4, hipMemcpyDeviceToHost, s));
+    GNN_HIP(hipStreamSynchronize(s));
+    if (nf < 0 || base + f + nf > n) return fail(GNN_ERR_DEVICE, "RCM: level larger than the graph");
+    if (nf > 0) {
+      hipLaunchKernelGGL(k_child_emit, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited,
+                         claim, coff, next);
+      GNN_LAUNCH_CHECK("rcm level emit");
+      hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, visited);
+      GNN_LAUNCH_CHECK("rcm mark");
+    }
+    base += f;
+    f = nf;
+  }
+  if (base + f != n) return fail(GNN_ERR_DEVICE, "RCM: levels do not cover every vertex");
+
+  // 6. (component, level, position) order by a stable sort on the label; reverse
+  hipLaunchKernelGGL(k_final_keys, dim3(nb(n)), dim3(256), 0, s, concat, label, n, idbits, keys);
+  GNN_LAUNCH_CHECK("rcm final keys");
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, 2 * idbits, s));
+  hipLaunchKernelGGL(k_final_perm, dim3(nb(n)), dim3(256), 0, s, keys, concat, n, idbits, perm);
+  GNN_LAUNCH_CHECK("rcm perm");
+
+  for (void* q : {(void*)keys, (void*)tmp, (void*)adj, (void*)adj_row, (void*)cnt, (void*)sym_ptr,
+                  (void*)order, (void*)rank, (void*)label, (void*)changed, (void*)concat,
+                  (void*)visited, (void*)claim, (void*)ccnt, (void*)coff})
+    GNN_HIP(hipFreeAsync(q, s));
+  return GNN_OK;
+}
+
+int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t* ci_out,
+                hipStream_t s) {
+  const int32_t n = c->n_rows;
+  const int64_t nnz = c->nnz;
+  int32_t *inv = nullptr, *deg = nullptr;
+  GNN_HIP(hipMallocAsync((void**)&inv, (size_t)n * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&deg, (size_t)n * 4, s));
+  hipLaunchKernelGGL(k_inverse, dim3(nb(n)), dim3(256), 0, s, perm, n, inv);
+  hipLaunchKernelGGL(k_new_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, perm, n, deg);
+  GNN_LAUNCH_CHECK("permute degrees");
+  GNN_TRY(exclusive_scan_i32(deg, rp_out, n, s));
+  if (nnz > 0) {
+    const int colbits = bits_for(n);
+    uint64_t *keys = nullptr, *tmp = nullptr;
+    GNN_HIP(hipMallocAsync((void**)&keys, (size_t)nnz * 8, s));
+    GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)nnz * 8, s));
+    hipLaunchKernelGGL(k_perm_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
+                       rp_out, n, nnz, colbits, keys);
+    GNN_LAUNCH_CHECK("permute keys");
+    GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, 2 * colbits, s));
+    hipLaunchKernelGGL(k_low_bits, dim3(nb(nnz)), dim3(256), 0, s, keys, nnz, colbits, ci_out);
+    GNN_LAUNCH_CHECK("permute cols");
+    GNN_HIP(hipFreeAsync(keys, s));
+    GNN_HIP(hipFreeAsync(tmp, s));
+  }
+  GNN_HIP(hipFreeAsync(inv, s));
+  GNN_HIP(hipFreeAsync(deg, s));
+  return GNN_OK;
+}
+
+}  // namespace
+
+int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* rp_out,
+                   int32_t* ci_out, hipStream_t s) {
+  if (kind == GNN_REORDER_DEGREE) GNN_TRY(degree_perm(csr, perm, s));
+  else GNN_TRY(rcm_perm(csr, perm, s));
+  if (rp_out) GNN_TRY(permute_csr(csr, perm, rp_out, ci_out, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  return GNN_OK;
+}
+
+}  // namespace gnn

@@ -76,10 +76,11 @@ __global__ __launch_bounds__(RT) void k_rs_scatter(const uint64_t* keys, uint64_
 
 }  // namespace
 
-// Sorts keys[0..n) by bits [0, nbits) ascending, stably; the result ends up
-// in `keys` (tmp is scratch of the same size).  n < 2^31.
-int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int nbits, hipStream_t s) {
-  if (n <= 1 || nbits <= 0) return GNN_OK;
+// Sorts keys[0..n) by bits [begin_bit, end_bit) ascending, stably; the result
+// ends up in `keys` (tmp is scratch of the same size).  n < 2^31.
+int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
+                   hipStream_t s) {
+  if (n <= 1 || end_bit <= begin_bit) return GNN_OK;
   const int64_t ntiles = (n + RTILE - 1) / RTILE;
   if (ntiles * 256 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "radix sort too large");
   int32_t* hist = nullptr;
@@ -89,7 +90,7 @@ int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int nbits, hipStrea
   uint64_t* src = keys;
   uint64_t* dst = tmp;
   int rc = GNN_OK;
-  for (int shift = 0; shift < nbits && rc == GNN_OK; shift += 8) {
+  for (int shift = begin_bit; shift < end_bit && rc == GNN_OK; shift += 8) {
     hipLaunchKernelGGL(k_rs_hist, dim3((unsigned)ntiles), dim3(RT), 0, s, src, n, shift, hist,
                        (int32_t)ntiles);
     GNN_LAUNCH_CHECK("radix hist");

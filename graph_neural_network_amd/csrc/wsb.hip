@@ -210,7 +210,7 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
   hipLaunchKernelGGL(k_wsb_keys, dim3(nblk(nnz)), dim3(256), 0, s, p->row_ptr, p->col_idx, n, nnz,
                      colbits, keys);
   GNN_LAUNCH_CHECK("wsb keys");
-  GNN_TRY(radix_sort_u64(keys, tmp, nnz, colbits + winbits, s));
+  GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, colbits + winbits, s));
   hipLaunchKernelGGL(k_wsb_flags, dim3(nblk(nnz)), dim3(256), 0, s, keys, nnz, flag);
   GNN_LAUNCH_CHECK("wsb flags");
   GNN_TRY(exclusive_scan_i32(flag, uidx, nnz, s));

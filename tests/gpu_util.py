@@ -24,7 +24,7 @@ def dev_bf16(u16: np.ndarray) -> torch.Tensor:
 def dev_csr(rp, ci, n_cols=None, edge_val=None) -> gnn.Csr:
     ev = None if edge_val is None else dev(edge_val.astype(np.float32))
     return gnn.Csr(dev(rp.astype(np.int32)), dev(ci.astype(np.int32)) if ci.size else
-                   torch.zeros(1, dtype=torch.int32, device="cuda"), n_cols=n_cols, edge_val=ev)
+                   torch.zeros(0, dtype=torch.int32, device="cuda"), n_cols=n_cols, edge_val=ev)
 
 
 def host(t: torch.Tensor) -> np.ndarray:
