@@ -239,7 +239,88 @@ def wl_gt(args, mode="csr"):
             "keep": (w, csr, plan, q, k, v, out, lse)}
 
 
+def wl_spmm_large(args):
+    """SpMM A.X on R-MAT 16,000,000 nodes / 256,000,000 edges, X 16,000,000 x 256 bf16, fp32 out;
+    one step = the product in the original (randomly relabelled) order, after a degree sort and
+    after RCM.  Reordering (permutation, relabelled CSR, permuted X) is preprocessing, timed
+    apart and reported in the config."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    t0 = time.perf_counter()
+    w = gen.spmm_rmat_large()
+    gen_s = time.perf_counter() - t0
+    n, m, F = w.n, w.nnz, w.params["F"]
+    X = _to_bf16(w.arrays["X"])
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    Y = torch.empty((n, F), dtype=torch.float32, device="cuda")
+    variants = {"original": (csr, X, gnn.gnn_plan_create(csr))}
+    reorder_ms = {}
+    for kind in ("degree", "rcm"):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        perm, rp2, ci2 = gnn.gnn_reorder(csr, kind)
+        X2 = gnn.gnn_permute_rows(perm, X)
+        torch.cuda.synchronize()
+        reorder_ms[kind] = round((time.perf_counter() - t0) * 1e3, 1)
+        c2 = gnn.Csr(rp2, ci2)
+        variants[kind] = (c2, X2, gnn.gnn_plan_create(c2))
+    b = m * (4 + F * 2) + n * (4 + F * 4)
+    ops = [Op(k, (lambda c=c, x=x, pl=pl: gnn.gnn_spmm(c, x, "none", Y=Y, plan=pl)), m, b)
+           for k, (c, x, pl) in variants.items()]
+
+    def cpu(budget_s):
+        import oracle
+        return _oracle_rows_rate(w, lambda r: oracle.spmm(w.row_ptr, w.col_idx, w.arrays["X"], "none", rows=r,
+                                                          x_is_bf16=True, want_abs=False),
+                                 budget_s, "SpMM (bf16 X, original order)")
+
+    cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m, "F": F,
+           "x_dtype": "bf16", "orders": list(variants), "reorder_ms": reorder_ms,
+           "input_generation_s": round(gen_s, 1),
+           "plan": gnn.gnn_plan_stats(variants["original"][2])}
+    return {"ops": ops, "dominant": "original", "kernel": "k_aggregate<unsigned short, 32, 8, 0, false>",
+            "config": cfg, "dtype": "bf16", "cpu": cpu, "keep": (w, X, csr, Y, variants)}
+
+
+def wl_gcn_small(args):
+    """GCN aggregation D^-1/2 (A+I) D^-1/2 X on Erdos-Renyi 2,000 nodes / 8,000 undirected pairs
+    + self loops, X 2,000 x 64 float32 (launch-bound: the whole input fits one L2)."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gcn_small()
+    n, m, F = w.n, w.nnz, w.params["F"]
+    X = torch.from_numpy(w.arrays["X"]).cuda()
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    Y = torch.empty((n, F), dtype=torch.float32, device="cuda")
+    b = m * (4 + 4 + F * 4) + n * (4 + F * 4)
+    ops = [Op("gcn", lambda: gnn.gnn_spmm(csr, X, "both", Y=Y, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(budget_s, 2.0):
+            oracle.spmm(w.row_ptr, w.col_idx, w.arrays["X"], "both", want_abs=False)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": m / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"whole graph, {reps} repetitions, fp64"}
+
+    cfg = {"workload": w.name, "graph": "erdos-renyi G(2000, 8000) symmetric + self-loops", "nodes": n,
+           "edges": m, "F": F, "x_dtype": "f32", "norm": "both"}
+    return {"ops": ops, "dominant": "gcn", "kernel": "k_aggregate<float, 16, 4, 0, false>", "config": cfg,
+            "dtype": "f32", "cpu": cpu, "keep": (w, X, csr, plan, Y)}
+
+
 WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
+             "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
              "gt_block16": lambda a: wl_gt(a, "block16")}
 
 

@@ -364,7 +364,8 @@ int gen_permutation(uint64_t seed, int32_t n, int32_t* perm) {
   return 0;
 }
 
-/* R-MAT.  Attempt t draws `scale` uniforms at counters t*64 + level. */
+/* R-MAT.  Attempt t draws its quadrant choices from counters t*16 + l/3:
+ * each 64-bit word gives three 21-bit uniforms, one per recursion level. */
 int gen_rmat(uint64_t seed, int32_t n, int64_t m, double a, double b, double c, int relabel,
              int add_loops, gen_graph* out) {
   if (n <= 1 || m < 0 || m > (int64_t)n * (n - 1)) return -3;
@@ -395,8 +396,11 @@ int gen_rmat(uint64_t seed, int32_t n, int64_t m, double a, double b, double c, 
     for (int64_t k = 0; k < batch; ++k) {
       uint64_t t = t0 + (uint64_t)k;
       int64_t u = 0, v = 0;
+      uint64_t word = 0;
       for (int32_t l = 0; l < scale; ++l) {
-        double r = u01(seed, t * 64 + (uint64_t)l);
+        /* three levels per 64-bit draw, 21 random bits (resolution 2^-21) each */
+        if (l % 3 == 0) word = gen_draw(seed, t * 16 + (uint64_t)(l / 3));
+        double r = (double)((word >> (21 * (l % 3))) & 0x1FFFFF) * (1.0 / 2097152.0);
         int64_t bit = (int64_t)1 << (scale - 1 - l);
         if (r < a) {
         } else if (r < ab) {
