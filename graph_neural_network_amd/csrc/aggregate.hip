@@ -86,24 +86,33 @@ __device__ __forceinline__ void loadv<uint16_t, 1>(const uint16_t* p, float (&o)
   o[0] = __uint_as_float((uint32_t)(*p) << 16);
 }
 
+// Outputs and column indices are touched once: non-temporal accesses keep
+// them from displacing the gathered feature rows in L2 / the MALL.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
 template <int VE>
 __device__ __forceinline__ void storev(float* p, const float (&v)[VE]) {
   if constexpr (VE == 1) {
-    *p = v[0];
+    __builtin_nontemporal_store(v[0], p);
   } else {
 #pragma unroll
-    for (int k = 0; k < VE; k += 4)
-      *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+    for (int k = 0; k < VE; k += 4) {
+      f32x4_t t = {v[k], v[k + 1], v[k + 2], v[k + 3]};
+      __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p + k));
+    }
   }
 }
 template <int VE>
 __device__ __forceinline__ void storei(int32_t* p, const int (&v)[VE]) {
   if constexpr (VE == 1) {
-    *p = v[0];
+    __builtin_nontemporal_store(v[0], p);
   } else {
 #pragma unroll
-    for (int k = 0; k < VE; k += 4)
-      *reinterpret_cast<int4*>(p + k) = make_int4(v[k], v[k + 1], v[k + 2], v[k + 3]);
+    for (int k = 0; k < VE; k += 4) {
+      i32x4_t t = {v[k], v[k + 1], v[k + 2], v[k + 3]};
+      __builtin_nontemporal_store(t, reinterpret_cast<i32x4_t*>(p + k));
+    }
   }
 }
 
@@ -111,50 +120,52 @@ __device__ __forceinline__ void storei(int32_t* p, const int (&v)[VE]) {
 // per-lane reduction state
 // ---------------------------------------------------------------------------
 
+// SUM keeps float accumulators.  MAX / MIN keep, per element, one 64-bit
+// word (order_key << 32) | t with t = 0xFFFFFFFF - source (MAX) or source
+// (MIN): one unsigned 64-bit compare then picks the larger (smaller) value
+// and, on equal values, the smaller source index; without an index output
+// the 32-bit key alone is kept.
 template <int KIND, int VE, bool ARG>
 struct State {
-  // SUM: acc; MAX / MIN: order keys (+ source index)
   float acc[VE];
   uint32_t key[VE];
-  int idx[VE];
+  unsigned long long pk[VE];
+
+  static constexpr unsigned long long kInit = (KIND == K_MIN) ? ~0ull : 0ull;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       acc[v] = 0.0f;
       key[v] = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
-      idx[v] = 0x7FFFFFFF;
+      pk[v] = kInit;
     }
   }
+  __device__ __forceinline__ static uint32_t tie(int j) {
+    return (KIND == K_MAX) ? ~(uint32_t)j : (uint32_t)j;
+  }
   __device__ __forceinline__ void add(const float (&x)[VE], float w, int j) {
+    const uint32_t t = tie(j);
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       if constexpr (KIND == K_SUM) {
         acc[v] = fmaf(w, x[v], acc[v]);
+      } else if constexpr (ARG) {
+        const unsigned long long c = ((unsigned long long)dev::order_key(x[v]) << 32) | t;
+        pk[v] = (KIND == K_MAX) ? (c > pk[v] ? c : pk[v]) : (c < pk[v] ? c : pk[v]);
       } else {
-        uint32_t k = dev::order_key(x[v]);
-        bool better = (KIND == K_MAX) ? (k > key[v]) : (k < key[v]);
-        if constexpr (ARG) better = better || (k == key[v] && j < idx[v]);
-        if (better) {
-          key[v] = k;
-          if constexpr (ARG) idx[v] = j;
-        }
+        const uint32_t k = dev::order_key(x[v]);
+        key[v] = (KIND == K_MAX) ? max(key[v], k) : min(key[v], k);
       }
     }
   }
-  // merge another state (used for LDS merges in slot order)
-  __device__ __forceinline__ static void merge1(float& a, uint32_t& k, int& i, float a2, uint32_t k2,
-                                                int i2) {
-    if constexpr (KIND == K_SUM) {
-      a += a2;
-    } else {
-      bool better = (KIND == K_MAX) ? (k2 > k) : (k2 < k);
-      if constexpr (ARG) better = better || (k2 == k && i2 < i);
-      if (better) {
-        k = k2;
-        i = i2;
-      }
-    }
+  // value and source index of a packed word / key
+  __device__ __forceinline__ float value(int v) const {
+    return dev::key_to_float(ARG ? (uint32_t)(pk[v] >> 32) : key[v]);
+  }
+  __device__ __forceinline__ int index(int v) const {
+    const uint32_t lo = (uint32_t)pk[v];
+    return (int)((KIND == K_MAX) ? ~lo : lo);
   }
 };
 
@@ -186,7 +197,7 @@ __device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, i
     int my_c = 0;
     float my_w = 1.0f;
     if (sl < nb) {
-      my_c = p.col_idx[my_e];
+      my_c = __builtin_nontemporal_load(p.col_idx + my_e);
       if (KIND == K_SUM && p.weighted) my_w = edge_weight(p, my_e, my_c);
     }
     for (int u0 = 0; u0 < nb; u0 += U) {
@@ -218,8 +229,8 @@ __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg,
     if constexpr (KIND == K_SUM) {
       out[v] = row_factor(p, st.acc[v], deg);
     } else {
-      out[v] = deg > 0 ? dev::key_to_float(st.key[v]) : 0.0f;
-      ai[v] = deg > 0 ? st.idx[v] : -1;
+      out[v] = deg > 0 ? st.value(v) : 0.0f;
+      if constexpr (ARG) ai[v] = deg > 0 ? st.index(v) : -1;
     }
   }
   storev<VE>(p.Y + (int64_t)row * p.ldy + f0, out);
@@ -258,15 +269,16 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
     st.init();
     scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
 
+    // merge the slots in LDS, in slot order
     __shared__ float s_acc[(KIND == K_SUM) ? SPB * FT : 1];
-    __shared__ uint32_t s_key[(KIND != K_SUM) ? SPB * FT : 1];
-    __shared__ int s_idx[(KIND != K_SUM && ARG) ? SPB * FT : 1];
+    __shared__ uint32_t s_key[(KIND != K_SUM && !ARG) ? SPB * FT : 1];
+    __shared__ unsigned long long s_pk[(KIND != K_SUM && ARG) ? SPB * FT : 1];
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       const int t = sl * VE + v;
       if constexpr (KIND == K_SUM) s_acc[slot * FT + t] = st.acc[v];
+      else if constexpr (ARG) s_pk[slot * FT + t] = st.pk[v];
       else s_key[slot * FT + t] = st.key[v];
-      if constexpr (KIND != K_SUM && ARG) s_idx[slot * FT + t] = st.idx[v];
     }
     __syncthreads();
     for (int t = threadIdx.x; t < FT; t += WG) {
@@ -274,33 +286,33 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
       if (f >= p.F) continue;
       float a = 0.0f;
       uint32_t k = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
-      int ix = 0x7FFFFFFF;
+      unsigned long long w = State<KIND, VE, ARG>::kInit;
       for (int s2 = 0; s2 < SPB; ++s2) {
-        float a2 = 0.0f;
-        uint32_t k2 = 0;
-        int i2 = 0x7FFFFFFF;
-        if constexpr (KIND == K_SUM) a2 = s_acc[s2 * FT + t];
-        else k2 = s_key[s2 * FT + t];
-        if constexpr (KIND != K_SUM && ARG) i2 = s_idx[s2 * FT + t];
-        State<KIND, VE, ARG>::merge1(a, k, ix, a2, k2, i2);
+        if constexpr (KIND == K_SUM) {
+          a += s_acc[s2 * FT + t];
+        } else if constexpr (ARG) {
+          const unsigned long long c = s_pk[s2 * FT + t];
+          w = (KIND == K_MAX) ? (c > w ? c : w) : (c < w ? c : w);
+        } else {
+          const uint32_t c = s_key[s2 * FT + t];
+          k = (KIND == K_MAX) ? max(k, c) : min(k, c);
+        }
       }
+      if constexpr (KIND != K_SUM && !ARG) w = ((unsigned long long)k << 32) | State<KIND, VE, ARG>::tie(0);
       if (m < 0) {
         const int deg = len;  // single item covers the whole row
         if constexpr (KIND == K_SUM) {
-          p.Y[(int64_t)row * p.ldy + f] = row_factor(p, a, deg);
+          __builtin_nontemporal_store(row_factor(p, a, deg), p.Y + (int64_t)row * p.ldy + f);
         } else {
-          p.Y[(int64_t)row * p.ldy + f] = dev::key_to_float(k);
-          if constexpr (ARG) p.arg[(int64_t)row * p.F + f] = ix;
+          const uint32_t lo = (uint32_t)w;
+          __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Y + (int64_t)row * p.ldy + f);
+          if constexpr (ARG)
+            __builtin_nontemporal_store((int)((KIND == K_MAX) ? ~lo : lo), p.arg + (int64_t)row * p.F + f);
         }
       } else {
         if constexpr (KIND == K_SUM) {
           p.partial[(int64_t)lid * p.F + f] = a;
         } else {
-          unsigned long long w;
-          if constexpr (KIND == K_MAX)
-            w = ((unsigned long long)k << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)ix);
-          else
-            w = ((unsigned long long)k << 32) | (unsigned long long)(uint32_t)ix;
           unsigned long long* dst = p.packed + (int64_t)m * p.F + f;
           if constexpr (KIND == K_MAX) atomicMax(dst, w);
           else atomicMin(dst, w);
