@@ -9,8 +9,10 @@
 // the logsumexp per row.  Every loaded key then serves 16 queries and every
 // query 16 keys.
 //
-// MI355X mapping.  One workgroup (4 waves) per window; wave w handles heads
-// w, w + 4, ...  For a tile the wave computes the transposed scores
+// MI355X mapping.  One workgroup of two waves per window; wave w handles
+// heads w, w + 2, ...  The window's tile metadata (columns, bitmaps) is staged
+// in LDS once, and each wave keeps the next tile's K / V loads in flight
+// while it computes the current one.  For a tile the wave computes the transposed scores
 // S^T = K_blk Q_win^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = the
 // window's queries, both loaded straight from memory in operand layout), so
 // that lane l holds S[row l % 16][cols 4 (l / 16) .. +3]: exactly the B-operand
@@ -29,11 +31,11 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(short)))) short s16x2;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int NWAVE = 4;
 
 struct B16Params {
   const uint16_t* q;
@@ -62,12 +64,29 @@ __device__ __forceinline__ uint16_t f2bf_rne(float f) {
 
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-template <int D>
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// dot of 8 bf16 pairs on v_dot2_f32_bf16
+__device__ __forceinline__ float dot8(const s16x8& a, const s16x8& b, float acc) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const s16x2 x = {a[2 * t], a[2 * t + 1]}, y = {b[2 * t], b[2 * t + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y),
+                                          acc, false);
+  }
+  return acc;
+}
+
+constexpr int MAXT = 32;  // tiles of a window staged in LDS (larger windows read metadata directly)
+
+template <int D, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
   constexpr int KC = D / 32;   // k-chunks of the score product
   constexpr int MB = D / 16;   // 16-dim blocks of the output
   constexpr int LDV = D + 8;   // padded LDS row (bf16 elements)
   __shared__ uint16_t s_v[NWAVE][16 * LDV];
+  __shared__ int32_t s_col[MAXT][16];                // the 16 columns of each tile
+  __shared__ unsigned long long s_bits[MAXT][4];     // block 0 words 0-1, block 1 words 0-1
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -76,9 +95,38 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
   const bool row_ok = row < p.n_rows;
   const int t_beg = p.tile_ptr[w], t_end = p.tile_ptr[w + 1];
   const int b_end = p.win_ptr[w + 1];
+  const int nt = t_end - t_beg;
+  const bool staged = nt <= MAXT;
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;  // elements per node row
   uint16_t* lv = s_v[wave];
+
+  // tile metadata of the window, one cooperative pass
+  if (staged) {
+    for (int i = threadIdx.x; i < nt * 16; i += NWAVE * 64) {
+      const int t = i >> 4, c = i & 15;
+      const int blk = p.tile_blk[t_beg + t] + (c >> 3);
+      s_col[t][c] = ((c >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+    }
+    for (int i = threadIdx.x; i < nt * 4; i += NWAVE * 64) {
+      const int t = i >> 2, q = i & 3;
+      const int blk = p.tile_blk[t_beg + t] + (q >> 1);
+      s_bits[t][q] = ((q >> 1) == 1 && blk >= b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (q & 1)];
+    }
+  }
+  __syncthreads();
+
+  auto tile_col = [&](int t) -> int {
+    if (staged) return s_col[t - t_beg][r];
+    const int blk = p.tile_blk[t] + (r >> 3);
+    return ((r >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (r & 7)];
+  };
+  auto tile_word = [&](int t) -> unsigned long long {
+    const int ub = g >> 1;  // which 16x8 block holds this lane's four columns
+    if (staged) return s_bits[t - t_beg][ub * 2 + (r >> 3)];
+    const int blk = p.tile_blk[t] + ub;
+    return (ub == 1 && blk >= b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+  };
 
   for (int h = wave; h < p.H; h += NWAVE) {
     // queries of the window in B-operand layout: lane l holds Q[row][kc*32 + 8g .. +7]
@@ -95,26 +143,20 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int t = t_beg; t < t_end; ++t) {
-      const int blk0 = p.tile_blk[t];
-      const bool has2 = blk0 + 1 < b_end;
-      // this lane's key / value column (A-operand row m = lane % 16)
-      const int cb = r >> 3;
-      const int col = (cb == 1 && !has2) ? 0 : p.blk_col[(blk0 + cb) * 8 + (r & 7)];
+    auto load_kv = [&](int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
+      const int col = tile_col(t);
       const uint16_t* krow = p.k + (int64_t)col * ldr + h * D;
       const uint16_t* vrow = p.v + (int64_t)col * ldr + h * D;
-      s16x8 ka[KC], va[KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         ka[kc] = *reinterpret_cast<const s16x8*>(krow + kc * 32 + 8 * g);
         va[kc] = *reinterpret_cast<const s16x8*>(vrow + kc * 32 + 8 * g);
       }
-      // occupancy bits of this lane's four (row, col) entries
-      const int ub = g >> 1;
-      const unsigned long long word =
-          (ub == 1 && !has2) ? 0ull : p.blk_bits[(int64_t)(blk0 + ub) * 2 + (r >> 3)];
-      const int base = (r & 7) * 8 + 4 * (g & 1);
+    };
 
+    auto process = [&](int t, const s16x8 (&ka)[KC], const s16x8 (&va)[KC]) {
+      const unsigned long long word = tile_word(t);
+      const int base = (r & 7) * 8 + 4 * (g & 1);
       f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
@@ -171,19 +213,36 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    };
+
+    // two-deep pipeline: the next tile's K / V are in flight while one computes
+    s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
+    if (t_beg < t_end) load_kv(t_beg, kA, vA);
+    for (int t = t_beg; t < t_end; t += 2) {
+      if (t + 1 < t_end) load_kv(t + 1, kB, vB);
+      process(t, kA, vA);
+      if (t + 1 < t_end) {
+        if (t + 2 < t_end) load_kv(t + 2, kA, vA);
+        process(t + 1, kB, vB);
+      }
     }
 
     // residual edges of this row: the row's four lanes split the head dims
+    int j_next = (res_b < res_e) ? p.res_col[res_b] : 0;
     for (int e = res_b; e < res_e; ++e) {
-      const int j = p.res_col[e];
+      const int j = j_next;
+      if (e + 1 < res_e) j_next = p.res_col[e + 1];
       const uint16_t* kr = p.k + (int64_t)j * ldr + h * D;
+      const uint16_t* vr = p.v + (int64_t)j * ldr + h * D;
+      s16x8 kv[KC];
+      s16x4 vv[MB];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kv[kc] = *reinterpret_cast<const s16x8*>(kr + kc * 32 + 8 * g);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) vv[mb] = *reinterpret_cast<const s16x4*>(vr + mb * 16 + 4 * g);
       float dot = 0.0f;
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const s16x8 kv = *reinterpret_cast<const s16x8*>(kr + kc * 32 + 8 * g);
-#pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) dot = fmaf(bf((uint16_t)qb[kc][t2]), bf((uint16_t)kv[t2]), dot);
-      }
+      for (int kc = 0; kc < KC; ++kc) dot = dot8(qb[kc], kv[kc], dot);
       dot += __shfl_xor(dot, 16, 64);
       dot += __shfl_xor(dot, 32, 64);
       const float sc = dot * p.scale_log2;
@@ -192,13 +251,10 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
       const float pe = exp2f(sc - mn);
       lsum = lsum * corr + pe;
       m = mn;
-      const uint16_t* vr = p.v + (int64_t)j * ldr + h * D;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const s16x4 vv = *reinterpret_cast<const s16x4*>(vr + mb * 16 + 4 * g);
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(pe, bf((uint16_t)vv[i]), acc[mb][i] * corr);
-      }
+        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(pe, bf((uint16_t)vv[mb][i]), acc[mb][i] * corr);
     }
 
     if (row_ok) {
@@ -235,13 +291,15 @@ int launch_gt_block16(gnn_plan* pl, const void* q, const void* k, const void* v,
   p.n_windows = pl->wsb.n_windows;
   p.H = H;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)p.n_windows), block(NWAVE * 64);
-  switch (D) {
-    case 32: hipLaunchKernelGGL(k_gt_block16<32>, grid, block, 0, s, p); break;
-    case 64: hipLaunchKernelGGL(k_gt_block16<64>, grid, block, 0, s, p); break;
-    case 128: hipLaunchKernelGGL(k_gt_block16<128>, grid, block, 0, s, p); break;
-    default: return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 head dim must be 32, 64 or 128");
-  }
+  // two waves per window, each looping over half of the heads: the window's
+  // tile metadata is staged once per workgroup and amortised over the heads
+  const dim3 grid((unsigned)p.n_windows);
+#define GNN_B16(DD) hipLaunchKernelGGL((k_gt_block16<DD, 2>), grid, dim3(2 * 64), 0, s, p)
+  if (D == 32) GNN_B16(32);
+  else if (D == 64) GNN_B16(64);
+  else if (D == 128) GNN_B16(128);
+  else return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 head dim must be 32, 64 or 128");
+#undef GNN_B16
   GNN_LAUNCH_CHECK("gt block16");
   return GNN_OK;
 }
