@@ -82,13 +82,20 @@ def wl_reduce_f128(args):
     plan_ms = (time.perf_counter() - t0) * 1e3
     Y = {op: torch.empty((n, F), dtype=torch.float32, device="cuda") for op in ("sum", "mean", "max", "min")}
     A = {op: torch.empty((n, F), dtype=torch.int32, device="cuda") for op in ("max", "min")}
+    outs = dict(Y)
+    outs.update({"arg" + k: v for k, v in A.items()})
     row_b = F * 4
-    ops = []
+    # one step: sum, mean, max + index and min + index of every row, computed
+    # in one pass (gnn_reduce_multi); per edge 4 B index + one feature row,
+    # per row 4 B pointer + four value rows + two index rows
+    b = m * (4 + row_b) + n * (4 + 6 * row_b)
+    ops = [Op("multi", lambda: gnn.gnn_reduce_multi(csr, X, out=outs, plan=plan), 4 * m, b)]
+    # the same four results as separate launches, timed apart for reference
+    separate = []
     for op in ("sum", "mean", "max", "min"):
         out_b = row_b + (F * 4 if op in A else 0)
-        b = m * (4 + row_b) + n * (4 + out_b)
-        ops.append(Op(op, (lambda op=op: gnn.gnn_reduce(csr, X, op, Y=Y[op], arg=A.get(op), plan=plan)),
-                      m, b))
+        separate.append(Op(op, (lambda op=op: gnn.gnn_reduce(csr, X, op, Y=Y[op], arg=A.get(op), plan=plan)),
+                           m, m * (4 + row_b) + n * (4 + out_b)))
 
     def cpu_sample(budget_s):
         import oracle
@@ -114,9 +121,11 @@ def wl_reduce_f128(args):
     stats = gnn.gnn_plan_stats(plan)
     cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
            "F": F, "x_dtype": "f32", "ops": ["sum", "mean", "max+arg", "min+arg"],
+           "step": "one fused pass (gnn_reduce_multi); value counts 4 aggregations x edges",
            "plan_build_ms": round(plan_ms, 2), "plan": stats}
-    return {"ops": ops, "dominant": "sum", "kernel": "k_aggregate<float, 32, 4, 0, false>",
-            "config": cfg, "dtype": "f32", "cpu": cpu_sample, "keep": (w, X, csr, plan, Y, A)}
+    return {"ops": ops, "dominant": "multi", "kernel": "k_aggregate<float, 32, 4, 3, true>",
+            "config": cfg, "dtype": "f32", "cpu": cpu_sample, "separate": separate,
+            "keep": (w, X, csr, plan, Y, A, outs)}
 
 
 def wl_copy(args):
@@ -366,6 +375,20 @@ def main():
     wall = time.perf_counter() - t0
 
     per_op_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    separate_ms = None
+    if w.get("separate"):
+        separate_ms = {}
+        for o in w["separate"]:
+            for _ in range(2):
+                o.fn()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                o.fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            separate_ms[o.name] = round(a.elapsed_time(b) / 5, 4)
     step_ms = wall * 1e3 / args.steps
     edges = sum(o.edges for o in ops)
     bytes_alg = sum(o.bytes_alg for o in ops)
@@ -391,6 +414,7 @@ def main():
         "hbm_gbps_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9,
         "hbm_frac_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "per_op_ms": {k: round(v, 4) for k, v in per_op_ms.items()},
+        "separate_launch_ms": separate_ms,
         "roofline": {"bound": "hbm", "kernel": f"{dom.name}: {w['kernel']}", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},

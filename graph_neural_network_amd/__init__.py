@@ -31,7 +31,7 @@ REORDER = {"degree": 0, "rcm": 1}
 
 # every symbol include/gnn.h declares
 EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
-           "gnn_spmm", "gnn_reduce", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
+           "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error")
 
 
@@ -75,6 +75,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_plan_wsb_export": [vp, vp, vp, vp, vp],
         "gnn_spmm": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
         "gnn_reduce": [P(_Csr), vp, ci, i32, i64, ci, vp, i64, vp, vp, vp],
+        "gnn_reduce_multi": [P(_Csr), vp, ci, i32, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp],
         "gnn_gatv2_fused": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp],
         "gnn_gt_fused": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, ci, vp, vp, vp, vp],
         "gnn_reorder": [P(_Csr), ci, vp, vp, vp, vp],
@@ -219,6 +220,29 @@ def gnn_reduce(csr: Csr, X: torch.Tensor, op: str = "sum", Y: torch.Tensor | Non
                                      REDUCE_OP[op], _ptr(Y), Y.stride(0), _ptr(arg),
                                      _plan_h(plan), _stream(stream)), "gnn_reduce")
     return Y, arg
+
+
+def gnn_reduce_multi(csr: Csr, X: torch.Tensor, ops=("sum", "mean", "max", "min"), args: bool = True,
+                     out: dict | None = None, plan: Plan | None = None, stream=None) -> dict:
+    """One pass computing the requested reductions; returns {name: tensor} with
+    keys among sum, mean, max, min, argmax, argmin (indices only with args)."""
+    F = X.shape[1]
+    out = dict(out or {})
+    for op in ops:
+        if op not in out:
+            out[op] = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    if args:
+        for op in ("max", "min"):
+            if op in ops and "arg" + op not in out:
+                out["arg" + op] = torch.empty((csr.n_rows, F), dtype=torch.int32, device=X.device)
+    lds = {o.stride(0) for k, o in out.items() if not k.startswith("arg")}
+    if len(lds) != 1:
+        raise ValueError("value outputs must share one row stride")
+    _check(load_library().gnn_reduce_multi(
+        csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(out.get("sum")), _ptr(out.get("mean")),
+        _ptr(out.get("max")), _ptr(out.get("argmax")), _ptr(out.get("min")), _ptr(out.get("argmin")),
+        lds.pop(), _plan_h(plan), _stream(stream)), "gnn_reduce_multi")
+    return out
 
 
 def gnn_gatv2_fused(csr: Csr, xl: torch.Tensor, xr: torch.Tensor, att: torch.Tensor,

@@ -35,7 +35,8 @@ namespace {
 constexpr int WG = 256;  // 4 waves
 constexpr int U = 8;     // edges in flight per slot
 
-enum Kind { K_SUM = 0, K_MAX = 1, K_MIN = 2 };
+// K_ALL: sum, mean, max and min (with source indices) of one pass.
+enum Kind { K_SUM = 0, K_MAX = 1, K_MIN = 2, K_ALL = 3 };
 
 struct AggParams {
   const int32_t* row_ptr;
@@ -57,6 +58,13 @@ struct AggParams {
   int32_t n_light_blocks;
   int32_t norm;            // gnn_norm (SpMM); MEAN is expressed as LEFT
   int32_t weighted;        // edge_val present or RIGHT / BOTH
+  // K_ALL outputs (each nullable; Y above is the sum), and the min words
+  float* Ymean;
+  float* Ymax;
+  float* Ymin;
+  int32_t* argmax;
+  int32_t* argmin;
+  unsigned long long* packed2;
 };
 
 // ---------------------------------------------------------------------------
@@ -129,7 +137,8 @@ template <int KIND, int VE, bool ARG>
 struct State {
   float acc[VE];
   uint32_t key[VE];
-  unsigned long long pk[VE];
+  unsigned long long pk[VE];   // MAX / MIN word (K_ALL: the max word)
+  unsigned long long pk2[VE];  // K_ALL: the min word
 
   static constexpr unsigned long long kInit = (KIND == K_MIN) ? ~0ull : 0ull;
 
@@ -139,6 +148,7 @@ struct State {
       acc[v] = 0.0f;
       key[v] = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
       pk[v] = kInit;
+      pk2[v] = ~0ull;
     }
   }
   __device__ __forceinline__ static uint32_t tie(int j) {
@@ -150,6 +160,12 @@ struct State {
     for (int v = 0; v < VE; ++v) {
       if constexpr (KIND == K_SUM) {
         acc[v] = fmaf(w, x[v], acc[v]);
+      } else if constexpr (KIND == K_ALL) {
+        acc[v] += x[v];
+        const unsigned long long kk = (unsigned long long)dev::order_key(x[v]) << 32;
+        const unsigned long long cmax = kk | ~(uint32_t)j, cmin = kk | (uint32_t)j;
+        pk[v] = cmax > pk[v] ? cmax : pk[v];
+        pk2[v] = cmin < pk2[v] ? cmin : pk2[v];
       } else if constexpr (ARG) {
         const unsigned long long c = ((unsigned long long)dev::order_key(x[v]) << 32) | t;
         pk[v] = (KIND == K_MAX) ? (c > pk[v] ? c : pk[v]) : (c < pk[v] ? c : pk[v]);
@@ -222,6 +238,40 @@ __device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, i
 template <typename T, int LPR, int VE, int KIND, bool ARG>
 __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg, int f0,
                                            State<KIND, VE, ARG>& st) {
+  if constexpr (KIND == K_ALL) {
+    const int64_t oy = (int64_t)row * p.ldy + f0, oa = (int64_t)row * p.F + f0;
+    float o[VE];
+    int ai[VE];
+    if (p.Y) {
+#pragma unroll
+      for (int v = 0; v < VE; ++v) o[v] = st.acc[v];
+      storev<VE>(p.Y + oy, o);
+    }
+    if (p.Ymean) {
+#pragma unroll
+      for (int v = 0; v < VE; ++v) o[v] = deg > 0 ? st.acc[v] / (float)deg : 0.0f;
+      storev<VE>(p.Ymean + oy, o);
+    }
+    if (p.Ymax) {
+#pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        o[v] = deg > 0 ? dev::key_to_float((uint32_t)(st.pk[v] >> 32)) : 0.0f;
+        ai[v] = deg > 0 ? (int)~(uint32_t)st.pk[v] : -1;
+      }
+      storev<VE>(p.Ymax + oy, o);
+      if (p.argmax) storei<VE>(p.argmax + oa, ai);
+    }
+    if (p.Ymin) {
+#pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        o[v] = deg > 0 ? dev::key_to_float((uint32_t)(st.pk2[v] >> 32)) : 0.0f;
+        ai[v] = deg > 0 ? (int)(uint32_t)st.pk2[v] : -1;
+      }
+      storev<VE>(p.Ymin + oy, o);
+      if (p.argmin) storei<VE>(p.argmin + oa, ai);
+    }
+    return;
+  }
   float out[VE];
   int ai[VE];
 #pragma unroll
@@ -270,15 +320,24 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
     scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
 
     // merge the slots in LDS, in slot order
-    __shared__ float s_acc[(KIND == K_SUM) ? SPB * FT : 1];
-    __shared__ uint32_t s_key[(KIND != K_SUM && !ARG) ? SPB * FT : 1];
-    __shared__ unsigned long long s_pk[(KIND != K_SUM && ARG) ? SPB * FT : 1];
+    __shared__ float s_acc[(KIND == K_SUM || KIND == K_ALL) ? SPB * FT : 1];
+    __shared__ uint32_t s_key[(KIND == K_MAX || KIND == K_MIN) && !ARG ? SPB * FT : 1];
+    __shared__ unsigned long long s_pk[(KIND == K_ALL || (KIND != K_SUM && ARG)) ? SPB * FT : 1];
+    __shared__ unsigned long long s_pk2[(KIND == K_ALL) ? SPB * FT : 1];
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       const int t = sl * VE + v;
-      if constexpr (KIND == K_SUM) s_acc[slot * FT + t] = st.acc[v];
-      else if constexpr (ARG) s_pk[slot * FT + t] = st.pk[v];
-      else s_key[slot * FT + t] = st.key[v];
+      if constexpr (KIND == K_ALL) {
+        s_acc[slot * FT + t] = st.acc[v];
+        s_pk[slot * FT + t] = st.pk[v];
+        s_pk2[slot * FT + t] = st.pk2[v];
+      } else if constexpr (KIND == K_SUM) {
+        s_acc[slot * FT + t] = st.acc[v];
+      } else if constexpr (ARG) {
+        s_pk[slot * FT + t] = st.pk[v];
+      } else {
+        s_key[slot * FT + t] = st.key[v];
+      }
     }
     __syncthreads();
     for (int t = threadIdx.x; t < FT; t += WG) {
@@ -286,9 +345,14 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
       if (f >= p.F) continue;
       float a = 0.0f;
       uint32_t k = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
-      unsigned long long w = State<KIND, VE, ARG>::kInit;
+      unsigned long long w = State<KIND, VE, ARG>::kInit, w2 = ~0ull;
       for (int s2 = 0; s2 < SPB; ++s2) {
-        if constexpr (KIND == K_SUM) {
+        if constexpr (KIND == K_ALL) {
+          a += s_acc[s2 * FT + t];
+          const unsigned long long c = s_pk[s2 * FT + t], c2 = s_pk2[s2 * FT + t];
+          w = c > w ? c : w;
+          w2 = c2 < w2 ? c2 : w2;
+        } else if constexpr (KIND == K_SUM) {
           a += s_acc[s2 * FT + t];
         } else if constexpr (ARG) {
           const unsigned long long c = s_pk[s2 * FT + t];
@@ -299,6 +363,22 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
         }
       }
       if constexpr (KIND != K_SUM && !ARG) w = ((unsigned long long)k << 32) | State<KIND, VE, ARG>::tie(0);
+      if constexpr (KIND == K_ALL) {
+        const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
+        if (m < 0) {
+          if (p.Y) __builtin_nontemporal_store(a, p.Y + oy);
+          if (p.Ymean) __builtin_nontemporal_store(a / (float)len, p.Ymean + oy);
+          if (p.Ymax) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Ymax + oy);
+          if (p.argmax) __builtin_nontemporal_store((int)~(uint32_t)w, p.argmax + oa);
+          if (p.Ymin) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w2 >> 32)), p.Ymin + oy);
+          if (p.argmin) __builtin_nontemporal_store((int)(uint32_t)w2, p.argmin + oa);
+        } else {
+          p.partial[(int64_t)lid * p.F + f] = a;
+          atomicMax(p.packed + (int64_t)m * p.F + f, w);
+          atomicMin(p.packed2 + (int64_t)m * p.F + f, w2);
+        }
+        continue;
+      }
       if (m < 0) {
         const int deg = len;  // single item covers the whole row
         if constexpr (KIND == K_SUM) {
@@ -347,6 +427,26 @@ __global__ __launch_bounds__(256) void k_combine_sum(AggParams p, const int4* mu
   }
 }
 
+// K_ALL: sum / mean from the item partials (item order), max / min unpacked.
+__global__ __launch_bounds__(256) void k_combine_all(AggParams p, const int4* multi) {
+  const int4 mr = multi[blockIdx.x];
+  const int row = mr.x, first = mr.y, cnt = mr.z;
+  const int deg = p.row_ptr[row + 1] - p.row_ptr[row];
+  for (int f = threadIdx.x; f < p.F; f += blockDim.x) {
+    float a = 0.0f;
+    for (int c = 0; c < cnt; ++c) a += p.partial[(int64_t)(first + c) * p.F + f];
+    const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
+    if (p.Y) p.Y[oy] = a;
+    if (p.Ymean) p.Ymean[oy] = a / (float)deg;
+    const unsigned long long w = p.packed[(int64_t)blockIdx.x * p.F + f];
+    const unsigned long long w2 = p.packed2[(int64_t)blockIdx.x * p.F + f];
+    if (p.Ymax) p.Ymax[oy] = dev::key_to_float((uint32_t)(w >> 32));
+    if (p.argmax) p.argmax[oa] = (int)~(uint32_t)w;
+    if (p.Ymin) p.Ymin[oy] = dev::key_to_float((uint32_t)(w2 >> 32));
+    if (p.argmin) p.argmin[oa] = (int)(uint32_t)w2;
+  }
+}
+
 // Packed (key, index) words of heavy rows back to value and source index.
 template <int KIND, bool ARG>
 __global__ __launch_bounds__(256) void k_unpack(AggParams p, const int4* multi) {
@@ -380,9 +480,13 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "aggregate grid too large");
   if (KIND != K_SUM && pl->n_multi > 0) {
     int64_t nw = pl->n_multi * p.F;
-    hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)std::min<int64_t>((nw + 255) / 256, 16384)),
-                       dim3(256), 0, s, p.packed, nw, KIND == K_MAX ? 0ull : ~0ull);
+    const unsigned nb = (unsigned)std::min<int64_t>((nw + 255) / 256, 16384);
+    hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed, nw, KIND == K_MIN ? ~0ull : 0ull);
     GNN_LAUNCH_CHECK("fill packed");
+    if (KIND == K_ALL) {
+      hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed2, nw, ~0ull);
+      GNN_LAUNCH_CHECK("fill packed");
+    }
   }
   if (gx > 0) {
     hipLaunchKernelGGL((k_aggregate<T, LPR, VE, KIND, ARG>), dim3((unsigned)gx, (unsigned)ftiles),
@@ -390,7 +494,10 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
     GNN_LAUNCH_CHECK("aggregate");
   }
   if (pl->n_multi > 0) {
-    if constexpr (KIND == K_SUM) {
+    if constexpr (KIND == K_ALL) {
+      hipLaunchKernelGGL(k_combine_all, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
+                         (const int4*)pl->multi);
+    } else if constexpr (KIND == K_SUM) {
       hipLaunchKernelGGL(k_combine_sum, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
                          (const int4*)pl->multi);
     } else {
@@ -418,6 +525,7 @@ int pick_lpr(gnn_plan* pl, AggParams& p, int lpr, hipStream_t s) {
 
 template <typename T, int VE>
 int pick_kind(gnn_plan* pl, AggParams& p, int kind, bool arg, int lpr, hipStream_t s) {
+  if (kind == K_ALL) return pick_lpr<T, VE, K_ALL, true>(pl, p, lpr, s);
   if (kind == K_SUM) return pick_lpr<T, VE, K_SUM, false>(pl, p, lpr, s);
   if (kind == K_MAX)
     return arg ? pick_lpr<T, VE, K_MAX, true>(pl, p, lpr, s) : pick_lpr<T, VE, K_MAX, false>(pl, p, lpr, s);
@@ -473,6 +581,54 @@ int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64
   }
   return vec_ok ? pick_kind<float, 4>(pl, p, kind, arg != nullptr, lpr, s)
                 : pick_kind<float, 1>(pl, p, kind, arg != nullptr, lpr, s);
+}
+
+int launch_reduce_multi(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx,
+                        float* Ysum, float* Ymean, float* Ymax, int32_t* argmax, float* Ymin,
+                        int32_t* argmin, int64_t ldy, hipStream_t s) {
+  AggParams p{};
+  p.row_ptr = pl->row_ptr;
+  p.col_idx = pl->col_idx;
+  p.deg_out = pl->deg_out;
+  p.X = X;
+  p.ldx = ldx;
+  p.Y = Ysum;
+  p.Ymean = Ymean;
+  p.Ymax = Ymax;
+  p.Ymin = Ymin;
+  p.argmax = argmax;
+  p.argmin = argmin;
+  p.ldy = ldy;
+  p.items = pl->items;
+  p.n_rows = pl->n_rows;
+  p.F = F;
+  p.light_max = pl->light_max;
+  if (pl->n_multi > 0) {
+    void* ws = nullptr;
+    const size_t part = ((size_t)pl->n_items * F * 4 + 255) & ~(size_t)255;
+    const size_t words = (size_t)pl->n_multi * F * 8;
+    GNN_TRY(plan_workspace(pl, part + 2 * words, &ws));
+    p.partial = (float*)ws;
+    p.packed = (unsigned long long*)((char*)ws + part);
+    p.packed2 = (unsigned long long*)((char*)ws + part + words);
+  }
+  const int esz = (xt == GNN_BF16) ? 2 : 4;
+  const int64_t rowb = (int64_t)F * esz;
+  const uintptr_t outs = (uintptr_t)Ysum | (uintptr_t)Ymean | (uintptr_t)Ymax | (uintptr_t)Ymin |
+                         (uintptr_t)argmax | (uintptr_t)argmin;
+  const bool vec_ok = (rowb % 16 == 0) && ((ldx * esz) % 16 == 0) && ((uintptr_t)X % 16 == 0) &&
+                      (outs % 16 == 0) && (ldy % 4 == 0) && (F % 4 == 0);
+  int lpr = 64;
+  if (vec_ok) {
+    int lanes = (int)std::min<int64_t>(rowb / 16, 64);
+    lpr = 8;
+    while (lpr < lanes) lpr <<= 1;
+  }
+  if (xt == GNN_BF16)
+    return vec_ok ? pick_kind<uint16_t, 8>(pl, p, K_ALL, true, lpr, s)
+                  : pick_kind<uint16_t, 1>(pl, p, K_ALL, true, lpr, s);
+  return vec_ok ? pick_kind<float, 4>(pl, p, K_ALL, true, lpr, s)
+                : pick_kind<float, 1>(pl, p, K_ALL, true, lpr, s);
 }
 
 }  // namespace gnn

@@ -200,6 +200,25 @@ int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, in
   return launch_aggregate(p, X, xtype, F, ldx, Y, ldy, mode, GNN_NORM_NONE, nullptr, arg, s);
 }
 
+int gnn_reduce_multi(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+                     float* Y_sum, float* Y_mean, float* Y_max, int32_t* arg_max, float* Y_min,
+                     int32_t* arg_min, int64_t ldy, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (F <= 0 || ldx < F || ldy < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldx >= F, ldy >= F");
+  if (!Y_sum && !Y_mean && !Y_max && !Y_min) return fail(GNN_ERR_INVALID_VALUE, "no output requested");
+  if ((arg_max && !Y_max) || (arg_min && !Y_min))
+    return fail(GNN_ERR_INVALID_VALUE, "an index output needs its value output");
+  if (!X && csr->n_cols > 0) return fail(GNN_ERR_INVALID_VALUE, "X is NULL");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_reduce_multi(p, X, xtype, F, ldx, Y_sum, Y_mean, Y_max, arg_max, Y_min, arg_min, ldy, s);
+}
+
 int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,
                     const float* att, int32_t H, int32_t D, float neg_slope, float* out, float* lse,
                     gnn_plan* plan, void* stream) {

@@ -110,6 +110,9 @@ int check_plan(const gnn_plan* p, const gnn_csr* csr);
 int launch_aggregate(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y,
                      int64_t ldy, int mode, gnn_norm norm, const float* edge_val, int32_t* arg,
                      hipStream_t s);
+int launch_reduce_multi(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx,
+                        float* Ysum, float* Ymean, float* Ymax, int32_t* argmax, float* Ymin,
+                        int32_t* argmin, int64_t ldy, hipStream_t s);
 int launch_gatv2(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, const float* att,
                  int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s);
 int launch_gt_csr(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,

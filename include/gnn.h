@@ -7,6 +7,7 @@
  * gives the kernels):
  *   gnn_spmm         SpMM-based convolution Y = A_norm X      (section 2.2 (i), appendix D.4)
  *   gnn_reduce       segmented sum / mean / max / min          (section 2.2 (ii), appendix D.1)
+ *   gnn_reduce_multi the four reductions in one pass           (section 2.2 (ii), appendix D.1)
  *   gnn_gatv2_fused  GATv2 attention, one pass, online softmax (section 2.2 (iii), appendix D.2)
  *   gnn_gt_fused     Graph Transformer attention, CSR or 16x16 block-sparse
  *                                                              (appendix D.2 and D.3)
@@ -150,6 +151,18 @@ int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int6
  * Errors as gnn_spmm. */
 int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
                gnn_reduce_op op, float* Y, int64_t ldy, int32_t* arg, gnn_plan* plan, void* stream);
+
+/* All four segmented reductions of section 2.2 (ii) in one pass: every
+ * gathered neighbour row is read once and feeds the sum, mean, max and min
+ * (with their source indices), the same IO-aware idea the fused attention
+ * kernels apply (appendix D.2).  Definitions, tie rules and empty-row values
+ * as gnn_reduce.  Y_sum, Y_mean, Y_max, Y_min: device [n_rows, ldy] float32,
+ * each nullable (at least one required); arg_max / arg_min: device
+ * [n_rows, F] int32 or NULL (each needs its value output).
+ * Errors as gnn_reduce. */
+int gnn_reduce_multi(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+                     float* Y_sum, float* Y_mean, float* Y_max, int32_t* arg_max, float* Y_min,
+                     int32_t* arg_min, int64_t ldy, gnn_plan* plan, void* stream);
 
 /* Fused GATv2 forward (section 2.2 (iii); appendix D.2 "fused CSR forward
  * (GATv2)"): for each destination i and head h,

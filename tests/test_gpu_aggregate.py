@@ -284,3 +284,62 @@ def test_spmm_rmat1m_full_gcn(cfg_reduce):
     rows = sample_rows(w.row_ptr, 3000, 2)
     ref, mag = oracle.spmm(w.row_ptr, w.col_idx, X, "both", rows=rows)
     assert scaled_err(Y[rows], ref, mag) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# gnn_reduce_multi: the four reductions of one pass
+# ---------------------------------------------------------------------------
+
+def _multi_vs_separate(csr, Xd, plan, F, rows_check=None, ref=None):
+    out = gnn.gnn_reduce_multi(csr, Xd, plan=plan)
+    for op in ("sum", "mean", "max", "min"):
+        Y, arg = gnn.gnn_reduce(csr, Xd, op, arg=op in ("max", "min"), plan=plan)
+        assert torch.equal(out[op].view(torch.int32), Y.view(torch.int32)), op
+        if arg is not None:
+            assert torch.equal(out["arg" + op], arg), op
+    return out
+
+
+@pytest.mark.parametrize("F,dt", [(128, "f32"), (37, "f32"), (256, "bf16")])
+def test_reduce_multi_matches_separate_and_oracle(rmat_small, F, dt):
+    rp, ci = rmat_small
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    if dt == "f32":
+        Xh = gen.gauss_f32(21, (n, F))
+        Xd, Xo = dev(Xh), Xh
+    else:
+        Xb = gen.gauss_bf16(21, (n, F))
+        Xd, Xo = dev_bf16(Xb), gen.bf16_to_f32(Xb)
+    for plan in (gnn.gnn_plan_create(csr, **SMALL_PLAN), gnn.gnn_plan_create(csr)):
+        out = _multi_vs_separate(csr, Xd, plan, F)
+        for op in ("sum", "mean", "max", "min"):
+            check_reduce(rp, ci, Xo, host(out[op]), host(out["arg" + op]) if op in ("max", "min") else None, op)
+
+
+def test_reduce_multi_subsets_and_empty_rows():
+    n = 3000
+    rp, ci = gen.from_edges(n, np.r_[np.arange(1, n), [5, 7]], np.r_[np.zeros(n - 1, np.int64), [9, 9]])
+    csr = dev_csr(rp, ci)
+    X = gen.gauss_f32(4, (n, 64))
+    out = gnn.gnn_reduce_multi(csr, dev(X), ops=("mean", "min"), args=False)
+    assert set(out) == {"mean", "min"}
+    for op in ("mean", "min"):
+        Y, _ = gnn.gnn_reduce(csr, dev(X), op)
+        assert torch.equal(out[op], Y)
+    full = gnn.gnn_reduce_multi(csr, dev(X))
+    empty = np.diff(rp) == 0
+    for k in ("sum", "mean", "max", "min"):
+        assert np.all(host(full[k])[empty] == 0)
+    assert np.all(host(full["argmax"])[empty] == -1) and np.all(host(full["argmin"])[empty] == -1)
+
+
+def test_reduce_multi_rmat1m_full(cfg_reduce):
+    w, csr, plan = cfg_reduce
+    X = w.arrays["X"]
+    Xd = dev(X)
+    out = _multi_vs_separate(csr, Xd, plan, 128)
+    rows = sample_rows(w.row_ptr, 2000, 3)
+    for op in ("sum", "mean", "max", "min"):
+        check_reduce(w.row_ptr, w.col_idx, X, host(out[op]),
+                     host(out["arg" + op]) if op in ("max", "min") else None, op, rows)
