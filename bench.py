@@ -217,7 +217,7 @@ def wl_gt(args, mode="csr"):
     H, D = w.params["H"], w.params["D"]
     csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
     t0 = time.perf_counter()
-    plan = gnn.gnn_plan_create(csr, light_max_deg=64, build_wsb=(mode == "block16"))
+    plan = gnn.gnn_plan_create(csr, build_wsb=(mode == "block16"))
     plan_ms = (time.perf_counter() - t0) * 1e3
     q, k, v = (_to_bf16(w.arrays[x]) for x in ("q", "k", "v"))
     out = torch.empty((n, H, D), dtype=torch.float32, device="cuda")

@@ -21,8 +21,9 @@
 // flight; slots of a wave, waves of a workgroup and chunks of a split row
 // are merged with the same rescaling rule.  Logits live in the log2 domain
 // (log2 e folded into a or into q * scale) so every exponential is exp2.
-//   light rows : one slot per row (rows in natural order, XCD-contiguous)
-//   items      : one workgroup per medium row or per chunk of a heavy row;
+//   light rows : one slot per row up to 64 edges (rows in natural order,
+//                XCD-contiguous)
+//   items      : one workgroup per longer row or per chunk of a heavy row;
 //                chunks of a heavy row leave partial (m, l, acc) states that a
 //                combine kernel merges in chunk order.
 #include <algorithm>
@@ -33,7 +34,9 @@ namespace gnn {
 namespace {
 
 constexpr int WG = 256;
-constexpr int U = 4;
+#ifndef GNN_ATT_U
+#define GNN_ATT_U 4
+#endif
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -134,69 +137,106 @@ __device__ __forceinline__ void shfl_merge(Soft<VEL>& s, int lane_xor) {
   s.merge(m2, l2, a2);
 }
 
-// Process edges [eb, ee) of destination `row` for one slot.
-//   qv  : this lane's slice of the destination-side vector (GATv2: x_l,
-//         GT: q * scale * log2 e)
-//   av  : GATv2 attention-vector slice times log2 e (unused for GT)
-template <typename T, int LPE, int VEL, int KIND>
+// A lane's slice of one node row, kept as raw 16-byte words until used
+// (NV words = 8 NV bf16 or 4 NV float32 elements).
+template <int NV>
+struct Raw {
+  uint32_t u[4 * NV];
+};
+
+template <typename T, int NV>
+__device__ __forceinline__ void load_raw(const T* p, Raw<NV>& r) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+    r.u[4 * k] = v.x; r.u[4 * k + 1] = v.y; r.u[4 * k + 2] = v.z; r.u[4 * k + 3] = v.w;
+  }
+}
+
+// element k of a raw slice as float
+template <typename T, int NV>
+__device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
+  if constexpr (sizeof(T) == 2) return (k & 1) ? dev::bf16_hi(r.u[k >> 1]) : dev::bf16_lo(r.u[k >> 1]);
+  else return __uint_as_float(r.u[k]);
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+
+// Process edges [eb, ee) of destination `row` for one slot, UU edges in
+// flight.
+//   qv / qraw : this lane's slice of the destination-side vector (GATv2: x_l
+//               as float; GT: q, raw, its scale * log2 e applied after the
+//               head reduction)
+//   av        : GATv2 attention-vector slice times log2 e (unused for GT)
+template <typename T, int LPE, int NV, int KIND, int UU>
 __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, int sl, int slot_base,
-                                           bool d_ok, const float (&qv)[VEL], const float (&av)[VEL],
-                                           Soft<VEL>& st) {
+                                           bool d_ok, const float (&qv)[(16 / sizeof(T)) * NV],
+                                           const Raw<NV>& qraw,
+                                           const float (&av)[(16 / sizeof(T)) * NV],
+                                           Soft<(16 / sizeof(T)) * NV>& st) {
+  constexpr int VEL = (16 / (int)sizeof(T)) * NV;
   const T* K = reinterpret_cast<const T*>(p.k) + sl * VEL;
   const T* V = reinterpret_cast<const T*>(p.v) + sl * VEL;
   const int64_t ld = p.row_elems;
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
-    for (int u0 = 0; u0 < nb; u0 += U) {
-      int c[U];
-      float x[U][VEL];
-      float y[U][VEL];
+    for (int u0 = 0; u0 < nb; u0 += UU) {
+      int c[UU];
+      Raw<NV> x[UU];
+      Raw<NV> y[UU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) c[u] = __shfl(my_c, slot_base + u0 + u, 64);
+      for (int u = 0; u < UU; ++u) c[u] = __shfl(my_c, slot_base + u0 + u, 64);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         if (u0 + u < nb && d_ok) {
-          load_row<T, VEL>(K + (int64_t)c[u] * ld, x[u]);
-          if constexpr (KIND == K_GT) load_row<T, VEL>(V + (int64_t)c[u] * ld, y[u]);
+          load_raw<T, NV>(K + (int64_t)c[u] * ld, x[u]);
+          if constexpr (KIND == K_GT) load_raw<T, NV>(V + (int64_t)c[u] * ld, y[u]);
         } else {
 #pragma unroll
-          for (int k = 0; k < VEL; ++k) {
-            x[u][k] = 0.0f;
-            if constexpr (KIND == K_GT) y[u][k] = 0.0f;
+          for (int k = 0; k < 4 * NV; ++k) {
+            x[u].u[k] = 0u;
+            if constexpr (KIND == K_GT) y[u].u[k] = 0u;
           }
         }
       }
-      float s[U];
+      float s[UU];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         float t = 0.0f;
+        if constexpr (KIND == K_GATV2) {
 #pragma unroll
-        for (int k = 0; k < VEL; ++k) {
-          if constexpr (KIND == K_GATV2) {
-            const float z = qv[k] + x[u][k];
-            t = fmaf(av[k], z > 0.0f ? z : p.slope * z, t);
-          } else {
-            t = fmaf(qv[k], x[u][k], t);
+          for (int k = 0; k < VEL; ++k) {
+            const float z = qv[k] + elem<T, NV>(x[u], k);
+            t = fmaf(av[k], fmaxf(z, p.slope * z), t);
           }
+        } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int k = 0; k < 4 * NV; ++k)
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qraw.u[k]),
+                                                __builtin_bit_cast(bf16x2_t, x[u].u[k]), t, false);
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) t = fmaf(qv[k], elem<T, NV>(x[u], k), t);
         }
         for (int o = 1; o < p.lph; o <<= 1) t += __shfl_xor(t, o, 64);
+        if constexpr (KIND == K_GT) t *= p.qscale;
         s[u] = (u0 + u < nb) ? t : -INFINITY;
       }
       float mn = st.m;
 #pragma unroll
-      for (int u = 0; u < U; ++u) mn = fmaxf(mn, s[u]);
+      for (int u = 0; u < UU; ++u) mn = fmaxf(mn, s[u]);
       const float corr = exp2f(st.m - mn);
       st.l *= corr;
 #pragma unroll
       for (int k = 0; k < VEL; ++k) st.acc[k] *= corr;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < UU; ++u) {
         const float pu = exp2f(s[u] - mn);
         st.l += pu;
 #pragma unroll
         for (int k = 0; k < VEL; ++k)
-          st.acc[k] = fmaf(pu, (KIND == K_GT) ? y[u][k] : x[u][k], st.acc[k]);
+          st.acc[k] = fmaf(pu, (KIND == K_GT) ? elem<T, NV>(y[u], k) : elem<T, NV>(x[u], k), st.acc[k]);
       }
       st.m = mn;
     }
@@ -215,7 +255,7 @@ __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int
     p.lse[row * p.H + head] = st.l > 0.0f ? st.m * kLn2 + logf(st.l) : -INFINITY;
 }
 
-template <typename T, int LPE, int NV, int KIND>
+template <typename T, int LPE, int NV, int KIND, int UU>
 __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;  // elements per lane
   constexpr int SPW = 64 / LPE;
@@ -235,6 +275,8 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
     item = (int)dev::xcd_remap(blockIdx.x, n_item_pad);
     if (item >= p.n_item_blocks) return;
     const int4 it = p.items[item];
+    // single-chunk rows short enough for the light path are processed there
+    if (it.w < 0 && it.z - it.y <= p.light_max) return;
     row = it.x;
     m_idx = it.w;
     // split the item's edges over all slots of the workgroup
@@ -255,23 +297,25 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
 
   // destination-side slice (and the attention vector for GATv2)
   float qv[VEL], av[VEL];
+  Raw<NV> qraw;
   if (d_ok) {
-    load_row<T, VEL>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + sl * VEL, qv);
+    load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + sl * VEL, qraw);
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) qv[k] = elem<T, NV>(qraw, k);
     if constexpr (KIND == K_GATV2) {
 #pragma unroll
       for (int k = 0; k < VEL; ++k) av[k] = p.att[sl * VEL + k] * kLog2e;
-    } else {
-#pragma unroll
-      for (int k = 0; k < VEL; ++k) qv[k] *= p.qscale;
     }
   } else {
+#pragma unroll
+    for (int k = 0; k < 4 * NV; ++k) qraw.u[k] = 0u;
 #pragma unroll
     for (int k = 0; k < VEL; ++k) qv[k] = av[k] = 0.0f;
   }
 
   Soft<VEL> st;
   st.init();
-  scan_edges<T, LPE, VEL, KIND>(p, eb, ee, sl, slot_base, d_ok, qv, av, st);
+  scan_edges<T, LPE, NV, KIND, UU>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, st);
 
   if (!is_item) {
     if (d_ok) write_final<VEL>(p, row, sl, head, st);
@@ -335,12 +379,13 @@ __global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* mu
 
 template <typename T, int LPE, int NV, int KIND>
 int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
+  constexpr int UU = GNN_ATT_U;
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.n_item_blocks = (int32_t)pl->n_items;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
-  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND, UU>), dim3((unsigned)gx), dim3(WG), 0, s, p);
   GNN_LAUNCH_CHECK("attention");
   if (pl->n_multi > 0) {
     hipLaunchKernelGGL(k_att_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
@@ -393,7 +438,10 @@ int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* l
   p.row_elems = H * D;
   p.row_lanes = lanes;
   p.lph = lph;
-  p.light_max = pl->light_max;
+  // attention rows are cheaper per edge than the plan's aggregation rows:
+  // one slot per row up to 64 edges (never below the plan's own threshold,
+  // whose longer rows are the plan's items)
+  p.light_max = std::max(pl->light_max, 64);
   if (pl->n_multi > 0) {
     void* ws = nullptr;
     size_t need = (size_t)pl->n_items * (H * D + 2 * H) * 4;

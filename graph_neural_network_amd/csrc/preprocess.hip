@@ -277,7 +277,7 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   if (opts) p->opts = *opts;
   float gamma = p->opts.heavy_quantile == 0.0f ? 0.99f : p->opts.heavy_quantile;
   p->light_max = p->opts.light_max_deg > 0 ? p->opts.light_max_deg : 32;
-  p->chunk_edges = p->opts.chunk_edges > 0 ? p->opts.chunk_edges : 512;
+  p->chunk_edges = p->opts.chunk_edges > 0 ? p->opts.chunk_edges : 1024;
   if (p->opts.wsb_min_nnz <= 0) p->opts.wsb_min_nnz = 8;
 
   const int32_t n = p->n_rows;

@@ -93,7 +93,7 @@ typedef struct gnn_plan_opts {
   float heavy_quantile;    /* gamma: rows above this degree quantile are split
                               into edge chunks (default 0.99; < 0 = never split) */
   int32_t light_max_deg;   /* rows up to this degree run one per 32-lane slot (default 32) */
-  int32_t chunk_edges;     /* edges per chunk of a split row (default 512) */
+  int32_t chunk_edges;     /* edges per chunk of a split row (default 1024) */
   int32_t build_wsb;       /* 1 = also build the 16x16 block-sparse tiles (GT BLOCK16) */
   int32_t wsb_min_nnz;     /* tau: tiles with fewer edges go to the CSR residual (default 8) */
   int32_t reserved[4];
