@@ -201,42 +201,54 @@ __global__ void k_start_fill(const int32_t* order, const int32_t* flag, const in
   visited[v] = 1;
 }
 
-__global__ void k_claim(const int32_t* front, int32_t f, const int32_t* sym_ptr, const int32_t* adj,
-                        const int32_t* visited, int32_t* claim) {
+// ---- one BFS level over the frontier's flattened adjacency ----
+// Frontier edge q (0 <= q < E_f) belongs to frontier position k with
+// eoff[k] <= q < eoff[k+1]; its target is adj[sym_ptr[front[k]] + q - eoff[k]].
+// Edges are numbered in (frontier position, adjacency order), so emitting
+// them in q order keeps the queue order.
+
+__global__ void k_front_deg(const int32_t* front, int32_t f, const int32_t* sym_ptr, int32_t* deg) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= f) return;
-  const int u = front[k];
-  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
-    const int w = adj[e];
-    if (!visited[w]) atomicMin(&claim[w], (int32_t)k);
-  }
+  if (k < f) deg[k] = sym_ptr[front[k] + 1] - sym_ptr[front[k]];
 }
 
-__global__ void k_child_count(const int32_t* front, int32_t f, const int32_t* sym_ptr,
-                              const int32_t* adj, const int32_t* visited, const int32_t* claim,
-                              int32_t* cnt) {
-  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= f) return;
-  const int u = front[k];
-  int c = 0;
-  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
-    const int w = adj[e];
-    c += (!visited[w] && claim[w] == (int32_t)k) ? 1 : 0;
+__device__ __forceinline__ int front_of(const int32_t* eoff, int32_t f, int64_t q) {
+  int lo = 0, hi = f - 1;  // largest k with eoff[k] <= q
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (eoff[mid] <= q) lo = mid;
+    else hi = mid - 1;
   }
-  cnt[k] = c;
+  return lo;
 }
 
-__global__ void k_child_emit(const int32_t* front, int32_t f, const int32_t* sym_ptr,
-                             const int32_t* adj, const int32_t* visited, const int32_t* claim,
-                             const int32_t* off, int32_t* next) {
-  int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= f) return;
-  const int u = front[k];
-  int o = off[k];
-  for (int e = sym_ptr[u]; e < sym_ptr[u + 1]; ++e) {
-    const int w = adj[e];
-    if (!visited[w] && claim[w] == (int32_t)k) next[o++] = w;
-  }
+__global__ void k_claim(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
+                        const int32_t* sym_ptr, const int32_t* adj, const int32_t* visited,
+                        int32_t* claim) {
+  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= ef) return;
+  const int k = front_of(eoff, f, q);
+  const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
+  if (!visited[w]) atomicMin(&claim[w], k);
+}
+
+__global__ void k_child_flags(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
+                              const int32_t* sym_ptr, const int32_t* adj, const int32_t* visited,
+                              const int32_t* claim, int32_t* flag) {
+  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= ef) return;
+  const int k = front_of(eoff, f, q);
+  const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
+  flag[q] = (!visited[w] && claim[w] == k) ? 1 : 0;
+}
+
+__global__ void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
+                             const int32_t* sym_ptr, const int32_t* adj, const int32_t* flag,
+                             const int32_t* pos, int32_t* next) {
+  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= ef || !flag[q]) return;
+  const int k = front_of(eoff, f, q);
+  next[pos[q]] = adj[sym_ptr[front[k]] + (q - eoff[k])];
 }
 
 __global__ void k_mark(const int32_t* next, int32_t f, int32_t* visited) {
@@ -392,11 +404,15 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
 
   // 5. level-synchronous BFS of all components at once
   int32_t *concat = nullptr, *visited = nullptr, *claim = nullptr, *ccnt = nullptr, *coff = nullptr;
+  int32_t *qflag = nullptr, *qpos = nullptr;
   GNN_HIP(hipMallocAsync((void**)&concat, (size_t)n * 4, s));
   GNN_HIP(hipMallocAsync((void**)&visited, (size_t)n * 4, s));
   GNN_HIP(hipMallocAsync((void**)&claim, (size_t)n * 4, s));
   GNN_HIP(hipMallocAsync((void**)&ccnt, ((size_t)n + 1) * 4, s));
   GNN_HIP(hipMallocAsync((void**)&coff, ((size_t)n + 1) * 4, s));
+  // frontier-edge flags and positions: a level touches at most every entry once
+  GNN_HIP(hipMallocAsync((void**)&qflag, ((size_t)std::max<int64_t>(m, 1) + 1) * 4, s));
+  GNN_HIP(hipMallocAsync((void**)&qpos, ((size_t)std::max<int64_t>(m, 1) + 1) * 4, s));
   GNN_HIP(hipMemsetAsync(visited, 0, (size_t)n * 4, s));
   hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
   GNN_LAUNCH_CHECK("rcm claim init");
@@ -412,18 +428,29 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
   while (f > 0 && base + f < n) {
     const int32_t* front = concat + base;
     int32_t* next = concat + base + f;
-    hipLaunchKernelGGL(k_claim, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited, claim);
-    hipLaunchKernelGGL(k_child_count, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited,
-                       claim, ccnt);
-    GNN_LAUNCH_CHECK("rcm level count");
+    // frontier degrees -> offsets of the flattened frontier adjacency
+    hipLaunchKernelGGL(k_front_deg, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, ccnt);
+    GNN_LAUNCH_CHECK("rcm frontier degrees");
     GNN_TRY(exclusive_scan_i32(ccnt, coff, f, s));
-    int32_t nf = 0;
-    GNN_HIP(hipMemcpyAsync(&nf, coff + f, 4, hipMemcpyDeviceToHost, s));
+    int32_t ef = 0;
+    GNN_HIP(hipMemcpyAsync(&ef, coff + f, 4, hipMemcpyDeviceToHost, s));
     GNN_HIP(hipStreamSynchronize(s));
+    if (ef < 0 || ef > m) return fail(GNN_ERR_DEVICE, "RCM: frontier adjacency larger than the graph");
+    int32_t nf = 0;
+    if (ef > 0) {
+      hipLaunchKernelGGL(k_claim, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
+                         adj, visited, claim);
+      hipLaunchKernelGGL(k_child_flags, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
+                         sym_ptr, adj, visited, claim, qflag);
+      GNN_LAUNCH_CHECK("rcm level flags");
+      GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s));
+      GNN_HIP(hipMemcpyAsync(&nf, qpos + ef, 4, hipMemcpyDeviceToHost, s));
+      GNN_HIP(hipStreamSynchronize(s));
+    }
     if (nf < 0 || base + f + nf > n) return fail(GNN_ERR_DEVICE, "RCM: level larger than the graph");
     if (nf > 0) {
-      hipLaunchKernelGGL(k_child_emit, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, adj, visited,
-                         claim, coff, next);
+      hipLaunchKernelGGL(k_child_emit, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
+                         sym_ptr, adj, qflag, qpos, next);
       GNN_LAUNCH_CHECK("rcm level emit");
       hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, visited);
       GNN_LAUNCH_CHECK("rcm mark");
@@ -442,7 +469,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
 
   for (void* q : {(void*)keys, (void*)tmp, (void*)adj, (void*)adj_row, (void*)cnt, (void*)sym_ptr,
                   (void*)order, (void*)rank, (void*)label, (void*)changed, (void*)concat,
-                  (void*)visited, (void*)claim, (void*)ccnt, (void*)coff})
+                  (void*)visited, (void*)claim, (void*)ccnt, (void*)coff, (void*)qflag, (void*)qpos})
     GNN_HIP(hipFreeAsync(q, s));
   return GNN_OK;
 }
