@@ -14,9 +14,11 @@
 // and a wave holds 64 / LPR slots.  F = 128 float32 or F = 256 bf16 is a
 // 512-byte row: two slots per wave, each slot one dwordx4 wave-half load per
 // edge, 8 edges kept in flight per slot.
-//   light rows  (deg <= light_max): one slot per row, rows in natural order;
-//               the slot loads up to LPR column indices with one coalesced
-//               access and broadcasts them lane to lane (ds_bpermute).
+//   light rows  (deg <= light_max): LPR consecutive rows per slot, their
+//               edges walked as one flat sequence so that short rows still
+//               keep U gathers in flight; the slot loads up to LPR column
+//               indices with one coalesced access and broadcasts them lane to
+//               lane (ds_bpermute).
 //   items       (medium rows, and chunks of heavy rows): one workgroup of
 //               four waves per item; each slot takes a contiguous part of the
 //               item's edges, the slots are merged in LDS in slot order.
@@ -71,27 +73,31 @@ struct AggParams {
 // vector loads / stores of VE elements per lane
 // ---------------------------------------------------------------------------
 
-template <typename T, int VE>
-__device__ __forceinline__ void loadv(const T* p, float (&o)[VE]);
+// Gathered rows are kept as raw words until use (a bf16 row slice is 4
+// registers raw, 8 decoded), which keeps U rows in flight within the
+// register budget of four waves per SIMD.
+template <typename T, int VE> struct RawOf;
+template <> struct RawOf<float, 4> { using type = float4; };
+template <> struct RawOf<uint16_t, 8> { using type = uint4; };
+template <> struct RawOf<float, 1> { using type = float; };
+template <> struct RawOf<uint16_t, 1> { using type = uint16_t; };
 
-template <>
-__device__ __forceinline__ void loadv<float, 4>(const float* p, float (&o)[4]) {
-  float4 v = *reinterpret_cast<const float4*>(p);
+template <typename T, int VE>
+__device__ __forceinline__ typename RawOf<T, VE>::type load_raw(const T* p) {
+  return *reinterpret_cast<const typename RawOf<T, VE>::type*>(p);
+}
+__device__ __forceinline__ void decode(const float4& v, float (&o)[4]) {
   o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
 }
-template <>
-__device__ __forceinline__ void loadv<uint16_t, 8>(const uint16_t* p, float (&o)[8]) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void decode(const uint4& v, float (&o)[8]) {
   o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x);
   o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
   o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z);
   o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
 }
-template <>
-__device__ __forceinline__ void loadv<float, 1>(const float* p, float (&o)[1]) { o[0] = *p; }
-template <>
-__device__ __forceinline__ void loadv<uint16_t, 1>(const uint16_t* p, float (&o)[1]) {
-  o[0] = __uint_as_float((uint32_t)(*p) << 16);
+__device__ __forceinline__ void decode(const float& v, float (&o)[1]) { o[0] = v; }
+__device__ __forceinline__ void decode(const uint16_t& v, float (&o)[1]) {
+  o[0] = __uint_as_float((uint32_t)v << 16);
 }
 
 // Outputs and column indices are touched once: non-temporal accesses keep
@@ -219,7 +225,7 @@ __device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, i
     for (int u0 = 0; u0 < nb; u0 += U) {
       int c[U];
       float w[U];
-      float x[U][VE];
+      typename RawOf<T, VE>::type x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         c[u] = __shfl(my_c, slot_base + u0 + u, 64);
@@ -227,30 +233,98 @@ __device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, i
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (u0 + u < nb && f_ok) loadv<T, VE>(Xf + (int64_t)c[u] * p.ldx, x[u]);
+        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(Xf + (int64_t)c[u] * p.ldx);
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (u0 + u < nb && f_ok) st.add(x[u], KIND == K_SUM ? w[u] : 1.0f, c[u]);
+        if (u0 + u < nb && f_ok) {
+          float xv[VE];
+          decode(x[u], xv);
+          st.add(xv, KIND == K_SUM ? w[u] : 1.0f, c[u]);
+        }
     }
   }
 }
 
+// Store one lane group's part of an output row tile (`tile` = the row's first
+// element of this feature tile, `nvalid` = elements of the tile inside F).
+// With VE <= 4 a lane stores its own 16 bytes and one wave store covers whole
+// 128-byte lines.  With VE == 8 a lane owns 32 contiguous bytes: stored
+// directly, each store instruction leaves every line half written, and such
+// rows reach HBM at a third of its write bandwidth.  There the slot's tile is
+// staged in LDS (`stage`, LPR * 8 words of this slot) and stored as 16
+// contiguous bytes per lane.  Called by every lane of the slot.
+template <int LPR, int VE>
+__device__ __forceinline__ void put_tile(float* tile, const float (&v)[VE], int sl, int nvalid,
+                                         float* stage) {
+  if constexpr (VE == 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stage[sl * 8 + i] = v[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = stage[sl * 4 + i];
+      hi[i] = stage[LPR * 4 + sl * 4 + i];
+    }
+    // the stage is rewritten by the next tile only after every lane read it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (sl * 4 < nvalid) storev<4>(tile + sl * 4, lo);
+    if (LPR * 4 + sl * 4 < nvalid) storev<4>(tile + LPR * 4 + sl * 4, hi);
+  } else {
+    if (sl * VE < nvalid) storev<VE>(tile + sl * VE, v);
+  }
+}
+template <int LPR, int VE>
+__device__ __forceinline__ void put_tile_i(int32_t* tile, const int (&v)[VE], int sl, int nvalid,
+                                           float* stage) {
+  if constexpr (VE == 8) {
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __int_as_float(v[i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stage[sl * 8 + i] = f[i];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    int lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = __float_as_int(stage[sl * 4 + i]);
+      hi[i] = __float_as_int(stage[LPR * 4 + sl * 4 + i]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (sl * 4 < nvalid) storei<4>(tile + sl * 4, lo);
+    if (LPR * 4 + sl * 4 < nvalid) storei<4>(tile + LPR * 4 + sl * 4, hi);
+  } else {
+    if (sl * VE < nvalid) storei<VE>(tile + sl * VE, v);
+  }
+}
+
+// Write row `row` of the light path from the slot's state.  `ft0` = first
+// feature of this tile; every lane of the slot takes part.
 template <typename T, int LPR, int VE, int KIND, bool ARG>
-__device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg, int f0,
-                                           State<KIND, VE, ARG>& st) {
+__device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg, int ft0, int sl,
+                                           float* stage, State<KIND, VE, ARG>& st) {
+  const int nvalid = min(LPR * VE, p.F - ft0);
+  const int64_t oy = (int64_t)row * p.ldy + ft0, oa = (int64_t)row * p.F + ft0;
   if constexpr (KIND == K_ALL) {
-    const int64_t oy = (int64_t)row * p.ldy + f0, oa = (int64_t)row * p.F + f0;
     float o[VE];
     int ai[VE];
     if (p.Y) {
 #pragma unroll
       for (int v = 0; v < VE; ++v) o[v] = st.acc[v];
-      storev<VE>(p.Y + oy, o);
+      put_tile<LPR, VE>(p.Y + oy, o, sl, nvalid, stage);
     }
     if (p.Ymean) {
 #pragma unroll
       for (int v = 0; v < VE; ++v) o[v] = deg > 0 ? st.acc[v] / (float)deg : 0.0f;
-      storev<VE>(p.Ymean + oy, o);
+      put_tile<LPR, VE>(p.Ymean + oy, o, sl, nvalid, stage);
     }
     if (p.Ymax) {
 #pragma unroll
@@ -258,8 +332,8 @@ __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg,
         o[v] = deg > 0 ? dev::key_to_float((uint32_t)(st.pk[v] >> 32)) : 0.0f;
         ai[v] = deg > 0 ? (int)~(uint32_t)st.pk[v] : -1;
       }
-      storev<VE>(p.Ymax + oy, o);
-      if (p.argmax) storei<VE>(p.argmax + oa, ai);
+      put_tile<LPR, VE>(p.Ymax + oy, o, sl, nvalid, stage);
+      if (p.argmax) put_tile_i<LPR, VE>(p.argmax + oa, ai, sl, nvalid, stage);
     }
     if (p.Ymin) {
 #pragma unroll
@@ -267,8 +341,8 @@ __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg,
         o[v] = deg > 0 ? dev::key_to_float((uint32_t)(st.pk2[v] >> 32)) : 0.0f;
         ai[v] = deg > 0 ? (int)(uint32_t)st.pk2[v] : -1;
       }
-      storev<VE>(p.Ymin + oy, o);
-      if (p.argmin) storei<VE>(p.argmin + oa, ai);
+      put_tile<LPR, VE>(p.Ymin + oy, o, sl, nvalid, stage);
+      if (p.argmin) put_tile_i<LPR, VE>(p.argmin + oa, ai, sl, nvalid, stage);
     }
     return;
   }
@@ -283,8 +357,8 @@ __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg,
       if constexpr (ARG) ai[v] = deg > 0 ? st.index(v) : -1;
     }
   }
-  storev<VE>(p.Y + (int64_t)row * p.ldy + f0, out);
-  if constexpr (ARG) storei<VE>(p.arg + (int64_t)row * p.F + f0, ai);
+  put_tile<LPR, VE>(p.Y + oy, out, sl, nvalid, stage);
+  if constexpr (ARG) put_tile_i<LPR, VE>(p.arg + oa, ai, sl, nvalid, stage);
 }
 
 template <typename T, int LPR, int VE, int KIND, bool ARG>
@@ -300,6 +374,12 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
   const int f0 = blockIdx.y * FT + sl * VE;
   const bool f_ok = f0 < p.F;
   const T* Xf = reinterpret_cast<const T*>(p.X) + f0;
+  // item workgroups merge their slots here; light workgroups stage output
+  // tiles in the same memory (each array holds at least SPB * FT words)
+  __shared__ float s_acc[(KIND == K_SUM || KIND == K_ALL) ? SPB * FT : 1];
+  __shared__ uint32_t s_key[(KIND == K_MAX || KIND == K_MIN) && !ARG ? SPB * FT : 1];
+  __shared__ unsigned long long s_pk[(KIND == K_ALL || (KIND != K_SUM && ARG)) ? SPB * FT : 1];
+  __shared__ unsigned long long s_pk2[(KIND == K_ALL) ? SPB * FT : 1];
 
   // Item workgroups come first (hardware order spreads them over the XCDs);
   // their count is padded to a multiple of 8 so that the light part starts on
@@ -320,10 +400,6 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
     scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
 
     // merge the slots in LDS, in slot order
-    __shared__ float s_acc[(KIND == K_SUM || KIND == K_ALL) ? SPB * FT : 1];
-    __shared__ uint32_t s_key[(KIND == K_MAX || KIND == K_MIN) && !ARG ? SPB * FT : 1];
-    __shared__ unsigned long long s_pk[(KIND == K_ALL || (KIND != K_SUM && ARG)) ? SPB * FT : 1];
-    __shared__ unsigned long long s_pk2[(KIND == K_ALL) ? SPB * FT : 1];
 #pragma unroll
     for (int v = 0; v < VE; ++v) {
       const int t = sl * VE + v;
@@ -402,17 +478,102 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
     return;
   }
 
-  // ---------------- light rows: one slot per row ----------------
+  // ---------------- light rows: LPR consecutive rows per slot ----------------
+  // The slot's lanes hold one row each: a prefix sum of the light degrees
+  // lays the rows' edges out as one flat sequence, which the slot walks with
+  // U gathers in flight across row boundaries; a row is written when the
+  // walk leaves it.  Rows of the other classes inside the range count as
+  // empty here (their items write them); empty light rows get the identity.
   const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
-  const int64_t row = (int64_t)lb * SPB + slot;
-  if (row >= p.n_rows) return;
-  const int beg = p.row_ptr[row], end = p.row_ptr[row + 1];
-  const int deg = end - beg;
-  if (deg > p.light_max) return;  // handled as an item
+  const int64_t r0 = (int64_t)lb * WG + (int64_t)slot * LPR;
+  if (r0 >= p.n_rows) return;
+  const int ft0 = blockIdx.y * FT;
+  float* stage = ((KIND == K_SUM || KIND == K_ALL) ? s_acc
+                  : (KIND != K_SUM && ARG) ? reinterpret_cast<float*>(s_pk)
+                                           : reinterpret_cast<float*>(s_key)) + slot * FT;
+  const int64_t myr = r0 + sl;
+  int rs = 0, dr = -1;
+  if (myr < p.n_rows) {
+    rs = p.row_ptr[myr];
+    dr = p.row_ptr[myr + 1] - rs;
+  }
+  const bool lt = dr >= 0 && dr <= p.light_max;
+  const int d = lt ? dr : 0;
+  int incl = d;
+#pragma unroll
+  for (int o = 1; o < LPR; o <<= 1) {
+    const int t = __shfl_up(incl, o, LPR);
+    if (sl >= o) incl += t;
+  }
+  const int off = rs - (incl - d);  // edge position of flat index k in this row: off + k
+  const int total = __shfl(incl, slot_base + LPR - 1, 64);
+  {
+    const unsigned long long b = __ballot(lt && dr == 0);
+    unsigned long long em = (LPR == 64) ? b : (b >> slot_base) & ((1ull << (LPR & 63)) - 1);
+    State<KIND, VE, ARG> z;
+    z.init();
+    while (em) {
+      const int t = __builtin_ctzll(em);
+      em &= em - 1;
+      finish_row<T, LPR, VE, KIND, ARG>(p, (int)(r0 + t), 0, ft0, sl, stage, z);
+    }
+  }
   State<KIND, VE, ARG> st;
   st.init();
-  scan_edges<T, LPR, VE, KIND, ARG>(p, beg, end, sl, slot_base, Xf, f_ok, st);
-  if (f_ok) finish_row<T, LPR, VE, KIND, ARG>(p, (int)row, deg, f0, st);
+  int cur = -1;
+  for (int kb = 0; kb < total; kb += LPR) {
+    const int nb = min(LPR, total - kb);
+    const int k = kb + sl;
+    // local row of flat edge k: the number of rows whose inclusive end is <= k
+    int lo = 0;
+#pragma unroll
+    for (int step = LPR / 2; step >= 1; step >>= 1)
+      if (__shfl(incl, slot_base + lo + step - 1, 64) <= k) lo += step;
+    const int my_off = __shfl(off, slot_base + lo, 64);
+    int my_c = 0;
+    float my_w = 1.0f;
+    if (sl < nb) {
+      const int e = my_off + k;
+      my_c = __builtin_nontemporal_load(p.col_idx + e);
+      if (KIND == K_SUM && p.weighted) my_w = edge_weight(p, e, my_c);
+    }
+    for (int u0 = 0; u0 < nb; u0 += U) {
+      int c[U], tr[U];
+      float w[U];
+      typename RawOf<T, VE>::type x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        c[u] = __shfl(my_c, slot_base + u0 + u, 64);
+        tr[u] = __shfl(lo, slot_base + u0 + u, 64);
+        if (KIND == K_SUM) w[u] = p.weighted ? __shfl(my_w, slot_base + u0 + u, 64) : 1.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(Xf + (int64_t)c[u] * p.ldx);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (u0 + u < nb) {
+          if (tr[u] != cur) {  // uniform over the slot
+            if (cur >= 0) {
+              const int dd = __shfl(d, slot_base + cur, 64);
+              finish_row<T, LPR, VE, KIND, ARG>(p, (int)(r0 + cur), dd, ft0, sl, stage, st);
+            }
+            cur = tr[u];
+            st.init();
+          }
+          if (f_ok) {
+            float xv[VE];
+            decode(x[u], xv);
+            st.add(xv, KIND == K_SUM ? w[u] : 1.0f, c[u]);
+          }
+        }
+      }
+    }
+  }
+  if (cur >= 0) {
+    const int dd = __shfl(d, slot_base + cur, 64);
+    finish_row<T, LPR, VE, KIND, ARG>(p, (int)(r0 + cur), dd, ft0, sl, stage, st);
+  }
 }
 
 // Sum of a heavy row's item partials, in item order (deterministic).
@@ -471,11 +632,11 @@ __global__ void k_fill_u64(unsigned long long* p, int64_t n, unsigned long long 
 
 template <typename T, int LPR, int VE, int KIND, bool ARG>
 int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
-  constexpr int SPB = (64 / LPR) * (WG / 64);
   constexpr int FT = LPR * VE;
   const int ftiles = (p.F + FT - 1) / FT;
   p.n_item_blocks = (int32_t)pl->n_items;
-  p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
+  // a light workgroup covers WG rows: 64 / LPR slots per wave, LPR rows per slot
+  p.n_light_blocks = (int32_t)((p.n_rows + WG - 1) / WG);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "aggregate grid too large");
   if (KIND != K_SUM && pl->n_multi > 0) {
