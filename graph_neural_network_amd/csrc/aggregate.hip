@@ -376,9 +376,9 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
   const T* Xf = reinterpret_cast<const T*>(p.X) + f0;
   // item workgroups merge their slots here; light workgroups stage output
   // tiles in the same memory (each array holds at least SPB * FT words)
-  __shared__ float s_acc[(KIND == K_SUM || KIND == K_ALL) ? SPB * FT : 1];
-  __shared__ uint32_t s_key[(KIND == K_MAX || KIND == K_MIN) && !ARG ? SPB * FT : 1];
-  __shared__ unsigned long long s_pk[(KIND == K_ALL || (KIND != K_SUM && ARG)) ? SPB * FT : 1];
+  __shared__ __align__(16) float s_acc[(KIND == K_SUM || KIND == K_ALL) ? SPB * FT : 1];
+  __shared__ __align__(16) uint32_t s_key[(KIND == K_MAX || KIND == K_MIN) && !ARG ? SPB * FT : 1];
+  __shared__ __align__(16) unsigned long long s_pk[(KIND == K_ALL || (KIND != K_SUM && ARG)) ? SPB * FT : 1];
   __shared__ unsigned long long s_pk2[(KIND == K_ALL) ? SPB * FT : 1];
 
   // Item workgroups come first (hardware order spreads them over the XCDs);

@@ -243,15 +243,37 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
   }
 }
 
-template <int VEL>
-__device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int sl, int head,
-                                            const Soft<VEL>& st) {
+// Output row of one slot.  A lane holds VEL consecutive elements; with
+// VEL > 4 a direct store would leave every 128-byte line half written per
+// instruction (such rows reach HBM at a third of its write bandwidth), so the
+// row is staged in LDS (`stage`, LPE * VEL words of this slot) and stored as
+// 16 contiguous bytes per lane.  Called by every lane of the slot.
+template <int LPE, int VEL>
+__device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int sl, int head, bool d_ok,
+                                            const Soft<VEL>& st, float* stage) {
   float o[VEL];
   const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
 #pragma unroll
   for (int k = 0; k < VEL; ++k) o[k] = st.acc[k] * inv;
-  store_row<VEL>(p.out + row * p.row_elems + sl * VEL, o);
-  if (p.lse && (sl % p.lph) == 0)
+  float* dst = p.out + row * p.row_elems;
+  if constexpr (VEL <= 4) {
+    if (d_ok) store_row<VEL>(dst + sl * VEL, o);
+  } else {
+    if (d_ok) store_row<VEL>(stage + sl * VEL, o);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int j = 0; j < VEL / 4; ++j) {
+      const int c = (j * LPE + sl) * 4;
+      const float4 t = *reinterpret_cast<const float4*>(stage + c);
+      if (c < p.row_elems) *reinterpret_cast<float4*>(dst + c) = t;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (p.lse && d_ok && (sl % p.lph) == 0)
     p.lse[row * p.H + head] = st.l > 0.0f ? st.m * kLn2 + logf(st.l) : -INFINITY;
 }
 
@@ -317,15 +339,18 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
   st.init();
   scan_edges<T, LPE, NV, KIND, UU>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, st);
 
+  // s_a merges the waves of an item; light rows stage their output in it
+  // (one LPE x VEL region per slot)
+  __shared__ __align__(16) float s_a[NWAVE][64][VEL];
   if (!is_item) {
-    if (d_ok) write_final<VEL>(p, row, sl, head, st);
+    write_final<LPE, VEL>(p, row, sl, head, d_ok, st, &s_a[wave][slot_base][0]);
     return;
   }
 
   // merge the slots of each wave, then the waves through LDS
 #pragma unroll
   for (int o = LPE; o < 64; o <<= 1) shfl_merge<VEL>(st, o);
-  __shared__ float s_m[NWAVE][LPE], s_l[NWAVE][LPE], s_a[NWAVE][LPE][VEL];
+  __shared__ float s_m[NWAVE][LPE], s_l[NWAVE][LPE];
   if (sw == 0) {
     s_m[wave][sl] = st.m;
     s_l[wave][sl] = st.l;
@@ -341,10 +366,10 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
     for (int k = 0; k < VEL; ++k) a2[k] = s_a[w][sl][k];
     st.merge(s_m[w][sl], s_l[w][sl], a2);
   }
-  if (!d_ok) return;
   if (m_idx < 0) {
-    write_final<VEL>(p, row, sl, head, st);
+    write_final<LPE, VEL>(p, row, sl, head, d_ok, st, &s_a[0][0][0]);
   } else {
+    if (!d_ok) return;
     store_row<VEL>(p.pacc + (int64_t)item * p.row_elems + sl * VEL, st.acc);
     if ((sl % p.lph) == 0) {
       p.pml[((int64_t)item * 2 + 0) * p.H + head] = st.m;

@@ -84,7 +84,9 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
   constexpr int KC = D / 32;   // k-chunks of the score product
   constexpr int MB = D / 16;   // 16-dim blocks of the output
   constexpr int LDV = D + 8;   // padded LDS row (bf16 elements)
+  constexpr int LDO = D + 4;   // padded LDS row of the output stage (floats)
   __shared__ uint16_t s_v[NWAVE][16 * LDV];
+  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
   __shared__ int32_t s_col[MAXT][16];                // the 16 columns of each tile
   __shared__ unsigned long long s_bits[MAXT][4];     // block 0 words 0-1, block 1 words 0-1
 
@@ -100,6 +102,7 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;  // elements per node row
   uint16_t* lv = s_v[wave];
+  float* lo = s_o[wave];
 
   // tile metadata of the window, one cooperative pass
   if (staged) {
@@ -257,14 +260,34 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
         for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(pe, bf((uint16_t)vv[mb][i]), acc[mb][i] * corr);
     }
 
-    if (row_ok) {
+    // Lane (r, g) holds dims mb * 16 + 4g .. +3 of its row: stored directly,
+    // each instruction would write half of every 128-byte line.  Stage the
+    // window's 16 x D head slice in LDS and store whole row slices instead
+    // (256 / D rows per instruction, 16 contiguous bytes per lane).
+    {
       const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-      float* orow = p.out + (int64_t)row * ldr + h * D;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        *reinterpret_cast<float4*>(orow + mb * 16 + 4 * g) =
-            make_float4(acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv);
-      if (p.lse && g == 0)
+        *reinterpret_cast<f32x4*>(lo + r * LDO + mb * 16 + 4 * g) =
+            f32x4{acc[mb][0] * inv, acc[mb][1] * inv, acc[mb][2] * inv, acc[mb][3] * inv};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      constexpr int LPRW = D / 4;        // lanes per row slice
+      constexpr int RPI = 64 / LPRW;     // rows per store instruction
+      const int r0 = lane / LPRW, dd = (lane % LPRW) * 4;
+      const float* lsrc = lo + r0 * LDO + dd;
+      float* odst = p.out + (int64_t)(w * 16 + r0) * ldr + h * D + dd;
+      const int rows_left = p.n_rows - (w * 16 + r0);
+#pragma unroll
+      for (int q = 0; q < 16 / RPI; ++q) {
+        const f32x4 t = *reinterpret_cast<const f32x4*>(lsrc + q * RPI * LDO);
+        if (q * RPI < rows_left) *reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr) = t;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (row_ok && p.lse && g == 0)
         p.lse[(int64_t)row * p.H + h] = lsum > 0.0f ? m * kLn2 + logf(lsum) : -INFINITY;
     }
   }
