@@ -162,6 +162,25 @@ __device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
+// Sum over aligned groups of `lph` lanes (a head's lanes).  Groups up to 16
+// lanes use DPP lane swaps (no LDS round trip): xor 1 and xor 2 inside a quad,
+// then the half-row mirror (lane i <-> 7 - i) and the row mirror
+// (i <-> 15 - i), each of which pairs the lane with the other half of its
+// group once the halves are summed.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float head_sum(float t, int lph) {
+  if (lph > 1) t += dpp<0xB1>(t);   // quad_perm [1, 0, 3, 2]
+  if (lph > 2) t += dpp<0x4E>(t);   // quad_perm [2, 3, 0, 1]
+  if (lph > 4) t += dpp<0x141>(t);  // row_half_mirror
+  if (lph > 8) t += dpp<0x140>(t);  // row_mirror
+  if (lph > 16) t += __shfl_xor(t, 16, 64);
+  if (lph > 32) t += __shfl_xor(t, 32, 64);
+  return t;
+}
+
 // Process edges [eb, ee) of destination `row` for one slot, UU edges in
 // flight.
 //   qv / qraw : this lane's slice of the destination-side vector (GATv2: x_l
@@ -186,7 +205,9 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
       Raw<NV> x[UU];
       Raw<NV> y[UU];
 #pragma unroll
-      for (int u = 0; u < UU; ++u) c[u] = __shfl(my_c, slot_base + u0 + u, 64);
+      for (int u = 0; u < UU; ++u)
+        c[u] = (LPE == 64) ? __builtin_amdgcn_readlane(my_c, u0 + u)  // one slot per wave: scalar
+                           : __shfl(my_c, slot_base + u0 + u, 64);
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
         if (u0 + u < nb && d_ok) {
@@ -219,7 +240,7 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 #pragma unroll
           for (int k = 0; k < VEL; ++k) t = fmaf(qv[k], elem<T, NV>(x[u], k), t);
         }
-        for (int o = 1; o < p.lph; o <<= 1) t += __shfl_xor(t, o, 64);
+        t = head_sum(t, p.lph);
         if constexpr (KIND == K_GT) t *= p.qscale;
         s[u] = (u0 + u < nb) ? t : -INFINITY;
       }
