@@ -21,8 +21,9 @@
 // flight; slots of a wave, waves of a workgroup and chunks of a split row
 // are merged with the same rescaling rule.  Logits live in the log2 domain
 // (log2 e folded into a or into q * scale) so every exponential is exp2.
-//   light rows : one slot per row up to 64 edges (rows in natural order,
-//                XCD-contiguous)
+//   light rows : one slot per row up to 128 edges, rows taken from the
+//                plan's list in order of decreasing length, so that the four
+//                slots of a wave run the same number of steps
 //   items      : one workgroup per longer row or per chunk of a heavy row;
 //                chunks of a heavy row leave partial (m, l, acc) states that a
 //                combine kernel merges in chunk order.
@@ -38,6 +39,10 @@ constexpr int WG = 256;
 #define GNN_ATT_U 4
 #endif
 constexpr float kLog2e = 1.4426950408889634f;
+#ifndef GNN_ATT_LIGHT_MAX
+#define GNN_ATT_LIGHT_MAX 128
+#endif
+constexpr int32_t kAttLightMax = GNN_ATT_LIGHT_MAX;
 constexpr float kLn2 = 0.6931471805599453f;
 
 enum { K_GATV2 = 0, K_GT = 1 };
@@ -59,7 +64,9 @@ struct AttParams {
   int32_t row_elems;  // H * D
   int32_t row_lanes;  // lanes holding data (H * D / VEL)
   int32_t lph;        // lanes per head (power of two)
-  int32_t light_max;
+  int32_t light_max;         // rows of at most this many edges take one slot
+  const int32_t* att_rows;   // those rows, longest first
+  const int32_t* att_count;  // device: how many
   int32_t n_item_blocks;
   int32_t n_light_blocks;
   float slope;        // GATv2 LeakyReLU slope
@@ -331,11 +338,11 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
     ee = min(it.z, eb + per);
   } else {
     const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
-    row = ((int64_t)lb * NWAVE + wave) * SPW + sw;
-    if (row >= p.n_rows) return;
+    const int64_t idx = ((int64_t)lb * NWAVE + wave) * SPW + sw;
+    if (idx >= *p.att_count) return;
+    row = p.att_rows[idx];
     eb = p.row_ptr[row];
     ee = p.row_ptr[row + 1];
-    if (ee - eb > p.light_max) return;  // processed as an item
   }
 
   // destination-side slice (and the attention vector for GATv2)
@@ -484,10 +491,15 @@ int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* l
   p.row_elems = H * D;
   p.row_lanes = lanes;
   p.lph = lph;
-  // attention rows are cheaper per edge than the plan's aggregation rows:
-  // one slot per row up to 64 edges (never below the plan's own threshold,
-  // whose longer rows are the plan's items)
-  p.light_max = std::max(pl->light_max, 64);
+  // One slot per row up to kAttLightMax edges, never below the plan's own
+  // light threshold (its longer rows are the plan's items) and never above
+  // its heavy threshold (split rows go through the items alone).  The rows
+  // are listed longest first, so that the slots of a wave see rows of one
+  // length and finish together.
+  p.light_max = std::max(pl->light_max, std::min(kAttLightMax, pl->heavy_thr));
+  GNN_TRY(plan_att_rows(pl, p.light_max, s));
+  p.att_rows = pl->att_rows;
+  p.att_count = pl->att_count;
   if (pl->n_multi > 0) {
     void* ws = nullptr;
     size_t need = (size_t)pl->n_items * (H * D + 2 * H) * 4;

@@ -86,6 +86,12 @@ struct gnn_plan {
   int64_t n_multi = 0;
   int32_t max_items_per_row = 0;
 
+  // rows of at most att_lmax edges, longest first (built on the first
+  // attention call): one slot per row, equal lengths side by side
+  int32_t* att_rows = nullptr;   // [n_rows]
+  int32_t* att_count = nullptr;  // device: number of listed rows
+  int32_t att_lmax = -1;
+
   // workspace (partials / packed words); grows on demand
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -104,6 +110,7 @@ int plan_alloc(gnn_plan* p, void** ptr, size_t bytes);
 int plan_workspace(gnn_plan* p, size_t bytes, void** out);
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p);
 int plan_build_wsb(gnn_plan* p, hipStream_t s);
+int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
 int check_plan(const gnn_plan* p, const gnn_csr* csr);
 
 // Launchers (host).  All validate nothing: the entry points did.

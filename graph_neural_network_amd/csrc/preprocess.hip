@@ -210,7 +210,74 @@ __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, c
   multi[m] = make_int4((int)i, off, c, 0);
 }
 
+// Sort keys of the attention row list.  Rows of at most lmax edges are
+// ordered by window of 2^kAttWindowBits consecutive rows, then by decreasing
+// length, then by row: waves get rows of one length while the rows a window's
+// workgroups touch stay close (neighbourhoods of nearby rows overlap on
+// clustered graphs).  Longer rows get the top bit and sort behind.
+#ifndef GNN_ATT_WINDOW_BITS
+#define GNN_ATT_WINDOW_BITS 10
+#endif
+constexpr int kAttWindowBits = GNN_ATT_WINDOW_BITS;
+
+__global__ void k_att_keys(const int32_t* row_ptr, int32_t n, int32_t lmax, int wshift, int lbits,
+                           uint64_t* keys, int32_t* count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool listed = false;
+  if (i < n) {
+    const int d = row_ptr[i + 1] - row_ptr[i];
+    listed = d <= lmax;
+    const uint32_t hi = listed ? (((uint32_t)(i >> wshift) << lbits) | (uint32_t)(lmax - d))
+                               : 0x80000000u;
+    keys[i] = ((uint64_t)hi << 32) | (uint64_t)i;
+  }
+  const unsigned long long b = __ballot(listed);
+  if ((threadIdx.x & 63) == 0 && b) atomicAdd(count, (int)__popcll(b));
+}
+
+__global__ void k_att_rows(const uint64_t* keys, int64_t n, int32_t* rows) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) rows[i] = (int32_t)(uint32_t)keys[i];
+}
+
 }  // namespace
+
+int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
+  if (p->att_lmax == lmax) return GNN_OK;
+  const int32_t n = p->n_rows;
+  if (!p->att_rows) {
+    GNN_TRY(plan_alloc(p, (void**)&p->att_rows, (size_t)std::max(n, 1) * 4));
+    GNN_TRY(plan_alloc(p, (void**)&p->att_count, 16));
+  }
+  GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));
+  if (n > 0) {
+    uint64_t *keys = nullptr, *tmp = nullptr;
+    GNN_HIP(hipMallocAsync((void**)&keys, (size_t)n * 8, s));
+    GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)n * 8, s));
+    const unsigned nb = (unsigned)((n + 255) / 256);
+    // high word: window index above lbits of (lmax - length); the top bit
+    // marks unlisted rows.  Windows widen if both fields would not fit 31 bits.
+    auto bits_of = [](int64_t v) { int b = 0; while (v >> b) ++b; return b; };
+    const int lbits = std::max(1, bits_of(lmax));
+    int wshift = kAttWindowBits;
+    while (bits_of((int64_t)(n - 1) >> wshift) + lbits > 31) ++wshift;
+    const int wbits = bits_of((int64_t)(n - 1) >> wshift);
+    hipLaunchKernelGGL(k_att_keys, dim3(nb), dim3(256), 0, s, p->row_ptr, n, lmax, wshift, lbits, keys,
+                       p->att_count);
+    GNN_LAUNCH_CHECK("attention row keys");
+    int rc = radix_sort_u64(keys, tmp, n, 32, 32 + lbits + wbits, s);
+    if (rc == GNN_OK) rc = radix_sort_u64(keys, tmp, n, 63, 64, s);
+    if (rc == GNN_OK) {
+      hipLaunchKernelGGL(k_att_rows, dim3(nb), dim3(256), 0, s, keys, (int64_t)n, p->att_rows);
+      if (hipGetLastError() != hipSuccess) rc = fail(GNN_ERR_DEVICE, "attention row list launch failed");
+    }
+    GNN_HIP(hipFreeAsync(keys, s));
+    GNN_HIP(hipFreeAsync(tmp, s));
+    if (rc != GNN_OK) return rc;
+  }
+  p->att_lmax = lmax;
+  return GNN_OK;
+}
 
 int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s) {
   int64_t nb = (n + kScanTile - 1) / kScanTile;
