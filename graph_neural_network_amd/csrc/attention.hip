@@ -39,6 +39,10 @@ constexpr int WG = 256;
 #define GNN_ATT_U 4
 #endif
 constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on v_exp_f32 alone.  Softmax arguments are <= 0 (differences from the
+// running maximum), and results below 2^-126 of the maximum, which the
+// hardware may flush to zero, do not change any sum at fp32 precision.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 #ifndef GNN_ATT_LIGHT_MAX
 #define GNN_ATT_LIGHT_MAX 128
 #endif
@@ -126,7 +130,7 @@ struct Soft {
   __device__ __forceinline__ void merge(float m2, float l2, const float (&a2)[VEL]) {
     const float mn = fmaxf(m, m2);
     if (mn == -INFINITY) return;  // both empty
-    const float c1 = exp2f(m - mn), c2 = exp2f(m2 - mn);
+    const float c1 = ex2(m - mn), c2 = ex2(m2 - mn);
     l = l * c1 + l2 * c2;
 #pragma unroll
     for (int k = 0; k < VEL; ++k) acc[k] = acc[k] * c1 + a2[k] * c2;
@@ -169,7 +173,7 @@ __device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 
-// Sum over aligned groups of `lph` lanes (a head's lanes).  Groups up to 16
+// Sum over aligned groups of LPH lanes (a head's lanes).  Groups up to 16
 // lanes use DPP lane swaps (no LDS round trip): xor 1 and xor 2 inside a quad,
 // then the half-row mirror (lane i <-> 7 - i) and the row mirror
 // (i <-> 15 - i), each of which pairs the lane with the other half of its
@@ -178,13 +182,14 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-__device__ __forceinline__ float head_sum(float t, int lph) {
-  if (lph > 1) t += dpp<0xB1>(t);   // quad_perm [1, 0, 3, 2]
-  if (lph > 2) t += dpp<0x4E>(t);   // quad_perm [2, 3, 0, 1]
-  if (lph > 4) t += dpp<0x141>(t);  // row_half_mirror
-  if (lph > 8) t += dpp<0x140>(t);  // row_mirror
-  if (lph > 16) t += __shfl_xor(t, 16, 64);
-  if (lph > 32) t += __shfl_xor(t, 32, 64);
+template <int LPH>
+__device__ __forceinline__ float head_sum(float t) {
+  if constexpr (LPH > 1) t += dpp<0xB1>(t);   // quad_perm [1, 0, 3, 2]
+  if constexpr (LPH > 2) t += dpp<0x4E>(t);   // quad_perm [2, 3, 0, 1]
+  if constexpr (LPH > 4) t += dpp<0x141>(t);  // row_half_mirror
+  if constexpr (LPH > 8) t += dpp<0x140>(t);  // row_mirror
+  if constexpr (LPH > 16) t += __shfl_xor(t, 16, 64);
+  if constexpr (LPH > 32) t += __shfl_xor(t, 32, 64);
   return t;
 }
 
@@ -194,7 +199,7 @@ __device__ __forceinline__ float head_sum(float t, int lph) {
 //               as float; GT: q, raw, its scale * log2 e applied after the
 //               head reduction)
 //   av        : GATv2 attention-vector slice times log2 e (unused for GT)
-template <typename T, int LPE, int NV, int KIND, int UU>
+template <typename T, int LPE, int NV, int KIND, int UU, int LPH>
 __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, int sl, int slot_base,
                                            bool d_ok, const float (&qv)[(16 / sizeof(T)) * NV],
                                            const Raw<NV>& qraw,
@@ -247,20 +252,20 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 #pragma unroll
           for (int k = 0; k < VEL; ++k) t = fmaf(qv[k], elem<T, NV>(x[u], k), t);
         }
-        t = head_sum(t, p.lph);
+        t = head_sum<LPH>(t);
         if constexpr (KIND == K_GT) t *= p.qscale;
         s[u] = (u0 + u < nb) ? t : -INFINITY;
       }
       float mn = st.m;
 #pragma unroll
       for (int u = 0; u < UU; ++u) mn = fmaxf(mn, s[u]);
-      const float corr = exp2f(st.m - mn);
+      const float corr = ex2(st.m - mn);
       st.l *= corr;
 #pragma unroll
       for (int k = 0; k < VEL; ++k) st.acc[k] *= corr;
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
-        const float pu = exp2f(s[u] - mn);
+        const float pu = ex2(s[u] - mn);
         st.l += pu;
 #pragma unroll
         for (int k = 0; k < VEL; ++k)
@@ -276,7 +281,7 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 // instruction (such rows reach HBM at a third of its write bandwidth), so the
 // row is staged in LDS (`stage`, LPE * VEL words of this slot) and stored as
 // 16 contiguous bytes per lane.  Called by every lane of the slot.
-template <int LPE, int VEL>
+template <int LPE, int VEL, int LPH>
 __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int sl, int head, bool d_ok,
                                             const Soft<VEL>& st, float* stage) {
   float o[VEL];
@@ -301,11 +306,11 @@ __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (p.lse && d_ok && (sl % p.lph) == 0)
+  if (p.lse && d_ok && (sl % LPH) == 0)
     p.lse[row * p.H + head] = st.l > 0.0f ? st.m * kLn2 + logf(st.l) : -INFINITY;
 }
 
-template <typename T, int LPE, int NV, int KIND, int UU>
+template <typename T, int LPE, int NV, int KIND, int UU, int LPH>
 __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;  // elements per lane
   constexpr int SPW = 64 / LPE;
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
   const int sw = lane / LPE, sl = lane % LPE;
   const int slot_base = sw * LPE;
   const bool d_ok = sl < p.row_lanes;
-  const int head = d_ok ? sl / p.lph : 0;
+  const int head = d_ok ? sl / LPH : 0;
 
   const int n_item_pad = (p.n_item_blocks + 7) & ~7;
   const bool is_item = (int)blockIdx.x < n_item_pad;
@@ -365,13 +370,13 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
 
   Soft<VEL> st;
   st.init();
-  scan_edges<T, LPE, NV, KIND, UU>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, st);
+  scan_edges<T, LPE, NV, KIND, UU, LPH>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, st);
 
   // s_a merges the waves of an item; light rows stage their output in it
   // (one LPE x VEL region per slot)
   __shared__ __align__(16) float s_a[NWAVE][64][VEL];
   if (!is_item) {
-    write_final<LPE, VEL>(p, row, sl, head, d_ok, st, &s_a[wave][slot_base][0]);
+    write_final<LPE, VEL, LPH>(p, row, sl, head, d_ok, st, &s_a[wave][slot_base][0]);
     return;
   }
 
@@ -395,11 +400,11 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
     st.merge(s_m[w][sl], s_l[w][sl], a2);
   }
   if (m_idx < 0) {
-    write_final<LPE, VEL>(p, row, sl, head, d_ok, st, &s_a[0][0][0]);
+    write_final<LPE, VEL, LPH>(p, row, sl, head, d_ok, st, &s_a[0][0][0]);
   } else {
     if (!d_ok) return;
     store_row<VEL>(p.pacc + (int64_t)item * p.row_elems + sl * VEL, st.acc);
-    if ((sl % p.lph) == 0) {
+    if ((sl % LPH) == 0) {
       p.pml[((int64_t)item * 2 + 0) * p.H + head] = st.m;
       p.pml[((int64_t)item * 2 + 1) * p.H + head] = st.l;
     }
@@ -420,7 +425,7 @@ __global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* mu
       const float a2 = p.pacc[it * p.row_elems + t];
       const float mn = fmaxf(m, m2);
       if (mn == -INFINITY) continue;
-      const float c1 = exp2f(m - mn), c2 = exp2f(m2 - mn);
+      const float c1 = ex2(m - mn), c2 = ex2(m2 - mn);
       l = l * c1 + l2 * c2;
       a = a * c1 + a2 * c2;
       m = mn;
@@ -430,15 +435,15 @@ __global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* mu
   }
 }
 
-template <typename T, int LPE, int NV, int KIND>
-int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
+template <typename T, int LPE, int NV, int KIND, int LPH>
+int launch_att_h(gnn_plan* pl, AttParams& p, hipStream_t s) {
   constexpr int UU = GNN_ATT_U;
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.n_item_blocks = (int32_t)pl->n_items;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
-  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND, UU>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND, UU, LPH>), dim3((unsigned)gx), dim3(WG), 0, s, p);
   GNN_LAUNCH_CHECK("attention");
   if (pl->n_multi > 0) {
     hipLaunchKernelGGL(k_att_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
@@ -446,6 +451,22 @@ int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
     GNN_LAUNCH_CHECK("attention combine");
   }
   return GNN_OK;
+}
+
+// lanes per head is a power of two no larger than the slot
+template <typename T, int LPE, int NV, int KIND>
+int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
+  switch (p.lph) {
+    case 1: return launch_att_h<T, LPE, NV, KIND, 1>(pl, p, s);
+    case 2: return launch_att_h<T, LPE, NV, KIND, 2>(pl, p, s);
+    case 4: return launch_att_h<T, LPE, NV, KIND, 4>(pl, p, s);
+    case 8: return launch_att_h<T, LPE, NV, KIND, 8>(pl, p, s);
+    default: break;
+  }
+  if constexpr (LPE >= 16) if (p.lph == 16) return launch_att_h<T, LPE, NV, KIND, 16>(pl, p, s);
+  if constexpr (LPE >= 32) if (p.lph == 32) return launch_att_h<T, LPE, NV, KIND, 32>(pl, p, s);
+  if constexpr (LPE >= 64) if (p.lph == 64) return launch_att_h<T, LPE, NV, KIND, 64>(pl, p, s);
+  return fail(GNN_ERR_UNSUPPORTED, "lanes per head exceed the slot");
 }
 
 template <typename T, int KIND>

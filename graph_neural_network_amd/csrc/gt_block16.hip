@@ -36,6 +36,10 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr float kLn2 = 0.6931471805599453f;
+// 2^x on v_exp_f32 alone: every argument is a difference from the running
+// maximum (<= 0), and results below 2^-126 of it, which the hardware may
+// flush to zero, do not change any sum at fp32 precision.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 struct B16Params {
   const uint16_t* q;
@@ -179,10 +183,10 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
       uint16_t pb[4];
       float rs = 0.0f;
       if (mn != -INFINITY) {
-        corr = exp2f(m - mn);
+        corr = ex2(m - mn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[i] = f2bf_rne(exp2f(s[i] - mn));
+          pb[i] = f2bf_rne(ex2(s[i] - mn));
           rs += bf(pb[i]);
         }
       } else {
@@ -250,8 +254,8 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
       dot += __shfl_xor(dot, 32, 64);
       const float sc = dot * p.scale_log2;
       const float mn = fmaxf(m, sc);
-      const float corr = exp2f(m - mn);
-      const float pe = exp2f(sc - mn);
+      const float corr = ex2(m - mn);
+      const float pe = ex2(sc - mn);
       lsum = lsum * corr + pe;
       m = mn;
 #pragma unroll
