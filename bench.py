@@ -200,7 +200,7 @@ def wl_gatv2(args):
 
     cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)+self-loops", "nodes": n, "edges": m,
            "heads": H, "head_dim": D, "x_dtype": "bf16", "plan": gnn.gnn_plan_stats(plan)}
-    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 1, 0, 4>",
+    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 1, 0, 4, 4>",
             "config": cfg, "dtype": "bf16", "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse)}
 
 
@@ -243,7 +243,7 @@ def wl_gt(args, mode="csr"):
     cfg = {"workload": w.name + ("_block16" if mode == "block16" else "_csr"), "graph": "cluster(64, 0.5, 1%)+self-loops",
            "nodes": n, "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16", "mode": mode,
            "plan_build_ms": round(plan_ms, 2), "plan": st}
-    kern = "k_attention<unsigned short, 64, 1, 1, 4>" if mode == "csr" else "k_gt_block16<64, 2>"
+    kern = "k_attention<unsigned short, 64, 1, 1, 4, 8>" if mode == "csr" else "k_gt_block16<64, 2>"
     return {"ops": ops, "dominant": "gt", "kernel": kern, "config": cfg, "dtype": "bf16", "cpu": cpu,
             "keep": (w, csr, plan, q, k, v, out, lse)}
 
