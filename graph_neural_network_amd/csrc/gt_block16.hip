@@ -83,8 +83,12 @@ __device__ __forceinline__ float dot8(const s16x8& a, const s16x8& b, float acc)
 
 constexpr int MAXT = 32;  // tiles of a window staged in LDS (larger windows read metadata directly)
 
+// Latency decides this kernel's speed (each wave keeps one tile of K / V in
+// flight while it computes another), so D <= 64 asks for four waves per SIMD
+// (at most 128 VGPRs) rather than the three its natural allocation allows.
 template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) void k_gt_block16(B16Params p) {
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 1)))
+void k_gt_block16(B16Params p) {
   constexpr int KC = D / 32;   // k-chunks of the score product
   constexpr int MB = D / 16;   // 16-dim blocks of the output
   constexpr int LDV = D + 8;   // padded LDS row (bf16 elements)
