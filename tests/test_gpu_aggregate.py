@@ -86,7 +86,8 @@ def rmat_small():
 
 
 @pytest.mark.parametrize("F,dt", [(64, "f32"), (128, "f32"), (100, "f32"), (200, "f32"), (37, "f32"),
-                                  (600, "f32"), (256, "bf16"), (64, "bf16"), (40, "bf16"), (13, "bf16")])
+                                  (600, "f32"), (256, "bf16"), (64, "bf16"), (40, "bf16"), (13, "bf16"),
+                                  (1200, "bf16")])
 @pytest.mark.parametrize("planned", [False, True])
 def test_spmm_rmat_widths(rmat_small, F, dt, planned):
     rp, ci = rmat_small
@@ -142,7 +143,8 @@ def test_spmm_strided_and_rectangular():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("op", ["sum", "mean", "max", "min"])
-@pytest.mark.parametrize("F,dt", [(128, "f32"), (64, "f32"), (37, "f32"), (256, "bf16")])
+@pytest.mark.parametrize("F,dt", [(128, "f32"), (64, "f32"), (37, "f32"), (256, "bf16"), (40, "bf16"),
+                                  (200, "bf16")])
 def test_reduce_rmat_small(rmat_small, op, F, dt):
     rp, ci = rmat_small
     n = rp.size - 1
@@ -300,7 +302,7 @@ def _multi_vs_separate(csr, Xd, plan, F, rows_check=None, ref=None):
     return out
 
 
-@pytest.mark.parametrize("F,dt", [(128, "f32"), (37, "f32"), (256, "bf16")])
+@pytest.mark.parametrize("F,dt", [(128, "f32"), (37, "f32"), (256, "bf16"), (40, "bf16"), (200, "bf16")])
 def test_reduce_multi_matches_separate_and_oracle(rmat_small, F, dt):
     rp, ci = rmat_small
     n = rp.size - 1
@@ -315,6 +317,50 @@ def test_reduce_multi_matches_separate_and_oracle(rmat_small, F, dt):
         out = _multi_vs_separate(csr, Xd, plan, F)
         for op in ("sum", "mean", "max", "min"):
             check_reduce(rp, ci, Xo, host(out[op]), host(out["arg" + op]) if op in ("max", "min") else None, op)
+
+
+@pytest.mark.parametrize("light_max", [1, 64, 1000])
+@pytest.mark.parametrize("F,dt", [(128, "f32"), (256, "bf16")])
+def test_light_threshold_extremes(rmat_small, light_max, F, dt):
+    """Light rows are walked LPR rows per slot as one edge sequence: a light
+    threshold of 1 leaves almost every row to the items, 1000 sends every row
+    (hubs included) through the walk."""
+    rp, ci = rmat_small
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, light_max_deg=light_max, heavy_quantile=-1.0)
+    if dt == "f32":
+        Xh = gen.gauss_f32(31, (n, F))
+        Xd, Xo = dev(Xh), Xh
+    else:
+        Xb = gen.gauss_bf16(31, (n, F))
+        Xd, Xo = dev_bf16(Xb), gen.bf16_to_f32(Xb)
+    out = gnn.gnn_reduce_multi(csr, Xd, plan=plan)
+    for op in ("sum", "mean", "max", "min"):
+        check_reduce(rp, ci, Xo, host(out[op]), host(out["arg" + op]) if op in ("max", "min") else None, op)
+    Y = host(gnn.gnn_spmm(csr, Xd, "both", plan=plan))
+    ref, mag = oracle.spmm(rp, ci, Xo, "both")
+    assert scaled_err(Y, ref, mag) <= TOL
+
+
+def test_light_walk_runs_of_empty_rows():
+    """Long runs of empty rows between short rows, so slots see many rows
+    with no edges, rows whose edges straddle column batches, and a tail
+    shorter than one workgroup of rows."""
+    n = 5000
+    rng = np.random.default_rng(5)
+    deg = np.zeros(n, np.int64)
+    nz = rng.choice(n, 700, replace=False)
+    deg[nz] = rng.integers(1, 33, nz.size)
+    dst = np.repeat(np.arange(n), deg)
+    src = rng.integers(0, n, dst.size)
+    rp, ci = gen.from_edges(n, src, dst)
+    csr = dev_csr(rp, ci)
+    Xb = gen.gauss_bf16(6, (n, 256))
+    Xd, Xo = dev_bf16(Xb), gen.bf16_to_f32(Xb)
+    out = gnn.gnn_reduce_multi(csr, Xd)
+    for op in ("sum", "mean", "max", "min"):
+        check_reduce(rp, ci, Xo, host(out[op]), host(out["arg" + op]) if op in ("max", "min") else None, op)
 
 
 def test_reduce_multi_subsets_and_empty_rows():

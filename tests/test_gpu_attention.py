@@ -131,6 +131,29 @@ def test_gt_special_cases(rmat_loops):
     check(host(out), host(lse), ro, rl, va, tol=TOL)
 
 
+@pytest.mark.parametrize("opts", [dict(light_max_deg=150), dict(light_max_deg=1, chunk_edges=16),
+                                  dict(heavy_quantile=-1.0)])
+def test_attention_plan_thresholds(rmat_loops, opts):
+    """One-slot rows come from the plan's length-sorted list: its bound
+    follows the plan's light threshold when that is larger, stops below
+    split rows when chunks are small, and covers everything below 128 edges
+    when nothing is split."""
+    rp, ci = rmat_loops
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, **opts)
+    H, D = 4, 32
+    xl, xr = gen.gauss_bf16(41, (n, H, D)), gen.gauss_bf16(42, (n, H, D))
+    att = gen.gauss_f32(43, (H, D), std=(1.0 / D) ** 0.5)
+    out, lse = gnn.gnn_gatv2_fused(csr, dev_bf16(xl), dev_bf16(xr), dev(att), 0.2, plan=plan)
+    ro, rl, va = oracle.gatv2(rp, ci, xl, xr, att, 0.2)
+    check(host(out), host(lse), ro, rl, va)
+    q, k, v = bf16_inputs(n, H, D, 44, 3)
+    out, lse = gnn.gnn_gt_fused(csr, dev_bf16(q), dev_bf16(k), dev_bf16(v), plan=plan)
+    ro, rl, va = oracle.gt(rp, ci, q, k, v)
+    check(host(out), host(lse), ro, rl, va)
+
+
 def test_attention_single_edge_and_empty_rows():
     # row 0 <- {2}; row 1 empty; rows 2.. <- {0, 1}; plus a hub row
     n = 3000
