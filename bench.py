@@ -34,12 +34,27 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "aggregation edges/s and achieved HBM GB/s (% of 8 TB/s) at F=128, 1 GPU"
 
 
-def kernel_source_hash() -> str:
+# sources that decide each workload's dominant kernel and the plan it reads
+_COMMON = ("gnn_internal.h", "api.hip", "preprocess.hip")
+SOURCES = {
+    "reduce_f128": _COMMON + ("aggregate.hip",),
+    "gcn_small": _COMMON + ("aggregate.hip",),
+    "spmm_large": _COMMON + ("aggregate.hip",),
+    "gatv2": _COMMON + ("attention.hip", "sort.hip"),
+    "gt_csr": _COMMON + ("attention.hip", "sort.hip"),
+    "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
+    "copy": ("gnn_internal.h", "api.hip", "util.hip"),
+}
+
+
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources behind a workload's dominant kernel: a stored
+    counter profile stays valid while none of them changes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "graph_neural_network_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in sorted(SOURCES[workload]):
+        h.update(f.encode())
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -53,7 +68,7 @@ def load_traffic(workload: str, kernel: str):
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(workload):
         return None
     return d.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
 
