@@ -158,34 +158,64 @@ __global__ __launch_bounds__(256) void k_quantile(const int32_t* hist, int32_t n
   if (threadIdx.x == 0) *out = found;
 }
 
-__global__ void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max, int32_t thr,
-                           int32_t chunk, int32_t* cnt, int32_t* is_multi,
-                           unsigned long long* stats /* light, medium, heavy, max_chunks */) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Row classes.  Each workgroup writes its (light, medium, heavy, max chunks)
+// totals to part[blockIdx.x]; k_stats_total folds them.  (One atomic per wave
+// on four shared counters serialises at the L2 on large graphs.)
+__global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max,
+                                                  int32_t thr, int32_t chunk, int32_t* cnt,
+                                                  int32_t* is_multi, unsigned long long* part) {
+  __shared__ unsigned long long ws[4][4];
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int c = 0;
   if (i < n) {
-    int d = row_ptr[i + 1] - row_ptr[i];
+    const int d = row_ptr[i + 1] - row_ptr[i];
     if (d <= light_max) c = 0;
     else if (d <= thr) c = 1;
     else c = (d + chunk - 1) / chunk;
     cnt[i] = c;
     is_multi[i] = c > 1 ? 1 : 0;
   }
-  // block totals, one atomic each
-  unsigned long long l = (i < n && c == 0), m = (i < n && c == 1), h = (i < n && c > 1);
-  for (int d = 32; d >= 1; d >>= 1) {
-    l += __shfl_xor(l, d);
-    m += __shfl_xor(m, d);
-    h += __shfl_xor(h, d);
-  }
+  const unsigned long long l = __popcll(__ballot(i < n && c == 0));
+  const unsigned long long m = __popcll(__ballot(i < n && c == 1));
+  const unsigned long long h = __popcll(__ballot(i < n && c > 1));
   int cm = c;
   for (int d = 32; d >= 1; d >>= 1) cm = max(cm, __shfl_xor(cm, d));
+  const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    if (l) atomicAdd(&stats[0], l);
-    if (m) atomicAdd(&stats[1], m);
-    if (h) atomicAdd(&stats[2], h);
-    atomicMax(&stats[3], (unsigned long long)cm);
+    ws[wave][0] = l;
+    ws[wave][1] = m;
+    ws[wave][2] = h;
+    ws[wave][3] = (unsigned long long)cm;
   }
+  __syncthreads();
+  if (threadIdx.x < 4) {
+    unsigned long long v = 0;
+    for (int w = 0; w < 4; ++w)
+      v = threadIdx.x == 3 ? (ws[w][3] > v ? ws[w][3] : v) : v + ws[w][threadIdx.x];
+    part[(int64_t)blockIdx.x * 4 + threadIdx.x] = v;
+  }
+}
+
+// Sum (the first three words) and maximum (the fourth) of nb partials.
+__global__ __launch_bounds__(256) void k_stats_total(const unsigned long long* part, int64_t nb,
+                                                     unsigned long long* stats) {
+  __shared__ unsigned long long red[4][256];
+  unsigned long long a[4] = {0, 0, 0, 0};
+  for (int64_t b = threadIdx.x; b < nb; b += blockDim.x) {
+    for (int k = 0; k < 3; ++k) a[k] += part[b * 4 + k];
+    a[3] = part[b * 4 + 3] > a[3] ? part[b * 4 + 3] : a[3];
+  }
+  for (int k = 0; k < 4; ++k) red[k][threadIdx.x] = a[k];
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if ((int)threadIdx.x < o) {
+      for (int k = 0; k < 3; ++k) red[k][threadIdx.x] += red[k][threadIdx.x + o];
+      red[3][threadIdx.x] = red[3][threadIdx.x + o] > red[3][threadIdx.x] ? red[3][threadIdx.x + o]
+                                                                          : red[3][threadIdx.x];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x < 4) stats[threadIdx.x] = red[threadIdx.x][0];
 }
 
 __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, const int32_t* cnt,
@@ -221,18 +251,27 @@ __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, c
 constexpr int kAttWindowBits = GNN_ATT_WINDOW_BITS;
 
 __global__ void k_att_keys(const int32_t* row_ptr, int32_t n, int32_t lmax, int wshift, int lbits,
-                           uint64_t* keys, int32_t* count) {
+                           uint64_t* keys) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool listed = false;
   if (i < n) {
     const int d = row_ptr[i + 1] - row_ptr[i];
-    listed = d <= lmax;
-    const uint32_t hi = listed ? (((uint32_t)(i >> wshift) << lbits) | (uint32_t)(lmax - d))
-                               : 0x80000000u;
+    const uint32_t hi = d <= lmax ? (((uint32_t)(i >> wshift) << lbits) | (uint32_t)(lmax - d))
+                                  : 0x80000000u;
     keys[i] = ((uint64_t)hi << 32) | (uint64_t)i;
   }
-  const unsigned long long b = __ballot(listed);
-  if ((threadIdx.x & 63) == 0 && b) atomicAdd(count, (int)__popcll(b));
+}
+
+// Number of listed rows: the position of the first sorted key with the top
+// bit set (binary search by one thread).
+__global__ void k_att_count(const uint64_t* keys, int64_t n, int32_t* count) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (keys[mid] >> 63) hi = mid;
+    else lo = mid + 1;
+  }
+  *count = (int32_t)lo;
 }
 
 __global__ void k_att_rows(const uint64_t* keys, int64_t n, int32_t* rows) {
@@ -249,7 +288,7 @@ int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
     GNN_TRY(plan_alloc(p, (void**)&p->att_rows, (size_t)std::max(n, 1) * 4));
     GNN_TRY(plan_alloc(p, (void**)&p->att_count, 16));
   }
-  GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));
+  GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));  // stays 0 for an empty graph
   if (n > 0) {
     uint64_t *keys = nullptr, *tmp = nullptr;
     GNN_HIP(hipMallocAsync((void**)&keys, (size_t)n * 8, s));
@@ -262,13 +301,13 @@ int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
     int wshift = kAttWindowBits;
     while (bits_of((int64_t)(n - 1) >> wshift) + lbits > 31) ++wshift;
     const int wbits = bits_of((int64_t)(n - 1) >> wshift);
-    hipLaunchKernelGGL(k_att_keys, dim3(nb), dim3(256), 0, s, p->row_ptr, n, lmax, wshift, lbits, keys,
-                       p->att_count);
+    hipLaunchKernelGGL(k_att_keys, dim3(nb), dim3(256), 0, s, p->row_ptr, n, lmax, wshift, lbits, keys);
     GNN_LAUNCH_CHECK("attention row keys");
     int rc = radix_sort_u64(keys, tmp, n, 32, 32 + lbits + wbits, s);
     if (rc == GNN_OK) rc = radix_sort_u64(keys, tmp, n, 63, 64, s);
     if (rc == GNN_OK) {
       hipLaunchKernelGGL(k_att_rows, dim3(nb), dim3(256), 0, s, keys, (int64_t)n, p->att_rows);
+      hipLaunchKernelGGL(k_att_count, dim3(1), dim3(64), 0, s, keys, (int64_t)n, p->att_count);
       if (hipGetLastError() != hipSuccess) rc = fail(GNN_ERR_DEVICE, "attention row list launch failed");
     }
     GNN_HIP(hipFreeAsync(keys, s));
@@ -386,12 +425,15 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   GNN_HIP(hipMallocAsync((void**)&ism, nn * 4, s));
   GNN_HIP(hipMallocAsync((void**)&ioff, (nn + 1) * 4, s));
   GNN_HIP(hipMallocAsync((void**)&moff, (nn + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&stats, 4 * 8, s));
-  GNN_HIP(hipMemsetAsync(stats, 0, 4 * 8, s));
+  const int64_t ncb = std::max<int64_t>((n + 255) / 256, 1);
+  GNN_HIP(hipMallocAsync((void**)&stats, (4 + ncb * 4) * 8, s));
+  GNN_HIP(hipMemsetAsync(stats, 0, (4 + ncb * 4) * 8, s));
   if (n > 0) {
-    hipLaunchKernelGGL(k_classify, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p->row_ptr, n,
-                       p->light_max, p->heavy_thr, p->chunk_edges, cnt, ism, stats);
+    hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max,
+                       p->heavy_thr, p->chunk_edges, cnt, ism, stats + 4);
     GNN_LAUNCH_CHECK("classify");
+    hipLaunchKernelGGL(k_stats_total, dim3(1), dim3(256), 0, s, stats + 4, ncb, stats);
+    GNN_LAUNCH_CHECK("classify totals");
   }
   GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
   GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
