@@ -44,6 +44,9 @@ SOURCES = {
     "gt_csr": _COMMON + ("attention.hip", "sort.hip"),
     "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
     "copy": ("gnn_internal.h", "api.hip", "util.hip"),
+    "plan_cfg2": _COMMON,
+    "wsb_cfg4": _COMMON + ("wsb.hip", "sort.hip"),
+    "reorder_cfg5": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
 }
 
 
@@ -343,9 +346,127 @@ def wl_gcn_small(args):
             "dtype": "f32", "cpu": cpu, "keep": (w, X, csr, plan, Y)}
 
 
+# ---------------------------------------------------------------------------
+# preprocessing rows: plan (degrees, bins, items), WSB build, reordering.
+# One op is one whole library call (all its kernels, allocations and host
+# synchronisations); the roofline charges the compulsory bytes of the call
+# (each input array read once, each output written once) to its duration.
+# ---------------------------------------------------------------------------
+
+def _edges_rate(fn, edges, label, sample):
+    import oracle
+    t0 = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t0
+    return {"value": edges / dt, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{sample}, {label}, {dt:.1f} s"}
+
+
+def wl_plan(args):
+    """Plan build (degrees, degree bins, chunk items) on R-MAT 1,000,000 nodes / 16,000,000 edges."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.reduce_rmat(with_x=False)
+    n, m = w.n, w.nnz
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    st = gnn.gnn_plan_stats(gnn.gnn_plan_create(csr))
+
+    def make():
+        gnn.gnn_plan_create(csr).destroy()
+
+    # read row_ptr and col_idx; write deg_out and the items (16 B) and split-row records (16 B)
+    b = 4 * (n + 1) + 4 * m + 4 * n + 16 * st["items"]
+    ops = [Op("plan", make, m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        return _edges_rate(lambda: oracle.degrees(w.row_ptr, w.col_idx), m, "in- and out-degrees",
+                           "the whole graph")
+
+    cfg = {"workload": "plan_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
+           "plan": st}
+    return {"ops": ops, "dominant": "plan", "kernel": "gnn_plan_create (all kernels)", "config": cfg,
+            "dtype": "int32", "cpu": cpu, "keep": (w, csr)}
+
+
+def wl_wsb(args):
+    """WSB build: 16-row windows, 8-column blocks, 16 x 16 tiles and the residual CSR on the
+    cluster graph of 512,000 nodes (64-node clusters); timed as plan with WSB minus plan alone."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gt_cluster(with_x=False)
+    n, m = w.n, w.nnz
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    st = gnn.gnn_plan_stats(gnn.gnn_plan_create(csr, build_wsb=True))
+
+    def with_wsb():
+        gnn.gnn_plan_create(csr, build_wsb=True).destroy()
+
+    def plain():
+        gnn.gnn_plan_create(csr).destroy()
+
+    nw, nb, nt, nr = st["wsb_windows"], st["wsb_blocks"], st["wsb_dense_tiles"], st["wsb_residual_edges"]
+    # read the CSR; write window pointers, block columns (32 B) and bitmaps (16 B), tile
+    # pointers and tile blocks, residual row pointers and columns
+    b_wsb = 4 * (n + 1) + 4 * m + 4 * (nw + 1) + 48 * nb + 4 * (nw + 1) + 4 * nt + 4 * (n + 1) + 4 * nr
+    ops = [Op("plan_wsb", with_wsb, m, b_wsb), Op("plan", plain, 0, 0)]
+
+    def cpu(budget_s):
+        import oracle
+        return _edges_rate(lambda: oracle.wsb_build(w.row_ptr, w.col_idx), m, "WSB windows, blocks, bitmaps",
+                           "the whole graph")
+
+    cfg = {"workload": "wsb_" + w.name, "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m,
+           "tau": 8, "plan": st,
+           "note": "wsb build alone = per_op_ms.plan_wsb - per_op_ms.plan"}
+    return {"ops": ops, "dominant": "plan_wsb", "kernel": "gnn_plan_create with WSB (all kernels)",
+            "config": cfg, "dtype": "int32", "cpu": cpu, "keep": (w, csr)}
+
+
+def wl_reorder(args):
+    """Reordering of R-MAT 16,000,000 nodes / 256,000,000 edges: degree sort and RCM, each
+    with the relabelled CSR (P A P^T) and the permuted feature rows (X 16M x 256 bf16)."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.spmm_rmat_large(with_x=False)
+    n, m, F = w.n, w.nnz, w.params["F"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    X = torch.randn((n, F), device="cuda").to(torch.bfloat16)
+    Xo = torch.empty_like(X)
+
+    def run(kind):
+        perm, rp, ci = gnn.gnn_reorder(csr, kind)
+        gnn.gnn_permute_rows(perm, X, out=Xo)
+
+    # read row_ptr and col_idx, write perm and the relabelled CSR; gather and write X
+    b = 4 * (n + 1) + 4 * m + 4 * n + 4 * (n + 1) + 4 * m + 2 * n * F * 2
+    ops = [Op("rcm", lambda: run("rcm"), m, b), Op("degree", lambda: run("degree"), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        s = gen.reduce_rmat(with_x=False)
+        return _edges_rate(lambda: oracle.rcm(s.row_ptr, s.col_idx), s.nnz, "RCM (symmetrise, BFS, reverse)",
+                           f"R-MAT {s.n} nodes / {s.nnz} edges, same generator parameters")
+
+    cfg = {"workload": "reorder_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
+           "F": F, "x_dtype": "bf16"}
+    return {"ops": ops, "dominant": "rcm", "kernel": "gnn_reorder RCM + gnn_permute_rows (all kernels)",
+            "config": cfg, "dtype": "int32", "cpu": cpu, "keep": (w, csr, X, Xo)}
+
+
 WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
              "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
-             "gt_block16": lambda a: wl_gt(a, "block16")}
+             "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
+             "reorder_cfg5": wl_reorder}
 
 
 # ---------------------------------------------------------------------------

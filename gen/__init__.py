@@ -239,12 +239,13 @@ def gatv2_rmat(n=200_000, m=4_000_000, H=4, D=32, k=3) -> Workload:
                     {"xl": xl, "xr": xr, "att": att}, {"H": H, "D": D, "slope": 0.2})
 
 
-def gt_cluster(n=512_000, csize=64, p=0.5, frac=0.01, H=8, D=64, k=4) -> Workload:
+def gt_cluster(n=512_000, csize=64, p=0.5, frac=0.01, H=8, D=64, k=4, with_x=True) -> Workload:
     rp, ci = cluster(GRAPH_SEED + k, n, csize, p, frac, self_loops=True)
-    q = gauss_bf16(FEAT_SEED + k, (n, H, D))
-    kk = gauss_bf16(FEAT_SEED + 100 + k, (n, H, D))
-    v = gauss_bf16(FEAT_SEED + 200 + k, (n, H, D))
-    return Workload(f"gt_cluster{n}_c{csize}_h{H}d{D}", n, rp, ci, {"q": q, "k": kk, "v": v},
+    arrays = {}
+    if with_x:
+        arrays = {"q": gauss_bf16(FEAT_SEED + k, (n, H, D)), "k": gauss_bf16(FEAT_SEED + 100 + k, (n, H, D)),
+                  "v": gauss_bf16(FEAT_SEED + 200 + k, (n, H, D))}
+    return Workload(f"gt_cluster{n}_c{csize}_h{H}d{D}", n, rp, ci, arrays,
                     {"H": H, "D": D, "scale": 1.0 / D ** 0.5})
 
 
