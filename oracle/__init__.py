@@ -53,6 +53,12 @@ def _load():
     lib.oracle_rcm.argtypes = [i32, vp, vp, vp]
     lib.oracle_permute_csr.argtypes = [i32, vp, vp, vp, vp, vp]
     lib.oracle_wsb_build.argtypes = [i32, vp, vp, vp, vp, vp, vp]
+    lib.oracle_spmm_backward.argtypes = [i32, i32, vp, vp, vp, ci, vp, i32, vp, vp]
+    lib.oracle_reduce_backward.argtypes = [i32, i32, vp, vp, ci, vp, vp, i32, vp, vp]
+    lib.oracle_gt_backward.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp,
+                                       vp, vp]
+    lib.oracle_gatv2_backward.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp,
+                                          vp, vp, vp]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -197,3 +203,66 @@ def wsb_build(row_ptr, col_idx):
     tb = np.empty((nt.value, 2), np.uint64)
     _rc(lib.oracle_wsb_build(n, _p(rp), _p(ci), _p(wp), _p(tc), _p(tb), ctypes.byref(nt)), "wsb")
     return wp, tc, tb
+
+
+# ---------------------------------------------------------------------------
+# backward passes
+# ---------------------------------------------------------------------------
+
+def spmm_backward(row_ptr, col_idx, dY, norm="none", edge_val=None, n_cols=None):
+    """(dX fp64 [n_cols, F], |.|-sum) of dX = A_norm^T dY; dY float32 [n_rows, F]."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    n_cols = n if n_cols is None else n_cols
+    dY = np.ascontiguousarray(dY, np.float32)
+    F = dY.shape[1]
+    dX = np.empty((n_cols, F), np.float64)
+    A = np.empty((n_cols, F), np.float64)
+    _rc(_load().oracle_spmm_backward(n, n_cols, _p(rp), _p(ci), _p(_c(edge_val, np.float32)), NORM[norm],
+                                     _p(dY), F, _p(dX), _p(A)), "spmm_backward")
+    return dX, A
+
+
+def reduce_backward(row_ptr, col_idx, dY, op, arg=None, n_cols=None):
+    """(dX fp64 [n_cols, F], |.|-sum); arg int32 [n_rows, F] for max / min."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    n_cols = n if n_cols is None else n_cols
+    dY = np.ascontiguousarray(dY, np.float32)
+    F = dY.shape[1]
+    dX = np.empty((n_cols, F), np.float64)
+    A = np.empty((n_cols, F), np.float64)
+    _rc(_load().oracle_reduce_backward(n, n_cols, _p(rp), _p(ci), OP[op], _p(dY), _p(_c(arg, np.int32)), F,
+                                       _p(dX), _p(A)), "reduce_backward")
+    return dX, A
+
+
+def gt_backward(row_ptr, col_idx, q, k, v, dO, scale=0.0):
+    """(dq, dk, dv, dq_abs, dk_abs, dv_abs) fp64; q, k, v bf16 bits [n, H, D], dO float32."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    q, k, v = _c(q, np.uint16), _c(k, np.uint16), _c(v, np.uint16)
+    dO = np.ascontiguousarray(dO, np.float32)
+    H, D = q.shape[1], q.shape[2]
+    nc = k.shape[0]
+    outs = [np.empty((n, H, D)), np.empty((nc, H, D)), np.empty((nc, H, D)),
+            np.empty((n, H, D)), np.empty((nc, H, D)), np.empty((nc, H, D))]
+    _rc(_load().oracle_gt_backward(n, nc, _p(rp), _p(ci), _p(q), _p(k), _p(v), H, D, scale, _p(dO),
+                                   *[_p(o) for o in outs]), "gt_backward")
+    return tuple(outs)
+
+
+def gatv2_backward(row_ptr, col_idx, xl, xr, att, dO, slope=0.2):
+    """(dxl, dxr, datt, dxl_abs, dxr_abs, datt_abs) fp64; xl, xr bf16 bits [n, H, D]."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    xl, xr = _c(xl, np.uint16), _c(xr, np.uint16)
+    att = np.ascontiguousarray(att, np.float32)
+    dO = np.ascontiguousarray(dO, np.float32)
+    H, D = xl.shape[1], xl.shape[2]
+    nc = xr.shape[0]
+    outs = [np.empty((n, H, D)), np.empty((nc, H, D)), np.empty((H, D)),
+            np.empty((n, H, D)), np.empty((nc, H, D)), np.empty((H, D))]
+    _rc(_load().oracle_gatv2_backward(n, nc, _p(rp), _p(ci), _p(xl), _p(xr), _p(att), H, D, slope, _p(dO),
+                                      *[_p(o) for o in outs]), "gatv2_backward")
+    return tuple(outs)

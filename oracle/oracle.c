@@ -620,3 +620,243 @@ int oracle_wsb_build(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_
   *n_tcb = win_ptr[nw];
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward passes                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* SpMM backward: dX = A_norm^T dY, i.e. for every entry e = (i <- j) of row
+ * i, dX[j, :] += w_e * dY[i, :] with the forward's weight w_e (paper: the
+ * SpMM and reduction appendix, backward of Y = A X).  dY [n_rows, F] fp32,
+ * dX and dXabs (sum of |w_e dY|) [n_cols, F] fp64.  A plain serial scatter. */
+int oracle_spmm_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                         const float* edge_val, int norm, const float* dY, int32_t F, double* dX,
+                         double* dXabs) {
+  if (!row_ptr || !col_idx || !dY || !dX || F <= 0 || norm < 0 || norm > 3) return -1;
+  int32_t* dout = (int32_t*)malloc((size_t)(n_cols > 0 ? n_cols : 1) * 4);
+  if (!dout) return -2;
+  if (oracle_degrees(n_rows, n_cols, row_ptr, col_idx, NULL, dout)) {
+    free(dout);
+    return -1;
+  }
+  memset(dX, 0, (size_t)n_cols * F * 8);
+  if (dXabs) memset(dXabs, 0, (size_t)n_cols * F * 8);
+  for (int32_t i = 0; i < n_rows; ++i) {
+    int32_t din = row_ptr[i + 1] - row_ptr[i];
+    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      int32_t j = col_idx[e];
+      if (j < 0 || j >= n_cols) {
+        free(dout);
+        return -1;
+      }
+      double w = edge_weight(norm, din, dout[j], edge_val, e);
+      for (int32_t f = 0; f < F; ++f) {
+        double t = w * (double)dY[(int64_t)i * F + f];
+        dX[(int64_t)j * F + f] += t;
+        if (dXabs) dXabs[(int64_t)j * F + f] += fabs(t);
+      }
+    }
+  }
+  free(dout);
+  return 0;
+}
+
+/* Reduction backward (paper: reduction appendix, backward pass).  op 0 SUM:
+ * dX[j] += dY[i] for each entry (i <- j); 1 MEAN: dX[j] += dY[i] / deg_in(i);
+ * 2 MAX, 3 MIN: the gradient flows only to the selected source,
+ * dX[arg[i, f], f] += dY[i, f] (rows without entries have arg -1 and pass
+ * nothing).  dY, arg [n_rows, F]; dX, dXabs [n_cols, F] fp64. */
+int oracle_reduce_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                           int op, const float* dY, const int32_t* arg, int32_t F, double* dX,
+                           double* dXabs) {
+  if (!row_ptr || !col_idx || !dY || !dX || F <= 0 || op < 0 || op > 3) return -1;
+  if (op <= 1) return oracle_spmm_backward(n_rows, n_cols, row_ptr, col_idx, NULL, op, dY, F, dX, dXabs);
+  if (!arg) return -1;
+  memset(dX, 0, (size_t)n_cols * F * 8);
+  if (dXabs) memset(dXabs, 0, (size_t)n_cols * F * 8);
+  for (int32_t i = 0; i < n_rows; ++i) {
+    for (int32_t f = 0; f < F; ++f) {
+      int32_t j = arg[(int64_t)i * F + f];
+      if (j < 0) continue;
+      if (j >= n_cols) return -1;
+      double t = (double)dY[(int64_t)i * F + f];
+      dX[(int64_t)j * F + f] += t;
+      if (dXabs) dXabs[(int64_t)j * F + f] += fabs(t);
+    }
+  }
+  return 0;
+}
+
+/* Softmax weights of one (i, h) row from its logits (two passes). */
+static void softmax_weights(const double* logits, int32_t deg, double* alpha) {
+  double m = -INFINITY;
+  for (int32_t k = 0; k < deg; ++k)
+    if (logits[k] > m) m = logits[k];
+  double s = 0.0;
+  for (int32_t k = 0; k < deg; ++k) s += exp(logits[k] - m);
+  for (int32_t k = 0; k < deg; ++k) alpha[k] = exp(logits[k] - m) / s;
+}
+
+/* Graph Transformer backward (paper: attention appendix, backward pass with
+ * the cached logsumexp and Delta[i, h] = <O[i, h, :], dO[i, h, :]>), written
+ * from the definition of the forward: out_i = sum_j alpha_ij v_j,
+ * alpha_ij = softmax_j(e_ij), e_ij = scale <q_i, k_j>.  With
+ * g_ij = <dO_i, v_j> and Delta_i = sum_j alpha_ij g_ij (= <dO_i, out_i>),
+ * de_ij = alpha_ij (g_ij - Delta_i), and
+ *   dq_i += scale de_ij k_j,  dk_j += scale de_ij q_i,  dv_j += alpha_ij dO_i.
+ * q [n_rows, H, D], k, v [n_cols, H, D] bf16; dO [n_rows, H, D] fp32; outputs
+ * fp64 with magnitudes (sums of the absolute terms) for the error scale. */
+int oracle_gt_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                       const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t H, int32_t D,
+                       float scale, const float* dO, double* dq, double* dk, double* dv, double* dq_abs,
+                       double* dk_abs, double* dv_abs) {
+  if (!row_ptr || !col_idx || !q || !k || !v || !dO || !dq || !dk || !dv || H <= 0 || D <= 0) return -1;
+  const double sc = scale > 0.0f ? (double)scale : 1.0 / sqrt((double)D);
+  const int64_t HD = (int64_t)H * D;
+  memset(dq, 0, (size_t)n_rows * HD * 8);
+  memset(dk, 0, (size_t)n_cols * HD * 8);
+  memset(dv, 0, (size_t)n_cols * HD * 8);
+  if (dq_abs) memset(dq_abs, 0, (size_t)n_rows * HD * 8);
+  if (dk_abs) memset(dk_abs, 0, (size_t)n_cols * HD * 8);
+  if (dv_abs) memset(dv_abs, 0, (size_t)n_cols * HD * 8);
+  int32_t cap = 0;
+  double *e = NULL, *a = NULL, *g = NULL;
+  int rc = 0;
+  for (int32_t i = 0; i < n_rows && rc == 0; ++i) {
+    int32_t b = row_ptr[i], deg = row_ptr[i + 1] - b;
+    if (deg > cap) {
+      free(e); free(a); free(g);
+      cap = deg;
+      e = (double*)malloc((size_t)cap * 8);
+      a = (double*)malloc((size_t)cap * 8);
+      g = (double*)malloc((size_t)cap * 8);
+      if (!e || !a || !g) { rc = -2; break; }
+    }
+    for (int32_t h = 0; h < H; ++h) {
+      const uint16_t* qi = q + (int64_t)i * HD + (int64_t)h * D;
+      const float* doi = dO + (int64_t)i * HD + (int64_t)h * D;
+      for (int32_t t = 0; t < deg; ++t) {
+        int32_t j = col_idx[b + t];
+        if (j < 0 || j >= n_cols) { rc = -1; break; }
+        const uint16_t* kj = k + (int64_t)j * HD + (int64_t)h * D;
+        const uint16_t* vj = v + (int64_t)j * HD + (int64_t)h * D;
+        double dot = 0.0, gv = 0.0;
+        for (int32_t d = 0; d < D; ++d) {
+          dot += bf16_to_double(qi[d]) * bf16_to_double(kj[d]);
+          gv += (double)doi[d] * bf16_to_double(vj[d]);
+        }
+        e[t] = dot * sc;
+        g[t] = gv;
+      }
+      if (rc) break;
+      if (deg == 0) continue;
+      softmax_weights(e, deg, a);
+      double delta = 0.0;
+      for (int32_t t = 0; t < deg; ++t) delta += a[t] * g[t];
+      for (int32_t t = 0; t < deg; ++t) {
+        int32_t j = col_idx[b + t];
+        const uint16_t* kj = k + (int64_t)j * HD + (int64_t)h * D;
+        const double de = a[t] * (g[t] - delta);
+        for (int32_t d = 0; d < D; ++d) {
+          const int64_t oi = (int64_t)i * HD + (int64_t)h * D + d, oj = (int64_t)j * HD + (int64_t)h * D + d;
+          const double tq = sc * de * bf16_to_double(kj[d]);
+          const double tk = sc * de * bf16_to_double(qi[d]);
+          const double tv = a[t] * (double)doi[d];
+          dq[oi] += tq;
+          dk[oj] += tk;
+          dv[oj] += tv;
+          if (dq_abs) dq_abs[oi] += fabs(tq);
+          if (dk_abs) dk_abs[oj] += fabs(tk);
+          if (dv_abs) dv_abs[oj] += fabs(tv);
+        }
+      }
+    }
+  }
+  free(e); free(a); free(g);
+  return rc;
+}
+
+/* GATv2 backward (paper: attention appendix, the two-kernel backward with
+ * G_{i,h} = sum_j alpha_ij <dh_i, r_j> and the attention-vector gradient
+ * reduced over nodes), written from the forward: e_ij = sum_d a_d s(z_ijd),
+ * z_ij = l_i + r_j, s = LeakyReLU (s(z) = z if z > 0 else slope z, so its
+ * derivative is 1 for z > 0 and slope otherwise, the branch the forward
+ * takes at z = 0), out_i = sum_j alpha_ij r_j.  With g_ij = <dO_i, r_j>,
+ * G_i = sum_j alpha_ij g_ij and de_ij = alpha_ij (g_ij - G_i):
+ *   dl_i  += de_ij a (.) s'(z_ij)
+ *   dr_j  += alpha_ij dO_i + de_ij a (.) s'(z_ij)
+ *   da    += de_ij s(z_ij)            (summed over all entries)
+ * xl [n_rows, H, D], xr [n_cols, H, D] bf16; att [H, D] fp32; dO fp32;
+ * outputs fp64 with magnitudes for the error scale. */
+int oracle_gatv2_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                          const uint16_t* xl, const uint16_t* xr, const float* att, int32_t H, int32_t D,
+                          float slope, const float* dO, double* dl, double* dr, double* da, double* dl_abs,
+                          double* dr_abs, double* da_abs) {
+  if (!row_ptr || !col_idx || !xl || !xr || !att || !dO || !dl || !dr || !da || H <= 0 || D <= 0) return -1;
+  const int64_t HD = (int64_t)H * D;
+  const double sl = (double)slope;
+  memset(dl, 0, (size_t)n_rows * HD * 8);
+  memset(dr, 0, (size_t)n_cols * HD * 8);
+  memset(da, 0, (size_t)HD * 8);
+  if (dl_abs) memset(dl_abs, 0, (size_t)n_rows * HD * 8);
+  if (dr_abs) memset(dr_abs, 0, (size_t)n_cols * HD * 8);
+  if (da_abs) memset(da_abs, 0, (size_t)HD * 8);
+  int32_t cap = 0;
+  double *e = NULL, *a = NULL, *g = NULL;
+  int rc = 0;
+  for (int32_t i = 0; i < n_rows && rc == 0; ++i) {
+    int32_t b = row_ptr[i], deg = row_ptr[i + 1] - b;
+    if (deg > cap) {
+      free(e); free(a); free(g);
+      cap = deg;
+      e = (double*)malloc((size_t)cap * 8);
+      a = (double*)malloc((size_t)cap * 8);
+      g = (double*)malloc((size_t)cap * 8);
+      if (!e || !a || !g) { rc = -2; break; }
+    }
+    for (int32_t h = 0; h < H; ++h) {
+      const uint16_t* li = xl + (int64_t)i * HD + (int64_t)h * D;
+      const float* doi = dO + (int64_t)i * HD + (int64_t)h * D;
+      const float* ah = att + (int64_t)h * D;
+      for (int32_t t = 0; t < deg; ++t) {
+        int32_t j = col_idx[b + t];
+        if (j < 0 || j >= n_cols) { rc = -1; break; }
+        const uint16_t* rj = xr + (int64_t)j * HD + (int64_t)h * D;
+        double ev = 0.0, gv = 0.0;
+        for (int32_t d = 0; d < D; ++d) {
+          double z = bf16_to_double(li[d]) + bf16_to_double(rj[d]);
+          ev += (double)ah[d] * (z > 0.0 ? z : sl * z);
+          gv += (double)doi[d] * bf16_to_double(rj[d]);
+        }
+        e[t] = ev;
+        g[t] = gv;
+      }
+      if (rc) break;
+      if (deg == 0) continue;
+      softmax_weights(e, deg, a);
+      double G = 0.0;
+      for (int32_t t = 0; t < deg; ++t) G += a[t] * g[t];
+      for (int32_t t = 0; t < deg; ++t) {
+        int32_t j = col_idx[b + t];
+        const uint16_t* rj = xr + (int64_t)j * HD + (int64_t)h * D;
+        const double de = a[t] * (g[t] - G);
+        for (int32_t d = 0; d < D; ++d) {
+          const int64_t oi = (int64_t)i * HD + (int64_t)h * D + d, oj = (int64_t)j * HD + (int64_t)h * D + d;
+          const double z = bf16_to_double(li[d]) + bf16_to_double(rj[d]);
+          const double ds = z > 0.0 ? 1.0 : sl;
+          const double tl = de * (double)ah[d] * ds;
+          const double tv = a[t] * (double)doi[d];
+          const double ta = de * (z > 0.0 ? z : sl * z);
+          dl[oi] += tl;
+          dr[oj] += tv + tl;
+          da[(int64_t)h * D + d] += ta;
+          if (dl_abs) dl_abs[oi] += fabs(tl);
+          if (dr_abs) dr_abs[oj] += fabs(tv) + fabs(tl);
+          if (da_abs) da_abs[(int64_t)h * D + d] += fabs(ta);
+        }
+      }
+    }
+  }
+  free(e); free(a); free(g);
+  return rc;
+}

@@ -526,3 +526,154 @@ def test_wsb_bijection(rng):
                     got.add((16 * w + r, int(tc[b, c])))
     rows = np.repeat(np.arange(n), np.diff(rp))
     assert got == set(zip(rows.tolist(), ci.tolist()))
+
+
+# ----------------------------------------------------------------------------
+# backward passes: adjoint identities against the (pinned) forward oracle,
+# automatic differentiation of dense fp64 formulations, closed forms
+# ----------------------------------------------------------------------------
+
+def _dot(a, b):
+    return float(np.sum(np.asarray(a, np.float64) * np.asarray(b, np.float64)))
+
+
+@pytest.mark.parametrize("norm", ["none", "left", "right", "both"])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_spmm_backward_adjoint(rng, norm, weighted):
+    """<A_norm X, dY> = <X, A_norm^T dY> for random X, dY: a dropped weight,
+    a transposed index or a wrong degree breaks the identity."""
+    n, nc, F = 70, 90, 5
+    src = rng.integers(0, nc, 600)
+    dst = rng.integers(0, n, 600)
+    keep = np.unique(dst.astype(np.int64) * nc + src)        # sorted by (row, column), no duplicates
+    rp = np.zeros(n + 1, np.int32)
+    np.cumsum(np.bincount(keep // nc, minlength=n), out=rp[1:])
+    ci = (keep % nc).astype(np.int32)
+    ev = rng.standard_normal(ci.size).astype(np.float32) if weighted else None
+    X = rng.standard_normal((nc, F)).astype(np.float32)
+    dY = rng.standard_normal((n, F)).astype(np.float32)
+    Y, _ = oracle.spmm(rp, ci, X, norm, edge_val=ev, n_cols=nc)
+    dX, dXa = oracle.spmm_backward(rp, ci, dY, norm, edge_val=ev, n_cols=nc)
+    lhs, rhs = _dot(Y, dY), _dot(X, dX)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (lhs, rhs)
+    assert np.all(dXa >= np.abs(dX) - 1e-12)
+    # a column that no row uses gets no gradient
+    used = np.zeros(nc, bool)
+    used[ci] = True
+    assert np.all(dX[~used] == 0)
+
+
+@pytest.mark.parametrize("op", ["sum", "mean", "max", "min"])
+def test_reduce_backward_adjoint(rng, op):
+    """For fixed selected sources the reductions are linear in X, so
+    <reduce(X), dY> = <X, dX> holds exactly for every op; max / min route each
+    gradient element to the source the forward selected."""
+    n, p = 60, 0.1
+    A, rp, ci = random_graph(rng, n, p)
+    F = 4
+    X = rng.standard_normal((n, F)).astype(np.float32)
+    dY = rng.standard_normal((n, F)).astype(np.float32)
+    Y, arg, _ = oracle.reduce(rp, ci, X, op)
+    dX, _ = oracle.reduce_backward(rp, ci, dY, op, arg=arg if op in ("max", "min") else None)
+    lhs, rhs = _dot(Y, dY), _dot(X, dX)
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), (lhs, rhs)
+
+
+def test_reduce_max_backward_autograd(rng):
+    """Dense masked maximum differentiated by torch (distinct values, so the
+    maximum is unique): the gradient reaches exactly the selected source."""
+    torch = pytest.importorskip("torch")
+    n, F = 30, 3
+    A, rp, ci = random_graph(rng, n, 0.2)
+    X = rng.permutation(n * F).reshape(n, F).astype(np.float32) / 7.0
+    dY = rng.standard_normal((n, F)).astype(np.float32)
+    for op in ("max", "min"):
+        Y, arg, _ = oracle.reduce(rp, ci, X, op)
+        dX, _ = oracle.reduce_backward(rp, ci, dY, op, arg=arg)
+        Xt = torch.tensor(X, dtype=torch.float64, requires_grad=True)
+        mask = torch.tensor(A)
+        fill = -math.inf if op == "max" else math.inf
+        M = torch.where(mask[:, :, None], Xt[None, :, :], torch.tensor(fill, dtype=torch.float64))
+        red = M.amax(dim=1) if op == "max" else M.amin(dim=1)
+        has = mask.any(dim=1)[:, None]
+        red = torch.where(has, red, torch.zeros_like(red))
+        (red * torch.tensor(dY, dtype=torch.float64)).sum().backward()
+        np.testing.assert_allclose(dX, Xt.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def _dense_attention_grads(torch, A, E_fn, V, dO):
+    """Autograd of sum(dO * out) with out_i = sum_j softmax_j(E_ij) V_j over the
+    entries of A (rows without entries give 0)."""
+    E = E_fn()
+    mask = torch.tensor(A)
+    Em = torch.where(mask, E, torch.tensor(-math.inf, dtype=torch.float64))
+    has = mask.any(dim=1, keepdim=True)
+    P = torch.softmax(torch.where(has, Em, torch.zeros_like(Em)), dim=1)
+    P = torch.where(mask, P, torch.zeros_like(P))
+    out = P @ V
+    (out * dO).sum().backward()
+
+
+def test_gt_backward_autograd(rng):
+    torch = pytest.importorskip("torch")
+    n, H, D = 36, 2, 8
+    A, rp, ci = random_graph(rng, n, 0.25, loops=True)
+    A[5, :] = False                                   # one row without entries
+    rp, ci = gen.from_edges(n, *np.nonzero(A)[::-1])
+    q, k, v = bf16(rng, (n, H, D)), bf16(rng, (n, H, D)), bf16(rng, (n, H, D))
+    dO = rng.standard_normal((n, H, D)).astype(np.float32)
+    dq, dk, dv, *_ = oracle.gt_backward(rp, ci, q, k, v, dO)
+    for h in range(H):
+        Q, K, V = (torch.tensor(dec(x)[:, h], requires_grad=True) for x in (q, k, v))
+        _dense_attention_grads(torch, A, lambda: (Q @ K.T) / math.sqrt(D), V,
+                               torch.tensor(dO[:, h], dtype=torch.float64))
+        np.testing.assert_allclose(dq[:, h], Q.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dk[:, h], K.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dv[:, h], V.grad.numpy(), atol=1e-11, rtol=0)
+
+
+def test_gatv2_backward_autograd(rng):
+    torch = pytest.importorskip("torch")
+    n, H, D = 32, 2, 6
+    A, rp, ci = random_graph(rng, n, 0.25, loops=True)
+    xl, xr = bf16(rng, (n, H, D)), bf16(rng, (n, H, D))
+    xl[0, 0, :3] = gen.f32_to_bf16(-gen.bf16_to_f32(xr[0, 0, :3]))   # z = 0 exactly on a self loop
+    att = rng.standard_normal((H, D)).astype(np.float32)
+    dO = rng.standard_normal((n, H, D)).astype(np.float32)
+    dl, dr, da, *_ = oracle.gatv2_backward(rp, ci, xl, xr, att, dO, 0.2)
+    slope = float(np.float32(0.2))
+    for h in range(H):
+        Lt, Rt = (torch.tensor(dec(x)[:, h], requires_grad=True) for x in (xl, xr))
+        at = torch.tensor(att[h], dtype=torch.float64, requires_grad=True)
+
+        def E():
+            Z = Lt[:, None, :] + Rt[None, :, :]
+            return torch.nn.functional.leaky_relu(Z, slope) @ at
+        _dense_attention_grads(torch, A, E, Rt, torch.tensor(dO[:, h], dtype=torch.float64))
+        np.testing.assert_allclose(dl[:, h], Lt.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(dr[:, h], Rt.grad.numpy(), atol=1e-11, rtol=0)
+        np.testing.assert_allclose(da[h], at.grad.numpy(), atol=1e-11, rtol=0)
+
+
+def test_attention_backward_closed_forms(rng):
+    """Single-entry rows: alpha = 1, so only the value path carries gradient
+    (dq = dk = 0, dv_j = sum of dO over the rows j feeds).  Uniform weights
+    (K = 0, or a = 0): the value gradient is the mean-SpMM backward of dO."""
+    n, H, D = 50, 2, 4
+    src = rng.integers(0, n, n)
+    rp, ci = gen.from_edges(n, src, np.arange(n))
+    q, k, v = bf16(rng, (n, H, D)), bf16(rng, (n, H, D)), bf16(rng, (n, H, D))
+    dO = rng.standard_normal((n, H, D)).astype(np.float32)
+    dq, dk, dv, *_ = oracle.gt_backward(rp, ci, q, k, v, dO)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    expect = np.zeros((n, H, D))
+    np.add.at(expect, src, dO.astype(np.float64))
+    np.testing.assert_allclose(dv, expect, atol=1e-12, rtol=0)
+
+    A, rp, ci = random_graph(rng, n, 0.15, loops=True)
+    zero = np.zeros((n, H, D), np.uint16)
+    ref, _ = oracle.spmm_backward(rp, ci, dO.reshape(n, H * D), "left")
+    _, _, dv, *_ = oracle.gt_backward(rp, ci, q, zero, v, dO)
+    np.testing.assert_allclose(dv.reshape(n, H * D), ref, atol=1e-12, rtol=0)
+    _, dr, _, *_ = oracle.gatv2_backward(rp, ci, q, v, np.zeros((H, D), np.float32), dO, 0.2)
+    np.testing.assert_allclose(dr.reshape(n, H * D), ref, atol=1e-12, rtol=0)
