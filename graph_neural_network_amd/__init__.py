@@ -32,7 +32,8 @@ REORDER = {"degree": 0, "rcm": 1}
 # every symbol include/gnn.h declares
 EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
-           "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error")
+           "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
+           "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward")
 
 
 class GnnError(RuntimeError):
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH):
         "gnn_reorder": [P(_Csr), ci, vp, vp, vp, vp],
         "gnn_permute_rows": [vp, i32, vp, ci, i32, i64, vp, i64, vp],
         "gnn_copy_bytes": [vp, vp, i64, vp],
+        "gnn_spmm_backward": [P(_Csr), vp, i32, i64, vp, i64, ci, vp, vp],
+        "gnn_reduce_backward": [P(_Csr), ci, vp, i32, i64, vp, vp, i64, vp, vp],
+        "gnn_gatv2_backward": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
+        "gnn_gt_backward": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -277,6 +282,58 @@ def gnn_gt_fused(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
                                        float(scale), GT_MODE[mode], _ptr(out), _ptr(lse),
                                        _plan_h(plan), _stream(stream)), "gnn_gt_fused")
     return out, lse
+
+
+def gnn_spmm_backward(csr: Csr, dY: torch.Tensor, norm: str = "none", dX: torch.Tensor | None = None,
+                      plan: Plan | None = None, stream=None) -> torch.Tensor:
+    """dX [n_cols, F] = A_norm^T dY (float32)."""
+    F = dY.shape[1]
+    if dX is None:
+        dX = torch.empty((csr.n_cols, F), dtype=torch.float32, device=dY.device)
+    _check(load_library().gnn_spmm_backward(csr.ref, _ptr(dY), F, dY.stride(0), _ptr(dX), dX.stride(0),
+                                            NORM[norm], _plan_h(plan), _stream(stream)), "gnn_spmm_backward")
+    return dX
+
+
+def gnn_reduce_backward(csr: Csr, dY: torch.Tensor, op: str = "sum", arg: torch.Tensor | None = None,
+                        dX: torch.Tensor | None = None, plan: Plan | None = None, stream=None) -> torch.Tensor:
+    """dX [n_cols, F] (float32); arg: the forward's source indices (max / min)."""
+    F = dY.shape[1]
+    if dX is None:
+        dX = torch.empty((csr.n_cols, F), dtype=torch.float32, device=dY.device)
+    _check(load_library().gnn_reduce_backward(csr.ref, REDUCE_OP[op], _ptr(dY), F, dY.stride(0), _ptr(arg),
+                                              _ptr(dX), dX.stride(0), _plan_h(plan), _stream(stream)),
+           "gnn_reduce_backward")
+    return dX
+
+
+def gnn_gatv2_backward(csr: Csr, xl: torch.Tensor, xr: torch.Tensor, att: torch.Tensor, out: torch.Tensor,
+                       lse: torch.Tensor, dout: torch.Tensor, neg_slope: float = 0.2, plan: Plan | None = None,
+                       stream=None):
+    """-> (dxl [n_rows, H, D], dxr [n_cols, H, D], datt [H, D]), float32."""
+    H, D = xl.shape[1], xl.shape[2]
+    dxl = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=xl.device)
+    dxr = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=xl.device)
+    datt = torch.empty((H, D), dtype=torch.float32, device=xl.device)
+    _check(load_library().gnn_gatv2_backward(csr.ref, _ptr(xl), _ptr(xr), _dtype_code(xl), _ptr(att), H, D,
+                                             float(neg_slope), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dxl),
+                                             _ptr(dxr), _ptr(datt), _plan_h(plan), _stream(stream)),
+           "gnn_gatv2_backward")
+    return dxl, dxr, datt
+
+
+def gnn_gt_backward(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                    lse: torch.Tensor, dout: torch.Tensor, scale: float = 0.0, plan: Plan | None = None,
+                    stream=None):
+    """-> (dq [n_rows, H, D], dk, dv [n_cols, H, D]), float32."""
+    H, D = q.shape[1], q.shape[2]
+    dq = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    _check(load_library().gnn_gt_backward(csr.ref, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), H, D, float(scale),
+                                          _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                          _plan_h(plan), _stream(stream)), "gnn_gt_backward")
+    return dq, dk, dv
 
 
 def gnn_reorder(csr: Csr, kind: str = "degree", apply: bool = True, stream=None):

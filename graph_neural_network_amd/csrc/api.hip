@@ -125,11 +125,16 @@ int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream,
 int gnn_plan_destroy(gnn_plan* p) {
   if (!p) return GNN_OK;
   int rc = GNN_OK;
+  if (p->tplan) {
+    rc = gnn_plan_destroy(p->tplan);  // its CSR arrays belong to p and are freed below
+    p->tplan = nullptr;
+  }
   if (p->n_allocs > 0 || p->ws) {
     if (hipStreamSynchronize(p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "plan stream sync failed");
   }
   for (int k = 0; k < p->n_allocs; ++k) hipFree(p->allocs[k]);
   if (p->ws) hipFree(p->ws);
+  if (p->delta) hipFree(p->delta);
   delete p;
   return rc;
 }
@@ -266,6 +271,82 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   PlanGuard g{p, tr};
   if (mode == GNN_GT_BLOCK16) return launch_gt_block16(p, q, k, v, H, D, sc, out, lse, s);
   return launch_gt_csr(p, q, k, v, xtype, H, D, sc, out, lse, s);
+}
+
+int gnn_spmm_backward(const gnn_csr* csr, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
+                      gnn_norm norm, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  if (norm < GNN_NORM_NONE || norm > GNN_NORM_BOTH) return fail(GNN_ERR_INVALID_VALUE, "unknown norm");
+  if (F <= 0 || ldy < F || ldx < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldy >= F, ldx >= F");
+  if ((!dY && csr->n_rows > 0) || (!dX && csr->n_cols > 0)) return fail(GNN_ERR_INVALID_VALUE, "dY or dX is NULL");
+  if (csr->n_cols == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_spmm_backward(p, dY, F, ldy, dX, ldx, norm, csr->edge_val, s);
+}
+
+int gnn_reduce_backward(const gnn_csr* csr, gnn_reduce_op op, const float* dY, int32_t F, int64_t ldy,
+                        const int32_t* arg, float* dX, int64_t ldx, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  if (op < GNN_SUM || op > GNN_MIN) return fail(GNN_ERR_INVALID_VALUE, "unknown reduce op");
+  if (F <= 0 || ldy < F || ldx < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldy >= F, ldx >= F");
+  if ((!dY && csr->n_rows > 0) || (!dX && csr->n_cols > 0)) return fail(GNN_ERR_INVALID_VALUE, "dY or dX is NULL");
+  if ((op == GNN_MAX || op == GNN_MIN) && !arg && csr->n_rows > 0)
+    return fail(GNN_ERR_INVALID_VALUE, "MAX / MIN backward needs the forward's arg");
+  if (csr->n_cols == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_reduce_backward(p, op, dY, F, ldy, arg, dX, ldx, s);
+}
+
+int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype, const float* att,
+                       int32_t H, int32_t D, float neg_slope, const float* out, const float* lse,
+                       const float* dout, float* dxl, float* dxr, float* datt, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
+  if (!att || !datt || ((!xl || !out || !lse || !dout || !dxl) && csr->n_rows > 0) ||
+      ((!xr || !dxr) && csr->n_cols > 0))
+    return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
+  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
+  if ((D * esz) % 16 != 0 || H * D * esz > 1024)
+    return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
+  if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dxl | (uintptr_t)dxr) % 16)
+    return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_gatv2_backward(p, xl, xr, xtype, att, H, D, neg_slope, out, lse, dout, dxl, dxr, datt, s);
+}
+
+int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype, int32_t H,
+                    int32_t D, float scale, const float* out, const float* lse, const float* dout, float* dq,
+                    float* dk, float* dv, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
+  if (((!q || !out || !lse || !dout || !dq) && csr->n_rows > 0) || ((!k || !v || !dk || !dv) && csr->n_cols > 0))
+    return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
+  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
+  if ((D * esz) % 16 != 0 || H * D * esz > 2048)
+    return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) % 16)
+    return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_gt_backward(p, q, k, v, xtype, H, D, scale, out, lse, dout, dq, dk, dv, s);
 }
 
 int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* row_ptr_out,

@@ -29,25 +29,21 @@
 //                combine kernel merges in chunk order.
 #include <algorithm>
 
-#include "gnn_internal.h"
+#include "att_common.h"
 
 namespace gnn {
 namespace {
+
+using namespace att;
 
 constexpr int WG = 256;
 #ifndef GNN_ATT_U
 #define GNN_ATT_U 4
 #endif
-constexpr float kLog2e = 1.4426950408889634f;
-// 2^x on v_exp_f32 alone.  Softmax arguments are <= 0 (differences from the
-// running maximum), and results below 2^-126 of the maximum, which the
-// hardware may flush to zero, do not change any sum at fp32 precision.
-__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 #ifndef GNN_ATT_LIGHT_MAX
 #define GNN_ATT_LIGHT_MAX 128
 #endif
 constexpr int32_t kAttLightMax = GNN_ATT_LIGHT_MAX;
-constexpr float kLn2 = 0.6931471805599453f;
 
 enum { K_GATV2 = 0, K_GT = 1 };
 
@@ -76,43 +72,6 @@ struct AttParams {
   float slope;        // GATv2 LeakyReLU slope
   float qscale;       // GT: scale * log2(e)
 };
-
-template <typename T, int N>
-__device__ __forceinline__ void load_row(const T* p, float (&o)[N]);
-
-template <>
-__device__ __forceinline__ void load_row<uint16_t, 8>(const uint16_t* p, float (&o)[8]) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
-  o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x); o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
-  o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z); o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
-}
-template <>
-__device__ __forceinline__ void load_row<uint16_t, 16>(const uint16_t* p, float (&o)[16]) {
-  uint4 v = *reinterpret_cast<const uint4*>(p);
-  uint4 w = *reinterpret_cast<const uint4*>(p + 8);
-  o[0] = dev::bf16_lo(v.x); o[1] = dev::bf16_hi(v.x); o[2] = dev::bf16_lo(v.y); o[3] = dev::bf16_hi(v.y);
-  o[4] = dev::bf16_lo(v.z); o[5] = dev::bf16_hi(v.z); o[6] = dev::bf16_lo(v.w); o[7] = dev::bf16_hi(v.w);
-  o[8] = dev::bf16_lo(w.x); o[9] = dev::bf16_hi(w.x); o[10] = dev::bf16_lo(w.y); o[11] = dev::bf16_hi(w.y);
-  o[12] = dev::bf16_lo(w.z); o[13] = dev::bf16_hi(w.z); o[14] = dev::bf16_lo(w.w); o[15] = dev::bf16_hi(w.w);
-}
-template <>
-__device__ __forceinline__ void load_row<float, 4>(const float* p, float (&o)[4]) {
-  float4 v = *reinterpret_cast<const float4*>(p);
-  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
-}
-template <>
-__device__ __forceinline__ void load_row<float, 8>(const float* p, float (&o)[8]) {
-  float4 v = *reinterpret_cast<const float4*>(p);
-  float4 w = *reinterpret_cast<const float4*>(p + 4);
-  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w; o[4] = w.x; o[5] = w.y; o[6] = w.z; o[7] = w.w;
-}
-
-template <int N>
-__device__ __forceinline__ void store_row(float* p, const float (&v)[N]) {
-#pragma unroll
-  for (int k = 0; k < N; k += 4)
-    *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
-}
 
 // Online-softmax state of one slot lane: running max m (log2 units), running
 // sum l, accumulator acc over this lane's VEL output elements.
@@ -146,51 +105,6 @@ __device__ __forceinline__ void shfl_merge(Soft<VEL>& s, int lane_xor) {
 #pragma unroll
   for (int k = 0; k < VEL; ++k) a2[k] = __shfl_xor(s.acc[k], lane_xor, 64);
   s.merge(m2, l2, a2);
-}
-
-// A lane's slice of one node row, kept as raw 16-byte words until used
-// (NV words = 8 NV bf16 or 4 NV float32 elements).
-template <int NV>
-struct Raw {
-  uint32_t u[4 * NV];
-};
-
-template <typename T, int NV>
-__device__ __forceinline__ void load_raw(const T* p, Raw<NV>& r) {
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const uint4 v = reinterpret_cast<const uint4*>(p)[k];
-    r.u[4 * k] = v.x; r.u[4 * k + 1] = v.y; r.u[4 * k + 2] = v.z; r.u[4 * k + 3] = v.w;
-  }
-}
-
-// element k of a raw slice as float
-template <typename T, int NV>
-__device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
-  if constexpr (sizeof(T) == 2) return (k & 1) ? dev::bf16_hi(r.u[k >> 1]) : dev::bf16_lo(r.u[k >> 1]);
-  else return __uint_as_float(r.u[k]);
-}
-
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
-
-// Sum over aligned groups of LPH lanes (a head's lanes).  Groups up to 16
-// lanes use DPP lane swaps (no LDS round trip): xor 1 and xor 2 inside a quad,
-// then the half-row mirror (lane i <-> 7 - i) and the row mirror
-// (i <-> 15 - i), each of which pairs the lane with the other half of its
-// group once the halves are summed.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-template <int LPH>
-__device__ __forceinline__ float head_sum(float t) {
-  if constexpr (LPH > 1) t += dpp<0xB1>(t);   // quad_perm [1, 0, 3, 2]
-  if constexpr (LPH > 2) t += dpp<0x4E>(t);   // quad_perm [2, 3, 0, 1]
-  if constexpr (LPH > 4) t += dpp<0x141>(t);  // row_half_mirror
-  if constexpr (LPH > 8) t += dpp<0x140>(t);  // row_mirror
-  if constexpr (LPH > 16) t += __shfl_xor(t, 16, 64);
-  if constexpr (LPH > 32) t += __shfl_xor(t, 32, 64);
-  return t;
 }
 
 // Process edges [eb, ee) of destination `row` for one slot, UU edges in

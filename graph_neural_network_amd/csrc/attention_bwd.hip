@@ -1,0 +1,577 @@
+// Backward of the fused CSR attention layers (Graph Transformer, GATv2).
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", attention appendix, backward passes: only the per-(node,
+// head) logsumexp L of the forward is kept, the weights are recomputed on the
+// fly as alpha_ij = exp(e_ij - L_i), Delta[i, h] = <O[i, h, :], dO[i, h, :]>
+// (for GATv2 the same statistic is G_{i,h} = sum_j alpha_ij <dO_i, r_j>), a
+// walk over the transposed CSR gathers the gradients of the source-side
+// tensors, and the attention-vector gradient of GATv2 is reduced over nodes.
+// With de_ij = alpha_ij (<dO_i, v_j> - Delta_i):
+//   Graph Transformer (e = s <q_i, k_j>): dq_i = s sum_j de_ij k_j,
+//     dk_j = s sum_i de_ij q_i, dv_j = sum_i alpha_ij dO_i;
+//   GATv2 (e = a . LReLU(l_i + r_j), v_j = r_j): dl_i = sum_j de_ij a (.) LReLU'(z_ij),
+//     dr_j = sum_i (alpha_ij dO_i + de_ij a (.) LReLU'(z_ij)),
+//     da = sum_ij de_ij LReLU(z_ij).
+//
+// MI355X mapping: two walks and no atomics.  The destination walk (rows of
+// the CSR) forms Delta_i from O_i and dO_i, then per entry alpha and de, and
+// accumulates the destination gradient (dq_i, or dl_i and the workgroup's
+// share of da).  The source walk (rows of the plan's transpose) recomputes
+// the same alpha and de per entry from the stored L_i and Delta_i and
+// accumulates the source gradients.  Every output row is summed by one slot,
+// one workgroup, or ordered chunk partials (hub rows), so results are
+// deterministic; the pages' own backward instead updates one gradient with
+// atomic adds along the transposed walk, which at H * D = 512 would be 512
+// fp32 atomics per entry.  Lanes hold 16-byte slices of a node row and
+// per-head dot products use the DPP lane sums, as in the forward kernels.
+#include <algorithm>
+
+#include "att_common.h"
+
+namespace gnn {
+namespace {
+
+using namespace att;
+
+constexpr int WG = 256;
+constexpr int UB = 4;                 // entries in flight per slot
+constexpr int32_t kBwdLightMax = 64;  // one slot per row up to this many entries
+
+enum { B_GT_DST = 0, B_GT_SRC = 1, B_GAT_DST = 2, B_GAT_SRC = 3 };
+
+struct BwdParams {
+  // the walked graph (the CSR, or the plan's transpose) and its work split
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int4* items;
+  int32_t n_rows;
+  int32_t light_max;
+  int32_t n_item_blocks;
+  int32_t n_light_blocks;
+  // tensors: "dst" are indexed by destinations (rows of the CSR), "src" by sources
+  const void* q;     // dst: GT q; GATv2 x_l
+  const void* k;     // src: GT k; GATv2 x_r
+  const void* v;     // src: GT v; GATv2 x_r
+  const float* att;  // GATv2 a [H, D]
+  const float* out;  // dst: forward output
+  const float* lse;  // dst: forward logsumexp (natural log)
+  const float* dout; // dst: gradient of the output
+  float* delta;      // dst [.., H]: written by the destination walk, read by the source walk
+  float* g0;         // GT dst: dq; GT src: dk; GATv2 dst: dl; GATv2 src: dr
+  float* g1;         // GT src: dv
+  float* dapart;     // GATv2 dst: [gridDim.x, H * D] per-workgroup shares of da
+  float* part;       // split rows: [n_items, 2, H * D] chunk partials
+  int32_t H, D, row_elems, row_lanes;
+  float scale;       // GT score scale
+  float slope;       // GATv2 LeakyReLU slope
+};
+
+template <int VEL>
+__device__ __forceinline__ void load_f32(const float* p, float (&o)[VEL]) {
+#pragma unroll
+  for (int k = 0; k < VEL; k += 4) {
+    const float4 t = *reinterpret_cast<const float4*>(p + k);
+    o[k] = t.x; o[k + 1] = t.y; o[k + 2] = t.z; o[k + 3] = t.w;
+  }
+}
+
+template <typename T, int NV>
+__device__ __forceinline__ void decode(const Raw<NV>& r, float (&o)[(16 / sizeof(T)) * NV]) {
+#pragma unroll
+  for (int k = 0; k < (16 / (int)sizeof(T)) * NV; ++k) o[k] = elem<T, NV>(r, k);
+}
+
+// Per-row state: the row's own data and the accumulators.
+template <typename T, int NV, int KIND>
+struct Row {
+  static constexpr int VEL = (16 / (int)sizeof(T)) * NV;
+  Raw<NV> own;        // GT dst: q_i; GT src: k_j
+  float f0[VEL];      // dst: dO_i; GT src: v_j; GATv2 src: r_j
+  float f1[VEL];      // GATv2 dst: l_i
+  float a[VEL];       // GATv2: a
+  float L2 = 0.0f;    // dst: L_i * log2 e
+  float delta = 0.0f; // dst: Delta_i
+  float acc0[VEL], acc1[VEL];
+};
+
+// Work on entries [eb, ee) of walk row `row` for one slot (LPE lanes).
+template <typename T, int LPE, int NV, int KIND, int LPH>
+__device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl, int slot_base, bool d_ok,
+                                     int head, Row<T, NV, KIND>& R) {
+  constexpr int VEL = (16 / (int)sizeof(T)) * NV;
+  const int64_t ld = p.row_elems;
+  const float sc2 = p.scale * kLog2e;
+  for (int e0 = eb; e0 < ee; e0 += LPE) {
+    const int nb = min(LPE, ee - e0);
+    const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
+    for (int u0 = 0; u0 < nb; u0 += UB) {
+      int c[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u)
+        c[u] = (LPE == 64) ? __builtin_amdgcn_readlane(my_c, u0 + u) : __shfl(my_c, slot_base + u0 + u, 64);
+      // gathers of the other end of each entry
+      Raw<NV> x[UB], y[UB];
+      float g[UB][VEL];
+      float Lc[UB], Dc[UB];
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const bool ok = u0 + u < nb && d_ok;
+        const int64_t o = (int64_t)c[u] * ld + sl * VEL;
+        if constexpr (KIND == B_GT_DST) {
+          if (ok) {
+            load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + o, x[u]);
+            load_raw<T, NV>(reinterpret_cast<const T*>(p.v) + o, y[u]);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4 * NV; ++t) x[u].u[t] = y[u].u[t] = 0u;
+          }
+        } else if constexpr (KIND == B_GAT_DST) {
+          if (ok) load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + o, x[u]);
+          else {
+#pragma unroll
+            for (int t = 0; t < 4 * NV; ++t) x[u].u[t] = 0u;
+          }
+        } else {  // source walks: the destination's q / l, dO, L and Delta
+          if (ok) {
+            load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + o, x[u]);
+            load_f32<VEL>(p.dout + o, g[u]);
+            Lc[u] = p.lse[(int64_t)c[u] * p.H + head] * kLog2e;
+            Dc[u] = p.delta[(int64_t)c[u] * p.H + head];
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4 * NV; ++t) x[u].u[t] = 0u;
+#pragma unroll
+            for (int k = 0; k < VEL; ++k) g[u][k] = 0.0f;
+            Lc[u] = 0.0f;
+            Dc[u] = 0.0f;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const bool valid = u0 + u < nb;
+        if constexpr (KIND == B_GT_DST) {
+          float dot = 0.0f, gv = 0.0f;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int t = 0; t < 4 * NV; ++t)
+              dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, R.own.u[t]),
+                                                    __builtin_bit_cast(bf16x2_t, x[u].u[t]), dot, false);
+          } else {
+#pragma unroll
+            for (int k = 0; k < VEL; ++k) dot = fmaf(elem<T, NV>(R.own, k), elem<T, NV>(x[u], k), dot);
+          }
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) gv = fmaf(R.f0[k], elem<T, NV>(y[u], k), gv);
+          dot = head_sum<LPH>(dot);
+          gv = head_sum<LPH>(gv);
+          const float al = valid ? ex2(dot * sc2 - R.L2) : 0.0f;
+          const float w = p.scale * al * (gv - R.delta);
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) R.acc0[k] = fmaf(w, elem<T, NV>(x[u], k), R.acc0[k]);
+        } else if constexpr (KIND == B_GT_SRC) {
+          float dot = 0.0f, gv = 0.0f;
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int t = 0; t < 4 * NV; ++t)
+              dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x[u].u[t]),
+                                                    __builtin_bit_cast(bf16x2_t, R.own.u[t]), dot, false);
+          } else {
+#pragma unroll
+            for (int k = 0; k < VEL; ++k) dot = fmaf(elem<T, NV>(x[u], k), elem<T, NV>(R.own, k), dot);
+          }
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) gv = fmaf(g[u][k], R.f0[k], gv);
+          dot = head_sum<LPH>(dot);
+          gv = head_sum<LPH>(gv);
+          const float al = valid ? ex2(dot * sc2 - Lc[u]) : 0.0f;
+          const float w = p.scale * al * (gv - Dc[u]);
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) {
+            R.acc0[k] = fmaf(w, elem<T, NV>(x[u], k), R.acc0[k]);
+            R.acc1[k] = fmaf(al, g[u][k], R.acc1[k]);
+          }
+        } else if constexpr (KIND == B_GAT_DST) {
+          float e = 0.0f, gv = 0.0f, z[VEL];
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) {
+            const float r = elem<T, NV>(x[u], k);
+            z[k] = R.f1[k] + r;
+            e = fmaf(R.a[k], fmaxf(z[k], p.slope * z[k]), e);
+            gv = fmaf(R.f0[k], r, gv);
+          }
+          e = head_sum<LPH>(e);
+          gv = head_sum<LPH>(gv);
+          const float al = valid ? ex2(e * kLog2e - R.L2) : 0.0f;
+          const float de = al * (gv - R.delta);
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) {
+            const bool pos = z[k] > 0.0f;
+            R.acc0[k] = fmaf(de * R.a[k], pos ? 1.0f : p.slope, R.acc0[k]);
+            R.acc1[k] = fmaf(de, pos ? z[k] : p.slope * z[k], R.acc1[k]);
+          }
+        } else {  // B_GAT_SRC
+          float e = 0.0f, gv = 0.0f, z[VEL];
+#pragma unroll
+          for (int k = 0; k < VEL; ++k) {
+            z[k] = elem<T, NV>(x[u], k) + R.f0[k];
+            e = fmaf(R.a[k], fmaxf(z[k], p.slope * z[k]), e);
+            gv = fmaf(g[u][k], R.f0[k], gv);
+          }
+          e = head_sum<LPH>(e);
+          gv = head_sum<LPH>(gv);
+          const float al = valid ? ex2(e * kLog2e - Lc[u]) : 0.0f;
+          const float de = al * (gv - Dc[u]);
+#pragma unroll
+          for (int k = 0; k < VEL; ++k)
+            R.acc0[k] = fmaf(al, g[u][k], fmaf(de * R.a[k], z[k] > 0.0f ? 1.0f : p.slope, R.acc0[k]));
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int LPE, int NV, int KIND, int LPH>
+__global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
+  constexpr int VEL = (16 / (int)sizeof(T)) * NV;
+  constexpr int SPW = 64 / LPE;
+  constexpr int NWAVE = WG / 64;
+  constexpr bool DST = KIND == B_GT_DST || KIND == B_GAT_DST;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sw = lane / LPE, sl = lane % LPE;
+  const int slot_base = sw * LPE;
+  const bool d_ok = sl < p.row_lanes;
+  const int head = d_ok ? sl / LPH : 0;
+
+  const int n_item_pad = (p.n_item_blocks + 7) & ~7;
+  const bool is_item = (int)blockIdx.x < n_item_pad;
+  int64_t row = -1;
+  int eb = 0, ee = 0, m_idx = -1, item = -1;
+  bool active = true;  // GATv2 dst workgroups reach the block reduction even when idle
+  if (is_item) {
+    item = (int)dev::xcd_remap(blockIdx.x, n_item_pad);
+    active = item < p.n_item_blocks;
+    if (active) {
+      const int4 it = p.items[item];
+      active = !(it.w < 0 && it.z - it.y <= p.light_max);  // short rows: light path
+      row = it.x;
+      m_idx = it.w;
+      const int nslots = SPW * NWAVE, slot = wave * SPW + sw;
+      const int len = it.z - it.y, per = (len + nslots - 1) / nslots;
+      eb = min(it.z, it.y + slot * per);
+      ee = min(it.z, eb + per);
+    }
+  } else {
+    const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
+    row = ((int64_t)lb * NWAVE + wave) * SPW + sw;
+    active = row < p.n_rows;
+    if (active) {
+      eb = p.row_ptr[row];
+      ee = p.row_ptr[row + 1];
+      active = ee - eb <= p.light_max;
+    }
+  }
+  if (KIND != B_GAT_DST && !active) return;  // uniform over the workgroup for items, over the slot otherwise
+
+  Row<T, NV, KIND> R;
+#pragma unroll
+  for (int k = 0; k < VEL; ++k) R.acc0[k] = R.acc1[k] = R.a[k] = R.f0[k] = R.f1[k] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 4 * NV; ++t) R.own.u[t] = 0u;
+  const int64_t ro = row * (int64_t)p.row_elems + sl * VEL;
+  if (active && d_ok) {
+    if constexpr (DST) {
+      float o[VEL];
+      load_f32<VEL>(p.dout + ro, R.f0);
+      load_f32<VEL>(p.out + ro, o);
+      float t = 0.0f;
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) t = fmaf(R.f0[k], o[k], t);
+      R.delta = t;
+      R.L2 = p.lse[row * p.H + head] * kLog2e;
+      if constexpr (KIND == B_GT_DST) load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + ro, R.own);
+      else {
+        Raw<NV> l;
+        load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + ro, l);
+        decode<T, NV>(l, R.f1);
+      }
+    } else {
+      Raw<NV> f;
+      if constexpr (KIND == B_GT_SRC) {
+        load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + ro, R.own);
+        load_raw<T, NV>(reinterpret_cast<const T*>(p.v) + ro, f);
+      } else {
+        load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + ro, f);
+      }
+      decode<T, NV>(f, R.f0);
+    }
+    if constexpr (KIND == B_GAT_DST || KIND == B_GAT_SRC) {
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) R.a[k] = p.att[sl * VEL + k];
+    }
+  }
+  if constexpr (DST) R.delta = head_sum<LPH>(R.delta);
+  if (DST && active && d_ok && (sl % LPH) == 0 && (!is_item || m_idx < 0 || p.items[item].y == p.row_ptr[row]))
+    p.delta[row * p.H + head] = R.delta;  // once per row: the light slot, the single item, or chunk 0
+
+  if (active) scan<T, LPE, NV, KIND, LPH>(p, eb, ee, sl, slot_base, d_ok, head, R);
+
+  __shared__ __align__(16) float s_acc[NWAVE][2][64 * VEL];
+
+  if constexpr (KIND == B_GAT_DST) {
+    // the workgroup's share of da: the sum of acc1 over every slot, in slot order
+#pragma unroll
+    for (int o = LPE; o < 64; o <<= 1)
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) R.acc1[k] += __shfl_xor(R.acc1[k], o, 64);
+    if (sw == 0) {
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) s_acc[wave][1][sl * VEL + k] = R.acc1[k];
+    }
+    __syncthreads();
+    if (wave == 0 && sw == 0 && d_ok) {
+#pragma unroll
+      for (int k = 0; k < VEL; ++k) {
+        float t = s_acc[0][1][sl * VEL + k];
+        for (int w = 1; w < NWAVE; ++w) t += s_acc[w][1][sl * VEL + k];
+        p.dapart[(int64_t)blockIdx.x * p.row_elems + sl * VEL + k] = t;
+      }
+    }
+  }
+
+  if (!is_item) {
+    if (active && d_ok) {
+      store_row<VEL>(p.g0 + ro, R.acc0);
+      if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.g1 + ro, R.acc1);
+    }
+    return;
+  }
+  if (!active) return;  // uniform over an item workgroup
+
+  // an item: sum the slots of each wave, then the waves in order
+#pragma unroll
+  for (int o = LPE; o < 64; o <<= 1)
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) {
+      R.acc0[k] += __shfl_xor(R.acc0[k], o, 64);
+      if constexpr (KIND == B_GT_SRC) R.acc1[k] += __shfl_xor(R.acc1[k], o, 64);
+    }
+  if (KIND == B_GAT_DST) __syncthreads();  // s_acc[.][1] was read above
+  if (sw == 0) {
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) {
+      s_acc[wave][0][sl * VEL + k] = R.acc0[k];
+      if constexpr (KIND == B_GT_SRC) s_acc[wave][1][sl * VEL + k] = R.acc1[k];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || sw != 0 || !d_ok) return;
+#pragma unroll
+  for (int k = 0; k < VEL; ++k) {
+    float t0 = s_acc[0][0][sl * VEL + k], t1 = s_acc[0][1][sl * VEL + k];
+    for (int w = 1; w < NWAVE; ++w) {
+      t0 += s_acc[w][0][sl * VEL + k];
+      if constexpr (KIND == B_GT_SRC) t1 += s_acc[w][1][sl * VEL + k];
+    }
+    R.acc0[k] = t0;
+    R.acc1[k] = t1;
+  }
+  if (m_idx < 0) {
+    store_row<VEL>(p.g0 + ro, R.acc0);
+    if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.g1 + ro, R.acc1);
+  } else {
+    const int64_t po = (int64_t)item * 2 * p.row_elems + sl * VEL;
+    store_row<VEL>(p.part + po, R.acc0);
+    if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.part + po + p.row_elems, R.acc1);
+  }
+}
+
+// Rows split into chunks: sum the chunk partials in chunk order.
+__global__ __launch_bounds__(256) void k_bwd_combine(const float* part, const int4* multi, int32_t row_elems,
+                                                     int two, float* g0, float* g1) {
+  const int4 mr = multi[blockIdx.x];
+  const int row = mr.x, first = mr.y, cnt = mr.z;
+  for (int t = threadIdx.x; t < row_elems; t += blockDim.x) {
+    float a = 0.0f, b = 0.0f;
+    for (int c = 0; c < cnt; ++c) {
+      a += part[(int64_t)(first + c) * 2 * row_elems + t];
+      if (two) b += part[(int64_t)(first + c) * 2 * row_elems + row_elems + t];
+    }
+    g0[(int64_t)row * row_elems + t] = a;
+    if (two) g1[(int64_t)row * row_elems + t] = b;
+  }
+}
+
+// da = sum over workgroups of their shares, in two ordered levels: block b
+// sums rows [b * per, (b + 1) * per) of the shares into mid[b], then one
+// block sums mid.
+__global__ __launch_bounds__(256) void k_da_level(const float* in, int64_t rows, int64_t per, int32_t cols,
+                                                  float* out) {
+  const int64_t r0 = (int64_t)blockIdx.x * per, r1 = min(rows, r0 + per);
+  for (int c = threadIdx.x; c < cols; c += blockDim.x) {
+    float t = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) t += in[r * cols + c];
+    out[(int64_t)blockIdx.x * cols + c] = t;
+  }
+}
+
+template <typename T, int LPE, int NV, int KIND, int LPH>
+int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
+  constexpr int SPB = (64 / LPE) * (WG / 64);
+  p.row_ptr = pl->row_ptr;
+  p.col_idx = pl->col_idx;
+  p.items = pl->items;
+  p.n_rows = pl->n_rows;
+  p.light_max = std::max(pl->light_max, std::min(kBwdLightMax, pl->heavy_thr));
+  p.n_item_blocks = (int32_t)pl->n_items;
+  p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
+  const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
+  if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention backward grid too large");
+  const size_t part_b = ((size_t)std::max<int64_t>(pl->n_items, 1) * 2 * p.row_elems * 4 + 255) & ~(size_t)255;
+  const size_t da_b = KIND == B_GAT_DST ? (size_t)gx * p.row_elems * 4 : 0;
+  void* ws = nullptr;
+  GNN_TRY(plan_workspace(pl, part_b + da_b + 2 * 256 * (size_t)p.row_elems * 4 + 256, &ws));
+  p.part = (float*)ws;
+  p.dapart = KIND == B_GAT_DST ? (float*)((char*)ws + part_b) : nullptr;
+  if (gx > 0) {
+    hipLaunchKernelGGL((k_att_bwd<T, LPE, NV, KIND, LPH>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+    GNN_LAUNCH_CHECK("attention backward");
+  }
+  if (pl->n_multi > 0) {
+    hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p.part,
+                       (const int4*)pl->multi, p.row_elems, KIND == B_GT_SRC ? 1 : 0, p.g0, p.g1);
+    GNN_LAUNCH_CHECK("attention backward combine");
+  }
+  if constexpr (KIND == B_GAT_DST) {
+    // da: ordered two-level sum of the workgroup shares
+    float* mid = (float*)((char*)ws + part_b + da_b);
+    const int64_t nb = std::min<int64_t>(256, std::max<int64_t>(gx, 1));
+    const int64_t per = (std::max<int64_t>(gx, 1) + nb - 1) / nb;
+    if (gx > 0) {
+      hipLaunchKernelGGL(k_da_level, dim3((unsigned)nb), dim3(256), 0, s, p.dapart, gx, per, p.row_elems, mid);
+      hipLaunchKernelGGL(k_da_level, dim3(1), dim3(256), 0, s, mid, nb, nb, p.row_elems, p.g1);
+    } else {
+      hipLaunchKernelGGL(k_da_level, dim3(1), dim3(256), 0, s, mid, 0, 1, p.row_elems, p.g1);
+    }
+    GNN_LAUNCH_CHECK("attention backward da");
+  }
+  return GNN_OK;
+}
+
+template <typename T, int LPE, int NV, int KIND>
+int by_lph(gnn_plan* pl, const BwdParams& p, int lph, hipStream_t s) {
+  switch (lph) {
+    case 1: return launch_walk<T, LPE, NV, KIND, 1>(pl, p, s);
+    case 2: return launch_walk<T, LPE, NV, KIND, 2>(pl, p, s);
+    case 4: return launch_walk<T, LPE, NV, KIND, 4>(pl, p, s);
+    case 8: return launch_walk<T, LPE, NV, KIND, 8>(pl, p, s);
+    default: break;
+  }
+  if constexpr (LPE >= 16) if (lph == 16) return launch_walk<T, LPE, NV, KIND, 16>(pl, p, s);
+  if constexpr (LPE >= 32) if (lph == 32) return launch_walk<T, LPE, NV, KIND, 32>(pl, p, s);
+  if constexpr (LPE >= 64) if (lph == 64) return launch_walk<T, LPE, NV, KIND, 64>(pl, p, s);
+  return fail(GNN_ERR_UNSUPPORTED, "lanes per head exceed the slot");
+}
+
+template <typename T, int KIND>
+int by_shape(gnn_plan* pl, const BwdParams& p, int lpe, int nv, int lph, hipStream_t s) {
+  if (nv == 2) {
+    switch (lpe) {
+      case 8: return by_lph<T, 8, 2, KIND>(pl, p, lph, s);
+      case 16: return by_lph<T, 16, 2, KIND>(pl, p, lph, s);
+      case 32: return by_lph<T, 32, 2, KIND>(pl, p, lph, s);
+      default: return by_lph<T, 64, 2, KIND>(pl, p, lph, s);
+    }
+  }
+  switch (lpe) {
+    case 8: return by_lph<T, 8, 1, KIND>(pl, p, lph, s);
+    case 16: return by_lph<T, 16, 1, KIND>(pl, p, lph, s);
+    case 32: return by_lph<T, 32, 1, KIND>(pl, p, lph, s);
+    default: return by_lph<T, 64, 1, KIND>(pl, p, lph, s);
+  }
+}
+
+// Lane layout of a row of H * D elements (as in the forward kernels).
+int shape(gnn_dtype xt, int32_t H, int32_t D, int* lpe, int* nv, int* lph, int* lanes) {
+  const int esz = xt == GNN_BF16 ? 2 : 4;
+  const int rowb = H * D * esz;
+  *nv = rowb > 1024 ? 2 : 1;
+  const int vb = 16 * *nv;
+  if ((D * esz) % vb != 0) return fail(GNN_ERR_UNSUPPORTED, "head dimension does not fill whole lane vectors");
+  *lph = D * esz / vb;
+  if ((*lph & (*lph - 1)) != 0) return fail(GNN_ERR_UNSUPPORTED, "lanes per head must be a power of two");
+  *lanes = rowb / vb;
+  int l = 8;
+  while (l < *lanes) l <<= 1;
+  if (l > 64) return fail(GNN_ERR_UNSUPPORTED, "row too wide");
+  *lpe = l;
+  return GNN_OK;
+}
+
+template <int KIND>
+int run(gnn_plan* pl, const BwdParams& p, gnn_dtype xt, int lpe, int nv, int lph, hipStream_t s) {
+  return xt == GNN_BF16 ? by_shape<uint16_t, KIND>(pl, p, lpe, nv, lph, s)
+                        : by_shape<float, KIND>(pl, p, lpe, nv, lph, s);
+}
+
+}  // namespace
+
+int launch_gt_backward(gnn_plan* pl, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
+                       int32_t D, float scale, const float* out, const float* lse, const float* dout,
+                       float* dq, float* dk, float* dv, hipStream_t s) {
+  int lpe, nv, lph, lanes;
+  GNN_TRY(shape(xt, H, D, &lpe, &nv, &lph, &lanes));
+  GNN_TRY(plan_transpose(pl, s));
+  BwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.H = H;
+  p.D = D;
+  p.row_elems = H * D;
+  p.row_lanes = lanes;
+  p.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
+  // Delta lives in the plan of the destinations, sized [n_rows, H]
+  GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
+  p.delta = pl->delta;
+  p.g0 = dq;
+  GNN_TRY(run<B_GT_DST>(pl, p, xt, lpe, nv, lph, s));
+  p.g0 = dk;
+  p.g1 = dv;
+  return run<B_GT_SRC>(pl->tplan, p, xt, lpe, nv, lph, s);
+}
+
+int launch_gatv2_backward(gnn_plan* pl, const void* xl, const void* xr, gnn_dtype xt, const float* att,
+                          int32_t H, int32_t D, float slope, const float* out, const float* lse,
+                          const float* dout, float* dxl, float* dxr, float* datt, hipStream_t s) {
+  int lpe, nv, lph, lanes;
+  GNN_TRY(shape(xt, H, D, &lpe, &nv, &lph, &lanes));
+  GNN_TRY(plan_transpose(pl, s));
+  BwdParams p{};
+  p.q = xl;
+  p.k = xr;
+  p.v = xr;
+  p.att = att;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.H = H;
+  p.D = D;
+  p.row_elems = H * D;
+  p.row_lanes = lanes;
+  p.slope = slope;
+  GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
+  p.delta = pl->delta;
+  p.g0 = dxl;
+  p.g1 = datt;
+  GNN_TRY(run<B_GAT_DST>(pl, p, xt, lpe, nv, lph, s));
+  p.g0 = dxr;
+  p.g1 = nullptr;
+  return run<B_GAT_SRC>(pl->tplan, p, xt, lpe, nv, lph, s);
+}
+
+}  // namespace gnn

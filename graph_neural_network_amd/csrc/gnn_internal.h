@@ -92,6 +92,16 @@ struct gnn_plan {
   int32_t* att_count = nullptr;  // device: number of listed rows
   int32_t att_lmax = -1;
 
+  // the transpose A^T (built on the first backward call): its CSR arrays,
+  // the position in A of each of its entries, and a plan over it
+  gnn_plan* tplan = nullptr;
+  int32_t* t_row_ptr = nullptr;  // [n_cols + 1]
+  int32_t* t_col = nullptr;      // [nnz] rows of A
+  int32_t* t_edge = nullptr;     // [nnz]
+  float* t_val = nullptr;        // [nnz] edge values in transposed order (per call)
+  float* delta = nullptr;        // attention backward: [n_rows, H] <O, dO> per (row, head)
+  size_t delta_cap = 0;
+
   // workspace (partials / packed words); grows on demand
   void* ws = nullptr;
   size_t ws_bytes = 0;
@@ -108,9 +118,12 @@ namespace gnn {
 
 int plan_alloc(gnn_plan* p, void** ptr, size_t bytes);
 int plan_workspace(gnn_plan* p, size_t bytes, void** out);
+// a plan-owned buffer that grows on demand (freed with the plan)
+int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes);
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p);
 int plan_build_wsb(gnn_plan* p, hipStream_t s);
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
+int plan_transpose(gnn_plan* p, hipStream_t s);
 int check_plan(const gnn_plan* p, const gnn_csr* csr);
 
 // Launchers (host).  All validate nothing: the entry points did.
@@ -140,6 +153,18 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
 // in `keys`, `tmp` is scratch of n keys.
 int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
                    hipStream_t s);
+
+// Backward launchers (transposed walks; see transpose.hip, attention_bwd.hip)
+int launch_spmm_backward(gnn_plan* p, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
+                         gnn_norm norm, const float* edge_val, hipStream_t s);
+int launch_reduce_backward(gnn_plan* p, int op, const float* dY, int32_t F, int64_t ldy,
+                           const int32_t* arg, float* dX, int64_t ldx, hipStream_t s);
+int launch_gt_backward(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
+                       int32_t D, float scale, const float* out, const float* lse, const float* dout,
+                       float* dq, float* dk, float* dv, hipStream_t s);
+int launch_gatv2_backward(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, const float* att,
+                          int32_t H, int32_t D, float slope, const float* out, const float* lse,
+                          const float* dout, float* dxl, float* dxr, float* datt, hipStream_t s);
 
 // Aggregation modes for launch_aggregate
 enum AggMode { AGG_SUM = 0, AGG_MEAN = 1, AGG_MAX = 2, AGG_MIN = 3, AGG_SPMM = 4 };

@@ -373,6 +373,23 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
   return GNN_OK;
 }
 
+int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes) {
+  if (*buf && *cap >= bytes) return GNN_OK;
+  if (*buf) {
+    GNN_HIP(hipStreamSynchronize(p->stream));
+    GNN_HIP(hipFree(*buf));
+    *buf = nullptr;
+    *cap = 0;
+  }
+  hipError_t e = hipMalloc(buf, bytes);
+  if (e != hipSuccess) {
+    *buf = nullptr;
+    return fail(GNN_ERR_OUT_OF_MEMORY, std::string("plan buffer: ") + hipGetErrorString(e));
+  }
+  *cap = bytes;
+  return GNN_OK;
+}
+
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p) {
   p->n_rows = csr->n_rows;
   p->n_cols = csr->n_cols;

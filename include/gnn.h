@@ -11,6 +11,8 @@
  *   gnn_gatv2_fused  GATv2 attention, one pass, online softmax (section 2.2 (iii), appendix D.2)
  *   gnn_gt_fused     Graph Transformer attention, CSR or 16x16 block-sparse
  *                                                              (appendix D.2 and D.3)
+ *   gnn_*_backward   gradients of SpMM, the reductions and both attention layers
+ *                                                              (appendix D.1 and D.2, backward passes)
  *   gnn_reorder      degree-sort or RCM vertex reordering      (section 2.4; RCM as in
  *                    Tang et al., "A High-Throughput Solver for Marginalized Graph
  *                    Kernels on GPU", graph reordering section)
@@ -203,6 +205,73 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
 int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype,
                  int32_t H, int32_t D, float scale, gnn_gt_mode mode, float* out, float* lse,
                  gnn_plan* plan, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward passes.  Each takes the gradient of a forward output and returns
+ * the gradients of its inputs, all float32, dense, owned by the caller and
+ * fully overwritten.  They walk the transpose A^T, which the plan builds on
+ * its first backward call (the entries of each transposed row keep their order
+ * in A) and keeps; without a plan a transient one is built and freed.  A plan
+ * serves one call at a time.
+ * ------------------------------------------------------------------------- */
+
+/* SpMM backward: dX = A_norm^T dY, i.e. dX[j, :] = sum over entries (i <- j)
+ * of w_e dY[i, :], with the forward's weight w_e (norm and csr->edge_val as in
+ * gnn_spmm).  dY: device [n_rows, F] float32, row stride ldy; dX: device
+ * [n_cols, F] float32, row stride ldx (columns without entries get 0).
+ * Deterministic.  Errors: INVALID_VALUE, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_spmm_backward(const gnn_csr* csr, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
+                      gnn_norm norm, gnn_plan* plan, void* stream);
+
+/* Reduction backward (appendix D.1, backward pass).  SUM: dX = A^T dY;
+ * MEAN: dX[j] = sum over entries (i <- j) of dY[i] / deg_in(i); MAX / MIN:
+ * the gradient reaches only the source the forward selected,
+ * dX[arg[i, f], f] += dY[i, f] (arg -1 passes nothing; values outside
+ * [0, n_cols) are ignored), as a scatter with atomic adds, so when several
+ * rows selected one source the order of its additions, and the last bits of
+ * the sum, may differ between runs.  dY: device [n_rows, F] float32 (row
+ * stride ldy); arg: device [n_rows, F] int32 as written by gnn_reduce /
+ * gnn_reduce_multi (row stride F; required for MAX / MIN, ignored otherwise);
+ * dX: device [n_cols, F] float32 (row stride ldx).
+ * Errors: INVALID_VALUE, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_reduce_backward(const gnn_csr* csr, gnn_reduce_op op, const float* dY, int32_t F, int64_t ldy,
+                        const int32_t* arg, float* dX, int64_t ldx, gnn_plan* plan, void* stream);
+
+/* GATv2 backward (appendix D.2, backward pass: weights recomputed as
+ * alpha_ij = exp(e_ij - lse_i) from the forward's logsumexp; the per-(i, h)
+ * statistic G = sum_j alpha_ij <dO_i, xr_j> = <dO_i, out_i>; a walk over A^T
+ * for the right features; the attention-vector gradient reduced over nodes).
+ * With z = xl_i + xr_j and de_ij = alpha_ij (<dO_i, xr_j> - G_i), per head:
+ *   dxl[i] = sum_j de_ij att (.) LReLU'(z)
+ *   dxr[j] = sum_i (alpha_ij dO_i + de_ij att (.) LReLU'(z))
+ *   datt   = sum over entries of de_ij LReLU(z)
+ * where LReLU'(z) = 1 for z > 0 and neg_slope otherwise.  Inputs as in
+ * gnn_gatv2_fused, plus out [n_rows, H, D] and lse [n_rows, H] of the forward
+ * (required) and dout [n_rows, H, D] float32.  Outputs (float32): dxl
+ * [n_rows, H, D], dxr [n_cols, H, D], datt [H, D].  Two walks and an ordered
+ * reduction; no atomics, deterministic.  The plan also keeps the per-(i, h)
+ * statistic between the walks.  Supported shapes as in gnn_gatv2_fused; all
+ * row tensors 16-byte aligned.
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype, const float* att,
+                       int32_t H, int32_t D, float neg_slope, const float* out, const float* lse,
+                       const float* dout, float* dxl, float* dxr, float* datt, gnn_plan* plan, void* stream);
+
+/* Graph Transformer backward (appendix D.2, backward pass: the cached
+ * logsumexp and Delta[i, h] = <out[i, h, :], dout[i, h, :]>, weights
+ * recomputed on the fly, a walk over A^T).  With e_ij = scale <q_i, k_j>,
+ * alpha_ij = exp(e_ij - lse_i) and de_ij = alpha_ij (<dO_i, v_j> - Delta_i):
+ *   dq[i] = scale sum_j de_ij k_j,  dk[j] = scale sum_i de_ij q_i,
+ *   dv[j] = sum_i alpha_ij dO_i.
+ * Inputs as in gnn_gt_fused (CSR layout; scale <= 0 means 1/sqrt(D)), plus
+ * out [n_rows, H, D], lse [n_rows, H] of the forward (required) and dout
+ * [n_rows, H, D] float32.  Outputs (float32): dq [n_rows, H, D], dk and dv
+ * [n_cols, H, D].  Two walks, no atomics, deterministic.  Supported shapes as
+ * in GNN_GT_CSR; all row tensors 16-byte aligned.
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype, int32_t H,
+                    int32_t D, float scale, const float* out, const float* lse, const float* dout, float* dq,
+                    float* dk, float* dv, gnn_plan* plan, void* stream);
 
 /* Vertex reordering of a square CSR (n_rows == n_cols).
  * DEGREE: perm sorts vertices by descending deg_in, ties by ascending id

@@ -705,7 +705,11 @@ static void softmax_weights(const double* logits, int32_t deg, double* alpha) {
  * de_ij = alpha_ij (g_ij - Delta_i), and
  *   dq_i += scale de_ij k_j,  dk_j += scale de_ij q_i,  dv_j += alpha_ij dO_i.
  * q [n_rows, H, D], k, v [n_cols, H, D] bf16; dO [n_rows, H, D] fp32; outputs
- * fp64 with magnitudes (sums of the absolute terms) for the error scale. */
+ * fp64.  The magnitudes (error scales) sum the absolute values of every
+ * product that enters an element, those inside de_ij included:
+ * |de|~ = alpha_ij (sum_d |dO_id v_jd| + sum_j' alpha_ij' sum_d |dO_id v_j'd|),
+ * dq_abs_i = scale sum_j |de|~ |k_j|, dk_abs_j = scale sum_i |de|~ |q_i|,
+ * dv_abs_j = sum_i alpha_ij |dO_i|. */
 int oracle_gt_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
                        const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t H, int32_t D,
                        float scale, const float* dO, double* dq, double* dk, double* dv, double* dq_abs,
@@ -720,17 +724,18 @@ int oracle_gt_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, c
   if (dk_abs) memset(dk_abs, 0, (size_t)n_cols * HD * 8);
   if (dv_abs) memset(dv_abs, 0, (size_t)n_cols * HD * 8);
   int32_t cap = 0;
-  double *e = NULL, *a = NULL, *g = NULL;
+  double *e = NULL, *a = NULL, *g = NULL, *ga = NULL;
   int rc = 0;
   for (int32_t i = 0; i < n_rows && rc == 0; ++i) {
     int32_t b = row_ptr[i], deg = row_ptr[i + 1] - b;
     if (deg > cap) {
-      free(e); free(a); free(g);
+      free(e); free(a); free(g); free(ga);
       cap = deg;
       e = (double*)malloc((size_t)cap * 8);
       a = (double*)malloc((size_t)cap * 8);
       g = (double*)malloc((size_t)cap * 8);
-      if (!e || !a || !g) { rc = -2; break; }
+      ga = (double*)malloc((size_t)cap * 8);
+      if (!e || !a || !g || !ga) { rc = -2; break; }
     }
     for (int32_t h = 0; h < H; ++h) {
       const uint16_t* qi = q + (int64_t)i * HD + (int64_t)h * D;
@@ -740,39 +745,44 @@ int oracle_gt_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, c
         if (j < 0 || j >= n_cols) { rc = -1; break; }
         const uint16_t* kj = k + (int64_t)j * HD + (int64_t)h * D;
         const uint16_t* vj = v + (int64_t)j * HD + (int64_t)h * D;
-        double dot = 0.0, gv = 0.0;
+        double dot = 0.0, gv = 0.0, gav = 0.0;
         for (int32_t d = 0; d < D; ++d) {
           dot += bf16_to_double(qi[d]) * bf16_to_double(kj[d]);
           gv += (double)doi[d] * bf16_to_double(vj[d]);
+          gav += fabs((double)doi[d] * bf16_to_double(vj[d]));
         }
         e[t] = dot * sc;
         g[t] = gv;
+        ga[t] = gav;
       }
       if (rc) break;
       if (deg == 0) continue;
       softmax_weights(e, deg, a);
-      double delta = 0.0;
-      for (int32_t t = 0; t < deg; ++t) delta += a[t] * g[t];
+      double delta = 0.0, delta_abs = 0.0;
+      for (int32_t t = 0; t < deg; ++t) {
+        delta += a[t] * g[t];
+        delta_abs += a[t] * ga[t];
+      }
       for (int32_t t = 0; t < deg; ++t) {
         int32_t j = col_idx[b + t];
         const uint16_t* kj = k + (int64_t)j * HD + (int64_t)h * D;
         const double de = a[t] * (g[t] - delta);
+        const double de_abs = a[t] * (ga[t] + delta_abs);
         for (int32_t d = 0; d < D; ++d) {
           const int64_t oi = (int64_t)i * HD + (int64_t)h * D + d, oj = (int64_t)j * HD + (int64_t)h * D + d;
-          const double tq = sc * de * bf16_to_double(kj[d]);
-          const double tk = sc * de * bf16_to_double(qi[d]);
+          const double kd = bf16_to_double(kj[d]), qd = bf16_to_double(qi[d]);
           const double tv = a[t] * (double)doi[d];
-          dq[oi] += tq;
-          dk[oj] += tk;
+          dq[oi] += sc * de * kd;
+          dk[oj] += sc * de * qd;
           dv[oj] += tv;
-          if (dq_abs) dq_abs[oi] += fabs(tq);
-          if (dk_abs) dk_abs[oj] += fabs(tk);
+          if (dq_abs) dq_abs[oi] += sc * de_abs * fabs(kd);
+          if (dk_abs) dk_abs[oj] += sc * de_abs * fabs(qd);
           if (dv_abs) dv_abs[oj] += fabs(tv);
         }
       }
     }
   }
-  free(e); free(a); free(g);
+  free(e); free(a); free(g); free(ga);
   return rc;
 }
 
@@ -787,7 +797,10 @@ int oracle_gt_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, c
  *   dr_j  += alpha_ij dO_i + de_ij a (.) s'(z_ij)
  *   da    += de_ij s(z_ij)            (summed over all entries)
  * xl [n_rows, H, D], xr [n_cols, H, D] bf16; att [H, D] fp32; dO fp32;
- * outputs fp64 with magnitudes for the error scale. */
+ * outputs fp64.  Magnitudes as for the Graph Transformer: with
+ * |de|~ = alpha_ij (sum_d |dO_id r_jd| + sum_j' alpha_ij' sum_d |dO_id r_j'd|),
+ * dl_abs += |de|~ |a (.) s'|, dr_abs += alpha |dO_i| + |de|~ |a (.) s'|,
+ * da_abs += |de|~ |s(z)|. */
 int oracle_gatv2_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
                           const uint16_t* xl, const uint16_t* xr, const float* att, int32_t H, int32_t D,
                           float slope, const float* dO, double* dl, double* dr, double* da, double* dl_abs,
@@ -802,17 +815,18 @@ int oracle_gatv2_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr
   if (dr_abs) memset(dr_abs, 0, (size_t)n_cols * HD * 8);
   if (da_abs) memset(da_abs, 0, (size_t)HD * 8);
   int32_t cap = 0;
-  double *e = NULL, *a = NULL, *g = NULL;
+  double *e = NULL, *a = NULL, *g = NULL, *ga = NULL;
   int rc = 0;
   for (int32_t i = 0; i < n_rows && rc == 0; ++i) {
     int32_t b = row_ptr[i], deg = row_ptr[i + 1] - b;
     if (deg > cap) {
-      free(e); free(a); free(g);
+      free(e); free(a); free(g); free(ga);
       cap = deg;
       e = (double*)malloc((size_t)cap * 8);
       a = (double*)malloc((size_t)cap * 8);
       g = (double*)malloc((size_t)cap * 8);
-      if (!e || !a || !g) { rc = -2; break; }
+      ga = (double*)malloc((size_t)cap * 8);
+      if (!e || !a || !g || !ga) { rc = -2; break; }
     }
     for (int32_t h = 0; h < H; ++h) {
       const uint16_t* li = xl + (int64_t)i * HD + (int64_t)h * D;
@@ -822,41 +836,47 @@ int oracle_gatv2_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr
         int32_t j = col_idx[b + t];
         if (j < 0 || j >= n_cols) { rc = -1; break; }
         const uint16_t* rj = xr + (int64_t)j * HD + (int64_t)h * D;
-        double ev = 0.0, gv = 0.0;
+        double ev = 0.0, gv = 0.0, gav = 0.0;
         for (int32_t d = 0; d < D; ++d) {
           double z = bf16_to_double(li[d]) + bf16_to_double(rj[d]);
           ev += (double)ah[d] * (z > 0.0 ? z : sl * z);
           gv += (double)doi[d] * bf16_to_double(rj[d]);
+          gav += fabs((double)doi[d] * bf16_to_double(rj[d]));
         }
         e[t] = ev;
         g[t] = gv;
+        ga[t] = gav;
       }
       if (rc) break;
       if (deg == 0) continue;
       softmax_weights(e, deg, a);
-      double G = 0.0;
-      for (int32_t t = 0; t < deg; ++t) G += a[t] * g[t];
+      double G = 0.0, G_abs = 0.0;
+      for (int32_t t = 0; t < deg; ++t) {
+        G += a[t] * g[t];
+        G_abs += a[t] * ga[t];
+      }
       for (int32_t t = 0; t < deg; ++t) {
         int32_t j = col_idx[b + t];
         const uint16_t* rj = xr + (int64_t)j * HD + (int64_t)h * D;
         const double de = a[t] * (g[t] - G);
+        const double de_abs = a[t] * (ga[t] + G_abs);
         for (int32_t d = 0; d < D; ++d) {
           const int64_t oi = (int64_t)i * HD + (int64_t)h * D + d, oj = (int64_t)j * HD + (int64_t)h * D + d;
           const double z = bf16_to_double(li[d]) + bf16_to_double(rj[d]);
           const double ds = z > 0.0 ? 1.0 : sl;
+          const double act = z > 0.0 ? z : sl * z;
           const double tl = de * (double)ah[d] * ds;
           const double tv = a[t] * (double)doi[d];
-          const double ta = de * (z > 0.0 ? z : sl * z);
           dl[oi] += tl;
           dr[oj] += tv + tl;
-          da[(int64_t)h * D + d] += ta;
-          if (dl_abs) dl_abs[oi] += fabs(tl);
-          if (dr_abs) dr_abs[oj] += fabs(tv) + fabs(tl);
-          if (da_abs) da_abs[(int64_t)h * D + d] += fabs(ta);
+          da[(int64_t)h * D + d] += de * act;
+          if (dl_abs) dl_abs[oi] += de_abs * fabs((double)ah[d] * ds);
+          if (dr_abs) dr_abs[oj] += fabs(tv) + de_abs * fabs((double)ah[d] * ds);
+          if (da_abs) da_abs[(int64_t)h * D + d] += de_abs * fabs(act);
         }
       }
     }
   }
-  free(e); free(a); free(g);
+  free(e); free(a); free(g); free(ga);
   return rc;
 }

@@ -73,6 +73,16 @@ INV, UNS, OVF = 1, 2, 5
     ("reorder null perm", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 0, None, None, None, None), INV),
     ("reorder one output", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 0, P(8), P(8), None, None), INV),
     ("reorder bad kind", lambda: call("gnn_reorder", ctypes.byref(fake_csr()), 4, P(8), None, None, None), INV),
+    ("spmm bwd null dY", lambda: call("gnn_spmm_backward", ctypes.byref(fake_csr()), None, 4, 4, P(16), 4, 0, None, None), INV),
+    ("spmm bwd ldx<F", lambda: call("gnn_spmm_backward", ctypes.byref(fake_csr()), P(16), 8, 8, P(16), 4, 0, None, None), INV),
+    ("spmm bwd bad norm", lambda: call("gnn_spmm_backward", ctypes.byref(fake_csr()), P(16), 4, 4, P(16), 4, 7, None, None), INV),
+    ("reduce bwd max without arg", lambda: call("gnn_reduce_backward", ctypes.byref(fake_csr()), 2, P(16), 4, 4, None, P(16), 4, None, None), INV),
+    ("reduce bwd bad op", lambda: call("gnn_reduce_backward", ctypes.byref(fake_csr()), 9, P(16), 4, 4, None, P(16), 4, None, None), INV),
+    ("gt bwd null lse", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), P(16), None, P(16), P(16), P(16), P(16), None, None), INV),
+    ("gt bwd too wide", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 256, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd misaligned", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), P(16), P(16), P(20), P(16), P(16), P(16), None, None), UNS),
+    ("gatv2 bwd null datt", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 4, 32, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), None, None, None), INV),
+    ("gatv2 bwd too wide", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
                                    ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),

@@ -622,7 +622,9 @@ def test_gt_backward_autograd(rng):
     rp, ci = gen.from_edges(n, *np.nonzero(A)[::-1])
     q, k, v = bf16(rng, (n, H, D)), bf16(rng, (n, H, D)), bf16(rng, (n, H, D))
     dO = rng.standard_normal((n, H, D)).astype(np.float32)
-    dq, dk, dv, *_ = oracle.gt_backward(rp, ci, q, k, v, dO)
+    dq, dk, dv, mq, mk, mv = oracle.gt_backward(rp, ci, q, k, v, dO)
+    for g, m in ((dq, mq), (dk, mk), (dv, mv)):      # error scales bound the values
+        assert np.all(m >= np.abs(g) * (1 - 1e-12))
     for h in range(H):
         Q, K, V = (torch.tensor(dec(x)[:, h], requires_grad=True) for x in (q, k, v))
         _dense_attention_grads(torch, A, lambda: (Q @ K.T) / math.sqrt(D), V,
@@ -640,7 +642,9 @@ def test_gatv2_backward_autograd(rng):
     xl[0, 0, :3] = gen.f32_to_bf16(-gen.bf16_to_f32(xr[0, 0, :3]))   # z = 0 exactly on a self loop
     att = rng.standard_normal((H, D)).astype(np.float32)
     dO = rng.standard_normal((n, H, D)).astype(np.float32)
-    dl, dr, da, *_ = oracle.gatv2_backward(rp, ci, xl, xr, att, dO, 0.2)
+    dl, dr, da, ml, mr, ma = oracle.gatv2_backward(rp, ci, xl, xr, att, dO, 0.2)
+    for g, m in ((dl, ml), (dr, mr), (da, ma)):
+        assert np.all(m >= np.abs(g) * (1 - 1e-12))
     slope = float(np.float32(0.2))
     for h in range(H):
         Lt, Rt = (torch.tensor(dec(x)[:, h], requires_grad=True) for x in (xl, xr))
