@@ -40,13 +40,17 @@ SOURCES = {
     "reduce_f128": _COMMON + ("aggregate.hip",),
     "gcn_small": _COMMON + ("aggregate.hip",),
     "spmm_large": _COMMON + ("aggregate.hip",),
-    "gatv2": _COMMON + ("attention.hip", "sort.hip"),
-    "gt_csr": _COMMON + ("attention.hip", "sort.hip"),
+    "gatv2": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
+    "gt_csr": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
     "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
     "copy": ("gnn_internal.h", "api.hip", "util.hip"),
     "plan_cfg2": _COMMON,
     "wsb_cfg4": _COMMON + ("wsb.hip", "sort.hip"),
     "reorder_cfg5": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
+    "spmm_bwd_cfg5": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
+    "reduce_bwd_cfg2": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
+    "gatv2_bwd_cfg3": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
+    "gt_bwd_cfg4": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
 }
 
 
@@ -73,7 +77,11 @@ def load_traffic(workload: str, kernel: str):
         return None
     if d.get("source_hash") != kernel_source_hash(workload):
         return None
-    return d.get("kernels", {}).get(kernel, {}).get("bytes_per_launch")
+    ks = d.get("kernels", {})
+    if isinstance(kernel, list):  # several kernels make one call: the sum of their bytes per call
+        tot = [v["bytes_per_launch"] for k, v in ks.items() if any(k.startswith(pfx) for pfx in kernel)]
+        return int(sum(tot)) if tot else None
+    return ks.get(kernel, {}).get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------
@@ -463,10 +471,163 @@ def wl_reorder(args):
             "config": cfg, "dtype": "int32", "cpu": cpu, "keep": (w, csr, X, Xo)}
 
 
+# ---------------------------------------------------------------------------
+# backward passes.  One op is one library call; the forward outputs they need
+# (out, lse, arg) and the plan's transpose are made during setup and warm-up.
+# Byte models: every gathered row and every written row once per use.
+# ---------------------------------------------------------------------------
+
+def wl_spmm_bwd(args):
+    """SpMM backward dX = A^T dY on R-MAT 16,000,000 nodes / 256,000,000 edges, dY 16M x 256 float32."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.spmm_rmat_large(with_x=False)
+    n, m, F = w.n, w.nnz, w.params["F"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    dY = torch.randn((n, F), device="cuda")
+    dX = torch.empty((n, F), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gnn.gnn_spmm_backward(csr, dY, "none", dX=dX, plan=plan)  # builds the transpose
+    torch.cuda.synchronize()
+    tr_ms = (time.perf_counter() - t0) * 1e3
+    # per entry of A^T: its row index + one dY row; per output row: pointer + the row
+    b = m * (4 + 4 * F) + n * (4 + 4 * F)
+    ops = [Op("spmm_bwd", lambda: gnn.gnn_spmm_backward(csr, dY, "none", dX=dX, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        s = gen.reduce_rmat(with_x=False)
+        dy = gen.gauss_f32(7, (s.n, 64))
+        return _edges_rate(lambda: oracle.spmm_backward(s.row_ptr, s.col_idx, dy), s.nnz,
+                           "SpMM backward, serial scatter", f"R-MAT {s.n} nodes / {s.nnz} edges, F = 64")
+
+    cfg = {"workload": "spmm_bwd_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
+           "F": F, "dy_dtype": "f32", "first_call_with_transpose_ms": round(tr_ms, 1),
+           "plan": gnn.gnn_plan_stats(plan)}
+    return {"ops": ops, "dominant": "spmm_bwd", "kernel": "k_aggregate<float, 64, 4, 0, false>", "config": cfg,
+            "dtype": "f32", "cpu": cpu, "keep": (w, csr, plan, dY, dX)}
+
+
+def wl_reduce_bwd(args):
+    """Reduction backward on R-MAT 1,000,000 nodes / 16,000,000 edges, F = 128: sum and mean
+    through the transpose, max and min by scatter through the forward's source indices."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.reduce_rmat()
+    n, m, F = w.n, w.nnz, w.params["F"]
+    X = torch.from_numpy(w.arrays["X"]).cuda()
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    fwd = gnn.gnn_reduce_multi(csr, X, plan=plan)
+    dY = torch.randn((n, F), device="cuda")
+    dX = torch.empty((n, F), dtype=torch.float32, device="cuda")
+    b_walk = m * (4 + 4 * F) + n * (4 + 4 * F)
+    b_scat = n * F * (4 + 4 + 4 + 8)   # arg, dY, zeroing dX, one read-modify-write per element
+    ops = [Op("sum_bwd", lambda: gnn.gnn_reduce_backward(csr, dY, "sum", dX=dX, plan=plan), m, b_walk),
+           Op("mean_bwd", lambda: gnn.gnn_reduce_backward(csr, dY, "mean", dX=dX, plan=plan), m, b_walk),
+           Op("max_bwd", lambda: gnn.gnn_reduce_backward(csr, dY, "max", arg=fwd["argmax"], dX=dX, plan=plan),
+              m, b_scat),
+           Op("min_bwd", lambda: gnn.gnn_reduce_backward(csr, dY, "min", arg=fwd["argmin"], dX=dX, plan=plan),
+              m, b_scat)]
+
+    def cpu(budget_s):
+        import oracle
+        dy = gen.gauss_f32(8, (n, F))
+        return _edges_rate(lambda: oracle.reduce_backward(w.row_ptr, w.col_idx, dy, "sum"), m,
+                           "sum backward, serial scatter", "the whole graph")
+
+    cfg = {"workload": "reduce_bwd_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
+           "F": F, "ops": ["sum", "mean", "max", "min"], "plan": gnn.gnn_plan_stats(plan)}
+    return {"ops": ops, "dominant": "sum_bwd", "kernel": "k_aggregate<float, 32, 4, 0, false>", "config": cfg,
+            "dtype": "f32", "cpu": cpu, "keep": (w, X, csr, plan, fwd, dY, dX)}
+
+
+def wl_gatv2_bwd(args):
+    """GATv2 backward on the GATv2 forward's workload (R-MAT 200,000 nodes, 4,000,000 edges +
+    self loops, H = 4, D = 32 bf16): destination walk (dxl, shares of datt) and source walk (dxr)."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gatv2_rmat()
+    n, m = w.n, w.nnz
+    H, D = w.params["H"], w.params["D"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    xl, xr = _to_bf16(w.arrays["xl"]), _to_bf16(w.arrays["xr"])
+    att = torch.from_numpy(w.arrays["att"]).cuda()
+    out, lse = gnn.gnn_gatv2_fused(csr, xl, xr, att, 0.2, plan=plan)
+    dO = torch.randn((n, H, D), device="cuda")
+    hd, rb = H * D, H * D * 2
+    b = (m * (4 + rb) + n * (rb + 12 * hd + 8 * H)              # destination walk
+         + m * (4 + rb + 4 * hd + 8 * H) + n * (4 + rb + 4 * hd))  # source walk
+    ops = [Op("gatv2_bwd", lambda: gnn.gnn_gatv2_backward(csr, xl, xr, att, out, lse, dO, 0.2, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        s = gen.gatv2_rmat(n=50_000, m=1_000_000)
+        do = gen.gauss_f32(9, (s.n, H, D))
+        return _edges_rate(lambda: oracle.gatv2_backward(s.row_ptr, s.col_idx, s.arrays["xl"], s.arrays["xr"],
+                                                         s.arrays["att"], do, 0.2), s.nnz,
+                           "GATv2 backward, fp64", f"R-MAT {s.n} nodes / {s.nnz} edges + self loops, same H, D")
+
+    cfg = {"workload": "gatv2_bwd_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)+self-loops", "nodes": n,
+           "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16"}
+    return {"ops": ops, "dominant": "gatv2_bwd", "kernel": "k_att_bwd (both walks)",
+            "traffic_kernels": ["k_att_bwd", "k_bwd_combine", "k_da_level"], "config": cfg, "dtype": "bf16",
+            "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse, dO)}
+
+
+def wl_gt_bwd(args):
+    """Graph Transformer backward on the cluster graph (512,000 nodes, H = 8, D = 64 bf16):
+    destination walk (dq) and source walk over the transpose (dk, dv)."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gt_cluster()
+    n, m = w.n, w.nnz
+    H, D = w.params["H"], w.params["D"]
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr)
+    q, k, v = (_to_bf16(w.arrays[x]) for x in ("q", "k", "v"))
+    out, lse = gnn.gnn_gt_fused(csr, q, k, v, plan=plan)
+    dO = torch.randn((n, H, D), device="cuda")
+    hd, rb = H * D, H * D * 2
+    b = (m * (4 + 2 * rb) + n * (rb + 12 * hd + 8 * H)                # destination walk
+         + m * (4 + rb + 4 * hd + 8 * H) + n * (4 + 2 * rb + 8 * hd))  # source walk
+    ops = [Op("gt_bwd", lambda: gnn.gnn_gt_backward(csr, q, k, v, out, lse, dO, plan=plan), m, b)]
+
+    def cpu(budget_s):
+        import oracle
+        s = gen.gt_cluster(n=32_000)
+        do = gen.gauss_f32(10, (s.n, H, D))
+        return _edges_rate(lambda: oracle.gt_backward(s.row_ptr, s.col_idx, s.arrays["q"], s.arrays["k"],
+                                                      s.arrays["v"], do), s.nnz,
+                           "Graph Transformer backward, fp64", f"cluster graph {s.n} nodes / {s.nnz} edges, same H, D")
+
+    cfg = {"workload": "gt_bwd_" + w.name, "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m,
+           "heads": H, "head_dim": D, "x_dtype": "bf16"}
+    return {"ops": ops, "dominant": "gt_bwd", "kernel": "k_att_bwd (both walks)",
+            "traffic_kernels": ["k_att_bwd", "k_bwd_combine"], "config": cfg, "dtype": "bf16", "cpu": cpu,
+            "keep": (w, csr, plan, q, k, v, out, lse, dO)}
+
+
 WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
              "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
              "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
-             "reorder_cfg5": wl_reorder}
+             "reorder_cfg5": wl_reorder, "spmm_bwd_cfg5": wl_spmm_bwd, "reduce_bwd_cfg2": wl_reduce_bwd,
+             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd}
 
 
 # ---------------------------------------------------------------------------
@@ -531,7 +692,7 @@ def main():
     dom = next(o for o in ops if o.name == w["dominant"])
     dom_ms = per_op_ms[dom.name]
     achieved = dom.bytes_alg / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(args.workload, w["kernel"])
+    traffic = load_traffic(args.workload, w.get("traffic_kernels", w["kernel"]))
 
     out = {
         "metric": METRIC,
