@@ -19,7 +19,9 @@
 // accumulates the destination gradient (dq_i, or dl_i and the workgroup's
 // share of da).  The source walk (rows of the plan's transpose) recomputes
 // the same alpha and de per entry from the stored L_i and Delta_i and
-// accumulates the source gradients.  Every output row is summed by one slot,
+// accumulates the source gradients.  Short rows take one slot each, in the
+// plan's length-sorted row list (as the forward kernels).  Every output row is
+// summed by one slot,
 // one workgroup, or ordered chunk partials (hub rows), so results are
 // deterministic; the pages' own backward instead updates one gradient with
 // atomic adds along the transposed walk, which at H * D = 512 would be 512
@@ -36,7 +38,7 @@ using namespace att;
 
 constexpr int WG = 256;
 constexpr int UB = 4;                 // entries in flight per slot
-constexpr int32_t kBwdLightMax = 64;  // one slot per row up to this many entries
+constexpr int32_t kBwdLightMax = 128;  // one slot per row up to this many entries
 
 enum { B_GT_DST = 0, B_GT_SRC = 1, B_GAT_DST = 2, B_GAT_SRC = 3 };
 
@@ -47,6 +49,8 @@ struct BwdParams {
   const int4* items;
   int32_t n_rows;
   int32_t light_max;
+  const int32_t* light_rows;   // rows of at most light_max entries, by length within windows
+  const int32_t* light_count;  // device: how many
   int32_t n_item_blocks;
   int32_t n_light_blocks;
   // tensors: "dst" are indexed by destinations (rows of the CSR), "src" by sources
@@ -264,12 +268,12 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     }
   } else {
     const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
-    row = ((int64_t)lb * NWAVE + wave) * SPW + sw;
-    active = row < p.n_rows;
+    const int64_t idx = ((int64_t)lb * NWAVE + wave) * SPW + sw;
+    active = idx < *p.light_count;
     if (active) {
+      row = p.light_rows[idx];
       eb = p.row_ptr[row];
       ee = p.row_ptr[row + 1];
-      active = ee - eb <= p.light_max;
     }
   }
   if (KIND != B_GAT_DST && !active) return;  // uniform over the workgroup for items, over the slot otherwise
@@ -403,9 +407,8 @@ __global__ __launch_bounds__(256) void k_bwd_combine(const float* part, const in
   }
 }
 
-// da = sum over workgroups of their shares, in two ordered levels: block b
-// sums rows [b * per, (b + 1) * per) of the shares into mid[b], then one
-// block sums mid.
+// da = sum over workgroups of their shares, as a tree of ordered levels:
+// block b of a level sums rows [b * per, (b + 1) * per) of its input.
 __global__ __launch_bounds__(256) void k_da_level(const float* in, int64_t rows, int64_t per, int32_t cols,
                                                   float* out) {
   const int64_t r0 = (int64_t)blockIdx.x * per, r1 = min(rows, r0 + per);
@@ -424,6 +427,9 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   p.items = pl->items;
   p.n_rows = pl->n_rows;
   p.light_max = std::max(pl->light_max, std::min(kBwdLightMax, pl->heavy_thr));
+  GNN_TRY(plan_att_rows(pl, p.light_max, s));
+  p.light_rows = pl->att_rows;
+  p.light_count = pl->att_count;
   p.n_item_blocks = (int32_t)pl->n_items;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
@@ -431,7 +437,8 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   const size_t part_b = ((size_t)std::max<int64_t>(pl->n_items, 1) * 2 * p.row_elems * 4 + 255) & ~(size_t)255;
   const size_t da_b = KIND == B_GAT_DST ? (size_t)gx * p.row_elems * 4 : 0;
   void* ws = nullptr;
-  GNN_TRY(plan_workspace(pl, part_b + da_b + 2 * 256 * (size_t)p.row_elems * 4 + 256, &ws));
+  const size_t mid_b = 2 * (size_t)((gx + 15) / 16 + 1) * p.row_elems * 4;
+  GNN_TRY(plan_workspace(pl, part_b + da_b + (KIND == B_GAT_DST ? mid_b : 0) + 256, &ws));
   p.part = (float*)ws;
   p.dapart = KIND == B_GAT_DST ? (float*)((char*)ws + part_b) : nullptr;
   if (gx > 0) {
@@ -444,16 +451,22 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
     GNN_LAUNCH_CHECK("attention backward combine");
   }
   if constexpr (KIND == B_GAT_DST) {
-    // da: ordered two-level sum of the workgroup shares
-    float* mid = (float*)((char*)ws + part_b + da_b);
-    const int64_t nb = std::min<int64_t>(256, std::max<int64_t>(gx, 1));
-    const int64_t per = (std::max<int64_t>(gx, 1) + nb - 1) / nb;
-    if (gx > 0) {
-      hipLaunchKernelGGL(k_da_level, dim3((unsigned)nb), dim3(256), 0, s, p.dapart, gx, per, p.row_elems, mid);
-      hipLaunchKernelGGL(k_da_level, dim3(1), dim3(256), 0, s, mid, nb, nb, p.row_elems, p.g1);
-    } else {
-      hipLaunchKernelGGL(k_da_level, dim3(1), dim3(256), 0, s, mid, 0, 1, p.row_elems, p.g1);
+    // da: the workgroup shares summed by an ordered tree, 16 rows per block
+    // and level (two scratch areas of ceil(gx / 16) rows alternate)
+    constexpr int64_t PER = 16;
+    float* mid[2] = {(float*)((char*)ws + part_b + da_b), nullptr};
+    mid[1] = mid[0] + ((gx + PER - 1) / PER + 1) * p.row_elems;
+    const float* in = p.dapart;
+    int64_t rows = gx;
+    int lvl = 0;
+    while (rows > PER) {
+      const int64_t nb = (rows + PER - 1) / PER;
+      hipLaunchKernelGGL(k_da_level, dim3((unsigned)nb), dim3(256), 0, s, in, rows, PER, p.row_elems, mid[lvl]);
+      in = mid[lvl];
+      rows = nb;
+      lvl ^= 1;
     }
+    hipLaunchKernelGGL(k_da_level, dim3(1), dim3(256), 0, s, in, rows, PER, p.row_elems, p.g1);
     GNN_LAUNCH_CHECK("attention backward da");
   }
   return GNN_OK;
