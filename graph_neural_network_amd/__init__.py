@@ -26,7 +26,7 @@ STATUS = {0: "GNN_OK", 1: "GNN_ERR_INVALID_VALUE", 2: "GNN_ERR_UNSUPPORTED",
 DTYPE = {"f32": 0, "bf16": 1}
 NORM = {"none": 0, "left": 1, "right": 2, "both": 3}
 REDUCE_OP = {"sum": 0, "mean": 1, "max": 2, "min": 3}
-GT_MODE = {"csr": 0, "block16": 1}
+GT_MODE = {"csr": 0, "block16": 1, "auto": 2}
 REORDER = {"degree": 0, "rcm": 1}
 
 # every symbol include/gnn.h declares

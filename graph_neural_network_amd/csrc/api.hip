@@ -249,9 +249,21 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
 int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype,
                  int32_t H, int32_t D, float scale, gnn_gt_mode mode, float* out, float* lse,
                  gnn_plan* plan, void* stream) {
+  if (mode != GNN_GT_CSR && mode != GNN_GT_BLOCK16 && mode != GNN_GT_AUTO)
+    return fail(GNN_ERR_INVALID_VALUE, "unknown GT mode");
+  if (mode == GNN_GT_AUTO) {
+    const int64_t esz0 = xtype == GNN_BF16 ? 2 : 4;
+    bool fits = xtype == GNN_BF16 && (D == 32 || D == 64 || D == 128) && csr && csr->n_rows == csr->n_cols &&
+                (D * esz0) % 16 == 0 && H > 0 && H * D * esz0 <= 2048;
+    mode = GNN_GT_CSR;
+    if (fits && plan && plan->has_wsb && check_plan(plan, csr) == GNN_OK) {
+      const int64_t dense = plan->nnz - plan->wsb.n_resid;
+      if (plan->wsb.n_tiles > 0 && 2 * dense >= plan->nnz && dense >= 32 * plan->wsb.n_tiles)
+        mode = GNN_GT_BLOCK16;
+    }
+  }
   GNN_TRY(check_csr(csr, mode == GNN_GT_BLOCK16));
   GNN_TRY(check_dtype(xtype));
-  if (mode != GNN_GT_CSR && mode != GNN_GT_BLOCK16) return fail(GNN_ERR_INVALID_VALUE, "unknown GT mode");
   if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
   if (!q || !out || ((!k || !v) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "q, k, v or out is NULL");

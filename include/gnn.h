@@ -74,8 +74,14 @@ typedef enum { GNN_SUM = 0, GNN_MEAN = 1, GNN_MAX = 2, GNN_MIN = 3 } gnn_reduce_
 
 /* Graph Transformer kernel choice: streaming CSR (appendix D.2) or the
  * 16x16 block-sparse matrix-core path on WSB tiles (appendix D.3), whose
- * sparse leftovers are processed by the CSR loop inside the same kernel. */
-typedef enum { GNN_GT_CSR = 0, GNN_GT_BLOCK16 = 1 } gnn_gt_mode;
+ * sparse leftovers are processed by the CSR loop inside the same kernel.
+ * AUTO picks from the plan's tiles (the pages' adaptive selection by local
+ * density, appendix D.3): BLOCK16 when the plan has WSB tiles, the input
+ * fits BLOCK16, at least half of the entries lie in dense tiles and those
+ * average at least 32 entries per 16x16 tile (below that a tile's 32 gathered
+ * K / V rows serve fewer entries than CSR's two rows per entry would); CSR
+ * otherwise, and always without a plan with WSB tiles. */
+typedef enum { GNN_GT_CSR = 0, GNN_GT_BLOCK16 = 1, GNN_GT_AUTO = 2 } gnn_gt_mode;
 
 typedef enum { GNN_REORDER_DEGREE = 0, GNN_REORDER_RCM = 1 } gnn_reorder_kind;
 

@@ -134,3 +134,27 @@ def test_gt_block16_cluster512k_full():
     rows = np.unique(rng.integers(0, rp.size - 1, 3000)).astype(np.int32)
     ro, rl, va = oracle.gt(rp, ci, q, k, v, rows=rows)
     check(out, lse, ro, rl, va, rows=rows)
+
+
+def test_gt_auto_mode_selection():
+    """AUTO takes BLOCK16 on a locally dense graph (tiles of ~100 entries) and
+    CSR on a power-law graph (tiles of ~16 entries) or without a WSB plan; the
+    outputs are then bit-identical to the chosen mode's."""
+    H, D = 4, 64
+    for rp, ci, want in ((*gen.cluster(0x5EED0340, 64 * 24, 64, 0.5, 0.01, self_loops=True), "block16"),
+                         (*gen.rmat(0x5EED0341, 4000, 60000, self_loops=True), "csr")):
+        n = rp.size - 1
+        q, k, v = (dev_bf16(gen.gauss_bf16(0x4000 + i, (n, H, D))) for i in range(3))
+        csr = dev_csr(rp, ci)
+        plan = gnn.gnn_plan_create(csr, build_wsb=True)
+        st = gnn.gnn_plan_stats(plan)
+        dense = ci.size - st["wsb_residual_edges"]
+        chosen = "block16" if (2 * dense >= ci.size and dense >= 32 * max(st["wsb_dense_tiles"], 1)
+                               and st["wsb_dense_tiles"] > 0) else "csr"
+        assert chosen == want, (want, st)
+        oa, la = gnn.gnn_gt_fused(csr, q, k, v, mode="auto", plan=plan)
+        ow, lw = gnn.gnn_gt_fused(csr, q, k, v, mode=want, plan=plan)
+        assert torch.equal(oa, ow) and torch.equal(la, lw), want
+        on, ln = gnn.gnn_gt_fused(csr, q, k, v, mode="auto")   # no plan: CSR
+        oc, lc = gnn.gnn_gt_fused(csr, q, k, v, mode="csr")
+        assert torch.equal(on, oc) and torch.equal(ln, lc)
