@@ -33,7 +33,8 @@ REORDER = {"degree": 0, "rcm": 1}
 EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
-           "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward")
+           "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
+           "gnn_spmm_block16")
 
 
 class GnnError(RuntimeError):
@@ -83,6 +84,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_permute_rows": [vp, i32, vp, ci, i32, i64, vp, i64, vp],
         "gnn_copy_bytes": [vp, vp, i64, vp],
         "gnn_spmm_backward": [P(_Csr), vp, i32, i64, vp, i64, ci, vp, vp],
+        "gnn_spmm_block16": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
         "gnn_reduce_backward": [P(_Csr), ci, vp, i32, i64, vp, vp, i64, vp, vp],
         "gnn_gatv2_backward": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_gt_backward": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
@@ -208,6 +210,17 @@ def gnn_spmm(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | No
     _check(load_library().gnn_spmm(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y),
                                    Y.stride(0), NORM[norm], _plan_h(plan), _stream(stream)),
            "gnn_spmm")
+    return Y
+
+
+def gnn_spmm_block16(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | None = None,
+                     plan: Plan | None = None, stream=None) -> torch.Tensor:
+    """Y = A_norm X on the plan's 16 x 16 block-sparse tiles (plan built with build_wsb)."""
+    F = X.shape[1]
+    if Y is None:
+        Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    _check(load_library().gnn_spmm_block16(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y), Y.stride(0),
+                                           NORM[norm], _plan_h(plan), _stream(stream)), "gnn_spmm_block16")
     return Y
 
 

@@ -186,6 +186,27 @@ int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int6
   return launch_aggregate(p, X, xtype, F, ldx, Y, ldy, AGG_SPMM, norm, csr->edge_val, nullptr, s);
 }
 
+int gnn_spmm_block16(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
+                     int64_t ldy, gnn_norm norm, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, true));
+  GNN_TRY(check_dtype(xtype));
+  if (norm < GNN_NORM_NONE || norm > GNN_NORM_BOTH) return fail(GNN_ERR_INVALID_VALUE, "unknown norm");
+  if (F <= 0 || ldx < F || ldy < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldx >= F, ldy >= F");
+  if (!Y || (!X && csr->n_cols > 0)) return fail(GNN_ERR_INVALID_VALUE, "X or Y is NULL");
+  if (csr->edge_val) return fail(GNN_ERR_UNSUPPORTED, "the block-sparse SpMM takes no edge values");
+  const int64_t epc = xtype == GNN_BF16 ? 8 : 4;  // elements per 16-byte chunk
+  if (F % epc != 0 || ldx % epc != 0 || ldy % 4 != 0 || ((uintptr_t)X | (uintptr_t)Y) % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "block-sparse SpMM needs 16-byte rows: F and ldx multiples of 16 bytes, "
+                                     "ldy a multiple of 4, X and Y 16-byte aligned");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, true));
+  PlanGuard g{p, tr};
+  return launch_spmm_block16(p, X, xtype, F, ldx, Y, ldy, norm, s);
+}
+
 int gnn_reduce(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
                gnn_reduce_op op, float* Y, int64_t ldy, int32_t* arg, gnn_plan* plan, void* stream) {
   GNN_TRY(check_csr(csr, false));

@@ -154,6 +154,9 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
 int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
                    hipStream_t s);
 
+int launch_spmm_block16(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y, int64_t ldy,
+                        gnn_norm norm, hipStream_t s);
+
 // Backward launchers (transposed walks; see transpose.hip, attention_bwd.hip)
 int launch_spmm_backward(gnn_plan* p, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
                          gnn_norm norm, const float* edge_val, hipStream_t s);

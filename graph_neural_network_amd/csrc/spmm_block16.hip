@@ -1,0 +1,219 @@
+// SpMM on 16 x 16 block-sparse tiles with fp32 matrix cores (WSB-SpMM).
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", appendix D.3: the windowed segmented bitmap format
+// (16-row windows, blocks of 8 distinct source columns with a 128-bit mask)
+// serves the SpMM convolution as well as attention: per window, each dense
+// 16 x 16 tile of A multiplies the 16 gathered feature rows of its columns,
+// so a gathered row serves every entry of its column in the window instead of
+// one.  The plan's residual CSR (entries of tiles below the density
+// threshold) is added by a plain loop into the same accumulators.
+//
+// MI355X mapping.  One workgroup per (window, 256-feature slice); wave w owns
+// features 64 w .. 64 w + 63 of the slice as four 16-wide chunks.  For each
+// dense tile the workgroup stages the 16 X rows (the slice of each) in LDS,
+// double-buffered (the next tile's rows are loaded into registers while the
+// current one computes), and each wave runs 4 k-steps x 4 chunks of
+// v_mfma_f32_16x16x4_f32.  A is built in registers from the tile bitmap and
+// the column weights in fp32, and B is read from LDS as fp32, so every product
+// is an fp32 product, as in the CSR kernel.  Lane layouts (checked on the
+// device): A: lane l holds A[l % 16][l / 16]; B: lane l holds B[l / 16][l % 16];
+// D: lane l holds D[4 (l / 16) + r][l % 16], r = 0..3.  Output rows are staged
+// through LDS so that each store writes whole lines.
+#include <algorithm>
+
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+constexpr int FW = 256;  // features per workgroup
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct B16SpmmParams {
+  const int32_t* row_ptr;
+  const int32_t* deg_out;
+  const int32_t* win_ptr;
+  const int32_t* blk_col;
+  const unsigned long long* blk_bits;
+  const int32_t* tile_ptr;
+  const int32_t* tile_blk;
+  const int32_t* res_ptr;
+  const int32_t* res_col;
+  const void* X;
+  int64_t ldx;
+  float* Y;
+  int64_t ldy;
+  int32_t F;
+  int32_t n_rows;
+  int32_t norm;
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// weight of a column j (the destination's factor is applied per row at the end)
+__device__ __forceinline__ float col_weight(const B16SpmmParams& p, int j) {
+  if (p.norm == GNN_NORM_RIGHT) return 1.0f / (float)p.deg_out[j];
+  if (p.norm == GNN_NORM_BOTH) return rsqrtf((float)p.deg_out[j]);
+  return 1.0f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_spmm_b16(B16SpmmParams p) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPR = FW / EPC;              // chunks per staged row slice
+  constexpr int CPT = 16 * CPR / 256;        // chunks per thread per tile
+  __shared__ __align__(16) T s_x[2][16][FW];
+  __shared__ int32_t s_cols[2][16];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const int f0 = blockIdx.y * FW;                 // first feature of the slice
+  const int fw = f0 + wave * 64;                  // first feature of this wave
+  const int t_beg = p.tile_ptr[w], t_end = p.tile_ptr[w + 1];
+  const int b_end = p.win_ptr[w + 1];
+  const T* X = reinterpret_cast<const T*>(p.X);
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // column of tile column c (0..15) of tile t; 0 where the second block is past the window
+  auto tile_col = [&](int t, int c) -> int {
+    const int blk = p.tile_blk[t] + (c >> 3);
+    return ((c >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+  };
+  // this thread's share of the 16 staged rows of tile t
+  uint4 pre[CPT];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int chunk = threadIdx.x + q * 256;   // 0 .. 16 * CPR - 1
+      const int r = chunk / CPR, cc = chunk % CPR;
+      const int col = tile_col(t, r);
+      const int f = f0 + cc * EPC;
+      pre[q] = (f < p.F) ? *reinterpret_cast<const uint4*>(X + (int64_t)col * p.ldx + f) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf, int t) {
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+      const int chunk = threadIdx.x + q * 256;
+      const int r = chunk / CPR, cc = chunk % CPR;
+      *reinterpret_cast<uint4*>(&s_x[buf][r][cc * EPC]) = pre[q];
+    }
+    if (threadIdx.x < 16) s_cols[buf][threadIdx.x] = tile_col(t, threadIdx.x);
+  };
+
+  if (t_beg < t_end) {
+    load_tile(t_beg);
+    store_tile(0, t_beg);
+  }
+  __syncthreads();
+  for (int t = t_beg; t < t_end; ++t) {
+    const int buf = (t - t_beg) & 1;
+    if (t + 1 < t_end) load_tile(t + 1);
+    // A values of this lane: row li, tile columns 4 s + lg
+    float a[4];
+    const int blk0 = p.tile_blk[t];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = 4 * s + lg;
+      const int blk = blk0 + (c >> 3);
+      const bool have = !((c >> 3) == 1 && blk >= b_end);
+      const unsigned long long word = have ? p.blk_bits[(int64_t)blk * 2 + (li >> 3)] : 0ull;
+      const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
+      a[s] = bit ? col_weight(p, s_cols[buf][c]) : 0.0f;
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int fl = wave * 64 + ch * 16 + li;   // feature within the slice
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float b = to_f32<T>(s_x[buf][4 * s + lg][fl]);
+        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[ch], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // every wave is done with the other buffer before it is refilled
+    if (t + 1 < t_end) store_tile(buf ^ 1, t + 1);
+    __syncthreads();
+  }
+
+  // residual entries of the window's rows: lane (li, lg) owns rows 4 lg .. 4 lg + 3 of
+  // feature fw + 16 ch + li
+  const int row0 = w * 16;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * lg + r;
+    if (row >= p.n_rows) continue;
+    const int e1 = p.res_ptr[row + 1];
+    for (int e = p.res_ptr[row]; e < e1; ++e) {
+      const int j = p.res_col[e];
+      const float wj = col_weight(p, j);
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const int f = fw + ch * 16 + li;
+        if (f < p.F) acc[ch][r] = fmaf(wj, to_f32<T>(X[(int64_t)j * p.ldx + f]), acc[ch][r]);
+      }
+    }
+  }
+
+  // destination factor, then stage the 16 x FW slice in LDS and store whole rows
+  float* s_y = reinterpret_cast<float*>(&s_x[0][0][0]);   // 16 x FW floats fit the two buffers
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = row0 + 4 * lg + r;
+    float rf = 1.0f;
+    if (row < p.n_rows && (p.norm == GNN_NORM_LEFT || p.norm == GNN_NORM_BOTH)) {
+      const int d = p.row_ptr[row + 1] - p.row_ptr[row];
+      rf = d > 0 ? (p.norm == GNN_NORM_LEFT ? 1.0f / (float)d : rsqrtf((float)d)) : 0.0f;
+    }
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) s_y[(4 * lg + r) * FW + wave * 64 + ch * 16 + li] = acc[ch][r] * rf;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 16 * FW / 4; q += 256) {
+    const int r = q / (FW / 4), f = f0 + (q % (FW / 4)) * 4;
+    const int row = row0 + r;
+    if (row < p.n_rows && f < p.F)
+      *reinterpret_cast<float4*>(p.Y + (int64_t)row * p.ldy + f) =
+          *reinterpret_cast<const float4*>(s_y + r * FW + (f - f0));
+  }
+}
+
+}  // namespace
+
+int launch_spmm_block16(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y, int64_t ldy,
+                        gnn_norm norm, hipStream_t s) {
+  B16SpmmParams p{};
+  p.row_ptr = pl->row_ptr;
+  p.deg_out = pl->deg_out;
+  p.win_ptr = pl->wsb.win_ptr;
+  p.blk_col = pl->wsb.blk_col;
+  p.blk_bits = (const unsigned long long*)pl->wsb.blk_bits;
+  p.tile_ptr = pl->wsb.tile_ptr;
+  p.tile_blk = pl->wsb.tile_blk;
+  p.res_ptr = pl->wsb.res_ptr;
+  p.res_col = pl->wsb.res_col;
+  p.X = X;
+  p.ldx = ldx;
+  p.Y = Y;
+  p.ldy = ldy;
+  p.F = F;
+  p.n_rows = pl->n_rows;
+  p.norm = (int)norm;
+  if (pl->wsb.n_windows == 0) return GNN_OK;
+  const dim3 grid((unsigned)pl->wsb.n_windows, (unsigned)((F + FW - 1) / FW));
+  if (xt == GNN_BF16) hipLaunchKernelGGL(k_spmm_b16<uint16_t>, grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL(k_spmm_b16<float>, grid, dim3(256), 0, s, p);
+  GNN_LAUNCH_CHECK("spmm block16");
+  return GNN_OK;
+}
+
+}  // namespace gnn

@@ -6,6 +6,7 @@
  * implementations"; section 2.2 names the three operator families, appendix D
  * gives the kernels):
  *   gnn_spmm         SpMM-based convolution Y = A_norm X      (section 2.2 (i), appendix D.4)
+ *   gnn_spmm_block16 the same on 16x16 block-sparse tiles      (appendix D.3)
  *   gnn_reduce       segmented sum / mean / max / min          (section 2.2 (ii), appendix D.1)
  *   gnn_reduce_multi the four reductions in one pass           (section 2.2 (ii), appendix D.1)
  *   gnn_gatv2_fused  GATv2 attention, one pass, online softmax (section 2.2 (iii), appendix D.2)
@@ -148,6 +149,23 @@ int gnn_plan_wsb_export(const gnn_plan* plan, int32_t* win_ptr, int32_t* blk_col
  * PLAN_MISMATCH, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
 int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
              int64_t ldy, gnn_norm norm, gnn_plan* plan, void* stream);
+
+/* Block-sparse SpMM on the plan's WSB tiles (appendix D.3, the windowed
+ * segmented bitmap format serving SpMM): the same product as gnn_spmm
+ * (Y = A_norm X, norms as there), with each dense 16 x 16 tile of a 16-row
+ * window multiplied by the 16 gathered feature rows of its columns on fp32
+ * matrix cores (v_mfma_f32_16x16x4_f32: weights and features enter as fp32,
+ * so products are fp32 products), and the plan's residual CSR added by a
+ * plain loop.  For locally dense graphs, where a gathered row then serves
+ * many entries of its window.  Needs a square CSR without edge values
+ * (UNSUPPORTED otherwise) and a plan built with build_wsb = 1 (NULL builds a
+ * transient one, WSB included); X device [n_cols, F] `xtype` with F and ldx
+ * whole 16-byte chunks and X 16-byte aligned; Y device [n_rows, F] float32,
+ * 16-byte aligned, ldy a multiple of 4.  Deterministic; the summation order
+ * differs from gnn_spmm's.
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_spmm_block16(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
+                     int64_t ldy, gnn_norm norm, gnn_plan* plan, void* stream);
 
 /* Segmented reduction over each row's sources: Y[i, f] = op_j X[j, f].
  * arg: device [n_rows, lda = F] int32 or NULL; for MAX / MIN it receives the

@@ -83,6 +83,9 @@ INV, UNS, OVF = 1, 2, 5
     ("gt bwd misaligned", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), P(16), P(16), P(20), P(16), P(16), P(16), None, None), UNS),
     ("gatv2 bwd null datt", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 4, 32, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), None, None, None), INV),
     ("gatv2 bwd too wide", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("spmm b16 non-square", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), 1, 16, 16, P(16), 16, 0, None, None), INV),
+    ("spmm b16 F not 16 B", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(16), 1, 12, 12, P(16), 12, 0, None, None), UNS),
+    ("spmm b16 misaligned", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(24), 0, 16, 16, P(16), 16, 0, None, None), UNS),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
                                    ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),

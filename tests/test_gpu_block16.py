@@ -158,3 +158,54 @@ def test_gt_auto_mode_selection():
         on, ln = gnn.gnn_gt_fused(csr, q, k, v, mode="auto")   # no plan: CSR
         oc, lc = gnn.gnn_gt_fused(csr, q, k, v, mode="csr")
         assert torch.equal(on, oc) and torch.equal(ln, lc)
+
+
+# ---------------------------------------------------------------------------
+# block-sparse SpMM (fp32 matrix cores on the WSB tiles)
+# ---------------------------------------------------------------------------
+
+SPMM_TOL = 1e-5
+
+
+@pytest.mark.parametrize("norm", ["none", "left", "right", "both"])
+@pytest.mark.parametrize("F,dt", [(256, "bf16"), (64, "bf16"), (200, "bf16"), (512, "bf16"), (128, "f32"),
+                                  (36, "f32")])
+@pytest.mark.parametrize("tau", [1, 8, 10**6])
+def test_spmm_block16_cluster(norm, F, dt, tau):
+    rp, ci = gen.cluster(0x5EED0350, 64 * 25, 64, 0.4, 0.02, self_loops=True)
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, build_wsb=True, wsb_min_nnz=tau)
+    st = gnn.gnn_plan_stats(plan)
+    if tau == 10**6:
+        assert st["wsb_dense_tiles"] == 0
+    if dt == "bf16":
+        Xh = gen.gauss_bf16(0x5000 + F, (n, F))
+        Xd = dev_bf16(Xh)
+    else:
+        Xh = gen.gauss_f32(0x5000 + F, (n, F))
+        Xd = torch.from_numpy(Xh).cuda()
+    Y = host(gnn.gnn_spmm_block16(csr, Xd, norm, plan=plan))
+    ref, mag = oracle.spmm(rp, ci, Xh, norm, x_is_bf16=dt == "bf16")
+    assert scaled_err(Y, ref, mag) <= SPMM_TOL, (norm, F, dt, tau)
+    Y2 = host(gnn.gnn_spmm_block16(csr, Xd, norm, plan=plan))
+    assert np.array_equal(Y, Y2), "not deterministic"
+
+
+def test_spmm_block16_rmat_partial_window_and_errors():
+    rp, ci = gen.rmat(0x5EED0351, 3003, 40000)
+    n = rp.size - 1
+    assert (np.diff(rp) == 0).any()
+    csr = dev_csr(rp, ci)
+    Xh = gen.gauss_bf16(0x5100, (n, 96))
+    for norm in ("none", "both"):
+        Y = host(gnn.gnn_spmm_block16(csr, dev_bf16(Xh), norm))      # transient plan with WSB
+        ref, mag = oracle.spmm(rp, ci, Xh, norm, x_is_bf16=True)
+        assert scaled_err(Y, ref, mag) <= SPMM_TOL
+        assert np.all(Y[np.diff(rp) == 0] == 0)
+    ev = dev_csr(rp, ci, edge_val=np.ones(ci.size, np.float32))
+    with pytest.raises(gnn.GnnError):
+        gnn.gnn_spmm_block16(ev, dev_bf16(Xh))
+    plain = gnn.gnn_plan_create(csr)
+    with pytest.raises(gnn.GnnError):
+        gnn.gnn_spmm_block16(csr, dev_bf16(Xh), plan=plain)        # no WSB tiles in the plan
