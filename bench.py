@@ -35,7 +35,7 @@ METRIC = "aggregation edges/s and achieved HBM GB/s (% of 8 TB/s) at F=128, 1 GP
 
 
 # sources that decide each workload's dominant kernel and the plan it reads
-_COMMON = ("gnn_internal.h", "api.hip", "preprocess.hip")
+_COMMON = ("gnn_internal.h", "preprocess.hip")
 SOURCES = {
     "reduce_f128": _COMMON + ("aggregate.hip",),
     "gcn_small": _COMMON + ("aggregate.hip",),
@@ -43,7 +43,7 @@ SOURCES = {
     "gatv2": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
     "gt_csr": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
     "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
-    "copy": ("gnn_internal.h", "api.hip", "util.hip"),
+    "copy": ("gnn_internal.h", "util.hip"),
     "plan_cfg2": _COMMON,
     "wsb_cfg4": _COMMON + ("wsb.hip", "sort.hip"),
     "reorder_cfg5": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
@@ -51,6 +51,7 @@ SOURCES = {
     "reduce_bwd_cfg2": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
     "gatv2_bwd_cfg3": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
     "gt_bwd_cfg4": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
+    "spmm_b16_cfg4": _COMMON + ("spmm_block16.hip", "wsb.hip", "sort.hip"),
 }
 
 
@@ -471,6 +472,46 @@ def wl_reorder(args):
             "config": cfg, "dtype": "int32", "cpu": cpu, "keep": (w, csr, X, Xo)}
 
 
+def wl_spmm_b16(args):
+    """SpMM Y = D^-1/2 A D^-1/2 X on the 512,000-node cluster graph (64-node clusters, p = 0.5,
+    1% inter-cluster, self loops), X 512k x 256 bf16: block-sparse tiles on fp32 matrix cores,
+    beside the CSR kernel on the same input."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    w = gen.gt_cluster(with_x=False)
+    n, m, F = w.n, w.nnz, 256
+    csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    plan = gnn.gnn_plan_create(csr, build_wsb=True)
+    st = gnn.gnn_plan_stats(plan)
+    X = torch.randn((n, F), device="cuda").to(torch.bfloat16)
+    Y = torch.empty((n, F), dtype=torch.float32, device="cuda")
+    rb = F * 2
+    # per dense tile: 16 X rows + two block descriptors (32 B columns + 16 B bitmap each);
+    # per residual entry: column + X row; per row: Y row + residual and row pointers;
+    # per window: two offsets
+    b16 = (st["wsb_dense_tiles"] * (16 * rb + 96) + st["wsb_residual_edges"] * (4 + rb)
+           + n * (4 * F + 16) + st["wsb_windows"] * 8)
+    bcsr = m * (4 + rb) + n * (4 + 4 * F)
+    ops = [Op("block16", lambda: gnn.gnn_spmm_block16(csr, X, "both", Y=Y, plan=plan), m, b16),
+           Op("csr", lambda: gnn.gnn_spmm(csr, X, "both", Y=Y, plan=plan), m, bcsr)]
+
+    def cpu(budget_s):
+        import oracle
+        xh = gen.gauss_bf16(11, (n, F))
+        return _oracle_rows_rate(w, lambda r: oracle.spmm(w.row_ptr, w.col_idx, xh, "both", rows=r,
+                                                          x_is_bf16=True, want_abs=False),
+                                 budget_s, "SpMM (bf16 X, both)")
+
+    cfg = {"workload": "spmm_b16_" + w.name, "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m,
+           "F": F, "x_dtype": "bf16", "norm": "both", "plan": st,
+           "note": "per_op_ms.csr is gnn_spmm on the same input"}
+    return {"ops": ops, "dominant": "block16", "kernel": "k_spmm_b16<unsigned short>", "config": cfg,
+            "dtype": "bf16", "cpu": cpu, "keep": (w, csr, plan, X, Y)}
+
+
 # ---------------------------------------------------------------------------
 # backward passes.  One op is one library call; the forward outputs they need
 # (out, lse, arg) and the plan's transpose are made during setup and warm-up.
@@ -627,7 +668,7 @@ WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, 
              "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
              "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
              "reorder_cfg5": wl_reorder, "spmm_bwd_cfg5": wl_spmm_bwd, "reduce_bwd_cfg2": wl_reduce_bwd,
-             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd}
+             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd, "spmm_b16_cfg4": wl_spmm_b16}
 
 
 # ---------------------------------------------------------------------------
