@@ -59,6 +59,7 @@ def _load():
                                        vp, vp]
     lib.oracle_gatv2_backward.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp,
                                           vp, vp, vp]
+    lib.oracle_dot_aggr.argtypes = [i32, vp, vp, vp, i32, i64, i64, vp, vp, vp]
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -266,3 +267,18 @@ def gatv2_backward(row_ptr, col_idx, xl, xr, att, dO, slope=0.2):
     _rc(_load().oracle_gatv2_backward(n, nc, _p(rp), _p(ci), _p(xl), _p(xr), _p(att), H, D, slope, _p(dO),
                                       *[_p(o) for o in outs]), "gatv2_backward")
     return tuple(outs)
+
+
+def dot_aggr(row_ptr, col_idx, X, rows=None, want_abs=True):
+    """(y [n_sel], yabs [n_sel]) in fp64: y_i = sum over row i's sources j of <X[i], X[j]>.
+    X float32 [n, D] (rows of the square graph)."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    X = np.ascontiguousarray(X, np.float32)
+    assert X.ndim == 2 and X.shape[0] == n
+    D = X.shape[1]
+    r, ns = _rows(rows, n)
+    y = np.empty(ns, np.float64)
+    a = np.empty(ns, np.float64) if want_abs else None
+    _rc(_load().oracle_dot_aggr(n, _p(rp), _p(ci), _p(X), D, D, ns, _p(r), _p(y), _p(a)), "dot_aggr")
+    return (y, a) if want_abs else y

@@ -880,3 +880,51 @@ int oracle_gatv2_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr
   free(e); free(a); free(g); free(ga);
   return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* dot-aggr reordering micro-benchmark                                       */
+/* ------------------------------------------------------------------------ */
+
+/* dot-aggr (paper: Experiments, the graph-reordering results with Figure 1,
+ * and appendix E.1 with Figure 2).  The pages name the kernel (a dot product
+ * followed by an aggregation) and fix that its feature-parallel and its
+ * neighbour-parallel mapping do the same arithmetic; with one lane per
+ * neighbour that arithmetic is a full dot product per edge.  So for every
+ * destination i:  y_i = sum over the sources j of row i of
+ * sum_d X[i, d] * X[j, d], a scalar per node; yabs_i = the same sum of
+ * |X[i, d] * X[j, d]| (error scale).  The graph is square: sources index
+ * rows of the same X. */
+int oracle_dot_aggr(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const float* X,
+                    int32_t D, int64_t ldx, int64_t n_sel, const int32_t* rows, double* y,
+                    double* yabs) {
+  if (n_rows < 0 || !row_ptr || !y || D <= 0 || ldx < D) return -1;
+  if (n_rows > 0 && !X) return -1;
+  if (!rows) n_sel = n_rows;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t s = 0; s < n_sel; ++s) {
+    int32_t i = rows ? rows[s] : (int32_t)s;
+    y[s] = 0.0;
+    if (yabs) yabs[s] = 0.0;
+    if (i < 0 || i >= n_rows) {
+      bad = 1;
+      continue;
+    }
+    double acc = 0.0, mag = 0.0;
+    for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      int32_t j = col_idx[e];
+      if (j < 0 || j >= n_rows) {
+        bad = 1;
+        break;
+      }
+      for (int32_t d = 0; d < D; ++d) {
+        double t = (double)X[(int64_t)i * ldx + d] * (double)X[(int64_t)j * ldx + d];
+        acc += t;
+        mag += fabs(t);
+      }
+    }
+    y[s] = acc;
+    if (yabs) yabs[s] = mag;
+  }
+  return bad ? -1 : 0;
+}

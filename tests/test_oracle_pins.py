@@ -681,3 +681,71 @@ def test_attention_backward_closed_forms(rng):
     np.testing.assert_allclose(dv.reshape(n, H * D), ref, atol=1e-12, rtol=0)
     _, dr, _, *_ = oracle.gatv2_backward(rp, ci, q, v, np.zeros((H, D), np.float32), dO, 0.2)
     np.testing.assert_allclose(dr.reshape(n, H * D), ref, atol=1e-12, rtol=0)
+
+
+# ----------------------------------------------------------------------------
+# dot-aggr (reordering micro-benchmark): dense brute force, closed forms,
+# one-hot class counts, permutation equivariance
+# ----------------------------------------------------------------------------
+
+def test_dot_aggr_dense_brute_force(rng):
+    """y = row sums of A o (X X^T): the Gram matrix masked by the adjacency."""
+    for n, D, p in ((1, 3, 1.0), (17, 5, 0.3), (40, 33, 0.15), (64, 1, 0.5)):
+        A, rp, ci = random_graph(rng, n, p, loops=True)
+        X = rng.standard_normal((n, D)).astype(np.float32)
+        Xd = X.astype(np.float64)
+        G = Xd @ Xd.T
+        want = (A * G).sum(axis=1)
+        want_abs = (A * (np.abs(Xd) @ np.abs(Xd).T)).sum(axis=1)
+        y, a = oracle.dot_aggr(rp, ci, X)
+        np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(a, want_abs, rtol=1e-12, atol=0)
+
+
+def test_dot_aggr_ones_and_one_hot(rng):
+    n, D = 500, 7
+    rp, ci = gen.rmat(21, n, 6000)
+    deg = np.diff(rp)
+    y, a = oracle.dot_aggr(rp, ci, np.ones((n, D), np.float32))
+    assert np.array_equal(y, (D * deg).astype(np.float64))
+    assert np.array_equal(a, y)
+    # one-hot class rows: <x_i, x_j> = [c(i) == c(j)], so y_i counts same-class sources
+    c = rng.integers(0, 4, n)
+    X = np.zeros((n, 4), np.float32)
+    X[np.arange(n), c] = 1.0
+    y, _ = oracle.dot_aggr(rp, ci, X)
+    rows = np.repeat(np.arange(n), deg)
+    want = np.bincount(rows, weights=(c[rows] == c[ci]).astype(np.float64), minlength=n)
+    assert np.array_equal(y, want)
+
+
+def test_dot_aggr_single_feature_and_empty_rows(rng):
+    """D = 1: y_i = x_i * (sum of the sources' x); rows without sources give 0."""
+    n = 300
+    rp, ci = gen.rmat(22, n, 900)          # R-MAT at this density leaves empty rows
+    deg = np.diff(rp)
+    assert (deg == 0).any()
+    X = rng.standard_normal((n, 1)).astype(np.float32)
+    y, _ = oracle.dot_aggr(rp, ci, X)
+    x = X[:, 0].astype(np.float64)
+    want = np.array([x[i] * x[ci[rp[i]:rp[i + 1]]].sum() for i in range(n)])
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-15)
+    assert np.all(y[deg == 0] == 0.0)
+
+
+def test_dot_aggr_permutation_equivariance_and_rows(rng):
+    n, D = 400, 12
+    rp, ci = gen.rmat(23, n, 5000)
+    X = rng.standard_normal((n, D)).astype(np.float32)
+    pi = rng.permutation(n)
+    rows = np.repeat(np.arange(n), np.diff(rp))
+    rp2, ci2 = gen.from_edges(n, pi[ci], pi[rows])
+    X2 = np.empty_like(X)
+    X2[pi] = X
+    y, a = oracle.dot_aggr(rp, ci, X)
+    y2, a2 = oracle.dot_aggr(rp2, ci2, X2)
+    np.testing.assert_allclose(y2[pi], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a2[pi], a, rtol=1e-12, atol=0)
+    sel = np.sort(rng.choice(n, 50, replace=False)).astype(np.int32)
+    ys, _ = oracle.dot_aggr(rp, ci, X, rows=sel)
+    assert np.array_equal(ys, y[sel])
