@@ -52,6 +52,7 @@ SOURCES = {
     "gatv2_bwd_cfg3": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
     "gt_bwd_cfg4": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
     "spmm_b16_cfg4": _COMMON + ("spmm_block16.hip", "wsb.hip", "sort.hip"),
+    "dotaggr_cfg2": _COMMON + ("dot_aggr.hip",),
 }
 
 
@@ -90,8 +91,11 @@ def load_traffic(workload: str, kernel: str):
 # ---------------------------------------------------------------------------
 
 class Op:
-    def __init__(self, name, fn, edges, bytes_alg):
-        self.name, self.fn, self.edges, self.bytes_alg = name, fn, edges, bytes_alg
+    """One timed call.  warm=True: every timed call follows an identical
+    untimed one (a warm second pass over the same data)."""
+
+    def __init__(self, name, fn, edges, bytes_alg, warm=False):
+        self.name, self.fn, self.edges, self.bytes_alg, self.warm = name, fn, edges, bytes_alg, warm
 
 
 def wl_reduce_f128(args):
@@ -664,11 +668,89 @@ def wl_gt_bwd(args):
             "keep": (w, csr, plan, q, k, v, out, lse, dO)}
 
 
+DOT_DIMS = (32, 64, 128, 256, 512)
+DOT_VARIANTS = [(m, l) for m in ("feature", "neighbor") for l in ("scalar", "vec16")]
+
+
+def wl_dot_aggr(args):
+    """dot-aggr reordering micro-benchmark: y_i = sum over row i's sources of <x_i, x_j>, one wave
+    per node, feature- or neighbour-parallel, 4- or 16-byte loads, D = 32 ... 512 float32, on
+    R-MAT 1,000,000 nodes / 16,000,000 edges and on a relabelled 1000 x 1000 grid (3,996,000
+    entries), each in the original, degree-sorted and RCM numberings.  Every timed launch follows an
+    identical untimed one.  Reordering gap per (graph, order, D, load width):
+    s = t_original / t_reordered per mapping, delta_s = s_neighbor - s_feature."""
+    import torch
+
+    import gen
+    import graph_neural_network_amd as gnn
+
+    rm = gen.reduce_rmat(with_x=False)
+    graphs = {"rmat": (rm.row_ptr, rm.col_idx), "grid": gen.grid2d(gen.GRAPH_SEED + 6, 1000)}
+    ops, keep, gstats = [], [], {}
+    for gname, (rp, ci) in graphs.items():
+        n, m = rp.size - 1, ci.size
+        csr = gnn.Csr(torch.from_numpy(rp).cuda(), torch.from_numpy(ci).cuda())
+        orders = {"original": (csr, None)}
+        for kind in ("degree", "rcm"):
+            perm, rp2, ci2 = gnn.gnn_reorder(csr, kind)
+            orders[kind] = (gnn.Csr(rp2, ci2), perm)
+        gstats[gname] = {"nodes": n, "edges": m, **{k: v for k, v in gen.degree_stats(rp).items()
+                                                    if k in ("max_deg", "q50", "q99", "empty_rows")}}
+        base = {D: torch.randn((n, D), device="cuda") for D in DOT_DIMS}
+        for oname, (c, perm) in orders.items():
+            plan = gnn.gnn_plan_create(c, chunk_edges=256)
+            y = torch.empty(n, dtype=torch.float32, device="cuda")
+            keep.append((c, perm, plan, y))
+            for D in DOT_DIMS:
+                X = base[D] if perm is None else gnn.gnn_permute_rows(perm, base[D])
+                keep.append(X)
+                # per edge: column index + the source row; per node: row pointer, its own row, y
+                b = m * (4 + 4 * D) + n * (8 + 4 * D)
+                for mp, ld in DOT_VARIANTS:
+                    ops.append(Op(f"{gname}:{oname}:D{D}:{mp}:{ld}",
+                                  (lambda c=c, X=X, mp=mp, ld=ld, y=y, plan=plan:
+                                   gnn.gnn_dot_aggr(c, X, mp, ld, y=y, plan=plan)), m, b, warm=True))
+        keep.append((csr, base))
+
+    def post(per_op_ms):
+        gap, speed = {}, {}
+        for g in graphs:
+            for kind in ("degree", "rcm"):
+                for D in DOT_DIMS:
+                    for ld in ("scalar", "vec16"):
+                        t = {(o, mp): per_op_ms.get(f"{g}:{o}:D{D}:{mp}:{ld}") for o in ("original", kind)
+                             for mp in ("feature", "neighbor")}
+                        if any(v is None for v in t.values()):
+                            continue
+                        s_f = t[("original", "feature")] / t[(kind, "feature")]
+                        s_n = t[("original", "neighbor")] / t[(kind, "neighbor")]
+                        key = f"{g}:{kind}:D{D}:{ld}"
+                        speed[key] = {"s_feature": round(s_f, 3), "s_neighbor": round(s_n, 3)}
+                        gap[key] = round(s_n - s_f, 3)
+        return {"delta_s": gap, "speedups": speed}
+
+    def cpu(budget_s):
+        import oracle
+        xh = gen.gauss_f32(gen.FEAT_SEED + 6, (rm.n, 128))
+        return _oracle_rows_rate(rm, lambda r: oracle.dot_aggr(rm.row_ptr, rm.col_idx, xh, rows=r, want_abs=False),
+                                 budget_s, "dot-aggr, D = 128")
+
+    cfg = {"workload": "dotaggr_rmat1000000_16000000_grid1000", "graphs": gstats,
+           "graph_kinds": {"rmat": "rmat(0.57,0.19,0.19,0.05)", "grid": "1000 x 1000 four-neighbour grid, "
+                           "random labels"},
+           "D": list(DOT_DIMS), "x_dtype": "f32", "plan_chunk_edges": 256,
+           "timing": "each timed launch follows an identical untimed launch"}
+    return {"ops": ops, "dominant": "rmat:original:D128:feature:vec16", "kernel": "k_dot_nodes<0, true, 1, 8>",
+            "traffic_kernels": ["k_dot_nodes<0, true, 1, 8>", "k_dot_items<0, true, 1, 8>", "k_dot_combine"],
+            "config": cfg, "dtype": "f32", "cpu": cpu, "post": post, "keep": (rm, graphs, keep)}
+
+
 WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
              "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
              "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
              "reorder_cfg5": wl_reorder, "spmm_bwd_cfg5": wl_spmm_bwd, "reduce_bwd_cfg2": wl_reduce_bwd,
-             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd, "spmm_b16_cfg4": wl_spmm_b16}
+             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd, "spmm_b16_cfg4": wl_spmm_b16,
+             "dotaggr_cfg2": wl_dot_aggr}
 
 
 # ---------------------------------------------------------------------------
@@ -681,6 +763,7 @@ def main():
     ap.add_argument("--workload", default="reduce_f128", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
+    ap.add_argument("--ops", default=None, help="run only the workload's ops whose names match this glob")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -691,6 +774,13 @@ def main():
 
     torch.cuda.set_device(0)
     w = WORKLOADS[args.workload](args)
+    if args.ops:
+        import fnmatch
+        w["ops"] = [o for o in w["ops"] if fnmatch.fnmatch(o.name, args.ops)]
+        if not w["ops"]:
+            sys.exit(f"--ops {args.ops!r} matches no op of {args.workload}")
+        if all(o.name != w["dominant"] for o in w["ops"]):
+            w["dominant"] = w["ops"][0].name
     ops = w["ops"]
     stream = torch.cuda.current_stream()
 
@@ -703,6 +793,8 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         for o in ops:
+            if o.warm:
+                o.fn()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -728,6 +820,10 @@ def main():
             torch.cuda.synchronize()
             separate_ms[o.name] = round(a.elapsed_time(b) / 5, 4)
     step_ms = wall * 1e3 / args.steps
+    wall_step_ms = step_ms
+    if any(o.warm for o in ops):
+        # untimed warm passes ran inside the loop: the step is the timed launches
+        step_ms = sum(per_op_ms.values())
     edges = sum(o.edges for o in ops)
     bytes_alg = sum(o.bytes_alg for o in ops)
     dom = next(o for o in ops if o.name == w["dominant"])
@@ -753,10 +849,13 @@ def main():
         "hbm_frac_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "per_op_ms": {k: round(v, 4) for k, v in per_op_ms.items()},
         "separate_launch_ms": separate_ms,
+        "step_wall_ms": wall_step_ms,
         "roofline": {"bound": "hbm", "kernel": f"{dom.name}: {w['kernel']}", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
     }
+    if w.get("post"):
+        out["results"] = w["post"](per_op_ms)
     if not args.no_cpu:
         out["cpu_baseline"] = w["cpu"](args.cpu_budget)
     else:

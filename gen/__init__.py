@@ -166,6 +166,22 @@ def cluster(seed: int, n: int, csize: int = 64, p: float = 0.5, frac: float = 0.
     return _take(g)
 
 
+def grid2d(seed: int, k: int):
+    """k x k four-neighbour grid, every undirected edge stored both ways, no
+    self loops; vertex labels drawn by a seeded uniform permutation, so the
+    stored numbering carries no locality (a road-network-like stand-in:
+    degree at most 4)."""
+    r, c = np.divmod(np.arange(k * k, dtype=np.int64), k)
+    right = np.nonzero(c < k - 1)[0]
+    down = np.nonzero(r < k - 1)[0]
+    a = np.r_[right, down]
+    b = np.r_[right + 1, down + k]
+    lab = permutation(seed, k * k).astype(np.int64)
+    src = lab[np.r_[a, b]]
+    dst = lab[np.r_[b, a]]
+    return from_edges(k * k, src, dst)
+
+
 def from_edges(n: int, src, dst):
     """CSR (rows = destinations) from an explicit edge list src[k] -> dst[k]."""
     s = np.ascontiguousarray(src, np.int32)

@@ -28,13 +28,15 @@ NORM = {"none": 0, "left": 1, "right": 2, "both": 3}
 REDUCE_OP = {"sum": 0, "mean": 1, "max": 2, "min": 3}
 GT_MODE = {"csr": 0, "block16": 1, "auto": 2}
 REORDER = {"degree": 0, "rcm": 1}
+DOT_MAP = {"feature": 0, "neighbor": 1}
+DOT_LOAD = {"scalar": 0, "vec16": 1}
 
 # every symbol include/gnn.h declares
 EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
-           "gnn_spmm_block16")
+           "gnn_spmm_block16", "gnn_dot_aggr")
 
 
 class GnnError(RuntimeError):
@@ -88,6 +90,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_reduce_backward": [P(_Csr), ci, vp, i32, i64, vp, vp, i64, vp, vp],
         "gnn_gatv2_backward": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_gt_backward": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
+        "gnn_dot_aggr": [P(_Csr), vp, i32, i64, ci, ci, vp, vp, vp],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -222,6 +225,20 @@ def gnn_spmm_block16(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Ten
     _check(load_library().gnn_spmm_block16(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y), Y.stride(0),
                                            NORM[norm], _plan_h(plan), _stream(stream)), "gnn_spmm_block16")
     return Y
+
+
+def gnn_dot_aggr(csr: Csr, X: torch.Tensor, map: str = "feature", load: str = "scalar",
+                 y: torch.Tensor | None = None, plan: Plan | None = None, stream=None) -> torch.Tensor:
+    """dot-aggr micro-benchmark: y[i] = sum over row i's sources j of <X[i], X[j]> (float32 X);
+    map "feature" | "neighbor", load "scalar" (4-byte) | "vec16" (16-byte per lane)."""
+    D = X.shape[1]
+    if y is None:
+        y = torch.empty(csr.n_rows, dtype=torch.float32, device=X.device)
+    if X.dtype != torch.float32:
+        raise TypeError("gnn_dot_aggr takes float32 features")
+    _check(load_library().gnn_dot_aggr(csr.ref, _ptr(X), D, X.stride(0), DOT_MAP[map], DOT_LOAD[load], _ptr(y),
+                                       _plan_h(plan), _stream(stream)), "gnn_dot_aggr")
+    return y
 
 
 def gnn_reduce(csr: Csr, X: torch.Tensor, op: str = "sum", Y: torch.Tensor | None = None,

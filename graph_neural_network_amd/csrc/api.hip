@@ -404,6 +404,26 @@ int gnn_permute_rows(const int32_t* perm, int32_t n, const void* X, gnn_dtype xt
                              (hipStream_t)stream);
 }
 
+int gnn_dot_aggr(const gnn_csr* csr, const float* X, int32_t D, int64_t ldx, gnn_dot_map map,
+                 gnn_dot_load load, float* y, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, true));
+  if (map != GNN_DOT_FEATURE && map != GNN_DOT_NEIGHBOR) return fail(GNN_ERR_INVALID_VALUE, "unknown dot-aggr map");
+  if (load != GNN_LOAD_SCALAR && load != GNN_LOAD_VEC16) return fail(GNN_ERR_INVALID_VALUE, "unknown load width");
+  if (D <= 0 || ldx < D) return fail(GNN_ERR_INVALID_VALUE, "need D > 0 and ldx >= D");
+  if (D > 1024) return fail(GNN_ERR_UNSUPPORTED, "dot-aggr supports D <= 1024");
+  if (csr->edge_val) return fail(GNN_ERR_INVALID_VALUE, "dot-aggr takes no edge values");
+  if (csr->n_rows > 0 && (!X || !y)) return fail(GNN_ERR_INVALID_VALUE, "X or y is NULL");
+  if (load == GNN_LOAD_VEC16 && (D % 4 != 0 || ldx % 4 != 0 || (uintptr_t)X % 16 != 0))
+    return fail(GNN_ERR_INVALID_VALUE, "16-byte loads need D and ldx multiples of 4 and X 16-byte aligned");
+  if (csr->n_rows == 0) return GNN_OK;
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  PlanGuard g{p, tr};
+  return launch_dot_aggr(p, X, D, ldx, map == GNN_DOT_NEIGHBOR ? 1 : 0, load == GNN_LOAD_VEC16, y, s);
+}
+
 int gnn_copy_bytes(const void* src, void* dst, int64_t n, void* stream) {
   if (n < 0 || (n > 0 && (!src || !dst))) return fail(GNN_ERR_INVALID_VALUE, "bad copy arguments");
   if (n == 0) return GNN_OK;

@@ -154,6 +154,11 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
 int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
                    hipStream_t s);
 
+// dot-aggr micro-benchmark (dot_aggr.hip): map 0 = feature-parallel,
+// 1 = neighbour-parallel; vec = 16-byte loads per lane
+int launch_dot_aggr(gnn_plan* p, const float* X, int32_t D, int64_t ldx, int map, bool vec, float* y,
+                    hipStream_t s);
+
 int launch_spmm_block16(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y, int64_t ldy,
                         gnn_norm norm, hipStream_t s);
 
@@ -197,15 +202,20 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X; this
 // maps the hardware workgroup id to a logical one so that each XCD receives
-// a contiguous range of logical ids (neighbouring rows share one L2).
+// runs of `run` consecutive logical ids (neighbouring rows share one L2),
+// the runs of the 8 XCDs interleaved so that all XCDs sweep the row range
+// together.  run = 0: one run per XCD (each XCD a contiguous eighth).  Ids
+// past the last whole group of 8 runs keep the hardware order.
+#ifndef GNN_XCD_RUN
+#define GNN_XCD_RUN 0
+#endif
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
   constexpr uint32_t NX = 8;
-  uint32_t per = nblocks / NX, rem = nblocks % NX;
-  uint32_t x = bid % NX, k = bid / NX;
-  // XCD x owns per (+1 for x < rem) consecutive logical ids
-  uint32_t base = x * per + (x < rem ? x : rem);
-  uint32_t lid = base + k;
-  return lid;
+  const uint32_t run = GNN_XCD_RUN > 0 ? (uint32_t)GNN_XCD_RUN : (nblocks / NX > 0 ? nblocks / NX : 1);
+  const uint32_t full = nblocks / (NX * run) * (NX * run);
+  if (bid >= full) return bid;
+  const uint32_t x = bid % NX, k = bid / NX;
+  return ((k / run) * NX + x) * run + k % run;
 }
 
 }  // namespace dev

@@ -17,6 +17,9 @@
  *   gnn_reorder      degree-sort or RCM vertex reordering      (section 2.4; RCM as in
  *                    Tang et al., "A High-Throughput Solver for Marginalized Graph
  *                    Kernels on GPU", graph reordering section)
+ *   gnn_dot_aggr     dot-aggr reordering micro-benchmark, feature- or
+ *                    neighbour-parallel                        (Experiments, graph reordering,
+ *                                                               Figure 1; appendix E.1)
  *
  * Conventions for every entry point:
  *   - Graph: CSR whose rows are DESTINATIONS: row i lists the sources j of the
@@ -85,6 +88,13 @@ typedef enum { GNN_SUM = 0, GNN_MEAN = 1, GNN_MAX = 2, GNN_MIN = 3 } gnn_reduce_
 typedef enum { GNN_GT_CSR = 0, GNN_GT_BLOCK16 = 1, GNN_GT_AUTO = 2 } gnn_gt_mode;
 
 typedef enum { GNN_REORDER_DEGREE = 0, GNN_REORDER_RCM = 1 } gnn_reorder_kind;
+
+/* dot-aggr mappings (Experiments, graph reordering): one wave per node, lanes
+ * over features (sources walked one after another, coalesced row loads) or
+ * lanes over sources (each lane walks its source's features: gathers). */
+typedef enum { GNN_DOT_FEATURE = 0, GNN_DOT_NEIGHBOR = 1 } gnn_dot_map;
+/* Per-lane load width of dot-aggr: 4-byte scalar or 16-byte vector loads. */
+typedef enum { GNN_LOAD_SCALAR = 0, GNN_LOAD_VEC16 = 1 } gnn_dot_load;
 
 typedef struct gnn_csr {
   int32_t n_rows;          /* destinations */
@@ -316,6 +326,24 @@ int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_
  * reordered vertex numbering.  Errors: INVALID_VALUE, DEVICE. */
 int gnn_permute_rows(const int32_t* perm, int32_t n, const void* X, gnn_dtype xtype, int32_t F,
                      int64_t ldx, void* Xout, int64_t ldo, void* stream);
+
+/* dot-aggr, the cache-sensitive micro-benchmark with which the pages study
+ * graph reordering (Experiments, graph reordering, Figure 1; appendix E.1,
+ * Figure 2): for every node i of a square CSR,
+ *   y[i] = sum over the sources j of row i of sum_d X[i, d] * X[j, d].
+ * X: device float32 [n_rows, D], row stride ldx >= D (elements); y: device
+ * float32 [n_rows].  map selects the wave-per-node mapping (gnn_dot_map),
+ * load the per-lane load width (gnn_dot_load); every combination computes the
+ * same sums, in a different order.  Rows longer than the plan's split
+ * threshold run as the plan's edge chunks, one wave each, added in chunk order.
+ * Supported: 1 <= D <= 1024; GNN_LOAD_VEC16 needs D and ldx multiples of 4
+ * and X 16-byte aligned.  edge_val must be NULL (no weights).  plan may be
+ * NULL (a transient plan is built, synchronising `stream`).
+ * Errors: INVALID_VALUE (null pointer, not square, bad D / ldx / enum, edge
+ * values given, misaligned VEC16 input), UNSUPPORTED (D > 1024),
+ * PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_dot_aggr(const gnn_csr* csr, const float* X, int32_t D, int64_t ldx, gnn_dot_map map,
+                 gnn_dot_load load, float* y, gnn_plan* plan, void* stream);
 
 /* Plain streaming copy of n bytes (device to device), used to calibrate
  * bandwidth measurements and hardware counters.  Asynchronous. */

@@ -86,6 +86,17 @@ INV, UNS, OVF = 1, 2, 5
     ("spmm b16 non-square", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), 1, 16, 16, P(16), 16, 0, None, None), INV),
     ("spmm b16 F not 16 B", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(16), 1, 12, 12, P(16), 12, 0, None, None), UNS),
     ("spmm b16 misaligned", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(24), 0, 16, 16, P(16), 16, 0, None, None), UNS),
+    ("dot non-square", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr(n_cols=5)), P(16), 4, 4, 0, 0, P(16), None, None), INV),
+    ("dot D=0", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 0, 4, 0, 0, P(16), None, None), INV),
+    ("dot ldx<D", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 8, 4, 0, 0, P(16), None, None), INV),
+    ("dot D>1024", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 1028, 1028, 0, 0, P(16), None, None), UNS),
+    ("dot bad map", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 4, 4, 2, 0, P(16), None, None), INV),
+    ("dot bad load", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 4, 4, 0, 3, P(16), None, None), INV),
+    ("dot null y", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 4, 4, 0, 0, None, None, None), INV),
+    ("dot vec16 D%4", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 6, 8, 1, 1, P(16), None, None), INV),
+    ("dot vec16 ldx%4", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 4, 6, 1, 1, P(16), None, None), INV),
+    ("dot vec16 misaligned", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(20), 4, 4, 0, 1, P(16), None, None), INV),
+    ("dot edge values", lambda: call("gnn_dot_aggr", ctypes.byref(gnn._Csr(4, 4, 4, 0x1000, 0x2000, 0x3000)), P(16), 4, 4, 0, 0, P(16), None, None), INV),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
                                    ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),
@@ -107,4 +118,5 @@ def test_empty_calls_are_noops():
     empty = gnn._Csr(0, 0, 0, 0x1000, None, None)
     assert lib.gnn_spmm(ctypes.byref(empty), None, 0, 4, 4, P(8), 4, 0, None, None) == 0
     assert lib.gnn_copy_bytes(None, None, 0, None) == 0
+    assert lib.gnn_dot_aggr(ctypes.byref(empty), None, 4, 4, 0, 1, None, None, None) == 0
     assert lib.gnn_plan_destroy(None) == 0
