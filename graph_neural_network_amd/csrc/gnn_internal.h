@@ -205,9 +205,12 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 // runs of `run` consecutive logical ids (neighbouring rows share one L2),
 // the runs of the 8 XCDs interleaved so that all XCDs sweep the row range
 // together.  run = 0: one run per XCD (each XCD a contiguous eighth).  Ids
-// past the last whole group of 8 runs keep the hardware order.
+// past the last whole group of 8 runs keep the hardware order.  One run per
+// XCD loads one XCD with all the heavy rows of a degree-sorted graph; runs
+// of 128 workgroups keep the locality and spread every part of the row range
+// over all eight XCDs.
 #ifndef GNN_XCD_RUN
-#define GNN_XCD_RUN 0
+#define GNN_XCD_RUN 128
 #endif
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t nblocks) {
   constexpr uint32_t NX = 8;
