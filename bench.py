@@ -740,8 +740,8 @@ def wl_dot_aggr(args):
                            "random labels"},
            "D": list(DOT_DIMS), "x_dtype": "f32", "plan_chunk_edges": 256,
            "timing": "each timed launch follows an identical untimed launch"}
-    return {"ops": ops, "dominant": "rmat:original:D128:feature:vec16", "kernel": "k_dot_nodes<0, true, 1, 8>",
-            "traffic_kernels": ["k_dot_nodes<0, true, 1, 8>", "k_dot_items<0, true, 1, 8>", "k_dot_combine"],
+    return {"ops": ops, "dominant": "rmat:original:D128:feature:vec16", "kernel": "k_dot<0, true, 1, 8>",
+            "traffic_kernels": ["k_dot<0, true, 1, 8>", "k_dot_combine"],
             "config": cfg, "dtype": "f32", "cpu": cpu, "post": post, "keep": (rm, graphs, keep)}
 
 

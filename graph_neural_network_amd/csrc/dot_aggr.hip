@@ -13,8 +13,8 @@
 // Each lane loads 4 bytes (SCALAR) or 16 bytes (VEC16) per instruction.
 //
 // Rows longer than the plan's split threshold are cut into the plan's edge
-// chunks (the degree-aware split of appendix D.1), one wave per chunk; the
-// chunk partials are added in chunk order.  Both mappings see the same
+// chunks (the degree-aware split of appendix D.1), one wave per chunk in the
+// same launch; a second launch adds the chunk partials in chunk order.  Both mappings see the same
 // split, so the comparison between them is unchanged, and no single
 // hub row's chain of dependent loads sets the kernel time.
 #include <algorithm>
@@ -173,31 +173,32 @@ __device__ __forceinline__ float dot_range(const DotParams& p, float* s_xi, int6
   }
 }
 
-// One wave per node; rows above the split threshold are left to k_dot_items.
+// One launch: first the chunk waves of split rows (hardware order spreads them
+// over the XCDs; their workgroup count is padded to a multiple of 8), each
+// writing its chunk's partial dot-sum; then one wave per node, workgroups
+// remapped in per-XCD runs, skipping the split rows.
 template <int MAP, bool VEC, int K, int U>
-__global__ __launch_bounds__(64 * kWaves) void k_dot_nodes(DotParams p) {
+__global__ __launch_bounds__(64 * kWaves) void k_dot(DotParams p, int32_t n_item_blocks) {
   extern __shared__ __align__(16) float s_dyn[];  // NEIGHBOR: [kWaves][D]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t i = (int64_t)dev::xcd_remap(blockIdx.x, gridDim.x) * kWaves + w;
+  float* s_xi = s_dyn + (size_t)w * p.D;
+  const int32_t n_item_pad = (n_item_blocks + 7) & ~7;
+  if ((int32_t)blockIdx.x < n_item_pad) {
+    const int64_t it = (int64_t)blockIdx.x * kWaves + w;
+    if (it >= p.n_items) return;
+    const int4 item = p.items[it];
+    if (item.w < 0) return;  // a whole-row item: that row runs as a node
+    const float acc = wave_sum(dot_range<MAP, VEC, K, U>(p, s_xi, item.x, item.y, item.z, lane));
+    if (lane == 0) p.partial[it] = acc;
+    return;
+  }
+  const uint32_t nb = gridDim.x - (uint32_t)n_item_pad;
+  const int64_t i = (int64_t)dev::xcd_remap(blockIdx.x - (uint32_t)n_item_pad, nb) * kWaves + w;
   if (i >= p.n) return;
   const int32_t beg = p.row_ptr[i], end = p.row_ptr[i + 1];
   if (end - beg > p.split_thr) return;
-  const float acc = wave_sum(dot_range<MAP, VEC, K, U>(p, s_dyn + (size_t)w * p.D, i, beg, end, lane));
+  const float acc = wave_sum(dot_range<MAP, VEC, K, U>(p, s_xi, i, beg, end, lane));
   if (lane == 0) p.y[i] = acc;
-}
-
-// One wave per chunk of a split row: the chunk's partial dot-sum.
-template <int MAP, bool VEC, int K, int U>
-__global__ __launch_bounds__(64 * kWaves) void k_dot_items(DotParams p) {
-  extern __shared__ __align__(16) float s_dyn[];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t it = (int64_t)blockIdx.x * kWaves + w;
-  if (it >= p.n_items) return;
-  const int4 item = p.items[it];
-  if (item.w < 0) return;  // a whole-row item: its row runs in k_dot_nodes
-  const float acc =
-      wave_sum(dot_range<MAP, VEC, K, U>(p, s_dyn + (size_t)w * p.D, item.x, item.y, item.z, lane));
-  if (lane == 0) p.partial[it] = acc;
 }
 
 // y[row] = the row's chunk partials added in chunk order (deterministic).
@@ -214,13 +215,11 @@ template <int MAP, bool VEC, int K, int U>
 int launch_shape(gnn_plan* pl, const DotParams& p, hipStream_t s) {
   const size_t lds = MAP == NEIGHBOR ? (size_t)kWaves * p.D * sizeof(float) : 0;
   const int64_t nb = (p.n + kWaves - 1) / kWaves;
-  if (p.n_items > 0) {
-    const int64_t ib = (p.n_items + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL((k_dot_items<MAP, VEC, K, U>), dim3((unsigned)ib), dim3(64 * kWaves), lds, s, p);
-    GNN_LAUNCH_CHECK("k_dot_items");
-  }
-  hipLaunchKernelGGL((k_dot_nodes<MAP, VEC, K, U>), dim3((unsigned)nb), dim3(64 * kWaves), lds, s, p);
-  GNN_LAUNCH_CHECK("k_dot_nodes");
+  const int64_t ib = (p.n_items + kWaves - 1) / kWaves;
+  const int64_t grid = ((ib + 7) & ~(int64_t)7) + nb;
+  if (grid > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "dot-aggr: grid too large");
+  hipLaunchKernelGGL((k_dot<MAP, VEC, K, U>), dim3((unsigned)grid), dim3(64 * kWaves), lds, s, p, (int32_t)ib);
+  GNN_LAUNCH_CHECK("k_dot");
   if (pl->n_multi > 0) {
     const unsigned cb = (unsigned)((pl->n_multi + 255) / 256);
     hipLaunchKernelGGL(k_dot_combine, dim3(cb), dim3(256), 0, s, p, (const int4*)pl->multi, pl->n_multi);
