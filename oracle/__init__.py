@@ -54,6 +54,7 @@ def _load():
     lib.oracle_permute_csr.argtypes = [i32, vp, vp, vp, vp, vp]
     lib.oracle_wsb_build.argtypes = [i32, vp, vp, vp, vp, vp, vp]
     lib.oracle_spmm_backward.argtypes = [i32, i32, vp, vp, vp, ci, vp, i32, vp, vp]
+    lib.oracle_spmm_backward_cols.argtypes = [i32, i32, vp, vp, vp, ci, vp, i32, i64, vp, vp, vp]
     lib.oracle_reduce_backward.argtypes = [i32, i32, vp, vp, ci, vp, vp, i32, vp, vp]
     lib.oracle_gt_backward.argtypes = [i32, i32, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp,
                                        vp, vp]
@@ -210,17 +211,26 @@ def wsb_build(row_ptr, col_idx):
 # backward passes
 # ---------------------------------------------------------------------------
 
-def spmm_backward(row_ptr, col_idx, dY, norm="none", edge_val=None, n_cols=None):
-    """(dX fp64 [n_cols, F], |.|-sum) of dX = A_norm^T dY; dY float32 [n_rows, F]."""
+def spmm_backward(row_ptr, col_idx, dY, norm="none", edge_val=None, n_cols=None, cols=None):
+    """(dX fp64 [n_cols, F], |.|-sum) of dX = A_norm^T dY; dY float32 [n_rows, F].
+    cols: distinct column ids to evaluate (outputs packed [len(cols), F] in that order)."""
     rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
     n = rp.size - 1
     n_cols = n if n_cols is None else n_cols
     dY = np.ascontiguousarray(dY, np.float32)
     F = dY.shape[1]
-    dX = np.empty((n_cols, F), np.float64)
-    A = np.empty((n_cols, F), np.float64)
-    _rc(_load().oracle_spmm_backward(n, n_cols, _p(rp), _p(ci), _p(_c(edge_val, np.float32)), NORM[norm],
-                                     _p(dY), F, _p(dX), _p(A)), "spmm_backward")
+    ev = _p(_c(edge_val, np.float32))
+    if cols is None:
+        dX = np.empty((n_cols, F), np.float64)
+        A = np.empty((n_cols, F), np.float64)
+        _rc(_load().oracle_spmm_backward(n, n_cols, _p(rp), _p(ci), ev, NORM[norm], _p(dY), F, _p(dX), _p(A)),
+            "spmm_backward")
+        return dX, A
+    c = np.ascontiguousarray(cols, np.int32)
+    dX = np.empty((c.size, F), np.float64)
+    A = np.empty((c.size, F), np.float64)
+    _rc(_load().oracle_spmm_backward_cols(n, n_cols, _p(rp), _p(ci), ev, NORM[norm], _p(dY), F, c.size, _p(c),
+                                          _p(dX), _p(A)), "spmm_backward_cols")
     return dX, A
 
 

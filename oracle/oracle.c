@@ -629,18 +629,17 @@ int oracle_wsb_build(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_
  * i, dX[j, :] += w_e * dY[i, :] with the forward's weight w_e (paper: the
  * SpMM and reduction appendix, backward of Y = A X).  dY [n_rows, F] fp32,
  * dX and dXabs (sum of |w_e dY|) [n_cols, F] fp64.  A plain serial scatter. */
-int oracle_spmm_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
-                         const float* edge_val, int norm, const float* dY, int32_t F, double* dX,
-                         double* dXabs) {
-  if (!row_ptr || !col_idx || !dY || !dX || F <= 0 || norm < 0 || norm > 3) return -1;
+static int spmm_backward_impl(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                              const float* edge_val, int norm, const float* dY, int32_t F,
+                              const int32_t* slot, int64_t n_out, double* dX, double* dXabs) {
   int32_t* dout = (int32_t*)malloc((size_t)(n_cols > 0 ? n_cols : 1) * 4);
   if (!dout) return -2;
   if (oracle_degrees(n_rows, n_cols, row_ptr, col_idx, NULL, dout)) {
     free(dout);
     return -1;
   }
-  memset(dX, 0, (size_t)n_cols * F * 8);
-  if (dXabs) memset(dXabs, 0, (size_t)n_cols * F * 8);
+  memset(dX, 0, (size_t)n_out * F * 8);
+  if (dXabs) memset(dXabs, 0, (size_t)n_out * F * 8);
   for (int32_t i = 0; i < n_rows; ++i) {
     int32_t din = row_ptr[i + 1] - row_ptr[i];
     for (int32_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
@@ -649,16 +648,47 @@ int oracle_spmm_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr,
         free(dout);
         return -1;
       }
+      int64_t o = slot ? slot[j] : j;  /* output row of column j, or -1: not selected */
+      if (o < 0) continue;
       double w = edge_weight(norm, din, dout[j], edge_val, e);
       for (int32_t f = 0; f < F; ++f) {
         double t = w * (double)dY[(int64_t)i * F + f];
-        dX[(int64_t)j * F + f] += t;
-        if (dXabs) dXabs[(int64_t)j * F + f] += fabs(t);
+        dX[o * F + f] += t;
+        if (dXabs) dXabs[o * F + f] += fabs(t);
       }
     }
   }
   free(dout);
   return 0;
+}
+
+int oracle_spmm_backward(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                         const float* edge_val, int norm, const float* dY, int32_t F, double* dX,
+                         double* dXabs) {
+  if (!row_ptr || !col_idx || !dY || !dX || F <= 0 || norm < 0 || norm > 3) return -1;
+  return spmm_backward_impl(n_rows, n_cols, row_ptr, col_idx, edge_val, norm, dY, F, NULL, n_cols, dX, dXabs);
+}
+
+/* The same for the selected columns cols[0 .. n_sel) only (distinct, each in
+ * [0, n_cols)); output rows packed in that order.  Every entry of A is still
+ * visited, so the cost is one pass over the CSR plus the selected terms. */
+int oracle_spmm_backward_cols(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
+                              const float* edge_val, int norm, const float* dY, int32_t F, int64_t n_sel,
+                              const int32_t* cols, double* dX, double* dXabs) {
+  if (!row_ptr || !col_idx || !dY || !dX || !cols || F <= 0 || norm < 0 || norm > 3 || n_sel < 0) return -1;
+  int32_t* slot = (int32_t*)malloc((size_t)(n_cols > 0 ? n_cols : 1) * 4);
+  if (!slot) return -2;
+  for (int32_t j = 0; j < n_cols; ++j) slot[j] = -1;
+  for (int64_t s = 0; s < n_sel; ++s) {
+    if (cols[s] < 0 || cols[s] >= n_cols || slot[cols[s]] != -1) {
+      free(slot);
+      return -1;
+    }
+    slot[cols[s]] = (int32_t)s;
+  }
+  int rc = spmm_backward_impl(n_rows, n_cols, row_ptr, col_idx, edge_val, norm, dY, F, slot, n_sel, dX, dXabs);
+  free(slot);
+  return rc;
 }
 
 /* Reduction backward (paper: reduction appendix, backward pass).  op 0 SUM:

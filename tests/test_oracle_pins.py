@@ -563,6 +563,23 @@ def test_spmm_backward_adjoint(rng, norm, weighted):
     assert np.all(dX[~used] == 0)
 
 
+@pytest.mark.parametrize("norm", ["none", "both"])
+def test_spmm_backward_column_selection(rng, norm):
+    """Selected columns reproduce the full result's rows exactly (same terms in
+    the same order), in the order given; repeated or out-of-range columns fail."""
+    rp, ci = gen.rmat(24, 800, 12000)
+    dY = rng.standard_normal((800, 7)).astype(np.float32)
+    full, fa = oracle.spmm_backward(rp, ci, dY, norm)
+    deg_out = np.bincount(ci, minlength=800)
+    cols = np.r_[rng.permutation(800)[:60], np.argsort(-deg_out)[:5], np.nonzero(deg_out == 0)[0][:3]]
+    cols = np.array(list(dict.fromkeys(cols.tolist())), np.int32)
+    part, pa = oracle.spmm_backward(rp, ci, dY, norm, cols=cols)
+    assert np.array_equal(part, full[cols]) and np.array_equal(pa, fa[cols])
+    for bad in ([3, 3], [800], [-1]):
+        with pytest.raises(RuntimeError):
+            oracle.spmm_backward(rp, ci, dY, norm, cols=np.array(bad, np.int32))
+
+
 @pytest.mark.parametrize("op", ["sum", "mean", "max", "min"])
 def test_reduce_backward_adjoint(rng, op):
     """For fixed selected sources the reductions are linear in X, so
