@@ -1,0 +1,69 @@
+"""Backward passes at the benchmark's sizes, against the fp64 oracle over
+every output (the 16M-node SpMM backward is in test_gpu_large.py):
+  - reductions on R-MAT 1,000,000 nodes / 16,000,000 edges, F = 128;
+  - GATv2 on R-MAT 200,000 nodes / 4,000,000 edges + self loops, H = 4, D = 32 bf16;
+  - Graph Transformer on the 512,000-node cluster graph, H = 8, D = 64 bf16.
+Plans are the benchmark's (defaults).  Bars as in test_gpu_backward.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import graph_neural_network_amd as gnn
+import oracle
+from gpu_util import dev, dev_bf16, dev_csr, host
+from test_gpu_backward import TOL_AGG, TOL_ATT, bwd_err
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+def test_reduce_backward_rmat1m_full():
+    w = gen.reduce_rmat()
+    n, F = w.n, w.params["F"]
+    csr = dev_csr(w.row_ptr, w.col_idx)
+    plan = gnn.gnn_plan_create(csr)
+    fwd = gnn.gnn_reduce_multi(csr, dev(w.arrays["X"]), plan=plan)
+    dYh = gen.gauss_f32(0xFEA70601, (n, F))
+    dY = dev(dYh)
+    for op in ("sum", "mean", "max", "min"):
+        arg = None
+        if op in ("max", "min"):
+            _, ra, _ = oracle.reduce(w.row_ptr, w.col_idx, w.arrays["X"], op, want_abs=False)
+            arg = fwd["arg" + op]
+            assert np.array_equal(host(arg), ra), f"{op}: forward source indices differ"
+        dX = gnn.gnn_reduce_backward(csr, dY, op, arg=arg, plan=plan)
+        ref, mag = oracle.reduce_backward(w.row_ptr, w.col_idx, dYh, op, arg=None if arg is None else ra)
+        assert bwd_err(host(dX), ref, mag) <= TOL_AGG, op
+
+
+def test_gatv2_backward_cfg3_full():
+    w = gen.gatv2_rmat()
+    n, H, D = w.n, w.params["H"], w.params["D"]
+    csr = dev_csr(w.row_ptr, w.col_idx)
+    plan = gnn.gnn_plan_create(csr)
+    xl, xr, att = w.arrays["xl"], w.arrays["xr"], w.arrays["att"]
+    dl, dr, da_ = dev_bf16(xl), dev_bf16(xr), dev(att)
+    out, lse = gnn.gnn_gatv2_fused(csr, dl, dr, da_, 0.2, plan=plan)
+    dOh = gen.gauss_f32(0xFEA70602, (n, H, D))
+    dxl, dxr, datt = gnn.gnn_gatv2_backward(csr, dl, dr, da_, out, lse, dev(dOh), 0.2, plan=plan)
+    rl, rr, ra, ml, mr, ma = oracle.gatv2_backward(w.row_ptr, w.col_idx, xl, xr, att, dOh, 0.2)
+    assert bwd_err(host(dxl), rl, ml) <= TOL_ATT, "dxl"
+    assert bwd_err(host(dxr), rr, mr) <= TOL_ATT, "dxr"
+    assert bwd_err(host(datt), ra, ma) <= TOL_ATT, "datt"
+
+
+def test_gt_backward_cfg4_full():
+    w = gen.gt_cluster()
+    n, H, D = w.n, w.params["H"], w.params["D"]
+    csr = dev_csr(w.row_ptr, w.col_idx)
+    plan = gnn.gnn_plan_create(csr)
+    q, k, v = (w.arrays[x] for x in ("q", "k", "v"))
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = gnn.gnn_gt_fused(csr, dq_, dk_, dv_, plan=plan)
+    dOh = gen.gauss_f32(0xFEA70603, (n, H, D))
+    dq, dk, dv = gnn.gnn_gt_backward(csr, dq_, dk_, dv_, out, lse, dev(dOh), plan=plan)
+    rq, rk, rv, mq, mk, mv = oracle.gt_backward(w.row_ptr, w.col_idx, q, k, v, dOh)
+    assert bwd_err(host(dq), rq, mq) <= TOL_ATT, "dq"
+    assert bwd_err(host(dk), rk, mk) <= TOL_ATT, "dk"
+    assert bwd_err(host(dv), rv, mv) <= TOL_ATT, "dv"

@@ -59,3 +59,25 @@ def test_spmm_rmat16m_all_orders(big):
         assert scaled_err(got, ref, mag) <= 1e-5, kind
         assert np.array_equal(np.diff(host(rp2))[inv[rows]], np.diff(w.row_ptr)[rows])
         del Y2, X2
+
+
+def test_spmm_backward_rmat16m(big):
+    """dX = A^T dY at the 16M-node size with dY 16M x 256 float32 (the benchmark's
+    backward launch), through the plan's transpose; sampled columns (uniform,
+    the 16 most used, and unused ones) against the oracle's column selection."""
+    from test_gpu_backward import TOL_AGG, bwd_err
+    w, X, csr = big
+    n = w.n
+    dYh = gen.gauss_f32(0xFEA70600, (n, 256))
+    dY = torch.from_numpy(dYh).cuda()
+    plan = gnn.gnn_plan_create(csr)
+    dX = gnn.gnn_spmm_backward(csr, dY, "none", plan=plan)
+    deg_out = np.bincount(w.col_idx, minlength=n)
+    rng = np.random.default_rng(13)
+    cols = np.r_[rng.integers(0, n, 1500), np.argsort(-deg_out, kind="stable")[:16],
+                 np.nonzero(deg_out == 0)[0][:8]]
+    cols = np.array(list(dict.fromkeys(cols.tolist())), np.int32)
+    ref, mag = oracle.spmm_backward(w.row_ptr, w.col_idx, dYh, "none", cols=cols)
+    got = host(dX[torch.from_numpy(cols).long().cuda()])
+    assert bwd_err(got, ref, mag) <= TOL_AGG
+    assert np.all(got[deg_out[cols] == 0] == 0)
