@@ -18,8 +18,11 @@
 // the column weights in fp32, and B is read from LDS as fp32, so every product
 // is an fp32 product, as in the CSR kernel.  Lane layouts (checked on the
 // device): A: lane l holds A[l % 16][l / 16]; B: lane l holds B[l / 16][l % 16];
-// D: lane l holds D[4 (l / 16) + r][l % 16], r = 0..3.  Output rows are staged
-// through LDS so that each store writes whole lines.
+// D: lane l holds D[4 (l / 16) + r][l % 16], r = 0..3.  The window's tile
+// metadata (columns, weights, bitmap words) is staged in LDS up front, so a
+// tile's row gathers wait on one memory latency instead of three dependent
+// ones.  Output rows are staged through LDS so that each store writes whole
+// lines.
 #include <algorithm>
 
 #include "gnn_internal.h"
@@ -27,7 +30,8 @@
 namespace gnn {
 namespace {
 
-constexpr int FW = 256;  // features per workgroup
+constexpr int FW = 256;   // features per workgroup
+constexpr int MAXT = 16;  // tiles whose metadata is staged at once
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct B16SpmmParams {
@@ -63,13 +67,18 @@ __device__ __forceinline__ float col_weight(const B16SpmmParams& p, int j) {
   return 1.0f;
 }
 
+// bf16: 64 VGPRs and 19 KB of LDS allow eight workgroups per CU
 template <typename T>
-__global__ __launch_bounds__(256) void k_spmm_b16(B16SpmmParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 8 : 4))) void k_spmm_b16(B16SpmmParams p) {
   constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int CPR = FW / EPC;              // chunks per staged row slice
   constexpr int CPT = 16 * CPR / 256;        // chunks per thread per tile
   __shared__ __align__(16) T s_x[2][16][FW];
-  __shared__ int32_t s_cols[2][16];
+  // the window's tile metadata, MAXT tiles at a time: the 16 columns of each
+  // tile, their weights (0 for padding) and the two blocks' bitmap words
+  __shared__ int32_t s_tcol[MAXT][16];
+  __shared__ float s_tw[MAXT][16];
+  __shared__ unsigned long long s_tbits[MAXT][4];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lg = lane >> 4;
@@ -84,65 +93,72 @@ __global__ __launch_bounds__(256) void k_spmm_b16(B16SpmmParams p) {
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // column of tile column c (0..15) of tile t; 0 where the second block is past the window
-  auto tile_col = [&](int t, int c) -> int {
-    const int blk = p.tile_blk[t] + (c >> 3);
-    return ((c >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
-  };
-  // this thread's share of the 16 staged rows of tile t
+  // this thread's share of the 16 staged rows of local tile k
   uint4 pre[CPT];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int k) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int chunk = threadIdx.x + q * 256;   // 0 .. 16 * CPR - 1
       const int r = chunk / CPR, cc = chunk % CPR;
-      const int col = tile_col(t, r);
+      const int col = s_tcol[k][r];
       const int f = f0 + cc * EPC;
       pre[q] = (f < p.F) ? *reinterpret_cast<const uint4*>(X + (int64_t)col * p.ldx + f) : uint4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_tile = [&](int buf, int t) {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < CPT; ++q) {
       const int chunk = threadIdx.x + q * 256;
       const int r = chunk / CPR, cc = chunk % CPR;
       *reinterpret_cast<uint4*>(&s_x[buf][r][cc * EPC]) = pre[q];
     }
-    if (threadIdx.x < 16) s_cols[buf][threadIdx.x] = tile_col(t, threadIdx.x);
   };
 
-  if (t_beg < t_end) {
-    load_tile(t_beg);
-    store_tile(0, t_beg);
-  }
-  __syncthreads();
-  for (int t = t_beg; t < t_end; ++t) {
-    const int buf = (t - t_beg) & 1;
-    if (t + 1 < t_end) load_tile(t + 1);
-    // A values of this lane: row li, tile columns 4 s + lg
-    float a[4];
-    const int blk0 = p.tile_blk[t];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int c = 4 * s + lg;
-      const int blk = blk0 + (c >> 3);
-      const bool have = !((c >> 3) == 1 && blk >= b_end);
-      const unsigned long long word = have ? p.blk_bits[(int64_t)blk * 2 + (li >> 3)] : 0ull;
-      const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
-      a[s] = bit ? col_weight(p, s_cols[buf][c]) : 0.0f;
-    }
-#pragma unroll
-    for (int ch = 0; ch < 4; ++ch) {
-      const int fl = wave * 64 + ch * 16 + li;   // feature within the slice
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float b = to_f32<T>(s_x[buf][4 * s + lg][fl]);
-        acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[ch], 0, 0, 0);
+  for (int tb = t_beg; tb < t_end; tb += MAXT) {
+    const int nt = min(MAXT, t_end - tb);
+    __syncthreads();  // the previous batch is done with the metadata and the buffers
+    for (int q = threadIdx.x; q < nt * 16; q += 256) {
+      const int k = q >> 4, c = q & 15;
+      const int blk = p.tile_blk[tb + k] + (c >> 3);
+      const bool have = !((c >> 3) == 1 && blk >= b_end);   // second block past the window: padding
+      const int col = have ? p.blk_col[blk * 8 + (c & 7)] : 0;
+      s_tcol[k][c] = col;
+      s_tw[k][c] = have ? col_weight(p, col) : 0.0f;
+      if (c < 4) {
+        const int bb = p.tile_blk[tb + k] + (c >> 1);
+        const bool hb = !((c >> 1) == 1 && bb >= b_end);
+        s_tbits[k][c] = hb ? p.blk_bits[(int64_t)bb * 2 + (c & 1)] : 0ull;
       }
     }
-    __syncthreads();  // every wave is done with the other buffer before it is refilled
-    if (t + 1 < t_end) store_tile(buf ^ 1, t + 1);
     __syncthreads();
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int k = 0; k < nt; ++k) {
+      const int buf = k & 1;
+      if (k + 1 < nt) load_tile(k + 1);
+      // A values of this lane: row li, tile columns 4 s + lg
+      float a[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 4 * s + lg;
+        const unsigned long long word = s_tbits[k][(c >> 3) * 2 + (li >> 3)];
+        const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
+        a[s] = bit ? s_tw[k][c] : 0.0f;
+      }
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const int fl = wave * 64 + ch * 16 + li;   // feature within the slice
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float b = to_f32<T>(s_x[buf][4 * s + lg][fl]);
+          acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[ch], 0, 0, 0);
+        }
+      }
+      __syncthreads();  // every wave is done with the other buffer before it is refilled
+      if (k + 1 < nt) store_tile(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   // residual entries of the window's rows: lane (li, lg) owns rows 4 lg .. 4 lg + 3 of

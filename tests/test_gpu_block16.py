@@ -209,3 +209,28 @@ def test_spmm_block16_rmat_partial_window_and_errors():
     plain = gnn.gnn_plan_create(csr)
     with pytest.raises(gnn.GnnError):
         gnn.gnn_spmm_block16(csr, dev_bf16(Xh), plan=plain)        # no WSB tiles in the plan
+
+
+def test_spmm_block16_cluster512k_full():
+    """The benchmark's block-sparse SpMM: the 512,000-node cluster graph, X 512k x 256
+    bf16, BOTH norm, default plan with WSB tiles; sampled rows (uniform and the
+    longest) against the oracle, and the whole output against the CSR SpMM."""
+    w = gen.gt_cluster(with_x=False)
+    rp, ci = w.row_ptr, w.col_idx
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, build_wsb=True)
+    assert gnn.gnn_plan_stats(plan)["wsb_dense_tiles"] > 0
+    Xh = gen.gauss_bf16(0xFEA70700, (n, 256))
+    Xd = dev_bf16(Xh)
+    Y = gnn.gnn_spmm_block16(csr, Xd, "both", plan=plan)
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.r_[rng.integers(0, n, 3000), np.argsort(-np.diff(rp), kind="stable")[:32]]).astype(np.int32)
+    ref, mag = oracle.spmm(rp, ci, Xh, "both", rows=rows, x_is_bf16=True)
+    assert scaled_err(host(Y[torch.from_numpy(rows).long().cuda()]), ref, mag) <= SPMM_TOL
+    # whole output: both kernels are within the bar of the exact sums, so they
+    # agree within twice the bar on the scale sum |w x| (A_norm |X|, exact 0 on
+    # rows without entries)
+    Yc = gnn.gnn_spmm(csr, Xd, "both", plan=plan)
+    mag_all = gnn.gnn_spmm(csr, Xd.abs(), "both", plan=plan)
+    assert bool(((Y - Yc).abs() <= 2 * SPMM_TOL * mag_all).all())
