@@ -112,12 +112,16 @@ __device__ __forceinline__ void shfl_merge(Soft<VEL>& s, int lane_xor) {
 //   qv / qraw : this lane's slice of the destination-side vector (GATv2: x_l
 //               as float; GT: q, raw, its scale * log2 e applied after the
 //               head reduction)
-//   av        : GATv2 attention-vector slice times log2 e (unused for GT)
+//   av, an    : GATv2 attention-vector slice times log2 e times (1 + slope) / 2
+//               and (1 - slope) / 2 (unused for GT): a * LReLU(z) =
+//               av * z + an * |z|, two multiply-adds (|z| is a free operand
+//               modifier) instead of a multiply, a max and a multiply-add
 template <typename T, int LPE, int NV, int KIND, int UU, int LPH>
 __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, int sl, int slot_base,
                                            bool d_ok, const float (&qv)[(16 / sizeof(T)) * NV],
                                            const Raw<NV>& qraw,
                                            const float (&av)[(16 / sizeof(T)) * NV],
+                                           const float (&an)[(16 / sizeof(T)) * NV],
                                            Soft<(16 / sizeof(T)) * NV>& st) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;
   const T* K = reinterpret_cast<const T*>(p.k) + sl * VEL;
@@ -155,7 +159,7 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 #pragma unroll
           for (int k = 0; k < VEL; ++k) {
             const float z = qv[k] + elem<T, NV>(x[u], k);
-            t = fmaf(av[k], fmaxf(z, p.slope * z), t);
+            t = fmaf(av[k], z, fmaf(an[k], fabsf(z), t));
           }
         } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
   }
 
   // destination-side slice (and the attention vector for GATv2)
-  float qv[VEL], av[VEL];
+  float qv[VEL], av[VEL], an[VEL];
   Raw<NV> qraw;
   if (d_ok) {
     load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + sl * VEL, qraw);
@@ -273,18 +277,22 @@ __global__ __launch_bounds__(WG) void k_attention(AttParams p) {
     for (int k = 0; k < VEL; ++k) qv[k] = elem<T, NV>(qraw, k);
     if constexpr (KIND == K_GATV2) {
 #pragma unroll
-      for (int k = 0; k < VEL; ++k) av[k] = p.att[sl * VEL + k] * kLog2e;
+      for (int k = 0; k < VEL; ++k) {
+        const float a = p.att[sl * VEL + k] * kLog2e;
+        av[k] = a * (0.5f + 0.5f * p.slope);
+        an[k] = a * (0.5f - 0.5f * p.slope);
+      }
     }
   } else {
 #pragma unroll
     for (int k = 0; k < 4 * NV; ++k) qraw.u[k] = 0u;
 #pragma unroll
-    for (int k = 0; k < VEL; ++k) qv[k] = av[k] = 0.0f;
+    for (int k = 0; k < VEL; ++k) qv[k] = av[k] = an[k] = 0.0f;
   }
 
   Soft<VEL> st;
   st.init();
-  scan_edges<T, LPE, NV, KIND, UU, LPH>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, st);
+  scan_edges<T, LPE, NV, KIND, UU, LPH>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, an, st);
 
   // s_a merges the waves of an item; light rows stage their output in it
   // (one LPE x VEL region per slot)

@@ -22,8 +22,8 @@
 // rounded weights.  Edges of tiles too sparse for the matrix cores (the
 // residual CSR of the plan) are then streamed per row into the same (m, l,
 // acc) state, the four lanes of a row splitting the head dimension.
-// Windows are mapped XCD-contiguously so the windows of one locally dense
-// cluster share an L2.
+// Windows are mapped to XCDs in runs of consecutive windows, so the windows of
+// one locally dense cluster share an L2.
 #include "gnn_internal.h"
 
 namespace gnn {
