@@ -755,6 +755,24 @@ WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, 
 
 # ---------------------------------------------------------------------------
 
+def _keep_pool_memory(device: int = 0) -> bool:
+    """Raise the release threshold of the device's default stream-ordered
+    memory pool, so memory the library frees (per-call temporaries of plan
+    builds and reorders) stays mapped for the next call instead of going back
+    to the driver, as in a long-running process.  HIP runtime API via ctypes."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return False
+    pool = ctypes.c_void_p()
+    if hip.hipDeviceGetDefaultMemPool(ctypes.byref(pool), device) != 0:
+        return False
+    threshold = ctypes.c_uint64(2 ** 63)
+    HIP_MEMPOOL_ATTR_RELEASE_THRESHOLD = 4
+    return hip.hipMemPoolSetAttribute(pool, HIP_MEMPOOL_ATTR_RELEASE_THRESHOLD, ctypes.byref(threshold)) == 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -773,6 +791,7 @@ def main():
     import torch
 
     torch.cuda.set_device(0)
+    pool_kept = _keep_pool_memory(0)
     w = WORKLOADS[args.workload](args)
     if args.ops:
         import fnmatch
@@ -850,6 +869,7 @@ def main():
         "per_op_ms": {k: round(v, 4) for k, v in per_op_ms.items()},
         "separate_launch_ms": separate_ms,
         "step_wall_ms": wall_step_ms,
+        "pool_memory_kept": pool_kept,
         "roofline": {"bound": "hbm", "kernel": f"{dom.name}: {w['kernel']}", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},

@@ -146,13 +146,31 @@ int launch_permute_rows(const int32_t* perm, int32_t n, const void* X, int elem_
 int launch_copy(const void* src, void* dst, int64_t n, hipStream_t s);
 
 // Device-wide exclusive scan of int32 counts into int32 offsets (out has n+1
-// entries, out[n] = total); scratch is allocated and freed stream-ordered.
-int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s);
+// entries, out[n] = total).  Scratch: scan_scratch_bytes(n) bytes at
+// `scratch`, or (NULL) allocated and freed stream-ordered.
+size_t scan_scratch_bytes(int64_t n);
+int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s, void* scratch = nullptr);
 
 // Stable LSD radix sort of 64-bit keys by bits [begin_bit, end_bit); result
-// in `keys`, `tmp` is scratch of n keys.
+// in `keys`, `tmp` is scratch of n keys.  Further scratch:
+// radix_scratch_bytes(n) bytes at `scratch`, or (NULL) allocated.
+size_t radix_scratch_bytes(int64_t n);
 int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
-                   hipStream_t s);
+                   hipStream_t s, void* scratch = nullptr);
+
+// Bump allocator over one device block: every temporary of a call carved
+// from a single allocation (256-byte aligned pieces).
+struct Arena {
+  char* base = nullptr;
+  size_t cap = 0, off = 0;
+  static size_t round(size_t b) { return (b + 255) & ~(size_t)255; }
+  template <typename T>
+  T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base + off);
+    off += round(count * sizeof(T));
+    return p;
+  }
+};
 
 // dot-aggr micro-benchmark (dot_aggr.hip): map 0 = feature-parallel,
 // 1 = neighbour-parallel; vec = 16-byte loads per lane

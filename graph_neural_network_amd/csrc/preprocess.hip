@@ -318,27 +318,36 @@ int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
   return GNN_OK;
 }
 
-int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s) {
+size_t scan_scratch_bytes(int64_t n) {
+  const int64_t nb = (n + kScanTile - 1) / kScanTile;
+  if (nb <= 1) return 0;
+  return Arena::round((size_t)nb * 4) + Arena::round((size_t)(nb + 1) * 4) + scan_scratch_bytes(nb);
+}
+
+int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s, void* scratch) {
   int64_t nb = (n + kScanTile - 1) / kScanTile;
   if (nb <= 1) {
     hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kScanThreads), 0, s, in, n, nullptr, out);
     GNN_LAUNCH_CHECK("scan");
     return GNN_OK;
   }
-  int32_t* sums = nullptr;
-  int32_t* offs = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&sums, nb * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&offs, (nb + 1) * 4, s));
+  void* own = nullptr;
+  if (!scratch) {
+    GNN_HIP(hipMallocAsync(&own, scan_scratch_bytes(n), s));
+    scratch = own;
+  }
+  Arena a{static_cast<char*>(scratch), scan_scratch_bytes(n), 0};
+  int32_t* sums = a.take<int32_t>(nb);
+  int32_t* offs = a.take<int32_t>(nb + 1);
   hipLaunchKernelGGL(k_scan_block_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, sums);
   GNN_LAUNCH_CHECK("scan sums");
-  int rc = exclusive_scan_i32(sums, offs, nb, s);
+  int rc = exclusive_scan_i32(sums, offs, nb, s, a.base + a.off);
   if (rc == GNN_OK) {
     hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, offs,
                        out);
     GNN_LAUNCH_CHECK("scan tiles");
   }
-  GNN_HIP(hipFreeAsync(sums, s));
-  GNN_HIP(hipFreeAsync(offs, s));
+  if (own) GNN_HIP(hipFreeAsync(own, s));
   return rc;
 }
 

@@ -277,11 +277,16 @@ __global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
 
 // ---------------------------------------------------------------------------
 
-int degree_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
+size_t degree_bytes(int32_t n) {
+  return Arena::round(4) + 2 * Arena::round((size_t)n * 8) + radix_scratch_bytes(n);
+}
+
+int degree_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   const int32_t n = c->n_rows;
-  int32_t* mx = nullptr;
-  uint64_t *keys = nullptr, *tmp = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&mx, 4, s));
+  int32_t* mx = ar.take<int32_t>(1);
+  uint64_t* keys = ar.take<uint64_t>(n);
+  uint64_t* tmp = ar.take<uint64_t>(n);
+  void* ws = ar.base + ar.off;
   GNN_HIP(hipMemsetAsync(mx, 0, 4, s));
   hipLaunchKernelGGL(k_max_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, n, mx);
   GNN_LAUNCH_CHECK("max degree");
@@ -291,85 +296,90 @@ int degree_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
   const int idbits = bits_for(n);
   const int dbits = bits_for(maxdeg);
   if (idbits + dbits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "degree keys exceed 64 bits");
-  GNN_HIP(hipMallocAsync((void**)&keys, (size_t)n * 8, s));
-  GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)n * 8, s));
   hipLaunchKernelGGL(k_deg_keys, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, n, maxdeg, idbits, keys);
   GNN_LAUNCH_CHECK("degree keys");
-  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + dbits, s));
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + dbits, s, ws));
   hipLaunchKernelGGL(k_low_bits, dim3(nb(n)), dim3(256), 0, s, keys, (int64_t)n, idbits, perm);
   GNN_LAUNCH_CHECK("degree perm");
-  GNN_HIP(hipFreeAsync(mx, s));
-  GNN_HIP(hipFreeAsync(keys, s));
-  GNN_HIP(hipFreeAsync(tmp, s));
   return GNN_OK;
 }
 
-int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
+// Temporaries of rcm_perm: two flag / offset slabs of 2 nnz + 1 entries
+// (loop flags, then duplicate flags, then frontier-edge flags, each with its
+// scan), two key arrays, the symmetrised adjacency with its row ids, eleven
+// per-vertex arrays, and scan / sort scratch.
+size_t rcm_bytes(int32_t n, int64_t nnz) {
+  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
+  size_t b = 2 * Arena::round((size_t)(M2 + 1) * 4) + 2 * Arena::round((size_t)NN * 8) +
+             2 * Arena::round((size_t)M2 * 4) + 4 * Arena::round((size_t)(n + 1) * 4) +
+             6 * Arena::round((size_t)n * 4) + Arena::round(4);
+  return b + std::max(scan_scratch_bytes(NN + 1), radix_scratch_bytes(NN));
+}
+
+int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   const int32_t n = c->n_rows;
   const int64_t nnz = c->nnz;
   const int idbits = bits_for(n);
   if (2 * idbits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM keys exceed 64 bits");
+  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
+  int32_t* slab0 = ar.take<int32_t>(M2 + 1);
+  int32_t* slab1 = ar.take<int32_t>(M2 + 1);
+  uint64_t* keys = ar.take<uint64_t>(NN);
+  uint64_t* tmp = ar.take<uint64_t>(NN);
+  int32_t* adj = ar.take<int32_t>(M2);
+  int32_t* adj_row = ar.take<int32_t>(M2);
+  int32_t* cnt = ar.take<int32_t>(n + 1);
+  int32_t* sym_ptr = ar.take<int32_t>(n + 1);
+  int32_t* ccnt = ar.take<int32_t>(n + 1);
+  int32_t* coff = ar.take<int32_t>(n + 1);
+  int32_t* order = ar.take<int32_t>(n);
+  int32_t* rank = ar.take<int32_t>(n);
+  int32_t* label = ar.take<int32_t>(n);
+  int32_t* concat = ar.take<int32_t>(n);
+  int32_t* visited = ar.take<int32_t>(n);
+  int32_t* claim = ar.take<int32_t>(n);
+  int32_t* changed = ar.take<int32_t>(1);
+  void* ws = ar.base + ar.off;  // scan and sort scratch
 
   // 1. symmetrised pattern without loops, as sorted unique (row, col) keys
-  int32_t *flag = nullptr, *pos = nullptr;
-  size_t fl = (size_t)std::max<int64_t>(nnz, 1) + 1;
-  GNN_HIP(hipMallocAsync((void**)&flag, fl * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&pos, fl * 4, s));
+  int32_t *flag = slab0, *pos = slab1;
   if (nnz > 0) {
     hipLaunchKernelGGL(k_loop_flags, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag);
     GNN_LAUNCH_CHECK("rcm loop flags");
   }
-  GNN_TRY(exclusive_scan_i32(flag, pos, nnz, s));
+  GNN_TRY(exclusive_scan_i32(flag, pos, nnz, s, ws));
   int32_t nl = 0;
   GNN_HIP(hipMemcpyAsync(&nl, pos + nnz, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   const int64_t m2 = 2 * (int64_t)nl;
   if (m2 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM: symmetrised pattern too large");
-  uint64_t *keys = nullptr, *tmp = nullptr;
-  const size_t kb = (size_t)std::max<int64_t>(std::max<int64_t>(m2, n), 1) * 8;
-  GNN_HIP(hipMallocAsync((void**)&keys, kb, s));
-  GNN_HIP(hipMallocAsync((void**)&tmp, kb, s));
   if (nnz > 0) {
     hipLaunchKernelGGL(k_sym_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag,
                        pos, idbits, keys);
     GNN_LAUNCH_CHECK("rcm sym keys");
   }
-  GNN_HIP(hipFreeAsync(flag, s));
-  GNN_HIP(hipFreeAsync(pos, s));
-  GNN_TRY(radix_sort_u64(keys, tmp, m2, 0, 2 * idbits, s));
-  int32_t *uf = nullptr, *up = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&uf, ((size_t)m2 + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&up, ((size_t)m2 + 1) * 4, s));
+  GNN_TRY(radix_sort_u64(keys, tmp, m2, 0, 2 * idbits, s, ws));
+  int32_t *uf = slab0, *up = slab1;  // the loop flags are no longer needed
   if (m2 > 0) {
     hipLaunchKernelGGL(k_uniq_flags, dim3(nb(m2)), dim3(256), 0, s, keys, m2, uf);
     GNN_LAUNCH_CHECK("rcm unique");
   }
-  GNN_TRY(exclusive_scan_i32(uf, up, m2, s));
+  GNN_TRY(exclusive_scan_i32(uf, up, m2, s, ws));
   int32_t m32 = 0;
   GNN_HIP(hipMemcpyAsync(&m32, up + m2, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   const int64_t m = m32;  // entries of the symmetrised pattern
-  int32_t *adj = nullptr, *adj_row = nullptr, *cnt = nullptr, *sym_ptr = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&adj, (size_t)std::max<int64_t>(m, 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&adj_row, (size_t)std::max<int64_t>(m, 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&cnt, ((size_t)n + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&sym_ptr, ((size_t)n + 1) * 4, s));
   GNN_HIP(hipMemsetAsync(cnt, 0, ((size_t)n + 1) * 4, s));
   if (m2 > 0) {
     hipLaunchKernelGGL(k_sym_fill, dim3(nb(m2)), dim3(256), 0, s, keys, uf, up, m2, idbits, adj, adj_row, cnt);
     GNN_LAUNCH_CHECK("rcm sym fill");
   }
-  GNN_TRY(exclusive_scan_i32(cnt, sym_ptr, n, s));
-  GNN_HIP(hipFreeAsync(uf, s));
-  GNN_HIP(hipFreeAsync(up, s));
+  GNN_TRY(exclusive_scan_i32(cnt, sym_ptr, n, s, ws));
 
   // 2. global (delta, id) order and ranks
-  int32_t *order = nullptr, *rank = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&order, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&rank, (size_t)n * 4, s));
   hipLaunchKernelGGL(k_rank_keys, dim3(nb(n)), dim3(256), 0, s, sym_ptr, n, idbits, keys);
   GNN_LAUNCH_CHECK("rcm rank keys");
-  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + bits_for(m + 1), s));
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, idbits + bits_for(m + 1), s, ws));
   hipLaunchKernelGGL(k_rank, dim3(nb(n)), dim3(256), 0, s, keys, n, idbits, order, rank);
   GNN_LAUNCH_CHECK("rcm rank");
 
@@ -377,15 +387,12 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
   if (m > 0) {
     hipLaunchKernelGGL(k_adj_keys, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, m, idbits, keys);
     GNN_LAUNCH_CHECK("rcm adj keys");
-    GNN_TRY(radix_sort_u64(keys, tmp, m, 0, 2 * idbits, s));
+    GNN_TRY(radix_sort_u64(keys, tmp, m, 0, 2 * idbits, s, ws));
     hipLaunchKernelGGL(k_adj_from_keys, dim3(nb(m)), dim3(256), 0, s, keys, order, m, idbits, adj);
     GNN_LAUNCH_CHECK("rcm adj sort");
   }
 
   // 4. component labels: smallest rank in the component
-  int32_t *label = nullptr, *changed = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&label, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&changed, 4, s));
   GNN_HIP(hipMemcpyAsync(label, rank, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
   for (int it = 0;; ++it) {
     int32_t ch = 0;
@@ -403,22 +410,15 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
   }
 
   // 5. level-synchronous BFS of all components at once
-  int32_t *concat = nullptr, *visited = nullptr, *claim = nullptr, *ccnt = nullptr, *coff = nullptr;
-  int32_t *qflag = nullptr, *qpos = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&concat, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&visited, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&claim, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&ccnt, ((size_t)n + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&coff, ((size_t)n + 1) * 4, s));
-  // frontier-edge flags and positions: a level touches at most every entry once
-  GNN_HIP(hipMallocAsync((void**)&qflag, ((size_t)std::max<int64_t>(m, 1) + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&qpos, ((size_t)std::max<int64_t>(m, 1) + 1) * 4, s));
+  // frontier-edge flags and positions (a level touches at most every entry
+  // once) in the slabs, whose duplicate flags are no longer needed
+  int32_t *qflag = slab0, *qpos = slab1;
   GNN_HIP(hipMemsetAsync(visited, 0, (size_t)n * 4, s));
   hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
   GNN_LAUNCH_CHECK("rcm claim init");
   hipLaunchKernelGGL(k_start_flags, dim3(nb(n)), dim3(256), 0, s, order, label, n, ccnt);
   GNN_LAUNCH_CHECK("rcm starts");
-  GNN_TRY(exclusive_scan_i32(ccnt, coff, n, s));
+  GNN_TRY(exclusive_scan_i32(ccnt, coff, n, s, ws));
   hipLaunchKernelGGL(k_start_fill, dim3(nb(n)), dim3(256), 0, s, order, ccnt, coff, n, concat, visited);
   GNN_LAUNCH_CHECK("rcm level 0");
   int32_t f = 0;
@@ -431,7 +431,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
     // frontier degrees -> offsets of the flattened frontier adjacency
     hipLaunchKernelGGL(k_front_deg, dim3(nb(f)), dim3(256), 0, s, front, f, sym_ptr, ccnt);
     GNN_LAUNCH_CHECK("rcm frontier degrees");
-    GNN_TRY(exclusive_scan_i32(ccnt, coff, f, s));
+    GNN_TRY(exclusive_scan_i32(ccnt, coff, f, s, ws));
     int32_t ef = 0;
     GNN_HIP(hipMemcpyAsync(&ef, coff + f, 4, hipMemcpyDeviceToHost, s));
     GNN_HIP(hipStreamSynchronize(s));
@@ -443,7 +443,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
       hipLaunchKernelGGL(k_child_flags, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
                          sym_ptr, adj, visited, claim, qflag);
       GNN_LAUNCH_CHECK("rcm level flags");
-      GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s));
+      GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s, ws));
       GNN_HIP(hipMemcpyAsync(&nf, qpos + ef, 4, hipMemcpyDeviceToHost, s));
       GNN_HIP(hipStreamSynchronize(s));
     }
@@ -463,55 +463,65 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, hipStream_t s) {
   // 6. (component, level, position) order by a stable sort on the label; reverse
   hipLaunchKernelGGL(k_final_keys, dim3(nb(n)), dim3(256), 0, s, concat, label, n, idbits, keys);
   GNN_LAUNCH_CHECK("rcm final keys");
-  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, 2 * idbits, s));
+  GNN_TRY(radix_sort_u64(keys, tmp, n, idbits, 2 * idbits, s, ws));
   hipLaunchKernelGGL(k_final_perm, dim3(nb(n)), dim3(256), 0, s, keys, concat, n, idbits, perm);
   GNN_LAUNCH_CHECK("rcm perm");
-
-  for (void* q : {(void*)keys, (void*)tmp, (void*)adj, (void*)adj_row, (void*)cnt, (void*)sym_ptr,
-                  (void*)order, (void*)rank, (void*)label, (void*)changed, (void*)concat,
-                  (void*)visited, (void*)claim, (void*)ccnt, (void*)coff, (void*)qflag, (void*)qpos})
-    GNN_HIP(hipFreeAsync(q, s));
   return GNN_OK;
 }
 
-int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t* ci_out,
+size_t permute_bytes(int32_t n, int64_t nnz) {
+  const int64_t m = std::max<int64_t>(nnz, 1);
+  return 2 * Arena::round((size_t)n * 4) + 2 * Arena::round((size_t)m * 8) +
+         std::max(scan_scratch_bytes(n), radix_scratch_bytes(m));
+}
+
+int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t* ci_out, Arena& ar,
                 hipStream_t s) {
   const int32_t n = c->n_rows;
   const int64_t nnz = c->nnz;
-  int32_t *inv = nullptr, *deg = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&inv, (size_t)n * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&deg, (size_t)n * 4, s));
+  int32_t* inv = ar.take<int32_t>(n);
+  int32_t* deg = ar.take<int32_t>(n);
+  uint64_t* keys = ar.take<uint64_t>(std::max<int64_t>(nnz, 1));
+  uint64_t* tmp = ar.take<uint64_t>(std::max<int64_t>(nnz, 1));
+  void* ws = ar.base + ar.off;
   hipLaunchKernelGGL(k_inverse, dim3(nb(n)), dim3(256), 0, s, perm, n, inv);
   hipLaunchKernelGGL(k_new_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, perm, n, deg);
   GNN_LAUNCH_CHECK("permute degrees");
-  GNN_TRY(exclusive_scan_i32(deg, rp_out, n, s));
+  GNN_TRY(exclusive_scan_i32(deg, rp_out, n, s, ws));
   if (nnz > 0) {
     const int colbits = bits_for(n);
-    uint64_t *keys = nullptr, *tmp = nullptr;
-    GNN_HIP(hipMallocAsync((void**)&keys, (size_t)nnz * 8, s));
-    GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)nnz * 8, s));
     hipLaunchKernelGGL(k_perm_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
                        rp_out, n, nnz, colbits, keys);
     GNN_LAUNCH_CHECK("permute keys");
-    GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, 2 * colbits, s));
+    GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, 2 * colbits, s, ws));
     hipLaunchKernelGGL(k_low_bits, dim3(nb(nnz)), dim3(256), 0, s, keys, nnz, colbits, ci_out);
     GNN_LAUNCH_CHECK("permute cols");
-    GNN_HIP(hipFreeAsync(keys, s));
-    GNN_HIP(hipFreeAsync(tmp, s));
   }
-  GNN_HIP(hipFreeAsync(inv, s));
-  GNN_HIP(hipFreeAsync(deg, s));
   return GNN_OK;
 }
 
 }  // namespace
 
+// One device block per call holds every temporary (the permutation step, then
+// the relabelling, which reuses it in stream order).
 int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* rp_out,
                    int32_t* ci_out, hipStream_t s) {
-  if (kind == GNN_REORDER_DEGREE) GNN_TRY(degree_perm(csr, perm, s));
-  else GNN_TRY(rcm_perm(csr, perm, s));
-  if (rp_out) GNN_TRY(permute_csr(csr, perm, rp_out, ci_out, s));
-  GNN_HIP(hipStreamSynchronize(s));
+  const int32_t n = csr->n_rows;
+  size_t need = kind == GNN_REORDER_DEGREE ? degree_bytes(n) : rcm_bytes(n, csr->nnz);
+  if (rp_out) need = std::max(need, permute_bytes(n, csr->nnz));
+  void* blk = nullptr;
+  GNN_HIP(hipMallocAsync(&blk, need, s));
+  Arena ar{static_cast<char*>(blk), need, 0};
+  int rc = kind == GNN_REORDER_DEGREE ? degree_perm(csr, perm, ar, s) : rcm_perm(csr, perm, ar, s);
+  if (rc == GNN_OK && rp_out) {
+    ar.off = 0;
+    rc = permute_csr(csr, perm, rp_out, ci_out, ar, s);
+  }
+  const hipError_t e1 = hipFreeAsync(blk, s);
+  const hipError_t e2 = hipStreamSynchronize(s);
+  if (rc != GNN_OK) return rc;
+  if (e1 != hipSuccess || e2 != hipSuccess)
+    return fail(GNN_ERR_DEVICE, std::string("reorder: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
   return GNN_OK;
 }
 

@@ -76,17 +76,28 @@ __global__ __launch_bounds__(RT) void k_rs_scatter(const uint64_t* keys, uint64_
 
 }  // namespace
 
+size_t radix_scratch_bytes(int64_t n) {
+  const int64_t ntiles = (n + RTILE - 1) / RTILE;
+  return Arena::round((size_t)ntiles * 256 * 4) + Arena::round((size_t)(ntiles * 256 + 1) * 4) +
+         scan_scratch_bytes(ntiles * 256);
+}
+
 // Sorts keys[0..n) by bits [begin_bit, end_bit) ascending, stably; the result
 // ends up in `keys` (tmp is scratch of the same size).  n < 2^31.
 int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int end_bit,
-                   hipStream_t s) {
+                   hipStream_t s, void* scratch) {
   if (n <= 1 || end_bit <= begin_bit) return GNN_OK;
   const int64_t ntiles = (n + RTILE - 1) / RTILE;
   if (ntiles * 256 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "radix sort too large");
-  int32_t* hist = nullptr;
-  int32_t* offs = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&hist, ntiles * 256 * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&offs, (ntiles * 256 + 1) * 4, s));
+  void* own = nullptr;
+  if (!scratch) {
+    GNN_HIP(hipMallocAsync(&own, radix_scratch_bytes(n), s));
+    scratch = own;
+  }
+  Arena a{static_cast<char*>(scratch), radix_scratch_bytes(n), 0};
+  int32_t* hist = a.take<int32_t>(ntiles * 256);
+  int32_t* offs = a.take<int32_t>(ntiles * 256 + 1);
+  void* scan_ws = a.base + a.off;
   uint64_t* src = keys;
   uint64_t* dst = tmp;
   int rc = GNN_OK;
@@ -94,7 +105,7 @@ int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int 
     hipLaunchKernelGGL(k_rs_hist, dim3((unsigned)ntiles), dim3(RT), 0, s, src, n, shift, hist,
                        (int32_t)ntiles);
     GNN_LAUNCH_CHECK("radix hist");
-    rc = exclusive_scan_i32(hist, offs, ntiles * 256, s);
+    rc = exclusive_scan_i32(hist, offs, ntiles * 256, s, scan_ws);
     if (rc != GNN_OK) break;
     hipLaunchKernelGGL(k_rs_scatter, dim3((unsigned)ntiles), dim3(RT), 0, s, src, dst, n, shift, offs,
                        (int32_t)ntiles);
@@ -103,8 +114,7 @@ int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int 
   }
   if (rc == GNN_OK && src != keys)
     GNN_HIP(hipMemcpyAsync(keys, src, n * 8, hipMemcpyDeviceToDevice, s));
-  GNN_HIP(hipFreeAsync(hist, s));
-  GNN_HIP(hipFreeAsync(offs, s));
+  if (own) GNN_HIP(hipFreeAsync(own, s));
   return rc;
 }
 
