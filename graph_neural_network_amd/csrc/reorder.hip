@@ -125,13 +125,26 @@ __global__ void k_uniq_flags(const uint64_t* keys, int64_t m, int32_t* flag) {
 }
 
 __global__ void k_sym_fill(const uint64_t* keys, const int32_t* flag, const int32_t* pos, int64_t m,
-                           int idbits, int32_t* adj, int32_t* adj_row, int32_t* cnt) {
+                           int idbits, int32_t* adj, int32_t* adj_row) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= m || !flag[e]) return;
-  const int r = (int)(keys[e] >> idbits);
   adj[pos[e]] = (int32_t)(keys[e] & ((1ull << idbits) - 1));
-  adj_row[pos[e]] = r;
-  atomicAdd(&cnt[r], 1);
+  adj_row[pos[e]] = (int32_t)(keys[e] >> idbits);
+}
+
+// Row pointers of the symmetrised pattern: adj_row is sorted, so row r starts
+// at the first entry not below r (a binary search per row; r = n gives m).
+// Counting entries per row with atomics instead serialises on hub rows.
+__global__ void k_row_bounds(const int32_t* adj_row, int64_t m, int32_t n, int32_t* sym_ptr) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r > n) return;
+  int64_t lo = 0, hi = m;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (adj_row[mid] < r) lo = mid + 1;
+    else hi = mid;
+  }
+  sym_ptr[r] = (int32_t)lo;
 }
 
 __global__ void k_rank_keys(const int32_t* sym_ptr, int32_t n, int idbits, uint64_t* keys) {
@@ -163,27 +176,45 @@ __global__ void k_adj_from_keys(const uint64_t* keys, const int32_t* order, int6
 }
 
 // min-label propagation over edges, then shortcutting through the label's vertex
+// adj_row is sorted, so the entries of one row are consecutive lanes: a
+// segmented minimum over the wave leaves each row's smallest neighbour label
+// in the row's first lane, which alone updates the row's label (hub rows
+// would otherwise take one contended atomic per entry).  One store of the
+// `changed` flag per wave.
 __global__ void k_label_edges(const int32_t* adj, const int32_t* adj_row, int64_t m, int32_t* label,
                               int32_t* changed) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= m) return;
-  const int a = adj_row[e], b = adj[e];
-  const int la = label[a], lb = label[b];
-  if (lb < la) {
-    atomicMin(&label[a], lb);
-    *changed = 1;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const bool ok = e < m;
+  const int a = ok ? adj_row[e] : -1;
+  int lb = ok ? label[adj[e]] : 0x7FFFFFFF;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int a2 = __shfl_down(a, o, 64);
+    const int l2 = __shfl_down(lb, o, 64);
+    if (lane + o < 64 && a2 == a) lb = min(lb, l2);
   }
+  const int a_prev = __shfl_up(a, 1, 64);
+  bool ch = false;
+  if (ok && (lane == 0 || a_prev != a) && lb < label[a]) {
+    atomicMin(&label[a], lb);
+    ch = true;
+  }
+  if (__ballot(ch) && lane == 0) *changed = 1;
 }
 
 __global__ void k_label_jump(const int32_t* order, int32_t n, int32_t* label, int32_t* changed) {
-  int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= n) return;
-  const int l = label[v];
-  const int l2 = label[order[l]];
-  if (l2 < l) {
-    atomicMin(&label[v], l2);
-    *changed = 1;
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  bool ch = false;
+  if (v < n) {
+    const int l = label[v];
+    const int l2 = label[order[l]];
+    if (l2 < l) {
+      atomicMin(&label[v], l2);
+      ch = true;
+    }
   }
+  if (__ballot(ch) && (threadIdx.x & 63) == 0) *changed = 1;
 }
 
 __global__ void k_start_flags(const int32_t* order, const int32_t* label, int32_t n, int32_t* flag) {
@@ -306,12 +337,12 @@ int degree_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
 
 // Temporaries of rcm_perm: two flag / offset slabs of 2 nnz + 1 entries
 // (loop flags, then duplicate flags, then frontier-edge flags, each with its
-// scan), two key arrays, the symmetrised adjacency with its row ids, eleven
+// scan), two key arrays, the symmetrised adjacency with its row ids, ten
 // per-vertex arrays, and scan / sort scratch.
 size_t rcm_bytes(int32_t n, int64_t nnz) {
   const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
   size_t b = 2 * Arena::round((size_t)(M2 + 1) * 4) + 2 * Arena::round((size_t)NN * 8) +
-             2 * Arena::round((size_t)M2 * 4) + 4 * Arena::round((size_t)(n + 1) * 4) +
+             2 * Arena::round((size_t)M2 * 4) + 3 * Arena::round((size_t)(n + 1) * 4) +
              6 * Arena::round((size_t)n * 4) + Arena::round(4);
   return b + std::max(scan_scratch_bytes(NN + 1), radix_scratch_bytes(NN));
 }
@@ -328,7 +359,6 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   uint64_t* tmp = ar.take<uint64_t>(NN);
   int32_t* adj = ar.take<int32_t>(M2);
   int32_t* adj_row = ar.take<int32_t>(M2);
-  int32_t* cnt = ar.take<int32_t>(n + 1);
   int32_t* sym_ptr = ar.take<int32_t>(n + 1);
   int32_t* ccnt = ar.take<int32_t>(n + 1);
   int32_t* coff = ar.take<int32_t>(n + 1);
@@ -369,12 +399,12 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   GNN_HIP(hipMemcpyAsync(&m32, up + m2, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   const int64_t m = m32;  // entries of the symmetrised pattern
-  GNN_HIP(hipMemsetAsync(cnt, 0, ((size_t)n + 1) * 4, s));
   if (m2 > 0) {
-    hipLaunchKernelGGL(k_sym_fill, dim3(nb(m2)), dim3(256), 0, s, keys, uf, up, m2, idbits, adj, adj_row, cnt);
+    hipLaunchKernelGGL(k_sym_fill, dim3(nb(m2)), dim3(256), 0, s, keys, uf, up, m2, idbits, adj, adj_row);
     GNN_LAUNCH_CHECK("rcm sym fill");
   }
-  GNN_TRY(exclusive_scan_i32(cnt, sym_ptr, n, s, ws));
+  hipLaunchKernelGGL(k_row_bounds, dim3(nb((int64_t)n + 1)), dim3(256), 0, s, adj_row, m, n, sym_ptr);
+  GNN_LAUNCH_CHECK("rcm row bounds");
 
   // 2. global (delta, id) order and ranks
   hipLaunchKernelGGL(k_rank_keys, dim3(nb(n)), dim3(256), 0, s, sym_ptr, n, idbits, keys);
