@@ -58,6 +58,7 @@ struct AggParams {
   int32_t light_max;
   int32_t n_item_blocks;   // item workgroups in grid.x
   int32_t n_light_blocks;
+  int32_t rps;             // light rows per slot (LPR on large graphs)
   int32_t norm;            // gnn_norm (SpMM); MEAN is expressed as LEFT
   int32_t weighted;        // edge_val present or RIGHT / BOTH
   // K_ALL outputs (each nullable; Y above is the sum), and the min words
@@ -478,14 +479,14 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
     return;
   }
 
-  // ---------------- light rows: LPR consecutive rows per slot ----------------
-  // The slot's lanes hold one row each: a prefix sum of the light degrees
+  // ---------------- light rows: rps <= LPR consecutive rows per slot ----------------
+  // The slot's first rps lanes hold one row each: a prefix sum of the light degrees
   // lays the rows' edges out as one flat sequence, which the slot walks with
   // U gathers in flight across row boundaries; a row is written when the
   // walk leaves it.  Rows of the other classes inside the range count as
   // empty here (their items write them); empty light rows get the identity.
   const uint32_t lb = dev::xcd_remap(blockIdx.x - n_item_pad, p.n_light_blocks);
-  const int64_t r0 = (int64_t)lb * WG + (int64_t)slot * LPR;
+  const int64_t r0 = ((int64_t)lb * (WG / LPR) + slot) * p.rps;
   if (r0 >= p.n_rows) return;
   const int ft0 = blockIdx.y * FT;
   float* stage = ((KIND == K_SUM || KIND == K_ALL) ? s_acc
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
                                            : reinterpret_cast<float*>(s_key)) + slot * FT;
   const int64_t myr = r0 + sl;
   int rs = 0, dr = -1;
-  if (myr < p.n_rows) {
+  if (sl < p.rps && myr < p.n_rows) {
     rs = p.row_ptr[myr];
     dr = p.row_ptr[myr + 1] - rs;
   }
@@ -635,8 +636,15 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   constexpr int FT = LPR * VE;
   const int ftiles = (p.F + FT - 1) / FT;
   p.n_item_blocks = (int32_t)pl->n_items;
-  // a light workgroup covers WG rows: 64 / LPR slots per wave, LPR rows per slot
-  p.n_light_blocks = (int32_t)((p.n_rows + WG - 1) / WG);
+  // a light workgroup covers (WG / LPR) * rps rows: 64 / LPR slots per wave,
+  // rps rows per slot.  rps = LPR unless that leaves fewer than 1024
+  // workgroups (four per CU): a slot walks its rows' edges as one dependent
+  // sequence, so on small graphs fewer rows per slot cut the latency chain.
+  const int64_t spw = WG / LPR;
+  int rps = LPR;
+  while (rps > 1 && (p.n_rows + spw * rps - 1) / (spw * rps) * ftiles < 1024) rps >>= 1;
+  p.rps = rps;
+  p.n_light_blocks = (int32_t)((p.n_rows + spw * rps - 1) / (spw * rps));
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "aggregate grid too large");
   if (KIND != K_SUM && pl->n_multi > 0) {
