@@ -124,8 +124,11 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
                                            const float (&an)[(16 / sizeof(T)) * NV],
                                            Soft<(16 / sizeof(T)) * NV>& st) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;
-  const T* K = reinterpret_cast<const T*>(p.k) + sl * VEL;
-  const T* V = reinterpret_cast<const T*>(p.v) + sl * VEL;
+  const T* K = reinterpret_cast<const T*>(p.k);
+  const T* V = reinterpret_cast<const T*>(p.v);
+  // this lane's slice of a row; lanes past the row read its first slice (their
+  // query / attention-vector slices are zero, so they add nothing)
+  const uint32_t loff = d_ok ? (uint32_t)(sl * VEL) : 0u;
   const int64_t ld = p.row_elems;
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
@@ -138,18 +141,14 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
       for (int u = 0; u < UU; ++u)
         c[u] = (LPE == 64) ? __builtin_amdgcn_readlane(my_c, u0 + u)  // one slot per wave: scalar
                            : __shfl(my_c, slot_base + u0 + u, 64);
+      // every slot loads UU rows without branches: edges past the slot's end
+      // re-read its first edge's row (finite values; their score is -inf, so
+      // their weight is 0)
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
-        if (u0 + u < nb && d_ok) {
-          load_raw<T, NV>(K + (int64_t)c[u] * ld, x[u]);
-          if constexpr (KIND == K_GT) load_raw<T, NV>(V + (int64_t)c[u] * ld, y[u]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4 * NV; ++k) {
-            x[u].u[k] = 0u;
-            if constexpr (KIND == K_GT) y[u].u[k] = 0u;
-          }
-        }
+        const int cu = (u0 + u < nb) ? c[u] : c[0];
+        load_raw<T, NV>(K + (int64_t)cu * ld + loff, x[u]);
+        if constexpr (KIND == K_GT) load_raw<T, NV>(V + (int64_t)cu * ld + loff, y[u]);
       }
       float s[UU];
 #pragma unroll
