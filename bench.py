@@ -154,8 +154,11 @@ def wl_reduce_f128(args):
            "F": F, "x_dtype": "f32", "ops": ["sum", "mean", "max+arg", "min+arg"],
            "step": "one fused pass (gnn_reduce_multi); value counts 4 aggregations x edges",
            "plan_build_ms": round(plan_ms, 2), "plan": stats}
+    # every tensor once: row pointers, column indices, X, four value outputs, two index outputs
+    comp = 4 * (n + 1) + 4 * m + 7 * n * row_b
     return {"ops": ops, "dominant": "multi", "kernel": "k_aggregate<float, 32, 4, 3, true>",
-            "config": cfg, "dtype": "f32", "cpu": cpu_sample, "separate": separate,
+            "config": cfg, "dtype": "f32", "cpu": cpu_sample, "separate": separate, "compulsory": comp,
+            "cpu_1thread": True,
             "keep": (w, X, csr, plan, Y, A, outs)}
 
 
@@ -231,8 +234,10 @@ def wl_gatv2(args):
 
     cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)+self-loops", "nodes": n, "edges": m,
            "heads": H, "head_dim": D, "x_dtype": "bf16", "plan": gnn.gnn_plan_stats(plan)}
+    comp = 4 * (n + 1) + 4 * m + 2 * n * row_b + H * D * 4 + n * (H * D * 4 + H * 4)
     return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 1, 0, 4, 4>",
-            "config": cfg, "dtype": "bf16", "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse)}
+            "config": cfg, "dtype": "bf16", "cpu": cpu, "compulsory": comp, "cpu_1thread": True,
+            "keep": (w, csr, plan, xl, xr, att, out, lse)}
 
 
 def wl_gt(args, mode="csr"):
@@ -275,7 +280,14 @@ def wl_gt(args, mode="csr"):
            "nodes": n, "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16", "mode": mode,
            "plan_build_ms": round(plan_ms, 2), "plan": st}
     kern = "k_attention<unsigned short, 64, 1, 1, 4, 8>" if mode == "csr" else "k_gt_block16<64, 2>"
+    # every tensor once (BLOCK16 also reads the WSB layout: window and tile offsets, 48-byte
+    # blocks, tile list, residual CSR)
+    comp = 4 * (n + 1) + 4 * m + 3 * n * row_b + n * (H * D * 4 + H * 4)
+    if mode != "csr":
+        comp += (8 * st["wsb_windows"] + 48 * st["wsb_blocks"] + 4 * st["wsb_dense_tiles"]
+                 + 4 * (n + 1) + 4 * st["wsb_residual_edges"])
     return {"ops": ops, "dominant": "gt", "kernel": kern, "config": cfg, "dtype": "bf16", "cpu": cpu,
+            "compulsory": comp,
             "keep": (w, csr, plan, q, k, v, out, lse)}
 
 
@@ -321,8 +333,9 @@ def wl_spmm_large(args):
            "x_dtype": "bf16", "orders": list(variants), "reorder_ms": reorder_ms,
            "input_generation_s": round(gen_s, 1),
            "plan": gnn.gnn_plan_stats(variants["original"][2])}
+    comp = 4 * (n + 1) + 4 * m + n * F * 2 + n * F * 4
     return {"ops": ops, "dominant": "original", "kernel": "k_aggregate<unsigned short, 32, 8, 0, false>",
-            "config": cfg, "dtype": "bf16", "cpu": cpu, "keep": (w, X, csr, Y, variants)}
+            "config": cfg, "dtype": "bf16", "cpu": cpu, "compulsory": comp, "keep": (w, X, csr, Y, variants)}
 
 
 def wl_gcn_small(args):
@@ -355,8 +368,9 @@ def wl_gcn_small(args):
 
     cfg = {"workload": w.name, "graph": "erdos-renyi G(2000, 8000) symmetric + self-loops", "nodes": n,
            "edges": m, "F": F, "x_dtype": "f32", "norm": "both"}
+    comp = 4 * (n + 1) + 4 * m + 4 * n + 2 * n * F * 4   # + out-degrees
     return {"ops": ops, "dominant": "gcn", "kernel": "k_aggregate<float, 16, 4, 0, false>", "config": cfg,
-            "dtype": "f32", "cpu": cpu, "keep": (w, X, csr, plan, Y)}
+            "dtype": "f32", "cpu": cpu, "compulsory": comp, "cpu_1thread": True, "keep": (w, X, csr, plan, Y)}
 
 
 # ---------------------------------------------------------------------------
@@ -512,8 +526,10 @@ def wl_spmm_b16(args):
     cfg = {"workload": "spmm_b16_" + w.name, "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m,
            "F": F, "x_dtype": "bf16", "norm": "both", "plan": st,
            "note": "per_op_ms.csr is gnn_spmm on the same input"}
+    comp = (n * rb + n * 4 * F + 4 * (n + 1) + 4 * n + 8 * st["wsb_windows"] + 48 * st["wsb_blocks"]
+            + 4 * st["wsb_dense_tiles"] + 4 * (n + 1) + 4 * st["wsb_residual_edges"])
     return {"ops": ops, "dominant": "block16", "kernel": "k_spmm_b16<unsigned short>", "config": cfg,
-            "dtype": "bf16", "cpu": cpu, "keep": (w, csr, plan, X, Y)}
+            "dtype": "bf16", "cpu": cpu, "compulsory": comp, "keep": (w, csr, plan, X, Y)}
 
 
 # ---------------------------------------------------------------------------
@@ -874,10 +890,24 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
     }
+    if w.get("compulsory"):
+        # each input and output tensor once: the floor if every gather hit in cache
+        c = w["compulsory"]
+        out["hbm_compulsory"] = {"bytes": c, "gbps": c / (dom_ms * 1e-3) / 1e9,
+                                 "frac": c / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                 "amplification": (traffic / c) if traffic else None}
     if w.get("post"):
         out["results"] = w["post"](per_op_ms)
     if not args.no_cpu:
         out["cpu_baseline"] = w["cpu"](args.cpu_budget)
+        if w.get("cpu_1thread") and out["cpu_baseline"]:
+            import oracle
+            all_threads = oracle.num_threads()
+            oracle.set_threads(1)
+            one = w["cpu"](min(args.cpu_budget, 8.0))
+            oracle.set_threads(all_threads)
+            out["cpu_baseline"]["value_1thread"] = one["value"]
+            out["cpu_baseline"]["sample_1thread"] = one["sample"]
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -62,6 +62,8 @@ def _load():
                                           vp, vp, vp]
     lib.oracle_dot_aggr.argtypes = [i32, vp, vp, vp, i32, i64, i64, vp, vp, vp]
     lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -81,6 +83,11 @@ def _rc(rc, what):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the following oracle calls."""
+    _load().oracle_set_threads(int(n))
 
 
 def _rows(rows, n):

@@ -49,6 +49,11 @@ static double load_x(const void* X, int x_bf16, int64_t idx) {
 
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Threads for the following calls (n <= 0 leaves the setting unchanged). */
+void oracle_set_threads(int n) {
+  if (n > 0) omp_set_num_threads(n);
+}
+
 /* Degrees (paper: SpMM convolutions appendix, "normalisation as a
  * preprocessing step" — node degrees precomputed from the CSR). */
 int oracle_degrees(int32_t n_rows, int32_t n_cols, const int32_t* row_ptr, const int32_t* col_idx,
