@@ -56,14 +56,24 @@ SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (a comment edit leaves the
+    compiled kernels, and so a stored profile, unchanged)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_source_hash(workload: str) -> str:
-    """Hash of the sources behind a workload's dominant kernel: a stored
-    counter profile stays valid while none of them changes."""
+    """Hash of the code (comments left out) of the sources behind a workload's
+    dominant kernel: a stored counter profile stays valid while none of them
+    changes."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "graph_neural_network_amd", "csrc")
     for f in sorted(SOURCES[workload]):
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

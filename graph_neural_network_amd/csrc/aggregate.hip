@@ -384,7 +384,7 @@ __global__ __launch_bounds__(WG) void k_aggregate(AggParams p) {
 
   // Item workgroups come first (hardware order spreads them over the XCDs);
   // their count is padded to a multiple of 8 so that the light part starts on
-  // XCD 0 and can be remapped to contiguous row ranges per XCD.
+  // XCD 0 and can be remapped to per-XCD runs of consecutive row ranges.
   const int n_item_pad = (p.n_item_blocks + 7) & ~7;
   if ((int)blockIdx.x < n_item_pad) {
     // ---------------- one workgroup per work item ----------------
