@@ -315,7 +315,11 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
  * perm: device [n_rows] int32, perm[new] = old (required).
  * row_ptr_out [n_rows + 1] and col_idx_out [nnz] (device, both or neither):
  * if given, receive the relabelled CSR P A P^T with each row's columns
- * sorted ascending.  Synchronises `stream` (RCM runs level by level).
+ * sorted ascending.  Synchronises `stream` (RCM runs level by level) and
+ * returns when the outputs are complete.  Temporaries: one stream-ordered
+ * device allocation per call (RCM: about 64 bytes per CSR entry plus 40 per
+ * vertex; degree sort with relabelling: about 16 per entry), freed before
+ * return.
  * Errors: INVALID_VALUE (null, not square, one of the two outputs missing),
  * SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
 int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* row_ptr_out,
