@@ -36,7 +36,7 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
-           "gnn_spmm_block16", "gnn_dot_aggr")
+           "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16")
 
 
 class GnnError(RuntimeError):
@@ -91,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_gatv2_backward": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_gt_backward": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_dot_aggr": [P(_Csr), vp, i32, i64, ci, ci, vp, vp, vp],
+        "gnn_gt_backward_block16": [P(_Csr), vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -363,6 +364,23 @@ def gnn_gt_backward(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     _check(load_library().gnn_gt_backward(csr.ref, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), H, D, float(scale),
                                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                           _plan_h(plan), _stream(stream)), "gnn_gt_backward")
+    return dq, dk, dv
+
+
+def gnn_gt_backward_block16(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                            lse: torch.Tensor, dout: torch.Tensor, scale: float = 0.0, plan: Plan | None = None,
+                            stream=None):
+    """Block-sparse (bf16 matrix cores) Graph Transformer backward; bf16 q, k, v.
+    -> (dq, dk, dv), float32 [n, H, D]."""
+    H, D = q.shape[1], q.shape[2]
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the block-sparse backward takes bf16 q, k, v")
+    dq = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    _check(load_library().gnn_gt_backward_block16(csr.ref, _ptr(q), _ptr(k), _ptr(v), H, D, float(scale),
+                                                  _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                                  _plan_h(plan), _stream(stream)), "gnn_gt_backward_block16")
     return dq, dk, dv
 
 

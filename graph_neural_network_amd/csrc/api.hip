@@ -382,6 +382,28 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
   return launch_gt_backward(p, q, k, v, xtype, H, D, scale, out, lse, dout, dq, dk, dv, s);
 }
 
+int gnn_gt_backward_block16(const gnn_csr* csr, const void* q, const void* k, const void* v, int32_t H,
+                            int32_t D, float scale, const float* out, const float* lse, const float* dout,
+                            float* dq, float* dk, float* dv, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, true));
+  if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
+  if ((!q || !out || !lse || !dout || !dq || !k || !v || !dk || !dv) && csr->n_rows > 0)
+    return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
+  if (D != 32 && D != 64) return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs bf16 and D in {32, 64}");
+  if (H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "H*D*2 must be at most 2048 bytes");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
+       (uintptr_t)dk | (uintptr_t)dv) % 16)
+    return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");
+  if (csr->n_rows == 0) return GNN_OK;
+  const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
+  hipStream_t s = (hipStream_t)stream;
+  gnn_plan* p = nullptr;
+  bool tr = false;
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, true));
+  PlanGuard g{p, tr};
+  return launch_gt_backward_block16(p, q, k, v, H, D, sc, out, lse, dout, dq, dk, dv, s);
+}
+
 int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* row_ptr_out,
                 int32_t* col_idx_out, void* stream) {
   GNN_TRY(check_csr(csr, true));

@@ -124,6 +124,7 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
 int plan_build_wsb(gnn_plan* p, hipStream_t s);
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
 int plan_transpose(gnn_plan* p, hipStream_t s);
+int plan_transpose_wsb(gnn_plan* p, hipStream_t s);
 int check_plan(const gnn_plan* p, const gnn_csr* csr);
 
 // Launchers (host).  All validate nothing: the entry points did.
@@ -188,6 +189,9 @@ int launch_reduce_backward(gnn_plan* p, int op, const float* dY, int32_t F, int6
 int launch_gt_backward(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
                        int32_t D, float scale, const float* out, const float* lse, const float* dout,
                        float* dq, float* dk, float* dv, hipStream_t s);
+int launch_gt_backward_block16(gnn_plan* p, const void* q, const void* k, const void* v, int32_t H, int32_t D,
+                               float scale, const float* out, const float* lse, const float* dout, float* dq,
+                               float* dk, float* dv, hipStream_t s);
 int launch_gatv2_backward(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, const float* att,
                           int32_t H, int32_t D, float slope, const float* out, const float* lse,
                           const float* dout, float* dxl, float* dxr, float* datt, hipStream_t s);

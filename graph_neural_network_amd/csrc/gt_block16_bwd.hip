@@ -1,0 +1,541 @@
+// Graph Transformer backward on 16 x 16 block-sparse tiles with bf16 MFMA.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations": appendix D.2 (backward with cached statistics: only the
+// per-(row, head) logsumexp L_i of the forward is kept; alpha_ij =
+// exp(e_ij - L_i), Delta_i = <dO_i, O_i>, dS_ij = alpha_ij (<dO_i, v_j> -
+// Delta_i)) and appendix D.3 (the windowed block-sparse layout, here used for
+// training as well as inference).  With e_ij = scale <q_i, k_j>:
+//   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
+//   dv_j = sum_i alpha_ij dO_i.
+//
+// Two walks, no atomics, as in the CSR backward:
+//   destination walk (WSB tiles of A, 16 destination rows per window): per
+//     dense tile S^T = K_blk Q_win^T and dP^T = V_blk dO_win^T (16x16x32 bf16
+//     MFMA, both operands straight from memory), alpha and dS per entry, then
+//     dQ_win += dS K_blk (16x16x16 bf16 MFMA; dS is already in A-operand
+//     layout, K_blk is read transposed from LDS).  Writes Delta for the other
+//     walk.
+//   source walk (WSB tiles of A^T, 16 source columns per window): per dense
+//     tile S'^T = Q_blk K_win^T and dP'^T = dO_blk V_win^T, alpha and dS, then
+//     dK_win += dS^T Q_blk and dV_win += alpha^T dO_blk.
+// Entries of tiles below the density threshold (the residual CSR of each
+// layout) are added per row by the row's four lanes, each holding a quarter of
+// the head dimension, into row-layout accumulators merged in LDS at the end.
+// The matrix cores take dO, alpha and dS rounded to bf16 (q, k, v are bf16
+// already): the results carry bf16 rounding of those three, as the
+// block-sparse forward carries it for alpha.
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short s16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(short)))) short s16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int MAXT = 32;  // tiles of a window whose metadata is staged in LDS
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// dot of 8 bf16 pairs on v_dot2_f32_bf16
+__device__ __forceinline__ float dot8(const s16x8& a, const s16x8& b, float acc) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const s16x2 x = {a[2 * t], a[2 * t + 1]}, y = {b[2 * t], b[2 * t + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, y), acc,
+                                          false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct B16BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const float* out;
+  const float* lse;
+  const float* dout;
+  float* delta;  // [destinations, H]: written by the destination walk, read by the source walk
+  float* g0;     // destination walk: dq; source walk: dk
+  float* g1;     // source walk: dv
+  // block-sparse layout of the walked matrix (A, or A^T for the source walk)
+  const int32_t* win_ptr;
+  const int32_t* blk_col;
+  const unsigned long long* blk_bits;
+  const int32_t* tile_ptr;
+  const int32_t* tile_blk;
+  const int32_t* res_ptr;
+  const int32_t* res_col;
+  int32_t n_rows;  // rows of the walked matrix
+  int32_t H;
+  float scale;
+};
+
+// A row slice of 8 * KC elements of this lane (dims kc * 32 + 8g .. +7).
+template <int KC>
+__device__ __forceinline__ void load_bf(const uint16_t* row, int g, s16x8 (&x)[KC]) {
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) x[kc] = *reinterpret_cast<const s16x8*>(row + kc * 32 + 8 * g);
+}
+template <int KC>
+__device__ __forceinline__ void load_f32(const float* row, int g, float (&x)[KC][8]) {
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + kc * 32 + 8 * g);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + kc * 32 + 8 * g + 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[kc][t] = a[t];
+      x[kc][4 + t] = b[t];
+    }
+  }
+}
+template <int KC>
+__device__ __forceinline__ void to_bf(const float (&x)[KC][8], s16x8 (&y)[KC]) {
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) y[kc][t] = (short)f2bf(x[kc][t]);
+}
+
+// Window tile metadata (columns and bitmap words), staged in LDS when the
+// window has at most MAXT tiles.
+struct Tiles {
+  int t_beg, t_end, b_end;
+  bool staged;
+};
+
+template <int NWAVE>
+__device__ __forceinline__ Tiles stage_tiles(const B16BwdParams& p, int w, int32_t (*s_col)[16],
+                                             unsigned long long (*s_bits)[4]) {
+  Tiles T;
+  T.t_beg = p.tile_ptr[w];
+  T.t_end = p.tile_ptr[w + 1];
+  T.b_end = p.win_ptr[w + 1];
+  const int nt = T.t_end - T.t_beg;
+  T.staged = nt <= MAXT;
+  if (T.staged) {
+    for (int i = threadIdx.x; i < nt * 16; i += NWAVE * 64) {
+      const int t = i >> 4, c = i & 15;
+      const int blk = p.tile_blk[T.t_beg + t] + (c >> 3);
+      s_col[t][c] = ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+    }
+    for (int i = threadIdx.x; i < nt * 4; i += NWAVE * 64) {
+      const int t = i >> 2, q = i & 3;
+      const int blk = p.tile_blk[T.t_beg + t] + (q >> 1);
+      s_bits[t][q] = ((q >> 1) == 1 && blk >= T.b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (q & 1)];
+    }
+  }
+  __syncthreads();
+  return T;
+}
+
+// column c (0..15) of tile t
+__device__ __forceinline__ int tile_col(const B16BwdParams& p, const Tiles& T, const int32_t (*s_col)[16], int t,
+                                        int c) {
+  if (T.staged) return s_col[t - T.t_beg][c];
+  const int blk = p.tile_blk[t] + (c >> 3);
+  return ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+}
+// bitmap word holding window row r, tile columns 4g .. 4g + 3
+__device__ __forceinline__ unsigned long long tile_word(const B16BwdParams& p, const Tiles& T,
+                                                        const unsigned long long (*s_bits)[4], int t, int r,
+                                                        int g) {
+  const int ub = g >> 1;
+  if (T.staged) return s_bits[t - T.t_beg][ub * 2 + (r >> 3)];
+  const int blk = p.tile_blk[t] + ub;
+  return (ub == 1 && blk >= T.b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+}
+
+// Stage a 16 x D D-layout accumulator set (lane l: rows 4g + i, dims mb*16 + r)
+// plus a row-layout one (lane l: row r, dims kc*32 + 8g + t) in LDS, then store
+// the window's rows of head h, 16 contiguous bytes per lane.
+template <int D>
+__device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16], const float (&res)[D / 32][8],
+                                           float* dst, int64_t ldr, int h, int w, int n_rows, int lane) {
+  constexpr int MB = D / 16, KC = D / 32, LDO = D + 4;
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo[(4 * g + i) * LDO + mb * 16 + r] = acc[mb][i];
+  wave_sync();
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) lo[r * LDO + kc * 32 + 8 * g + t] += res[kc][t];
+  wave_sync();
+  constexpr int LPRW = D / 4;     // lanes per row slice
+  constexpr int RPI = 64 / LPRW;  // rows per store instruction
+  const int r0 = lane / LPRW, dd = (lane % LPRW) * 4;
+  const float* lsrc = lo + r0 * LDO + dd;
+  float* odst = dst + (int64_t)(w * 16 + r0) * ldr + h * D + dd;
+  const int rows_left = n_rows - (w * 16 + r0);
+#pragma unroll
+  for (int q = 0; q < 16 / RPI; ++q) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(lsrc + q * RPI * LDO);
+    if (q * RPI < rows_left) *reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr) = t;
+  }
+  wave_sync();
+}
+
+// ---------------------------------------------------------------------------
+// destination walk: dq (and Delta)
+// ---------------------------------------------------------------------------
+template <int D, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
+  constexpr int KC = D / 32, MB = D / 16;
+  constexpr int LDK = D + 8;  // padded LDS row (bf16)
+  constexpr int LDO = D + 4;  // padded LDS row (floats)
+  __shared__ uint16_t s_k[NWAVE][16 * LDK];
+  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
+  __shared__ int32_t s_col[MAXT][16];
+  __shared__ unsigned long long s_bits[MAXT][4];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const int row = w * 16 + r;
+  const bool row_ok = row < p.n_rows;
+  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
+  const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
+  const int64_t ldr = (int64_t)p.H * D;
+  const float sc2 = p.scale * kLog2e;
+  uint16_t* lk = s_k[wave];
+  float* lo = s_o[wave];
+
+  for (int h = wave; h < p.H; h += NWAVE) {
+    // this lane's slices of the row: q, dO (rounded to bf16 for the matrix
+    // cores) in B-operand layout; Delta = <dO, O> over the head, lse
+    s16x8 qb[KC], gb[KC];
+    float L2 = 0.0f, dl = 0.0f;
+    if (row_ok) {
+      const int64_t ro = (int64_t)row * ldr + h * D;
+      load_bf<KC>(p.q + ro, g, qb);
+      float go[KC][8], o[KC][8];
+      load_f32<KC>(p.dout + ro, g, go);
+      load_f32<KC>(p.out + ro, g, o);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dl = fmaf(go[kc][t], o[kc][t], dl);
+      to_bf<KC>(go, gb);
+      L2 = p.lse[(int64_t)row * p.H + h] * kLog2e;
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) qb[kc] = gb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    dl += __shfl_xor(dl, 16, 64);
+    dl += __shfl_xor(dl, 32, 64);
+    if (row_ok && g == 0) p.delta[(int64_t)row * p.H + h] = dl;
+
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float res[KC][8];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) res[kc][t] = 0.0f;
+
+    auto load_kv = [&](int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
+      const int64_t co = (int64_t)tile_col(p, T, s_col, t, r) * ldr + h * D;
+      load_bf<KC>(p.k + co, g, ka);
+      load_bf<KC>(p.v + co, g, va);
+    };
+    auto process = [&](int t, const s16x8 (&ka)[KC], const s16x8 (&va)[KC]) {
+      // lane holds S and dP of row r, tile columns 4g .. 4g + 3
+      f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, dp = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[kc]),
+                                                     __builtin_bit_cast(bf16x8, qb[kc]), st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[kc]),
+                                                     __builtin_bit_cast(bf16x8, gb[kc]), dp, 0, 0, 0);
+      }
+      const unsigned long long word = tile_word(p, T, s_bits, t, r, g);
+      const int base = (r & 7) * 8 + 4 * (g & 1);
+      s16x4 dsb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = ((word >> (base + i)) & 1ull) ? ex2(st[i] * sc2 - L2) : 0.0f;
+        dsb[i] = (short)f2bf(a * (dp[i] - dl) * p.scale);
+      }
+      // K block to LDS as [column][dim], read transposed as the B operand
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) *reinterpret_cast<s16x8*>(lk + r * LDK + kc * 32 + 8 * g) = ka[kc];
+      wave_sync();
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s16x4 kt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kt[i] = (short)lk[(4 * g + i) * LDK + mb * 16 + r];
+        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsb, kt, acc[mb], 0, 0, 0);
+      }
+      wave_sync();
+    };
+
+    // two-deep pipeline over the window's dense tiles
+    s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
+    if (T.t_beg < T.t_end) load_kv(T.t_beg, kA, vA);
+    for (int t = T.t_beg; t < T.t_end; t += 2) {
+      if (t + 1 < T.t_end) load_kv(t + 1, kB, vB);
+      process(t, kA, vA);
+      if (t + 1 < T.t_end) {
+        if (t + 2 < T.t_end) load_kv(t + 2, kA, vA);
+        process(t + 1, kB, vB);
+      }
+    }
+
+    // residual entries of this row: the row's four lanes each hold a quarter
+    // of the head dimension
+    for (int e = res_b; e < res_e; ++e) {
+      const int64_t co = (int64_t)p.res_col[e] * ldr + h * D;
+      s16x8 kv[KC], vv[KC];
+      load_bf<KC>(p.k + co, g, kv);
+      load_bf<KC>(p.v + co, g, vv);
+      float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s = dot8(qb[kc], kv[kc], s);
+        dpv = dot8(gb[kc], vv[kc], dpv);
+      }
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      dpv += __shfl_xor(dpv, 16, 64);
+      dpv += __shfl_xor(dpv, 32, 64);
+      const float ds = ex2(s * sc2 - L2) * (dpv - dl) * p.scale;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) res[kc][t] = fmaf(ds, bf((uint16_t)kv[kc][t]), res[kc][t]);
+    }
+
+    store_rows<D>(lo, acc, res, p.g0, ldr, h, w, p.n_rows, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// source walk over A^T: dk, dv
+// ---------------------------------------------------------------------------
+template <int D, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_src(B16BwdParams p) {
+  constexpr int KC = D / 32, MB = D / 16;
+  constexpr int LDK = D + 8;
+  constexpr int LDO = D + 4;
+  __shared__ uint16_t s_q[NWAVE][16 * LDK];   // the tile's q rows, [destination][dim]
+  __shared__ uint16_t s_g[NWAVE][16 * LDK];   // the tile's dO rows in bf16
+  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
+  __shared__ int32_t s_col[MAXT][16];
+  __shared__ unsigned long long s_bits[MAXT][4];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const int row = w * 16 + r;  // a source node (row of A^T)
+  const bool row_ok = row < p.n_rows;
+  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
+  const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
+  const int64_t ldr = (int64_t)p.H * D;
+  const float sc2 = p.scale * kLog2e;
+  uint16_t* lq = s_q[wave];
+  uint16_t* lg = s_g[wave];
+  float* lo = s_o[wave];
+
+  for (int h = wave; h < p.H; h += NWAVE) {
+    // this lane's slices of its source row: k and v in B-operand layout
+    s16x8 kb[KC], vb[KC];
+    if (row_ok) {
+      const int64_t ro = (int64_t)row * ldr + h * D;
+      load_bf<KC>(p.k + ro, g, kb);
+      load_bf<KC>(p.v + ro, g, vb);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) kb[kc] = vb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    f32x4 acck[MB], accv[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acck[mb] = accv[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float resk[KC][8], resv[KC][8];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) resk[kc][t] = resv[kc][t] = 0.0f;
+
+    // one tile's destination rows for this lane (tile column r): q, dO, L, Delta
+    struct Dst {
+      s16x8 q[KC];
+      float go[KC][8];
+      float L2, dl;
+    };
+    auto load_dst = [&](int t, Dst& d) {
+      const int i = tile_col(p, T, s_col, t, r);
+      const int64_t io = (int64_t)i * ldr + h * D;
+      load_bf<KC>(p.q + io, g, d.q);
+      load_f32<KC>(p.dout + io, g, d.go);
+      d.L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
+      d.dl = p.delta[(int64_t)i * p.H + h];
+    };
+    auto process = [&](int t, const Dst& d) {
+      s16x8 gb[KC];
+      to_bf<KC>(d.go, gb);
+      // lane holds S and dP of source r with destinations 4g .. 4g + 3 of the tile
+      f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, dp = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d.q[kc]),
+                                                     __builtin_bit_cast(bf16x8, kb[kc]), st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, gb[kc]),
+                                                     __builtin_bit_cast(bf16x8, vb[kc]), dp, 0, 0, 0);
+      }
+      const unsigned long long word = tile_word(p, T, s_bits, t, r, g);
+      const int base = (r & 7) * 8 + 4 * (g & 1);
+      s16x4 dsb, ab;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float Lc = __shfl(d.L2, 4 * g + i, 64);  // lane c (0..15) holds destination c
+        const float Dc = __shfl(d.dl, 4 * g + i, 64);
+        const float a = ((word >> (base + i)) & 1ull) ? ex2(st[i] * sc2 - Lc) : 0.0f;
+        ab[i] = (short)f2bf(a);
+        dsb[i] = (short)f2bf(a * (dp[i] - Dc) * p.scale);
+      }
+      // the tile's q and dO rows to LDS as [destination][dim], read transposed
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        *reinterpret_cast<s16x8*>(lq + r * LDK + kc * 32 + 8 * g) = d.q[kc];
+        *reinterpret_cast<s16x8*>(lg + r * LDK + kc * 32 + 8 * g) = gb[kc];
+      }
+      wave_sync();
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        s16x4 qt, gt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          qt[i] = (short)lq[(4 * g + i) * LDK + mb * 16 + r];
+          gt[i] = (short)lg[(4 * g + i) * LDK + mb * 16 + r];
+        }
+        acck[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsb, qt, acck[mb], 0, 0, 0);
+        accv[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, gt, accv[mb], 0, 0, 0);
+      }
+      wave_sync();
+    };
+
+    Dst dA, dB;
+    if (T.t_beg < T.t_end) load_dst(T.t_beg, dA);
+    for (int t = T.t_beg; t < T.t_end; t += 2) {
+      if (t + 1 < T.t_end) load_dst(t + 1, dB);
+      process(t, dA);
+      if (t + 1 < T.t_end) {
+        if (t + 2 < T.t_end) load_dst(t + 2, dA);
+        process(t + 1, dB);
+      }
+    }
+
+    // residual entries of this source row (destinations i)
+    for (int e = res_b; e < res_e; ++e) {
+      const int i = p.res_col[e];
+      const int64_t io = (int64_t)i * ldr + h * D;
+      s16x8 qv[KC], gv[KC];
+      float go[KC][8];
+      load_bf<KC>(p.q + io, g, qv);
+      load_f32<KC>(p.dout + io, g, go);
+      to_bf<KC>(go, gv);
+      const float L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
+      const float dl = p.delta[(int64_t)i * p.H + h];
+      float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s = dot8(qv[kc], kb[kc], s);
+        dpv = dot8(gv[kc], vb[kc], dpv);
+      }
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      dpv += __shfl_xor(dpv, 16, 64);
+      dpv += __shfl_xor(dpv, 32, 64);
+      const float a = ex2(s * sc2 - L2);
+      const float ds = a * (dpv - dl) * p.scale;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          resk[kc][t] = fmaf(ds, bf((uint16_t)qv[kc][t]), resk[kc][t]);
+          resv[kc][t] = fmaf(a, bf((uint16_t)gv[kc][t]), resv[kc][t]);
+        }
+    }
+
+    store_rows<D>(lo, acck, resk, p.g0, ldr, h, w, p.n_rows, lane);
+    store_rows<D>(lo, accv, resv, p.g1, ldr, h, w, p.n_rows, lane);
+  }
+}
+
+void fill_layout(B16BwdParams& p, const gnn_plan* pl) {
+  p.win_ptr = pl->wsb.win_ptr;
+  p.blk_col = pl->wsb.blk_col;
+  p.blk_bits = (const unsigned long long*)pl->wsb.blk_bits;
+  p.tile_ptr = pl->wsb.tile_ptr;
+  p.tile_blk = pl->wsb.tile_blk;
+  p.res_ptr = pl->wsb.res_ptr;
+  p.res_col = pl->wsb.res_col;
+  p.n_rows = pl->n_rows;
+}
+
+}  // namespace
+
+int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const void* v, int32_t H, int32_t D,
+                               float scale, const float* out, const float* lse, const float* dout, float* dq,
+                               float* dk, float* dv, hipStream_t s) {
+  if (D != 32 && D != 64) return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs D in {32, 64}");
+  GNN_TRY(plan_transpose(pl, s));
+  GNN_TRY(plan_transpose_wsb(pl, s));
+  GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
+  B16BwdParams p{};
+  p.q = (const uint16_t*)q;
+  p.k = (const uint16_t*)k;
+  p.v = (const uint16_t*)v;
+  p.out = out;
+  p.lse = lse;
+  p.dout = dout;
+  p.delta = pl->delta;
+  p.H = H;
+  p.scale = scale;
+  constexpr int NW = 2;  // waves per window, each looping over half of the heads
+  fill_layout(p, pl);
+  p.g0 = dq;
+  if (pl->wsb.n_windows > 0) {
+    const dim3 grid((unsigned)pl->wsb.n_windows);
+    if (D == 32) hipLaunchKernelGGL((k_gt_b16_bwd_dst<32, NW>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((k_gt_b16_bwd_dst<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    GNN_LAUNCH_CHECK("block-sparse GT backward (destinations)");
+  }
+  const gnn_plan* tp = pl->tplan;
+  fill_layout(p, tp);
+  p.g0 = dk;
+  p.g1 = dv;
+  if (tp->wsb.n_windows > 0) {
+    const dim3 grid((unsigned)tp->wsb.n_windows);
+    if (D == 32) hipLaunchKernelGGL((k_gt_b16_bwd_src<32, NW>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((k_gt_b16_bwd_src<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    GNN_LAUNCH_CHECK("block-sparse GT backward (sources)");
+  }
+  return GNN_OK;
+}
+
+}  // namespace gnn

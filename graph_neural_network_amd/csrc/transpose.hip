@@ -138,6 +138,15 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   return GNN_OK;
 }
 
+// The block-sparse layout of A^T (windows of 16 source columns), built on the
+// first block-sparse backward call with the plan's density threshold.
+int plan_transpose_wsb(gnn_plan* p, hipStream_t s) {
+  GNN_TRY(plan_transpose(p, s));
+  if (p->tplan->has_wsb) return GNN_OK;
+  p->tplan->opts.wsb_min_nnz = p->opts.wsb_min_nnz;
+  return plan_build_wsb(p->tplan, s);
+}
+
 int launch_spmm_backward(gnn_plan* p, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
                          gnn_norm norm, const float* edge_val, hipStream_t s) {
   GNN_TRY(plan_transpose(p, s));

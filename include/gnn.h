@@ -13,7 +13,9 @@
  *   gnn_gt_fused     Graph Transformer attention, CSR or 16x16 block-sparse
  *                                                              (appendix D.2 and D.3)
  *   gnn_*_backward   gradients of SpMM, the reductions and both attention layers
- *                                                              (appendix D.1 and D.2, backward passes)
+ *                                                              (appendix D.1 and D.2, backward passes;
+ *                                                               gnn_gt_backward_block16 on the tiles
+ *                                                               of appendix D.3)
  *   gnn_reorder      degree-sort or RCM vertex reordering      (section 2.4; RCM as in
  *                    Tang et al., "A High-Throughput Solver for Marginalized Graph
  *                    Kernels on GPU", graph reordering section)
@@ -306,6 +308,22 @@ int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_d
 int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype, int32_t H,
                     int32_t D, float scale, const float* out, const float* lse, const float* dout, float* dq,
                     float* dk, float* dv, gnn_plan* plan, void* stream);
+
+/* The same gradients as gnn_gt_backward computed on 16x16 block-sparse tiles
+ * with bf16 matrix cores (appendix D.2 backward with cached statistics,
+ * appendix D.3 block-sparse layout): a destination walk over the plan's
+ * tiles of A gives dq (and Delta), a source walk over tiles of A^T gives dk
+ * and dv; entries of sparse tiles run through the layouts' residual CSRs.
+ * dO, alpha and dS are rounded to bf16 for the matrix cores, as alpha is in
+ * the block-sparse forward: results are within the attention tolerance of
+ * the exact gradients, not to fp32 rounding.  Square CSR, bf16 q, k, v only,
+ * D in {32, 64}, H*D*2 <= 2048; other arguments as in gnn_gt_backward.  The
+ * plan must carry WSB tiles (NULL: a transient one is built); the tiles of
+ * A^T are built on its first block-sparse backward call.
+ * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+int gnn_gt_backward_block16(const gnn_csr* csr, const void* q, const void* k, const void* v, int32_t H,
+                            int32_t D, float scale, const float* out, const float* lse, const float* dout,
+                            float* dq, float* dk, float* dv, gnn_plan* plan, void* stream);
 
 /* Vertex reordering of a square CSR (n_rows == n_cols).
  * DEGREE: perm sorts vertices by descending deg_in, ties by ascending id

@@ -97,6 +97,10 @@ INV, UNS, OVF = 1, 2, 5
     ("dot vec16 ldx%4", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(16), 4, 6, 1, 1, P(16), None, None), INV),
     ("dot vec16 misaligned", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(20), 4, 4, 0, 1, P(16), None, None), INV),
     ("dot edge values", lambda: call("gnn_dot_aggr", ctypes.byref(gnn._Csr(4, 4, 4, 0x1000, 0x2000, 0x3000)), P(16), 4, 4, 0, 0, P(16), None, None), INV),
+    ("b16 bwd non-square", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), INV),
+    ("b16 bwd D=128", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2, 128, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("b16 bwd null dk", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), None, P(16), None, None), INV),
+    ("b16 bwd misaligned", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(24), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
                                    ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),

@@ -17,7 +17,7 @@ import torch
 import gen
 import graph_neural_network_amd as gnn
 import oracle
-from gpu_util import dev_bf16, dev_csr, host, scaled_err
+from gpu_util import dev, dev_bf16, dev_csr, host, scaled_err
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -234,3 +234,67 @@ def test_spmm_block16_cluster512k_full():
     Yc = gnn.gnn_spmm(csr, Xd, "both", plan=plan)
     mag_all = gnn.gnn_spmm(csr, Xd.abs(), "both", plan=plan)
     assert bool(((Y - Yc).abs() <= 2 * SPMM_TOL * mag_all).all())
+
+
+# ---------------------------------------------------------------------------
+# block-sparse Graph Transformer backward
+# ---------------------------------------------------------------------------
+
+B16_BWD_TOL = 2e-2   # the attention bar: dO, alpha and dS pass through bf16 on the matrix cores
+
+
+def _b16_bwd_case(rp, ci, H, D, tau, seed):
+    from test_gpu_backward import bwd_err
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, build_wsb=True, wsb_min_nnz=tau)
+    q, k, v = (gen.gauss_bf16(seed + i, (n, H, D)) for i in range(3))
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = gnn.gnn_gt_fused(csr, dq_, dk_, dv_, mode="csr", plan=plan)
+    dO = gen.gauss_f32(seed + 3, (n, H, D))
+    dq, dk, dv = gnn.gnn_gt_backward_block16(csr, dq_, dk_, dv_, out, lse, dev(dO), plan=plan)
+    rq, rk, rv, mq, mk, mv = oracle.gt_backward(rp, ci, q, k, v, dO)
+    errs = tuple(bwd_err(host(g), r, m) for g, r, m in ((dq, rq, mq), (dk, rk, mk), (dv, rv, mv)))
+    again = gnn.gnn_gt_backward_block16(csr, dq_, dk_, dv_, out, lse, dev(dO), plan=plan)
+    same = all(torch.equal(a, b) for a, b in zip((dq, dk, dv), again))
+    return errs, same, gnn.gnn_plan_stats(plan)
+
+
+@pytest.mark.parametrize("H,D", [(8, 64), (2, 32), (1, 64), (3, 32)])
+@pytest.mark.parametrize("tau", [1, 8, 10**6])
+def test_gt_block16_backward_cluster(H, D, tau):
+    rp, ci = gen.cluster(0x5EED0360, 64 * 25, 64, 0.4, 0.02, self_loops=True)
+    errs, same, st = _b16_bwd_case(rp, ci, H, D, tau, 0x6100)
+    if tau == 10**6:
+        assert st["wsb_dense_tiles"] == 0
+    assert max(errs) <= B16_BWD_TOL, errs
+    assert same, "not deterministic"
+
+
+def test_gt_block16_backward_rmat_partial_windows():
+    """R-MAT with empty rows, hub rows and a last window of 3 rows: most
+    entries go through the residual CSRs of A and A^T."""
+    rp, ci = gen.rmat(0x5EED0361, 3 * 1000 + 3, 40000, self_loops=True)
+    errs, same, _ = _b16_bwd_case(rp, ci, 4, 32, 8, 0x6200)
+    assert max(errs) <= B16_BWD_TOL, errs
+    assert same
+
+
+@pytest.mark.slow
+def test_gt_block16_backward_cluster512k_full():
+    """The benchmark's backward on the 512,000-node cluster graph (H = 8, D = 64):
+    every output against the oracle."""
+    from test_gpu_backward import bwd_err
+    w = gen.gt_cluster()
+    rp, ci = w.row_ptr, w.col_idx
+    n, H, D = w.n, w.params["H"], w.params["D"]
+    csr = dev_csr(rp, ci)
+    plan = gnn.gnn_plan_create(csr, build_wsb=True)
+    q, k, v = (w.arrays[x] for x in ("q", "k", "v"))
+    dq_, dk_, dv_ = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    out, lse = gnn.gnn_gt_fused(csr, dq_, dk_, dv_, mode="block16", plan=plan)
+    dO = gen.gauss_f32(0xFEA70604, (n, H, D))
+    dq, dk, dv = gnn.gnn_gt_backward_block16(csr, dq_, dk_, dv_, out, lse, dev(dO), plan=plan)
+    rq, rk, rv, mq, mk, mv = oracle.gt_backward(rp, ci, q, k, v, dO)
+    for name, g, r, m in (("dq", dq, rq, mq), ("dk", dk, rk, mk), ("dv", dv, rv, mv)):
+        assert bwd_err(host(g), r, m) <= B16_BWD_TOL, name
