@@ -52,6 +52,7 @@ SOURCES = {
     "gatv2_bwd_cfg3": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
     "gt_bwd_cfg4": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
     "spmm_b16_cfg4": _COMMON + ("spmm_block16.hip", "wsb.hip", "sort.hip"),
+    "gt_bwd_b16_cfg4": _COMMON + ("gt_block16_bwd.hip", "wsb.hip", "sort.hip", "transpose.hip"),
     "dotaggr_cfg2": _COMMON + ("dot_aggr.hip",),
 }
 
@@ -658,9 +659,11 @@ def wl_gatv2_bwd(args):
             "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse, dO)}
 
 
-def wl_gt_bwd(args):
+def wl_gt_bwd(args, mode="csr"):
     """Graph Transformer backward on the cluster graph (512,000 nodes, H = 8, D = 64 bf16):
-    destination walk (dq) and source walk over the transpose (dk, dv)."""
+    destination walk (dq) and source walk over the transpose (dk, dv); CSR edges, or 16x16
+    block-sparse tiles with bf16 matrix cores (mode "block16")."""
+    import numpy as np
     import torch
 
     import gen
@@ -670,14 +673,39 @@ def wl_gt_bwd(args):
     n, m = w.n, w.nnz
     H, D = w.params["H"], w.params["D"]
     csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
-    plan = gnn.gnn_plan_create(csr)
+    plan = gnn.gnn_plan_create(csr, build_wsb=(mode == "block16"))
     q, k, v = (_to_bf16(w.arrays[x]) for x in ("q", "k", "v"))
-    out, lse = gnn.gnn_gt_fused(csr, q, k, v, plan=plan)
+    out, lse = gnn.gnn_gt_fused(csr, q, k, v, 0.0, mode, plan=plan)
     dO = torch.randn((n, H, D), device="cuda")
     hd, rb = H * D, H * D * 2
-    b = (m * (4 + 2 * rb) + n * (rb + 12 * hd + 8 * H)                # destination walk
-         + m * (4 + rb + 4 * hd + 8 * H) + n * (4 + 2 * rb + 8 * hd))  # source walk
-    ops = [Op("gt_bwd", lambda: gnn.gnn_gt_backward(csr, q, k, v, out, lse, dO, plan=plan), m, b)]
+    extra = {}
+    if mode == "csr":
+        b = (m * (4 + 2 * rb) + n * (rb + 12 * hd + 8 * H)                # destination walk
+             + m * (4 + rb + 4 * hd + 8 * H) + n * (4 + 2 * rb + 8 * hd))  # source walk
+        fn = lambda: gnn.gnn_gt_backward(csr, q, k, v, out, lse, dO, plan=plan)
+    else:
+        # tile counts of A^T from a plan over the transposed CSR (preprocessing, not timed)
+        order = np.argsort(w.col_idx, kind="stable")
+        rows = np.repeat(np.arange(n, dtype=np.int32), np.diff(w.row_ptr))
+        t_rp = np.zeros(n + 1, np.int32)
+        np.cumsum(np.bincount(w.col_idx, minlength=n), out=t_rp[1:])
+        t_csr = gnn.Csr(torch.from_numpy(t_rp).cuda(), torch.from_numpy(rows[order]).cuda())
+        t_plan = gnn.gnn_plan_create(t_csr, build_wsb=True)
+        sa, st = gnn.gnn_plan_stats(plan), gnn.gnn_plan_stats(t_plan)
+        gnn.gnn_plan_destroy(t_plan)
+        del t_csr
+        # destination walk: per dense tile 16 K + 16 V rows and two 48-byte blocks, per residual
+        # edge a column and a K and a V row, per row q, dO, O, lse in and dq, dO (bf16), Delta out;
+        # source walk: per dense tile 16 q + 16 dO (bf16) rows, 16 (lse, Delta) and the blocks,
+        # per residual edge the same per destination, per row k, v in and dk, dv out
+        b = (sa["wsb_dense_tiles"] * (32 * rb + 96) + sa["wsb_residual_edges"] * (4 + 2 * rb)
+             + n * (rb + 12 * hd + 4 * H + 4 * hd + 2 * hd + 4 * H)
+             + st["wsb_dense_tiles"] * (32 * rb + 16 * 8 * H + 96)
+             + st["wsb_residual_edges"] * (4 + 2 * rb + 8 * H) + n * (2 * rb + 8 * hd))
+        extra = {"tiles_A": sa["wsb_dense_tiles"], "residual_A": sa["wsb_residual_edges"],
+                 "tiles_AT": st["wsb_dense_tiles"], "residual_AT": st["wsb_residual_edges"]}
+        fn = lambda: gnn.gnn_gt_backward_block16(csr, q, k, v, out, lse, dO, plan=plan)
+    ops = [Op("gt_bwd" if mode == "csr" else "gt_bwd_b16", fn, m, b)]
 
     def cpu(budget_s):
         import oracle
@@ -687,11 +715,16 @@ def wl_gt_bwd(args):
                                                       s.arrays["v"], do), s.nnz,
                            "Graph Transformer backward, fp64", f"cluster graph {s.n} nodes / {s.nnz} edges, same H, D")
 
-    cfg = {"workload": "gt_bwd_" + w.name, "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m,
-           "heads": H, "head_dim": D, "x_dtype": "bf16"}
-    return {"ops": ops, "dominant": "gt_bwd", "kernel": "k_att_bwd (both walks)",
-            "traffic_kernels": ["k_att_bwd", "k_bwd_combine"], "config": cfg, "dtype": "bf16", "cpu": cpu,
-            "keep": (w, csr, plan, q, k, v, out, lse, dO)}
+    cfg = {"workload": ("gt_bwd_" if mode == "csr" else "gt_bwd_b16_") + w.name,
+           "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m, "heads": H, "head_dim": D,
+           "x_dtype": "bf16", "mode": mode, **extra}
+    if mode == "csr":
+        return {"ops": ops, "dominant": "gt_bwd", "kernel": "k_att_bwd (both walks)",
+                "traffic_kernels": ["k_att_bwd", "k_bwd_combine"], "config": cfg, "dtype": "bf16", "cpu": cpu,
+                "keep": (w, csr, plan, q, k, v, out, lse, dO)}
+    return {"ops": ops, "dominant": "gt_bwd_b16", "kernel": "k_gt_b16_bwd (both walks)",
+            "traffic_kernels": ["k_gt_b16_bwd_dst", "k_gt_b16_bwd_src"], "config": cfg, "dtype": "bf16",
+            "cpu": cpu, "keep": (w, csr, plan, q, k, v, out, lse, dO)}
 
 
 DOT_DIMS = (32, 64, 128, 256, 512)
@@ -776,6 +809,7 @@ WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, 
              "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
              "reorder_cfg5": wl_reorder, "spmm_bwd_cfg5": wl_spmm_bwd, "reduce_bwd_cfg2": wl_reduce_bwd,
              "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd, "spmm_b16_cfg4": wl_spmm_b16,
+             "gt_bwd_b16_cfg4": lambda a: wl_gt_bwd(a, "block16"),
              "dotaggr_cfg2": wl_dot_aggr}
 
 

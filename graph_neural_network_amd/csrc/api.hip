@@ -135,6 +135,7 @@ int gnn_plan_destroy(gnn_plan* p) {
   for (int k = 0; k < p->n_allocs; ++k) hipFree(p->allocs[k]);
   if (p->ws) hipFree(p->ws);
   if (p->delta) hipFree(p->delta);
+  if (p->dob) hipFree(p->dob);
   delete p;
   return rc;
 }

@@ -101,6 +101,8 @@ struct gnn_plan {
   float* t_val = nullptr;        // [nnz] edge values in transposed order (per call)
   float* delta = nullptr;        // attention backward: [n_rows, H] <O, dO> per (row, head)
   size_t delta_cap = 0;
+  uint16_t* dob = nullptr;       // block-sparse attention backward: dO in bf16, [n_rows, H, D]
+  size_t dob_cap = 0;
 
   // workspace (partials / packed words); grows on demand
   void* ws = nullptr;

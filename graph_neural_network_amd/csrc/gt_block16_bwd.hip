@@ -14,14 +14,17 @@
 //     dense tile S^T = K_blk Q_win^T and dP^T = V_blk dO_win^T (16x16x32 bf16
 //     MFMA, both operands straight from memory), alpha and dS per entry, then
 //     dQ_win += dS K_blk (16x16x16 bf16 MFMA; dS is already in A-operand
-//     layout, K_blk is read transposed from LDS).  Writes Delta for the other
-//     walk.
+//     layout, K_blk is read transposed from LDS).  Writes Delta and dO in
+//     bf16 for the other walk, which gathers them per tile.
 //   source walk (WSB tiles of A^T, 16 source columns per window): per dense
 //     tile S'^T = Q_blk K_win^T and dP'^T = dO_blk V_win^T, alpha and dS, then
 //     dK_win += dS^T Q_blk and dV_win += alpha^T dO_blk.
+// The transposed B operands come from LDS through the gfx950 transpose read
+// (ds_read_b64_tr_b16), one instruction per 16 x 16 block.
 // Entries of tiles below the density threshold (the residual CSR of each
 // layout) are added per row by the row's four lanes, each holding a quarter of
-// the head dimension, into row-layout accumulators merged in LDS at the end.
+// the head dimension, into row-layout partial sums placed in LDS before the
+// tile loop and merged with the tile results at the end.
 // The matrix cores take dO, alpha and dS rounded to bf16 (q, k, v are bf16
 // already): the results carry bf16 rounding of those three, as the
 // block-sparse forward carries it for alpha.
@@ -39,6 +42,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int MAXT = 32;  // tiles of a window whose metadata is staged in LDS
+template <int D>
+constexpr int ldk() { return D + 8; }  // padded LDS row (bf16)
+template <int D>
+constexpr int ldo() { return D + 4; }  // padded LDS row (floats)
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -60,6 +67,20 @@ __device__ __forceinline__ float dot8(const s16x8& a, const s16x8& b, float acc)
   return acc;
 }
 
+// The B operand of a 16x16x16 bf16 MFMA (lane 16g + r: rows 4g .. 4g + 3 of
+// column r) from a 16 x 16 block stored row-major in LDS (row stride ld), by
+// the LDS transpose read: within each 16 lanes, lane 16g + 4i + a names row
+// 4g + i, columns 4a .. 4a + 3, and lane 16g + 4a + j receives element j of
+// the four rows named by lanes 16g + a, 16g + 4 + a, ...  Needs every lane
+// active.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_b_operand(const uint16_t* blk, int ld, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* a = blk + (4 * g + (r >> 2)) * ld + 4 * (r & 3);
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)a);
+  return __builtin_bit_cast(s16x4, v);
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -73,7 +94,8 @@ struct B16BwdParams {
   const float* out;
   const float* lse;
   const float* dout;
-  float* delta;  // [destinations, H]: written by the destination walk, read by the source walk
+  float* delta;   // [destinations, H]: written by the destination walk, read by the source walk
+  uint16_t* dob;  // [destinations, H, D] dO in bf16: the same hand-over
   float* g0;     // destination walk: dq; source walk: dk
   float* g1;     // source walk: dv
   // block-sparse layout of the walked matrix (A, or A^T for the source walk)
@@ -148,40 +170,59 @@ __device__ __forceinline__ Tiles stage_tiles(const B16BwdParams& p, int w, int32
   return T;
 }
 
-// column c (0..15) of tile t
+// Column c (0..15) of tile t.  ST (staged) is a template parameter: with a
+// run-time choice the compiler merges the LDS and global reads into one flat
+// load, whose wait then also waits for every prefetch in flight.
+template <bool ST>
 __device__ __forceinline__ int tile_col(const B16BwdParams& p, const Tiles& T, const int32_t (*s_col)[16], int t,
                                         int c) {
-  if (T.staged) return s_col[t - T.t_beg][c];
-  const int blk = p.tile_blk[t] + (c >> 3);
-  return ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+  if constexpr (ST) {
+    return s_col[t - T.t_beg][c];
+  } else {
+    const int blk = p.tile_blk[t] + (c >> 3);
+    return ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+  }
 }
 // bitmap word holding window row r, tile columns 4g .. 4g + 3
+template <bool ST>
 __device__ __forceinline__ unsigned long long tile_word(const B16BwdParams& p, const Tiles& T,
                                                         const unsigned long long (*s_bits)[4], int t, int r,
                                                         int g) {
   const int ub = g >> 1;
-  if (T.staged) return s_bits[t - T.t_beg][ub * 2 + (r >> 3)];
-  const int blk = p.tile_blk[t] + ub;
-  return (ub == 1 && blk >= T.b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+  if constexpr (ST) {
+    return s_bits[t - T.t_beg][ub * 2 + (r >> 3)];
+  } else {
+    const int blk = p.tile_blk[t] + ub;
+    return (ub == 1 && blk >= T.b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+  }
 }
 
-// Stage a 16 x D D-layout accumulator set (lane l: rows 4g + i, dims mb*16 + r)
-// plus a row-layout one (lane l: row r, dims kc*32 + 8g + t) in LDS, then store
-// the window's rows of head h, 16 contiguous bytes per lane.
+// Row-layout partial results (lane l: row r, dims kc*32 + 8g + t) are placed
+// in a 16 x D LDS tile first, so that their registers are free during the
+// tile loop.
 template <int D>
-__device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16], const float (&res)[D / 32][8],
-                                           float* dst, int64_t ldr, int h, int w, int n_rows, int lane) {
-  constexpr int MB = D / 16, KC = D / 32, LDO = D + 4;
+__device__ __forceinline__ void put_rows(float* lo, const float (&res)[D / 32][8], int lane) {
+  constexpr int KC = D / 32, LDO = ldo<D>();
   const int r = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo[(4 * g + i) * LDO + mb * 16 + r] = acc[mb][i];
-  wave_sync();
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) lo[r * LDO + kc * 32 + 8 * g + t] += res[kc][t];
+    for (int t = 0; t < 8; ++t) lo[r * LDO + kc * 32 + 8 * g + t] = res[kc][t];
+}
+
+// Add a D-layout accumulator set (lane l: rows 4g + i, dims mb*16 + r) to
+// the LDS tile, then store the window's rows of head h, 16 contiguous bytes
+// per lane.
+template <int D>
+__device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16], float* dst, int64_t ldr, int h,
+                                           int w, int n_rows, int lane) {
+  constexpr int MB = D / 16, LDO = ldo<D>();
+  const int r = lane & 15, g = lane >> 4;
+  wave_sync();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo[(4 * g + i) * LDO + mb * 16 + r] += acc[mb][i];
   wave_sync();
   constexpr int LPRW = D / 4;     // lanes per row slice
   constexpr int RPI = 64 / LPRW;  // rows per store instruction
@@ -200,31 +241,23 @@ __device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16]
 // ---------------------------------------------------------------------------
 // destination walk: dq (and Delta)
 // ---------------------------------------------------------------------------
-template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
+template <int D, int NWAVE, bool ST>
+__device__ __forceinline__ void dst_walk(const B16BwdParams& p, const Tiles& T, int w, const int32_t (*s_col)[16],
+                                         const unsigned long long (*s_bits)[4], uint16_t* lk, float* lo) {
   constexpr int KC = D / 32, MB = D / 16;
-  constexpr int LDK = D + 8;  // padded LDS row (bf16)
-  constexpr int LDO = D + 4;  // padded LDS row (floats)
-  __shared__ uint16_t s_k[NWAVE][16 * LDK];
-  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
-  __shared__ int32_t s_col[MAXT][16];
-  __shared__ unsigned long long s_bits[MAXT][4];
-
+  constexpr int LDK = ldk<D>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
   const int row = w * 16 + r;
   const bool row_ok = row < p.n_rows;
-  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;
   const float sc2 = p.scale * kLog2e;
-  uint16_t* lk = s_k[wave];
-  float* lo = s_o[wave];
 
   for (int h = wave; h < p.H; h += NWAVE) {
     // this lane's slices of the row: q, dO (rounded to bf16 for the matrix
-    // cores) in B-operand layout; Delta = <dO, O> over the head, lse
+    // cores, and stored so for the source walk) in B-operand layout; Delta =
+    // <dO, O> over the head, lse
     s16x8 qb[KC], gb[KC];
     float L2 = 0.0f, dl = 0.0f;
     if (row_ok) {
@@ -238,6 +271,8 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) dl = fmaf(go[kc][t], o[kc][t], dl);
       to_bf<KC>(go, gb);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) *reinterpret_cast<s16x8*>(p.dob + ro + kc * 32 + 8 * g) = gb[kc];
       L2 = p.lse[(int64_t)row * p.H + h] * kLog2e;
     } else {
 #pragma unroll
@@ -246,18 +281,42 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
     dl += __shfl_xor(dl, 16, 64);
     dl += __shfl_xor(dl, 32, 64);
     if (row_ok && g == 0) p.delta[(int64_t)row * p.H + h] = dl;
-
+    {
+      float res[KC][8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) res[kc][t] = 0.0f;
+      // residual entries of this row: the row's four lanes each hold a
+      // quarter of the head dimension
+      for (int e = res_b; e < res_e; ++e) {
+        const int64_t co = (int64_t)p.res_col[e] * ldr + h * D;
+        s16x8 kv[KC], vv[KC];
+        load_bf<KC>(p.k + co, g, kv);
+        load_bf<KC>(p.v + co, g, vv);
+        float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          s = dot8(qb[kc], kv[kc], s);
+          dpv = dot8(gb[kc], vv[kc], dpv);
+        }
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        dpv += __shfl_xor(dpv, 16, 64);
+        dpv += __shfl_xor(dpv, 32, 64);
+        const float ds = ex2(s * sc2 - L2) * (dpv - dl) * p.scale;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) res[kc][t] = fmaf(ds, bf((uint16_t)kv[kc][t]), res[kc][t]);
+      }
+      put_rows<D>(lo, res, lane);
+    }
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float res[KC][8];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) res[kc][t] = 0.0f;
-
     auto load_kv = [&](int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
-      const int64_t co = (int64_t)tile_col(p, T, s_col, t, r) * ldr + h * D;
+      const int64_t co = (int64_t)tile_col<ST>(p, T, s_col, t, r) * ldr + h * D;
       load_bf<KC>(p.k + co, g, ka);
       load_bf<KC>(p.v + co, g, va);
     };
@@ -271,7 +330,7 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
         dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va[kc]),
                                                      __builtin_bit_cast(bf16x8, gb[kc]), dp, 0, 0, 0);
       }
-      const unsigned long long word = tile_word(p, T, s_bits, t, r, g);
+      const unsigned long long word = tile_word<ST>(p, T, s_bits, t, r, g);
       const int base = (r & 7) * 8 + 4 * (g & 1);
       s16x4 dsb;
 #pragma unroll
@@ -285,9 +344,7 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
       wave_sync();
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        s16x4 kt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kt[i] = (short)lk[(4 * g + i) * LDK + mb * 16 + r];
+        const s16x4 kt = lds_b_operand(lk + mb * 16, LDK, lane);
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsb, kt, acc[mb], 0, 0, 0);
       }
       wave_sync();
@@ -305,61 +362,51 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_dst(B16BwdParams p) {
       }
     }
 
-    // residual entries of this row: the row's four lanes each hold a quarter
-    // of the head dimension
-    for (int e = res_b; e < res_e; ++e) {
-      const int64_t co = (int64_t)p.res_col[e] * ldr + h * D;
-      s16x8 kv[KC], vv[KC];
-      load_bf<KC>(p.k + co, g, kv);
-      load_bf<KC>(p.v + co, g, vv);
-      float s = 0.0f, dpv = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s = dot8(qb[kc], kv[kc], s);
-        dpv = dot8(gb[kc], vv[kc], dpv);
-      }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      dpv += __shfl_xor(dpv, 16, 64);
-      dpv += __shfl_xor(dpv, 32, 64);
-      const float ds = ex2(s * sc2 - L2) * (dpv - dl) * p.scale;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) res[kc][t] = fmaf(ds, bf((uint16_t)kv[kc][t]), res[kc][t]);
-    }
-
-    store_rows<D>(lo, acc, res, p.g0, ldr, h, w, p.n_rows, lane);
+    store_rows<D>(lo, acc, p.g0, ldr, h, w, p.n_rows, lane);
   }
+}
+
+// (waves_per_eu: without it the compiler splits the registers into VGPRs
+// and AGPRs and loses a wave of occupancy)
+template <int D, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_gt_b16_bwd_dst(
+    B16BwdParams p) {
+  __shared__ uint16_t s_k[NWAVE][16 * ldk<D>()];
+  __shared__ __align__(16) float s_o[NWAVE][16 * ldo<D>()];
+  __shared__ int32_t s_col[MAXT][16];
+  __shared__ unsigned long long s_bits[MAXT][4];
+  const int wave = threadIdx.x >> 6;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
+  if (T.staged) dst_walk<D, NWAVE, true>(p, T, w, s_col, s_bits, s_k[wave], s_o[wave]);
+  else dst_walk<D, NWAVE, false>(p, T, w, s_col, s_bits, s_k[wave], s_o[wave]);
 }
 
 // ---------------------------------------------------------------------------
 // source walk over A^T: dk, dv
 // ---------------------------------------------------------------------------
-template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_src(B16BwdParams p) {
+// lq, lg: the tile's q and dO rows ([destination][dim], bf16); lo, lo2: the
+// window's dk and dv rows
+template <int D, int NWAVE, bool ST>
+__device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, int w, const int32_t (*s_col)[16],
+                                         const unsigned long long (*s_bits)[4], uint16_t* lq, uint16_t* lg,
+                                         float* lo, float* lo2) {
   constexpr int KC = D / 32, MB = D / 16;
-  constexpr int LDK = D + 8;
-  constexpr int LDO = D + 4;
-  __shared__ uint16_t s_q[NWAVE][16 * LDK];   // the tile's q rows, [destination][dim]
-  __shared__ uint16_t s_g[NWAVE][16 * LDK];   // the tile's dO rows in bf16
-  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
-  __shared__ int32_t s_col[MAXT][16];
-  __shared__ unsigned long long s_bits[MAXT][4];
-
+  constexpr int LDK = ldk<D>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
   const int row = w * 16 + r;  // a source node (row of A^T)
   const bool row_ok = row < p.n_rows;
-  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;
   const float sc2 = p.scale * kLog2e;
-  uint16_t* lq = s_q[wave];
-  uint16_t* lg = s_g[wave];
-  float* lo = s_o[wave];
 
+  // one destination row's slices for this lane: q, dO (bf16), lse, Delta
+  // (lse raw: arithmetic on it at load time would wait for the loads)
+  struct Dst {
+    s16x8 q[KC], g[KC];
+    float lse, dl;
+  };
   for (int h = wave; h < p.H; h += NWAVE) {
     // this lane's slices of its source row: k and v in B-operand layout
     s16x8 kb[KC], vb[KC];
@@ -371,47 +418,71 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_src(B16BwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) kb[kc] = vb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
+    {
+      float resk[KC][8], resv[KC][8];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) resk[kc][t] = resv[kc][t] = 0.0f;
+      // residual entries of this source row (destinations i)
+      for (int e = res_b; e < res_e; ++e) {
+        const int i = p.res_col[e];
+        const int64_t io = (int64_t)i * ldr + h * D;
+        s16x8 qv[KC], gv[KC];
+        load_bf<KC>(p.q + io, g, qv);
+        load_bf<KC>(p.dob + io, g, gv);
+        const float L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
+        const float dl = p.delta[(int64_t)i * p.H + h];
+        float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          s = dot8(qv[kc], kb[kc], s);
+          dpv = dot8(gv[kc], vb[kc], dpv);
+        }
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        dpv += __shfl_xor(dpv, 16, 64);
+        dpv += __shfl_xor(dpv, 32, 64);
+        const float a = ex2(s * sc2 - L2);
+        const float ds = a * (dpv - dl) * p.scale;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            resk[kc][t] = fmaf(ds, bf((uint16_t)qv[kc][t]), resk[kc][t]);
+            resv[kc][t] = fmaf(a, bf((uint16_t)gv[kc][t]), resv[kc][t]);
+          }
+      }
+      put_rows<D>(lo, resk, lane);
+      put_rows<D>(lo2, resv, lane);
+    }
     f32x4 acck[MB], accv[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acck[mb] = accv[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float resk[KC][8], resv[KC][8];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) resk[kc][t] = resv[kc][t] = 0.0f;
-
-    // one tile's destination rows for this lane (tile column r): q, dO, L, Delta
-    struct Dst {
-      s16x8 q[KC];
-      float go[KC][8];
-      float L2, dl;
-    };
     auto load_dst = [&](int t, Dst& d) {
-      const int i = tile_col(p, T, s_col, t, r);
+      const int i = tile_col<ST>(p, T, s_col, t, r);
       const int64_t io = (int64_t)i * ldr + h * D;
       load_bf<KC>(p.q + io, g, d.q);
-      load_f32<KC>(p.dout + io, g, d.go);
-      d.L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
+      load_bf<KC>(p.dob + io, g, d.g);
+      d.lse = p.lse[(int64_t)i * p.H + h];
       d.dl = p.delta[(int64_t)i * p.H + h];
     };
     auto process = [&](int t, const Dst& d) {
-      s16x8 gb[KC];
-      to_bf<KC>(d.go, gb);
       // lane holds S and dP of source r with destinations 4g .. 4g + 3 of the tile
       f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f}, dp = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d.q[kc]),
                                                      __builtin_bit_cast(bf16x8, kb[kc]), st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, gb[kc]),
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, d.g[kc]),
                                                      __builtin_bit_cast(bf16x8, vb[kc]), dp, 0, 0, 0);
       }
-      const unsigned long long word = tile_word(p, T, s_bits, t, r, g);
+      const unsigned long long word = tile_word<ST>(p, T, s_bits, t, r, g);
       const int base = (r & 7) * 8 + 4 * (g & 1);
       s16x4 dsb, ab;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float Lc = __shfl(d.L2, 4 * g + i, 64);  // lane c (0..15) holds destination c
+        const float Lc = __shfl(d.lse, 4 * g + i, 64) * kLog2e;  // lane c (0..15) holds destination c
         const float Dc = __shfl(d.dl, 4 * g + i, 64);
         const float a = ((word >> (base + i)) & 1ull) ? ex2(st[i] * sc2 - Lc) : 0.0f;
         ab[i] = (short)f2bf(a);
@@ -421,23 +492,20 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_src(B16BwdParams p) {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         *reinterpret_cast<s16x8*>(lq + r * LDK + kc * 32 + 8 * g) = d.q[kc];
-        *reinterpret_cast<s16x8*>(lg + r * LDK + kc * 32 + 8 * g) = gb[kc];
+        *reinterpret_cast<s16x8*>(lg + r * LDK + kc * 32 + 8 * g) = d.g[kc];
       }
       wave_sync();
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        s16x4 qt, gt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qt[i] = (short)lq[(4 * g + i) * LDK + mb * 16 + r];
-          gt[i] = (short)lg[(4 * g + i) * LDK + mb * 16 + r];
-        }
+        const s16x4 qt = lds_b_operand(lq + mb * 16, LDK, lane);
+        const s16x4 gt = lds_b_operand(lg + mb * 16, LDK, lane);
         acck[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(dsb, qt, acck[mb], 0, 0, 0);
         accv[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ab, gt, accv[mb], 0, 0, 0);
       }
       wave_sync();
     };
 
+    // two-deep pipeline over the window's dense tiles
     Dst dA, dB;
     if (T.t_beg < T.t_end) load_dst(T.t_beg, dA);
     for (int t = T.t_beg; t < T.t_end; t += 2) {
@@ -449,41 +517,25 @@ __global__ __launch_bounds__(NWAVE * 64) void k_gt_b16_bwd_src(B16BwdParams p) {
       }
     }
 
-    // residual entries of this source row (destinations i)
-    for (int e = res_b; e < res_e; ++e) {
-      const int i = p.res_col[e];
-      const int64_t io = (int64_t)i * ldr + h * D;
-      s16x8 qv[KC], gv[KC];
-      float go[KC][8];
-      load_bf<KC>(p.q + io, g, qv);
-      load_f32<KC>(p.dout + io, g, go);
-      to_bf<KC>(go, gv);
-      const float L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
-      const float dl = p.delta[(int64_t)i * p.H + h];
-      float s = 0.0f, dpv = 0.0f;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        s = dot8(qv[kc], kb[kc], s);
-        dpv = dot8(gv[kc], vb[kc], dpv);
-      }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      dpv += __shfl_xor(dpv, 16, 64);
-      dpv += __shfl_xor(dpv, 32, 64);
-      const float a = ex2(s * sc2 - L2);
-      const float ds = a * (dpv - dl) * p.scale;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          resk[kc][t] = fmaf(ds, bf((uint16_t)qv[kc][t]), resk[kc][t]);
-          resv[kc][t] = fmaf(a, bf((uint16_t)gv[kc][t]), resv[kc][t]);
-        }
-    }
-
-    store_rows<D>(lo, acck, resk, p.g0, ldr, h, w, p.n_rows, lane);
-    store_rows<D>(lo, accv, resv, p.g1, ldr, h, w, p.n_rows, lane);
+    store_rows<D>(lo, acck, p.g0, ldr, h, w, p.n_rows, lane);
+    store_rows<D>(lo2, accv, p.g1, ldr, h, w, p.n_rows, lane);
   }
+}
+
+template <int D, int NWAVE>
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gt_b16_bwd_src(
+    B16BwdParams p) {
+  __shared__ uint16_t s_q[NWAVE][16 * ldk<D>()];
+  __shared__ uint16_t s_g[NWAVE][16 * ldk<D>()];
+  __shared__ __align__(16) float s_o[NWAVE][16 * ldo<D>()];
+  __shared__ __align__(16) float s_o2[NWAVE][16 * ldo<D>()];
+  __shared__ int32_t s_col[MAXT][16];
+  __shared__ unsigned long long s_bits[MAXT][4];
+  const int wave = threadIdx.x >> 6;
+  const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
+  const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
+  if (T.staged) src_walk<D, NWAVE, true>(p, T, w, s_col, s_bits, s_q[wave], s_g[wave], s_o[wave], s_o2[wave]);
+  else src_walk<D, NWAVE, false>(p, T, w, s_col, s_bits, s_q[wave], s_g[wave], s_o[wave], s_o2[wave]);
 }
 
 void fill_layout(B16BwdParams& p, const gnn_plan* pl) {
@@ -506,6 +558,7 @@ int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const
   GNN_TRY(plan_transpose(pl, s));
   GNN_TRY(plan_transpose_wsb(pl, s));
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
+  GNN_TRY(plan_grow(pl, (void**)&pl->dob, &pl->dob_cap, (size_t)std::max(pl->n_rows, 1) * H * D * 2));
   B16BwdParams p{};
   p.q = (const uint16_t*)q;
   p.k = (const uint16_t*)k;
@@ -514,6 +567,7 @@ int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const
   p.lse = lse;
   p.dout = dout;
   p.delta = pl->delta;
+  p.dob = pl->dob;
   p.H = H;
   p.scale = scale;
   constexpr int NW = 2;  // waves per window, each looping over half of the heads

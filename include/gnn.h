@@ -319,7 +319,9 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
  * the exact gradients, not to fp32 rounding.  Square CSR, bf16 q, k, v only,
  * D in {32, 64}, H*D*2 <= 2048; other arguments as in gnn_gt_backward.  The
  * plan must carry WSB tiles (NULL: a transient one is built); the tiles of
- * A^T are built on its first block-sparse backward call.
+ * A^T are built on its first block-sparse backward call.  The plan keeps,
+ * between the two walks, Delta [n_rows, H] float32 and dO rounded to bf16
+ * [n_rows, H, D] (grown on demand, freed with the plan).
  * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
 int gnn_gt_backward_block16(const gnn_csr* csr, const void* q, const void* k, const void* v, int32_t H,
                             int32_t D, float scale, const float* out, const float* lse, const float* dout,
