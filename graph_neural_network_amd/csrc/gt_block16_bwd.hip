@@ -197,9 +197,8 @@ __device__ __forceinline__ unsigned long long tile_word(const B16BwdParams& p, c
   }
 }
 
-// Row-layout partial results (lane l: row r, dims kc*32 + 8g + t) are placed
-// in a 16 x D LDS tile first, so that their registers are free during the
-// tile loop.
+// Row-layout partial results (lane l: row r, dims kc*32 + 8g + t) placed in
+// a 16 x D LDS tile.
 template <int D>
 __device__ __forceinline__ void put_rows(float* lo, const float (&res)[D / 32][8], int lane) {
   constexpr int KC = D / 32, LDO = ldo<D>();
@@ -210,22 +209,41 @@ __device__ __forceinline__ void put_rows(float* lo, const float (&res)[D / 32][8
     for (int t = 0; t < 8; ++t) lo[r * LDO + kc * 32 + 8 * g + t] = res[kc][t];
 }
 
-// Add a D-layout accumulator set (lane l: rows 4g + i, dims mb*16 + r) to
-// the LDS tile, then store the window's rows of head h, 16 contiguous bytes
-// per lane.
-template <int D>
-__device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16], float* dst, int64_t ldr, int h,
-                                           int w, int n_rows, int lane) {
+// A D-layout accumulator set (lane l: rows 4g + i, dims mb*16 + r) into the
+// LDS tile: stored, or added to what is there.
+template <int D, bool ADD>
+__device__ __forceinline__ void put_acc(float* lo, const f32x4 (&acc)[D / 16], int lane) {
   constexpr int MB = D / 16, LDO = ldo<D>();
   const int r = lane & 15, g = lane >> 4;
-  wave_sync();
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lo[(4 * g + i) * LDO + mb * 16 + r] += acc[mb][i];
-  wave_sync();
+    for (int i = 0; i < 4; ++i) {
+      float& x = lo[(4 * g + i) * LDO + mb * 16 + r];
+      x = ADD ? x + acc[mb][i] : acc[mb][i];
+    }
+}
+
+// Add row-layout partial results (lane l: row r, dims kc*32 + 8g + t).
+template <int D>
+__device__ __forceinline__ void add_rows(float* lo, const float (&res)[D / 32][8], int lane) {
+  constexpr int KC = D / 32, LDO = ldo<D>();
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) lo[r * LDO + kc * 32 + 8 * g + t] += res[kc][t];
+}
+
+// Store the LDS tile as the window's rows of head h, 16 contiguous bytes per
+// lane (rows past the end skipped).
+template <int D>
+__device__ __forceinline__ void write_rows(const float* lo, float* dst, int64_t ldr, int h, int w, int n_rows,
+                                           int lane) {
+  constexpr int LDO = ldo<D>();
   constexpr int LPRW = D / 4;     // lanes per row slice
   constexpr int RPI = 64 / LPRW;  // rows per store instruction
+  wave_sync();
   const int r0 = lane / LPRW, dd = (lane % LPRW) * 4;
   const float* lsrc = lo + r0 * LDO + dd;
   float* odst = dst + (int64_t)(w * 16 + r0) * ldr + h * D + dd;
@@ -236,6 +254,15 @@ __device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16]
     if (q * RPI < rows_left) *reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr) = t;
   }
   wave_sync();
+}
+
+// Add a D-layout accumulator set to the LDS tile and store it.
+template <int D>
+__device__ __forceinline__ void store_rows(float* lo, const f32x4 (&acc)[D / 16], float* dst, int64_t ldr, int h,
+                                           int w, int n_rows, int lane) {
+  wave_sync();
+  put_acc<D, true>(lo, acc, lane);
+  write_rows<D>(lo, dst, ldr, h, w, n_rows, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -385,12 +412,12 @@ __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3)))
 // ---------------------------------------------------------------------------
 // source walk over A^T: dk, dv
 // ---------------------------------------------------------------------------
-// lq, lg: the tile's q and dO rows ([destination][dim], bf16); lo, lo2: the
-// window's dk and dv rows
+// buf: the wave's LDS: during the tile loop the tile's q and dO rows
+// ([destination][dim], bf16), after it the window's dk rows (fp32); lo2: the
+// window's dv rows
 template <int D, int NWAVE, bool ST>
 __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, int w, const int32_t (*s_col)[16],
-                                         const unsigned long long (*s_bits)[4], uint16_t* lq, uint16_t* lg,
-                                         float* lo, float* lo2) {
+                                         const unsigned long long (*s_bits)[4], char* buf, float* lo2) {
   constexpr int KC = D / 32, MB = D / 16;
   constexpr int LDK = ldk<D>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -400,6 +427,9 @@ __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, 
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;
   const float sc2 = p.scale * kLog2e;
+  uint16_t* lq = reinterpret_cast<uint16_t*>(buf);
+  uint16_t* lg = lq + 16 * LDK;
+  float* lo = reinterpret_cast<float*>(buf);
 
   // one destination row's slices for this lane: q, dO (bf16), lse, Delta
   // (lse raw: arithmetic on it at load time would wait for the loads)
@@ -417,44 +447,6 @@ __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, 
     } else {
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) kb[kc] = vb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-    {
-      float resk[KC][8], resv[KC][8];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int t = 0; t < 8; ++t) resk[kc][t] = resv[kc][t] = 0.0f;
-      // residual entries of this source row (destinations i)
-      for (int e = res_b; e < res_e; ++e) {
-        const int i = p.res_col[e];
-        const int64_t io = (int64_t)i * ldr + h * D;
-        s16x8 qv[KC], gv[KC];
-        load_bf<KC>(p.q + io, g, qv);
-        load_bf<KC>(p.dob + io, g, gv);
-        const float L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
-        const float dl = p.delta[(int64_t)i * p.H + h];
-        float s = 0.0f, dpv = 0.0f;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          s = dot8(qv[kc], kb[kc], s);
-          dpv = dot8(gv[kc], vb[kc], dpv);
-        }
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        dpv += __shfl_xor(dpv, 16, 64);
-        dpv += __shfl_xor(dpv, 32, 64);
-        const float a = ex2(s * sc2 - L2);
-        const float ds = a * (dpv - dl) * p.scale;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            resk[kc][t] = fmaf(ds, bf((uint16_t)qv[kc][t]), resk[kc][t]);
-            resv[kc][t] = fmaf(a, bf((uint16_t)gv[kc][t]), resv[kc][t]);
-          }
-      }
-      put_rows<D>(lo, resk, lane);
-      put_rows<D>(lo2, resv, lane);
     }
     f32x4 acck[MB], accv[MB];
 #pragma unroll
@@ -517,25 +509,70 @@ __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, 
       }
     }
 
-    store_rows<D>(lo, acck, p.g0, ldr, h, w, p.n_rows, lane);
-    store_rows<D>(lo2, accv, p.g1, ldr, h, w, p.n_rows, lane);
+    // tile results to LDS: dk over the q / dO staging, which the tiles no
+    // longer need, dv beside it
+    wave_sync();
+    put_acc<D, false>(lo, acck, lane);
+    put_acc<D, false>(lo2, accv, lane);
+
+    float resk[KC][8], resv[KC][8];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) resk[kc][t] = resv[kc][t] = 0.0f;
+    // residual entries of this source row (destinations i)
+    for (int e = res_b; e < res_e; ++e) {
+      const int i = p.res_col[e];
+      const int64_t io = (int64_t)i * ldr + h * D;
+      s16x8 qv[KC], gv[KC];
+      load_bf<KC>(p.q + io, g, qv);
+      load_bf<KC>(p.dob + io, g, gv);
+      const float L2 = p.lse[(int64_t)i * p.H + h] * kLog2e;
+      const float dl = p.delta[(int64_t)i * p.H + h];
+      float s = 0.0f, dpv = 0.0f;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        s = dot8(qv[kc], kb[kc], s);
+        dpv = dot8(gv[kc], vb[kc], dpv);
+      }
+      s += __shfl_xor(s, 16, 64);
+      s += __shfl_xor(s, 32, 64);
+      dpv += __shfl_xor(dpv, 16, 64);
+      dpv += __shfl_xor(dpv, 32, 64);
+      const float a = ex2(s * sc2 - L2);
+      const float ds = a * (dpv - dl) * p.scale;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          resk[kc][t] = fmaf(ds, bf((uint16_t)qv[kc][t]), resk[kc][t]);
+          resv[kc][t] = fmaf(a, bf((uint16_t)gv[kc][t]), resv[kc][t]);
+        }
+    }
+
+    wave_sync();
+    add_rows<D>(lo, resk, lane);
+    add_rows<D>(lo2, resv, lane);
+    write_rows<D>(lo, p.g0, ldr, h, w, p.n_rows, lane);
+    write_rows<D>(lo2, p.g1, ldr, h, w, p.n_rows, lane);
   }
 }
 
+// (three waves per SIMD at D = 64 cost three spilled registers, reloaded once
+// per head, and are faster than two)
 template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_gt_b16_bwd_src(
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_gt_b16_bwd_src(
     B16BwdParams p) {
-  __shared__ uint16_t s_q[NWAVE][16 * ldk<D>()];
-  __shared__ uint16_t s_g[NWAVE][16 * ldk<D>()];
-  __shared__ __align__(16) float s_o[NWAVE][16 * ldo<D>()];
+  constexpr int BUF = 2 * 16 * ldk<D>() * 2 > 16 * ldo<D>() * 4 ? 2 * 16 * ldk<D>() * 2 : 16 * ldo<D>() * 4;
+  __shared__ __align__(16) char s_buf[NWAVE][BUF];
   __shared__ __align__(16) float s_o2[NWAVE][16 * ldo<D>()];
   __shared__ int32_t s_col[MAXT][16];
   __shared__ unsigned long long s_bits[MAXT][4];
   const int wave = threadIdx.x >> 6;
   const int w = (int)dev::xcd_remap(blockIdx.x, gridDim.x);
   const Tiles T = stage_tiles<NWAVE>(p, w, s_col, s_bits);
-  if (T.staged) src_walk<D, NWAVE, true>(p, T, w, s_col, s_bits, s_q[wave], s_g[wave], s_o[wave], s_o2[wave]);
-  else src_walk<D, NWAVE, false>(p, T, w, s_col, s_bits, s_q[wave], s_g[wave], s_o[wave], s_o2[wave]);
+  if (T.staged) src_walk<D, NWAVE, true>(p, T, w, s_col, s_bits, s_buf[wave], s_o2[wave]);
+  else src_walk<D, NWAVE, false>(p, T, w, s_col, s_bits, s_buf[wave], s_o2[wave]);
 }
 
 void fill_layout(B16BwdParams& p, const gnn_plan* pl) {
