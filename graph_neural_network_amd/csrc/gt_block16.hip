@@ -18,7 +18,7 @@
 // that lane l holds S[row l % 16][cols 4 (l / 16) .. +3]: exactly the B-operand
 // layout of v_mfma_f32_16x16x16_bf16 for O^T += V_blk^T P^T.  The value block
 // is transposed through LDS (V rows are dimension-contiguous, the MFMA needs
-// column-contiguous k).  P is rounded to bf16 for that product; l sums the
+// column-contiguous k), read back with the LDS transpose read.  P is rounded to bf16 for that product; l sums the
 // rounded weights.  Edges of tiles too sparse for the matrix cores (the
 // residual CSR of the plan) are then streamed per row into the same (m, l,
 // acc) state, the four lanes of a row splitting the head dimension.
@@ -70,6 +70,20 @@ __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
+// A 16x16x16 bf16 MFMA operand holding, in lane 16g + r, rows 4g .. 4g + 3 of
+// column r of a 16 x 16 block stored row-major in LDS (row stride ld), read
+// with the gfx950 LDS transpose read: within each 16 lanes, lane 16g + 4i + a
+// names row 4g + i, columns 4a .. 4a + 3, and lane 16g + 4a + j receives
+// element j of the rows named by lanes 16g + a, 16g + 4 + a, ...  Needs every
+// lane active.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_tr_operand(const uint16_t* blk, int ld, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* a = blk + (4 * g + (r >> 2)) * ld + 4 * (r & 3);
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)a);
+  return __builtin_bit_cast(s16x4, v);
+}
+
 // dot of 8 bf16 pairs on v_dot2_f32_bf16
 __device__ __forceinline__ float dot8(const s16x8& a, const s16x8& b, float acc) {
 #pragma unroll
@@ -87,7 +101,7 @@ constexpr int MAXT = 32;  // tiles of a window staged in LDS (larger windows rea
 // flight while it computes another), so D <= 64 asks for four waves per SIMD
 // (at most 128 VGPRs) rather than the three its natural allocation allows.
 template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 1)))
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2)))
 void k_gt_block16(B16Params p) {
   constexpr int KC = D / 32;   // k-chunks of the score product
   constexpr int MB = D / 16;   // 16-dim blocks of the output
@@ -216,9 +230,7 @@ void k_gt_block16(B16Params p) {
       const s16x4 pt = s16x4{(short)pb[0], (short)pb[1], (short)pb[2], (short)pb[3]};
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        s16x4 vt;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vt[i] = (short)lv[(4 * g + i) * LDV + mb * 16 + r];
+        const s16x4 vt = lds_tr_operand(lv + mb * 16, LDV, lane);
         acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pt, acc[mb], 0, 0, 0);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
