@@ -13,12 +13,20 @@
 // features 64 w .. 64 w + 63 of the slice as four 16-wide chunks.  For each
 // dense tile the workgroup stages the 16 X rows (the slice of each) in LDS,
 // double-buffered (the next tile's rows are loaded into registers while the
-// current one computes), and each wave runs 4 k-steps x 4 chunks of
-// v_mfma_f32_16x16x4_f32.  A is built in registers from the tile bitmap and
-// the column weights in fp32, and B is read from LDS as fp32, so every product
-// is an fp32 product, as in the CSR kernel.  Lane layouts (checked on the
-// device): A: lane l holds A[l % 16][l / 16]; B: lane l holds B[l / 16][l % 16];
-// D: lane l holds D[4 (l / 16) + r][l % 16], r = 0..3.  The window's tile
+// current one computes).  A is built in registers from the tile bitmap and the
+// column weights; every product is exact in fp32 and accumulates in fp32, as
+// in the CSR kernel:
+//   bf16 X: per chunk one v_mfma_f32_16x16x16_bf16 over the tile's 16
+//     columns, B read from LDS with the transpose read.  A column weight that
+//     is not 1 (RIGHT, BOTH) is split exactly into three bf16 parts, w = hi +
+//     mid + lo (8 significant bits each, 24 in all), one MFMA each: a
+//     bf16 x bf16 product is exact in fp32, so the sum of the three products
+//     is w x up to the fp32 accumulation.
+//   fp32 X: 4 k-steps x 4 chunks of v_mfma_f32_16x16x4_f32.
+// Lane layouts (checked on the device): 16x16x4 f32: A: lane l holds
+// A[l % 16][l / 16]; B: B[l / 16][l % 16].  16x16x16 bf16: A: lane l holds
+// A[l % 16][4 (l / 16) .. +3]; B: B[4 (l / 16) .. +3][l % 16].  Both: D: lane
+// l holds D[4 (l / 16) + r][l % 16], r = 0..3.  The window's tile
 // metadata (columns, weights, bitmap words) is staged in LDS up front, so a
 // tile's row gathers wait on one memory latency instead of three dependent
 // ones.  Output rows are staged through LDS so that each store writes whole
@@ -31,8 +39,29 @@ namespace gnn {
 namespace {
 
 constexpr int FW = 256;   // features per workgroup
+constexpr int LDX = FW + 8;  // staged row stride: 16 rows of one transpose read land on distinct LDS banks
 constexpr int MAXT = 16;  // tiles whose metadata is staged at once
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// The B operand of a 16x16x16 bf16 MFMA (lane 16g + r: rows 4g .. 4g + 3 of
+// column r) from a 16 x 16 block stored row-major in LDS (row stride ld), by
+// the gfx950 LDS transpose read: within each 16 lanes, lane 16g + 4i + a
+// names row 4g + i, columns 4a .. 4a + 3, and lane 16g + 4a + j receives
+// element j of the rows named by lanes 16g + a, 16g + 4 + a, ...  Needs every
+// lane active.
+__device__ __forceinline__ s16x4 lds_tr_operand(const uint16_t* blk, int ld, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint16_t* a = blk + (4 * g + (r >> 2)) * ld + 4 * (r & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)a);
+}
 
 struct B16SpmmParams {
   const int32_t* row_ptr;
@@ -67,13 +96,13 @@ __device__ __forceinline__ float col_weight(const B16SpmmParams& p, int j) {
   return 1.0f;
 }
 
-// bf16: 64 VGPRs and 19 KB of LDS allow eight workgroups per CU
+// bf16: at most 64 VGPRs and 19.4 KB of LDS allow eight workgroups per CU
 template <typename T>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 8 : 4))) void k_spmm_b16(B16SpmmParams p) {
   constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
   constexpr int CPR = FW / EPC;              // chunks per staged row slice
   constexpr int CPT = 16 * CPR / 256;        // chunks per thread per tile
-  __shared__ __align__(16) T s_x[2][16][FW];
+  __shared__ __align__(16) T s_x[2][16][LDX];
   // the window's tile metadata, MAXT tiles at a time: the 16 columns of each
   // tile, their weights (0 for padding) and the two blocks' bitmap words
   __shared__ int32_t s_tcol[MAXT][16];
@@ -137,22 +166,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     for (int k = 0; k < nt; ++k) {
       const int buf = k & 1;
       if (k + 1 < nt) load_tile(k + 1);
-      // A values of this lane: row li, tile columns 4 s + lg
-      float a[4];
+      if constexpr (sizeof(T) == 2) {
+        // A values of this lane: row li, tile columns 4 lg .. 4 lg + 3; the
+        // four B operands of its chunks
+        float a[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int c = 4 * s + lg;
-        const unsigned long long word = s_tbits[k][(c >> 3) * 2 + (li >> 3)];
-        const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
-        a[s] = bit ? s_tw[k][c] : 0.0f;
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * lg + i;
+          const unsigned long long word = s_tbits[k][(c >> 3) * 2 + (li >> 3)];
+          const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
+          a[i] = bit ? s_tw[k][c] : 0.0f;
+        }
+        s16x4 b[4];
 #pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        const int fl = wave * 64 + ch * 16 + li;   // feature within the slice
+        for (int ch = 0; ch < 4; ++ch)
+          b[ch] = lds_tr_operand(reinterpret_cast<const uint16_t*>(&s_x[buf][0][wave * 64 + ch * 16]), LDX, lane);
+        // the weights in exact bf16 parts, high to low: a part is a rounded
+        // to bf16, and a keeps the (exact) remainder; one part when every
+        // weight is 1
+        const int parts = (p.norm == GNN_NORM_RIGHT || p.norm == GNN_NORM_BOTH) ? 3 : 1;
+        for (int q = 0; q < parts; ++q) {
+          s16x4 ap;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint16_t h = f2bf(a[i]);
+            ap[i] = (short)h;
+            a[i] -= bf2f(h);
+          }
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) acc[ch] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ap, b[ch], acc[ch], 0, 0, 0);
+        }
+      } else {
+        // A values of this lane: row li, tile columns 4 s + lg
+        float a[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const float b = to_f32<T>(s_x[buf][4 * s + lg][fl]);
-          acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[ch], 0, 0, 0);
+          const int c = 4 * s + lg;
+          const unsigned long long word = s_tbits[k][(c >> 3) * 2 + (li >> 3)];
+          const bool bit = (word >> ((li & 7) * 8 + (c & 7))) & 1ull;
+          a[s] = bit ? s_tw[k][c] : 0.0f;
+        }
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const int fl = wave * 64 + ch * 16 + li;   // feature within the slice
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float b = to_f32<T>(s_x[buf][4 * s + lg][fl]);
+            acc[ch] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b, acc[ch], 0, 0, 0);
+          }
         }
       }
       __syncthreads();  // every wave is done with the other buffer before it is refilled
