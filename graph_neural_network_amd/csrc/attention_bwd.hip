@@ -93,7 +93,10 @@ struct Row {
   Raw<NV> own;        // GT dst: q_i; GT src: k_j
   float f0[VEL];      // dst: dO_i; GT src: v_j; GATv2 src: r_j
   float f1[VEL];      // GATv2 dst: l_i
-  float a[VEL];       // GATv2: a
+  // GATv2: a (1 + slope) / 2 and a (1 - slope) / 2: a LeakyReLU(z) = av z +
+  // an |z|, and a LeakyReLU'(z) = av + an for z > 0, av - an otherwise
+  float av[VEL], an[VEL];
+  float sde = 0.0f;   // GATv2: sum of de over the slot's entries (the av part of acc0)
   float L2 = 0.0f;    // dst: L_i * log2 e
   float delta = 0.0f; // dst: Delta_i
   float acc0[VEL], acc1[VEL];
@@ -202,34 +205,35 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           for (int k = 0; k < VEL; ++k) {
             const float r = elem<T, NV>(x[u], k);
             z[k] = R.f1[k] + r;
-            e = fmaf(R.a[k], fmaxf(z[k], p.slope * z[k]), e);
+            e = fmaf(R.av[k], z[k], fmaf(R.an[k], fabsf(z[k]), e));
             gv = fmaf(R.f0[k], r, gv);
           }
           e = head_sum<LPH>(e);
           gv = head_sum<LPH>(gv);
           const float al = valid ? ex2(e * kLog2e - R.L2) : 0.0f;
           const float de = al * (gv - R.delta);
+          R.sde += de;
 #pragma unroll
           for (int k = 0; k < VEL; ++k) {
-            const bool pos = z[k] > 0.0f;
-            R.acc0[k] = fmaf(de * R.a[k], pos ? 1.0f : p.slope, R.acc0[k]);
-            R.acc1[k] = fmaf(de, pos ? z[k] : p.slope * z[k], R.acc1[k]);
+            R.acc0[k] = fmaf(de, z[k] > 0.0f ? R.an[k] : -R.an[k], R.acc0[k]);
+            R.acc1[k] = fmaf(de, fmaxf(z[k], p.slope * z[k]), R.acc1[k]);
           }
         } else {  // B_GAT_SRC
           float e = 0.0f, gv = 0.0f, z[VEL];
 #pragma unroll
           for (int k = 0; k < VEL; ++k) {
             z[k] = elem<T, NV>(x[u], k) + R.f0[k];
-            e = fmaf(R.a[k], fmaxf(z[k], p.slope * z[k]), e);
+            e = fmaf(R.av[k], z[k], fmaf(R.an[k], fabsf(z[k]), e));
             gv = fmaf(g[u][k], R.f0[k], gv);
           }
           e = head_sum<LPH>(e);
           gv = head_sum<LPH>(gv);
           const float al = valid ? ex2(e * kLog2e - Lc[u]) : 0.0f;
           const float de = al * (gv - Dc[u]);
+          R.sde += de;
 #pragma unroll
           for (int k = 0; k < VEL; ++k)
-            R.acc0[k] = fmaf(al, g[u][k], fmaf(de * R.a[k], z[k] > 0.0f ? 1.0f : p.slope, R.acc0[k]));
+            R.acc0[k] = fmaf(al, g[u][k], fmaf(de, z[k] > 0.0f ? R.an[k] : -R.an[k], R.acc0[k]));
         }
       }
     }
@@ -280,7 +284,7 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
 
   Row<T, NV, KIND> R;
 #pragma unroll
-  for (int k = 0; k < VEL; ++k) R.acc0[k] = R.acc1[k] = R.a[k] = R.f0[k] = R.f1[k] = 0.0f;
+  for (int k = 0; k < VEL; ++k) R.acc0[k] = R.acc1[k] = R.av[k] = R.an[k] = R.f0[k] = R.f1[k] = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4 * NV; ++t) R.own.u[t] = 0u;
   const int64_t ro = row * (int64_t)p.row_elems + sl * VEL;
@@ -312,7 +316,11 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     }
     if constexpr (KIND == B_GAT_DST || KIND == B_GAT_SRC) {
 #pragma unroll
-      for (int k = 0; k < VEL; ++k) R.a[k] = p.att[sl * VEL + k];
+      for (int k = 0; k < VEL; ++k) {
+        const float a = p.att[sl * VEL + k];
+        R.av[k] = a * (0.5f + 0.5f * p.slope);
+        R.an[k] = a * (0.5f - 0.5f * p.slope);
+      }
     }
   }
   if constexpr (DST) R.delta = head_sum<LPH>(R.delta);
@@ -320,6 +328,11 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     p.delta[row * p.H + head] = R.delta;  // once per row: the light slot, the single item, or chunk 0
 
   if (active) scan<T, LPE, NV, KIND, LPH>(p, eb, ee, sl, slot_base, d_ok, head, R);
+  if constexpr (KIND == B_GAT_DST || KIND == B_GAT_SRC) {
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) R.acc0[k] = fmaf(R.av[k], R.sde, R.acc0[k]);
+  }
+
 
   __shared__ __align__(16) float s_acc[NWAVE][2][64 * VEL];
 
