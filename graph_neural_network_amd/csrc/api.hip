@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/gnn.h.
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <new>
 #include <string>
@@ -68,6 +69,49 @@ struct PlanGuard {
   }
 };
 
+// The checks of the CSR contents that host validation leaves out, O(n + nnz):
+// bad[0] row_ptr decreases somewhere, bad[1] row_ptr[0] != 0 or row_ptr[n] !=
+// nnz, bad[2] a column outside [0, n_cols).  Reads the two arrays only within
+// their stated sizes and never indexes by their values.
+__global__ void k_check_csr(const int32_t* rp, const int32_t* ci, int32_t n, int64_t nnz, int32_t n_cols,
+                            int* bad) {
+  const int64_t i0 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t r = i0; r < n; r += stride)
+    if (rp[r] > rp[r + 1]) bad[0] = 1;
+  if (i0 == 0 && (rp[0] != 0 || (int64_t)rp[n] != nnz)) bad[1] = 1;
+  for (int64_t e = i0; e < nnz; e += stride) {
+    const int32_t c = ci[e];
+    if (c < 0 || c >= n_cols) bad[2] = 1;
+  }
+}
+
+// With GNN_DEBUG_VALIDATE=1 in the environment, run k_check_csr before
+// anything reads the CSR (synchronises the stream; allocates).
+int debug_validate(const gnn_csr* c, hipStream_t s) {
+  const char* env = getenv("GNN_DEBUG_VALIDATE");
+  if (!env || strcmp(env, "1") != 0) return GNN_OK;
+  int* d = nullptr;
+  GNN_HIP(hipMalloc((void**)&d, 3 * sizeof(int)));
+  int h[3] = {0, 0, 0};
+  hipError_t e = hipMemcpy(d, h, sizeof(h), hipMemcpyHostToDevice);
+  if (e == hipSuccess) {
+    const int64_t work = std::max<int64_t>(c->n_rows, c->nnz);
+    const unsigned blocks = (unsigned)std::min<int64_t>(std::max<int64_t>((work + 255) / 256, 1), 4096);
+    hipLaunchKernelGGL(k_check_csr, dim3(blocks), dim3(256), 0, s, c->row_ptr, c->col_idx, c->n_rows, c->nnz,
+                       c->n_cols, d);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
+  hipFree(d);
+  if (e != hipSuccess) return fail(GNN_ERR_DEVICE, std::string("CSR check: ") + hipGetErrorString(e));
+  if (h[1]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr[0] != 0 or row_ptr[n_rows] != nnz");
+  if (h[0]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr decreases");
+  if (h[2]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: a column index outside [0, n_cols)");
+  return GNN_OK;
+}
+
 }  // namespace
 
 int check_plan(const gnn_plan* p, const gnn_csr* csr) {
@@ -109,6 +153,7 @@ int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream,
     if (opts->build_wsb && csr->n_rows != csr->n_cols)
       return fail(GNN_ERR_INVALID_VALUE, "WSB tiles need a square CSR");
   }
+  GNN_TRY(debug_validate(csr, (hipStream_t)stream));
   gnn_plan* p = new (std::nothrow) gnn_plan();
   if (!p) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
   int rc = plan_build(csr, opts, (hipStream_t)stream, p);
@@ -414,6 +459,7 @@ int gnn_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_
   if ((row_ptr_out == nullptr) != (col_idx_out == nullptr))
     return fail(GNN_ERR_INVALID_VALUE, "give both row_ptr_out and col_idx_out, or neither");
   if (csr->n_rows == 0) return GNN_OK;
+  GNN_TRY(debug_validate(csr, (hipStream_t)stream));
   return launch_reorder(csr, kind, perm, row_ptr_out, col_idx_out, (hipStream_t)stream);
 }
 

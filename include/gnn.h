@@ -41,6 +41,13 @@
  *     message for the last failing call on the calling thread.
  *   - Empty neighbourhoods: sum / mean / SpMM give 0; max / min give 0 with
  *     arg -1; attention gives out 0 and lse = -inf.
+ *   - The CSR's contents are not read on the host.  With GNN_DEBUG_VALIDATE=1
+ *     in the environment, gnn_plan_create (and so every call that builds a
+ *     transient plan) and gnn_reorder first check them on the device:
+ *     row_ptr[0] = 0, row_ptr[n_rows] = nnz, row_ptr never decreasing, every
+ *     col_idx in [0, n_cols).  The check synchronises the stream and
+ *     allocates; a violation returns INVALID_VALUE before any other kernel
+ *     reads the CSR.  Without it, an invalid CSR is undefined behaviour.
  */
 #ifndef GNN_H_
 #define GNN_H_
