@@ -131,7 +131,7 @@ void k_gt_block16(B16Params p) {
     for (int i = threadIdx.x; i < nt * 16; i += NWAVE * 64) {
       const int t = i >> 4, c = i & 15;
       const int blk = p.tile_blk[t_beg + t] + (c >> 3);
-      s_col[t][c] = ((c >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+      s_col[t][c] = ((c >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (c & 7)];
     }
     for (int i = threadIdx.x; i < nt * 4; i += NWAVE * 64) {
       const int t = i >> 2, q = i & 3;
@@ -144,7 +144,7 @@ void k_gt_block16(B16Params p) {
   auto tile_col = [&](int t) -> int {
     if (staged) return s_col[t - t_beg][r];
     const int blk = p.tile_blk[t] + (r >> 3);
-    return ((r >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[blk * 8 + (r & 7)];
+    return ((r >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (r & 7)];
   };
   auto tile_word = [&](int t) -> unsigned long long {
     const int ub = g >> 1;  // which 16x8 block holds this lane's four columns

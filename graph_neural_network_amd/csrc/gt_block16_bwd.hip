@@ -158,7 +158,7 @@ __device__ __forceinline__ Tiles stage_tiles(const B16BwdParams& p, int w, int32
     for (int i = threadIdx.x; i < nt * 16; i += NWAVE * 64) {
       const int t = i >> 4, c = i & 15;
       const int blk = p.tile_blk[T.t_beg + t] + (c >> 3);
-      s_col[t][c] = ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+      s_col[t][c] = ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (c & 7)];
     }
     for (int i = threadIdx.x; i < nt * 4; i += NWAVE * 64) {
       const int t = i >> 2, q = i & 3;
@@ -180,7 +180,7 @@ __device__ __forceinline__ int tile_col(const B16BwdParams& p, const Tiles& T, c
     return s_col[t - T.t_beg][c];
   } else {
     const int blk = p.tile_blk[t] + (c >> 3);
-    return ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[blk * 8 + (c & 7)];
+    return ((c >> 3) == 1 && blk >= T.b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (c & 7)];
   }
 }
 // bitmap word holding window row r, tile columns 4g .. 4g + 3

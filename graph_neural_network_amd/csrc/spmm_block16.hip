@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
       const int k = q >> 4, c = q & 15;
       const int blk = p.tile_blk[tb + k] + (c >> 3);
       const bool have = !((c >> 3) == 1 && blk >= b_end);   // second block past the window: padding
-      const int col = have ? p.blk_col[blk * 8 + (c & 7)] : 0;
+      const int col = have ? p.blk_col[(int64_t)blk * 8 + (c & 7)] : 0;
       s_tcol[k][c] = col;
       s_tw[k][c] = have ? col_weight(p, col) : 0.0f;
       if (c < 4) {
