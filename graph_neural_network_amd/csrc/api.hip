@@ -300,7 +300,7 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
   if (!xl || !att || !out || (!xr && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "xl, xr, att or out is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || H * D * esz > 1024)
+  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 1024)
     return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
   if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out) % 16 != 0)
     return fail(GNN_ERR_UNSUPPORTED, "xl, xr and out must be 16-byte aligned");
@@ -321,7 +321,7 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   if (mode == GNN_GT_AUTO) {
     const int64_t esz0 = xtype == GNN_BF16 ? 2 : 4;
     bool fits = xtype == GNN_BF16 && (D == 32 || D == 64 || D == 128) && csr && csr->n_rows == csr->n_cols &&
-                (D * esz0) % 16 == 0 && H > 0 && H * D * esz0 <= 2048;
+                (D * esz0) % 16 == 0 && H > 0 && (int64_t)H * D * esz0 <= 2048;
     mode = GNN_GT_CSR;
     if (fits && plan && plan->has_wsb && check_plan(plan, csr) == GNN_OK) {
       const int64_t dense = plan->nnz - plan->wsb.n_resid;
@@ -335,7 +335,7 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   if (!q || !out || ((!k || !v) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "q, k, v or out is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || H * D * esz > 2048)
+  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 2048)
     return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
     return fail(GNN_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
@@ -394,7 +394,7 @@ int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_d
       ((!xr || !dxr) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || H * D * esz > 1024)
+  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 1024)
     return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
   if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dxl | (uintptr_t)dxr) % 16)
     return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");
@@ -415,7 +415,7 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
   if (((!q || !out || !lse || !dout || !dq) && csr->n_rows > 0) || ((!k || !v || !dk || !dv) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || H * D * esz > 2048)
+  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 2048)
     return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) % 16)
@@ -436,7 +436,7 @@ int gnn_gt_backward_block16(const gnn_csr* csr, const void* q, const void* k, co
   if ((!q || !out || !lse || !dout || !dq || !k || !v || !dk || !dv) && csr->n_rows > 0)
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
   if (D != 32 && D != 64) return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs bf16 and D in {32, 64}");
-  if (H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "H*D*2 must be at most 2048 bytes");
+  if ((int64_t)H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "H*D*2 must be at most 2048 bytes");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) % 16)
     return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");

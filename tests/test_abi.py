@@ -64,6 +64,8 @@ INV, UNS, OVF = 1, 2, 5
     ("gatv2 H=0", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 0, 32, ctypes.c_float(0.2), P(16), None, None, None), INV),
     ("gatv2 too wide", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), None, None, None), UNS),
     ("gatv2 D*2 % 16", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 12, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gatv2 H*D overflow", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2**28, 16, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gt H*D overflow", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), 0, P(16), None, None, None), UNS),
     ("gt bad mode", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), 5, P(16), None, None, None), INV),
     ("gt block16 f32", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 0, 8, 64, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
     ("gt block16 D=48", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2, 48, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
@@ -100,6 +102,8 @@ INV, UNS, OVF = 1, 2, 5
     ("b16 bwd non-square", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), INV),
     ("b16 bwd D=128", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2, 128, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("b16 bwd null dk", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), None, P(16), None, None), INV),
+    ("b16 bwd H*D overflow", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2**27, 32, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd H*D overflow", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("b16 bwd misaligned", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(24), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
