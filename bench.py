@@ -815,6 +815,17 @@ WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, 
 
 # ---------------------------------------------------------------------------
 
+def _cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), for the oracle baseline."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _keep_pool_memory(device: int = 0) -> bool:
     """Raise the release threshold of the device's default stream-ordered
     memory pool, so memory the library frees (per-call temporaries of plan
@@ -884,6 +895,9 @@ def main():
     wall = time.perf_counter() - t0
 
     per_op_ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    per_op_stats = {k: {"mean": round(float(np.mean(t)), 4), "median": round(float(np.median(t)), 4),
+                        "min": round(float(np.min(t)), 4)}
+                    for k, t in ((k, [a.elapsed_time(b) for a, b in v]) for k, v in ev.items())}
     separate_ms = None
     if w.get("separate"):
         separate_ms = {}
@@ -927,6 +941,7 @@ def main():
         "hbm_gbps_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9,
         "hbm_frac_algorithmic": bytes_alg / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "per_op_ms": {k: round(v, 4) for k, v in per_op_ms.items()},
+        "per_op_stats_ms": per_op_stats,
         "separate_launch_ms": separate_ms,
         "step_wall_ms": wall_step_ms,
         "pool_memory_kept": pool_kept,
@@ -934,6 +949,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
     }
+    if traffic:
+        # calibrated FETCH_SIZE + WRITE_SIZE bytes of the dominant launch over its time
+        out["hbm_counter"] = {"bytes": traffic, "gbps": traffic / (dom_ms * 1e-3) / 1e9,
+                              "frac": traffic / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     if w.get("compulsory"):
         # each input and output tensor once: the floor if every gather hit in cache
         c = w["compulsory"]
@@ -944,6 +963,8 @@ def main():
         out["results"] = w["post"](per_op_ms)
     if not args.no_cpu:
         out["cpu_baseline"] = w["cpu"](args.cpu_budget)
+        if out["cpu_baseline"]:
+            out["cpu_baseline"]["cpu_model"] = _cpu_model()
         if w.get("cpu_1thread") and out["cpu_baseline"]:
             import oracle
             all_threads = oracle.num_threads()
