@@ -271,6 +271,17 @@ def test_gt_block16_backward_cluster(H, D, tau):
     assert same, "not deterministic"
 
 
+@pytest.mark.parametrize("p_in,H,D", [(0.1, 4, 64), (0.05, 16, 32), (0.9, 2, 64)])
+def test_gt_block16_backward_cluster_densities(p_in, H, D):
+    """Sparse clusters (most tiles below the threshold: long residual rows,
+    partly filled tiles), many heads at D = 32, and nearly full tiles."""
+    rp, ci = gen.cluster(0x5EED0362, 64 * 41, 64, p_in, 0.03, self_loops=True)
+    errs, same, st = _b16_bwd_case(rp, ci, H, D, 8, 0x6300)
+    assert st["wsb_dense_tiles"] > 0 and st["wsb_residual_edges"] > 0, st
+    assert max(errs) <= B16_BWD_TOL, errs
+    assert same
+
+
 def test_gt_block16_backward_rmat_partial_windows():
     """R-MAT with empty rows, hub rows and a last window of 3 rows: most
     entries go through the residual CSRs of A and A^T."""
