@@ -104,7 +104,8 @@ int debug_validate(const gnn_csr* c, hipStream_t s) {
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e == hipSuccess) e = hipMemcpy(h, d, sizeof(h), hipMemcpyDeviceToHost);
-  hipFree(d);
+  const hipError_t ef = hipFree(d);
+  if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return fail(GNN_ERR_DEVICE, std::string("CSR check: ") + hipGetErrorString(e));
   if (h[1]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr[0] != 0 or row_ptr[n_rows] != nnz");
   if (h[0]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr decreases");
@@ -177,10 +178,13 @@ int gnn_plan_destroy(gnn_plan* p) {
   if (p->n_allocs > 0 || p->ws) {
     if (hipStreamSynchronize(p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "plan stream sync failed");
   }
-  for (int k = 0; k < p->n_allocs; ++k) hipFree(p->allocs[k]);
-  if (p->ws) hipFree(p->ws);
-  if (p->delta) hipFree(p->delta);
-  if (p->dob) hipFree(p->dob);
+  auto release = [&rc](void* ptr) {
+    if (ptr && hipFree(ptr) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "hipFree of a plan buffer failed");
+  };
+  for (int k = 0; k < p->n_allocs; ++k) release(p->allocs[k]);
+  release(p->ws);
+  release(p->delta);
+  release(p->dob);
   delete p;
   return rc;
 }
