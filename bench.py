@@ -855,7 +855,7 @@ def main():
     ap.add_argument("--ops", default=None, help="run only the workload's ops whose names match this glob")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1 (the sharded design is described, not built)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
