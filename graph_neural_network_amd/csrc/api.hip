@@ -439,7 +439,8 @@ int gnn_gt_backward_block16(const gnn_csr* csr, const void* q, const void* k, co
   if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
   if ((!q || !out || !lse || !dout || !dq || !k || !v || !dk || !dv) && csr->n_rows > 0)
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
-  if (D != 32 && D != 64) return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs bf16 and D in {32, 64}");
+  if (D != 32 && D != 64 && D != 128)
+    return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs bf16 and D in {32, 64, 128}");
   if ((int64_t)H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "H*D*2 must be at most 2048 bytes");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) % 16)

@@ -396,7 +396,7 @@ __device__ __forceinline__ void dst_walk(const B16BwdParams& p, const Tiles& T, 
 // (waves_per_eu: without it the compiler splits the registers into VGPRs
 // and AGPRs and loses a wave of occupancy)
 template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_gt_b16_bwd_dst(
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void k_gt_b16_bwd_dst(
     B16BwdParams p) {
   __shared__ uint16_t s_k[NWAVE][16 * ldk<D>()];
   __shared__ __align__(16) float s_o[NWAVE][16 * ldo<D>()];
@@ -558,10 +558,11 @@ __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, 
   }
 }
 
-// (three waves per SIMD at D = 64 cost three spilled registers, reloaded once
-// per head, and are faster than two)
+// (D <= 64: three waves per SIMD, a few registers spilled and reloaded once
+// per head, faster than two; D = 128: two waves with some spills, faster than
+// one without)
 template <int D, int NWAVE>
-__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(3))) void k_gt_b16_bwd_src(
+__global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2))) void k_gt_b16_bwd_src(
     B16BwdParams p) {
   constexpr int BUF = 2 * 16 * ldk<D>() * 2 > 16 * ldo<D>() * 4 ? 2 * 16 * ldk<D>() * 2 : 16 * ldo<D>() * 4;
   __shared__ __align__(16) char s_buf[NWAVE][BUF];
@@ -591,7 +592,8 @@ void fill_layout(B16BwdParams& p, const gnn_plan* pl) {
 int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const void* v, int32_t H, int32_t D,
                                float scale, const float* out, const float* lse, const float* dout, float* dq,
                                float* dk, float* dv, hipStream_t s) {
-  if (D != 32 && D != 64) return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs D in {32, 64}");
+  if (D != 32 && D != 64 && D != 128)
+    return fail(GNN_ERR_UNSUPPORTED, "block-sparse GT backward needs D in {32, 64, 128}");
   GNN_TRY(plan_transpose(pl, s));
   GNN_TRY(plan_transpose_wsb(pl, s));
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
@@ -613,7 +615,8 @@ int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const
   if (pl->wsb.n_windows > 0) {
     const dim3 grid((unsigned)pl->wsb.n_windows);
     if (D == 32) hipLaunchKernelGGL((k_gt_b16_bwd_dst<32, NW>), grid, dim3(NW * 64), 0, s, p);
-    else hipLaunchKernelGGL((k_gt_b16_bwd_dst<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    else if (D == 64) hipLaunchKernelGGL((k_gt_b16_bwd_dst<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((k_gt_b16_bwd_dst<128, NW>), grid, dim3(NW * 64), 0, s, p);
     GNN_LAUNCH_CHECK("block-sparse GT backward (destinations)");
   }
   const gnn_plan* tp = pl->tplan;
@@ -623,7 +626,8 @@ int launch_gt_backward_block16(gnn_plan* pl, const void* q, const void* k, const
   if (tp->wsb.n_windows > 0) {
     const dim3 grid((unsigned)tp->wsb.n_windows);
     if (D == 32) hipLaunchKernelGGL((k_gt_b16_bwd_src<32, NW>), grid, dim3(NW * 64), 0, s, p);
-    else hipLaunchKernelGGL((k_gt_b16_bwd_src<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    else if (D == 64) hipLaunchKernelGGL((k_gt_b16_bwd_src<64, NW>), grid, dim3(NW * 64), 0, s, p);
+    else hipLaunchKernelGGL((k_gt_b16_bwd_src<128, NW>), grid, dim3(NW * 64), 0, s, p);
     GNN_LAUNCH_CHECK("block-sparse GT backward (sources)");
   }
   return GNN_OK;

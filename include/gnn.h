@@ -324,7 +324,7 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
  * dO, alpha and dS are rounded to bf16 for the matrix cores, as alpha is in
  * the block-sparse forward: results are within the attention tolerance of
  * the exact gradients, not to fp32 rounding.  Square CSR, bf16 q, k, v only,
- * D in {32, 64}, H*D*2 <= 2048; other arguments as in gnn_gt_backward.  The
+ * D in {32, 64, 128}, H*D*2 <= 2048; other arguments as in gnn_gt_backward.  The
  * plan must carry WSB tiles (NULL: a transient one is built); the tiles of
  * A^T are built on its first block-sparse backward call.  The plan keeps,
  * between the two walks, Delta [n_rows, H] float32 and dO rounded to bf16

@@ -100,7 +100,7 @@ INV, UNS, OVF = 1, 2, 5
     ("dot vec16 misaligned", lambda: call("gnn_dot_aggr", ctypes.byref(fake_csr()), P(20), 4, 4, 0, 1, P(16), None, None), INV),
     ("dot edge values", lambda: call("gnn_dot_aggr", ctypes.byref(gnn._Csr(4, 4, 4, 0x1000, 0x2000, 0x3000)), P(16), 4, 4, 0, 0, P(16), None, None), INV),
     ("b16 bwd non-square", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), INV),
-    ("b16 bwd D=128", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2, 128, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("b16 bwd D=96", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2, 96, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("b16 bwd null dk", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), None, P(16), None, None), INV),
     ("b16 bwd H*D overflow", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2**27, 32, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("gt bwd H*D overflow", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),

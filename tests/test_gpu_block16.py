@@ -260,7 +260,7 @@ def _b16_bwd_case(rp, ci, H, D, tau, seed):
     return errs, same, gnn.gnn_plan_stats(plan)
 
 
-@pytest.mark.parametrize("H,D", [(8, 64), (2, 32), (1, 64), (3, 32)])
+@pytest.mark.parametrize("H,D", [(8, 64), (2, 32), (1, 64), (3, 32), (8, 128), (2, 128)])
 @pytest.mark.parametrize("tau", [1, 8, 10**6])
 def test_gt_block16_backward_cluster(H, D, tau):
     rp, ci = gen.cluster(0x5EED0360, 64 * 25, 64, 0.4, 0.02, self_loops=True)
