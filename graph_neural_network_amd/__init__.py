@@ -120,6 +120,38 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+F32 = (torch.float32,)
+FEAT = (torch.float32, torch.bfloat16)
+
+
+def _need(t, name: str, rows: int, tail: tuple, dtypes: tuple, rows_strided: bool = False):
+    """Check a tensor argument before its pointer reaches the library, which
+    reads or writes rows [0, rows) at the layout it is told: at least `rows`
+    rows, trailing sizes `tail` (None: any), a dtype of `dtypes`; contiguous,
+    or (rows_strided) unit stride along the last dimension only.  The device
+    is checked apart (_gpu), after every argument's shape."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
+    if t.dim() != 1 + len(tail) or t.shape[0] < rows or any(b is not None and a != b
+                                                            for a, b in zip(t.shape[1:], tail)):
+        want = "x".join(str(x) for x in (f">={rows}",) + tuple("*" if b is None else b for b in tail))
+        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected [{want}]")
+    if rows_strided:
+        if t.dim() > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must have unit stride along its last dimension")
+    elif not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gpu(**tensors):
+    """Every given tensor (None skipped) must live on a GPU."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return DTYPE["f32"]
@@ -136,6 +168,9 @@ class Csr:
         for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
             if t.dtype != torch.int32 or not t.is_contiguous():
                 raise TypeError(f"{name} must be a contiguous int32 tensor")
+        if edge_val is not None and (edge_val.dtype != torch.float32 or not edge_val.is_contiguous()
+                                     or edge_val.numel() != col_idx.numel()):
+            raise TypeError("edge_val must be a contiguous float32 tensor with one value per entry")
         self.row_ptr, self.col_idx, self.edge_val = row_ptr, col_idx, edge_val
         self.n_rows = row_ptr.numel() - 1
         self.n_cols = self.n_rows if n_cols is None else int(n_cols)
@@ -208,9 +243,14 @@ def _plan_h(plan):
 
 def gnn_spmm(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | None = None,
              plan: Plan | None = None, stream=None) -> torch.Tensor:
+    _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
     F = X.shape[1]
     if Y is None:
         Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    _need(Y, "Y", csr.n_rows, (None,), F32, rows_strided=True)
+    if Y.shape[1] < F:
+        raise ValueError("Y must have at least as many columns as X")
+    _gpu(X=X, Y=Y)
     _check(load_library().gnn_spmm(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y),
                                    Y.stride(0), NORM[norm], _plan_h(plan), _stream(stream)),
            "gnn_spmm")
@@ -220,9 +260,14 @@ def gnn_spmm(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | No
 def gnn_spmm_block16(csr: Csr, X: torch.Tensor, norm: str = "none", Y: torch.Tensor | None = None,
                      plan: Plan | None = None, stream=None) -> torch.Tensor:
     """Y = A_norm X on the plan's 16 x 16 block-sparse tiles (plan built with build_wsb)."""
+    _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
     F = X.shape[1]
     if Y is None:
         Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    _need(Y, "Y", csr.n_rows, (None,), F32, rows_strided=True)
+    if Y.shape[1] < F:
+        raise ValueError("Y must have at least as many columns as X")
+    _gpu(X=X, Y=Y)
     _check(load_library().gnn_spmm_block16(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(Y), Y.stride(0),
                                            NORM[norm], _plan_h(plan), _stream(stream)), "gnn_spmm_block16")
     return Y
@@ -232,11 +277,12 @@ def gnn_dot_aggr(csr: Csr, X: torch.Tensor, map: str = "feature", load: str = "s
                  y: torch.Tensor | None = None, plan: Plan | None = None, stream=None) -> torch.Tensor:
     """dot-aggr micro-benchmark: y[i] = sum over row i's sources j of <X[i], X[j]> (float32 X);
     map "feature" | "neighbor", load "scalar" (4-byte) | "vec16" (16-byte per lane)."""
+    _need(X, "X", max(csr.n_rows, csr.n_cols), (None,), F32, rows_strided=True)
     D = X.shape[1]
     if y is None:
         y = torch.empty(csr.n_rows, dtype=torch.float32, device=X.device)
-    if X.dtype != torch.float32:
-        raise TypeError("gnn_dot_aggr takes float32 features")
+    _need(y, "y", csr.n_rows, (), F32)
+    _gpu(X=X, y=y)
     _check(load_library().gnn_dot_aggr(csr.ref, _ptr(X), D, X.stride(0), DOT_MAP[map], DOT_LOAD[load], _ptr(y),
                                        _plan_h(plan), _stream(stream)), "gnn_dot_aggr")
     return y
@@ -245,13 +291,20 @@ def gnn_dot_aggr(csr: Csr, X: torch.Tensor, map: str = "feature", load: str = "s
 def gnn_reduce(csr: Csr, X: torch.Tensor, op: str = "sum", Y: torch.Tensor | None = None,
                arg: torch.Tensor | bool | None = None, plan: Plan | None = None, stream=None):
     """Returns (Y, arg); arg=True allocates the source-index output (max / min)."""
+    _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
     F = X.shape[1]
     if Y is None:
         Y = torch.empty((csr.n_rows, F), dtype=torch.float32, device=X.device)
+    _need(Y, "Y", csr.n_rows, (None,), F32, rows_strided=True)
+    if Y.shape[1] < F:
+        raise ValueError("Y must have at least as many columns as X")
     if arg is True:
         arg = torch.empty((csr.n_rows, F), dtype=torch.int32, device=X.device)
     elif arg is False:
         arg = None
+    if arg is not None:
+        _need(arg, "arg", csr.n_rows, (F,), (torch.int32,))
+    _gpu(X=X, Y=Y, arg=arg)
     _check(load_library().gnn_reduce(csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0),
                                      REDUCE_OP[op], _ptr(Y), Y.stride(0), _ptr(arg),
                                      _plan_h(plan), _stream(stream)), "gnn_reduce")
@@ -262,6 +315,7 @@ def gnn_reduce_multi(csr: Csr, X: torch.Tensor, ops=("sum", "mean", "max", "min"
                      out: dict | None = None, plan: Plan | None = None, stream=None) -> dict:
     """One pass computing the requested reductions; returns {name: tensor} with
     keys among sum, mean, max, min, argmax, argmin (indices only with args)."""
+    _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
     F = X.shape[1]
     out = dict(out or {})
     for op in ops:
@@ -271,9 +325,17 @@ def gnn_reduce_multi(csr: Csr, X: torch.Tensor, ops=("sum", "mean", "max", "min"
         for op in ("max", "min"):
             if op in ops and "arg" + op not in out:
                 out["arg" + op] = torch.empty((csr.n_rows, F), dtype=torch.int32, device=X.device)
+    for k, o in out.items():
+        if k.startswith("arg"):
+            _need(o, k, csr.n_rows, (F,), (torch.int32,))
+        else:
+            _need(o, k, csr.n_rows, (None,), F32, rows_strided=True)
+            if o.shape[1] < F:
+                raise ValueError(f"{k} must have at least as many columns as X")
     lds = {o.stride(0) for k, o in out.items() if not k.startswith("arg")}
     if len(lds) != 1:
         raise ValueError("value outputs must share one row stride")
+    _gpu(X=X, **out)
     _check(load_library().gnn_reduce_multi(
         csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(out.get("sum")), _ptr(out.get("mean")),
         _ptr(out.get("max")), _ptr(out.get("argmax")), _ptr(out.get("min")), _ptr(out.get("argmin")),
@@ -285,13 +347,20 @@ def gnn_gatv2_fused(csr: Csr, xl: torch.Tensor, xr: torch.Tensor, att: torch.Ten
                     neg_slope: float = 0.2, out: torch.Tensor | None = None,
                     lse: torch.Tensor | bool | None = True, plan: Plan | None = None, stream=None):
     """xl [n_rows, H, D], xr [n_cols, H, D] (bf16 or f32), att [H, D] f32 -> (out, lse)."""
+    _need(xl, "xl", csr.n_rows, (None, None), FEAT)
     H, D = xl.shape[1], xl.shape[2]
+    _need(xr, "xr", csr.n_cols, (H, D), (xl.dtype,))
+    _need(att, "att", H, (D,), F32)
     if out is None:
         out = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=xl.device)
     if lse is True:
         lse = torch.empty((csr.n_rows, H), dtype=torch.float32, device=xl.device)
     elif lse is False:
         lse = None
+    _need(out, "out", csr.n_rows, (H, D), F32)
+    if lse is not None:
+        _need(lse, "lse", csr.n_rows, (H,), F32)
+    _gpu(xl=xl, xr=xr, att=att, out=out, lse=lse)
     _check(load_library().gnn_gatv2_fused(csr.ref, _ptr(xl), _ptr(xr), _dtype_code(xl), _ptr(att),
                                           H, D, float(neg_slope), _ptr(out), _ptr(lse),
                                           _plan_h(plan), _stream(stream)), "gnn_gatv2_fused")
@@ -302,13 +371,20 @@ def gnn_gt_fused(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
                  mode: str = "csr", out: torch.Tensor | None = None,
                  lse: torch.Tensor | bool | None = True, plan: Plan | None = None, stream=None):
     """q [n_rows, H, D], k, v [n_cols, H, D] -> (out [n_rows, H, D] f32, lse [n_rows, H])."""
+    _need(q, "q", csr.n_rows, (None, None), FEAT)
     H, D = q.shape[1], q.shape[2]
+    _need(k, "k", csr.n_cols, (H, D), (q.dtype,))
+    _need(v, "v", csr.n_cols, (H, D), (q.dtype,))
     if out is None:
         out = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
     if lse is True:
         lse = torch.empty((csr.n_rows, H), dtype=torch.float32, device=q.device)
     elif lse is False:
         lse = None
+    _need(out, "out", csr.n_rows, (H, D), F32)
+    if lse is not None:
+        _need(lse, "lse", csr.n_rows, (H,), F32)
+    _gpu(q=q, k=k, v=v, out=out, lse=lse)
     _check(load_library().gnn_gt_fused(csr.ref, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), H, D,
                                        float(scale), GT_MODE[mode], _ptr(out), _ptr(lse),
                                        _plan_h(plan), _stream(stream)), "gnn_gt_fused")
@@ -318,9 +394,14 @@ def gnn_gt_fused(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
 def gnn_spmm_backward(csr: Csr, dY: torch.Tensor, norm: str = "none", dX: torch.Tensor | None = None,
                       plan: Plan | None = None, stream=None) -> torch.Tensor:
     """dX [n_cols, F] = A_norm^T dY (float32)."""
+    _need(dY, "dY", csr.n_rows, (None,), F32, rows_strided=True)
     F = dY.shape[1]
     if dX is None:
         dX = torch.empty((csr.n_cols, F), dtype=torch.float32, device=dY.device)
+    _need(dX, "dX", csr.n_cols, (None,), F32, rows_strided=True)
+    if dX.shape[1] < F:
+        raise ValueError("dX must have at least as many columns as dY")
+    _gpu(dY=dY, dX=dX)
     _check(load_library().gnn_spmm_backward(csr.ref, _ptr(dY), F, dY.stride(0), _ptr(dX), dX.stride(0),
                                             NORM[norm], _plan_h(plan), _stream(stream)), "gnn_spmm_backward")
     return dX
@@ -329,9 +410,16 @@ def gnn_spmm_backward(csr: Csr, dY: torch.Tensor, norm: str = "none", dX: torch.
 def gnn_reduce_backward(csr: Csr, dY: torch.Tensor, op: str = "sum", arg: torch.Tensor | None = None,
                         dX: torch.Tensor | None = None, plan: Plan | None = None, stream=None) -> torch.Tensor:
     """dX [n_cols, F] (float32); arg: the forward's source indices (max / min)."""
+    _need(dY, "dY", csr.n_rows, (None,), F32, rows_strided=True)
     F = dY.shape[1]
     if dX is None:
         dX = torch.empty((csr.n_cols, F), dtype=torch.float32, device=dY.device)
+    _need(dX, "dX", csr.n_cols, (None,), F32, rows_strided=True)
+    if dX.shape[1] < F:
+        raise ValueError("dX must have at least as many columns as dY")
+    if arg is not None:
+        _need(arg, "arg", csr.n_rows, (F,), (torch.int32,))
+    _gpu(dY=dY, dX=dX, arg=arg)
     _check(load_library().gnn_reduce_backward(csr.ref, REDUCE_OP[op], _ptr(dY), F, dY.stride(0), _ptr(arg),
                                               _ptr(dX), dX.stride(0), _plan_h(plan), _stream(stream)),
            "gnn_reduce_backward")
@@ -342,10 +430,17 @@ def gnn_gatv2_backward(csr: Csr, xl: torch.Tensor, xr: torch.Tensor, att: torch.
                        lse: torch.Tensor, dout: torch.Tensor, neg_slope: float = 0.2, plan: Plan | None = None,
                        stream=None):
     """-> (dxl [n_rows, H, D], dxr [n_cols, H, D], datt [H, D]), float32."""
+    _need(xl, "xl", csr.n_rows, (None, None), FEAT)
     H, D = xl.shape[1], xl.shape[2]
+    _need(xr, "xr", csr.n_cols, (H, D), (xl.dtype,))
+    _need(att, "att", H, (D,), F32)
+    for name, t in (("out", out), ("dout", dout)):
+        _need(t, name, csr.n_rows, (H, D), F32)
+    _need(lse, "lse", csr.n_rows, (H,), F32)
     dxl = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=xl.device)
     dxr = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=xl.device)
     datt = torch.empty((H, D), dtype=torch.float32, device=xl.device)
+    _gpu(xl=xl, xr=xr, att=att, out=out, lse=lse, dout=dout)
     _check(load_library().gnn_gatv2_backward(csr.ref, _ptr(xl), _ptr(xr), _dtype_code(xl), _ptr(att), H, D,
                                              float(neg_slope), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dxl),
                                              _ptr(dxr), _ptr(datt), _plan_h(plan), _stream(stream)),
@@ -357,10 +452,17 @@ def gnn_gt_backward(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     lse: torch.Tensor, dout: torch.Tensor, scale: float = 0.0, plan: Plan | None = None,
                     stream=None):
     """-> (dq [n_rows, H, D], dk, dv [n_cols, H, D]), float32."""
+    _need(q, "q", csr.n_rows, (None, None), FEAT)
     H, D = q.shape[1], q.shape[2]
+    _need(k, "k", csr.n_cols, (H, D), (q.dtype,))
+    _need(v, "v", csr.n_cols, (H, D), (q.dtype,))
+    for name, t in (("out", out), ("dout", dout)):
+        _need(t, name, csr.n_rows, (H, D), F32)
+    _need(lse, "lse", csr.n_rows, (H,), F32)
     dq = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    _gpu(q=q, k=k, v=v, out=out, lse=lse, dout=dout)
     _check(load_library().gnn_gt_backward(csr.ref, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), H, D, float(scale),
                                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                           _plan_h(plan), _stream(stream)), "gnn_gt_backward")
@@ -372,12 +474,17 @@ def gnn_gt_backward_block16(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch
                             stream=None):
     """Block-sparse (bf16 matrix cores) Graph Transformer backward; bf16 q, k, v.
     -> (dq, dk, dv), float32 [n, H, D]."""
+    _need(q, "q", csr.n_rows, (None, None), (torch.bfloat16,))
     H, D = q.shape[1], q.shape[2]
-    if q.dtype != torch.bfloat16:
-        raise TypeError("the block-sparse backward takes bf16 q, k, v")
+    _need(k, "k", csr.n_cols, (H, D), (torch.bfloat16,))
+    _need(v, "v", csr.n_cols, (H, D), (torch.bfloat16,))
+    for name, t in (("out", out), ("dout", dout)):
+        _need(t, name, csr.n_rows, (H, D), F32)
+    _need(lse, "lse", csr.n_rows, (H,), F32)
     dq = torch.empty((csr.n_rows, H, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((csr.n_cols, H, D), dtype=torch.float32, device=q.device)
+    _gpu(q=q, k=k, v=v, out=out, lse=lse, dout=dout)
     _check(load_library().gnn_gt_backward_block16(csr.ref, _ptr(q), _ptr(k), _ptr(v), H, D, float(scale),
                                                   _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                                                   _plan_h(plan), _stream(stream)), "gnn_gt_backward_block16")
