@@ -134,12 +134,17 @@ def _need(t, name: str, rows: int, tail: tuple, dtypes: tuple, rows_strided: boo
         raise TypeError(f"{name} must be a tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}; expected one of {dtypes}")
-    if t.dim() != 1 + len(tail) or t.shape[0] < rows or any(b is not None and a != b
-                                                            for a, b in zip(t.shape[1:], tail)):
+    shape = t.shape
+    ok = len(shape) == 1 + len(tail) and shape[0] >= rows
+    if ok:
+        for i, b in enumerate(tail):
+            if b is not None and shape[i + 1] != b:
+                ok = False
+    if not ok:
         want = "x".join(str(x) for x in (f">={rows}",) + tuple("*" if b is None else b for b in tail))
-        raise ValueError(f"{name} has shape {tuple(t.shape)}; expected [{want}]")
+        raise ValueError(f"{name} has shape {tuple(shape)}; expected [{want}]")
     if rows_strided:
-        if t.dim() > 1 and t.stride(-1) != 1:
+        if len(shape) > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name} must have unit stride along its last dimension")
     elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -148,7 +153,7 @@ def _need(t, name: str, rows: int, tail: tuple, dtypes: tuple, rows_strided: boo
 def _gpu(**tensors):
     """Every given tensor (None skipped) must live on a GPU."""
     for name, t in tensors.items():
-        if t is not None and t.device.type != "cuda":
+        if t is not None and not t.is_cuda:
             raise ValueError(f"{name} must be a GPU tensor")
 
 
