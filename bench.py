@@ -539,7 +539,7 @@ def wl_spmm_b16(args):
            "note": "per_op_ms.csr is gnn_spmm on the same input"}
     comp = (n * rb + n * 4 * F + 4 * (n + 1) + 4 * n + 8 * st["wsb_windows"] + 48 * st["wsb_blocks"]
             + 4 * st["wsb_dense_tiles"] + 4 * (n + 1) + 4 * st["wsb_residual_edges"])
-    return {"ops": ops, "dominant": "block16", "kernel": "k_spmm_b16<unsigned short>", "config": cfg,
+    return {"ops": ops, "dominant": "block16", "kernel": "k_spmm_b16<unsigned short, false>", "config": cfg,
             "dtype": "bf16", "cpu": cpu, "compulsory": comp, "keep": (w, csr, plan, X, Y)}
 
 
