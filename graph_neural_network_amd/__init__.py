@@ -30,13 +30,14 @@ GT_MODE = {"csr": 0, "block16": 1, "auto": 2}
 REORDER = {"degree": 0, "rcm": 1}
 DOT_MAP = {"feature": 0, "neighbor": 1}
 DOT_LOAD = {"scalar": 0, "vec16": 1}
+TUNE_OP = {"spmm": 0, "sum": 1, "multi": 2}
 
 # every symbol include/gnn.h declares
 EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_wsb_export",
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
-           "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16")
+           "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune")
 
 
 class GnnError(RuntimeError):
@@ -92,6 +93,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_gt_backward": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_dot_aggr": [P(_Csr), vp, i32, i64, ci, ci, vp, vp, vp],
         "gnn_gt_backward_block16": [P(_Csr), vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
+        "gnn_plan_autotune": [P(_Csr), vp, ci, i32, i64, ci, i32, P(_PlanOpts), P(f32), P(f32), vp],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -221,6 +223,22 @@ def gnn_plan_create(csr: Csr, heavy_quantile: float = 0.0, light_max_deg: int = 
 
 def gnn_plan_destroy(plan: Plan):
     plan.destroy()
+
+
+def gnn_plan_autotune(csr: Csr, X: torch.Tensor, op: str = "multi", reps: int = 5, stream=None) -> dict:
+    """Time the plan-option candidates for one aggregation on this graph and
+    features; -> {"opts": {heavy_quantile, light_max_deg, chunk_edges},
+    "best_ms": ..., "default_ms": ...}.  Pass opts to gnn_plan_create."""
+    _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
+    _gpu(X=X)
+    o = _PlanOpts()
+    best, dflt = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    _check(load_library().gnn_plan_autotune(csr.ref, _ptr(X), _dtype_code(X), X.shape[1], X.stride(0),
+                                            TUNE_OP[op], int(reps), ctypes.byref(o), ctypes.byref(best),
+                                            ctypes.byref(dflt), _stream(stream)), "gnn_plan_autotune")
+    return {"opts": {"heavy_quantile": round(o.heavy_quantile, 6), "light_max_deg": o.light_max_deg,
+                     "chunk_edges": o.chunk_edges},
+            "best_ms": best.value, "default_ms": dflt.value}
 
 
 def gnn_plan_stats(plan: Plan) -> dict:

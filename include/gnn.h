@@ -152,6 +152,25 @@ int gnn_plan_destroy(gnn_plan* plan);
  * [8] = residual CSR edges.  Host memory, n >= 9. */
 int gnn_plan_stats(const gnn_plan* plan, int64_t* counts, int32_t n);
 
+/* Operation an autotuning run times. */
+typedef enum { GNN_TUNE_SPMM = 0, GNN_TUNE_SUM = 1, GNN_TUNE_MULTI = 2 } gnn_tune_op;
+
+/* Measured choice of a plan's degree-binning knobs for one aggregation
+ * (appendix D.1 "degree threshold and autotuning parameters"): for every
+ * candidate of heavy_quantile in {0.99, 0.999, -1 (no split)} x light_max_deg
+ * in {16, 32} x chunk_edges in {256, 1024} (the defaults are one candidate),
+ * build a plan, run the operation once untimed and `reps` times between HIP
+ * events on `stream`, and keep the candidate of least mean time.  op:
+ * GNN_TUNE_SPMM (gnn_spmm, norm NONE), GNN_TUNE_SUM (gnn_reduce SUM) or
+ * GNN_TUNE_MULTI (gnn_reduce_multi with all six outputs).  X as in those
+ * calls; reps in [1, 1000].  Outputs (host): *best receives the winning
+ * options (other fields zero), *best_ms its mean time, *default_ms (nullable)
+ * the defaults' mean time.  Allocates its output buffers and plans, frees
+ * them, and synchronises `stream`.
+ * Errors: INVALID_VALUE, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
+int gnn_plan_autotune(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, gnn_tune_op op,
+                      int32_t reps, gnn_plan_opts* best, float* best_ms, float* default_ms, void* stream);
+
 /* Copy the plan's WSB layout (appendix D.3: windows of 16 rows, sorted
  * distinct source columns cut into blocks of 8 zero-padded columns, a 16x8
  * occupancy bitmap as two 64-bit words with bit r*8+c) into caller DEVICE

@@ -110,6 +110,16 @@ INV, UNS, OVF = 1, 2, 5
                                    ctypes.byref(gnn._PlanOpts(2.0, 0, 0, 0, 0)), None, ctypes.byref(P())), INV),
     ("plan wsb non-square", lambda: call("gnn_plan_create", ctypes.byref(fake_csr(n_cols=9)),
                                          ctypes.byref(gnn._PlanOpts(0, 0, 0, 1, 0)), None, ctypes.byref(P())), INV),
+    ("autotune null csr", lambda: call("gnn_plan_autotune", None, P(16), 0, 4, 4, 0, 3, ctypes.byref(gnn._PlanOpts()),
+                                       ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune reps=0", lambda: call("gnn_plan_autotune", ctypes.byref(fake_csr()), P(16), 0, 4, 4, 0, 0,
+                                     ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune bad op", lambda: call("gnn_plan_autotune", ctypes.byref(fake_csr()), P(16), 0, 4, 4, 7, 3,
+                                     ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune null best", lambda: call("gnn_plan_autotune", ctypes.byref(fake_csr()), P(16), 0, 4, 4, 0, 3, None,
+                                        ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune ldx<F", lambda: call("gnn_plan_autotune", ctypes.byref(fake_csr()), P(16), 0, 8, 4, 0, 3,
+                                    ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_float()), None, None), INV),
     ("stats null", lambda: call("gnn_plan_stats", None, None, 9), INV),
     ("permute bad F", lambda: call("gnn_permute_rows", P(8), 4, P(8), 0, 0, 4, P(8), 4, None), INV),
     ("copy negative", lambda: call("gnn_copy_bytes", P(8), P(8), -1, None), INV),

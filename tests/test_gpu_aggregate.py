@@ -389,3 +389,28 @@ def test_reduce_multi_rmat1m_full(cfg_reduce):
     for op in ("sum", "mean", "max", "min"):
         check_reduce(w.row_ptr, w.col_idx, X, host(out[op]),
                      host(out["arg" + op]) if op in ("max", "min") else None, op, rows)
+
+
+@pytest.mark.parametrize("op", ["spmm", "sum", "multi"])
+def test_plan_autotune(rmat_small, op):
+    """The autotuner returns one of its candidates, no slower than the defaults
+    it timed beside them, and a plan built with its choice computes the same
+    results as the oracle."""
+    rp, ci = rmat_small
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    Xh = gen.gauss_f32(31, (n, 64))
+    Xd = dev(Xh)
+    res = gnn.gnn_plan_autotune(csr, Xd, op, reps=3)
+    o = res["opts"]
+    assert o["heavy_quantile"] in (0.99, 0.999, -1.0) and o["light_max_deg"] in (16, 32)
+    assert o["chunk_edges"] in (256, 1024)
+    assert 0 < res["best_ms"] <= res["default_ms"]
+    plan = gnn.gnn_plan_create(csr, **o)
+    if op == "spmm":
+        ref, mag = oracle.spmm(rp, ci, Xh, "none")
+        assert scaled_err(host(gnn.gnn_spmm(csr, Xd, plan=plan)), ref, mag) <= TOL
+    else:
+        out = gnn.gnn_reduce_multi(csr, Xd, plan=plan)
+        for r in ("sum", "max"):
+            check_reduce(rp, ci, Xh, host(out[r]), host(out["argmax"]) if r == "max" else None, r)
