@@ -44,16 +44,16 @@ SOURCES = {
     "gt_csr": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
     "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
     "copy": ("gnn_internal.h", "util.hip"),
-    "plan_cfg2": _COMMON,
-    "wsb_cfg4": _COMMON + ("wsb.hip", "sort.hip"),
-    "reorder_cfg5": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
-    "spmm_bwd_cfg5": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
-    "reduce_bwd_cfg2": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
-    "gatv2_bwd_cfg3": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
-    "gt_bwd_cfg4": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
-    "spmm_b16_cfg4": _COMMON + ("spmm_block16.hip", "wsb.hip", "sort.hip"),
-    "gt_bwd_b16_cfg4": _COMMON + ("gt_block16_bwd.hip", "wsb.hip", "sort.hip", "transpose.hip"),
-    "dotaggr_cfg2": _COMMON + ("dot_aggr.hip",),
+    "plan_rmat1m": _COMMON,
+    "wsb_cluster512k": _COMMON + ("wsb.hip", "sort.hip"),
+    "reorder_rmat16m": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
+    "spmm_bwd_rmat16m": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
+    "reduce_bwd_rmat1m": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
+    "gatv2_bwd": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
+    "gt_bwd_csr": _COMMON + ("attention_bwd.hip", "att_common.h", "transpose.hip", "sort.hip"),
+    "spmm_block16": _COMMON + ("spmm_block16.hip", "wsb.hip", "sort.hip"),
+    "gt_bwd_block16": _COMMON + ("gt_block16_bwd.hip", "wsb.hip", "sort.hip", "transpose.hip"),
+    "dotaggr": _COMMON + ("dot_aggr.hip",),
 }
 
 
@@ -109,7 +109,7 @@ class Op:
         self.name, self.fn, self.edges, self.bytes_alg, self.warm = name, fn, edges, bytes_alg, warm
 
 
-TUNED_CFG2 = {"heavy_quantile": 0.999, "light_max_deg": 32, "chunk_edges": 1024}
+TUNED_RMAT1M = {"heavy_quantile": 0.999, "light_max_deg": 32, "chunk_edges": 1024}
 
 
 def wl_reduce_f128(args):
@@ -126,7 +126,7 @@ def wl_reduce_f128(args):
     # quantile 0.999 with the default light bound and chunk size (1.46 ms
     # against 1.48 ms for the defaults); tuning is preprocessing, done offline
     t0 = time.perf_counter()
-    plan = gnn.gnn_plan_create(csr, **TUNED_CFG2)
+    plan = gnn.gnn_plan_create(csr, **TUNED_RMAT1M)
     plan_ms = (time.perf_counter() - t0) * 1e3
     Y = {op: torch.empty((n, F), dtype=torch.float32, device="cuda") for op in ("sum", "mean", "max", "min")}
     A = {op: torch.empty((n, F), dtype=torch.int32, device="cuda") for op in ("max", "min")}
@@ -170,7 +170,7 @@ def wl_reduce_f128(args):
     cfg = {"workload": w.name, "graph": "rmat(0.57,0.19,0.19,0.05)", "nodes": n, "edges": m,
            "F": F, "x_dtype": "f32", "ops": ["sum", "mean", "max+arg", "min+arg"],
            "step": "one fused pass (gnn_reduce_multi); value counts 4 aggregations x edges",
-           "plan_build_ms": round(plan_ms, 2), "plan": stats, "plan_opts": TUNED_CFG2}
+           "plan_build_ms": round(plan_ms, 2), "plan": stats, "plan_opts": TUNED_RMAT1M}
     # every tensor once: row pointers, column indices, X, four value outputs, two index outputs
     comp = 4 * (n + 1) + 4 * m + 7 * n * row_b
     return {"ops": ops, "dominant": "multi", "kernel": "k_aggregate<float, 32, 4, 3, true>",
@@ -812,11 +812,11 @@ def wl_dot_aggr(args):
 
 WORKLOADS = {"reduce_f128": wl_reduce_f128, "copy": wl_copy, "gatv2": wl_gatv2, "gt_csr": wl_gt,
              "spmm_large": wl_spmm_large, "gcn_small": wl_gcn_small,
-             "gt_block16": lambda a: wl_gt(a, "block16"), "plan_cfg2": wl_plan, "wsb_cfg4": wl_wsb,
-             "reorder_cfg5": wl_reorder, "spmm_bwd_cfg5": wl_spmm_bwd, "reduce_bwd_cfg2": wl_reduce_bwd,
-             "gatv2_bwd_cfg3": wl_gatv2_bwd, "gt_bwd_cfg4": wl_gt_bwd, "spmm_b16_cfg4": wl_spmm_b16,
-             "gt_bwd_b16_cfg4": lambda a: wl_gt_bwd(a, "block16"),
-             "dotaggr_cfg2": wl_dot_aggr}
+             "gt_block16": lambda a: wl_gt(a, "block16"), "plan_rmat1m": wl_plan, "wsb_cluster512k": wl_wsb,
+             "reorder_rmat16m": wl_reorder, "spmm_bwd_rmat16m": wl_spmm_bwd, "reduce_bwd_rmat1m": wl_reduce_bwd,
+             "gatv2_bwd": wl_gatv2_bwd, "gt_bwd_csr": wl_gt_bwd, "spmm_block16": wl_spmm_b16,
+             "gt_bwd_block16": lambda a: wl_gt_bwd(a, "block16"),
+             "dotaggr": wl_dot_aggr}
 
 
 # ---------------------------------------------------------------------------

@@ -37,7 +37,7 @@ def test_reduce_backward_rmat1m_full():
         assert bwd_err(host(dX), ref, mag) <= TOL_AGG, op
 
 
-def test_gatv2_backward_cfg3_full():
+def test_gatv2_backward_rmat200k_full():
     w = gen.gatv2_rmat()
     n, H, D = w.n, w.params["H"], w.params["D"]
     csr = dev_csr(w.row_ptr, w.col_idx)
@@ -53,7 +53,7 @@ def test_gatv2_backward_cfg3_full():
     assert bwd_err(host(datt), ra, ma) <= TOL_ATT, "datt"
 
 
-def test_gt_backward_cfg4_full():
+def test_gt_backward_cluster512k_full():
     w = gen.gt_cluster()
     n, H, D = w.n, w.params["H"], w.params["D"]
     csr = dev_csr(w.row_ptr, w.col_idx)
