@@ -51,6 +51,17 @@ __device__ __forceinline__ void store_row(float* p, const float (&v)[N]) {
     *reinterpret_cast<float4*>(p + k) = make_float4(v[k], v[k + 1], v[k + 2], v[k + 3]);
 }
 
+// The same to global memory as streaming (non-temporal) stores: output rows
+// are not read again by the kernel, and kept out of L2 they leave it to the
+// gathered rows.
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+template <int N>
+__device__ __forceinline__ void store_row_nt(float* p, const float (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; k += 4)
+    __builtin_nontemporal_store(nt_f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]}, reinterpret_cast<nt_f32x4*>(p + k));
+}
+
 // A lane's slice of one node row, kept as raw 16-byte words until used
 // (NV words = 8 NV bf16 or 4 NV float32 elements).
 template <int NV>

@@ -207,7 +207,7 @@ __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int
   for (int k = 0; k < VEL; ++k) o[k] = st.acc[k] * inv;
   float* dst = p.out + row * p.row_elems;
   if constexpr (VEL <= 4) {
-    if (d_ok) store_row<VEL>(dst + sl * VEL, o);
+    if (d_ok) store_row_nt<VEL>(dst + sl * VEL, o);
   } else {
     if (d_ok) store_row<VEL>(stage + sl * VEL, o);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -217,7 +217,8 @@ __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int
     for (int j = 0; j < VEL / 4; ++j) {
       const int c = (j * LPE + sl) * 4;
       const float4 t = *reinterpret_cast<const float4*>(stage + c);
-      if (c < p.row_elems) *reinterpret_cast<float4*>(dst + c) = t;
+      if (c < p.row_elems)
+        __builtin_nontemporal_store(nt_f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<nt_f32x4*>(dst + c));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

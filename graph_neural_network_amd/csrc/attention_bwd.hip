@@ -359,8 +359,8 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
 
   if (!is_item) {
     if (active && d_ok) {
-      store_row<VEL>(p.g0 + ro, R.acc0);
-      if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.g1 + ro, R.acc1);
+      store_row_nt<VEL>(p.g0 + ro, R.acc0);
+      if constexpr (KIND == B_GT_SRC) store_row_nt<VEL>(p.g1 + ro, R.acc1);
     }
     return;
   }
@@ -395,8 +395,8 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     R.acc1[k] = t1;
   }
   if (m_idx < 0) {
-    store_row<VEL>(p.g0 + ro, R.acc0);
-    if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.g1 + ro, R.acc1);
+    store_row_nt<VEL>(p.g0 + ro, R.acc0);
+    if constexpr (KIND == B_GT_SRC) store_row_nt<VEL>(p.g1 + ro, R.acc1);
   } else {
     const int64_t po = (int64_t)item * 2 * p.row_elems + sl * VEL;
     store_row<VEL>(p.part + po, R.acc0);

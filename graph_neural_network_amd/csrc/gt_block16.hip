@@ -302,7 +302,7 @@ void k_gt_block16(B16Params p) {
 #pragma unroll
       for (int q = 0; q < 16 / RPI; ++q) {
         const f32x4 t = *reinterpret_cast<const f32x4*>(lsrc + q * RPI * LDO);
-        if (q * RPI < rows_left) *reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr) = t;
+        if (q * RPI < rows_left) __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr));
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();

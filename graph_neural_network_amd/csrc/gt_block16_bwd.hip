@@ -251,7 +251,7 @@ __device__ __forceinline__ void write_rows(const float* lo, float* dst, int64_t 
 #pragma unroll
   for (int q = 0; q < 16 / RPI; ++q) {
     const f32x4 t = *reinterpret_cast<const f32x4*>(lsrc + q * RPI * LDO);
-    if (q * RPI < rows_left) *reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr) = t;
+    if (q * RPI < rows_left) __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(odst + (int64_t)q * RPI * ldr));
   }
   wave_sync();
 }

@@ -265,8 +265,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
     const int r = q / (FW / 4), f = f0 + (q % (FW / 4)) * 4;
     const int row = row0 + r;
     if (row < p.n_rows && f < p.F)
-      *reinterpret_cast<float4*>(p.Y + (int64_t)row * p.ldy + f) =
-          *reinterpret_cast<const float4*>(s_y + r * FW + (f - f0));
+      __builtin_nontemporal_store(*reinterpret_cast<const f32x4_t*>(s_y + r * FW + (f - f0)),
+                                  reinterpret_cast<f32x4_t*>(p.Y + (int64_t)row * p.ldy + f));
   }
 }
 
