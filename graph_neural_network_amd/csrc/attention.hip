@@ -397,11 +397,17 @@ int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
 template <typename T, int KIND>
 int dispatch(gnn_plan* pl, AttParams& p, int lpe, int nv, hipStream_t s) {
   if (nv == 2) {
-    switch (lpe) {
-      case 8: return launch_att<T, 8, 2, KIND>(pl, p, s);
-      case 16: return launch_att<T, 16, 2, KIND>(pl, p, s);
-      case 32: return launch_att<T, 32, 2, KIND>(pl, p, s);
-      default: return launch_att<T, 64, 2, KIND>(pl, p, s);
+    // GATv2 rows are at most 1 KB (checked at the entry point), so only GT
+    // instantiates the 32-bytes-per-lane kernels.
+    if constexpr (KIND == K_GATV2) {
+      return fail(GNN_ERR_UNSUPPORTED, "GATv2 rows wider than 1 KB");
+    } else {
+      switch (lpe) {
+        case 8: return launch_att<T, 8, 2, KIND>(pl, p, s);
+        case 16: return launch_att<T, 16, 2, KIND>(pl, p, s);
+        case 32: return launch_att<T, 32, 2, KIND>(pl, p, s);
+        default: return launch_att<T, 64, 2, KIND>(pl, p, s);
+      }
     }
   }
   switch (lpe) {
