@@ -3,11 +3,16 @@
 degree-sorted and RCM orders, with the plans bench.py uses.
 
 The oracle computes sampled rows one by one (uniform rows plus the heaviest
-hubs); the degree permutation is compared whole; the RCM permutation is
-checked to be a bijection here (it is compared bit for bit with the oracle
-on the 1,000,000-node graph in the reordering tests, since the sequential
-oracle at this size takes minutes).
+hubs); the degree permutation is compared whole; the RCM permutation and the
+relabelled CSR are compared bit for bit with the oracle's, through the
+SHA-256 digests in tests/golden/rcm_rmat16m.txt, which
+tests/golden/make_rcm_rmat16m.py writes from the generator and the CPU
+oracle alone (reverse Cuthill-McKee as in Tang et al., "A High-Throughput
+Solver for Marginalized Graph Kernels on GPU", graph reordering section).
 """
+import hashlib
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +23,21 @@ import oracle
 from gpu_util import dev_bf16, host, scaled_err
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rcm_rmat16m.txt")
+
+
+def golden_rcm():
+    out = {}
+    for line in open(GOLDEN):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split(None, 1)
+            out[k] = v.strip()
+    return out
+
+
+def digest(a) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a, dtype="<i4").tobytes()).hexdigest()
 
 
 @pytest.fixture(scope="module")
@@ -49,7 +69,15 @@ def test_spmm_rmat16m_all_orders(big):
         if kind == "degree":
             assert np.array_equal(P, oracle.degree_sort(w.row_ptr))
         else:
+            g = golden_rcm()
+            assert digest(w.row_ptr) == g["graph_row_ptr"] and digest(w.col_idx) == g["graph_col_idx"], \
+                "the generator no longer gives the graph the digests were taken on"
             assert np.array_equal(np.sort(P), np.arange(P.size))
+            assert " ".join(map(str, P[:8])) == g["perm_head"], P[:8]
+            assert " ".join(map(str, P[-8:])) == g["perm_tail"], P[-8:]
+            assert digest(P) == g["perm"], "RCM permutation differs from the oracle's"
+            assert digest(host(rp2)) == g["row_ptr_out"], "relabelled row_ptr differs from the oracle's"
+            assert digest(host(ci2)) == g["col_idx_out"], "relabelled col_idx differs from the oracle's"
         X2 = gnn.gnn_permute_rows(perm, X)
         c2 = gnn.Csr(rp2, ci2)
         Y2 = gnn.gnn_spmm(c2, X2, "none", plan=gnn.gnn_plan_create(c2))
