@@ -49,6 +49,8 @@ def _load():
     lib.oracle_reduce.argtypes = [i32, vp, vp, vp, i32, i64, ci, i64, vp, vp, vp, vp]
     lib.oracle_gatv2.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, f32, i64, vp, vp, vp, vp]
     lib.oracle_gt.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, f32, i64, vp, vp, vp, vp]
+    lib.oracle_gatv2_f64.argtypes = [i32, vp, vp, vp, vp, vp, i32, i32, f32, i64, vp, vp, vp, vp]
+    lib.oracle_project.argtypes = [i64, i32, vp, i32, vp, vp, vp]
     lib.oracle_degree_sort.argtypes = [i32, vp, vp]
     lib.oracle_rcm.argtypes = [i32, vp, vp, vp]
     lib.oracle_permute_csr.argtypes = [i32, vp, vp, vp, vp, vp]
@@ -157,6 +159,44 @@ def gatv2(row_ptr, col_idx, xl, xr, att, slope=0.2, rows=None):
     _rc(_load().oracle_gatv2(n, _p(rp), _p(ci), _p(xl), _p(xr), _p(att), H, D, slope, ns, _p(r),
                              _p(out), _p(lse), _p(va)), "gatv2")
     return out, lse, va
+
+
+def gatv2_f64(row_ptr, col_idx, xl, xr, att, slope=0.2, rows=None):
+    """As gatv2, from float64 per-vertex vectors xl [n_rows,H,D], xr [n_cols,H,D]."""
+    rp, ci = _c(row_ptr, np.int32), _c(col_idx, np.int32)
+    n = rp.size - 1
+    xl, xr = _c(xl, np.float64), _c(xr, np.float64)
+    att = _c(att, np.float32)
+    H, D = xl.shape[1], xl.shape[2]
+    r, ns = _rows(rows, n)
+    out = np.empty((ns, H, D), np.float64)
+    lse = np.empty((ns, H), np.float64)
+    va = np.empty((ns, H, D), np.float64)
+    _rc(_load().oracle_gatv2_f64(n, _p(rp), _p(ci), _p(xl), _p(xr), _p(att), H, D, slope, ns, _p(r),
+                                 _p(out), _p(lse), _p(va)), "gatv2_f64")
+    return out, lse, va
+
+
+def project(X, W, want_abs=True):
+    """Y = X W^T in float64 (and sum |x w|) from bf16 bits X [n, f_in], W [f_out, f_in]."""
+    X, W = _c(X, np.uint16), _c(W, np.uint16)
+    n, fi = X.shape
+    fo = W.shape[0]
+    assert W.shape[1] == fi
+    Y = np.empty((n, fo), np.float64)
+    A = np.empty((n, fo), np.float64) if want_abs else None
+    _rc(_load().oracle_project(n, fi, _p(X), fo, _p(W), _p(Y), _p(A)), "project")
+    return (Y, A) if want_abs else Y
+
+
+def gatv2_layer(row_ptr, col_idx, X, W_l, W_r, att, H, D, slope=0.2, rows=None):
+    """The GATv2 layer from node features: l = X W_l^T, r = X W_r^T taken exactly
+    (float64), then the softmax aggregation.  X [n, f_in], W_* [H*D, f_in] bf16
+    bits -> (out, lse, vabs) as gatv2."""
+    n = np.asarray(row_ptr).size - 1
+    L = project(X, W_l, want_abs=False).reshape(-1, H, D)
+    R = project(X, W_r, want_abs=False).reshape(-1, H, D)
+    return gatv2_f64(row_ptr, col_idx, L[:n], R, att, slope, rows)
 
 
 def gt(row_ptr, col_idx, q, k, v, scale=0.0, rows=None):

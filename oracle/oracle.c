@@ -208,13 +208,20 @@ int oracle_reduce(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx
   return bad ? -1 : 0;
 }
 
+/* Element idx of a per-vertex attention input: bf16 bits (f64 = 0) or
+ * float64 values (f64 = 1, the exact projections of the layer-level GATv2). */
+static double load_att(const void* V, int f64, int64_t idx) {
+  if (f64) return ((const double*)V)[idx];
+  return bf16_to_double(((const uint16_t*)V)[idx]);
+}
+
 /* Softmax aggregation shared by both attention layers, two passes (paper:
  * attention-based layers, h_i' = sum_j alpha_ij v_j with alpha = softmax of
  * e_ij over the row; logsumexp kept per (i, h)).  logits[0..deg) for one
- * (i, h) are given; v rows come from V (bf16) at V[j, h, :].
- * Returns 0, or -3 if the weights do not sum to 1 within 1e-12. */
+ * (i, h) are given; v rows come from V (bf16, or float64 if v_f64) at
+ * V[j, h, :].  Returns 0, or -3 if the weights do not sum to 1 within 1e-12. */
 static int softmax_aggregate(const double* logits, const int32_t* cols, int32_t deg,
-                             const uint16_t* V, int32_t H, int32_t D, int32_t h, double* out,
+                             const void* V, int v_f64, int32_t H, int32_t D, int32_t h, double* out,
                              double* lse, double* vabs) {
   for (int32_t d = 0; d < D; ++d) {
     out[d] = 0.0;
@@ -233,9 +240,9 @@ static int softmax_aggregate(const double* logits, const int32_t* cols, int32_t 
   for (int32_t k = 0; k < deg; ++k) {
     double alpha = exp(logits[k] - m) / ssum;
     asum += alpha;
-    const uint16_t* vj = V + ((int64_t)cols[k] * H + h) * D;
+    const int64_t vj = ((int64_t)cols[k] * H + h) * D;
     for (int32_t d = 0; d < D; ++d) {
-      double v = bf16_to_double(vj[d]);
+      double v = load_att(V, v_f64, vj + d);
       out[d] += alpha * v;
       if (vabs) vabs[d] += alpha * fabs(v);
     }
@@ -246,13 +253,12 @@ static int softmax_aggregate(const double* logits, const int32_t* cols, int32_t 
 
 /* GATv2 (paper: section on the three families, e_ij = a^T LeakyReLU(W_l h_i
  * + W_r h_j), v_j = W_r h_j; fused GATv2 appendix, l_i and r_j precomputed
- * per vertex).  xl [n_rows, H, D] and xr [n_cols, H, D] bf16; att [H, D] fp32;
- * LeakyReLU(z) = z if z > 0 else slope * z.  out [n_sel, H, D], lse [n_sel, H],
- * vabs [n_sel, H, D] (sum_j alpha |r_j|). */
-int oracle_gatv2(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
-                 const uint16_t* xl, const uint16_t* xr, const float* att, int32_t H, int32_t D,
-                 float slope, int64_t n_sel, const int32_t* rows, double* out, double* lse,
-                 double* vabs) {
+ * per vertex).  xl [n_rows, H, D] and xr [n_cols, H, D], bf16 bits or (f64)
+ * float64; att [H, D] fp32; LeakyReLU(z) = z if z > 0 else slope * z.
+ * out [n_sel, H, D], lse [n_sel, H], vabs [n_sel, H, D] (sum_j alpha |r_j|). */
+static int gatv2_impl(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const void* xl,
+                      const void* xr, int f64, const float* att, int32_t H, int32_t D, float slope,
+                      int64_t n_sel, const int32_t* rows, double* out, double* lse, double* vabs) {
   if (!row_ptr || !col_idx || !xl || !xr || !att || !out || !lse || H <= 0 || D <= 0) return -1;
   if (!rows) n_sel = n_rows;
   int bad = 0;
@@ -280,18 +286,18 @@ int oracle_gatv2(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
         }
       }
       for (int32_t h = 0; h < H; ++h) {
-        const uint16_t* li = xl + ((int64_t)i * H + h) * D;
+        const int64_t li = ((int64_t)i * H + h) * D;
         for (int32_t k = 0; k < deg; ++k) {
-          const uint16_t* rj = xr + ((int64_t)col_idx[b + k] * H + h) * D;
+          const int64_t rj = ((int64_t)col_idx[b + k] * H + h) * D;
           double e = 0.0;
           for (int32_t d = 0; d < D; ++d) {
-            double z = bf16_to_double(li[d]) + bf16_to_double(rj[d]);
+            double z = load_att(xl, f64, li + d) + load_att(xr, f64, rj + d);
             double act = z > 0.0 ? z : sl * z;
             e += (double)att[h * D + d] * act;
           }
           logits[k] = e;
         }
-        int rc = softmax_aggregate(logits, col_idx + b, deg, xr, H, D, h, out + (s * H + h) * D,
+        int rc = softmax_aggregate(logits, col_idx + b, deg, xr, f64, H, D, h, out + (s * H + h) * D,
                                    lse + s * H + h, vabs ? vabs + (s * H + h) * D : NULL);
         if (rc) bad = 2;
       }
@@ -299,6 +305,49 @@ int oracle_gatv2(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx,
     free(logits);
   }
   return bad == 2 ? -3 : (bad ? -1 : 0);
+}
+
+int oracle_gatv2(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* xl,
+                 const uint16_t* xr, const float* att, int32_t H, int32_t D, float slope, int64_t n_sel,
+                 const int32_t* rows, double* out, double* lse, double* vabs) {
+  return gatv2_impl(n_rows, row_ptr, col_idx, xl, xr, 0, att, H, D, slope, n_sel, rows, out, lse, vabs);
+}
+
+/* The same GATv2 from float64 per-vertex vectors: the layer as section 2.2
+ * of the paper defines it, l_i = W_l h_i and r_j = W_r h_j taken exactly
+ * (oracle_project) instead of rounded to an input format. */
+int oracle_gatv2_f64(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, const double* xl,
+                     const double* xr, const float* att, int32_t H, int32_t D, float slope, int64_t n_sel,
+                     const int32_t* rows, double* out, double* lse, double* vabs) {
+  return gatv2_impl(n_rows, row_ptr, col_idx, xl, xr, 1, att, H, D, slope, n_sel, rows, out, lse, vabs);
+}
+
+/* Per-vertex linear projection of the attention layers (paper: section on
+ * the three families, l_i = W_l h_i, r_j = W_r h_j for GATv2, q_i = W_Q h_i,
+ * k_j = W_K h_j, v_j = W_V h_j for the Graph Transformer): for every vertex i
+ * and output feature o,
+ *   Y[i, o] = sum_k X[i, k] W[o, k],   Yabs[i, o] = sum_k |X[i, k] W[o, k]|,
+ * X [n, f_in] and W [f_out, f_in] bf16 bits (W stored output-major, one row
+ * per output feature), Y and Yabs [n, f_out] float64.  Yabs may be NULL. */
+int oracle_project(int64_t n, int32_t f_in, const uint16_t* X, int32_t f_out, const uint16_t* W, double* Y,
+                   double* Yabs) {
+  if (n < 0 || f_in <= 0 || f_out <= 0 || !X || !W || !Y) return -1;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint16_t* xi = X + i * f_in;
+    for (int32_t o = 0; o < f_out; ++o) {
+      const uint16_t* wo = W + (int64_t)o * f_in;
+      double y = 0.0, ya = 0.0;
+      for (int32_t k = 0; k < f_in; ++k) {
+        const double t = bf16_to_double(xi[k]) * bf16_to_double(wo[k]);
+        y += t;
+        ya += fabs(t);
+      }
+      Y[i * f_out + o] = y;
+      if (Yabs) Yabs[i * f_out + o] = ya;
+    }
+  }
+  return 0;
 }
 
 /* Graph Transformer (paper: section on the three families, q_i = W_Q h_i,
@@ -344,7 +393,7 @@ int oracle_gt(int32_t n_rows, const int32_t* row_ptr, const int32_t* col_idx, co
           for (int32_t d = 0; d < D; ++d) dot += bf16_to_double(qi[d]) * bf16_to_double(kj[d]);
           logits[t] = dot * sc;
         }
-        int rc = softmax_aggregate(logits, col_idx + b, deg, v, H, D, h, out + (s * H + h) * D,
+        int rc = softmax_aggregate(logits, col_idx + b, deg, v, 0, H, D, h, out + (s * H + h) * D,
                                    lse + s * H + h, vabs ? vabs + (s * H + h) * D : NULL);
         if (rc) bad = 2;
       }

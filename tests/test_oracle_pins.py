@@ -388,6 +388,62 @@ def test_attention_invariants(rng):
     assert np.isfinite(out).all() and np.isfinite(lse).all()
 
 
+def test_project_dense_and_closed_forms(rng):
+    # Y = X W^T (W output-major, one row per output feature), as a matrix product
+    n, fi, fo = 37, 64, 48
+    X, W = bf16(rng, (n, fi)), bf16(rng, (fo, fi), std=fi ** -0.5)
+    Y, Ya = oracle.project(X, W)
+    np.testing.assert_allclose(Y, dec(X) @ dec(W).T, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(Ya, np.abs(dec(X)) @ np.abs(dec(W)).T, atol=1e-12, rtol=0)
+    # identity weights give the input back exactly
+    I = gen.f32_to_bf16(np.eye(fi, dtype=np.float32))
+    Y, _ = oracle.project(X, I)
+    assert np.array_equal(Y, dec(X))
+    # a selector row picks one input feature, scaled: row o = 2 e_{(3o) mod fi}
+    S = np.zeros((fo, fi), np.float32)
+    S[np.arange(fo), (3 * np.arange(fo)) % fi] = 2.0
+    Y, _ = oracle.project(X, gen.f32_to_bf16(S))
+    assert np.array_equal(Y, 2.0 * dec(X)[:, (3 * np.arange(fo)) % fi])
+    # one input row of ones: each output is the sum of its weight row
+    ones = gen.f32_to_bf16(np.ones((1, fi), np.float32))
+    Y, _ = oracle.project(ones, W)
+    np.testing.assert_allclose(Y[0], dec(W).sum(1), atol=1e-13, rtol=0)
+
+
+def test_gatv2_f64_agrees_with_bf16_form(rng):
+    # float64 inputs that are bf16 values give exactly the bf16 oracle's result
+    n, H, D = 60, 2, 16
+    rp, ci = gen.rmat(41, n, 500, self_loops=True)
+    xl, xr = bf16(rng, (n, H, D)), bf16(rng, (n, H, D))
+    att = rng.standard_normal((H, D)).astype(np.float32)
+    a = oracle.gatv2(rp, ci, xl, xr, att, 0.2)
+    b = oracle.gatv2_f64(rp, ci, dec(xl), dec(xr), att, 0.2)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_gatv2_layer_dense_bruteforce(rng):
+    # the layer from node features: l = W_l h_i, r = W_r h_j, then the
+    # masked softmax of a^T LeakyReLU(l_i + r_j) over each row's sources
+    n, fi, H, D = 36, 32, 2, 8
+    A, rp, ci = random_graph(rng, n, 0.25, loops=True)
+    X = bf16(rng, (n, fi))
+    Wl, Wr = bf16(rng, (H * D, fi), std=fi ** -0.5), bf16(rng, (H * D, fi), std=fi ** -0.5)
+    att = (rng.standard_normal((H, D)) / math.sqrt(D)).astype(np.float32)
+    out, lse, va = oracle.gatv2_layer(rp, ci, X, Wl, Wr, att, H, D, 0.2)
+    L = (dec(X) @ dec(Wl).T).reshape(n, H, D)
+    R = (dec(X) @ dec(Wr).T).reshape(n, H, D)
+    for h in range(H):
+        Z = L[:, None, h, :] + R[None, :, h, :]
+        act = np.where(Z > 0, Z, np.float64(np.float32(0.2)) * Z)
+        E = act @ att[h].astype(np.float64)
+        o, ls = dense_softmax_aggregate(E, A, R[:, h, :])
+        np.testing.assert_allclose(out[:, h], o, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(lse[:, h], ls, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(va[:, h], dense_softmax_aggregate(E, A, np.abs(R[:, h, :]))[0],
+                                   atol=1e-12, rtol=0)
+
+
 def test_attention_single_edge_and_empty():
     # row 0 <- {2}; row 1 empty; row 2 <- {0}
     rp, ci = gen.from_edges(3, [2, 0], [0, 2])
