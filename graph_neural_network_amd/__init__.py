@@ -37,7 +37,8 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_spmm", "gnn_reduce", "gnn_reduce_multi", "gnn_gatv2_fused", "gnn_gt_fused", "gnn_reorder",
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
-           "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune")
+           "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune",
+           "gnn_reduce_multi_noalloc")
 
 
 class GnnError(RuntimeError):
@@ -81,6 +82,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_spmm": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
         "gnn_reduce": [P(_Csr), vp, ci, i32, i64, ci, vp, i64, vp, vp, vp],
         "gnn_reduce_multi": [P(_Csr), vp, ci, i32, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp],
+        "gnn_reduce_multi_noalloc": [P(_Csr), vp, ci, i32, i64, vp, vp, vp, vp, vp, vp, i64, vp, vp],
         "gnn_gatv2_fused": [P(_Csr), vp, vp, ci, vp, i32, i32, f32, vp, vp, vp, vp],
         "gnn_gt_fused": [P(_Csr), vp, vp, vp, ci, i32, i32, f32, ci, vp, vp, vp, vp],
         "gnn_reorder": [P(_Csr), ci, vp, vp, vp, vp],
@@ -338,6 +340,25 @@ def gnn_reduce_multi(csr: Csr, X: torch.Tensor, ops=("sum", "mean", "max", "min"
                      out: dict | None = None, plan: Plan | None = None, stream=None) -> dict:
     """One pass computing the requested reductions; returns {name: tensor} with
     keys among sum, mean, max, min, argmax, argmin (indices only with args)."""
+    return _reduce_multi("gnn_reduce_multi", csr, X, ops, args, out, plan, stream)
+
+
+def gnn_reduce_multi_noalloc(csr: Csr, X: torch.Tensor, out: dict, plan: Plan,
+                             ops=("sum", "mean", "max", "min"), args: bool = True, stream=None) -> dict:
+    """gnn_reduce_multi without any device allocation in the library: the plan
+    (required) is built beforehand, split-row partials use the library's fixed
+    per-GPU scratch array.  `out` must hold every requested output already
+    (this wrapper allocates nothing either)."""
+    if plan is None:
+        raise ValueError("gnn_reduce_multi_noalloc needs a plan")
+    want = set(ops) | ({"arg" + o for o in ("max", "min") if o in ops} if args else set())
+    missing = want - set(out)
+    if missing:
+        raise ValueError(f"out lacks {sorted(missing)}")
+    return _reduce_multi("gnn_reduce_multi_noalloc", csr, X, ops, args, out, plan, stream)
+
+
+def _reduce_multi(fn: str, csr: Csr, X, ops, args, out, plan, stream) -> dict:
     _need(X, "X", csr.n_cols, (None,), FEAT, rows_strided=True)
     F = X.shape[1]
     out = dict(out or {})
@@ -359,10 +380,10 @@ def gnn_reduce_multi(csr: Csr, X: torch.Tensor, ops=("sum", "mean", "max", "min"
     if len(lds) != 1:
         raise ValueError("value outputs must share one row stride")
     _gpu(X=X, **out)
-    _check(load_library().gnn_reduce_multi(
+    _check(getattr(load_library(), fn)(
         csr.ref, _ptr(X), _dtype_code(X), F, X.stride(0), _ptr(out.get("sum")), _ptr(out.get("mean")),
         _ptr(out.get("max")), _ptr(out.get("argmax")), _ptr(out.get("min")), _ptr(out.get("argmin")),
-        lds.pop(), _plan_h(plan), _stream(stream)), "gnn_reduce_multi")
+        lds.pop(), _plan_h(plan), _stream(stream)), fn)
     return out
 
 

@@ -756,9 +756,16 @@ int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64
                 : pick_kind<float, 1>(pl, p, kind, arg != nullptr, lpr, s);
 }
 
+size_t reduce_multi_ws_bytes(const gnn_plan* pl, int32_t F) {
+  if (pl->n_multi <= 0) return 0;
+  const size_t part = ((size_t)pl->n_items * F * 4 + 255) & ~(size_t)255;
+  const size_t words = (size_t)pl->n_multi * F * 8;
+  return part + 2 * words;
+}
+
 int launch_reduce_multi(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx,
                         float* Ysum, float* Ymean, float* Ymax, int32_t* argmax, float* Ymin,
-                        int32_t* argmin, int64_t ldy, hipStream_t s) {
+                        int32_t* argmin, int64_t ldy, hipStream_t s, void* ws_given) {
   AggParams p{};
   p.row_ptr = pl->row_ptr;
   p.col_idx = pl->col_idx;
@@ -777,10 +784,11 @@ int launch_reduce_multi(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, in
   p.F = F;
   p.light_max = pl->light_max;
   if (pl->n_multi > 0) {
-    void* ws = nullptr;
+    // split rows: item partial sums, then the packed max and min words
+    void* ws = ws_given;
     const size_t part = ((size_t)pl->n_items * F * 4 + 255) & ~(size_t)255;
     const size_t words = (size_t)pl->n_multi * F * 8;
-    GNN_TRY(plan_workspace(pl, part + 2 * words, &ws));
+    if (!ws) GNN_TRY(plan_workspace(pl, part + 2 * words, &ws));
     p.partial = (float*)ws;
     p.packed = (unsigned long long*)((char*)ws + part);
     p.packed2 = (unsigned long long*)((char*)ws + part + words);

@@ -4,10 +4,13 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
 #include "gnn_internal.h"
+
+static __device__ __align__(256) unsigned char scratch[GNN_NOALLOC_SCRATCH_BYTES];
 
 namespace gnn {
 
@@ -110,6 +113,40 @@ int debug_validate(const gnn_csr* c, hipStream_t s) {
   if (h[1]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr[0] != 0 or row_ptr[n_rows] != nnz");
   if (h[0]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: row_ptr decreases");
   if (h[2]) return fail(GNN_ERR_INVALID_VALUE, "CSR check: a column index outside [0, n_cols)");
+  return GNN_OK;
+}
+
+// Scratch memory of gnn_reduce_multi_noalloc (the array `scratch`, file
+// scope): every GPU the library runs on holds its own copy until the process
+// ends.  Host code never passes the array's name to a kernel (in host code it
+// is a host-side stand-in, not a device address): scratch_address() looks up
+// the device address once per device with hipGetSymbolAddress and keeps it.
+constexpr size_t kNoallocScratchBytes = (size_t)GNN_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the device that `s` belongs to, which must
+// be the calling thread's current device.
+int scratch_address(hipStream_t s, void** out) {
+  int dev = -1;
+  GNN_HIP(hipGetDevice(&dev));
+  if (s) {
+    hipDevice_t sdev = -1;
+    GNN_HIP(hipStreamGetDevice(s, &sdev));
+    if ((int)sdev != dev)
+      return fail(GNN_ERR_INVALID_VALUE, "the stream belongs to another device than the current one");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(GNN_ERR_DEVICE, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !a)
+      return fail(GNN_ERR_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_addr[dev] = a;
+  }
+  *out = g_scratch_addr[dev];
   return GNN_OK;
 }
 
@@ -293,6 +330,31 @@ int gnn_reduce_multi(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t
   GNN_TRY(get_plan(csr, plan, s, &p, &tr));
   PlanGuard g{p, tr};
   return launch_reduce_multi(p, X, xtype, F, ldx, Y_sum, Y_mean, Y_max, arg_max, Y_min, arg_min, ldy, s);
+}
+
+int gnn_reduce_multi_noalloc(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+                             float* Y_sum, float* Y_mean, float* Y_max, int32_t* arg_max, float* Y_min,
+                             int32_t* arg_min, int64_t ldy, gnn_plan* plan, void* stream) {
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_dtype(xtype));
+  if (F <= 0 || ldx < F || ldy < F) return fail(GNN_ERR_INVALID_VALUE, "need F > 0, ldx >= F, ldy >= F");
+  if (!Y_sum && !Y_mean && !Y_max && !Y_min) return fail(GNN_ERR_INVALID_VALUE, "no output requested");
+  if ((arg_max && !Y_max) || (arg_min && !Y_min))
+    return fail(GNN_ERR_INVALID_VALUE, "an index output needs its value output");
+  if (!X && csr->n_cols > 0) return fail(GNN_ERR_INVALID_VALUE, "X is NULL");
+  if (!plan) return fail(GNN_ERR_INVALID_VALUE, "the allocation-free call needs a plan built beforehand");
+  GNN_TRY(check_plan(plan, csr));
+  if (csr->n_rows == 0) return GNN_OK;
+  const size_t need = reduce_multi_ws_bytes(plan, F);
+  if (need > kNoallocScratchBytes)
+    return fail(GNN_ERR_SIZE_OVERFLOW, "the plan's split rows need " + std::to_string(need) +
+                                           " bytes of scratch at this F; the allocation-free call holds at most " +
+                                           std::to_string(kNoallocScratchBytes));
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (need > 0) GNN_TRY(scratch_address(s, &ws));
+  return launch_reduce_multi(plan, X, xtype, F, ldx, Y_sum, Y_mean, Y_max, arg_max, Y_min, arg_min, ldy, s,
+                             ws);
 }
 
 int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,

@@ -135,7 +135,10 @@ int launch_aggregate(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_
                      hipStream_t s);
 int launch_reduce_multi(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx,
                         float* Ysum, float* Ymean, float* Ymax, int32_t* argmax, float* Ymin,
-                        int32_t* argmin, int64_t ldy, hipStream_t s);
+                        int32_t* argmin, int64_t ldy, hipStream_t s, void* ws = nullptr);
+// Workspace bytes launch_reduce_multi needs for the plan's split rows at
+// width F (0 without split rows); `ws` above, when given, must hold them.
+size_t reduce_multi_ws_bytes(const gnn_plan* pl, int32_t F);
 int launch_gatv2(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, const float* att,
                  int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s);
 int launch_gt_csr(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,

@@ -228,6 +228,30 @@ int gnn_reduce_multi(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t
                      float* Y_sum, float* Y_mean, float* Y_max, int32_t* arg_max, float* Y_min,
                      int32_t* arg_min, int64_t ldy, gnn_plan* plan, void* stream);
 
+/* Bytes of device scratch memory that gnn_reduce_multi_noalloc may use. */
+#define GNN_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* gnn_reduce_multi for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as gnn_reduce_multi, except:
+ *   - plan is required (NULL is INVALID_VALUE): build it beforehand with
+ *     gnn_plan_create, which does allocate;
+ *   - the partial sums and packed (key, index) words of the plan's split rows
+ *     live in a fixed library array of GNN_NOALLOC_SCRATCH_BYTES per GPU
+ *     (held from the first call on that GPU until the process ends) instead
+ *     of the plan's workspace; a plan and width F that need more
+ *     (n_items * F * 4, rounded up to 256, plus 16 * split rows * F bytes)
+ *     return SIZE_OVERFLOW before any launch;
+ *   - `stream` must belong to the calling thread's current device;
+ *   - the call makes no device allocation, free or host synchronisation.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give wrong results;
+ * calls ordered on one stream are safe.  The array keeps the last call's
+ * contents; each call initialises what it reads. */
+int gnn_reduce_multi_noalloc(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx,
+                             float* Y_sum, float* Y_mean, float* Y_max, int32_t* arg_max, float* Y_min,
+                             int32_t* arg_min, int64_t ldy, gnn_plan* plan, void* stream);
+
 /* Fused GATv2 forward (section 2.2 (iii); appendix D.2 "fused CSR forward
  * (GATv2)"): for each destination i and head h,
  *   e_ij = sum_d att[h, d] * LeakyReLU(xl[i, h, d] + xr[j, h, d]),

@@ -61,6 +61,9 @@ INV, UNS, OVF = 1, 2, 5
     ("multi no output", lambda: call("gnn_reduce_multi", ctypes.byref(fake_csr()), P(16), 0, 4, 4, None, None, None, None, None, None, 4, None, None), INV),
     ("multi arg without value", lambda: call("gnn_reduce_multi", ctypes.byref(fake_csr()), P(16), 0, 4, 4, P(16), None, None, P(16), None, None, 4, None, None), INV),
     ("multi ldy<F", lambda: call("gnn_reduce_multi", ctypes.byref(fake_csr()), P(16), 0, 8, 8, P(16), None, None, None, None, None, 4, None, None), INV),
+    ("noalloc null plan", lambda: call("gnn_reduce_multi_noalloc", ctypes.byref(fake_csr()), P(16), 0, 4, 4, P(16), None, None, None, None, None, 4, None, None), INV),
+    ("noalloc no output", lambda: call("gnn_reduce_multi_noalloc", ctypes.byref(fake_csr()), P(16), 0, 4, 4, None, None, None, None, None, None, 4, None, None), INV),
+    ("noalloc null csr", lambda: call("gnn_reduce_multi_noalloc", None, P(16), 0, 4, 4, P(16), None, None, None, None, None, 4, None, None), INV),
     ("gatv2 H=0", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 0, 32, ctypes.c_float(0.2), P(16), None, None, None), INV),
     ("gatv2 too wide", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), None, None, None), UNS),
     ("gatv2 D*2 % 16", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 12, ctypes.c_float(0.2), P(16), None, None, None), UNS),
