@@ -255,6 +255,21 @@ def gatv2_rmat(n=200_000, m=4_000_000, H=4, D=32, k=3) -> Workload:
                     {"xl": xl, "xr": xr, "att": att}, {"H": H, "D": D, "slope": 0.2})
 
 
+def gatv2_layer_rmat(n=200_000, m=4_000_000, F_in=128, H=4, D=32, k=3) -> Workload:
+    """The GATv2 layer as configured from node features: X [n, F_in] bf16 ~ N(0, 1),
+    W_l, W_r [H*D, F_in] bf16 ~ N(0, 1/F_in) (variance 1/F_in, one row per output
+    feature), attention vector a [H, D] fp32 ~ N(0, 1/D), on the same graph as
+    gatv2_rmat."""
+    rp, ci = rmat(GRAPH_SEED + k, n, m, self_loops=True)
+    X = gauss_bf16(FEAT_SEED + 300 + k, (n, F_in))
+    std = (1.0 / F_in) ** 0.5
+    Wl = gauss_bf16(WEIGHT_SEED + 100 + k, (H * D, F_in), std=std)
+    Wr = gauss_bf16(WEIGHT_SEED + 200 + k, (H * D, F_in), std=std)
+    att = gauss_f32(WEIGHT_SEED + k, (H, D), std=(1.0 / D) ** 0.5)
+    return Workload(f"gatv2_layer_rmat{n}_{m}_f{F_in}_h{H}d{D}", n, rp, ci,
+                    {"X": X, "W_l": Wl, "W_r": Wr, "att": att}, {"F_in": F_in, "H": H, "D": D, "slope": 0.2})
+
+
 def gt_cluster(n=512_000, csize=64, p=0.5, frac=0.01, H=8, D=64, k=4, with_x=True) -> Workload:
     rp, ci = cluster(GRAPH_SEED + k, n, csize, p, frac, self_loops=True)
     arrays = {}

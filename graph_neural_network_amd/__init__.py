@@ -38,7 +38,7 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
            "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune",
-           "gnn_reduce_multi_noalloc")
+           "gnn_reduce_multi_noalloc", "gnn_project")
 
 
 class GnnError(RuntimeError):
@@ -96,6 +96,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_dot_aggr": [P(_Csr), vp, i32, i64, ci, ci, vp, vp, vp],
         "gnn_gt_backward_block16": [P(_Csr), vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_plan_autotune": [P(_Csr), vp, ci, i32, i64, ci, i32, P(_PlanOpts), P(f32), P(f32), vp],
+        "gnn_project": [vp, i32, i32, i64, i32, P(vp), i32, P(vp), vp],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -433,6 +434,34 @@ def gnn_gt_fused(csr: Csr, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
                                        float(scale), GT_MODE[mode], _ptr(out), _ptr(lse),
                                        _plan_h(plan), _stream(stream)), "gnn_gt_fused")
     return out, lse
+
+
+def gnn_project(X: torch.Tensor, W, out=None, stream=None):
+    """Y_m = X W_m^T for each bf16 weight W_m [f_out, f_in] (a tensor or a list of
+    up to three), bf16 X [n, f_in]; -> list of bf16 [n, f_out] (bf16 matrix cores,
+    fp32 accumulation, round to nearest even)."""
+    Ws = [W] if isinstance(W, torch.Tensor) else list(W)
+    if not 1 <= len(Ws) <= 3:
+        raise ValueError("one to three weight matrices")
+    _need(X, "X", 0, (None,), (torch.bfloat16,), rows_strided=True)
+    n, fi = X.shape
+    fo = Ws[0].shape[0]
+    for k, w in enumerate(Ws):
+        _need(w, f"W[{k}]", fo, (fi,), (torch.bfloat16,))
+        if w.shape[0] != fo:
+            raise ValueError("all weights need the same number of output features")
+    if out is None:
+        out = [torch.empty((n, fo), dtype=torch.bfloat16, device=X.device) for _ in Ws]
+    if len(out) != len(Ws):
+        raise ValueError("one output per weight")
+    for k, y in enumerate(out):
+        _need(y, f"Y[{k}]", n, (fo,), (torch.bfloat16,))
+    _gpu(X=X, **{f"W{k}": w for k, w in enumerate(Ws)}, **{f"Y{k}": y for k, y in enumerate(out)})
+    wp = (ctypes.c_void_p * len(Ws))(*[w.data_ptr() for w in Ws])
+    yp = (ctypes.c_void_p * len(Ws))(*[y.data_ptr() for y in out])
+    _check(load_library().gnn_project(_ptr(X), n, fi, X.stride(0), len(Ws), wp, fo, yp, _stream(stream)),
+           "gnn_project")
+    return out
 
 
 def gnn_spmm_backward(csr: Csr, dY: torch.Tensor, norm: str = "none", dX: torch.Tensor | None = None,

@@ -418,6 +418,27 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   return launch_gt_csr(p, q, k, v, xtype, H, D, sc, out, lse, s);
 }
 
+int gnn_project(const void* X, int32_t n, int32_t f_in, int64_t ldx, int32_t n_mat, const void* const* W,
+                int32_t f_out, void* const* Y, void* stream) {
+  if (n < 0 || f_in <= 0 || f_out <= 0) return fail(GNN_ERR_INVALID_VALUE, "need n >= 0, f_in > 0, f_out > 0");
+  if (n_mat < 1 || n_mat > 3) return fail(GNN_ERR_INVALID_VALUE, "n_mat must be 1, 2 or 3");
+  if (ldx < f_in) return fail(GNN_ERR_INVALID_VALUE, "need ldx >= f_in");
+  if (!W || !Y) return fail(GNN_ERR_INVALID_VALUE, "W or Y is NULL");
+  if (f_in % 32 != 0 || f_in > 512 || f_out % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "projection needs f_in a multiple of 32 up to 512 and f_out a multiple of 16");
+  if (ldx % 8 != 0 || (uintptr_t)X % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "X must be 16-byte aligned with ldx a multiple of 8");
+  for (int m = 0; m < n_mat; ++m) {
+    if (!W[m] || !Y[m]) return fail(GNN_ERR_INVALID_VALUE, "a weight or output pointer is NULL");
+    if (((uintptr_t)W[m] | (uintptr_t)Y[m]) % 16 != 0)
+      return fail(GNN_ERR_UNSUPPORTED, "weights and outputs must be 16-byte aligned");
+  }
+  if ((int64_t)n * f_out >= ((int64_t)1 << 40)) return fail(GNN_ERR_SIZE_OVERFLOW, "output too large");
+  if (n == 0) return GNN_OK;
+  if (!X) return fail(GNN_ERR_INVALID_VALUE, "X is NULL");
+  return launch_project(X, n, f_in, ldx, n_mat, W, f_out, Y, (hipStream_t)stream);
+}
+
 int gnn_spmm_backward(const gnn_csr* csr, const float* dY, int32_t F, int64_t ldy, float* dX, int64_t ldx,
                       gnn_norm norm, gnn_plan* plan, void* stream) {
   GNN_TRY(check_csr(csr, false));

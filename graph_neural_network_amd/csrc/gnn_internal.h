@@ -145,6 +145,8 @@ int launch_gt_csr(gnn_plan* p, const void* q, const void* k, const void* v, gnn_
                   int32_t D, float scale, float* out, float* lse, hipStream_t s);
 int launch_gt_block16(gnn_plan* p, const void* q, const void* k, const void* v, int32_t H,
                       int32_t D, float scale, float* out, float* lse, hipStream_t s);
+int launch_project(const void* X, int32_t n, int32_t f_in, int64_t ldx, int32_t n_mat, const void* const* W,
+                   int32_t f_out, void* const* Y, hipStream_t s);
 int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int32_t* rp_out,
                    int32_t* ci_out, hipStream_t s);
 int launch_permute_rows(const int32_t* perm, int32_t n, const void* X, int elem_bytes, int32_t F,

@@ -1,0 +1,163 @@
+// Per-vertex linear projections of the attention layers on bf16 matrix cores.
+//
+// Fomina et al., "On efficient scaling of GNNs via IO-aware layer
+// implementations", section 2.2 (iii): GATv2 scores a^T LeakyReLU(W_l h_i +
+// W_r h_j) with values v_j = W_r h_j; the Graph Transformer's q_i = W_Q h_i,
+// k_j = W_K h_j, v_j = W_V h_j.  Appendix D.2 runs the fused kernels on these
+// vectors precomputed once per vertex; this file computes them:
+//   Y_m[i, o] = sum_k X[i, k] W_m[o, k]   for m < n_mat (up to three weights),
+// X [n, f_in] bf16, W_m [f_out, f_in] bf16 (one row per output feature),
+// products exact in fp32, fp32 accumulation, output rounded to bf16 (nearest
+// even).  A dense contraction: it belongs on the matrix cores.
+//
+// MI355X mapping.  A wave owns 16 * MR rows of X and keeps their K = f_in
+// columns in registers as B operands of v_mfma_f32_16x16x32_bf16, loaded
+// straight from memory in operand layout (lane l: row l % 16, k 8 (l / 16)
+// .. +7, 16 contiguous bytes).  For every 16-feature output tile it streams
+// the weight rows in as A operands (W is tiny and stays in L1 / L2) and
+// forms Y^T = W X^T, so lane l ends with Y[row l % 16][o 4 (l / 16) .. +3]:
+// four consecutive outputs of one row, converted to bf16 in one instruction
+// and written as 8 bytes to the wave's LDS staging tile.  The staged
+// 16 * MR x 128 block is then stored as 16 contiguous bytes per lane, whole
+// lines per instruction.  Each weight fragment serves MR row tiles.
+#include "gnn_internal.h"
+
+namespace gnn {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr int WG = 256;
+constexpr int OCH = 128;           // output features staged per pass
+constexpr int SROW = OCH + 8;      // staging row stride (bf16), padded against bank conflicts
+
+struct ProjParams {
+  const uint16_t* X;
+  const uint16_t* W[3];
+  uint16_t* Y[3];
+  int64_t ldx;
+  int32_t n;
+  int32_t f_out;
+  int32_t n_mat;
+};
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int KS, int MR>
+__global__ __launch_bounds__(WG) void k_project(ProjParams p) {
+  constexpr int K = 32 * KS;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t r_base = ((int64_t)blockIdx.x * (WG / 64) + wave) * 16 * MR;
+  if (r_base >= p.n) return;  // the whole wave leaves; staging is wave-private
+  const int lr = lane & 15, lk = lane >> 4;
+
+  // B operands: this wave's rows of X (rows past n re-read the last row)
+  bf16x8 xf[MR][KS];
+#pragma unroll
+  for (int r = 0; r < MR; ++r) {
+    const int64_t row = min<int64_t>(r_base + 16 * r + lr, (int64_t)p.n - 1);
+    const uint16_t* src = p.X + row * p.ldx + 8 * lk;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) xf[r][k] = *reinterpret_cast<const bf16x8*>(src + 32 * k);
+  }
+
+  __shared__ __align__(16) uint16_t stage[WG / 64][16 * MR][SROW];
+  uint16_t(*st)[SROW] = stage[wave];
+  const int n_here = (int)min<int64_t>(16 * MR, (int64_t)p.n - r_base);
+
+  for (int m = 0; m < p.n_mat; ++m) {
+    const uint16_t* W = p.W[m];
+    uint16_t* Y = p.Y[m];
+    for (int o0 = 0; o0 < p.f_out; o0 += OCH) {
+      const int ow = min(OCH, p.f_out - o0);  // a multiple of 16
+      for (int t = 0; t < ow; t += 16) {
+        f32x4 acc[MR];
+#pragma unroll
+        for (int r = 0; r < MR; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint16_t* wrow = W + (int64_t)(o0 + t + lr) * K + 8 * lk;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 32 * k);
+#pragma unroll
+          for (int r = 0; r < MR; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[r][k], acc[r], 0, 0, 0);
+        }
+        // lane: row 16 r + lr, outputs t + 4 lk .. +3
+#pragma unroll
+        for (int r = 0; r < MR; ++r) {
+          const uint2 w2 = make_uint2(pack_bf16(acc[r][0], acc[r][1]), pack_bf16(acc[r][2], acc[r][3]));
+          *reinterpret_cast<uint2*>(&st[16 * r + lr][t + 4 * lk]) = w2;
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // store the staged rows: ow / 8 lanes of 16 bytes per row
+      const int lpr = ow / 8;
+      for (int q = lane; q < n_here * lpr; q += 64) {
+        const int row = q / lpr, c = (q % lpr) * 8;
+        const uint4 v = *reinterpret_cast<const uint4*>(&st[row][c]);
+        *reinterpret_cast<uint4*>(Y + (r_base + row) * p.f_out + o0 + c) = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+}
+
+template <int KS>
+int launch_ks(ProjParams& p, hipStream_t s) {
+  // MR * KS * 4 VGPRs hold the rows of X: at most 64
+  constexpr int MR = KS <= 4 ? 4 : (KS <= 8 ? 2 : 1);
+  const int64_t rows_per_block = (int64_t)(WG / 64) * 16 * MR;
+  const int64_t blocks = (p.n + rows_per_block - 1) / rows_per_block;
+  if (blocks > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "projection grid too large");
+  hipLaunchKernelGGL((k_project<KS, MR>), dim3((unsigned)blocks), dim3(WG), 0, s, p);
+  GNN_LAUNCH_CHECK("projection");
+  return GNN_OK;
+}
+
+}  // namespace
+
+int launch_project(const void* X, int32_t n, int32_t f_in, int64_t ldx, int32_t n_mat, const void* const* W,
+                   int32_t f_out, void* const* Y, hipStream_t s) {
+  ProjParams p{};
+  p.X = (const uint16_t*)X;
+  p.ldx = ldx;
+  p.n = n;
+  p.f_out = f_out;
+  p.n_mat = n_mat;
+  for (int m = 0; m < n_mat; ++m) {
+    p.W[m] = (const uint16_t*)W[m];
+    p.Y[m] = (uint16_t*)Y[m];
+  }
+  switch (f_in / 32) {
+    case 1: return launch_ks<1>(p, s);
+    case 2: return launch_ks<2>(p, s);
+    case 3: return launch_ks<3>(p, s);
+    case 4: return launch_ks<4>(p, s);
+    case 5: return launch_ks<5>(p, s);
+    case 6: return launch_ks<6>(p, s);
+    case 7: return launch_ks<7>(p, s);
+    case 8: return launch_ks<8>(p, s);
+    case 9: return launch_ks<9>(p, s);
+    case 10: return launch_ks<10>(p, s);
+    case 11: return launch_ks<11>(p, s);
+    case 12: return launch_ks<12>(p, s);
+    case 13: return launch_ks<13>(p, s);
+    case 14: return launch_ks<14>(p, s);
+    case 15: return launch_ks<15>(p, s);
+    case 16: return launch_ks<16>(p, s);
+    default: return fail(GNN_ERR_UNSUPPORTED, "projection needs f_in a multiple of 32, at most 512");
+  }
+}
+
+}  // namespace gnn

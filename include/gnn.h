@@ -292,6 +292,26 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
                  int32_t H, int32_t D, float scale, gnn_gt_mode mode, float* out, float* lse,
                  gnn_plan* plan, void* stream);
 
+/* Per-vertex projections that feed the attention layers (section 2.2 (iii):
+ * GATv2 l_i = W_l h_i and r_j = W_r h_j; the Graph Transformer's q_i = W_Q h_i,
+ * k_j = W_K h_j, v_j = W_V h_j; appendix D.2 consumes them precomputed per
+ * vertex): for m < n_mat and every row i < n,
+ *   Y[m][i, o] = sum_k X[i, k] * W[m][o, k],   o < f_out, k < f_in,
+ * on bf16 matrix cores: bf16 inputs (products exact in float32), float32
+ * accumulation, each output rounded to bf16 (round to nearest even).  One
+ * pass over X serves all n_mat weights.
+ * X: device bf16 [n, ldx], 16-byte aligned, ldx >= f_in a multiple of 8.
+ * W: HOST array of n_mat (1 to 3) DEVICE pointers, each bf16 [f_out, f_in]
+ * contiguous (one row per output feature, the nn.Linear layout), 16-byte
+ * aligned.  Y: HOST array of n_mat DEVICE pointers, each bf16 [n, f_out]
+ * contiguous, 16-byte aligned; as [n, H, D] with H * D = f_out they are the
+ * dense per-vertex inputs of gnn_gatv2_fused and gnn_gt_fused.
+ * Supported: f_in a multiple of 32 up to 512, f_out a multiple of 16.
+ * Asynchronous on `stream`; no allocation.
+ * Errors: INVALID_VALUE, UNSUPPORTED, SIZE_OVERFLOW, DEVICE. */
+int gnn_project(const void* X, int32_t n, int32_t f_in, int64_t ldx, int32_t n_mat, const void* const* W,
+                int32_t f_out, void* const* Y, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Backward passes.  Each takes the gradient of a forward output and returns
  * the gradients of its inputs, all float32, dense, owned by the caller and
