@@ -365,9 +365,8 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
   if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
   if (!xl || !att || !out || (!xr && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "xl, xr, att or out is NULL");
-  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 1024)
-    return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
+  if ((int64_t)H * D >= ((int64_t)1 << 28)) return fail(GNN_ERR_SIZE_OVERFLOW, "H * D too large");
+  GNN_TRY(attention_mapping_supported(0, xtype, H, D));
   if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out) % 16 != 0)
     return fail(GNN_ERR_UNSUPPORTED, "xl, xr and out must be 16-byte aligned");
   if (csr->n_rows == 0) return GNN_OK;
@@ -400,13 +399,15 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   if (H <= 0 || D <= 0) return fail(GNN_ERR_INVALID_VALUE, "need H > 0 and D > 0");
   if (!q || !out || ((!k || !v) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "q, k, v or out is NULL");
-  const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 2048)
-    return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
+  if ((int64_t)H * D >= ((int64_t)1 << 28)) return fail(GNN_ERR_SIZE_OVERFLOW, "H * D too large");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
     return fail(GNN_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
-  if (mode == GNN_GT_BLOCK16 && (xtype != GNN_BF16 || (D != 32 && D != 64 && D != 128)))
-    return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs bf16 and D in {32, 64, 128}");
+  if (mode == GNN_GT_BLOCK16) {
+    if (xtype != GNN_BF16 || (D != 32 && D != 64 && D != 128))
+      return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs bf16 and D in {32, 64, 128}");
+    if ((int64_t)H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs H*D*2 <= 2048 bytes");
+  }
+  GNN_TRY(attention_mapping_supported(1, xtype, H, D));
   if (csr->n_rows == 0) return GNN_OK;
   float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
   hipStream_t s = (hipStream_t)stream;

@@ -62,27 +62,71 @@ __device__ __forceinline__ void store_row_nt(float* p, const float (&v)[N]) {
     __builtin_nontemporal_store(nt_f32x4{v[k], v[k + 1], v[k + 2], v[k + 3]}, reinterpret_cast<nt_f32x4*>(p + k));
 }
 
-// A lane's slice of one node row, kept as raw 16-byte words until used
-// (NV words = 8 NV bf16 or 4 NV float32 elements).
-template <int NV>
-struct Raw {
-  uint32_t u[4 * NV];
-};
-
-template <typename T, int NV>
-__device__ __forceinline__ void load_raw(const T* p, Raw<NV>& r) {
+// The same for any VEL = 1, 2, 4, 8, ... elements: 16-byte pieces where the
+// slice allows them, else one 8-, 4-byte or single-element store.
+template <int VEL>
+__device__ __forceinline__ void store_elems(float* p, const float (&v)[VEL]) {
+  if constexpr (VEL % 4 == 0) {
+    store_row<VEL>(p, v);
+  } else if constexpr (VEL == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  } else {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const uint4 v = reinterpret_cast<const uint4*>(p)[k];
-    r.u[4 * k] = v.x; r.u[4 * k + 1] = v.y; r.u[4 * k + 2] = v.z; r.u[4 * k + 3] = v.w;
+    for (int k = 0; k < VEL; ++k) p[k] = v[k];
+  }
+}
+template <int VEL>
+__device__ __forceinline__ void store_elems_nt(float* p, const float (&v)[VEL]) {
+  if constexpr (VEL % 4 == 0) {
+    store_row_nt<VEL>(p, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < VEL; ++k) __builtin_nontemporal_store(v[k], p + k);
   }
 }
 
-// element k of a raw slice as float
+// A lane's slice of one node row, VB bytes (2, 4, 8, 16 or 32), kept as raw
+// 32-bit words until used (a 2-byte slice sits in the low half of its word,
+// the high half zero).
+template <int VB>
+struct RawB {
+  uint32_t u[VB >= 4 ? VB / 4 : 1];
+};
+// 16 NV bytes: the slices of the 16- and 32-byte lane mappings
+template <int NV>
+using Raw = RawB<16 * NV>;
+
+template <typename T, int VB>
+__device__ __forceinline__ void load_rawb(const T* p, RawB<VB>& r) {
+  if constexpr (VB == 2) {
+    r.u[0] = (uint32_t)*reinterpret_cast<const uint16_t*>(p);
+  } else if constexpr (VB == 4) {
+    r.u[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (VB == 8) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    r.u[0] = v.x; r.u[1] = v.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < VB / 16; ++k) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[k];
+      r.u[4 * k] = v.x; r.u[4 * k + 1] = v.y; r.u[4 * k + 2] = v.z; r.u[4 * k + 3] = v.w;
+    }
+  }
+}
 template <typename T, int NV>
-__device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
+__device__ __forceinline__ void load_raw(const T* p, Raw<NV>& r) {
+  load_rawb<T, 16 * NV>(p, r);
+}
+
+// element k of a raw slice as float
+template <typename T, int VB>
+__device__ __forceinline__ float elemb(const RawB<VB>& r, int k) {
   if constexpr (sizeof(T) == 2) return (k & 1) ? dev::bf16_hi(r.u[k >> 1]) : dev::bf16_lo(r.u[k >> 1]);
   else return __uint_as_float(r.u[k]);
+}
+template <typename T, int NV>
+__device__ __forceinline__ float elem(const Raw<NV>& r, int k) {
+  return elemb<T, 16 * NV>(r, k);
 }
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -104,6 +148,13 @@ __device__ __forceinline__ float head_sum(float t) {
   if constexpr (LPH > 8) t += dpp<0x140>(t);  // row_mirror
   if constexpr (LPH > 16) t += __shfl_xor(t, 16, 64);
   if constexpr (LPH > 32) t += __shfl_xor(t, 32, 64);
+  return t;
+}
+
+// head_sum with the lanes per head known only at run time (a power of two
+// up to 64): xor shuffles through the LDS crossbar, for the generic mapping.
+__device__ __forceinline__ float head_sum_rt(float t, int lph) {
+  for (int o = 1; o < lph; o <<= 1) t += __shfl_xor(t, o, 64);
   return t;
 }
 

@@ -13,11 +13,17 @@
 //     exp(m_w - m_global), logsumexp kept per (node, head).
 //
 // MI355X mapping.  An edge's feature row (all heads) is spread over a slot of
-// LPE lanes, 16 bytes (NV = 1) or 32 bytes (NV = 2) per lane; the lanes of one
-// head reduce the score with xor shuffles.  Config examples: GATv2 H = 4,
+// LPE lanes, VB = 16 or 32 bytes per lane; the lanes of one head (LPH, a power
+// of two: a head whose slices fill fewer lanes leaves the rest of its group
+// idle) reduce the score with lane swaps.  Config examples: GATv2 H = 4,
 // D = 32 bf16 is a 256-byte row = 16 lanes, four edges per wave instruction;
 // GT H = 8, D = 64 bf16 is a 1-KB row = one full wave per edge for K and one
-// for V.  Each slot keeps its own (m, l, acc) state over U = 4 edges in
+// for V.  Rows wider than a slot are cut into head groups of one slot each,
+// one group per grid row (blockIdx.y); each group walks the same edges.
+// Heads whose byte width is not a multiple of 16 take the generic mapping:
+// 8-, 4- or 2-byte slices per lane, 64-lane slots, lanes per head known at
+// run time (the pages' fallback beside the head-dimension specialisations,
+// appendix D.2).  Each slot keeps its own (m, l, acc) state over U = 4 edges in
 // flight; slots of a wave, waves of a workgroup and chunks of a split row
 // are merged with the same rescaling rule.  Logits live in the log2 domain
 // (log2 e folded into a or into q * scale) so every exponential is exp2.
@@ -62,8 +68,10 @@ struct AttParams {
   int32_t n_rows;
   int32_t H, D;
   int32_t row_elems;  // H * D
-  int32_t row_lanes;  // lanes holding data (H * D / VEL)
   int32_t lph;        // lanes per head (power of two)
+  int32_t lph_data;   // of which hold data (D / VEL)
+  int32_t hpg;        // heads per group (one group per grid row)
+  int32_t dv;         // D / VEL: lane slices per head
   int32_t light_max;         // rows of at most this many edges take one slot
   const int32_t* att_rows;   // those rows, longest first
   const int32_t* att_count;  // device: how many
@@ -116,27 +124,26 @@ __device__ __forceinline__ void shfl_merge(Soft<VEL>& s, int lane_xor) {
 //               and (1 - slope) / 2 (unused for GT): a * LReLU(z) =
 //               av * z + an * |z|, two multiply-adds (|z| is a free operand
 //               modifier) instead of a multiply, a max and a multiply-add
-template <typename T, int LPE, int NV, int KIND, int UU, int LPH>
+template <typename T, int LPE, int VB, int KIND, int UU, int LPH>
 __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, int sl, int slot_base,
-                                           bool d_ok, const float (&qv)[(16 / sizeof(T)) * NV],
-                                           const Raw<NV>& qraw,
-                                           const float (&av)[(16 / sizeof(T)) * NV],
-                                           const float (&an)[(16 / sizeof(T)) * NV],
-                                           Soft<(16 / sizeof(T)) * NV>& st) {
-  constexpr int VEL = (16 / (int)sizeof(T)) * NV;
+                                           uint32_t loff, const float (&qv)[VB / sizeof(T)],
+                                           const RawB<VB>& qraw, const float (&av)[VB / sizeof(T)],
+                                           const float (&an)[VB / sizeof(T)], Soft<VB / sizeof(T)>& st) {
+  constexpr int VEL = VB / (int)sizeof(T);
+  constexpr int NW = VB >= 4 ? VB / 4 : 1;
   const T* K = reinterpret_cast<const T*>(p.k);
   const T* V = reinterpret_cast<const T*>(p.v);
-  // this lane's slice of a row; lanes past the row read its first slice (their
-  // query / attention-vector slices are zero, so they add nothing)
-  const uint32_t loff = d_ok ? (uint32_t)(sl * VEL) : 0u;
+  // loff: this lane's slice of a row; lanes without data read their head
+  // group's first slice (their query / attention-vector slices are zero, so
+  // they add nothing)
   const int64_t ld = p.row_elems;
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
     for (int u0 = 0; u0 < nb; u0 += UU) {
       int c[UU];
-      Raw<NV> x[UU];
-      Raw<NV> y[UU];
+      RawB<VB> x[UU];
+      RawB<VB> y[UU];
 #pragma unroll
       for (int u = 0; u < UU; ++u)
         c[u] = (LPE == 64) ? __builtin_amdgcn_readlane(my_c, u0 + u)  // one slot per wave: scalar
@@ -147,8 +154,8 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
         const int cu = (u0 + u < nb) ? c[u] : c[0];
-        load_raw<T, NV>(K + (int64_t)cu * ld + loff, x[u]);
-        if constexpr (KIND == K_GT) load_raw<T, NV>(V + (int64_t)cu * ld + loff, y[u]);
+        load_rawb<T, VB>(K + (int64_t)cu * ld + loff, x[u]);
+        if constexpr (KIND == K_GT) load_rawb<T, VB>(V + (int64_t)cu * ld + loff, y[u]);
       }
       float s[UU];
 #pragma unroll
@@ -157,19 +164,21 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
         if constexpr (KIND == K_GATV2) {
 #pragma unroll
           for (int k = 0; k < VEL; ++k) {
-            const float z = qv[k] + elem<T, NV>(x[u], k);
+            const float z = qv[k] + elemb<T, VB>(x[u], k);
             t = fmaf(av[k], z, fmaf(an[k], fabsf(z), t));
           }
         } else if constexpr (sizeof(T) == 2) {
+          // a 2-byte slice has a zero high half in both words
 #pragma unroll
-          for (int k = 0; k < 4 * NV; ++k)
+          for (int k = 0; k < NW; ++k)
             t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qraw.u[k]),
                                                 __builtin_bit_cast(bf16x2_t, x[u].u[k]), t, false);
         } else {
 #pragma unroll
-          for (int k = 0; k < VEL; ++k) t = fmaf(qv[k], elem<T, NV>(x[u], k), t);
+          for (int k = 0; k < VEL; ++k) t = fmaf(qv[k], elemb<T, VB>(x[u], k), t);
         }
-        t = head_sum<LPH>(t);
+        if constexpr (LPH > 0) t = head_sum<LPH>(t);
+        else t = head_sum_rt(t, p.lph);
         if constexpr (KIND == K_GT) t *= p.qscale;
         s[u] = (u0 + u < nb) ? t : -INFINITY;
       }
@@ -186,30 +195,33 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
         st.l += pu;
 #pragma unroll
         for (int k = 0; k < VEL; ++k)
-          st.acc[k] = fmaf(pu, (KIND == K_GT) ? elem<T, NV>(y[u], k) : elem<T, NV>(x[u], k), st.acc[k]);
+          st.acc[k] = fmaf(pu, (KIND == K_GT) ? elemb<T, VB>(y[u], k) : elemb<T, VB>(x[u], k), st.acc[k]);
       }
       st.m = mn;
     }
   }
 }
 
-// Output row of one slot.  A lane holds VEL consecutive elements; with
-// VEL > 4 a direct store would leave every 128-byte line half written per
-// instruction (such rows reach HBM at a third of its write bandwidth), so the
-// row is staged in LDS (`stage`, LPE * VEL words of this slot) and stored as
-// 16 contiguous bytes per lane.  Called by every lane of the slot.
-template <int LPE, int VEL, int LPH>
-__device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int sl, int head, bool d_ok,
-                                            const Soft<VEL>& st, float* stage) {
+// Output slice of one slot: the head group's elements [goff, goff + gel) of
+// the row; this lane's VEL elements sit at loff (valid when d_ok).  A lane
+// with VEL > 4 holds more than 16 contiguous bytes, and stored directly each
+// instruction would leave every 128-byte line half written (such rows reach
+// HBM at a third of its write bandwidth), so the slice is staged in LDS
+// (`stage`, LPE * VEL words of this slot) and stored as 16 contiguous bytes
+// per lane.  Called by every lane of the slot.
+template <int LPE, int VEL>
+__device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int head, bool d_ok, bool lead,
+                                            uint32_t loff, uint32_t goff, int gel, int sl, const Soft<VEL>& st,
+                                            float* stage) {
   float o[VEL];
   const float inv = st.l > 0.0f ? 1.0f / st.l : 0.0f;
 #pragma unroll
   for (int k = 0; k < VEL; ++k) o[k] = st.acc[k] * inv;
   float* dst = p.out + row * p.row_elems;
   if constexpr (VEL <= 4) {
-    if (d_ok) store_row_nt<VEL>(dst + sl * VEL, o);
+    if (d_ok) store_elems_nt<VEL>(dst + loff, o);
   } else {
-    if (d_ok) store_row<VEL>(stage + sl * VEL, o);
+    if (d_ok) store_row<VEL>(stage + (loff - goff), o);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -217,31 +229,42 @@ __device__ __forceinline__ void write_final(const AttParams& p, int64_t row, int
     for (int j = 0; j < VEL / 4; ++j) {
       const int c = (j * LPE + sl) * 4;
       const float4 t = *reinterpret_cast<const float4*>(stage + c);
-      if (c < p.row_elems)
-        __builtin_nontemporal_store(nt_f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<nt_f32x4*>(dst + c));
+      if (c < gel)
+        __builtin_nontemporal_store(nt_f32x4{t.x, t.y, t.z, t.w}, reinterpret_cast<nt_f32x4*>(dst + goff + c));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  if (p.lse && d_ok && (sl % LPH) == 0)
+  if (p.lse && d_ok && lead)
     p.lse[row * p.H + head] = st.l > 0.0f ? st.m * kLn2 + logf(st.l) : -INFINITY;
 }
 
 // GATv2 asks for five waves per SIMD (90 VGPRs, no spills): left alone the
 // compiler takes 103 and four, and the VALU-bound kernel runs 7% slower.
-template <typename T, int LPE, int NV, int KIND, int UU, int LPH>
+template <typename T, int LPE, int VB, int KIND, int UU, int LPH>
 __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GATV2 ? 5 : 1))) void k_attention(
     AttParams p) {
-  constexpr int VEL = (16 / (int)sizeof(T)) * NV;  // elements per lane
+  constexpr int VEL = VB / (int)sizeof(T);  // elements per lane
   constexpr int SPW = 64 / LPE;
   constexpr int NWAVE = WG / 64;
+  constexpr int NW = VB >= 4 ? VB / 4 : 1;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sw = lane / LPE, sl = lane % LPE;
   const int slot_base = sw * LPE;
-  const bool d_ok = sl < p.row_lanes;
-  const int head = d_ok ? sl / LPH : 0;
+  // head group of this grid row; this lane's head in it and slice of the head
+  const int lph = LPH > 0 ? LPH : p.lph;
+  const int hin = sl / lph, j = sl % lph;
+  const int g0 = (int)blockIdx.y * p.hpg;
+  const int hg = g0 + hin;
+  const bool d_ok = hin < p.hpg && hg < p.H && j < p.lph_data;
+  const int head = d_ok ? hg : 0;
+  const uint32_t goff = (uint32_t)g0 * p.D;
+  // a multiple of VEL by construction (D = dv * VEL), so slice loads and
+  // stores stay vectorised
+  const uint32_t loff = d_ok ? (uint32_t)((hg * p.dv + j) * VEL) : goff;
+  const int gel = (min(p.H, g0 + p.hpg) - g0) * p.D;
 
   const int n_item_pad = (p.n_item_blocks + 7) & ~7;
   const bool is_item = (int)blockIdx.x < n_item_pad;
@@ -273,35 +296,35 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GA
 
   // destination-side slice (and the attention vector for GATv2)
   float qv[VEL], av[VEL], an[VEL];
-  Raw<NV> qraw;
+  RawB<VB> qraw;
   if (d_ok) {
-    load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + sl * VEL, qraw);
+    load_rawb<T, VB>(reinterpret_cast<const T*>(p.q) + row * p.row_elems + loff, qraw);
 #pragma unroll
-    for (int k = 0; k < VEL; ++k) qv[k] = elem<T, NV>(qraw, k);
+    for (int k = 0; k < VEL; ++k) qv[k] = elemb<T, VB>(qraw, k);
     if constexpr (KIND == K_GATV2) {
 #pragma unroll
       for (int k = 0; k < VEL; ++k) {
-        const float a = p.att[sl * VEL + k] * kLog2e;
+        const float a = p.att[loff + k] * kLog2e;
         av[k] = a * (0.5f + 0.5f * p.slope);
         an[k] = a * (0.5f - 0.5f * p.slope);
       }
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 4 * NV; ++k) qraw.u[k] = 0u;
+    for (int k = 0; k < NW; ++k) qraw.u[k] = 0u;
 #pragma unroll
     for (int k = 0; k < VEL; ++k) qv[k] = av[k] = an[k] = 0.0f;
   }
 
   Soft<VEL> st;
   st.init();
-  scan_edges<T, LPE, NV, KIND, UU, LPH>(p, eb, ee, sl, slot_base, d_ok, qv, qraw, av, an, st);
+  scan_edges<T, LPE, VB, KIND, UU, LPH>(p, eb, ee, sl, slot_base, loff, qv, qraw, av, an, st);
 
   // s_a merges the waves of an item; light rows stage their output in it
   // (one LPE x VEL region per slot)
   __shared__ __align__(16) float s_a[NWAVE][64][VEL];
   if (!is_item) {
-    write_final<LPE, VEL, LPH>(p, row, sl, head, d_ok, st, &s_a[wave][slot_base][0]);
+    write_final<LPE, VEL>(p, row, head, d_ok, j == 0, loff, goff, gel, sl, st, &s_a[wave][slot_base][0]);
     return;
   }
 
@@ -325,11 +348,11 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GA
     st.merge(s_m[w][sl], s_l[w][sl], a2);
   }
   if (m_idx < 0) {
-    write_final<LPE, VEL, LPH>(p, row, sl, head, d_ok, st, &s_a[0][0][0]);
+    write_final<LPE, VEL>(p, row, head, d_ok, j == 0, loff, goff, gel, sl, st, &s_a[0][0][0]);
   } else {
     if (!d_ok) return;
-    store_row<VEL>(p.pacc + (int64_t)item * p.row_elems + sl * VEL, st.acc);
-    if ((sl % LPH) == 0) {
+    store_elems<VEL>(p.pacc + (int64_t)item * p.row_elems + loff, st.acc);
+    if (j == 0) {
       p.pml[((int64_t)item * 2 + 0) * p.H + head] = st.m;
       p.pml[((int64_t)item * 2 + 1) * p.H + head] = st.l;
     }
@@ -360,15 +383,16 @@ __global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* mu
   }
 }
 
-template <typename T, int LPE, int NV, int KIND, int LPH>
-int launch_att_h(gnn_plan* pl, AttParams& p, hipStream_t s) {
+template <typename T, int LPE, int VB, int KIND, int LPH>
+int launch_att_h(gnn_plan* pl, AttParams& p, int groups, hipStream_t s) {
   constexpr int UU = GNN_ATT_U;
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.n_item_blocks = (int32_t)pl->n_items;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
-  if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
-  hipLaunchKernelGGL((k_attention<T, LPE, NV, KIND, UU, LPH>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+  if (gx > 0x7FFFFFFF || groups > 65535) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
+  hipLaunchKernelGGL((k_attention<T, LPE, VB, KIND, UU, LPH>), dim3((unsigned)gx, (unsigned)groups), dim3(WG), 0,
+                     s, p);
   GNN_LAUNCH_CHECK("attention");
   if (pl->n_multi > 0) {
     hipLaunchKernelGGL(k_att_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p,
@@ -379,61 +403,111 @@ int launch_att_h(gnn_plan* pl, AttParams& p, hipStream_t s) {
 }
 
 // lanes per head is a power of two no larger than the slot
-template <typename T, int LPE, int NV, int KIND>
-int launch_att(gnn_plan* pl, AttParams& p, hipStream_t s) {
+template <typename T, int LPE, int VB, int KIND>
+int launch_att(gnn_plan* pl, AttParams& p, int groups, hipStream_t s) {
   switch (p.lph) {
-    case 1: return launch_att_h<T, LPE, NV, KIND, 1>(pl, p, s);
-    case 2: return launch_att_h<T, LPE, NV, KIND, 2>(pl, p, s);
-    case 4: return launch_att_h<T, LPE, NV, KIND, 4>(pl, p, s);
-    case 8: return launch_att_h<T, LPE, NV, KIND, 8>(pl, p, s);
+    case 1: return launch_att_h<T, LPE, VB, KIND, 1>(pl, p, groups, s);
+    case 2: return launch_att_h<T, LPE, VB, KIND, 2>(pl, p, groups, s);
+    case 4: return launch_att_h<T, LPE, VB, KIND, 4>(pl, p, groups, s);
+    case 8: return launch_att_h<T, LPE, VB, KIND, 8>(pl, p, groups, s);
     default: break;
   }
-  if constexpr (LPE >= 16) if (p.lph == 16) return launch_att_h<T, LPE, NV, KIND, 16>(pl, p, s);
-  if constexpr (LPE >= 32) if (p.lph == 32) return launch_att_h<T, LPE, NV, KIND, 32>(pl, p, s);
-  if constexpr (LPE >= 64) if (p.lph == 64) return launch_att_h<T, LPE, NV, KIND, 64>(pl, p, s);
+  if constexpr (LPE >= 16) if (p.lph == 16) return launch_att_h<T, LPE, VB, KIND, 16>(pl, p, groups, s);
+  if constexpr (LPE >= 32) if (p.lph == 32) return launch_att_h<T, LPE, VB, KIND, 32>(pl, p, groups, s);
+  if constexpr (LPE >= 64) if (p.lph == 64) return launch_att_h<T, LPE, VB, KIND, 64>(pl, p, groups, s);
   return fail(GNN_ERR_UNSUPPORTED, "lanes per head exceed the slot");
 }
 
+// Lane mapping of one call: bytes per lane, slot width, head groups.
+struct Mapping {
+  int vb = 16, lpe = 64, groups = 1;
+};
+
 template <typename T, int KIND>
-int dispatch(gnn_plan* pl, AttParams& p, int lpe, int nv, hipStream_t s) {
-  if (nv == 2) {
-    // GATv2 rows are at most 1 KB (checked at the entry point), so only GT
-    // instantiates the 32-bytes-per-lane kernels.
+int dispatch(gnn_plan* pl, AttParams& p, const Mapping& mp, hipStream_t s) {
+  if (mp.vb < 16) {
+    // generic mapping: one 64-lane slot per edge, lanes per head at run time
+    if constexpr (sizeof(T) == 2) {
+      if (mp.vb == 2) return launch_att_h<T, 64, 2, KIND, 0>(pl, p, mp.groups, s);
+    }
+    if (mp.vb == 4) return launch_att_h<T, 64, 4, KIND, 0>(pl, p, mp.groups, s);
+    return launch_att_h<T, 64, 8, KIND, 0>(pl, p, mp.groups, s);
+  }
+  if (mp.vb == 32) {
+    // GATv2 rows of more than 1 KB take head groups of 16-byte lanes, so only
+    // GT instantiates the 32-bytes-per-lane kernels.
     if constexpr (KIND == K_GATV2) {
-      return fail(GNN_ERR_UNSUPPORTED, "GATv2 rows wider than 1 KB");
+      return fail(GNN_ERR_UNSUPPORTED, "GATv2 has no 32-byte lane mapping");
     } else {
-      switch (lpe) {
-        case 8: return launch_att<T, 8, 2, KIND>(pl, p, s);
-        case 16: return launch_att<T, 16, 2, KIND>(pl, p, s);
-        case 32: return launch_att<T, 32, 2, KIND>(pl, p, s);
-        default: return launch_att<T, 64, 2, KIND>(pl, p, s);
+      switch (mp.lpe) {
+        case 8: return launch_att<T, 8, 32, KIND>(pl, p, mp.groups, s);
+        case 16: return launch_att<T, 16, 32, KIND>(pl, p, mp.groups, s);
+        case 32: return launch_att<T, 32, 32, KIND>(pl, p, mp.groups, s);
+        default: return launch_att<T, 64, 32, KIND>(pl, p, mp.groups, s);
       }
     }
   }
-  switch (lpe) {
-    case 8: return launch_att<T, 8, 1, KIND>(pl, p, s);
-    case 16: return launch_att<T, 16, 1, KIND>(pl, p, s);
-    case 32: return launch_att<T, 32, 1, KIND>(pl, p, s);
-    default: return launch_att<T, 64, 1, KIND>(pl, p, s);
+  switch (mp.lpe) {
+    case 8: return launch_att<T, 8, 16, KIND>(pl, p, mp.groups, s);
+    case 16: return launch_att<T, 16, 16, KIND>(pl, p, mp.groups, s);
+    case 32: return launch_att<T, 32, 16, KIND>(pl, p, mp.groups, s);
+    default: return launch_att<T, 64, 16, KIND>(pl, p, mp.groups, s);
   }
 }
 
-int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* lpe, int* nv,
-          hipStream_t s) {
+int pow2_at_least(int x) {
+  int l = 1;
+  while (l < x) l <<= 1;
+  return l;
+}
+
+// The lane mapping for heads of D elements of esz bytes (the entry points
+// checked H, D > 0 and 16-byte aligned bases).
+//   - heads of a multiple of 16 bytes: 16-byte lane slices (32-byte ones for
+//     GT rows of 1-2 KB whose heads fill a power of two of them); lanes per
+//     head rounded up to a power of two; the row in one slot when it fits 64
+//     lanes, else cut into groups of 64 / lph heads;
+//   - other heads: the widest of 8-, 4- or 2-byte slices that divides the
+//     head, at most 64 lanes per head, 64-lane slots, groups as above.
+int choose_mapping(int kind, int esz, int H, int D, Mapping* mp, int* lph, int* lph_data, int* hpg) {
+  const int64_t hb = (int64_t)D * esz, rowb = (int64_t)H * hb;
+  const bool gt_wide = kind == K_GT && rowb > 1024 && rowb <= 2048 && hb % 32 == 0 &&
+                       ((hb / 32) & (hb / 32 - 1)) == 0;
+  if (gt_wide) {
+    mp->vb = 32;
+    *lph_data = *lph = (int)(hb / 32);
+  } else if (hb % 16 == 0 && hb / 16 <= 64) {
+    mp->vb = 16;
+    *lph_data = (int)(hb / 16);
+    *lph = pow2_at_least(*lph_data);
+  } else {
+    mp->vb = 0;
+    for (int vb = 8; vb >= esz; vb >>= 1)
+      if (hb % vb == 0 && hb / vb <= 64) {
+        mp->vb = vb;
+        break;
+      }
+    if (mp->vb == 0)
+      return fail(GNN_ERR_UNSUPPORTED, "head too wide for the generic attention mapping: D * sizeof must be a "
+                                       "multiple of 16 bytes up to 1 KB, or at most 64 slices of 8, 4 or 2 bytes");
+    *lph_data = (int)(hb / mp->vb);
+    *lph = pow2_at_least(*lph_data);
+  }
+  if (mp->vb >= 16 && (int64_t)H * *lph <= 64) {
+    *hpg = H;
+    mp->groups = 1;
+    mp->lpe = std::max(8, pow2_at_least(H * *lph));
+  } else {
+    *hpg = 64 / *lph;
+    mp->groups = (H + *hpg - 1) / *hpg;
+    mp->lpe = 64;
+  }
+  return GNN_OK;
+}
+
+int setup(gnn_plan* pl, AttParams& p, int kind, gnn_dtype xt, int32_t H, int32_t D, Mapping* mp, hipStream_t s) {
   const int esz = xt == GNN_BF16 ? 2 : 4;
-  const int rowb = H * D * esz;
-  *nv = rowb > 1024 ? 2 : 1;
-  const int vb = 16 * *nv;  // bytes per lane
-  if ((D * esz) % vb != 0)
-    return fail(GNN_ERR_UNSUPPORTED, "head dimension does not fill whole lane vectors");
-  const int lph = D * esz / vb;
-  if ((lph & (lph - 1)) != 0)
-    return fail(GNN_ERR_UNSUPPORTED, "lanes per head must be a power of two");
-  const int lanes = rowb / vb;
-  int l = 8;
-  while (l < lanes) l <<= 1;
-  if (l > 64) return fail(GNN_ERR_UNSUPPORTED, "row too wide");
-  *lpe = l;
+  GNN_TRY(choose_mapping(kind, esz, H, D, mp, &p.lph, &p.lph_data, &p.hpg));
   p.row_ptr = pl->row_ptr;
   p.col_idx = pl->col_idx;
   p.items = pl->items;
@@ -441,8 +515,7 @@ int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* l
   p.H = H;
   p.D = D;
   p.row_elems = H * D;
-  p.row_lanes = lanes;
-  p.lph = lph;
+  p.dv = (int32_t)((int64_t)D * esz / mp->vb);
   // One slot per row up to kAttLightMax edges, never below the plan's own
   // light threshold (its longer rows are the plan's items) and never above
   // its heavy threshold (split rows go through the items alone).  The rows
@@ -467,8 +540,8 @@ int setup(gnn_plan* pl, AttParams& p, gnn_dtype xt, int32_t H, int32_t D, int* l
 int launch_gatv2(gnn_plan* pl, const void* xl, const void* xr, gnn_dtype xt, const float* att,
                  int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s) {
   AttParams p{};
-  int lpe = 0, nv = 1;
-  GNN_TRY(setup(pl, p, xt, H, D, &lpe, &nv, s));
+  Mapping mp;
+  GNN_TRY(setup(pl, p, K_GATV2, xt, H, D, &mp, s));
   p.q = xl;
   p.k = xr;
   p.v = xr;
@@ -476,23 +549,29 @@ int launch_gatv2(gnn_plan* pl, const void* xl, const void* xr, gnn_dtype xt, con
   p.out = out;
   p.lse = lse;
   p.slope = slope;
-  if (xt == GNN_BF16) return dispatch<uint16_t, K_GATV2>(pl, p, lpe, nv, s);
-  return dispatch<float, K_GATV2>(pl, p, lpe, nv, s);
+  if (xt == GNN_BF16) return dispatch<uint16_t, K_GATV2>(pl, p, mp, s);
+  return dispatch<float, K_GATV2>(pl, p, mp, s);
 }
 
 int launch_gt_csr(gnn_plan* pl, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
                   int32_t D, float scale, float* out, float* lse, hipStream_t s) {
   AttParams p{};
-  int lpe = 0, nv = 1;
-  GNN_TRY(setup(pl, p, xt, H, D, &lpe, &nv, s));
+  Mapping mp;
+  GNN_TRY(setup(pl, p, K_GT, xt, H, D, &mp, s));
   p.q = q;
   p.k = k;
   p.v = v;
   p.out = out;
   p.lse = lse;
   p.qscale = scale * kLog2e;
-  if (xt == GNN_BF16) return dispatch<uint16_t, K_GT>(pl, p, lpe, nv, s);
-  return dispatch<float, K_GT>(pl, p, lpe, nv, s);
+  if (xt == GNN_BF16) return dispatch<uint16_t, K_GT>(pl, p, mp, s);
+  return dispatch<float, K_GT>(pl, p, mp, s);
+}
+
+int attention_mapping_supported(int gt, gnn_dtype xt, int32_t H, int32_t D) {
+  Mapping mp;
+  int a, b, c;
+  return choose_mapping(gt ? K_GT : K_GATV2, xt == GNN_BF16 ? 2 : 4, H, D, &mp, &a, &b, &c);
 }
 
 }  // namespace gnn

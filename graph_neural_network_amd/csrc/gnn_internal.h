@@ -143,6 +143,9 @@ int launch_gatv2(gnn_plan* p, const void* xl, const void* xr, gnn_dtype xt, cons
                  int32_t H, int32_t D, float slope, float* out, float* lse, hipStream_t s);
 int launch_gt_csr(gnn_plan* p, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
                   int32_t D, float scale, float* out, float* lse, hipStream_t s);
+// GNN_OK if the fused CSR attention kernels have a lane mapping for heads
+// of D elements of `xt` (gt: Graph Transformer, else GATv2).
+int attention_mapping_supported(int gt, gnn_dtype xt, int32_t H, int32_t D);
 int launch_gt_block16(gnn_plan* p, const void* q, const void* k, const void* v, int32_t H,
                       int32_t D, float scale, float* out, float* lse, hipStream_t s);
 int launch_project(const void* X, int32_t n, int32_t f_in, int64_t ldx, int32_t n_mat, const void* const* W,

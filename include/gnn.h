@@ -263,11 +263,15 @@ int gnn_reduce_multi_noalloc(const gnn_csr* csr, const void* X, gnn_dtype xtype,
  * (row stride H*D); att: device [H, D] float32; out: device [n_rows, H, D]
  * float32; lse: device [n_rows, H] float32 or NULL.  One pass with an online
  * softmax: no per-edge logits, weights or messages are written to memory.
- * Supported: xtype BF16 or F32, H*D*sizeof(xtype) at most 1024 bytes,
- * D*sizeof(xtype) a multiple of 16 bytes with D*sizeof(xtype)/16 (lanes per
- * head) a power of two.  plan may be
- * NULL (it then only selects heavy rows for the split-row variant).
- * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, DEVICE. */
+ * Supported head shapes (appendix D.2 pairs head-dimension specialisations
+ * with a fallback): xtype BF16 or F32, any H with H*D < 2^28, and a head of
+ * D*sizeof(xtype) bytes that is either a multiple of 16 bytes up to 1 KB
+ * (16-byte lane slices; lanes per head rounded up to a power of two; rows
+ * wider than 64 lanes run as head groups) or at most 64 slices of the
+ * widest of 8, 4 or 2 bytes dividing it (the generic mapping; every D <= 64
+ * qualifies).  xl, xr, out 16-byte aligned.  plan may be NULL (a transient
+ * one is built).
+ * Errors: INVALID_VALUE, UNSUPPORTED, SIZE_OVERFLOW, PLAN_MISMATCH, DEVICE. */
 int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype,
                     const float* att, int32_t H, int32_t D, float neg_slope, float* out, float* lse,
                     gnn_plan* plan, void* stream);
@@ -280,9 +284,9 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
  * q: device [n_rows, H, D]; k, v: device [n_cols, H, D]; `xtype` BF16 (or F32
  * in CSR mode); scale <= 0 means 1/sqrt(D); out: device [n_rows, H, D]
  * float32; lse: device [n_rows, H] float32 or NULL.
- * GNN_GT_CSR: streaming online softmax; H*D*sizeof(xtype) at most 2048 bytes;
- * a lane holds 16 bytes of a row (32 bytes when the row exceeds 1024 bytes),
- * D*sizeof(xtype) must fill a power-of-two number of lanes.
+ * GNN_GT_CSR: streaming online softmax; head shapes as for gnn_gatv2_fused
+ * (a lane holds 32 bytes of rows of 1-2 KB whose heads fill a power of two
+ * of such slices).
  * GNN_GT_BLOCK16: needs a plan built with build_wsb = 1, square CSR,
  * xtype BF16, D in {32, 64, 128}; dense 16x16 tiles run on bf16 MFMA with the
  * softmax weights rounded to bf16 for the P.V product; the residual edges of

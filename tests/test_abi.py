@@ -65,10 +65,11 @@ INV, UNS, OVF = 1, 2, 5
     ("noalloc no output", lambda: call("gnn_reduce_multi_noalloc", ctypes.byref(fake_csr()), P(16), 0, 4, 4, None, None, None, None, None, None, 4, None, None), INV),
     ("noalloc null csr", lambda: call("gnn_reduce_multi_noalloc", None, P(16), 0, 4, 4, P(16), None, None, None, None, None, 4, None, None), INV),
     ("gatv2 H=0", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 0, 32, ctypes.c_float(0.2), P(16), None, None, None), INV),
-    ("gatv2 too wide", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), None, None, None), UNS),
-    ("gatv2 D*2 % 16", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 12, ctypes.c_float(0.2), P(16), None, None, None), UNS),
-    ("gatv2 H*D overflow", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2**28, 16, ctypes.c_float(0.2), P(16), None, None, None), UNS),
-    ("gt H*D overflow", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), 0, P(16), None, None, None), UNS),
+    ("gatv2 head of 130 slices", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 1, 1040, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gatv2 head of 65 4-byte slices", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 130, ctypes.c_float(0.2), P(16), None, None, None), UNS),
+    ("gt head of 129 f32", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 0, 2, 129, ctypes.c_float(0), 0, P(16), None, None, None), UNS),
+    ("gatv2 H*D overflow", lambda: call("gnn_gatv2_fused", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2**28, 16, ctypes.c_float(0.2), P(16), None, None, None), OVF),
+    ("gt H*D overflow", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), 0, P(16), None, None, None), OVF),
     ("gt bad mode", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), 5, P(16), None, None, None), INV),
     ("gt block16 f32", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 0, 8, 64, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
     ("gt block16 D=48", lambda: call("gnn_gt_fused", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2, 48, ctypes.c_float(0), 1, P(16), None, None, None), UNS),
