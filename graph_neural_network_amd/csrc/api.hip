@@ -384,9 +384,8 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   if (mode != GNN_GT_CSR && mode != GNN_GT_BLOCK16 && mode != GNN_GT_AUTO)
     return fail(GNN_ERR_INVALID_VALUE, "unknown GT mode");
   if (mode == GNN_GT_AUTO) {
-    const int64_t esz0 = xtype == GNN_BF16 ? 2 : 4;
-    bool fits = xtype == GNN_BF16 && (D == 32 || D == 64 || D == 128) && csr && csr->n_rows == csr->n_cols &&
-                (D * esz0) % 16 == 0 && H > 0 && (int64_t)H * D * esz0 <= 2048;
+    bool fits = xtype == GNN_BF16 && (D == 32 || D == 64 || D == 128 || D == 256) && csr &&
+                csr->n_rows == csr->n_cols && H > 0 && (int64_t)H * D < ((int64_t)1 << 28);
     mode = GNN_GT_CSR;
     if (fits && plan && plan->has_wsb && check_plan(plan, csr) == GNN_OK) {
       const int64_t dense = plan->nnz - plan->wsb.n_resid;
@@ -402,11 +401,8 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   if ((int64_t)H * D >= ((int64_t)1 << 28)) return fail(GNN_ERR_SIZE_OVERFLOW, "H * D too large");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
     return fail(GNN_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
-  if (mode == GNN_GT_BLOCK16) {
-    if (xtype != GNN_BF16 || (D != 32 && D != 64 && D != 128))
-      return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs bf16 and D in {32, 64, 128}");
-    if ((int64_t)H * D * 2 > 2048) return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs H*D*2 <= 2048 bytes");
-  }
+  if (mode == GNN_GT_BLOCK16 && (xtype != GNN_BF16 || (D != 32 && D != 64 && D != 128 && D != 256)))
+    return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 needs bf16 and D in {32, 64, 128, 256}");
   GNN_TRY(attention_mapping_supported(1, xtype, H, D));
   if (csr->n_rows == 0) return GNN_OK;
   float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);

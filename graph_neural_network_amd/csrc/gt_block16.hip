@@ -10,7 +10,7 @@
 // query 16 keys.
 //
 // MI355X mapping.  One workgroup of two waves per window; wave w handles
-// heads w, w + 2, ...  The window's tile metadata (columns, bitmaps) is staged
+// heads w, w + 2, ... (D in {32, 64, 128, 256}, any number of heads).  The window's tile metadata (columns, bitmaps) is staged
 // in LDS once, and each wave keeps the next tile's K / V loads in flight
 // while it computes the current one.  For a tile the wave computes the transposed scores
 // S^T = K_blk Q_win^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = the
@@ -100,6 +100,8 @@ constexpr int MAXT = 32;  // tiles of a window staged in LDS (larger windows rea
 // Latency decides this kernel's speed (each wave keeps one tile of K / V in
 // flight while it computes another), so D <= 64 asks for four waves per SIMD
 // (at most 128 VGPRs) rather than the three its natural allocation allows.
+// At D = 256 a tile's K and V slices alone take 64 registers per lane and the
+// output block 64 more: one tile at a time, two waves per SIMD.
 template <int D, int NWAVE>
 __global__ __launch_bounds__(NWAVE * 64) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2)))
 void k_gt_block16(B16Params p) {
@@ -238,15 +240,23 @@ void k_gt_block16(B16Params p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    // two-deep pipeline: the next tile's K / V are in flight while one computes
-    s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
-    if (t_beg < t_end) load_kv(t_beg, kA, vA);
-    for (int t = t_beg; t < t_end; t += 2) {
-      if (t + 1 < t_end) load_kv(t + 1, kB, vB);
-      process(t, kA, vA);
-      if (t + 1 < t_end) {
-        if (t + 2 < t_end) load_kv(t + 2, kA, vA);
-        process(t + 1, kB, vB);
+    if constexpr (D <= 128) {
+      // two-deep pipeline: the next tile's K / V are in flight while one computes
+      s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
+      if (t_beg < t_end) load_kv(t_beg, kA, vA);
+      for (int t = t_beg; t < t_end; t += 2) {
+        if (t + 1 < t_end) load_kv(t + 1, kB, vB);
+        process(t, kA, vA);
+        if (t + 1 < t_end) {
+          if (t + 2 < t_end) load_kv(t + 2, kA, vA);
+          process(t + 1, kB, vB);
+        }
+      }
+    } else {
+      s16x8 kA[KC], vA[KC];
+      for (int t = t_beg; t < t_end; ++t) {
+        load_kv(t, kA, vA);
+        process(t, kA, vA);
       }
     }
 
@@ -341,7 +351,8 @@ int launch_gt_block16(gnn_plan* pl, const void* q, const void* k, const void* v,
   if (D == 32) GNN_B16(32);
   else if (D == 64) GNN_B16(64);
   else if (D == 128) GNN_B16(128);
-  else return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 head dim must be 32, 64 or 128");
+  else if (D == 256) GNN_B16(256);
+  else return fail(GNN_ERR_UNSUPPORTED, "BLOCK16 head dim must be 32, 64, 128 or 256");
 #undef GNN_B16
   GNN_LAUNCH_CHECK("gt block16");
   return GNN_OK;

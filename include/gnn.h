@@ -288,7 +288,7 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
  * (a lane holds 32 bytes of rows of 1-2 KB whose heads fill a power of two
  * of such slices).
  * GNN_GT_BLOCK16: needs a plan built with build_wsb = 1, square CSR,
- * xtype BF16, D in {32, 64, 128}; dense 16x16 tiles run on bf16 MFMA with the
+ * xtype BF16, D in {32, 64, 128, 256}, any H; dense 16x16 tiles run on bf16 MFMA with the
  * softmax weights rounded to bf16 for the P.V product; the residual edges of
  * sparse tiles run the CSR loop into the same per-row softmax state.
  * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, DEVICE. */

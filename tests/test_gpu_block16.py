@@ -75,10 +75,10 @@ def run_b16(rp, ci, q, k, v, tau=0, scale=0.0):
     return host(out), host(lse), gnn.gnn_plan_stats(plan)
 
 
-@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128, 256])
 @pytest.mark.parametrize("tau", [1, 32, 10**6])
 def test_gt_block16_cluster(D, tau):
-    H = 8 if D <= 64 else 4
+    H = 8 if D <= 64 else (4 if D == 128 else 2)
     rp, ci = gen.cluster(0x5EED0310, 64 * 30, 64, 0.5, 0.01)
     n = rp.size - 1
     q, k, v = (gen.gauss_bf16(0x1000 + i, (n, H, D)) for i in range(3))
@@ -122,6 +122,33 @@ def test_gt_block16_constant_values_and_csr_agreement():
     ro, rl, va = oracle.gt(rp, ci, q, k, v)
     check(b16, lb16, ro, rl, va)
     check(host(o2), host(l2), ro, rl, va, tol=1e-4)
+
+
+@pytest.mark.parametrize("H,D", [(4, 256), (8, 256), (16, 128), (3, 32)])
+def test_gt_block16_wide_rows(H, D):
+    """Rows of 2-4 KB and odd head counts: each wave of a window walks its
+    share of the heads; parity with the oracle and with the CSR kernel."""
+    rp, ci = gen.cluster(0x5EED0312, 64 * 12, 64, 0.5, 0.01, self_loops=True)
+    n = rp.size - 1
+    q, k, v = (gen.gauss_bf16(0x1100 + D + i, (n, H, D)) for i in range(3))
+    ro, rl, va = oracle.gt(rp, ci, q, k, v)
+    for tau in (1, 32):
+        out, lse, _ = run_b16(rp, ci, q, k, v, tau)
+        check(out, lse, ro, rl, va)
+
+
+def test_gt_block16_d256_config4_graph():
+    """BLOCK16 at H = 2, D = 256 on the 512,000-node cluster graph of the GT
+    configuration, sampled rows."""
+    w = gen.gt_cluster(H=2, D=256)
+    rp, ci = w.row_ptr, w.col_idx
+    q, k, v = w.arrays["q"], w.arrays["k"], w.arrays["v"]
+    out, lse, st = run_b16(rp, ci, q, k, v, -1)
+    assert st["wsb_dense_tiles"] > 0
+    rng = np.random.default_rng(10)
+    rows = np.unique(rng.integers(0, rp.size - 1, 2000)).astype(np.int32)
+    ro, rl, va = oracle.gt(rp, ci, q, k, v, rows=rows)
+    check(out, lse, ro, rl, va, rows=rows)
 
 
 def test_gt_block16_cluster512k_full():
