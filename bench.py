@@ -78,6 +78,22 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
+VALU_PEAK_GINST = 256 * 4 * 2.4 / 4  # wave64 VALU instructions per ns: 4 cycles per instruction per SIMD
+
+
+def load_profile(workload: str):
+    """The stored counter profile of a workload (profiles/traffic_<workload>.json)
+    if its kernel sources are unchanged since, else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    return d if d.get("source_hash") == kernel_source_hash(workload) else None
+
+
 def load_traffic(workload: str, kernel: str):
     """Counter-derived HBM bytes per launch, if a profile of the current
     kernel sources exists (profiles/traffic_<workload>.json)."""
@@ -273,7 +289,7 @@ def wl_gatv2(args):
            "step": "gnn_project (l, r) then gnn_gatv2_fused; value = edges / (both)",
            "plan": gnn.gnn_plan_stats(plan)}
     comp = 4 * (n + 1) + 4 * m + 2 * n * row_b + H * D * 4 + n * (H * D * 4 + H * 4)
-    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 1, 0, 4, 4>",
+    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 16, 0, 4, 4>",
             "config": cfg, "dtype": "bf16", "cpu": cpu, "compulsory": comp, "cpu_1thread": True,
             "keep": (w, csr, plan, X, Wl, Wr, xl, xr, att, out, lse)}
 
@@ -317,7 +333,7 @@ def wl_gt(args, mode="csr"):
     cfg = {"workload": w.name + ("_block16" if mode == "block16" else "_csr"), "graph": "cluster(64, 0.5, 1%)+self-loops",
            "nodes": n, "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16", "mode": mode,
            "plan_build_ms": round(plan_ms, 2), "plan": st}
-    kern = "k_attention<unsigned short, 64, 1, 1, 4, 8>" if mode == "csr" else "k_gt_block16<64, 2>"
+    kern = "k_attention<unsigned short, 64, 16, 1, 4, 8>" if mode == "csr" else "k_gt_block16<64, 2>"
     # every tensor once (BLOCK16 also reads the WSB layout: window and tile offsets, 48-byte
     # blocks, tile list, residual CSR)
     comp = 4 * (n + 1) + 4 * m + 3 * n * row_b + n * (H * D * 4 + H * 4)
@@ -982,6 +998,19 @@ def main():
         # calibrated FETCH_SIZE + WRITE_SIZE bytes of the dominant launch over its time
         out["hbm_counter"] = {"bytes": traffic, "gbps": traffic / (dom_ms * 1e-3) / 1e9,
                               "frac": traffic / (dom_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    prof = load_profile(args.workload)
+    kd = (prof or {}).get("kernels", {}).get(w["kernel"], {}) if isinstance(w["kernel"], str) else {}
+    if kd.get("sq"):
+        # issue roofline of the dominant kernel: its VALU wave instructions (SQ_INSTS_VALU of the
+        # stored profile) over this run's launch time, against 614.4 G/s; matrix-core busy share
+        sq = kd["sq"]
+        rate = sq["SQ_INSTS_VALU"] / (dom_ms * 1e-3) / 1e9
+        out["valu_issue"] = {"insts_per_launch": sq["SQ_INSTS_VALU"], "achieved_ginst_s": rate,
+                             "peak_ginst_s": VALU_PEAK_GINST, "frac": rate / VALU_PEAK_GINST,
+                             "insts_per_edge": sq["SQ_INSTS_VALU"] / dom.edges if dom.edges else None,
+                             "wait_frac": sq.get("SQ_WAIT_ANY", 0) / max(sq.get("SQ_WAVE_CYCLES", 1), 1)}
+        if kd.get("grbm_gui_active") and sq.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            out["valu_issue"]["mfma_busy"] = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (kd["grbm_gui_active"] / 8 * 1024)
     if w.get("compulsory"):
         # each input and output tensor once: the floor if every gather hit in cache
         c = w["compulsory"]

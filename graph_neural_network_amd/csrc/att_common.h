@@ -118,6 +118,33 @@ __device__ __forceinline__ void load_raw(const T* p, Raw<NV>& r) {
   load_rawb<T, 16 * NV>(p, r);
 }
 
+// The same slice through a buffer resource whose base is a node row held in
+// scalar registers (a row shared by the whole wave): the lane's byte offset
+// is the only per-lane address operand, so a gather costs no vector ALU
+// work.  num_records bounds the row; the descriptor's last word is the one
+// the gfx9 family (gfx950 included) takes for raw untyped buffer access.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(row), (short)0, bytes, kBufferWord3);
+}
+template <int VB>
+__device__ __forceinline__ void load_rawb_buf(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, RawB<VB>& r) {
+  if constexpr (VB == 2) {
+    r.u[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, byte_off, 0, 0);
+  } else if constexpr (VB == 4) {
+    r.u[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, 0, 0);
+  } else if constexpr (VB == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, 0, 0);
+    r.u[0] = v[0]; r.u[1] = v[1];
+  } else {
+#pragma unroll
+    for (int k = 0; k < VB / 16; ++k) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off + 16 * k, 0, 0);
+      r.u[4 * k] = v[0]; r.u[4 * k + 1] = v[1]; r.u[4 * k + 2] = v[2]; r.u[4 * k + 3] = v[3];
+    }
+  }
+}
+
 // element k of a raw slice as float
 template <typename T, int VB>
 __device__ __forceinline__ float elemb(const RawB<VB>& r, int k) {

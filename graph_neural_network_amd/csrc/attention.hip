@@ -137,6 +137,8 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
   // group's first slice (their query / attention-vector slices are zero, so
   // they add nothing)
   const int64_t ld = p.row_elems;
+  const int row_bytes = p.row_elems * (int)sizeof(T);
+  const uint32_t loff_b = loff * (uint32_t)sizeof(T);
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
@@ -154,8 +156,14 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
         const int cu = (u0 + u < nb) ? c[u] : c[0];
-        load_rawb<T, VB>(K + (int64_t)cu * ld + loff, x[u]);
-        if constexpr (KIND == K_GT) load_rawb<T, VB>(V + (int64_t)cu * ld + loff, y[u]);
+        if constexpr (LPE == 64) {
+          // the wave's row: base in scalar registers, the lane's slice an offset
+          load_rawb_buf<VB>(row_rsrc(K + (int64_t)cu * ld, row_bytes), loff_b, x[u]);
+          if constexpr (KIND == K_GT) load_rawb_buf<VB>(row_rsrc(V + (int64_t)cu * ld, row_bytes), loff_b, y[u]);
+        } else {
+          load_rawb<T, VB>(K + (int64_t)cu * ld + loff, x[u]);
+          if constexpr (KIND == K_GT) load_rawb<T, VB>(V + (int64_t)cu * ld + loff, y[u]);
+        }
       }
       float s[UU];
 #pragma unroll
@@ -179,19 +187,23 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
         }
         if constexpr (LPH > 0) t = head_sum<LPH>(t);
         else t = head_sum_rt(t, p.lph);
-        if constexpr (KIND == K_GT) t *= p.qscale;
         s[u] = (u0 + u < nb) ? t : -INFINITY;
       }
-      float mn = st.m;
+      // GT scores stay unscaled until the exponent: the batch maximum is
+      // scaled once, each weight is exp2(fma(s, scale log2 e, -max))
+      // (scale > 0; an edge past the slot's end gives exp2(-inf) = 0)
+      float mx = s[0];
 #pragma unroll
-      for (int u = 0; u < UU; ++u) mn = fmaxf(mn, s[u]);
+      for (int u = 1; u < UU; ++u) mx = fmaxf(mx, s[u]);
+      const float qs = (KIND == K_GT) ? p.qscale : 1.0f;
+      const float mn = fmaxf(st.m, (KIND == K_GT) ? mx * qs : mx);
       const float corr = ex2(st.m - mn);
       st.l *= corr;
 #pragma unroll
       for (int k = 0; k < VEL; ++k) st.acc[k] *= corr;
 #pragma unroll
       for (int u = 0; u < UU; ++u) {
-        const float pu = ex2(s[u] - mn);
+        const float pu = ex2((KIND == K_GT) ? fmaf(s[u], qs, -mn) : s[u] - mn);
         st.l += pu;
 #pragma unroll
         for (int k = 0; k < VEL; ++k)
@@ -250,7 +262,9 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GA
   constexpr int NWAVE = WG / 64;
   constexpr int NW = VB >= 4 ? VB / 4 : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // the wave index is uniform across the wave; saying so keeps a 64-lane
+  // slot's row, edge range and gathered row addresses in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sw = lane / LPE, sl = lane % LPE;
   const int slot_base = sw * LPE;
   // head group of this grid row; this lane's head in it and slice of the head
