@@ -38,7 +38,7 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
            "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune",
-           "gnn_reduce_multi_noalloc", "gnn_project")
+           "gnn_reduce_multi_noalloc", "gnn_project", "gnn_plan_verify")
 
 
 class GnnError(RuntimeError):
@@ -78,6 +78,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_plan_create": [P(_Csr), P(_PlanOpts), vp, P(vp)],
         "gnn_plan_destroy": [vp],
         "gnn_plan_stats": [vp, P(ctypes.c_int64), i32],
+        "gnn_plan_verify": [vp, P(_Csr), vp],
         "gnn_plan_wsb_export": [vp, vp, vp, vp, vp],
         "gnn_spmm": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
         "gnn_reduce": [P(_Csr), vp, ci, i32, i64, ci, vp, i64, vp, vp, vp],
@@ -242,6 +243,13 @@ def gnn_plan_autotune(csr: Csr, X: torch.Tensor, op: str = "multi", reps: int = 
     return {"opts": {"heavy_quantile": round(o.heavy_quantile, 6), "light_max_deg": o.light_max_deg,
                      "chunk_edges": o.chunk_edges},
             "best_ms": best.value, "default_ms": dflt.value}
+
+
+def gnn_plan_verify(plan: Plan, csr: Csr | None = None, stream=None):
+    """Raise GnnError (PLAN_MISMATCH) if the plan's CSR changed since it was built
+    (sizes, pointers, and sampled entries of row_ptr and col_idx)."""
+    c = csr if csr is not None else plan.csr
+    _check(load_library().gnn_plan_verify(plan.handle, c.ref, _stream(stream)), "gnn_plan_verify")
 
 
 def gnn_plan_stats(plan: Plan) -> dict:

@@ -43,13 +43,20 @@ int check_dtype(gnn_dtype t) {
   return GNN_OK;
 }
 
-// A plan given by the caller must be bound to this CSR; otherwise build a
+bool debug_validation() {
+  const char* env = getenv("GNN_DEBUG_VALIDATE");
+  return env && strcmp(env, "1") == 0;
+}
+
+// A plan given by the caller must be bound to this CSR (with
+// GNN_DEBUG_VALIDATE=1 also by its sampled contents); otherwise build a
 // transient one (synchronises the stream) that the caller of this helper frees.
 int get_plan(const gnn_csr* csr, gnn_plan* given, hipStream_t s, gnn_plan** use, bool* transient,
              bool need_wsb = false) {
   *transient = false;
   if (given) {
     GNN_TRY(check_plan(given, csr));
+    if (debug_validation()) GNN_TRY(plan_verify(given, s));
     if (need_wsb && !given->has_wsb)
       return fail(GNN_ERR_INVALID_VALUE, "plan was built without build_wsb");
     *use = given;
@@ -92,10 +99,9 @@ __global__ void k_check_csr(const int32_t* rp, const int32_t* ci, int32_t n, int
 // With GNN_DEBUG_VALIDATE=1 in the environment, run k_check_csr before
 // anything reads the CSR (synchronises the stream; allocates).
 int debug_validate(const gnn_csr* c, hipStream_t s) {
-  const char* env = getenv("GNN_DEBUG_VALIDATE");
-  if (!env || strcmp(env, "1") != 0) return GNN_OK;
+  if (!debug_validation()) return GNN_OK;
   int* d = nullptr;
-  GNN_HIP(hipMalloc((void**)&d, 3 * sizeof(int)));
+  GNN_TRY(dev_malloc((void**)&d, 3 * sizeof(int)));
   int h[3] = {0, 0, 0};
   hipError_t e = hipMemcpy(d, h, sizeof(h), hipMemcpyHostToDevice);
   if (e == hipSuccess) {
@@ -224,6 +230,13 @@ int gnn_plan_destroy(gnn_plan* p) {
   release(p->dob);
   delete p;
   return rc;
+}
+
+int gnn_plan_verify(gnn_plan* plan, const gnn_csr* csr, void* stream) {
+  if (!plan) return fail(GNN_ERR_INVALID_VALUE, "plan is NULL");
+  GNN_TRY(check_csr(csr, false));
+  GNN_TRY(check_plan(plan, csr));
+  return plan_verify(plan, (hipStream_t)stream);
 }
 
 int gnn_plan_stats(const gnn_plan* p, int64_t* c, int32_t n) {

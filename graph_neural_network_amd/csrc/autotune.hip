@@ -20,7 +20,7 @@ struct Buffers {
     for (void* q : ptrs) (void)hipFree(q);
   }
   int get(void** out, size_t bytes) {
-    GNN_HIP(hipMalloc(out, std::max<size_t>(bytes, 16)));
+    GNN_TRY(dev_malloc(out, std::max<size_t>(bytes, 16)));
     ptrs.push_back(*out);
     return GNN_OK;
   }

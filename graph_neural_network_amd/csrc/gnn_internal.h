@@ -41,8 +41,47 @@ int fail(int status, const std::string& msg);
     if (s_ != GNN_OK) return s_; \
   } while (0)
 
-// Device allocation tracked by the plan (freed in gnn_plan_destroy).
-int dev_alloc(void** p, size_t bytes);
+// Every device allocation of the library goes through these two calls.
+// GNN_FAIL_ALLOC=k (or k:tag; a new value restarts the count) in the
+// environment makes the k-th allocation after the variable took its value fail with GNN_ERR_OUT_OF_MEMORY before any
+// HIP call, so that the error paths can be exercised.
+int dev_malloc(void** p, size_t bytes);
+int dev_malloc_async(void** p, size_t bytes, hipStream_t s);
+
+// Stream-ordered temporaries of one call: taken on `s`, and all freed on `s`
+// when the object goes out of scope, early error returns included.
+struct StreamTemps {
+  hipStream_t s;
+  void* p[24] = {};
+  int n = 0;
+  explicit StreamTemps(hipStream_t st) : s(st) {}
+  StreamTemps(const StreamTemps&) = delete;
+  StreamTemps& operator=(const StreamTemps&) = delete;
+  template <typename T>
+  int get(T** out, size_t bytes) {
+    if (n >= (int)(sizeof(p) / sizeof(p[0]))) return fail(GNN_ERR_DEVICE, "too many temporaries");
+    void* q = nullptr;
+    int rc = dev_malloc_async(&q, bytes, s);
+    if (rc != GNN_OK) return rc;
+    p[n++] = q;
+    *out = static_cast<T*>(q);
+    return GNN_OK;
+  }
+  // free everything now, reporting a failed free
+  int release() {
+    hipError_t first = hipSuccess;
+    for (int k = 0; k < n; ++k) {
+      const hipError_t e = hipFreeAsync(p[k], s);
+      if (e != hipSuccess && first == hipSuccess) first = e;
+    }
+    n = 0;
+    if (first != hipSuccess) return fail(GNN_ERR_DEVICE, std::string("hipFreeAsync: ") + hipGetErrorString(first));
+    return GNN_OK;
+  }
+  ~StreamTemps() {
+    for (int k = 0; k < n; ++k) (void)hipFreeAsync(p[k], s);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Plan
@@ -71,6 +110,13 @@ struct gnn_plan {
   const int32_t* col_idx = nullptr;
   gnn_plan_opts opts{};
   hipStream_t stream = nullptr;
+
+  // structure fingerprint: kFingerprint evenly spaced entries of row_ptr
+  // (first and last included) and of col_idx, sampled when the plan was
+  // built (host copy) and re-sampled into fp_dev by plan_verify
+  static constexpr int kFingerprint = 64;
+  int32_t fp_host[2 * kFingerprint] = {};
+  int32_t* fp_dev = nullptr;
 
   // degrees
   int32_t* deg_out = nullptr;  // [n_cols]
@@ -128,6 +174,11 @@ int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
 int plan_transpose(gnn_plan* p, hipStream_t s);
 int plan_transpose_wsb(gnn_plan* p, hipStream_t s);
 int check_plan(const gnn_plan* p, const gnn_csr* csr);
+// Enqueue the fingerprint samples of the plan's CSR into p->fp_dev.
+int plan_sample_fingerprint(gnn_plan* p, hipStream_t s);
+// Re-sample the fingerprint and compare it with the one taken at build time
+// (synchronises `s`; allocates nothing): PLAN_MISMATCH if they differ.
+int plan_verify(gnn_plan* p, hipStream_t s);
 
 // Launchers (host).  All validate nothing: the entry points did.
 int launch_aggregate(gnn_plan* p, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y,

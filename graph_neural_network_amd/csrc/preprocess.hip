@@ -14,6 +14,8 @@
 //   heavy  : deg > thr                  ceil(deg / chunk) workgroups, merged
 #include <algorithm>
 
+#include <string.h>
+
 #include "gnn_internal.h"
 
 namespace gnn {
@@ -218,6 +220,16 @@ __global__ __launch_bounds__(256) void k_stats_total(const unsigned long long* p
   if (threadIdx.x < 4) stats[threadIdx.x] = red[threadIdx.x][0];
 }
 
+// Fingerprint samples: out[k] = row_ptr[k n / (K - 1)], out[K + k] =
+// col_idx[k (nnz - 1) / (K - 1)] (0 for an empty graph), k < K.
+__global__ void k_fingerprint(const int32_t* row_ptr, int32_t n, const int32_t* col_idx, int64_t nnz, int32_t K,
+                              int32_t* out) {
+  const int k = threadIdx.x;
+  if (k >= K) return;
+  out[k] = row_ptr[(int64_t)k * n / (K - 1)];
+  out[K + k] = nnz > 0 ? col_idx[(int64_t)k * (nnz - 1) / (K - 1)] : 0;
+}
+
 __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, const int32_t* cnt,
                              const int32_t* item_off, const int32_t* multi_off, int4* items,
                              int4* multi) {
@@ -284,15 +296,14 @@ __global__ void k_att_rows(const uint64_t* keys, int64_t n, int32_t* rows) {
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
   if (p->att_lmax == lmax) return GNN_OK;
   const int32_t n = p->n_rows;
-  if (!p->att_rows) {
-    GNN_TRY(plan_alloc(p, (void**)&p->att_rows, (size_t)std::max(n, 1) * 4));
-    GNN_TRY(plan_alloc(p, (void**)&p->att_count, 16));
-  }
+  if (!p->att_rows) GNN_TRY(plan_alloc(p, (void**)&p->att_rows, (size_t)std::max(n, 1) * 4));
+  if (!p->att_count) GNN_TRY(plan_alloc(p, (void**)&p->att_count, 16));
   GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));  // stays 0 for an empty graph
   if (n > 0) {
     uint64_t *keys = nullptr, *tmp = nullptr;
-    GNN_HIP(hipMallocAsync((void**)&keys, (size_t)n * 8, s));
-    GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)n * 8, s));
+    StreamTemps tt(s);
+    GNN_TRY(tt.get(&keys, (size_t)n * 8));
+    GNN_TRY(tt.get(&tmp, (size_t)n * 8));
     const unsigned nb = (unsigned)((n + 255) / 256);
     // high word: window index above lbits of (lmax - length); the top bit
     // marks unlisted rows.  Windows widen if both fields would not fit 31 bits.
@@ -310,8 +321,7 @@ int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
       hipLaunchKernelGGL(k_att_count, dim3(1), dim3(64), 0, s, keys, (int64_t)n, p->att_count);
       if (hipGetLastError() != hipSuccess) rc = fail(GNN_ERR_DEVICE, "attention row list launch failed");
     }
-    GNN_HIP(hipFreeAsync(keys, s));
-    GNN_HIP(hipFreeAsync(tmp, s));
+    GNN_TRY(tt.release());
     if (rc != GNN_OK) return rc;
   }
   p->att_lmax = lmax;
@@ -331,11 +341,8 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
     GNN_LAUNCH_CHECK("scan");
     return GNN_OK;
   }
-  void* own = nullptr;
-  if (!scratch) {
-    GNN_HIP(hipMallocAsync(&own, scan_scratch_bytes(n), s));
-    scratch = own;
-  }
+  StreamTemps tmp(s);
+  if (!scratch) GNN_TRY(tmp.get(&scratch, scan_scratch_bytes(n)));
   Arena a{static_cast<char*>(scratch), scan_scratch_bytes(n), 0};
   int32_t* sums = a.take<int32_t>(nb);
   int32_t* offs = a.take<int32_t>(nb + 1);
@@ -347,16 +354,15 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
                        out);
     GNN_LAUNCH_CHECK("scan tiles");
   }
-  if (own) GNN_HIP(hipFreeAsync(own, s));
-  return rc;
+  if (rc != GNN_OK) return rc;
+  return tmp.release();
 }
 
 int plan_alloc(gnn_plan* p, void** ptr, size_t bytes) {
   if (p->n_allocs >= (int)(sizeof(p->allocs) / sizeof(p->allocs[0])))
     return fail(GNN_ERR_DEVICE, "plan: too many allocations");
   void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes ? bytes : 16);
-  if (e != hipSuccess) return fail(GNN_ERR_OUT_OF_MEMORY, std::string("plan alloc: ") + hipGetErrorString(e));
+  GNN_TRY(dev_malloc(&q, bytes ? bytes : 16));
   p->allocs[p->n_allocs++] = q;
   *ptr = q;
   return GNN_OK;
@@ -374,8 +380,7 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
     p->ws_bytes = 0;
   }
   void* q = nullptr;
-  hipError_t e = hipMalloc(&q, bytes);
-  if (e != hipSuccess) return fail(GNN_ERR_OUT_OF_MEMORY, std::string("workspace: ") + hipGetErrorString(e));
+  GNN_TRY(dev_malloc(&q, bytes));
   p->ws = q;
   p->ws_bytes = bytes;
   *out = q;
@@ -390,12 +395,25 @@ int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes) {
     *buf = nullptr;
     *cap = 0;
   }
-  hipError_t e = hipMalloc(buf, bytes);
-  if (e != hipSuccess) {
-    *buf = nullptr;
-    return fail(GNN_ERR_OUT_OF_MEMORY, std::string("plan buffer: ") + hipGetErrorString(e));
-  }
+  GNN_TRY(dev_malloc(buf, bytes));
   *cap = bytes;
+  return GNN_OK;
+}
+
+int plan_sample_fingerprint(gnn_plan* p, hipStream_t s) {
+  hipLaunchKernelGGL(k_fingerprint, dim3(1), dim3(gnn_plan::kFingerprint), 0, s, p->row_ptr, p->n_rows, p->col_idx,
+                     p->nnz, (int32_t)gnn_plan::kFingerprint, p->fp_dev);
+  GNN_LAUNCH_CHECK("fingerprint");
+  return GNN_OK;
+}
+
+int plan_verify(gnn_plan* p, hipStream_t s) {
+  int32_t now[2 * gnn_plan::kFingerprint];
+  GNN_TRY(plan_sample_fingerprint(p, s));
+  GNN_HIP(hipMemcpyAsync(now, p->fp_dev, sizeof(now), hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  if (memcmp(now, p->fp_host, sizeof(now)) != 0)
+    return fail(GNN_ERR_PLAN_MISMATCH, "the CSR arrays changed since the plan was built (sampled entries differ)");
   return GNN_OK;
 }
 
@@ -414,6 +432,9 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
 
   const int32_t n = p->n_rows;
   GNN_TRY(plan_alloc(p, (void**)&p->deg_out, (size_t)std::max(p->n_cols, 1) * 4));
+  GNN_TRY(plan_alloc(p, (void**)&p->fp_dev, sizeof(p->fp_host)));
+  GNN_TRY(plan_sample_fingerprint(p, s));
+  GNN_HIP(hipMemcpyAsync(p->fp_host, p->fp_dev, sizeof(p->fp_host), hipMemcpyDeviceToHost, s));
   GNN_HIP(hipMemsetAsync(p->deg_out, 0, (size_t)std::max(p->n_cols, 1) * 4, s));
   if (p->nnz > 0) {
     int64_t blocks = std::min<int64_t>((p->nnz + 255) / 256, 65536);
@@ -423,9 +444,10 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   }
 
   // gamma-quantile degree threshold
+  StreamTemps tt(s);
   int32_t* hist = nullptr;
   int32_t* tmp = nullptr;  // [threshold]
-  GNN_HIP(hipMallocAsync((void**)&hist, kHistBins * 4 + 16, s));
+  GNN_TRY(tt.get(&hist, kHistBins * 4 + 16));
   tmp = hist + kHistBins;
   int32_t thr_host = INT32_MAX;
   if (gamma > 0.0f && n > 0) {
@@ -441,18 +463,17 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
     thr_host = std::max(thr_host, p->chunk_edges);
   }
   p->heavy_thr = thr_host;
-  GNN_HIP(hipFreeAsync(hist, s));
 
   // classify rows, scan counts, fill items
   int32_t *cnt = nullptr, *ism = nullptr, *ioff = nullptr, *moff = nullptr;
   unsigned long long* stats = nullptr;
   size_t nn = (size_t)std::max(n, 1);
-  GNN_HIP(hipMallocAsync((void**)&cnt, nn * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&ism, nn * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&ioff, (nn + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&moff, (nn + 1) * 4, s));
+  GNN_TRY(tt.get(&cnt, nn * 4));
+  GNN_TRY(tt.get(&ism, nn * 4));
+  GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
+  GNN_TRY(tt.get(&moff, (nn + 1) * 4));
   const int64_t ncb = std::max<int64_t>((n + 255) / 256, 1);
-  GNN_HIP(hipMallocAsync((void**)&stats, (4 + ncb * 4) * 8, s));
+  GNN_TRY(tt.get(&stats, (4 + ncb * 4) * 8));
   GNN_HIP(hipMemsetAsync(stats, 0, (4 + ncb * 4) * 8, s));
   if (n > 0) {
     hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max,
@@ -482,11 +503,7 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
                        n, p->chunk_edges, cnt, ioff, moff, p->items, p->multi);
     GNN_LAUNCH_CHECK("fill items");
   }
-  GNN_HIP(hipFreeAsync(cnt, s));
-  GNN_HIP(hipFreeAsync(ism, s));
-  GNN_HIP(hipFreeAsync(ioff, s));
-  GNN_HIP(hipFreeAsync(moff, s));
-  GNN_HIP(hipFreeAsync(stats, s));
+  GNN_TRY(tt.release());
   if (p->opts.build_wsb) GNN_TRY(plan_build_wsb(p, s));
   GNN_HIP(hipStreamSynchronize(s));
   return GNN_OK;

@@ -540,7 +540,7 @@ int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int
   size_t need = kind == GNN_REORDER_DEGREE ? degree_bytes(n) : rcm_bytes(n, csr->nnz);
   if (rp_out) need = std::max(need, permute_bytes(n, csr->nnz));
   void* blk = nullptr;
-  GNN_HIP(hipMallocAsync(&blk, need, s));
+  GNN_TRY(dev_malloc_async(&blk, need, s));
   Arena ar{static_cast<char*>(blk), need, 0};
   int rc = kind == GNN_REORDER_DEGREE ? degree_perm(csr, perm, ar, s) : rcm_perm(csr, perm, ar, s);
   if (rc == GNN_OK && rp_out) {

@@ -89,11 +89,8 @@ int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int 
   if (n <= 1 || end_bit <= begin_bit) return GNN_OK;
   const int64_t ntiles = (n + RTILE - 1) / RTILE;
   if (ntiles * 256 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "radix sort too large");
-  void* own = nullptr;
-  if (!scratch) {
-    GNN_HIP(hipMallocAsync(&own, radix_scratch_bytes(n), s));
-    scratch = own;
-  }
+  StreamTemps own(s);
+  if (!scratch) GNN_TRY(own.get(&scratch, radix_scratch_bytes(n)));
   Arena a{static_cast<char*>(scratch), radix_scratch_bytes(n), 0};
   int32_t* hist = a.take<int32_t>(ntiles * 256);
   int32_t* offs = a.take<int32_t>(ntiles * 256 + 1);
@@ -114,8 +111,8 @@ int radix_sort_u64(uint64_t* keys, uint64_t* tmp, int64_t n, int begin_bit, int 
   }
   if (rc == GNN_OK && src != keys)
     GNN_HIP(hipMemcpyAsync(keys, src, n * 8, hipMemcpyDeviceToDevice, s));
-  if (own) GNN_HIP(hipFreeAsync(own, s));
-  return rc;
+  if (rc != GNN_OK) return rc;
+  return own.release();
 }
 
 }  // namespace gnn

@@ -84,18 +84,20 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   if (p->tplan) return GNN_OK;
   const int32_t n = p->n_rows, nc = p->n_cols;
   const int64_t m = p->nnz;
-  GNN_TRY(plan_alloc(p, (void**)&p->t_row_ptr, ((size_t)nc + 1) * 4));
-  GNN_TRY(plan_alloc(p, (void**)&p->t_col, (size_t)std::max<int64_t>(m, 1) * 4));
-  GNN_TRY(plan_alloc(p, (void**)&p->t_edge, (size_t)std::max<int64_t>(m, 1) * 4));
+  // (kept across a failed attempt, so that a retry reuses them)
+  if (!p->t_row_ptr) GNN_TRY(plan_alloc(p, (void**)&p->t_row_ptr, ((size_t)nc + 1) * 4));
+  if (!p->t_col) GNN_TRY(plan_alloc(p, (void**)&p->t_col, (size_t)std::max<int64_t>(m, 1) * 4));
+  if (!p->t_edge) GNN_TRY(plan_alloc(p, (void**)&p->t_edge, (size_t)std::max<int64_t>(m, 1) * 4));
   // row pointers of A^T: the exclusive scan of the out-degrees
   GNN_TRY(exclusive_scan_i32(p->deg_out, p->t_row_ptr, nc, s));
   if (m > 0) {
     int32_t *ends = nullptr, *rows = nullptr;
     uint64_t *keys = nullptr, *tmp = nullptr;
-    GNN_HIP(hipMallocAsync((void**)&ends, ((size_t)m + 1) * 4, s));
-    GNN_HIP(hipMallocAsync((void**)&rows, ((size_t)m + 1) * 4, s));
-    GNN_HIP(hipMallocAsync((void**)&keys, (size_t)m * 8, s));
-    GNN_HIP(hipMallocAsync((void**)&tmp, (size_t)m * 8, s));
+    StreamTemps tt(s);
+    GNN_TRY(tt.get(&ends, ((size_t)m + 1) * 4));
+    GNN_TRY(tt.get(&rows, ((size_t)m + 1) * 4));
+    GNN_TRY(tt.get(&keys, (size_t)m * 8));
+    GNN_TRY(tt.get(&tmp, (size_t)m * 8));
     GNN_HIP(hipMemsetAsync(ends, 0, ((size_t)m + 1) * 4, s));
     hipLaunchKernelGGL(k_row_ends, dim3(grid_for(n)), dim3(256), 0, s, p->row_ptr, n, m, ends);
     GNN_LAUNCH_CHECK("transpose: row ends");
@@ -111,11 +113,8 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
                          p->t_edge);
       if (hipGetLastError() != hipSuccess) rc = fail(GNN_ERR_DEVICE, "transpose: fill launch failed");
     }
-    GNN_HIP(hipFreeAsync(ends, s));
-    GNN_HIP(hipFreeAsync(rows, s));
-    GNN_HIP(hipFreeAsync(keys, s));
-    GNN_HIP(hipFreeAsync(tmp, s));
     if (rc != GNN_OK) return rc;
+    GNN_TRY(tt.release());
   }
   gnn_csr t{};
   t.n_rows = nc;

@@ -1,10 +1,59 @@
 // Small data-movement kernels: row gather for reordered features and a plain
 // streaming copy used to calibrate bandwidth figures and hardware counters.
+#include <stdlib.h>
+
 #include <algorithm>
+#include <mutex>
+#include <string>
 
 #include "gnn_internal.h"
 
 namespace gnn {
+
+// The allocation-failure hook: with GNN_FAIL_ALLOC=k or k:tag, the k-th
+// allocation counted from when the variable last took its value fails.
+static std::mutex g_fault_mu;
+static std::string g_fault_value;
+static long g_fault_count = 0;
+
+static bool alloc_fault() {
+  const char* e = getenv("GNN_FAIL_ALLOC");
+  std::lock_guard<std::mutex> lock(g_fault_mu);
+  if (!e || !*e) {
+    g_fault_value.clear();
+    return false;
+  }
+  if (g_fault_value != e) {
+    g_fault_value = e;
+    g_fault_count = 0;
+  }
+  return ++g_fault_count == atol(e);
+}
+
+int dev_malloc(void** p, size_t bytes) {
+  *p = nullptr;
+  if (alloc_fault()) return fail(GNN_ERR_OUT_OF_MEMORY, "device allocation failed (GNN_FAIL_ALLOC)");
+  const hipError_t e = hipMalloc(p, bytes ? bytes : 16);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(e == hipErrorOutOfMemory ? GNN_ERR_OUT_OF_MEMORY : GNN_ERR_DEVICE,
+                std::string("hipMalloc: ") + hipGetErrorString(e));
+  }
+  return GNN_OK;
+}
+
+int dev_malloc_async(void** p, size_t bytes, hipStream_t s) {
+  *p = nullptr;
+  if (alloc_fault()) return fail(GNN_ERR_OUT_OF_MEMORY, "device allocation failed (GNN_FAIL_ALLOC)");
+  const hipError_t e = hipMallocAsync(p, bytes ? bytes : 16, s);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(e == hipErrorOutOfMemory ? GNN_ERR_OUT_OF_MEMORY : GNN_ERR_DEVICE,
+                std::string("hipMallocAsync: ") + hipGetErrorString(e));
+  }
+  return GNN_OK;
+}
+
 namespace {
 
 // One wave per destination row; 16-byte accesses when the row allows it.

@@ -200,12 +200,13 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
 
   uint64_t *keys = nullptr, *tmp = nullptr;
   int32_t *flag = nullptr, *uidx = nullptr, *ucnt = nullptr, *nbk = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&keys, nnz * 8, s));
-  GNN_HIP(hipMallocAsync((void**)&tmp, nnz * 8, s));
-  GNN_HIP(hipMallocAsync((void**)&flag, (nnz + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&uidx, (nnz + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&ucnt, (size_t)nw * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&nbk, (size_t)nw * 4, s));
+  StreamTemps tt(s);
+  GNN_TRY(tt.get(&keys, nnz * 8));
+  GNN_TRY(tt.get(&tmp, nnz * 8));
+  GNN_TRY(tt.get(&flag, (nnz + 1) * 4));
+  GNN_TRY(tt.get(&uidx, (nnz + 1) * 4));
+  GNN_TRY(tt.get(&ucnt, (size_t)nw * 4));
+  GNN_TRY(tt.get(&nbk, (size_t)nw * 4));
 
   hipLaunchKernelGGL(k_wsb_keys, dim3(nblk(nnz)), dim3(256), 0, s, p->row_ptr, p->col_idx, n, nnz,
                      colbits, keys);
@@ -235,8 +236,8 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
 
   // dense tiles
   int32_t *dense = nullptr, *tscan = nullptr;
-  GNN_HIP(hipMallocAsync((void**)&dense, (size_t)(L.n_blocks + 1) * 4, s));
-  GNN_HIP(hipMallocAsync((void**)&tscan, (size_t)(L.n_blocks + 1) * 4, s));
+  GNN_TRY(tt.get(&dense, (size_t)(L.n_blocks + 1) * 4));
+  GNN_TRY(tt.get(&tscan, (size_t)(L.n_blocks + 1) * 4));
   hipLaunchKernelGGL(k_wsb_dense, dim3(nblk(L.n_blocks)), dim3(256), 0, s, L.win_ptr, nw, L.n_blocks,
                      (const unsigned long long*)L.blk_bits, p->opts.wsb_min_nnz, dense);
   GNN_LAUNCH_CHECK("wsb dense");
@@ -270,14 +271,7 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
                      L.res_ptr);
   GNN_LAUNCH_CHECK("wsb residual ptr");
 
-  GNN_HIP(hipFreeAsync(keys, s));
-  GNN_HIP(hipFreeAsync(tmp, s));
-  GNN_HIP(hipFreeAsync(flag, s));
-  GNN_HIP(hipFreeAsync(uidx, s));
-  GNN_HIP(hipFreeAsync(ucnt, s));
-  GNN_HIP(hipFreeAsync(nbk, s));
-  GNN_HIP(hipFreeAsync(dense, s));
-  GNN_HIP(hipFreeAsync(tscan, s));
+  GNN_TRY(tt.release());
   p->has_wsb = true;
   return GNN_OK;
 }

@@ -48,6 +48,13 @@
  *     col_idx in [0, n_cols).  The check synchronises the stream and
  *     allocates; a violation returns INVALID_VALUE before any other kernel
  *     reads the CSR.  Without it, an invalid CSR is undefined behaviour.
+ *     Calls given a plan then also run gnn_plan_verify.
+ *   - Device memory: every allocation the library makes can fail with
+ *     OUT_OF_MEMORY; the call then returns it with nothing left allocated
+ *     and no output written beyond what finished kernels wrote.
+ *     GNN_FAIL_ALLOC=k (or k:tag) in the environment makes the k-th allocation
+ *     after the variable took that value fail that way, before any HIP call (a hook for
+ *     testing the error paths).
  */
 #ifndef GNN_H_
 #define GNN_H_
@@ -145,6 +152,19 @@ int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream,
 /* Free a plan and its device memory (the cache reset of appendix D.4).  Waits
  * for the plan's stream.  NULL is a no-op. */
 int gnn_plan_destroy(gnn_plan* plan);
+
+/* Check that a plan still matches its CSR's contents: the sizes and array
+ * pointers must be those it was built for (as every call checks), and 64
+ * evenly spaced entries of row_ptr (first and last included) and 64 of
+ * col_idx, sampled on the device, must equal the samples taken when the
+ * plan was built.  A cheap guard against a CSR rebuilt in place under a
+ * cached plan (the failure mode of a pointer-keyed structure cache); an edit
+ * of single entries between the samples goes unseen.  With
+ * GNN_DEBUG_VALIDATE=1 every call that is given a plan runs this check
+ * first (except gnn_reduce_multi_noalloc).  Synchronises `stream`;
+ * allocates nothing.
+ * Errors: INVALID_VALUE, PLAN_MISMATCH, DEVICE. */
+int gnn_plan_verify(gnn_plan* plan, const gnn_csr* csr, void* stream);
 
 /* Plan statistics for reports: counts[0] = light rows, [1] = medium rows,
  * [2] = heavy rows, [3] = chunk work items, [4] = degree threshold used,
