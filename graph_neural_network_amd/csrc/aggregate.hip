@@ -57,6 +57,7 @@ struct AggParams {
   int32_t F;
   int32_t light_max;
   int32_t n_item_blocks;   // item workgroups in grid.x
+  const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
   int32_t n_light_blocks;
   int32_t rps;             // light rows per slot (LPR on large graphs)
   int32_t norm;            // gnn_norm (SpMM); MEAN is expressed as LEFT
@@ -394,6 +395,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
     // ---------------- one workgroup per work item ----------------
     const int lid = blockIdx.x;
     if (lid >= p.n_item_blocks) return;
+    if (p.item_count && lid >= *p.item_count) return;
     const int4 it = p.items[lid];
     const int row = it.x, eb = it.y, ee = it.z, m = it.w;
     const int len = ee - eb;
@@ -640,6 +642,7 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   constexpr int FT = LPR * VE;
   const int ftiles = (p.F + FT - 1) / FT;
   p.n_item_blocks = (int32_t)pl->n_items;
+  p.item_count = pl->item_count;
   // a light workgroup covers (WG / LPR) * rps rows: 64 / LPR slots per wave,
   // rps rows per slot.  rps = LPR unless that leaves fewer than 1024
   // workgroups (four per CU): a slot walks its rows' edges as one dependent

@@ -48,6 +48,8 @@ bool debug_validation() {
   return env && strcmp(env, "1") == 0;
 }
 
+int debug_validate(const gnn_csr* c, hipStream_t s);
+
 // A plan given by the caller must be bound to this CSR (with
 // GNN_DEBUG_VALIDATE=1 also by its sampled contents); otherwise build a
 // transient one (synchronises the stream) that the caller of this helper frees.
@@ -62,10 +64,24 @@ int get_plan(const gnn_csr* csr, gnn_plan* given, hipStream_t s, gnn_plan** use,
     *use = given;
     return GNN_OK;
   }
-  gnn_plan_opts o{};
-  o.build_wsb = need_wsb ? 1 : 0;
   gnn_plan* p = nullptr;
-  GNN_TRY(gnn_plan_create(csr, &o, s, &p));
+  if (need_wsb) {
+    // the WSB layout is sized from counts read back to the host
+    gnn_plan_opts o{};
+    o.build_wsb = 1;
+    GNN_TRY(gnn_plan_create(csr, &o, s, &p));
+  } else {
+    GNN_TRY(debug_validate(csr, s));
+    p = new (std::nothrow) gnn_plan();
+    if (!p) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
+    const int rc = plan_build_async(csr, s, p);
+    if (rc != GNN_OK) {
+      std::string keep = g_last_error;
+      gnn_plan_destroy(p);
+      g_last_error = keep;
+      return rc;
+    }
+  }
   *use = p;
   *transient = true;
   return GNN_OK;
@@ -217,6 +233,18 @@ int gnn_plan_destroy(gnn_plan* p) {
   if (p->tplan) {
     rc = gnn_plan_destroy(p->tplan);  // its CSR arrays belong to p and are freed below
     p->tplan = nullptr;
+  }
+  if (p->async_mem) {
+    // a transient plan: everything is freed in stream order, no wait
+    auto release = [&rc, p](void* ptr) {
+      if (ptr && hipFreeAsync(ptr, p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "hipFreeAsync of a plan buffer failed");
+    };
+    for (int k = 0; k < p->n_allocs; ++k) release(p->allocs[k]);
+    release(p->ws);
+    release(p->delta);
+    release(p->dob);
+    delete p;
+    return rc;
   }
   if (p->n_allocs > 0 || p->ws) {
     if (hipStreamSynchronize(p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "plan stream sync failed");

@@ -76,6 +76,7 @@ struct AttParams {
   const int32_t* att_rows;   // those rows, longest first
   const int32_t* att_count;  // device: how many
   int32_t n_item_blocks;
+  const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
   int32_t n_light_blocks;
   float slope;        // GATv2 LeakyReLU slope
   float qscale;       // GT: scale * log2(e)
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GA
   if (is_item) {
     item = (int)dev::xcd_remap(blockIdx.x, n_item_pad);
     if (item >= p.n_item_blocks) return;
+    if (p.item_count && item >= *p.item_count) return;
     const int4 it = p.items[item];
     // single-chunk rows short enough for the light path are processed there
     if (it.w < 0 && it.z - it.y <= p.light_max) return;
@@ -402,6 +404,7 @@ int launch_att_h(gnn_plan* pl, AttParams& p, int groups, hipStream_t s) {
   constexpr int UU = GNN_ATT_U;
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.n_item_blocks = (int32_t)pl->n_items;
+  p.item_count = pl->item_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF || groups > 65535) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");

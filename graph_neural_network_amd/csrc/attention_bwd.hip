@@ -52,6 +52,7 @@ struct BwdParams {
   const int32_t* light_rows;   // rows of at most light_max entries, by length within windows
   const int32_t* light_count;  // device: how many
   int32_t n_item_blocks;
+  const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
   int32_t n_light_blocks;
   // tensors: "dst" are indexed by destinations (rows of the CSR), "src" by sources
   const void* q;     // dst: GT q; GATv2 x_l
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
   bool active = true;  // GATv2 dst workgroups reach the block reduction even when idle
   if (is_item) {
     item = (int)dev::xcd_remap(blockIdx.x, n_item_pad);
-    active = item < p.n_item_blocks;
+    active = item < p.n_item_blocks && (!p.item_count || item < *p.item_count);
     if (active) {
       const int4 it = p.items[item];
       active = !(it.w < 0 && it.z - it.y <= p.light_max);  // short rows: light path
@@ -444,6 +445,7 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   p.light_rows = pl->att_rows;
   p.light_count = pl->att_count;
   p.n_item_blocks = (int32_t)pl->n_items;
+  p.item_count = pl->item_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention backward grid too large");

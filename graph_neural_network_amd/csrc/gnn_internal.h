@@ -110,6 +110,9 @@ struct gnn_plan {
   const int32_t* col_idx = nullptr;
   gnn_plan_opts opts{};
   hipStream_t stream = nullptr;
+  // a transient plan: all its memory is allocated and freed stream-ordered on
+  // `stream`, and it was built without reading anything back to the host
+  bool async_mem = false;
 
   // structure fingerprint: kFingerprint evenly spaced entries of row_ptr
   // (first and last included) and of col_idx, sampled when the plan was
@@ -127,7 +130,8 @@ struct gnn_plan {
   int32_t chunk_edges = 512;
   int64_t n_light = 0, n_medium = 0, n_heavy = 0;
   int4* items = nullptr;     // [n_items] (row, e_begin, e_end, multi index or -1)
-  int64_t n_items = 0;
+  int64_t n_items = 0;       // (an upper bound when item_count is set)
+  int32_t* item_count = nullptr;  // device: the item count, for plans built without a host read-back
   int4* multi = nullptr;     // [n_multi] (row, first item, item count, 0)
   int64_t n_multi = 0;
   int32_t max_items_per_row = 0;
@@ -169,6 +173,11 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out);
 // a plan-owned buffer that grows on demand (freed with the plan)
 int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes);
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p);
+// The transient plan of a call made without one: degrees and one work item
+// per row longer than the light bound (no split rows), built on `s` with
+// stream-ordered memory and no host synchronisation; its item count stays on
+// the device (item_count), n_items holds an upper bound for grid sizes.
+int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p);
 int plan_build_wsb(gnn_plan* p, hipStream_t s);
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
 int plan_transpose(gnn_plan* p, hipStream_t s);

@@ -362,7 +362,8 @@ int plan_alloc(gnn_plan* p, void** ptr, size_t bytes) {
   if (p->n_allocs >= (int)(sizeof(p->allocs) / sizeof(p->allocs[0])))
     return fail(GNN_ERR_DEVICE, "plan: too many allocations");
   void* q = nullptr;
-  GNN_TRY(dev_malloc(&q, bytes ? bytes : 16));
+  if (p->async_mem) GNN_TRY(dev_malloc_async(&q, bytes ? bytes : 16, p->stream));
+  else GNN_TRY(dev_malloc(&q, bytes ? bytes : 16));
   p->allocs[p->n_allocs++] = q;
   *ptr = q;
   return GNN_OK;
@@ -374,13 +375,18 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
     return GNN_OK;
   }
   if (p->ws) {
-    GNN_HIP(hipStreamSynchronize(p->stream));
-    GNN_HIP(hipFree(p->ws));
+    if (p->async_mem) {
+      GNN_HIP(hipFreeAsync(p->ws, p->stream));
+    } else {
+      GNN_HIP(hipStreamSynchronize(p->stream));
+      GNN_HIP(hipFree(p->ws));
+    }
     p->ws = nullptr;
     p->ws_bytes = 0;
   }
   void* q = nullptr;
-  GNN_TRY(dev_malloc(&q, bytes));
+  if (p->async_mem) GNN_TRY(dev_malloc_async(&q, bytes, p->stream));
+  else GNN_TRY(dev_malloc(&q, bytes));
   p->ws = q;
   p->ws_bytes = bytes;
   *out = q;
@@ -390,12 +396,17 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
 int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes) {
   if (*buf && *cap >= bytes) return GNN_OK;
   if (*buf) {
-    GNN_HIP(hipStreamSynchronize(p->stream));
-    GNN_HIP(hipFree(*buf));
+    if (p->async_mem) {
+      GNN_HIP(hipFreeAsync(*buf, p->stream));
+    } else {
+      GNN_HIP(hipStreamSynchronize(p->stream));
+      GNN_HIP(hipFree(*buf));
+    }
     *buf = nullptr;
     *cap = 0;
   }
-  GNN_TRY(dev_malloc(buf, bytes));
+  if (p->async_mem) GNN_TRY(dev_malloc_async(buf, bytes, p->stream));
+  else GNN_TRY(dev_malloc(buf, bytes));
   *cap = bytes;
   return GNN_OK;
 }
@@ -415,6 +426,59 @@ int plan_verify(gnn_plan* p, hipStream_t s) {
   if (memcmp(now, p->fp_host, sizeof(now)) != 0)
     return fail(GNN_ERR_PLAN_MISMATCH, "the CSR arrays changed since the plan was built (sampled entries differ)");
   return GNN_OK;
+}
+
+int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
+  p->n_rows = csr->n_rows;
+  p->n_cols = csr->n_cols;
+  p->nnz = csr->nnz;
+  p->row_ptr = csr->row_ptr;
+  p->col_idx = csr->col_idx;
+  p->stream = s;
+  p->async_mem = true;
+  p->opts.wsb_min_nnz = 8;
+  p->light_max = 32;
+  p->chunk_edges = 1024;
+  p->heavy_thr = INT32_MAX;  // no row is split
+  const int32_t n = p->n_rows;
+  GNN_TRY(plan_alloc(p, (void**)&p->deg_out, (size_t)std::max(p->n_cols, 1) * 4));
+  GNN_HIP(hipMemsetAsync(p->deg_out, 0, (size_t)std::max(p->n_cols, 1) * 4, s));
+  if (p->nnz > 0) {
+    int64_t blocks = std::min<int64_t>((p->nnz + 255) / 256, 65536);
+    hipLaunchKernelGGL(k_deg_out, dim3((unsigned)blocks), dim3(256), 0, s, p->col_idx, p->nnz, p->deg_out);
+    GNN_LAUNCH_CHECK("deg_out");
+  }
+  // rows longer than the light bound: at most one per light_max + 1 entries
+  const int64_t bound = std::min<int64_t>(n, p->nnz / (p->light_max + 1));
+  p->n_items = bound;
+  p->n_multi = 0;
+  GNN_TRY(plan_alloc(p, (void**)&p->item_count, 16));
+  GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(bound, 1) * sizeof(int4)));
+  GNN_TRY(plan_alloc(p, (void**)&p->multi, sizeof(int4)));
+  if (n == 0 || bound == 0) {
+    GNN_HIP(hipMemsetAsync(p->item_count, 0, 4, s));
+    return GNN_OK;
+  }
+  StreamTemps tt(s);
+  int32_t *cnt = nullptr, *ism = nullptr, *ioff = nullptr, *moff = nullptr;
+  unsigned long long* part = nullptr;
+  const size_t nn = (size_t)n;
+  const int64_t ncb = (n + 255) / 256;
+  GNN_TRY(tt.get(&cnt, nn * 4));
+  GNN_TRY(tt.get(&ism, nn * 4));
+  GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
+  GNN_TRY(tt.get(&moff, (nn + 1) * 4));
+  GNN_TRY(tt.get(&part, (size_t)ncb * 4 * 8));
+  hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max, p->heavy_thr,
+                     p->chunk_edges, cnt, ism, part);
+  GNN_LAUNCH_CHECK("classify");
+  GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
+  GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
+  GNN_HIP(hipMemcpyAsync(p->item_count, ioff + n, 4, hipMemcpyDeviceToDevice, s));
+  hipLaunchKernelGGL(k_fill_items, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->chunk_edges, cnt, ioff,
+                     moff, p->items, p->multi);
+  GNN_LAUNCH_CHECK("fill items");
+  return tt.release();
 }
 
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p) {

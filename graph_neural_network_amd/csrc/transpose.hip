@@ -126,10 +126,12 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   o.build_wsb = 0;
   gnn_plan* tp = new (std::nothrow) gnn_plan();
   if (!tp) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
-  const int rc = plan_build(&t, &o, s, tp);
+  // a transient plan's transpose is transient too: built without a host wait
+  const int rc = p->async_mem ? plan_build_async(&t, s, tp) : plan_build(&t, &o, s, tp);
   if (rc != GNN_OK) {
-    for (int k = 0; k < tp->n_allocs; ++k) (void)hipFree(tp->allocs[k]);
-    if (tp->ws) (void)hipFree(tp->ws);
+    for (int k = 0; k < tp->n_allocs; ++k)
+      (void)(tp->async_mem ? hipFreeAsync(tp->allocs[k], s) : hipFree(tp->allocs[k]));
+    if (tp->ws) (void)(tp->async_mem ? hipFreeAsync(tp->ws, s) : hipFree(tp->ws));
     delete tp;
     return rc;
   }

@@ -37,6 +37,14 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream) unless stated.  Validation happens on the host before any
  *     launch; on an error nothing is launched and no output is touched.
+ *   - plan may be NULL in the calls that take one.  The call then builds a
+ *     transient plan in stream order (stream-ordered allocations, degrees
+ *     and one work item per row longer than 32 entries, its item count kept
+ *     on the device, freed stream-ordered): no host synchronisation, but no
+ *     row is split across workgroups, so skewed graphs run faster with a
+ *     plan built once by gnn_plan_create.  Calls that need the 16x16 tiles
+ *     (BLOCK16 modes, gnn_spmm_block16, gnn_gt_backward_block16) build a full
+ *     transient plan instead, which synchronises `stream`.
  *   - Return value: a gnn_status.  gnn_last_error() gives a thread-local
  *     message for the last failing call on the calling thread.
  *   - Empty neighbourhoods: sum / mean / SpMM give 0; max / min give 0 with
@@ -202,7 +210,7 @@ int gnn_plan_wsb_export(const gnn_plan* plan, int32_t* win_ptr, int32_t* blk_col
 
 /* SpMM: Y[i, f] = sum_{e in row i} w_e * X[col_idx[e], f], f < F.
  * X: device [n_cols, ldx] of `xtype`; Y: device [n_rows, ldy] float32.
- * plan may be NULL (a transient one is built, which synchronises `stream`).
+ * plan may be NULL (a transient one is built in stream order).
  * Errors: INVALID_VALUE (null, F <= 0, ldx < F, ldy < F, bad enum),
  * PLAN_MISMATCH, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
 int gnn_spmm(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, float* Y,
@@ -456,7 +464,7 @@ int gnn_permute_rows(const int32_t* perm, int32_t n, const void* X, gnn_dtype xt
  * threshold run as the plan's edge chunks, one wave each, added in chunk order.
  * Supported: 1 <= D <= 1024; GNN_LOAD_VEC16 needs D and ldx multiples of 4
  * and X 16-byte aligned.  edge_val must be NULL (no weights).  plan may be
- * NULL (a transient plan is built, synchronising `stream`).
+ * NULL (a transient plan is built in stream order).
  * Errors: INVALID_VALUE (null pointer, not square, bad D / ldx / enum, edge
  * values given, misaligned VEC16 input), UNSUPPORTED (D > 1024),
  * PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */

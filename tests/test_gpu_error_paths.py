@@ -142,3 +142,47 @@ def test_plan_verify_detects_graph_rebuilt_in_place():
     Y = gnn.gnn_spmm(csr, X, plan=plan)
     ref, mag = oracle.spmm(rp, ci, host(X), "none")
     assert scaled_err(host(Y), ref, mag) <= 1e-5
+
+
+def test_planless_calls_do_not_wait_for_the_gpu():
+    """A call without a plan builds its transient plan in stream order: it
+    returns while earlier work on the stream is still running (a 4-GiB copy,
+    about a millisecond), and its result is right once the stream drains."""
+    rp, ci = gen.rmat(0x5EED0404, 20000, 300000, self_loops=True)
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    X = gen.gauss_f32(0xFEA70404, (n, 64))
+    Xd = dev(X)
+    big = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+    big2 = torch.empty_like(big)
+    H, D = 4, 32
+    xl, xr = gen.gauss_bf16(0x4600, (n, H, D)), gen.gauss_bf16(0x4601, (n, H, D))
+    att = gen.gauss_f32(0x4602, (H, D), std=D ** -0.5)
+    dl, dr, da = dev_bf16(xl), dev_bf16(xr), dev(att)
+    # outputs allocated up front: a new torch allocation may wait for the GPU
+    Y0 = torch.empty((n, 64), device="cuda")
+    outs = {k: torch.empty((n, 64), device="cuda") for k in ("sum", "mean", "max", "min")}
+    outs.update({k: torch.empty((n, 64), dtype=torch.int32, device="cuda") for k in ("argmax", "argmin")})
+    o0, l0 = torch.empty((n, H, D), device="cuda"), torch.empty((n, H), device="cuda")
+    dX0 = torch.empty((n, 64), device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    busy = []
+    for call in (lambda: gnn.gnn_spmm(csr, Xd, "both", Y=Y0),
+                 lambda: gnn.gnn_reduce_multi(csr, Xd, out=outs),
+                 lambda: gnn.gnn_gatv2_fused(csr, dl, dr, da, 0.2, out=o0, lse=l0),
+                 lambda: gnn.gnn_spmm_backward(csr, Xd, "both", dX=dX0)):
+        gnn.gnn_copy_bytes(big, big2)
+        call()
+        busy.append(not stream.query())
+        torch.cuda.synchronize()
+    assert all(busy), busy
+    Y = gnn.gnn_spmm(csr, Xd, "both")
+    ref, mag = oracle.spmm(rp, ci, X, "both")
+    assert scaled_err(host(Y), ref, mag) <= 1e-5
+    out, lse = gnn.gnn_gatv2_fused(csr, dl, dr, da, 0.2)
+    ro, rl, va = oracle.gatv2(rp, ci, xl, xr, att, 0.2)
+    assert scaled_err(host(out), ro, va) <= 1e-4
+    dX = gnn.gnn_spmm_backward(csr, Xd, "both")
+    rb, mb = oracle.spmm_backward(rp, ci, X, "both")
+    assert bwd_err(host(dX), rb, mb) <= 1e-5
