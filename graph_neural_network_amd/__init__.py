@@ -38,7 +38,7 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
            "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune",
-           "gnn_reduce_multi_noalloc", "gnn_project", "gnn_plan_verify")
+           "gnn_reduce_multi_noalloc", "gnn_project", "gnn_plan_verify", "gnn_plan_autotune_attention")
 
 
 class GnnError(RuntimeError):
@@ -56,7 +56,8 @@ class _Csr(ctypes.Structure):
 class _PlanOpts(ctypes.Structure):
     _fields_ = [("heavy_quantile", ctypes.c_float), ("light_max_deg", ctypes.c_int32),
                 ("chunk_edges", ctypes.c_int32), ("build_wsb", ctypes.c_int32),
-                ("wsb_min_nnz", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
+                ("wsb_min_nnz", ctypes.c_int32), ("att_slot_max", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 3)]
 
 
 _lib = None
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH):
         "gnn_plan_destroy": [vp],
         "gnn_plan_stats": [vp, P(ctypes.c_int64), i32],
         "gnn_plan_verify": [vp, P(_Csr), vp],
+        "gnn_plan_autotune_attention": [P(_Csr), ci, vp, vp, vp, ci, vp, i32, i32, i32, P(_PlanOpts), P(ci),
+                                        P(f32), P(f32), vp],
         "gnn_plan_wsb_export": [vp, vp, vp, vp, vp],
         "gnn_spmm": [P(_Csr), vp, ci, i32, i64, vp, i64, ci, vp, vp],
         "gnn_reduce": [P(_Csr), vp, ci, i32, i64, ci, vp, i64, vp, vp, vp],
@@ -217,8 +220,8 @@ class Plan:
 
 def gnn_plan_create(csr: Csr, heavy_quantile: float = 0.0, light_max_deg: int = 0,
                     chunk_edges: int = 0, build_wsb: bool = False, wsb_min_nnz: int = 0,
-                    stream=None) -> Plan:
-    o = _PlanOpts(heavy_quantile, light_max_deg, chunk_edges, int(build_wsb), wsb_min_nnz)
+                    att_slot_max: int = 0, stream=None) -> Plan:
+    o = _PlanOpts(heavy_quantile, light_max_deg, chunk_edges, int(build_wsb), wsb_min_nnz, att_slot_max)
     h = ctypes.c_void_p()
     _check(load_library().gnn_plan_create(csr.ref, ctypes.byref(o), _stream(stream),
                                           ctypes.byref(h)), "gnn_plan_create")
@@ -250,6 +253,31 @@ def gnn_plan_verify(plan: Plan, csr: Csr | None = None, stream=None):
     (sizes, pointers, and sampled entries of row_ptr and col_idx)."""
     c = csr if csr is not None else plan.csr
     _check(load_library().gnn_plan_verify(plan.handle, c.ref, _stream(stream)), "gnn_plan_verify")
+
+
+def gnn_plan_autotune_attention(csr: Csr, op: str, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor | None = None,
+                                att: torch.Tensor | None = None, reps: int = 5, stream=None) -> dict:
+    """Time the attention plan candidates on this graph and these inputs;
+    op "gatv2" (q = xl, k = xr, att) or "gt" (q, k, v).  -> {"opts": {...},
+    "mode": "csr" | "block16", "best_ms": ..., "default_ms": ...}."""
+    _need(q, "q", csr.n_rows, (None, None), FEAT)
+    H, D = q.shape[1], q.shape[2]
+    _need(k, "k", csr.n_cols, (H, D), (q.dtype,))
+    if op == "gt":
+        _need(v, "v", csr.n_cols, (H, D), (q.dtype,))
+    else:
+        _need(att, "att", H, (D,), F32)
+    _gpu(q=q, k=k, v=v, att=att)
+    o = _PlanOpts()
+    mode = ctypes.c_int(0)
+    best, dflt = ctypes.c_float(0.0), ctypes.c_float(0.0)
+    _check(load_library().gnn_plan_autotune_attention(
+        csr.ref, 1 if op == "gt" else 0, _ptr(q), _ptr(k), _ptr(v), _dtype_code(q), _ptr(att), H, D, int(reps),
+        ctypes.byref(o), ctypes.byref(mode), ctypes.byref(best), ctypes.byref(dflt), _stream(stream)),
+        "gnn_plan_autotune_attention")
+    return {"opts": {"heavy_quantile": round(o.heavy_quantile, 6), "chunk_edges": o.chunk_edges,
+                     "att_slot_max": o.att_slot_max, "build_wsb": bool(o.build_wsb), "wsb_min_nnz": o.wsb_min_nnz},
+            "mode": "block16" if mode.value == 1 else "csr", "best_ms": best.value, "default_ms": dflt.value}
 
 
 def gnn_plan_stats(plan: Plan) -> dict:

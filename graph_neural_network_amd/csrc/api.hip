@@ -207,7 +207,7 @@ int gnn_plan_create(const gnn_csr* csr, const gnn_plan_opts* opts, void* stream,
   *out = nullptr;
   GNN_TRY(check_csr(csr, false));
   if (opts) {
-    if (opts->light_max_deg < 0 || opts->chunk_edges < 0 || opts->wsb_min_nnz < 0 ||
+    if (opts->light_max_deg < 0 || opts->chunk_edges < 0 || opts->wsb_min_nnz < 0 || opts->att_slot_max < 0 ||
         opts->heavy_quantile > 1.0f)
       return fail(GNN_ERR_INVALID_VALUE, "invalid plan options");
     if (opts->build_wsb && csr->n_rows != csr->n_cols)

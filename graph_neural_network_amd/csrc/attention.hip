@@ -538,7 +538,8 @@ int setup(gnn_plan* pl, AttParams& p, int kind, gnn_dtype xt, int32_t H, int32_t
   // its heavy threshold (split rows go through the items alone).  The rows
   // are listed longest first, so that the slots of a wave see rows of one
   // length and finish together.
-  p.light_max = std::max(pl->light_max, std::min(kAttLightMax, pl->heavy_thr));
+  const int32_t slot_max = pl->opts.att_slot_max > 0 ? pl->opts.att_slot_max : kAttLightMax;
+  p.light_max = std::max(pl->light_max, std::min(slot_max, pl->heavy_thr));
   GNN_TRY(plan_att_rows(pl, p.light_max, s));
   p.att_rows = pl->att_rows;
   p.att_count = pl->att_count;

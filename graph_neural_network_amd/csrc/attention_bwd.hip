@@ -440,7 +440,8 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   p.col_idx = pl->col_idx;
   p.items = pl->items;
   p.n_rows = pl->n_rows;
-  p.light_max = std::max(pl->light_max, std::min(kBwdLightMax, pl->heavy_thr));
+  const int32_t slot_max = pl->opts.att_slot_max > 0 ? pl->opts.att_slot_max : kBwdLightMax;
+  p.light_max = std::max(pl->light_max, std::min(slot_max, pl->heavy_thr));
   GNN_TRY(plan_att_rows(pl, p.light_max, s));
   p.light_rows = pl->att_rows;
   p.light_count = pl->att_count;

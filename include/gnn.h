@@ -139,7 +139,9 @@ typedef struct gnn_plan_opts {
   int32_t chunk_edges;     /* edges per chunk of a split row (default 1024) */
   int32_t build_wsb;       /* 1 = also build the 16x16 block-sparse tiles (GT BLOCK16) */
   int32_t wsb_min_nnz;     /* tau: tiles with fewer edges go to the CSR residual (default 8) */
-  int32_t reserved[4];
+  int32_t att_slot_max;    /* fused attention: rows of up to this many edges run one per slot,
+                              longer ones one workgroup per row or chunk (default 128) */
+  int32_t reserved[3];
 } gnn_plan_opts;
 
 /* Opaque plan: the per-graph cache of appendix D.4 made explicit.  It holds
@@ -198,6 +200,30 @@ typedef enum { GNN_TUNE_SPMM = 0, GNN_TUNE_SUM = 1, GNN_TUNE_MULTI = 2 } gnn_tun
  * Errors: INVALID_VALUE, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
 int gnn_plan_autotune(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t F, int64_t ldx, gnn_tune_op op,
                       int32_t reps, gnn_plan_opts* best, float* best_ms, float* default_ms, void* stream);
+
+/* Operation an attention autotuning run times. */
+typedef enum { GNN_TUNE_GATV2 = 0, GNN_TUNE_GT = 1 } gnn_tune_att_op;
+
+/* Measured choice of the plan knobs of a fused attention layer on the
+ * caller's graph and inputs (appendix D.1 autotuning parameters; appendix D.3
+ * and section 5 pick CSR or block-sparse attention by local density).  The
+ * CSR kernel is timed for heavy_quantile in {0.99, 0.999, -1 (no split)} x
+ * chunk_edges in {256, 1024} x att_slot_max in {32, 128, 512}; for GT with
+ * bf16 inputs, a square CSR and D in {32, 64, 128, 256} also the BLOCK16
+ * kernel with wsb_min_nnz (tau) in {1, 8, 32}.  Each candidate: a plan, one
+ * untimed call, `reps` timed calls between HIP events on `stream`; the one
+ * of least mean time wins.  GATv2: q = xl, k = xr, att required, slope 0.2,
+ * v unused; GT: q, k, v, scale 1/sqrt(D).  Shapes as gnn_gatv2_fused /
+ * gnn_gt_fused.  Outputs (host): *best the winning options (pass them to
+ * gnn_plan_create), *best_mode GNN_GT_CSR or GNN_GT_BLOCK16 (the mode to
+ * call gnn_gt_fused with; CSR for GATv2), *best_ms its mean time,
+ * *default_ms (nullable) the library defaults' (default plan, AUTO for GT).
+ * Allocates its outputs and plans, frees them, synchronises `stream`.
+ * Errors: INVALID_VALUE, UNSUPPORTED, SIZE_OVERFLOW, OUT_OF_MEMORY, DEVICE. */
+int gnn_plan_autotune_attention(const gnn_csr* csr, gnn_tune_att_op op, const void* q, const void* k,
+                                const void* v, gnn_dtype xtype, const float* att, int32_t H, int32_t D,
+                                int32_t reps, gnn_plan_opts* best, gnn_gt_mode* best_mode, float* best_ms,
+                                float* default_ms, void* stream);
 
 /* Copy the plan's WSB layout (appendix D.3: windows of 16 rows, sorted
  * distinct source columns cut into blocks of 8 zero-padded columns, a 16x8

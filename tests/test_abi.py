@@ -124,6 +124,20 @@ INV, UNS, OVF = 1, 2, 5
                                         ctypes.byref(ctypes.c_float()), None, None), INV),
     ("autotune ldx<F", lambda: call("gnn_plan_autotune", ctypes.byref(fake_csr()), P(16), 0, 8, 4, 0, 3,
                                     ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune att null csr", lambda: call("gnn_plan_autotune_attention", None, 1, P(16), P(16), P(16), 1, None, 8, 64, 3,
+                                           ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_int()),
+                                           ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune att bad op", lambda: call("gnn_plan_autotune_attention", ctypes.byref(fake_csr()), 5, P(16), P(16), P(16), 1,
+                                         None, 8, 64, 3, ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_int()),
+                                         ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune att gatv2 no att", lambda: call("gnn_plan_autotune_attention", ctypes.byref(fake_csr()), 0, P(16), P(16),
+                                               None, 1, None, 4, 32, 3, ctypes.byref(gnn._PlanOpts()),
+                                               ctypes.byref(ctypes.c_int()), ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("autotune att reps=0", lambda: call("gnn_plan_autotune_attention", ctypes.byref(fake_csr()), 1, P(16), P(16), P(16), 1,
+                                         None, 8, 64, 0, ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_int()),
+                                         ctypes.byref(ctypes.c_float()), None, None), INV),
+    ("plan bad slot max", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),
+                                       ctypes.byref(gnn._PlanOpts(0, 0, 0, 0, 0, -1)), None, ctypes.byref(P())), INV),
     ("stats null", lambda: call("gnn_plan_stats", None, None, 9), INV),
     ("permute bad F", lambda: call("gnn_permute_rows", P(8), 4, P(8), 0, 0, 4, P(8), 4, None), INV),
     ("copy negative", lambda: call("gnn_copy_bytes", P(8), P(8), -1, None), INV),

@@ -53,6 +53,9 @@ CASES = {
     "gnn_reorder": lambda: ("gnn_reorder", csr(), 1, P(16), P(16), P(16), None),
     "gnn_plan_autotune": lambda: ("gnn_plan_autotune", csr(), P(16), 0, 4, 4, 2, 3, ctypes.byref(gnn._PlanOpts()),
                                   ctypes.byref(F()), None, None),
+    "gnn_plan_autotune_attention": lambda: ("gnn_plan_autotune_attention", csr(), 1, P(16), P(16), P(16), 1, None, 8,
+                                            64, 3, ctypes.byref(gnn._PlanOpts()), ctypes.byref(ctypes.c_int()),
+                                            ctypes.byref(F()), None, None),
 }
 
 
