@@ -18,8 +18,10 @@
 // forms Y^T = W X^T, so lane l ends with Y[row l % 16][o 4 (l / 16) .. +3]:
 // four consecutive outputs of one row, converted to bf16 in one instruction
 // and written as 8 bytes to the wave's LDS staging tile.  The staged
-// 16 * MR x 128 block is then stored as 16 contiguous bytes per lane, whole
+// 16 * MR x 64 block is then stored as 16 contiguous bytes per lane, whole
 // lines per instruction.  Each weight fragment serves MR row tiles.
+#include <algorithm>
+
 #include "gnn_internal.h"
 
 namespace gnn {
@@ -30,7 +32,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 constexpr int WG = 256;
-constexpr int OCH = 128;           // output features staged per pass
+constexpr int OCH = 64;            // output features staged per pass
 constexpr int SROW = OCH + 8;      // staging row stride (bf16), padded against bank conflicts
 
 struct ProjParams {
@@ -73,43 +75,54 @@ __global__ __launch_bounds__(WG) void k_project(ProjParams p) {
   uint16_t(*st)[SROW] = stage[wave];
   const int n_here = (int)min<int64_t>(16 * MR, (int64_t)p.n - r_base);
 
-  for (int m = 0; m < p.n_mat; ++m) {
+  // output chunks of OCH features of each of the n_mat weights in turn
+  const int cpm = (p.f_out + OCH - 1) / OCH;  // chunks per weight
+  for (int cidx = 0; cidx < p.n_mat * cpm; ++cidx) {
+    const int m = cidx / cpm, o0 = (cidx % cpm) * OCH;
     const uint16_t* W = p.W[m];
     uint16_t* Y = p.Y[m];
-    for (int o0 = 0; o0 < p.f_out; o0 += OCH) {
-      const int ow = min(OCH, p.f_out - o0);  // a multiple of 16
-      for (int t = 0; t < ow; t += 16) {
-        f32x4 acc[MR];
+    const int ow = min(OCH, p.f_out - o0);  // a multiple of 16
+    // weight fragments of the next 16-feature tile are loaded while the
+    // current tile's products run
+    bf16x8 wcur[KS], wnxt[KS];
+    const uint16_t* w0 = W + (int64_t)(o0 + lr) * K + 8 * lk;
 #pragma unroll
-        for (int r = 0; r < MR; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint16_t* wrow = W + (int64_t)(o0 + t + lr) * K + 8 * lk;
+    for (int k = 0; k < KS; ++k) wcur[k] = *reinterpret_cast<const bf16x8*>(w0 + 32 * k);
+    for (int t = 0; t < ow; t += 16) {
+      const int tn = t + 16 < ow ? t + 16 : t;  // the last tile re-reads itself
+      const uint16_t* wn = W + (int64_t)(o0 + tn + lr) * K + 8 * lk;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + 32 * k);
+      for (int k = 0; k < KS; ++k) wnxt[k] = *reinterpret_cast<const bf16x8*>(wn + 32 * k);
+      f32x4 acc[MR];
 #pragma unroll
-          for (int r = 0; r < MR; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf, xf[r][k], acc[r], 0, 0, 0);
-        }
-        // lane: row 16 r + lr, outputs t + 4 lk .. +3
+      for (int r = 0; r < MR; ++r) acc[r] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          const uint2 w2 = make_uint2(pack_bf16(acc[r][0], acc[r][1]), pack_bf16(acc[r][2], acc[r][3]));
-          *reinterpret_cast<uint2*>(&st[16 * r + lr][t + 4 * lk]) = w2;
-        }
+      for (int k = 0; k < KS; ++k) {
+#pragma unroll
+        for (int r = 0; r < MR; ++r) acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wcur[k], xf[r][k], acc[r], 0, 0, 0);
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // store the staged rows: ow / 8 lanes of 16 bytes per row
-      const int lpr = ow / 8;
-      for (int q = lane; q < n_here * lpr; q += 64) {
-        const int row = q / lpr, c = (q % lpr) * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(&st[row][c]);
-        *reinterpret_cast<uint4*>(Y + (r_base + row) * p.f_out + o0 + c) = v;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) wcur[k] = wnxt[k];
+      // lane: row 16 r + lr, outputs t + 4 lk .. +3
+#pragma unroll
+      for (int r = 0; r < MR; ++r) {
+        const uint2 w2 = make_uint2(pack_bf16(acc[r][0], acc[r][1]), pack_bf16(acc[r][2], acc[r][3]));
+        *reinterpret_cast<uint2*>(&st[16 * r + lr][t + 4 * lk]) = w2;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // store the staged rows: ow / 8 lanes of 16 bytes per row
+    const int lpr = ow / 8;
+    for (int q = lane; q < n_here * lpr; q += 64) {
+      const int row = q / lpr, c = (q % lpr) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(&st[row][c]);
+      *reinterpret_cast<uint4*>(Y + (r_base + row) * p.f_out + o0 + c) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
