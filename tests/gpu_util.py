@@ -50,3 +50,18 @@ def bits_equal_f32(got, ref) -> bool:
     g = np.ascontiguousarray(np.asarray(got, np.float32))
     r = np.ascontiguousarray(np.asarray(ref, np.float64).astype(np.float32))
     return bool(np.array_equal(g.view(np.uint32), r.view(np.uint32)))
+
+
+def plain_rel(got, ref, floor_frac=1e-6):
+    """The plain relative error |got - ref| / |ref| over the outputs with |ref|
+    above floor_frac * max |ref| (a sum that cancels to near zero has no useful
+    relative error): {"median", "p99", "max", "n", "excluded"}."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    a = np.abs(ref)
+    keep = a > floor_frac * (a.max() if a.size else 0.0)
+    r = np.abs(got[keep] - ref[keep]) / a[keep]
+    if r.size == 0:
+        return {"median": 0.0, "p99": 0.0, "max": 0.0, "n": 0, "excluded": int((~keep).sum())}
+    return {"median": float(np.median(r)), "p99": float(np.quantile(r, 0.99)), "max": float(r.max()),
+            "n": int(r.size), "excluded": int((~keep).sum())}

@@ -14,7 +14,7 @@ import torch
 import gen
 import graph_neural_network_amd as gnn
 import oracle
-from gpu_util import bits_equal_f32, dev, dev_bf16, dev_csr, host, scaled_err
+from gpu_util import plain_rel, bits_equal_f32, dev, dev_bf16, dev_csr, host, scaled_err
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -37,6 +37,8 @@ def check_reduce(rp, ci, Xh, Yg, argg, op, rows=None):
         Yg2 = Yg if rows is None else Yg[rows]
         err = scaled_err(Yg2, y, mag)
         assert err <= TOL, f"{op}: scaled error {err}"
+        # the plain relative error, reported beside the bar's scaled one
+        print(f"{op}: scaled error {err:.2e}, plain relative error {plain_rel(Yg2, y)}", flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -50,6 +52,7 @@ def test_gcn_er2000():
     Y = host(gnn.gnn_spmm(csr, dev(X), "both"))
     ref, mag = oracle.spmm(w.row_ptr, w.col_idx, X, "both")
     assert scaled_err(Y, ref, mag) <= TOL
+    print(f"config 1 GCN: plain relative error {plain_rel(Y, ref)}", flush=True)
     # with a plan: same result bit for bit (deterministic)
     plan = gnn.gnn_plan_create(csr)
     Y2 = host(gnn.gnn_spmm(csr, dev(X), "both", plan=plan))
