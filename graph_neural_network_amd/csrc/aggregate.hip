@@ -713,6 +713,7 @@ int pick_kind(gnn_plan* pl, AggParams& p, int kind, bool arg, int lpr, hipStream
 int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y,
                      int64_t ldy, int mode, gnn_norm norm, const float* edge_val, int32_t* arg,
                      hipStream_t s) {
+  if (mode == AGG_SPMM && (norm == GNN_NORM_RIGHT || norm == GNN_NORM_BOTH)) GNN_TRY(plan_deg_out(pl, s));
   AggParams p{};
   p.row_ptr = pl->row_ptr;
   p.col_idx = pl->col_idx;

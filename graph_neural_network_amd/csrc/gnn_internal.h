@@ -122,7 +122,7 @@ struct gnn_plan {
   int32_t* fp_dev = nullptr;
 
   // degrees
-  int32_t* deg_out = nullptr;  // [n_cols]
+  int32_t* deg_out = nullptr;  // [n_cols]; NULL until counted (transient plans: on first use)
 
   // degree bins (appendix D.1: light / heavy split by a degree quantile)
   int32_t light_max = 32;
@@ -173,11 +173,17 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out);
 // a plan-owned buffer that grows on demand (freed with the plan)
 int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes);
 int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn_plan* p);
-// The transient plan of a call made without one: degrees and one work item
-// per row longer than the light bound (no split rows), built on `s` with
+// The transient plan of a call made without one: one work item per row
+// longer than the light bound (no split rows), built on `s` with
 // stream-ordered memory and no host synchronisation; its item count stays on
-// the device (item_count), n_items holds an upper bound for grid sizes.
+// the device (item_count), n_items holds an upper bound for grid sizes.  Its
+// out-degrees are counted on first use (plan_deg_out).
 int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p);
+// deg_out[j] = entries with column j (columns outside [0, n_cols) are not
+// counted); enqueued on `s`, temporaries stream-ordered.
+int count_out_degrees(const int32_t* col_idx, int64_t nnz, int32_t n_cols, int32_t* deg_out, hipStream_t s);
+// The plan's out-degrees, counted now if the plan does not hold them yet.
+int plan_deg_out(gnn_plan* p, hipStream_t s);
 int plan_build_wsb(gnn_plan* p, hipStream_t s);
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s);
 int plan_transpose(gnn_plan* p, hipStream_t s);

@@ -94,12 +94,6 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(const int32_t* in, 
 
 // ---------------------------------------------------------------------------
 
-__global__ void k_deg_out(const int32_t* col_idx, int64_t nnz, int32_t* deg_out) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; e < nnz; e += stride) atomicAdd(&deg_out[col_idx[e]], 1);
-}
-
 // Degree histogram.  Low degrees are very common on power-law graphs (most
 // rows have degree 0 or 1), so each workgroup counts bins below kLdsBins in
 // LDS and flushes its non-zero bins once; larger degrees go straight to the
@@ -428,6 +422,15 @@ int plan_verify(gnn_plan* p, hipStream_t s) {
   return GNN_OK;
 }
 
+int plan_deg_out(gnn_plan* p, hipStream_t s) {
+  if (p->deg_out) return GNN_OK;
+  int32_t* d = nullptr;
+  GNN_TRY(plan_alloc(p, (void**)&d, (size_t)std::max(p->n_cols, 1) * 4));
+  GNN_TRY(count_out_degrees(p->col_idx, p->nnz, p->n_cols, d, s));
+  p->deg_out = d;
+  return GNN_OK;
+}
+
 int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
   p->n_rows = csr->n_rows;
   p->n_cols = csr->n_cols;
@@ -441,13 +444,7 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
   p->chunk_edges = 1024;
   p->heavy_thr = INT32_MAX;  // no row is split
   const int32_t n = p->n_rows;
-  GNN_TRY(plan_alloc(p, (void**)&p->deg_out, (size_t)std::max(p->n_cols, 1) * 4));
-  GNN_HIP(hipMemsetAsync(p->deg_out, 0, (size_t)std::max(p->n_cols, 1) * 4, s));
-  if (p->nnz > 0) {
-    int64_t blocks = std::min<int64_t>((p->nnz + 255) / 256, 65536);
-    hipLaunchKernelGGL(k_deg_out, dim3((unsigned)blocks), dim3(256), 0, s, p->col_idx, p->nnz, p->deg_out);
-    GNN_LAUNCH_CHECK("deg_out");
-  }
+  // out-degrees on first use (plan_deg_out)
   // rows longer than the light bound: at most one per light_max + 1 entries
   const int64_t bound = std::min<int64_t>(n, p->nnz / (p->light_max + 1));
   p->n_items = bound;
@@ -499,13 +496,7 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   GNN_TRY(plan_alloc(p, (void**)&p->fp_dev, sizeof(p->fp_host)));
   GNN_TRY(plan_sample_fingerprint(p, s));
   GNN_HIP(hipMemcpyAsync(p->fp_host, p->fp_dev, sizeof(p->fp_host), hipMemcpyDeviceToHost, s));
-  GNN_HIP(hipMemsetAsync(p->deg_out, 0, (size_t)std::max(p->n_cols, 1) * 4, s));
-  if (p->nnz > 0) {
-    int64_t blocks = std::min<int64_t>((p->nnz + 255) / 256, 65536);
-    hipLaunchKernelGGL(k_deg_out, dim3((unsigned)blocks), dim3(256), 0, s, p->col_idx, p->nnz,
-                       p->deg_out);
-    GNN_LAUNCH_CHECK("deg_out");
-  }
+  GNN_TRY(count_out_degrees(p->col_idx, p->nnz, p->n_cols, p->deg_out, s));
 
   // gamma-quantile degree threshold
   StreamTemps tt(s);

@@ -276,6 +276,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
 
 int launch_spmm_block16(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64_t ldx, float* Y, int64_t ldy,
                         gnn_norm norm, hipStream_t s) {
+  if (norm == GNN_NORM_RIGHT || norm == GNN_NORM_BOTH) GNN_TRY(plan_deg_out(pl, s));
   B16SpmmParams p{};
   p.row_ptr = pl->row_ptr;
   p.deg_out = pl->deg_out;

@@ -89,6 +89,7 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   if (!p->t_col) GNN_TRY(plan_alloc(p, (void**)&p->t_col, (size_t)std::max<int64_t>(m, 1) * 4));
   if (!p->t_edge) GNN_TRY(plan_alloc(p, (void**)&p->t_edge, (size_t)std::max<int64_t>(m, 1) * 4));
   // row pointers of A^T: the exclusive scan of the out-degrees
+  GNN_TRY(plan_deg_out(p, s));
   GNN_TRY(exclusive_scan_i32(p->deg_out, p->t_row_ptr, nc, s));
   if (m > 0) {
     int32_t *ends = nullptr, *rows = nullptr;
