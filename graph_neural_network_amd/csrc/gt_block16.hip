@@ -24,6 +24,8 @@
 // acc) state, the four lanes of a row splitting the head dimension.
 // Windows are mapped to XCDs in runs of consecutive windows, so the windows of
 // one locally dense cluster share an L2.
+#include <type_traits>
+
 #include "gnn_internal.h"
 
 namespace gnn {
@@ -60,10 +62,22 @@ struct B16Params {
   float scale_log2;  // scale * log2(e)
 };
 
-__device__ __forceinline__ uint16_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Max / sum over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48) with
+// the gfx950 lane-swap instructions, on the VALU (a shuffle would go through
+// the LDS crossbar).  v_permlane32_swap(x, x) leaves x[l] and x[l ^ 32] in
+// the pair at every lane, v_permlane16_swap x[l] and x[l ^ 16]; every lane
+// of the row ends with the same value.
+__device__ __forceinline__ float row4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -109,8 +123,10 @@ void k_gt_block16(B16Params p) {
   constexpr int MB = D / 16;   // 16-dim blocks of the output
   constexpr int LDV = D + 8;   // padded LDS row (bf16 elements)
   constexpr int LDO = D + 4;   // padded LDS row of the output stage (floats)
-  __shared__ uint16_t s_v[NWAVE][16 * LDV];
-  __shared__ __align__(16) float s_o[NWAVE][16 * LDO];
+  // per wave: the value block of the current tile during the tile loop, the
+  // output block of the head after it (never both at once)
+  constexpr int STAGE_BYTES = 16 * LDO * 4 > 16 * LDV * 2 ? 16 * LDO * 4 : 16 * LDV * 2;
+  __shared__ __align__(16) unsigned char s_stage[NWAVE][STAGE_BYTES];
   __shared__ int32_t s_col[MAXT][16];                // the 16 columns of each tile
   __shared__ unsigned long long s_bits[MAXT][4];     // block 0 words 0-1, block 1 words 0-1
 
@@ -125,8 +141,8 @@ void k_gt_block16(B16Params p) {
   const bool staged = nt <= MAXT;
   const int res_b = row_ok ? p.res_ptr[row] : 0, res_e = row_ok ? p.res_ptr[row + 1] : 0;
   const int64_t ldr = (int64_t)p.H * D;  // elements per node row
-  uint16_t* lv = s_v[wave];
-  float* lo = s_o[wave];
+  uint16_t* lv = reinterpret_cast<uint16_t*>(s_stage[wave]);
+  float* lo = reinterpret_cast<float*>(s_stage[wave]);
 
   // tile metadata of the window, one cooperative pass
   if (staged) {
@@ -143,16 +159,26 @@ void k_gt_block16(B16Params p) {
   }
   __syncthreads();
 
-  auto tile_col = [&](int t) -> int {
-    if (staged) return s_col[t - t_beg][r];
-    const int blk = p.tile_blk[t] + (r >> 3);
-    return ((r >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (r & 7)];
+  // Tile metadata from LDS (ST) or from memory.  The two are separate
+  // instantiations of the tile loop: a metadata load from memory inside the
+  // loop would make the compiler wait for every outstanding load (the next
+  // tile's K / V included) before using it.
+  auto tile_col = [&](auto st, int t) -> int {
+    if constexpr (decltype(st)::value) {
+      return s_col[t - t_beg][r];
+    } else {
+      const int blk = p.tile_blk[t] + (r >> 3);
+      return ((r >> 3) == 1 && blk >= b_end) ? 0 : p.blk_col[(int64_t)blk * 8 + (r & 7)];
+    }
   };
-  auto tile_word = [&](int t) -> unsigned long long {
+  auto tile_word = [&](auto st, int t) -> unsigned long long {
     const int ub = g >> 1;  // which 16x8 block holds this lane's four columns
-    if (staged) return s_bits[t - t_beg][ub * 2 + (r >> 3)];
-    const int blk = p.tile_blk[t] + ub;
-    return (ub == 1 && blk >= b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+    if constexpr (decltype(st)::value) {
+      return s_bits[t - t_beg][ub * 2 + (r >> 3)];
+    } else {
+      const int blk = p.tile_blk[t] + ub;
+      return (ub == 1 && blk >= b_end) ? 0ull : p.blk_bits[(int64_t)blk * 2 + (r >> 3)];
+    }
   };
 
   for (int h = wave; h < p.H; h += NWAVE) {
@@ -170,8 +196,8 @@ void k_gt_block16(B16Params p) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto load_kv = [&](int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
-      const int col = tile_col(t);
+    auto load_kv = [&](auto st, int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
+      const int col = tile_col(st, t);
       const uint16_t* krow = p.k + (int64_t)col * ldr + h * D;
       const uint16_t* vrow = p.v + (int64_t)col * ldr + h * D;
 #pragma unroll
@@ -181,8 +207,8 @@ void k_gt_block16(B16Params p) {
       }
     };
 
-    auto process = [&](int t, const s16x8 (&ka)[KC], const s16x8 (&va)[KC]) {
-      const unsigned long long word = tile_word(t);
+    auto process = [&](auto stg, int t, const s16x8 (&ka)[KC], const s16x8 (&va)[KC]) {
+      const unsigned long long word = tile_word(stg, t);
       const int base = (r & 7) * 8 + 4 * (g & 1);
       f32x4 st = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -196,25 +222,29 @@ void k_gt_block16(B16Params p) {
         s[i] = ((word >> (base + i)) & 1ull) ? st[i] * p.scale_log2 : -INFINITY;
         mx = fmaxf(mx, s[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = row4_max(mx);
       const float mn = fmaxf(m, mx);
       float corr = 1.0f;
       uint16_t pb[4];
       float rs = 0.0f;
       if (mn != -INFINITY) {
         corr = ex2(m - mn);
+        // weights rounded to bf16 (nearest even) two at a time by v_cvt_pk_bf16_f32
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[i] = f2bf_rne(ex2(s[i] - mn));
-          rs += bf(pb[i]);
+        for (int i = 0; i < 4; i += 2) {
+          bf16x2 w2;
+          w2[0] = (__bf16)ex2(s[i] - mn);
+          w2[1] = (__bf16)ex2(s[i + 1] - mn);
+          const uint32_t u = __builtin_bit_cast(uint32_t, w2);
+          pb[i] = (uint16_t)(u & 0xffffu);
+          pb[i + 1] = (uint16_t)(u >> 16);
+          rs += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) pb[i] = 0;
       }
-      rs += __shfl_xor(rs, 16, 64);
-      rs += __shfl_xor(rs, 32, 64);
+      rs = row4_sum(rs);
       lsum = lsum * corr + rs;
       m = mn;
 #pragma unroll
@@ -240,25 +270,41 @@ void k_gt_block16(B16Params p) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     };
 
-    if constexpr (D <= 128) {
-      // two-deep pipeline: the next tile's K / V are in flight while one computes
-      s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
-      if (t_beg < t_end) load_kv(t_beg, kA, vA);
-      for (int t = t_beg; t < t_end; t += 2) {
-        if (t + 1 < t_end) load_kv(t + 1, kB, vB);
-        process(t, kA, vA);
-        if (t + 1 < t_end) {
-          if (t + 2 < t_end) load_kv(t + 2, kA, vA);
-          process(t + 1, kB, vB);
+    auto tiles = [&](auto st) {
+      if constexpr (D <= 128) {
+        // two-deep pipeline: the next tile's K / V are in flight while one
+        // computes.  The loop runs while both prefetches exist, and the last
+        // one or two tiles follow it: a prefetch under a branch inside the
+        // loop leaves the compiler two load counts to reconcile at the join,
+        // and it then waits for the prefetched tile with the current one.
+        if (t_beg < t_end) {
+          s16x8 kA[KC], vA[KC], kB[KC], vB[KC];
+          load_kv(st, t_beg, kA, vA);
+          int t = t_beg;
+          for (; t + 2 < t_end; t += 2) {
+            load_kv(st, t + 1, kB, vB);
+            process(st, t, kA, vA);
+            load_kv(st, t + 2, kA, vA);
+            process(st, t + 1, kB, vB);
+          }
+          if (t + 1 < t_end) {
+            load_kv(st, t + 1, kB, vB);
+            process(st, t, kA, vA);
+            process(st, t + 1, kB, vB);
+          } else {
+            process(st, t, kA, vA);
+          }
+        }
+      } else {
+        s16x8 kA[KC], vA[KC];
+        for (int t = t_beg; t < t_end; ++t) {
+          load_kv(st, t, kA, vA);
+          process(st, t, kA, vA);
         }
       }
-    } else {
-      s16x8 kA[KC], vA[KC];
-      for (int t = t_beg; t < t_end; ++t) {
-        load_kv(t, kA, vA);
-        process(t, kA, vA);
-      }
-    }
+    };
+    if (staged) tiles(std::true_type{});
+    else tiles(std::false_type{});
 
     // residual edges of this row: the row's four lanes split the head dims
     int j_next = (res_b < res_e) ? p.res_col[res_b] : 0;
@@ -276,8 +322,7 @@ void k_gt_block16(B16Params p) {
       float dot = 0.0f;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) dot = dot8(qb[kc], kv[kc], dot);
-      dot += __shfl_xor(dot, 16, 64);
-      dot += __shfl_xor(dot, 32, 64);
+      dot = row4_sum(dot);
       const float sc = dot * p.scale_log2;
       const float mn = fmaxf(m, sc);
       const float corr = ex2(m - mn);
