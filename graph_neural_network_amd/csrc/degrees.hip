@@ -46,11 +46,35 @@ __global__ void k_deg_out_atomic(const int32_t* col_idx, int64_t nnz, int32_t n_
   }
 }
 
-// Visit the columns of entries [e0, e1) with f(column): 16-byte loads when
-// col_idx is 16-byte aligned (e0 is a multiple of 4 in every caller), four
-// of them in flight per thread.
-template <typename Fn>
-__device__ __forceinline__ void for_each_col(const int32_t* col, int64_t e0, int64_t e1, bool vec, Fn&& f) {
+// h[v] += 1 for every lane's v.  A column with a large in-degree fills many
+// lanes of a wave with the same value, and same-address LDS atomics are
+// serialised: lanes sharing the first pending lane's value add once, by
+// their count, for as long as such a value is shared by two lanes or more
+// (at most three rounds); the rest add one each.
+__device__ __forceinline__ void wave_hist_add(int32_t* h, uint32_t v, bool valid) {
+  bool pending = valid;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    const unsigned long long act = __ballot(pending);
+    if (!act) return;
+    const int src = __ffsll((long long)act) - 1;
+    const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+    const unsigned long long same = __ballot(pending && v == u);
+    const int k = __popcll(same);
+    if (k < 2) break;
+    if ((int)(threadIdx.x & 63) == src) atomicAdd(&h[u], k);
+    pending = pending && v != u;
+  }
+  if (pending) atomicAdd(&h[v], 1);
+}
+
+// Visit the columns of entries [e0, e1): f4(c) with four consecutive columns
+// (an int4) over the 16-byte aligned middle when col_idx is 16-byte aligned
+// (e0 is a multiple of 4 in every caller), four loads in flight per thread;
+// f(c) with single columns otherwise.
+template <typename Fn, typename Fn4>
+__device__ __forceinline__ void for_each_col(const int32_t* col, int64_t e0, int64_t e1, bool vec, Fn&& f,
+                                             Fn4&& f4) {
   int64_t e = e0;
   if (vec) {
     const int64_t step = 16 * (int64_t)blockDim.x;
@@ -60,12 +84,7 @@ __device__ __forceinline__ void for_each_col(const int32_t* col, int64_t e0, int
       for (int k = 0; k < 4; ++k)
         c[k] = *reinterpret_cast<const int4*>(col + e + 4 * ((int64_t)threadIdx.x + (int64_t)k * blockDim.x));
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f(c[k].x);
-        f(c[k].y);
-        f(c[k].z);
-        f(c[k].w);
-      }
+      for (int k = 0; k < 4; ++k) f4(c[k]);
     }
   }
   for (e += threadIdx.x; e < e1; e += blockDim.x) f(col[e]);
@@ -80,8 +99,23 @@ __global__ __launch_bounds__(kSegThreads) void k_dego_count(const int32_t* col, 
   __syncthreads();
   const int64_t g = blockIdx.x, G = gridDim.x;
   const int64_t e0 = g * seg, e1 = std::min(nnz, e0 + seg);
-  for_each_col(col, e0, e1, vec, [&](int32_t c) {
+  // consecutive entries often share a bucket (a row's sources in one
+  // cluster, sorted columns): four equal buckets add once
+  auto one = [&](int32_t c) {
     if ((uint32_t)c < (uint32_t)n_cols) atomicAdd(&h[(uint32_t)c >> shift], 1);
+  };
+  for_each_col(col, e0, e1, vec, one, [&](int4 c) {
+    const uint32_t b = (uint32_t)c.x >> shift;
+    const uint32_t nc = (uint32_t)n_cols;
+    if ((uint32_t)c.x < nc && (uint32_t)c.y < nc && (uint32_t)c.z < nc && (uint32_t)c.w < nc &&
+        ((uint32_t)c.y >> shift) == b && ((uint32_t)c.z >> shift) == b && ((uint32_t)c.w >> shift) == b) {
+      atomicAdd(&h[b], 4);
+    } else {
+      one(c.x);
+      one(c.y);
+      one(c.z);
+      one(c.w);
+    }
   });
   __syncthreads();
   for (int b = threadIdx.x; b < nb; b += blockDim.x) cnt[(int64_t)b * G + g] = h[b];
@@ -163,9 +197,27 @@ __global__ __launch_bounds__(kSegThreads, 4) void k_dego_scatter(const int32_t* 
         c[k] = i < n_r ? col[r0 + i] : -1;
       }
     }
+    // ranks within the bucket; four consecutive entries of one bucket (the
+    // groups of a 16-byte load) take four ranks from one atomic
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      rank[k] = (uint32_t)c[k] < (uint32_t)n_cols ? atomicAdd(&lst[(uint32_t)c[k] >> shift], 1) : -1;
+    for (int q = 0; q < kPer / 4; ++q) {
+      const uint32_t b = (uint32_t)c[4 * q] >> shift;
+      bool four = vec && n_r == kSub;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        four = four && (uint32_t)c[4 * q + j] < (uint32_t)n_cols && ((uint32_t)c[4 * q + j] >> shift) == b;
+      if (four) {
+        const int base = atomicAdd(&lst[b], 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rank[4 * q + j] = base + j;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t cj = (uint32_t)c[4 * q + j];
+          rank[4 * q + j] = cj < (uint32_t)n_cols ? atomicAdd(&lst[cj >> shift], 1) : -1;
+        }
+      }
+    }
     __syncthreads();
     block_scan_buckets(lst, nb, wsum);
     __syncthreads();
@@ -236,28 +288,6 @@ __global__ __launch_bounds__(1024) void k_dego_parts(const int32_t* off, int64_t
     run += v[k];
   }
   if (threadIdx.x == 0) part_off[nb] = total;
-}
-
-// h[v] += 1 for every lane's v.  A column with a large in-degree fills many
-// lanes of a wave with the same value, and same-address LDS atomics are
-// serialised: lanes sharing the first pending lane's value add once, by
-// their count, for as long as such a value is shared by two lanes or more
-// (at most three rounds); the rest add one each.
-__device__ __forceinline__ void wave_hist_add(int32_t* h, uint32_t v, bool valid) {
-  bool pending = valid;
-#pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    const unsigned long long act = __ballot(pending);
-    if (!act) return;
-    const int src = __ffsll((long long)act) - 1;
-    const uint32_t u = (uint32_t)__builtin_amdgcn_readlane((int)v, src);
-    const unsigned long long same = __ballot(pending && v == u);
-    const int k = __popcll(same);
-    if (k < 2) break;
-    if ((int)(threadIdx.x & 63) == src) atomicAdd(&h[u], k);
-    pending = pending && v != u;
-  }
-  if (pending) atomicAdd(&h[v], 1);
 }
 
 // Workgroup g takes part p of bucket b (part_off[b] <= g < part_off[b + 1]):

@@ -19,7 +19,8 @@
 //   2. distinct keys -> per-window distinct column count -> blocks per window
 //      (ceil(count / 8)) -> win_ptr by a scan; block column lists filled.
 //   3. every CSR edge finds its column among its window's sorted distinct
-//      columns (binary search) and sets its bit (atomicOr).
+//      columns (binary search, one workgroup per window, the columns in LDS)
+//      and sets its bit in the window's LDS bitmaps, stored once.
 //   4. tiles: block pairs (0,1), (2,3), ... of each window; dense when their
 //      bit count >= tau -> tile list per window (scan).
 //   5. residual CSR: edges of non-dense tiles, in CSR order per row (scan).
@@ -30,23 +31,17 @@
 namespace gnn {
 namespace {
 
-__device__ __forceinline__ int row_of_edge(const int32_t* row_ptr, int32_t n, int64_t e) {
-  // largest r with row_ptr[r] <= e
-  int lo = 0, hi = n - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (row_ptr[mid] <= e) lo = mid;
-    else hi = mid - 1;
-  }
-  return lo;
-}
+// One workgroup per window of 16 rows: the window's entries are contiguous
+// in the CSR, so no entry has to search for its row or window.
+constexpr int kWinThreads = 256;
+constexpr int kWinLdsBlocks = 512;  // windows with at most this many blocks keep columns and bits in LDS
 
-__global__ void k_wsb_keys(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
-                           int colbits, uint64_t* keys) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz) return;
-  const int r = row_of_edge(row_ptr, n, e);
-  keys[e] = ((uint64_t)(r >> 4) << colbits) | (uint32_t)col_idx[e];
+__global__ __launch_bounds__(kWinThreads) void k_wsb_keys(const int32_t* row_ptr, const int32_t* col_idx,
+                                                          int32_t n, int colbits, uint64_t* keys) {
+  const int w = blockIdx.x;
+  const int64_t e0 = row_ptr[w * 16], e1 = row_ptr[min(w * 16 + 16, n)];
+  const uint64_t hi = (uint64_t)w << colbits;
+  for (int64_t e = e0 + threadIdx.x; e < e1; e += kWinThreads) keys[e] = hi | (uint32_t)col_idx[e];
 }
 
 __global__ void k_wsb_flags(const uint64_t* keys, int64_t nnz, int32_t* flag) {
@@ -89,17 +84,65 @@ __device__ __forceinline__ int col_pos(const int32_t* wcols, int u, int col) {
   return lo;
 }
 
-__global__ void k_wsb_bits(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
-                           const int32_t* win_ptr, const int32_t* ucnt, const int32_t* blk_col,
-                           unsigned long long* bits) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz) return;
-  const int r = row_of_edge(row_ptr, n, e);
-  const int w = r >> 4;
-  const int p = col_pos(blk_col + (int64_t)win_ptr[w] * 8, ucnt[w], col_idx[e]);
-  const int blk = win_ptr[w] + p / 8;
-  const int bit = (r & 15) * 8 + (p % 8);
-  atomicOr(&bits[(int64_t)blk * 2 + (bit >> 6)], 1ull << (bit & 63));
+// The window's row starts, its sorted distinct columns (in LDS when the
+// window has at most kWinLdsBlocks blocks) and, for entry e of the window,
+// its row within the window and its column's position among the distinct
+// columns.
+struct WinStage {
+  int32_t rp[17];
+  int32_t cols[kWinLdsBlocks * 8];
+};
+
+__device__ __forceinline__ void stage_window(WinStage& ws, const int32_t* row_ptr, int32_t n, int w,
+                                             const int32_t* wcols, int u, bool inl, int& nr) {
+  nr = min(16, n - w * 16);
+  if ((int)threadIdx.x <= nr) ws.rp[threadIdx.x] = row_ptr[w * 16 + threadIdx.x];
+  if (inl)
+    for (int i = threadIdx.x; i < u; i += kWinThreads) ws.cols[i] = wcols[i];
+}
+
+__device__ __forceinline__ int row_in_window(const WinStage& ws, int nr, int e) {
+  int lo = 0, hi = nr - 1;  // largest i with rp[i] <= e
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ws.rp[mid] <= e) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Each entry sets its bit of the window's 16 x 8 block bitmaps: LDS atomics
+// on the window's words, stored once (device-scope atomics, about 27 G/s on
+// this part, were the cost of the per-entry version).  Windows with more
+// than kWinLdsBlocks blocks set their bits in memory directly.
+__global__ __launch_bounds__(kWinThreads) void k_wsb_bits(const int32_t* row_ptr, const int32_t* col_idx, int32_t n,
+                                                          const int32_t* win_ptr, const int32_t* ucnt,
+                                                          const int32_t* blk_col, unsigned long long* bits) {
+  __shared__ WinStage ws;
+  __shared__ unsigned long long lb[kWinLdsBlocks * 2];
+  const int w = blockIdx.x;
+  const int b0 = win_ptr[w], nb = win_ptr[w + 1] - b0, u = ucnt[w];
+  const int32_t* wcols = blk_col + (int64_t)b0 * 8;
+  const bool inl = nb <= kWinLdsBlocks;
+  int nr;
+  stage_window(ws, row_ptr, n, w, wcols, u, inl, nr);
+  if (inl)
+    for (int i = threadIdx.x; i < 2 * nb; i += kWinThreads) lb[i] = 0ull;
+  __syncthreads();
+  const int e0 = ws.rp[0], e1 = ws.rp[nr];
+  for (int e = e0 + threadIdx.x; e < e1; e += kWinThreads) {
+    const int i = row_in_window(ws, nr, e);
+    const int c = col_idx[e];
+    const int pos = inl ? col_pos(ws.cols, u, c) : col_pos(wcols, u, c);
+    const int bit = i * 8 + (pos & 7);
+    const int word = (pos >> 3) * 2 + (bit >> 6);
+    if (inl) atomicOr(&lb[word], 1ull << (bit & 63));
+    else atomicOr(&bits[(int64_t)b0 * 2 + word], 1ull << (bit & 63));
+  }
+  if (inl) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2 * nb; i += kWinThreads) bits[(int64_t)b0 * 2 + i] = lb[i];
+  }
 }
 
 __device__ __forceinline__ int window_of_block(const int32_t* win_ptr, int32_t nw, int blk) {
@@ -141,16 +184,26 @@ __global__ void k_wsb_tile_ptr(const int32_t* win_ptr, const int32_t* tscan, int
   tile_ptr[w] = tscan[win_ptr[w]];
 }
 
-__global__ void k_wsb_resid_flags(const int32_t* row_ptr, const int32_t* col_idx, int32_t n,
-                                  int64_t nnz, const int32_t* win_ptr, const int32_t* ucnt,
-                                  const int32_t* blk_col, const int32_t* dense, int32_t* rflag) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz) return;
-  const int r = row_of_edge(row_ptr, n, e);
-  const int w = r >> 4;
-  const int p = col_pos(blk_col + (int64_t)win_ptr[w] * 8, ucnt[w], col_idx[e]);
-  const int first = win_ptr[w] + ((p / 8) & ~1);  // first block of the edge's tile
-  rflag[e] = dense[first] ? 0 : 1;
+// rflag[e] = 1 for an entry outside the dense tiles (the residual CSR).
+__global__ __launch_bounds__(kWinThreads) void k_wsb_resid_flags(const int32_t* row_ptr, const int32_t* col_idx,
+                                                                 int32_t n, const int32_t* win_ptr,
+                                                                 const int32_t* ucnt, const int32_t* blk_col,
+                                                                 const int32_t* dense, int32_t* rflag) {
+  __shared__ WinStage ws;
+  const int w = blockIdx.x;
+  const int b0 = win_ptr[w], nb = win_ptr[w + 1] - b0, u = ucnt[w];
+  const int32_t* wcols = blk_col + (int64_t)b0 * 8;
+  const bool inl = nb <= kWinLdsBlocks;
+  int nr;
+  stage_window(ws, row_ptr, n, w, wcols, u, inl, nr);
+  __syncthreads();
+  const int e0 = ws.rp[0], e1 = ws.rp[nr];
+  for (int e = e0 + threadIdx.x; e < e1; e += kWinThreads) {
+    const int c = col_idx[e];
+    const int pos = inl ? col_pos(ws.cols, u, c) : col_pos(wcols, u, c);
+    const int first = b0 + ((pos >> 3) & ~1);  // first block of the entry's tile
+    rflag[e] = dense[first] ? 0 : 1;
+  }
 }
 
 __global__ void k_wsb_resid_fill(const int32_t* col_idx, int64_t nnz, const int32_t* rflag,
@@ -208,8 +261,8 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
   GNN_TRY(tt.get(&ucnt, (size_t)nw * 4));
   GNN_TRY(tt.get(&nbk, (size_t)nw * 4));
 
-  hipLaunchKernelGGL(k_wsb_keys, dim3(nblk(nnz)), dim3(256), 0, s, p->row_ptr, p->col_idx, n, nnz,
-                     colbits, keys);
+  hipLaunchKernelGGL(k_wsb_keys, dim3((unsigned)nw), dim3(kWinThreads), 0, s, p->row_ptr, p->col_idx, n, colbits,
+                     keys);
   GNN_LAUNCH_CHECK("wsb keys");
   GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, colbits + winbits, s));
   hipLaunchKernelGGL(k_wsb_flags, dim3(nblk(nnz)), dim3(256), 0, s, keys, nnz, flag);
@@ -230,7 +283,7 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
   hipLaunchKernelGGL(k_wsb_fill_cols, dim3(nblk(nnz)), dim3(256), 0, s, keys, flag, uidx, nnz,
                      p->row_ptr, n, colbits, L.win_ptr, L.blk_col);
   GNN_LAUNCH_CHECK("wsb cols");
-  hipLaunchKernelGGL(k_wsb_bits, dim3(nblk(nnz)), dim3(256), 0, s, p->row_ptr, p->col_idx, n, nnz,
+  hipLaunchKernelGGL(k_wsb_bits, dim3((unsigned)nw), dim3(kWinThreads), 0, s, p->row_ptr, p->col_idx, n,
                      L.win_ptr, ucnt, L.blk_col, (unsigned long long*)L.blk_bits);
   GNN_LAUNCH_CHECK("wsb bits");
 
@@ -255,8 +308,8 @@ int plan_build_wsb(gnn_plan* p, hipStream_t s) {
   GNN_LAUNCH_CHECK("wsb tile ptr");
 
   // residual CSR
-  hipLaunchKernelGGL(k_wsb_resid_flags, dim3(nblk(nnz)), dim3(256), 0, s, p->row_ptr, p->col_idx, n,
-                     nnz, L.win_ptr, ucnt, L.blk_col, dense, flag);
+  hipLaunchKernelGGL(k_wsb_resid_flags, dim3((unsigned)nw), dim3(kWinThreads), 0, s, p->row_ptr, p->col_idx, n,
+                     L.win_ptr, ucnt, L.blk_col, dense, flag);
   GNN_LAUNCH_CHECK("wsb residual flags");
   GNN_TRY(exclusive_scan_i32(flag, uidx, nnz, s));
   int32_t nr32 = 0;

@@ -41,7 +41,17 @@ def export_layout(csr, **opts):
     return plan, host(wp), host(bc), host(bb).view(np.uint64)
 
 
-@pytest.mark.parametrize("graph", ["golden", "cluster", "rmat", "partial"])
+def wide_window_graph(seed=0x5EED0303, n=20000, per_row=600):
+    """Rows 0-15 take 600 random sources each (one window with about 9,000
+    distinct columns: more than the 4096 a window keeps in LDS while its
+    bitmaps are built); the other rows take 3 each."""
+    u = gen.uniform_u64(seed, 16 * per_row + 3 * (n - 16)) % np.uint64(n)
+    src = u.astype(np.int64).tolist()
+    dst = [r for r in range(16) for _ in range(per_row)] + [r for r in range(16, n) for _ in range(3)]
+    return gen.from_edges(n, src, dst)
+
+
+@pytest.mark.parametrize("graph", ["golden", "cluster", "rmat", "partial", "wide"])
 def test_wsb_layout_matches_oracle(graph):
     if graph == "golden":
         lines = [l.split("#")[0].split() for l in open(os.path.join(GOLDEN, "wsb_hand.txt"))]
@@ -57,8 +67,11 @@ def test_wsb_layout_matches_oracle(graph):
         rp, ci = gen.cluster(0x5EED0300, 64 * 40, 64, 0.5, 0.01)
     elif graph == "rmat":
         rp, ci = gen.rmat(0x5EED0301, 30000, 300000, self_loops=True)
-    else:
+    elif graph == "partial":
         rp, ci = gen.rmat(0x5EED0302, 1000 + 7, 9000)     # last window has 15 rows
+    else:
+        rp, ci = wide_window_graph()
+        assert np.unique(ci[: rp[16]]).size > 4096
     csr = dev_csr(rp, ci)
     _, wp, bc, bb = export_layout(csr)
     owp, obc, obb = oracle.wsb_build(rp, ci)
@@ -106,6 +119,19 @@ def test_gt_block16_rmat_partial_window_and_empty_rows():
         check(out, lse, ro, rl, va)
         empty = np.diff(rp) == 0
         assert np.all(out[empty] == 0) and np.all(np.isneginf(lse[empty]))
+
+
+def test_gt_block16_wide_window():
+    # a window whose distinct columns do not fit the LDS of the WSB build:
+    # its bitmaps and residual flags take the path through memory
+    rp, ci = wide_window_graph()
+    n = rp.size - 1
+    H, D = 2, 32
+    q, k, v = (gen.gauss_bf16(0x2100 + i, (n, H, D)) for i in range(3))
+    ro, rl, va = oracle.gt(rp, ci, q, k, v)
+    for tau in (1, 2, 10**6):
+        out, lse, st = run_b16(rp, ci, q, k, v, tau)
+        check(out, lse, ro, rl, va)
 
 
 def test_gt_block16_constant_values_and_csr_agreement():
