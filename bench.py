@@ -44,7 +44,7 @@ SOURCES = {
     "gt_csr": _COMMON + ("attention.hip", "att_common.h", "sort.hip"),
     "gt_block16": _COMMON + ("gt_block16.hip", "wsb.hip", "sort.hip"),
     "copy": ("gnn_internal.h", "util.hip"),
-    "plan_rmat1m": _COMMON,
+    "plan_rmat1m": _COMMON + ("degrees.hip",),
     "wsb_cluster512k": _COMMON + ("wsb.hip", "sort.hip"),
     "reorder_rmat16m": _COMMON + ("reorder.hip", "sort.hip", "util.hip"),
     "spmm_bwd_rmat16m": _COMMON + ("aggregate.hip", "transpose.hip", "sort.hip"),
@@ -216,7 +216,7 @@ def wl_reduce_f128(args):
     comp = 4 * (n + 1) + 4 * m + 7 * n * row_b
     return {"ops": ops, "dominant": "multi", "kernel": "k_aggregate<float, 32, 4, 3, true>",
             "config": cfg, "dtype": "f32", "cpu": cpu_sample, "separate": separate, "compulsory": comp,
-            "cpu_1thread": True,
+            "cpu_1thread": True, "gathers": (m, 4),
             "keep": (w, X, csr, plan, Y, A, outs)}
 
 
@@ -1021,6 +1021,15 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
     }
+    if w.get("gathers"):
+        # the same step as rates that compare with a one-output aggregation:
+        # `value` counts every (output, edge) pair of the fused pass
+        m_edges, n_out = w["gathers"]
+        rates = {"aggregation_edges_per_s": out["value"], "outputs_per_gather": n_out,
+                 "gathered_edges_per_s": m_edges / (step_ms * 1e-3)}
+        if separate_ms and "sum" in separate_ms:
+            rates["sum_alone_edges_per_s"] = m_edges / (separate_ms["sum"] * 1e-3)
+        out["rates"] = rates
     if traffic:
         # calibrated FETCH_SIZE + WRITE_SIZE bytes of the dominant launch over its time
         out["hbm_counter"] = {"bytes": traffic, "gbps": traffic / (dom_ms * 1e-3) / 1e9,

@@ -49,10 +49,17 @@ constexpr int ldo() { return D + 4; }  // padded LDS row (floats)
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// bf16 rounding to nearest even on v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Sum over the four lanes of a row (l, l ^ 16, l ^ 32, l ^ 48) on the VALU
+// lane-swap instructions: v_permlane32_swap(x, x) leaves x[l] and x[l ^ 32]
+// in the pair at every lane, v_permlane16_swap x[l] and x[l ^ 16].
+__device__ __forceinline__ float row4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -305,8 +312,7 @@ __device__ __forceinline__ void dst_walk(const B16BwdParams& p, const Tiles& T, 
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) qb[kc] = gb[kc] = s16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
-    dl += __shfl_xor(dl, 16, 64);
-    dl += __shfl_xor(dl, 32, 64);
+    dl = row4_sum(dl);
     if (row_ok && g == 0) p.delta[(int64_t)row * p.H + h] = dl;
     {
       float res[KC][8];
@@ -327,10 +333,8 @@ __device__ __forceinline__ void dst_walk(const B16BwdParams& p, const Tiles& T, 
           s = dot8(qb[kc], kv[kc], s);
           dpv = dot8(gb[kc], vv[kc], dpv);
         }
-        s += __shfl_xor(s, 16, 64);
-        s += __shfl_xor(s, 32, 64);
-        dpv += __shfl_xor(dpv, 16, 64);
-        dpv += __shfl_xor(dpv, 32, 64);
+        s = row4_sum(s);
+        dpv = row4_sum(dpv);
         const float ds = ex2(s * sc2 - L2) * (dpv - dl) * p.scale;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
@@ -535,10 +539,8 @@ __device__ __forceinline__ void src_walk(const B16BwdParams& p, const Tiles& T, 
         s = dot8(qv[kc], kb[kc], s);
         dpv = dot8(gv[kc], vb[kc], dpv);
       }
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      dpv += __shfl_xor(dpv, 16, 64);
-      dpv += __shfl_xor(dpv, 32, 64);
+      s = row4_sum(s);
+      dpv = row4_sum(dpv);
       const float a = ex2(s * sc2 - L2);
       const float ds = a * (dpv - dl) * p.scale;
 #pragma unroll
