@@ -145,6 +145,28 @@ __device__ __forceinline__ void load_rawb_buf(__amdgpu_buffer_rsrc_t rs, uint32_
   }
 }
 
+// The same through one descriptor over a whole array (below 2 GB): the
+// row's byte offset is a scalar operand (soffset), so a row costs one scalar
+// multiply instead of a descriptor of its own.
+template <int VB>
+__device__ __forceinline__ void load_rawb_buf_so(__amdgpu_buffer_rsrc_t rs, uint32_t byte_off, uint32_t row_off,
+                                                 RawB<VB>& r) {
+  if constexpr (VB == 2) {
+    r.u[0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, byte_off, row_off, 0);
+  } else if constexpr (VB == 4) {
+    r.u[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, byte_off, row_off, 0);
+  } else if constexpr (VB == 8) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, byte_off, row_off, 0);
+    r.u[0] = v[0]; r.u[1] = v[1];
+  } else {
+#pragma unroll
+    for (int k = 0; k < VB / 16; ++k) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off + 16 * k, row_off, 0);
+      r.u[4 * k] = v[0]; r.u[4 * k + 1] = v[1]; r.u[4 * k + 2] = v[2]; r.u[4 * k + 3] = v[3];
+    }
+  }
+}
+
 // element k of a raw slice as float
 template <typename T, int VB>
 __device__ __forceinline__ float elemb(const RawB<VB>& r, int k) {

@@ -80,6 +80,7 @@ struct AttParams {
   int32_t n_light_blocks;
   float slope;        // GATv2 LeakyReLU slope
   float qscale;       // GT: scale * log2(e)
+  int32_t kv_bytes;   // bytes of K (and of V) when below 2^31, else 0
 };
 
 // Online-softmax state of one slot lane: running max m (log2 units), running
@@ -140,6 +141,10 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
   const int64_t ld = p.row_elems;
   const int row_bytes = p.row_elems * (int)sizeof(T);
   const uint32_t loff_b = loff * (uint32_t)sizeof(T);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(K), (short)0, p.kv_bytes,
+                                                                      kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(V), (short)0, p.kv_bytes,
+                                                                      kBufferWord3);
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
@@ -158,9 +163,16 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
       for (int u = 0; u < UU; ++u) {
         const int cu = (u0 + u < nb) ? c[u] : c[0];
         if constexpr (LPE == 64) {
-          // the wave's row: base in scalar registers, the lane's slice an offset
-          load_rawb_buf<VB>(row_rsrc(K + (int64_t)cu * ld, row_bytes), loff_b, x[u]);
-          if constexpr (KIND == K_GT) load_rawb_buf<VB>(row_rsrc(V + (int64_t)cu * ld, row_bytes), loff_b, y[u]);
+          // the wave's row: its byte offset in a scalar register (one
+          // descriptor over the array), or its base in one of its own
+          if (p.kv_bytes > 0) {
+            const uint32_t ro = (uint32_t)cu * (uint32_t)row_bytes;
+            load_rawb_buf_so<VB>(rk, loff_b, ro, x[u]);
+            if constexpr (KIND == K_GT) load_rawb_buf_so<VB>(rv, loff_b, ro, y[u]);
+          } else {
+            load_rawb_buf<VB>(row_rsrc(K + (int64_t)cu * ld, row_bytes), loff_b, x[u]);
+            if constexpr (KIND == K_GT) load_rawb_buf<VB>(row_rsrc(V + (int64_t)cu * ld, row_bytes), loff_b, y[u]);
+          }
         } else {
           load_rawb<T, VB>(K + (int64_t)cu * ld + loff, x[u]);
           if constexpr (KIND == K_GT) load_rawb<T, VB>(V + (int64_t)cu * ld + loff, y[u]);
@@ -532,6 +544,8 @@ int setup(gnn_plan* pl, AttParams& p, int kind, gnn_dtype xt, int32_t H, int32_t
   p.H = H;
   p.D = D;
   p.row_elems = H * D;
+  const int64_t kvb = (int64_t)pl->n_cols * H * D * esz;
+  p.kv_bytes = kvb < ((int64_t)1 << 31) ? (int32_t)kvb : 0;
   p.dv = (int32_t)((int64_t)D * esz / mp->vb);
   // One slot per row up to kAttLightMax edges, never below the plan's own
   // light threshold (its longer rows are the plan's items) and never above

@@ -70,6 +70,9 @@ struct BwdParams {
   int32_t H, D, row_elems, row_lanes;
   float scale;       // GT score scale
   float slope;       // GATv2 LeakyReLU slope
+  // bytes of the gathered arrays when each is below 2^31 (else 0): k / v
+  // (rows = sources), q (rows = destinations), dO (fp32, destinations)
+  int32_t kv_bytes, q_bytes, do_bytes;
 };
 
 template <int VEL>
@@ -110,6 +113,10 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;
   const int64_t ld = p.row_elems;
   const float sc2 = p.scale * kLog2e;
+  const __amdgpu_buffer_rsrc_t rk = row_rsrc(p.k, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, p.kv_bytes);
+  const __amdgpu_buffer_rsrc_t rq = row_rsrc(p.q, p.q_bytes);
+  const __amdgpu_buffer_rsrc_t rd = row_rsrc(p.dout, p.do_bytes);
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
@@ -122,6 +129,38 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
       Raw<NV> x[UB], y[UB];
       float g[UB][VEL];
       float Lc[UB], Dc[UB];
+      if constexpr (LPE == 64) {
+        if (p.kv_bytes > 0 && p.q_bytes > 0 && p.do_bytes > 0) {
+          // one slot per wave: the entry's row offset is a scalar operand of
+          // buffer loads over the whole array, and an entry past the slot's
+          // end or a lane without data reads at an offset beyond the array,
+          // which returns zeros: no per-lane addresses, no branches
+#pragma unroll
+          for (int u = 0; u < UB; ++u) {
+            const bool ok = u0 + u < nb && d_ok;
+            const uint32_t so = (uint32_t)c[u] * (uint32_t)(ld * (int64_t)sizeof(T));
+            const uint32_t vo = ok ? (uint32_t)(sl * VEL * (int)sizeof(T)) : 0x80000000u;
+            if constexpr (KIND == B_GT_DST) {
+              load_rawb_buf_so<16 * NV>(rk, vo, so, x[u]);
+              load_rawb_buf_so<16 * NV>(rv, vo, so, y[u]);
+            } else if constexpr (KIND == B_GAT_DST) {
+              load_rawb_buf_so<16 * NV>(rk, vo, so, x[u]);
+            } else {
+              load_rawb_buf_so<16 * NV>(rq, vo, so, x[u]);
+              RawB<4 * VEL> gr;
+              load_rawb_buf_so<4 * VEL>(rd, ok ? (uint32_t)(sl * VEL * 4) : 0x80000000u,
+                                        (uint32_t)c[u] * (uint32_t)(ld * 4), gr);
+#pragma unroll
+              for (int k = 0; k < VEL; ++k) g[u][k] = __uint_as_float(gr.u[k]);
+              const float lc = p.lse[(int64_t)c[u] * p.H + head];
+              const float dc = p.delta[(int64_t)c[u] * p.H + head];
+              Lc[u] = ok ? lc * kLog2e : 0.0f;
+              Dc[u] = ok ? dc : 0.0f;
+            }
+          }
+          goto gathered;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const bool ok = u0 + u < nb && d_ok;
@@ -156,6 +195,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           }
         }
       }
+    gathered:
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const bool valid = u0 + u < nb;
@@ -544,6 +584,17 @@ int run(gnn_plan* pl, const BwdParams& p, gnn_dtype xt, int lpe, int nv, int lph
                         : by_shape<float, KIND>(pl, p, lpe, nv, lph, s);
 }
 
+// Sizes of the gathered arrays for the buffer loads of one-slot walks (0:
+// 2 GB or more, where those walks use per-lane addresses).
+void set_gather_bytes(const gnn_plan* pl, gnn_dtype xt, BwdParams& p) {
+  const int64_t esz = xt == GNN_BF16 ? 2 : 4, lim = (int64_t)1 << 31;
+  const int64_t kv = (int64_t)pl->n_cols * p.row_elems * esz, q = (int64_t)pl->n_rows * p.row_elems * esz;
+  const int64_t d = (int64_t)pl->n_rows * p.row_elems * 4;
+  p.kv_bytes = kv < lim ? (int32_t)kv : 0;
+  p.q_bytes = q < lim ? (int32_t)q : 0;
+  p.do_bytes = d < lim ? (int32_t)d : 0;
+}
+
 }  // namespace
 
 int launch_gt_backward(gnn_plan* pl, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
@@ -563,6 +614,7 @@ int launch_gt_backward(gnn_plan* pl, const void* q, const void* k, const void* v
   p.D = D;
   p.row_elems = H * D;
   p.row_lanes = lanes;
+  set_gather_bytes(pl, xt, p);
   p.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
   // Delta lives in the plan of the destinations, sized [n_rows, H]
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
@@ -592,6 +644,7 @@ int launch_gatv2_backward(gnn_plan* pl, const void* xl, const void* xr, gnn_dtyp
   p.D = D;
   p.row_elems = H * D;
   p.row_lanes = lanes;
+  set_gather_bytes(pl, xt, p);
   p.slope = slope;
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
   p.delta = pl->delta;
