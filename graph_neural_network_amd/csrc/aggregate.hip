@@ -47,6 +47,7 @@ struct AggParams {
   const int32_t* deg_out;  // for RIGHT / BOTH
   const void* X;
   int64_t ldx;
+  uint32_t ldx_b;          // ldx in bytes (below 2^32): a gathered row's offset is one 32 x 32 -> 64 multiply-add
   float* Y;
   int64_t ldy;
   int32_t* arg;            // nullable, ld = F
@@ -83,6 +84,14 @@ template <> struct RawOf<float, 4> { using type = float4; };
 template <> struct RawOf<uint16_t, 8> { using type = uint4; };
 template <> struct RawOf<float, 1> { using type = float; };
 template <> struct RawOf<uint16_t, 1> { using type = uint16_t; };
+
+// Row c of X at this lane's slice: c (a column index, >= 0) times the row
+// stride in bytes, as one unsigned 32 x 32 -> 64 multiply-add
+// (v_mad_u64_u32) instead of a signed 64-bit product.
+template <typename T>
+__device__ __forceinline__ const T* row_at(const T* base, int c, uint32_t ld_bytes) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + (uint64_t)(uint32_t)c * ld_bytes);
+}
 
 template <typename T, int VE>
 __device__ __forceinline__ typename RawOf<T, VE>::type load_raw(const T* p) {
@@ -235,7 +244,7 @@ __device__ __forceinline__ void scan_edges(const AggParams& p, int eb, int ee, i
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(Xf + (int64_t)c[u] * p.ldx);
+        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(row_at(Xf, c[u], p.ldx_b));
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (u0 + u < nb && f_ok) {
@@ -556,7 +565,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(Xf + (int64_t)c[u] * p.ldx);
+        if (u0 + u < nb && f_ok) x[u] = load_raw<T, VE>(row_at(Xf, c[u], p.ldx_b));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (u0 + u < nb) {
@@ -743,6 +752,8 @@ int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64
 
   const int esz = (xt == GNN_BF16) ? 2 : 4;
   const int64_t rowb = (int64_t)F * esz;
+  if (ldx * esz > (int64_t)UINT32_MAX) return fail(GNN_ERR_SIZE_OVERFLOW, "X row stride of 4 GB or more");
+  p.ldx_b = (uint32_t)(ldx * esz);
   const bool vec_ok = (rowb % 16 == 0) && ((ldx * esz) % 16 == 0) && ((uintptr_t)X % 16 == 0) &&
                       ((uintptr_t)Y % 16 == 0) && (ldy % 4 == 0) &&
                       (arg == nullptr || ((uintptr_t)arg % 16 == 0 && F % 4 == 0));
@@ -799,6 +810,8 @@ int launch_reduce_multi(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, in
   }
   const int esz = (xt == GNN_BF16) ? 2 : 4;
   const int64_t rowb = (int64_t)F * esz;
+  if (ldx * esz > (int64_t)UINT32_MAX) return fail(GNN_ERR_SIZE_OVERFLOW, "X row stride of 4 GB or more");
+  p.ldx_b = (uint32_t)(ldx * esz);
   const uintptr_t outs = (uintptr_t)Ysum | (uintptr_t)Ymean | (uintptr_t)Ymax | (uintptr_t)Ymin |
                          (uintptr_t)argmax | (uintptr_t)argmin;
   const bool vec_ok = (rowb % 16 == 0) && ((ldx * esz) % 16 == 0) && ((uintptr_t)X % 16 == 0) &&
