@@ -167,6 +167,14 @@ __device__ __forceinline__ void load_rawb_buf_so(__amdgpu_buffer_rsrc_t rs, uint
   }
 }
 
+// Row c (>= 0) of an array at byte stride ld_bytes (below 4 GB) from base:
+// one unsigned 32 x 32 -> 64 multiply-add (v_mad_u64_u32) per address
+// instead of a signed 64-bit product.
+template <typename T>
+__device__ __forceinline__ const T* row_at(const T* base, int c, uint32_t ld_bytes) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + (uint64_t)(uint32_t)c * ld_bytes);
+}
+
 // element k of a raw slice as float
 template <typename T, int VB>
 __device__ __forceinline__ float elemb(const RawB<VB>& r, int k) {

@@ -174,8 +174,8 @@ __device__ __forceinline__ void scan_edges(const AttParams& p, int eb, int ee, i
             if constexpr (KIND == K_GT) load_rawb_buf<VB>(row_rsrc(V + (int64_t)cu * ld, row_bytes), loff_b, y[u]);
           }
         } else {
-          load_rawb<T, VB>(K + (int64_t)cu * ld + loff, x[u]);
-          if constexpr (KIND == K_GT) load_rawb<T, VB>(V + (int64_t)cu * ld + loff, y[u]);
+          load_rawb<T, VB>(row_at(K + loff, cu, (uint32_t)row_bytes), x[u]);
+          if constexpr (KIND == K_GT) load_rawb<T, VB>(row_at(V + loff, cu, (uint32_t)row_bytes), y[u]);
         }
       }
       float s[UU];

@@ -112,6 +112,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
                                      int head, Row<T, NV, KIND>& R) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;
   const int64_t ld = p.row_elems;
+  const uint32_t rb = (uint32_t)(p.row_elems * (int)sizeof(T)), rb4 = (uint32_t)(p.row_elems * 4);
   const float sc2 = p.scale * kLog2e;
   const __amdgpu_buffer_rsrc_t rk = row_rsrc(p.k, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, p.kv_bytes);
@@ -164,25 +165,25 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const bool ok = u0 + u < nb && d_ok;
-        const int64_t o = (int64_t)c[u] * ld + sl * VEL;
+        const int o = sl * VEL;  // the lane's slice; rows by row_at
         if constexpr (KIND == B_GT_DST) {
           if (ok) {
-            load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + o, x[u]);
-            load_raw<T, NV>(reinterpret_cast<const T*>(p.v) + o, y[u]);
+            load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.k) + o, c[u], rb), x[u]);
+            load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.v) + o, c[u], rb), y[u]);
           } else {
 #pragma unroll
             for (int t = 0; t < 4 * NV; ++t) x[u].u[t] = y[u].u[t] = 0u;
           }
         } else if constexpr (KIND == B_GAT_DST) {
-          if (ok) load_raw<T, NV>(reinterpret_cast<const T*>(p.k) + o, x[u]);
+          if (ok) load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.k) + o, c[u], rb), x[u]);
           else {
 #pragma unroll
             for (int t = 0; t < 4 * NV; ++t) x[u].u[t] = 0u;
           }
         } else {  // source walks: the destination's q / l, dO, L and Delta
           if (ok) {
-            load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + o, x[u]);
-            load_f32<VEL>(p.dout + o, g[u]);
+            load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.q) + o, c[u], rb), x[u]);
+            load_f32<VEL>(row_at(p.dout + o, c[u], rb4), g[u]);
             Lc[u] = p.lse[(int64_t)c[u] * p.H + head] * kLog2e;
             Dc[u] = p.delta[(int64_t)c[u] * p.H + head];
           } else {

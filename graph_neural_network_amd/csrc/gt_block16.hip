@@ -198,8 +198,10 @@ void k_gt_block16(B16Params p) {
 
     auto load_kv = [&](auto st, int t, s16x8 (&ka)[KC], s16x8 (&va)[KC]) {
       const int col = tile_col(st, t);
-      const uint16_t* krow = p.k + (int64_t)col * ldr + h * D;
-      const uint16_t* vrow = p.v + (int64_t)col * ldr + h * D;
+      // row col at a byte stride below 4 GB: one unsigned 32 x 32 -> 64 multiply-add
+      const uint64_t ro = (uint64_t)(uint32_t)col * (uint32_t)(ldr * 2);
+      const uint16_t* krow = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.k) + ro) + h * D;
+      const uint16_t* vrow = reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(p.v) + ro) + h * D;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         ka[kc] = *reinterpret_cast<const s16x8*>(krow + kc * 32 + 8 * g);

@@ -135,7 +135,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) =
       const int r = chunk / CPR, cc = chunk % CPR;
       const int col = s_tcol[k][r];
       const int f = f0 + cc * EPC;
-      pre[q] = (f < p.F) ? *reinterpret_cast<const uint4*>(X + (int64_t)col * p.ldx + f) : uint4{0u, 0u, 0u, 0u};
+      // row col at a byte stride below 4 GB: one unsigned 32 x 32 -> 64 multiply-add
+      const T* xr = reinterpret_cast<const T*>(reinterpret_cast<const char*>(X) +
+                                               (uint64_t)(uint32_t)col * (uint32_t)(p.ldx * (int64_t)sizeof(T)));
+      pre[q] = (f < p.F) ? *reinterpret_cast<const uint4*>(xr + f) : uint4{0u, 0u, 0u, 0u};
     }
   };
   auto store_tile = [&](int buf) {
@@ -289,6 +292,7 @@ int launch_spmm_block16(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, in
   p.res_col = pl->wsb.res_col;
   p.X = X;
   p.ldx = ldx;
+  if (ldx * (xt == GNN_BF16 ? 2 : 4) > (int64_t)UINT32_MAX) return fail(GNN_ERR_SIZE_OVERFLOW, "X row stride of 4 GB or more");
   p.Y = Y;
   p.ldy = ldy;
   p.F = F;
