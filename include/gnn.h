@@ -79,7 +79,9 @@ typedef enum {
   GNN_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head dim for a mode) */
   GNN_ERR_OUT_OF_MEMORY = 3, /* device allocation failed */
   GNN_ERR_DEVICE = 4,        /* a HIP call failed (launch error, earlier fault) */
-  GNN_ERR_SIZE_OVERFLOW = 5, /* nnz >= 2^31, or a size product overflows */
+  GNN_ERR_SIZE_OVERFLOW = 5, /* nnz >= 2^31, a size product overflows, or a
+                                gathered row stride (ldx x element size) of
+                                4 GB or more */
   GNN_ERR_PLAN_MISMATCH = 6  /* plan was built for another CSR */
 } gnn_status;
 
