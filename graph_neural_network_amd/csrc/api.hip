@@ -519,8 +519,9 @@ int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_d
       ((!xr || !dxr) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 1024)
-    return fail(GNN_ERR_UNSUPPORTED, "GATv2 needs D*sizeof % 16 == 0 and H*D*sizeof <= 1024 bytes");
+  if ((int64_t)H * D >= ((int64_t)1 << 28)) return fail(GNN_ERR_SIZE_OVERFLOW, "H * D too large");
+  if ((D * esz) % 16 != 0 || D * esz > 1024)
+    return fail(GNN_ERR_UNSUPPORTED, "GATv2 backward needs D * element size a multiple of 16 bytes, at most 1 KB");
   if (((uintptr_t)xl | (uintptr_t)xr | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dxl | (uintptr_t)dxr) % 16)
     return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
@@ -540,8 +541,9 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
   if (((!q || !out || !lse || !dout || !dq) && csr->n_rows > 0) || ((!k || !v || !dk || !dv) && csr->n_cols > 0))
     return fail(GNN_ERR_INVALID_VALUE, "a required tensor is NULL");
   const int64_t esz = xtype == GNN_BF16 ? 2 : 4;
-  if ((D * esz) % 16 != 0 || (int64_t)H * D * esz > 2048)
-    return fail(GNN_ERR_UNSUPPORTED, "GT needs D*sizeof % 16 == 0 and H*D*sizeof <= 2048 bytes");
+  if ((int64_t)H * D >= ((int64_t)1 << 28)) return fail(GNN_ERR_SIZE_OVERFLOW, "H * D too large");
+  if ((D * esz) % 16 != 0 || D * esz > 1024)
+    return fail(GNN_ERR_UNSUPPORTED, "GT backward needs D * element size a multiple of 16 bytes, at most 1 KB");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
        (uintptr_t)dk | (uintptr_t)dv) % 16)
     return fail(GNN_ERR_UNSUPPORTED, "row tensors must be 16-byte aligned");

@@ -67,7 +67,10 @@ struct BwdParams {
   float* g1;         // GT src: dv
   float* dapart;     // GATv2 dst: [gridDim.x, H * D] per-workgroup shares of da
   float* part;       // split rows: [n_items, 2, H * D] chunk partials
-  int32_t H, D, row_elems, row_lanes;
+  int32_t H, D, row_elems;
+  // lane mapping (as in the forward): a slot covers the heads of one group
+  // (blockIdx.y), LPH lanes per head of which lph_data hold data
+  int32_t hpg, lph_data;
   float scale;       // GT score scale
   float slope;       // GATv2 LeakyReLU slope
   // bytes of the gathered arrays when each is below 2^31 (else 0): k / v
@@ -109,7 +112,7 @@ struct Row {
 // Work on entries [eb, ee) of walk row `row` for one slot (LPE lanes).
 template <typename T, int LPE, int NV, int KIND, int LPH>
 __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl, int slot_base, bool d_ok,
-                                     int head, Row<T, NV, KIND>& R) {
+                                     int head, int loff, Row<T, NV, KIND>& R) {
   constexpr int VEL = (16 / (int)sizeof(T)) * NV;
   const int64_t ld = p.row_elems;
   const uint32_t rb = (uint32_t)(p.row_elems * (int)sizeof(T)), rb4 = (uint32_t)(p.row_elems * 4);
@@ -140,7 +143,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           for (int u = 0; u < UB; ++u) {
             const bool ok = u0 + u < nb && d_ok;
             const uint32_t so = (uint32_t)c[u] * (uint32_t)(ld * (int64_t)sizeof(T));
-            const uint32_t vo = ok ? (uint32_t)(sl * VEL * (int)sizeof(T)) : 0x80000000u;
+            const uint32_t vo = ok ? (uint32_t)(loff * (int)sizeof(T)) : 0x80000000u;
             if constexpr (KIND == B_GT_DST) {
               load_rawb_buf_so<16 * NV>(rk, vo, so, x[u]);
               load_rawb_buf_so<16 * NV>(rv, vo, so, y[u]);
@@ -149,7 +152,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
             } else {
               load_rawb_buf_so<16 * NV>(rq, vo, so, x[u]);
               RawB<4 * VEL> gr;
-              load_rawb_buf_so<4 * VEL>(rd, ok ? (uint32_t)(sl * VEL * 4) : 0x80000000u,
+              load_rawb_buf_so<4 * VEL>(rd, ok ? (uint32_t)(loff * 4) : 0x80000000u,
                                         (uint32_t)c[u] * (uint32_t)(ld * 4), gr);
 #pragma unroll
               for (int k = 0; k < VEL; ++k) g[u][k] = __uint_as_float(gr.u[k]);
@@ -165,7 +168,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const bool ok = u0 + u < nb && d_ok;
-        const int o = sl * VEL;  // the lane's slice; rows by row_at
+        const int o = loff;  // the lane's slice; rows by row_at
         if constexpr (KIND == B_GT_DST) {
           if (ok) {
             load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.k) + o, c[u], rb), x[u]);
@@ -291,8 +294,11 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sw = lane / LPE, sl = lane % LPE;
   const int slot_base = sw * LPE;
-  const bool d_ok = sl < p.row_lanes;
-  const int head = d_ok ? sl / LPH : 0;
+  const int hin = sl / LPH, hj = sl % LPH;
+  const int head_g = (int)blockIdx.y * p.hpg + hin;
+  const bool d_ok = hin < p.hpg && head_g < p.H && hj < p.lph_data;
+  const int head = d_ok ? head_g : 0;
+  const int loff = d_ok ? head * p.D + hj * VEL : 0;  // the lane's slice of a row
 
   const int n_item_pad = (p.n_item_blocks + 7) & ~7;
   const bool is_item = (int)blockIdx.x < n_item_pad;
@@ -329,7 +335,7 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
   for (int k = 0; k < VEL; ++k) R.acc0[k] = R.acc1[k] = R.av[k] = R.an[k] = R.f0[k] = R.f1[k] = 0.0f;
 #pragma unroll
   for (int t = 0; t < 4 * NV; ++t) R.own.u[t] = 0u;
-  const int64_t ro = row * (int64_t)p.row_elems + sl * VEL;
+  const int64_t ro = row * (int64_t)p.row_elems + loff;
   if (active && d_ok) {
     if constexpr (DST) {
       float o[VEL];
@@ -359,17 +365,17 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     if constexpr (KIND == B_GAT_DST || KIND == B_GAT_SRC) {
 #pragma unroll
       for (int k = 0; k < VEL; ++k) {
-        const float a = p.att[sl * VEL + k];
+        const float a = p.att[loff + k];
         R.av[k] = a * (0.5f + 0.5f * p.slope);
         R.an[k] = a * (0.5f - 0.5f * p.slope);
       }
     }
   }
   if constexpr (DST) R.delta = head_sum<LPH>(R.delta);
-  if (DST && active && d_ok && (sl % LPH) == 0 && (!is_item || m_idx < 0 || p.items[item].y == p.row_ptr[row]))
+  if (DST && active && d_ok && hj == 0 && (!is_item || m_idx < 0 || p.items[item].y == p.row_ptr[row]))
     p.delta[row * p.H + head] = R.delta;  // once per row: the light slot, the single item, or chunk 0
 
-  if (active) scan<T, LPE, NV, KIND, LPH>(p, eb, ee, sl, slot_base, d_ok, head, R);
+  if (active) scan<T, LPE, NV, KIND, LPH>(p, eb, ee, sl, slot_base, d_ok, head, loff, R);
   if constexpr (KIND == B_GAT_DST || KIND == B_GAT_SRC) {
 #pragma unroll
     for (int k = 0; k < VEL; ++k) R.acc0[k] = fmaf(R.av[k], R.sde, R.acc0[k]);
@@ -394,7 +400,7 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
       for (int k = 0; k < VEL; ++k) {
         float t = s_acc[0][1][sl * VEL + k];
         for (int w = 1; w < NWAVE; ++w) t += s_acc[w][1][sl * VEL + k];
-        p.dapart[(int64_t)blockIdx.x * p.row_elems + sl * VEL + k] = t;
+        p.dapart[(int64_t)blockIdx.x * p.row_elems + loff + k] = t;
       }
     }
   }
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
     store_row_nt<VEL>(p.g0 + ro, R.acc0);
     if constexpr (KIND == B_GT_SRC) store_row_nt<VEL>(p.g1 + ro, R.acc1);
   } else {
-    const int64_t po = (int64_t)item * 2 * p.row_elems + sl * VEL;
+    const int64_t po = (int64_t)item * 2 * p.row_elems + loff;
     store_row<VEL>(p.part + po, R.acc0);
     if constexpr (KIND == B_GT_SRC) store_row<VEL>(p.part + po + p.row_elems, R.acc1);
   }
@@ -475,7 +481,7 @@ __global__ __launch_bounds__(256) void k_da_level(const float* in, int64_t rows,
 }
 
 template <typename T, int LPE, int NV, int KIND, int LPH>
-int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
+int launch_walk(gnn_plan* pl, BwdParams p, int groups, hipStream_t s) {
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.row_ptr = pl->row_ptr;
   p.col_idx = pl->col_idx;
@@ -490,7 +496,7 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   p.item_count = pl->item_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
-  if (gx > 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "attention backward grid too large");
+  if (gx > 0x7FFFFFFF || groups > 65535) return fail(GNN_ERR_SIZE_OVERFLOW, "attention backward grid too large");
   const size_t part_b = ((size_t)std::max<int64_t>(pl->n_items, 1) * 2 * p.row_elems * 4 + 255) & ~(size_t)255;
   const size_t da_b = KIND == B_GAT_DST ? (size_t)gx * p.row_elems * 4 : 0;
   void* ws = nullptr;
@@ -499,7 +505,7 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
   p.part = (float*)ws;
   p.dapart = KIND == B_GAT_DST ? (float*)((char*)ws + part_b) : nullptr;
   if (gx > 0) {
-    hipLaunchKernelGGL((k_att_bwd<T, LPE, NV, KIND, LPH>), dim3((unsigned)gx), dim3(WG), 0, s, p);
+    hipLaunchKernelGGL((k_att_bwd<T, LPE, NV, KIND, LPH>), dim3((unsigned)gx, (unsigned)groups), dim3(WG), 0, s, p);
     GNN_LAUNCH_CHECK("attention backward");
   }
   if (pl->n_multi > 0) {
@@ -530,59 +536,78 @@ int launch_walk(gnn_plan* pl, BwdParams p, hipStream_t s) {
 }
 
 template <typename T, int LPE, int NV, int KIND>
-int by_lph(gnn_plan* pl, const BwdParams& p, int lph, hipStream_t s) {
+int by_lph(gnn_plan* pl, const BwdParams& p, int lph, int groups, hipStream_t s) {
   switch (lph) {
-    case 1: return launch_walk<T, LPE, NV, KIND, 1>(pl, p, s);
-    case 2: return launch_walk<T, LPE, NV, KIND, 2>(pl, p, s);
-    case 4: return launch_walk<T, LPE, NV, KIND, 4>(pl, p, s);
-    case 8: return launch_walk<T, LPE, NV, KIND, 8>(pl, p, s);
+    case 1: return launch_walk<T, LPE, NV, KIND, 1>(pl, p, groups, s);
+    case 2: return launch_walk<T, LPE, NV, KIND, 2>(pl, p, groups, s);
+    case 4: return launch_walk<T, LPE, NV, KIND, 4>(pl, p, groups, s);
+    case 8: return launch_walk<T, LPE, NV, KIND, 8>(pl, p, groups, s);
     default: break;
   }
-  if constexpr (LPE >= 16) if (lph == 16) return launch_walk<T, LPE, NV, KIND, 16>(pl, p, s);
-  if constexpr (LPE >= 32) if (lph == 32) return launch_walk<T, LPE, NV, KIND, 32>(pl, p, s);
-  if constexpr (LPE >= 64) if (lph == 64) return launch_walk<T, LPE, NV, KIND, 64>(pl, p, s);
+  if constexpr (LPE >= 16) if (lph == 16) return launch_walk<T, LPE, NV, KIND, 16>(pl, p, groups, s);
+  if constexpr (LPE >= 32) if (lph == 32) return launch_walk<T, LPE, NV, KIND, 32>(pl, p, groups, s);
+  if constexpr (LPE >= 64) if (lph == 64) return launch_walk<T, LPE, NV, KIND, 64>(pl, p, groups, s);
   return fail(GNN_ERR_UNSUPPORTED, "lanes per head exceed the slot");
 }
 
 template <typename T, int KIND>
-int by_shape(gnn_plan* pl, const BwdParams& p, int lpe, int nv, int lph, hipStream_t s) {
+int by_shape(gnn_plan* pl, const BwdParams& p, int lpe, int nv, int lph, int groups, hipStream_t s) {
   if (nv == 2) {
     switch (lpe) {
-      case 8: return by_lph<T, 8, 2, KIND>(pl, p, lph, s);
-      case 16: return by_lph<T, 16, 2, KIND>(pl, p, lph, s);
-      case 32: return by_lph<T, 32, 2, KIND>(pl, p, lph, s);
-      default: return by_lph<T, 64, 2, KIND>(pl, p, lph, s);
+      case 8: return by_lph<T, 8, 2, KIND>(pl, p, lph, groups, s);
+      case 16: return by_lph<T, 16, 2, KIND>(pl, p, lph, groups, s);
+      case 32: return by_lph<T, 32, 2, KIND>(pl, p, lph, groups, s);
+      default: return by_lph<T, 64, 2, KIND>(pl, p, lph, groups, s);
     }
   }
   switch (lpe) {
-    case 8: return by_lph<T, 8, 1, KIND>(pl, p, lph, s);
-    case 16: return by_lph<T, 16, 1, KIND>(pl, p, lph, s);
-    case 32: return by_lph<T, 32, 1, KIND>(pl, p, lph, s);
-    default: return by_lph<T, 64, 1, KIND>(pl, p, lph, s);
+    case 8: return by_lph<T, 8, 1, KIND>(pl, p, lph, groups, s);
+    case 16: return by_lph<T, 16, 1, KIND>(pl, p, lph, groups, s);
+    case 32: return by_lph<T, 32, 1, KIND>(pl, p, lph, groups, s);
+    default: return by_lph<T, 64, 1, KIND>(pl, p, lph, groups, s);
   }
 }
 
-// Lane layout of a row of H * D elements (as in the forward kernels).
-int shape(gnn_dtype xt, int32_t H, int32_t D, int* lpe, int* nv, int* lph, int* lanes) {
-  const int esz = xt == GNN_BF16 ? 2 : 4;
-  const int rowb = H * D * esz;
-  *nv = rowb > 1024 ? 2 : 1;
-  const int vb = 16 * *nv;
-  if ((D * esz) % vb != 0) return fail(GNN_ERR_UNSUPPORTED, "head dimension does not fill whole lane vectors");
-  *lph = D * esz / vb;
-  if ((*lph & (*lph - 1)) != 0) return fail(GNN_ERR_UNSUPPORTED, "lanes per head must be a power of two");
-  *lanes = rowb / vb;
-  int l = 8;
-  while (l < *lanes) l <<= 1;
-  if (l > 64) return fail(GNN_ERR_UNSUPPORTED, "row too wide");
-  *lpe = l;
+// Lane layout of a row of H * D elements, as in the forward kernels: 16-byte
+// lane slices (32-byte ones for rows of 1-2 KB whose heads fill a power of
+// two of them), lanes per head rounded up to a power of two (the extra lanes
+// hold no data), the row in one slot when it fits 64 lanes, else cut into
+// groups of 64 / lph heads, one grid row per group.  Heads whose byte width
+// is not a multiple of 16 are not served.
+struct BwdShape {
+  int lpe, nv, lph, lph_data, hpg, groups;
+};
+
+int pow2_at_least(int x) {
+  int l = 1;
+  while (l < x) l <<= 1;
+  return l;
+}
+
+int shape(gnn_dtype xt, int32_t H, int32_t D, BwdShape* sh) {
+  const int64_t esz = xt == GNN_BF16 ? 2 : 4, hb = (int64_t)D * esz, rowb = (int64_t)H * hb;
+  if (hb % 16 != 0)
+    return fail(GNN_ERR_UNSUPPORTED, "attention backward: D * element size must be a multiple of 16 bytes");
+  sh->nv = (rowb > 1024 && rowb <= 2048 && hb % 32 == 0 && (((hb / 32) & (hb / 32 - 1)) == 0)) ? 2 : 1;
+  sh->lph_data = (int)(hb / (16 * sh->nv));
+  sh->lph = pow2_at_least(sh->lph_data);
+  if (sh->lph > 64) return fail(GNN_ERR_UNSUPPORTED, "attention backward: head wider than 64 lane slices");
+  if ((int64_t)H * sh->lph <= 64) {
+    sh->hpg = H;
+    sh->groups = 1;
+    sh->lpe = std::max(8, pow2_at_least(H * sh->lph));
+  } else {
+    sh->hpg = 64 / sh->lph;
+    sh->groups = (H + sh->hpg - 1) / sh->hpg;
+    sh->lpe = 64;
+  }
   return GNN_OK;
 }
 
 template <int KIND>
-int run(gnn_plan* pl, const BwdParams& p, gnn_dtype xt, int lpe, int nv, int lph, hipStream_t s) {
-  return xt == GNN_BF16 ? by_shape<uint16_t, KIND>(pl, p, lpe, nv, lph, s)
-                        : by_shape<float, KIND>(pl, p, lpe, nv, lph, s);
+int run(gnn_plan* pl, const BwdParams& p, gnn_dtype xt, const BwdShape& sh, hipStream_t s) {
+  return xt == GNN_BF16 ? by_shape<uint16_t, KIND>(pl, p, sh.lpe, sh.nv, sh.lph, sh.groups, s)
+                        : by_shape<float, KIND>(pl, p, sh.lpe, sh.nv, sh.lph, sh.groups, s);
 }
 
 // Sizes of the gathered arrays for the buffer loads of one-slot walks (0:
@@ -601,8 +626,8 @@ void set_gather_bytes(const gnn_plan* pl, gnn_dtype xt, BwdParams& p) {
 int launch_gt_backward(gnn_plan* pl, const void* q, const void* k, const void* v, gnn_dtype xt, int32_t H,
                        int32_t D, float scale, const float* out, const float* lse, const float* dout,
                        float* dq, float* dk, float* dv, hipStream_t s) {
-  int lpe, nv, lph, lanes;
-  GNN_TRY(shape(xt, H, D, &lpe, &nv, &lph, &lanes));
+  BwdShape sh;
+  GNN_TRY(shape(xt, H, D, &sh));
   GNN_TRY(plan_transpose(pl, s));
   BwdParams p{};
   p.q = q;
@@ -614,24 +639,25 @@ int launch_gt_backward(gnn_plan* pl, const void* q, const void* k, const void* v
   p.H = H;
   p.D = D;
   p.row_elems = H * D;
-  p.row_lanes = lanes;
+  p.hpg = sh.hpg;
+  p.lph_data = sh.lph_data;
   set_gather_bytes(pl, xt, p);
   p.scale = scale > 0.0f ? scale : 1.0f / sqrtf((float)D);
   // Delta lives in the plan of the destinations, sized [n_rows, H]
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
   p.delta = pl->delta;
   p.g0 = dq;
-  GNN_TRY(run<B_GT_DST>(pl, p, xt, lpe, nv, lph, s));
+  GNN_TRY(run<B_GT_DST>(pl, p, xt, sh, s));
   p.g0 = dk;
   p.g1 = dv;
-  return run<B_GT_SRC>(pl->tplan, p, xt, lpe, nv, lph, s);
+  return run<B_GT_SRC>(pl->tplan, p, xt, sh, s);
 }
 
 int launch_gatv2_backward(gnn_plan* pl, const void* xl, const void* xr, gnn_dtype xt, const float* att,
                           int32_t H, int32_t D, float slope, const float* out, const float* lse,
                           const float* dout, float* dxl, float* dxr, float* datt, hipStream_t s) {
-  int lpe, nv, lph, lanes;
-  GNN_TRY(shape(xt, H, D, &lpe, &nv, &lph, &lanes));
+  BwdShape sh;
+  GNN_TRY(shape(xt, H, D, &sh));
   GNN_TRY(plan_transpose(pl, s));
   BwdParams p{};
   p.q = xl;
@@ -644,17 +670,18 @@ int launch_gatv2_backward(gnn_plan* pl, const void* xl, const void* xr, gnn_dtyp
   p.H = H;
   p.D = D;
   p.row_elems = H * D;
-  p.row_lanes = lanes;
+  p.hpg = sh.hpg;
+  p.lph_data = sh.lph_data;
   set_gather_bytes(pl, xt, p);
   p.slope = slope;
   GNN_TRY(plan_grow(pl, (void**)&pl->delta, &pl->delta_cap, (size_t)std::max(pl->n_rows, 1) * H * 4));
   p.delta = pl->delta;
   p.g0 = dxl;
   p.g1 = datt;
-  GNN_TRY(run<B_GAT_DST>(pl, p, xt, lpe, nv, lph, s));
+  GNN_TRY(run<B_GAT_DST>(pl, p, xt, sh, s));
   p.g0 = dxr;
   p.g1 = nullptr;
-  return run<B_GAT_SRC>(pl->tplan, p, xt, lpe, nv, lph, s);
+  return run<B_GAT_SRC>(pl->tplan, p, xt, sh, s);
 }
 
 }  // namespace gnn

@@ -416,9 +416,12 @@ int gnn_reduce_backward(const gnn_csr* csr, gnn_reduce_op op, const float* dY, i
  * (required) and dout [n_rows, H, D] float32.  Outputs (float32): dxl
  * [n_rows, H, D], dxr [n_cols, H, D], datt [H, D].  Two walks and an ordered
  * reduction; no atomics, deterministic.  The plan also keeps the per-(i, h)
- * statistic between the walks.  Supported shapes as in gnn_gatv2_fused; all
- * row tensors 16-byte aligned.
- * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+ * statistic between the walks.  Shapes: any H with D * element size a
+ * multiple of 16 bytes, at most 1 KB, and H * D < 2^28 (rows wider than 64
+ * lane slices are cut into head groups; lanes per head are padded to a power
+ * of two); all row tensors 16-byte aligned.
+ * Errors: INVALID_VALUE, UNSUPPORTED (other head widths), SIZE_OVERFLOW,
+ * PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
 int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtype xtype, const float* att,
                        int32_t H, int32_t D, float neg_slope, const float* out, const float* lse,
                        const float* dout, float* dxl, float* dxr, float* datt, gnn_plan* plan, void* stream);
@@ -432,9 +435,10 @@ int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_d
  * Inputs as in gnn_gt_fused (CSR layout; scale <= 0 means 1/sqrt(D)), plus
  * out [n_rows, H, D], lse [n_rows, H] of the forward (required) and dout
  * [n_rows, H, D] float32.  Outputs (float32): dq [n_rows, H, D], dk and dv
- * [n_cols, H, D].  Two walks, no atomics, deterministic.  Supported shapes as
- * in GNN_GT_CSR; all row tensors 16-byte aligned.
- * Errors: INVALID_VALUE, UNSUPPORTED, PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
+ * [n_cols, H, D].  Two walks, no atomics, deterministic.  Shapes as in
+ * gnn_gatv2_backward; all row tensors 16-byte aligned.
+ * Errors: INVALID_VALUE, UNSUPPORTED (other head widths), SIZE_OVERFLOW,
+ * PLAN_MISMATCH, OUT_OF_MEMORY, DEVICE. */
 int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void* v, gnn_dtype xtype, int32_t H,
                     int32_t D, float scale, const float* out, const float* lse, const float* dout, float* dq,
                     float* dk, float* dv, gnn_plan* plan, void* stream);

@@ -85,10 +85,13 @@ INV, UNS, OVF = 1, 2, 5
     ("reduce bwd max without arg", lambda: call("gnn_reduce_backward", ctypes.byref(fake_csr()), 2, P(16), 4, 4, None, P(16), 4, None, None), INV),
     ("reduce bwd bad op", lambda: call("gnn_reduce_backward", ctypes.byref(fake_csr()), 9, P(16), 4, 4, None, P(16), 4, None, None), INV),
     ("gt bwd null lse", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), P(16), None, P(16), P(16), P(16), P(16), None, None), INV),
-    ("gt bwd too wide", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 256, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd head over 1 KB", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 1, 1024, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd head not 16-byte slices", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 20, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("gt bwd misaligned", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 8, 64, ctypes.c_float(0), P(16), P(16), P(20), P(16), P(16), P(16), None, None), UNS),
     ("gatv2 bwd null datt", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 4, 32, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), None, None, None), INV),
-    ("gatv2 bwd too wide", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 8, 128, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gatv2 bwd head over 1 KB", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 1, P(16), 2, 1024, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gatv2 bwd head not 16-byte slices", lambda: call("gnn_gatv2_backward", ctypes.byref(fake_csr()), P(16), P(16), 0, P(16), 4, 6, ctypes.c_float(0.2), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd H*D overflow, wide heads", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 1 << 20, 256, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), OVF),
     ("spmm b16 non-square", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr(n_cols=5)), P(16), 1, 16, 16, P(16), 16, 0, None, None), INV),
     ("spmm b16 F not 16 B", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(16), 1, 12, 12, P(16), 12, 0, None, None), UNS),
     ("spmm b16 misaligned", lambda: call("gnn_spmm_block16", ctypes.byref(fake_csr()), P(24), 0, 16, 16, P(16), 16, 0, None, None), UNS),
@@ -107,7 +110,7 @@ INV, UNS, OVF = 1, 2, 5
     ("b16 bwd D=96", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2, 96, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("b16 bwd null dk", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), None, P(16), None, None), INV),
     ("b16 bwd H*D overflow", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(16), P(16), P(16), 2**27, 32, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
-    ("gt bwd H*D overflow", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
+    ("gt bwd H*D overflow", lambda: call("gnn_gt_backward", ctypes.byref(fake_csr()), P(16), P(16), P(16), 1, 2**28, 16, ctypes.c_float(0), P(16), P(16), P(16), P(16), P(16), P(16), None, None), OVF),
     ("b16 bwd misaligned", lambda: call("gnn_gt_backward_block16", ctypes.byref(fake_csr()), P(24), P(16), P(16), 8, 64, 0.0, P(16), P(16), P(16), P(16), P(16), P(16), None, None), UNS),
     ("plan null out", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()), None, None, None), INV),
     ("plan bad opts", lambda: call("gnn_plan_create", ctypes.byref(fake_csr()),

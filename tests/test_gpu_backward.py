@@ -137,7 +137,10 @@ def _dev_x(a, dt):
 
 
 @pytest.mark.parametrize("H,D,dt", [(8, 64, "bf16"), (4, 32, "bf16"), (2, 16, "f32"), (8, 128, "bf16"),
-                                    (1, 8, "bf16"), (4, 64, "f32")])
+                                    (1, 8, "bf16"), (4, 64, "f32"),
+                                    # head groups (rows over 64 lane slices), padded lanes per head
+                                    (8, 256, "bf16"), (4, 256, "f32"), (16, 64, "bf16"), (8, 48, "bf16"),
+                                    (2, 96, "f32")])
 @pytest.mark.parametrize("planned", [False, True])
 def test_gt_backward(rmat_loops, H, D, dt, planned):
     rp, ci = rmat_loops
@@ -158,7 +161,9 @@ def test_gt_backward(rmat_loops, H, D, dt, planned):
 
 
 @pytest.mark.parametrize("H,D,dt", [(4, 32, "bf16"), (2, 64, "bf16"), (8, 16, "bf16"), (1, 8, "bf16"),
-                                    (4, 32, "f32"), (2, 16, "f32")])
+                                    (4, 32, "f32"), (2, 16, "f32"),
+                                    # 2 KB rows, head groups, padded lanes per head
+                                    (8, 128, "bf16"), (8, 256, "bf16"), (2, 256, "f32"), (4, 48, "bf16")])
 @pytest.mark.parametrize("planned", [False, True])
 def test_gatv2_backward(rmat_loops, H, D, dt, planned):
     rp, ci = rmat_loops
