@@ -38,7 +38,8 @@ EXPORTS = ("gnn_plan_create", "gnn_plan_destroy", "gnn_plan_stats", "gnn_plan_ws
            "gnn_permute_rows", "gnn_copy_bytes", "gnn_status_string", "gnn_last_error",
            "gnn_spmm_backward", "gnn_reduce_backward", "gnn_gatv2_backward", "gnn_gt_backward",
            "gnn_spmm_block16", "gnn_dot_aggr", "gnn_gt_backward_block16", "gnn_plan_autotune",
-           "gnn_reduce_multi_noalloc", "gnn_project", "gnn_plan_verify", "gnn_plan_autotune_attention")
+           "gnn_reduce_multi_noalloc", "gnn_project", "gnn_plan_verify", "gnn_plan_autotune_attention",
+           "gnn_release_cached_memory")
 
 
 class GnnError(RuntimeError):
@@ -101,6 +102,7 @@ def load_library(path: str = LIB_PATH):
         "gnn_gt_backward_block16": [P(_Csr), vp, vp, vp, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp],
         "gnn_plan_autotune": [P(_Csr), vp, ci, i32, i64, ci, i32, P(_PlanOpts), P(f32), P(f32), vp],
         "gnn_project": [vp, i32, i32, i64, i32, P(vp), i32, P(vp), vp],
+        "gnn_release_cached_memory": [],
         "gnn_status_string": [ci],
         "gnn_last_error": [],
     }
@@ -624,6 +626,11 @@ def gnn_permute_rows(perm: torch.Tensor, X: torch.Tensor, out: torch.Tensor | No
                                            _ptr(out), out.stride(0), _stream(stream)),
            "gnn_permute_rows")
     return out
+
+
+def gnn_release_cached_memory():
+    """Give the current device's cached stream-ordered temporaries back to the runtime."""
+    _check(load_library().gnn_release_cached_memory(), "gnn_release_cached_memory")
 
 
 def gnn_copy_bytes(src: torch.Tensor, dst: torch.Tensor, nbytes: int | None = None, stream=None):

@@ -52,13 +52,14 @@ struct AggParams {
   int64_t ldy;
   int32_t* arg;            // nullable, ld = F
   const int4* items;
-  float* partial;          // [n_items, F]
+  float* partial;          // [n_slots, F] chunk partials of split rows
   unsigned long long* packed;  // [n_multi, F]
   int32_t n_rows;
   int32_t F;
   int32_t light_max;
   int32_t n_item_blocks;   // item workgroups in grid.x
   const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
+  const int32_t* multi_count; // device split-row count (NULL: the launch's row count is exact)
   int32_t n_light_blocks;
   int32_t rps;             // light rows per slot (LPR on large graphs)
   int32_t norm;            // gnn_norm (SpMM); MEAN is expressed as LEFT
@@ -594,6 +595,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
 
 // Sum of a heavy row's item partials, in item order (deterministic).
 __global__ __launch_bounds__(256) void k_combine_sum(AggParams p, const int4* multi) {
+  if (p.multi_count && (int)blockIdx.x >= *p.multi_count) return;
   const int4 mr = multi[blockIdx.x];
   const int row = mr.x, first = mr.y, cnt = mr.z;
   const int deg = p.row_ptr[row + 1] - p.row_ptr[row];
@@ -606,6 +608,7 @@ __global__ __launch_bounds__(256) void k_combine_sum(AggParams p, const int4* mu
 
 // K_ALL: sum / mean from the item partials (item order), max / min unpacked.
 __global__ __launch_bounds__(256) void k_combine_all(AggParams p, const int4* multi) {
+  if (p.multi_count && (int)blockIdx.x >= *p.multi_count) return;
   const int4 mr = multi[blockIdx.x];
   const int row = mr.x, first = mr.y, cnt = mr.z;
   const int deg = p.row_ptr[row + 1] - p.row_ptr[row];
@@ -627,6 +630,7 @@ __global__ __launch_bounds__(256) void k_combine_all(AggParams p, const int4* mu
 // Packed (key, index) words of heavy rows back to value and source index.
 template <int KIND, bool ARG>
 __global__ __launch_bounds__(256) void k_unpack(AggParams p, const int4* multi) {
+  if (p.multi_count && (int)blockIdx.x >= *p.multi_count) return;
   const int row = multi[blockIdx.x].x;
   for (int f = threadIdx.x; f < p.F; f += blockDim.x) {
     unsigned long long w = p.packed[(int64_t)blockIdx.x * p.F + f];
@@ -636,7 +640,10 @@ __global__ __launch_bounds__(256) void k_unpack(AggParams p, const int4* multi) 
   }
 }
 
-__global__ void k_fill_u64(unsigned long long* p, int64_t n, unsigned long long v) {
+// p[0, n) = v; with rows set, only the first *rows * per words of them.
+__global__ void k_fill_u64(unsigned long long* p, int64_t n, unsigned long long v, const int32_t* rows,
+                           int32_t per) {
+  if (rows) n = min(n, (int64_t)*rows * per);
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (; i < n; i += stride) p[i] = v;
@@ -652,6 +659,7 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   const int ftiles = (p.F + FT - 1) / FT;
   p.n_item_blocks = (int32_t)pl->n_items;
   p.item_count = pl->item_count;
+  p.multi_count = pl->multi_count;
   // a light workgroup covers (WG / LPR) * rps rows: 64 / LPR slots per wave,
   // rps rows per slot.  rps = LPR unless that leaves fewer than 1024
   // workgroups (four per CU): a slot walks its rows' edges as one dependent
@@ -666,10 +674,11 @@ int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   if (KIND != K_SUM && pl->n_multi > 0) {
     int64_t nw = pl->n_multi * p.F;
     const unsigned nb = (unsigned)std::min<int64_t>((nw + 255) / 256, 16384);
-    hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed, nw, KIND == K_MIN ? ~0ull : 0ull);
+    hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed, nw, KIND == K_MIN ? ~0ull : 0ull,
+                       pl->multi_count, p.F);
     GNN_LAUNCH_CHECK("fill packed");
     if (KIND == K_ALL) {
-      hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed2, nw, ~0ull);
+      hipLaunchKernelGGL(k_fill_u64, dim3(nb), dim3(256), 0, s, p.packed2, nw, ~0ull, pl->multi_count, p.F);
       GNN_LAUNCH_CHECK("fill packed");
     }
   }
@@ -744,7 +753,7 @@ int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64
   // workspace: partials for sums of heavy rows, packed words for max / min
   if (pl->n_multi > 0) {
     void* ws = nullptr;
-    size_t need = (kind == K_SUM) ? (size_t)pl->n_items * F * 4 : (size_t)pl->n_multi * F * 8;
+    size_t need = (kind == K_SUM) ? (size_t)pl->n_slots * F * 4 : (size_t)pl->n_multi * F * 8;
     GNN_TRY(plan_workspace(pl, need, &ws));
     p.partial = (float*)ws;
     p.packed = (unsigned long long*)ws;
@@ -773,7 +782,7 @@ int launch_aggregate(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, int64
 
 size_t reduce_multi_ws_bytes(const gnn_plan* pl, int32_t F) {
   if (pl->n_multi <= 0) return 0;
-  const size_t part = ((size_t)pl->n_items * F * 4 + 255) & ~(size_t)255;
+  const size_t part = ((size_t)pl->n_slots * F * 4 + 255) & ~(size_t)255;
   const size_t words = (size_t)pl->n_multi * F * 8;
   return part + 2 * words;
 }
@@ -801,7 +810,7 @@ int launch_reduce_multi(gnn_plan* pl, const void* X, gnn_dtype xt, int32_t F, in
   if (pl->n_multi > 0) {
     // split rows: item partial sums, then the packed max and min words
     void* ws = ws_given;
-    const size_t part = ((size_t)pl->n_items * F * 4 + 255) & ~(size_t)255;
+    const size_t part = ((size_t)pl->n_slots * F * 4 + 255) & ~(size_t)255;
     const size_t words = (size_t)pl->n_multi * F * 8;
     if (!ws) GNN_TRY(plan_workspace(pl, part + 2 * words, &ws));
     p.partial = (float*)ws;

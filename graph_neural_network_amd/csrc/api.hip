@@ -237,7 +237,7 @@ int gnn_plan_destroy(gnn_plan* p) {
   if (p->async_mem) {
     // a transient plan: everything is freed in stream order, no wait
     auto release = [&rc, p](void* ptr) {
-      if (ptr && hipFreeAsync(ptr, p->stream) != hipSuccess) rc = fail(GNN_ERR_DEVICE, "hipFreeAsync of a plan buffer failed");
+      if (ptr && dev_free_async(ptr, p->stream) != GNN_OK) rc = GNN_ERR_DEVICE;
     };
     for (int k = 0; k < p->n_allocs; ++k) release(p->allocs[k]);
     release(p->ws);
@@ -620,6 +620,8 @@ int gnn_dot_aggr(const gnn_csr* csr, const float* X, int32_t D, int64_t ldx, gnn
   PlanGuard g{p, tr};
   return launch_dot_aggr(p, X, D, ldx, map == GNN_DOT_NEIGHBOR ? 1 : 0, load == GNN_LOAD_VEC16, y, s);
 }
+
+int gnn_release_cached_memory(void) { return release_cached_memory(); }
 
 int gnn_copy_bytes(const void* src, void* dst, int64_t n, void* stream) {
   if (n < 0 || (n > 0 && (!src || !dst))) return fail(GNN_ERR_INVALID_VALUE, "bad copy arguments");

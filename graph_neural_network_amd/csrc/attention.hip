@@ -63,8 +63,8 @@ struct AttParams {
   float* out;        // [n_rows, H, D]
   float* lse;        // [n_rows, H] or null
   const int4* items;
-  float* pacc;       // [n_items, H * D] partial accumulators of split rows
-  float* pml;        // [n_items, 2, H] partial (m, l) of split rows
+  float* pacc;       // [n_slots, H * D] partial accumulators of split rows
+  float* pml;        // [n_slots, 2, H] partial (m, l) of split rows
   int32_t n_rows;
   int32_t H, D;
   int32_t row_elems;  // H * D
@@ -77,6 +77,7 @@ struct AttParams {
   const int32_t* att_count;  // device: how many
   int32_t n_item_blocks;
   const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
+  const int32_t* multi_count; // device split-row count (NULL: the launch's row count is exact)
   int32_t n_light_blocks;
   float slope;        // GATv2 LeakyReLU slope
   float qscale;       // GT: scale * log2(e)
@@ -389,6 +390,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(KIND == K_GA
 
 // Merge the chunk states of each split row in chunk order (same rule).
 __global__ __launch_bounds__(256) void k_att_combine(AttParams p, const int4* multi) {
+  if (p.multi_count && (int)blockIdx.x >= *p.multi_count) return;
   const int4 mr = multi[blockIdx.x];
   const int row = mr.x, first = mr.y, cnt = mr.z;
   for (int t = threadIdx.x; t < p.row_elems; t += blockDim.x) {
@@ -417,6 +419,7 @@ int launch_att_h(gnn_plan* pl, AttParams& p, int groups, hipStream_t s) {
   constexpr int SPB = (64 / LPE) * (WG / 64);
   p.n_item_blocks = (int32_t)pl->n_items;
   p.item_count = pl->item_count;
+  p.multi_count = pl->multi_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF || groups > 65535) return fail(GNN_ERR_SIZE_OVERFLOW, "attention grid too large");
@@ -559,10 +562,10 @@ int setup(gnn_plan* pl, AttParams& p, int kind, gnn_dtype xt, int32_t H, int32_t
   p.att_count = pl->att_count;
   if (pl->n_multi > 0) {
     void* ws = nullptr;
-    size_t need = (size_t)pl->n_items * (H * D + 2 * H) * 4;
+    size_t need = (size_t)pl->n_slots * (H * D + 2 * H) * 4;
     GNN_TRY(plan_workspace(pl, need, &ws));
     p.pacc = (float*)ws;
-    p.pml = p.pacc + (size_t)pl->n_items * H * D;
+    p.pml = p.pacc + (size_t)pl->n_slots * H * D;
   }
   return GNN_OK;
 }

@@ -66,7 +66,7 @@ struct BwdParams {
   float* g0;         // GT dst: dq; GT src: dk; GATv2 dst: dl; GATv2 src: dr
   float* g1;         // GT src: dv
   float* dapart;     // GATv2 dst: [gridDim.x, H * D] per-workgroup shares of da
-  float* part;       // split rows: [n_items, 2, H * D] chunk partials
+  float* part;       // split rows: [n_slots, 2, H * D] chunk partials
   int32_t H, D, row_elems;
   // lane mapping (as in the forward): a slot covers the heads of one group
   // (blockIdx.y), LPH lanes per head of which lph_data hold data
@@ -453,8 +453,10 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
 }
 
 // Rows split into chunks: sum the chunk partials in chunk order.
-__global__ __launch_bounds__(256) void k_bwd_combine(const float* part, const int4* multi, int32_t row_elems,
-                                                     int two, float* g0, float* g1) {
+__global__ __launch_bounds__(256) void k_bwd_combine(const float* part, const int4* multi,
+                                                     const int32_t* multi_count, int32_t row_elems, int two,
+                                                     float* g0, float* g1) {
+  if (multi_count && (int)blockIdx.x >= *multi_count) return;
   const int4 mr = multi[blockIdx.x];
   const int row = mr.x, first = mr.y, cnt = mr.z;
   for (int t = threadIdx.x; t < row_elems; t += blockDim.x) {
@@ -497,7 +499,7 @@ int launch_walk(gnn_plan* pl, BwdParams p, int groups, hipStream_t s) {
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;
   if (gx > 0x7FFFFFFF || groups > 65535) return fail(GNN_ERR_SIZE_OVERFLOW, "attention backward grid too large");
-  const size_t part_b = ((size_t)std::max<int64_t>(pl->n_items, 1) * 2 * p.row_elems * 4 + 255) & ~(size_t)255;
+  const size_t part_b = ((size_t)std::max<int64_t>(pl->n_slots, 1) * 2 * p.row_elems * 4 + 255) & ~(size_t)255;
   const size_t da_b = KIND == B_GAT_DST ? (size_t)gx * p.row_elems * 4 : 0;
   void* ws = nullptr;
   const size_t mid_b = 2 * (size_t)((gx + 15) / 16 + 1) * p.row_elems * 4;
@@ -510,7 +512,7 @@ int launch_walk(gnn_plan* pl, BwdParams p, int groups, hipStream_t s) {
   }
   if (pl->n_multi > 0) {
     hipLaunchKernelGGL(k_bwd_combine, dim3((unsigned)pl->n_multi), dim3(256), 0, s, p.part,
-                       (const int4*)pl->multi, p.row_elems, KIND == B_GT_SRC ? 1 : 0, p.g0, p.g1);
+                       (const int4*)pl->multi, pl->multi_count, p.row_elems, KIND == B_GT_SRC ? 1 : 0, p.g0, p.g1);
     GNN_LAUNCH_CHECK("attention backward combine");
   }
   if constexpr (KIND == B_GAT_DST) {

@@ -34,8 +34,9 @@ struct DotParams {
   int64_t ldx;
   float* y;
   const int4* items;   // (row, e_begin, e_end, multi index or -1)
-  float* partial;      // [n_items]
-  int64_t n_items;
+  float* partial;      // [n_items] one per chunk of a split row
+  int64_t n_items;     // chunk items (a bound when item_count is set)
+  const int32_t* item_count;  // device: the plan's item count, or NULL
   int32_t n;
   int32_t D;
   int32_t split_thr;   // rows with more edges run as chunks
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_dot(DotParams p, int32_t n_item
   const int32_t n_item_pad = (n_item_blocks + 7) & ~7;
   if ((int32_t)blockIdx.x < n_item_pad) {
     const int64_t it = (int64_t)blockIdx.x * kWaves + w;
-    if (it >= p.n_items) return;
+    if (it >= p.n_items || (p.item_count && it >= *p.item_count)) return;
     const int4 item = p.items[it];
     if (item.w < 0) return;  // a whole-row item: that row runs as a node
     const float acc = wave_sum(dot_range<MAP, VEC, K, U>(p, s_xi, item.x, item.y, item.z, lane));
@@ -202,9 +203,10 @@ __global__ __launch_bounds__(64 * kWaves) void k_dot(DotParams p, int32_t n_item
 }
 
 // y[row] = the row's chunk partials added in chunk order (deterministic).
-__global__ __launch_bounds__(256) void k_dot_combine(DotParams p, const int4* multi, int64_t n_multi) {
+__global__ __launch_bounds__(256) void k_dot_combine(DotParams p, const int4* multi, int64_t n_multi,
+                                                     const int32_t* multi_count) {
   const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= n_multi) return;
+  if (m >= n_multi || (multi_count && m >= *multi_count)) return;
   const int4 mr = multi[m];
   float s = 0.f;
   for (int k = 0; k < mr.z; ++k) s += p.partial[mr.y + k];
@@ -222,7 +224,8 @@ int launch_shape(gnn_plan* pl, const DotParams& p, hipStream_t s) {
   GNN_LAUNCH_CHECK("k_dot");
   if (pl->n_multi > 0) {
     const unsigned cb = (unsigned)((pl->n_multi + 255) / 256);
-    hipLaunchKernelGGL(k_dot_combine, dim3(cb), dim3(256), 0, s, p, (const int4*)pl->multi, pl->n_multi);
+    hipLaunchKernelGGL(k_dot_combine, dim3(cb), dim3(256), 0, s, p, (const int4*)pl->multi, pl->n_multi,
+                       pl->multi_count);
     GNN_LAUNCH_CHECK("k_dot_combine");
   }
   return GNN_OK;
@@ -260,10 +263,12 @@ int launch_dot_aggr(gnn_plan* pl, const float* X, int32_t D, int64_t ldx, int ma
   // longer than the light limit, the heavy threshold and one chunk
   p.split_thr = std::max(std::max(pl->light_max, pl->heavy_thr), pl->chunk_edges);
   if (pl->n_multi > 0) {
+    // the chunks of split rows are the first n_slots items
     p.items = pl->items;
-    p.n_items = pl->n_items;
+    p.n_items = pl->n_slots;
+    p.item_count = pl->item_count;
     void* ws = nullptr;
-    GNN_TRY(plan_workspace(pl, (size_t)pl->n_items * sizeof(float), &ws));
+    GNN_TRY(plan_workspace(pl, (size_t)pl->n_slots * sizeof(float), &ws));
     p.partial = static_cast<float*>(ws);
   }
   if (map == FEATURE) return vec ? launch_feature<true>(pl, p, s) : launch_feature<false>(pl, p, s);

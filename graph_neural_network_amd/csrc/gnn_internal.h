@@ -47,6 +47,12 @@ int fail(int status, const std::string& msg);
 // HIP call, so that the error paths can be exercised.
 int dev_malloc(void** p, size_t bytes);
 int dev_malloc_async(void** p, size_t bytes, hipStream_t s);
+// Stream-ordered release of a dev_malloc_async block: kept in the library's
+// per-device, per-stream cache for the next request on `s` (other pointers go
+// to hipFreeAsync).  release_cached_memory hands the current device's cached
+// blocks back to the runtime.
+int dev_free_async(void* p, hipStream_t s);
+int release_cached_memory();
 
 // Stream-ordered temporaries of one call: taken on `s`, and all freed on `s`
 // when the object goes out of scope, early error returns included.
@@ -69,17 +75,16 @@ struct StreamTemps {
   }
   // free everything now, reporting a failed free
   int release() {
-    hipError_t first = hipSuccess;
+    int first = GNN_OK;
     for (int k = 0; k < n; ++k) {
-      const hipError_t e = hipFreeAsync(p[k], s);
-      if (e != hipSuccess && first == hipSuccess) first = e;
+      const int rc = dev_free_async(p[k], s);
+      if (rc != GNN_OK && first == GNN_OK) first = rc;
     }
     n = 0;
-    if (first != hipSuccess) return fail(GNN_ERR_DEVICE, std::string("hipFreeAsync: ") + hipGetErrorString(first));
-    return GNN_OK;
+    return first;
   }
   ~StreamTemps() {
-    for (int k = 0; k < n; ++k) (void)hipFreeAsync(p[k], s);
+    for (int k = 0; k < n; ++k) (void)dev_free_async(p[k], s);
   }
 };
 
@@ -129,10 +134,14 @@ struct gnn_plan {
   int32_t heavy_thr = 0;     // rows above are split into chunks (INT32_MAX: never)
   int32_t chunk_edges = 512;
   int64_t n_light = 0, n_medium = 0, n_heavy = 0;
+  // items: the chunks of split rows first, then one per medium row; the
+  // index of a chunk item is also its partial slot in the workspace
   int4* items = nullptr;     // [n_items] (row, e_begin, e_end, multi index or -1)
-  int64_t n_items = 0;       // (an upper bound when item_count is set)
-  int32_t* item_count = nullptr;  // device: the item count, for plans built without a host read-back
-  int4* multi = nullptr;     // [n_multi] (row, first item, item count, 0)
+  int64_t n_items = 0;       // (upper bounds when item_count is set)
+  int64_t n_slots = 0;       // chunk items of split rows
+  int32_t* item_count = nullptr;   // device, plans built without a host read-back: the item count
+  int32_t* multi_count = nullptr;  // device, same plans: the split-row count (item_count + 1)
+  int4* multi = nullptr;     // [n_multi] (row, first chunk item, chunk count, 0)
   int64_t n_multi = 0;
   int32_t max_items_per_row = 0;
 

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(256) void k_quantile(const int32_t* hist, int32_t n
 // on four shared counters serialises at the L2 on large graphs.)
 __global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max,
                                                   int32_t thr, int32_t chunk, int32_t* cnt,
-                                                  int32_t* is_multi, unsigned long long* part) {
+                                                  int32_t* is_multi, int32_t* split_cnt,
+                                                  unsigned long long* part) {
   __shared__ unsigned long long ws[4][4];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int c = 0;
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_
     else c = (d + chunk - 1) / chunk;
     cnt[i] = c;
     is_multi[i] = c > 1 ? 1 : 0;
+    split_cnt[i] = c > 1 ? c : 0;
   }
   const unsigned long long l = __popcll(__ballot(i < n && c == 0));
   const unsigned long long m = __popcll(__ballot(i < n && c == 1));
@@ -224,24 +226,32 @@ __global__ void k_fingerprint(const int32_t* row_ptr, int32_t n, const int32_t* 
   out[K + k] = nnz > 0 ? col_idx[(int64_t)k * (nnz - 1) / (K - 1)] : 0;
 }
 
+// Work items: the chunks of split rows first (chunk k of a row at split_off[row]
+// + k, so that an item index below the chunk total is also the row's partial
+// slot), then one item per medium row in row order.  multi[m] = (row, first
+// chunk, chunk count, 0).  counts (optional, device): [0] = items, [1] =
+// split rows.
 __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, const int32_t* cnt,
-                             const int32_t* item_off, const int32_t* multi_off, int4* items,
-                             int4* multi) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                             const int32_t* item_off, const int32_t* split_off, const int32_t* multi_off,
+                             int4* items, int4* multi, int32_t* counts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (counts && i == 0) {
+    counts[0] = item_off[n];
+    counts[1] = multi_off[n];
+  }
   if (i >= n) return;
-  int c = cnt[i];
+  const int c = cnt[i];
   if (c == 0) return;
-  int b = row_ptr[i], e = row_ptr[i + 1];
-  int off = item_off[i];
-  int m = c > 1 ? multi_off[i] : -1;
+  const int b = row_ptr[i], e = row_ptr[i + 1];
   if (c == 1) {
-    items[off] = make_int4((int)i, b, e, -1);
+    // medium rows follow all chunks: item_off - split_off counts them
+    items[split_off[n] + item_off[i] - split_off[i]] = make_int4((int)i, b, e, -1);
     return;
   }
+  const int off = split_off[i], m = multi_off[i];
   for (int k = 0; k < c; ++k) {
-    int eb = b + k * chunk;
-    int ee = min(e, eb + chunk);
-    items[off + k] = make_int4((int)i, eb, ee, m);
+    const int eb = b + k * chunk;
+    items[off + k] = make_int4((int)i, eb, min(e, eb + chunk), m);
   }
   multi[m] = make_int4((int)i, off, c, 0);
 }
@@ -370,7 +380,7 @@ int plan_workspace(gnn_plan* p, size_t bytes, void** out) {
   }
   if (p->ws) {
     if (p->async_mem) {
-      GNN_HIP(hipFreeAsync(p->ws, p->stream));
+      GNN_TRY(dev_free_async(p->ws, p->stream));
     } else {
       GNN_HIP(hipStreamSynchronize(p->stream));
       GNN_HIP(hipFree(p->ws));
@@ -391,7 +401,7 @@ int plan_grow(gnn_plan* p, void** buf, size_t* cap, size_t bytes) {
   if (*buf && *cap >= bytes) return GNN_OK;
   if (*buf) {
     if (p->async_mem) {
-      GNN_HIP(hipFreeAsync(*buf, p->stream));
+      GNN_TRY(dev_free_async(*buf, p->stream));
     } else {
       GNN_HIP(hipStreamSynchronize(p->stream));
       GNN_HIP(hipFree(*buf));
@@ -442,38 +452,48 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
   p->opts.wsb_min_nnz = 8;
   p->light_max = 32;
   p->chunk_edges = 1024;
-  p->heavy_thr = INT32_MAX;  // no row is split
+  // no degree quantile (it needs a read-back): every row longer than one
+  // chunk is split
+  p->heavy_thr = p->chunk_edges;
   const int32_t n = p->n_rows;
+  const int64_t nnz = p->nnz, lm = p->light_max, ch = p->chunk_edges;
   // out-degrees on first use (plan_deg_out)
-  // rows longer than the light bound: at most one per light_max + 1 entries
-  const int64_t bound = std::min<int64_t>(n, p->nnz / (p->light_max + 1));
-  p->n_items = bound;
-  p->n_multi = 0;
+  // Host bounds of the device counts.  A row of d > light_max entries gives
+  // one item, or ceil(d / chunk) <= d / (light_max + 1) chunks when split,
+  // so items <= nnz / (light_max + 1), and <= rows + nnz / chunk; split rows
+  // have more than one chunk of entries, so there are at most nnz / (chunk + 1)
+  // of them and at most nnz / chunk + nnz / (chunk + 1) chunks.
+  p->n_items = std::min<int64_t>(nnz / (lm + 1), (int64_t)n + nnz / ch);
+  p->n_multi = std::min<int64_t>(n, nnz / (ch + 1));
+  p->n_slots = std::min<int64_t>(p->n_items, nnz / ch + p->n_multi);
   GNN_TRY(plan_alloc(p, (void**)&p->item_count, 16));
-  GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(bound, 1) * sizeof(int4)));
-  GNN_TRY(plan_alloc(p, (void**)&p->multi, sizeof(int4)));
-  if (n == 0 || bound == 0) {
-    GNN_HIP(hipMemsetAsync(p->item_count, 0, 4, s));
+  p->multi_count = p->item_count + 1;
+  GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(p->n_items, 1) * sizeof(int4)));
+  GNN_TRY(plan_alloc(p, (void**)&p->multi, (size_t)std::max<int64_t>(p->n_multi, 1) * sizeof(int4)));
+  if (n == 0 || p->n_items == 0) {
+    GNN_HIP(hipMemsetAsync(p->item_count, 0, 8, s));
     return GNN_OK;
   }
   StreamTemps tt(s);
-  int32_t *cnt = nullptr, *ism = nullptr, *ioff = nullptr, *moff = nullptr;
+  int32_t *cnt = nullptr, *ism = nullptr, *spl = nullptr, *ioff = nullptr, *soff = nullptr, *moff = nullptr;
   unsigned long long* part = nullptr;
   const size_t nn = (size_t)n;
   const int64_t ncb = (n + 255) / 256;
   GNN_TRY(tt.get(&cnt, nn * 4));
   GNN_TRY(tt.get(&ism, nn * 4));
+  GNN_TRY(tt.get(&spl, nn * 4));
   GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
+  GNN_TRY(tt.get(&soff, (nn + 1) * 4));
   GNN_TRY(tt.get(&moff, (nn + 1) * 4));
   GNN_TRY(tt.get(&part, (size_t)ncb * 4 * 8));
   hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max, p->heavy_thr,
-                     p->chunk_edges, cnt, ism, part);
+                     p->chunk_edges, cnt, ism, spl, part);
   GNN_LAUNCH_CHECK("classify");
   GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
+  GNN_TRY(exclusive_scan_i32(spl, soff, n, s));
   GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
-  GNN_HIP(hipMemcpyAsync(p->item_count, ioff + n, 4, hipMemcpyDeviceToDevice, s));
   hipLaunchKernelGGL(k_fill_items, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->chunk_edges, cnt, ioff,
-                     moff, p->items, p->multi);
+                     soff, moff, p->items, p->multi, p->item_count);
   GNN_LAUNCH_CHECK("fill items");
   return tt.release();
 }
@@ -520,33 +540,38 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   p->heavy_thr = thr_host;
 
   // classify rows, scan counts, fill items
-  int32_t *cnt = nullptr, *ism = nullptr, *ioff = nullptr, *moff = nullptr;
+  int32_t *cnt = nullptr, *ism = nullptr, *spl = nullptr, *ioff = nullptr, *soff = nullptr, *moff = nullptr;
   unsigned long long* stats = nullptr;
   size_t nn = (size_t)std::max(n, 1);
   GNN_TRY(tt.get(&cnt, nn * 4));
   GNN_TRY(tt.get(&ism, nn * 4));
+  GNN_TRY(tt.get(&spl, nn * 4));
   GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
+  GNN_TRY(tt.get(&soff, (nn + 1) * 4));
   GNN_TRY(tt.get(&moff, (nn + 1) * 4));
   const int64_t ncb = std::max<int64_t>((n + 255) / 256, 1);
   GNN_TRY(tt.get(&stats, (4 + ncb * 4) * 8));
   GNN_HIP(hipMemsetAsync(stats, 0, (4 + ncb * 4) * 8, s));
   if (n > 0) {
     hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max,
-                       p->heavy_thr, p->chunk_edges, cnt, ism, stats + 4);
+                       p->heavy_thr, p->chunk_edges, cnt, ism, spl, stats + 4);
     GNN_LAUNCH_CHECK("classify");
     hipLaunchKernelGGL(k_stats_total, dim3(1), dim3(256), 0, s, stats + 4, ncb, stats);
     GNN_LAUNCH_CHECK("classify totals");
   }
   GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
+  GNN_TRY(exclusive_scan_i32(spl, soff, n, s));
   GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
-  int32_t tot[2] = {0, 0};
+  int32_t tot[3] = {0, 0, 0};
   unsigned long long st[4] = {0, 0, 0, 0};
   GNN_HIP(hipMemcpyAsync(&tot[0], ioff + n, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipMemcpyAsync(&tot[1], moff + n, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipMemcpyAsync(&tot[2], soff + n, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipMemcpyAsync(st, stats, 32, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   p->n_items = tot[0];
   p->n_multi = tot[1];
+  p->n_slots = tot[2];
   p->n_light = (int64_t)st[0];
   p->n_medium = (int64_t)st[1];
   p->n_heavy = (int64_t)st[2];
@@ -555,7 +580,7 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   GNN_TRY(plan_alloc(p, (void**)&p->multi, (size_t)std::max<int64_t>(p->n_multi, 1) * sizeof(int4)));
   if (n > 0) {
     hipLaunchKernelGGL(k_fill_items, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p->row_ptr,
-                       n, p->chunk_edges, cnt, ioff, moff, p->items, p->multi);
+                       n, p->chunk_edges, cnt, ioff, soff, moff, p->items, p->multi, nullptr);
     GNN_LAUNCH_CHECK("fill items");
   }
   GNN_TRY(tt.release());

@@ -547,11 +547,11 @@ int launch_reorder(const gnn_csr* csr, gnn_reorder_kind kind, int32_t* perm, int
     ar.off = 0;
     rc = permute_csr(csr, perm, rp_out, ci_out, ar, s);
   }
-  const hipError_t e1 = hipFreeAsync(blk, s);
+  const int r1 = dev_free_async(blk, s);
   const hipError_t e2 = hipStreamSynchronize(s);
   if (rc != GNN_OK) return rc;
-  if (e1 != hipSuccess || e2 != hipSuccess)
-    return fail(GNN_ERR_DEVICE, std::string("reorder: ") + hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  if (r1 != GNN_OK) return r1;
+  if (e2 != hipSuccess) return fail(GNN_ERR_DEVICE, std::string("reorder: ") + hipGetErrorString(e2));
   return GNN_OK;
 }
 

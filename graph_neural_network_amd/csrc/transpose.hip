@@ -131,8 +131,8 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   const int rc = p->async_mem ? plan_build_async(&t, s, tp) : plan_build(&t, &o, s, tp);
   if (rc != GNN_OK) {
     for (int k = 0; k < tp->n_allocs; ++k)
-      (void)(tp->async_mem ? hipFreeAsync(tp->allocs[k], s) : hipFree(tp->allocs[k]));
-    if (tp->ws) (void)(tp->async_mem ? hipFreeAsync(tp->ws, s) : hipFree(tp->ws));
+      (void)(tp->async_mem ? dev_free_async(tp->allocs[k], s) : (int)hipFree(tp->allocs[k]));
+    if (tp->ws) (void)(tp->async_mem ? dev_free_async(tp->ws, s) : (int)hipFree(tp->ws));
     delete tp;
     return rc;
   }

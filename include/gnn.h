@@ -39,10 +39,11 @@
  *     launch; on an error nothing is launched and no output is touched.
  *   - plan may be NULL in the calls that take one.  The call then builds a
  *     transient plan in stream order (stream-ordered allocations, degrees
- *     and one work item per row longer than 32 entries, its item count kept
- *     on the device, freed stream-ordered): no host synchronisation, but no
- *     row is split across workgroups, so skewed graphs run faster with a
- *     plan built once by gnn_plan_create.  Calls that need the 16x16 tiles
+ *     and one work item per row longer than 32 entries, rows longer than
+ *     1024 entries split into chunks of 1024, the counts kept on the device,
+ *     released stream-ordered): no host synchronisation.  A plan built once
+ *     by gnn_plan_create saves the per-call build and places the split
+ *     threshold at a degree quantile.  Calls that need the 16x16 tiles
  *     (BLOCK16 modes, gnn_spmm_block16, gnn_gt_backward_block16) build a full
  *     transient plan instead, which synchronises `stream`.
  *   - Return value: a gnn_status.  gnn_last_error() gives a thread-local
@@ -59,7 +60,12 @@
  *     Calls given a plan then also run gnn_plan_verify.
  *   - Device memory: every allocation the library makes can fail with
  *     OUT_OF_MEMORY; the call then returns it with nothing left allocated
- *     and no output written beyond what finished kernels wrote.
+ *     (beyond the block cache below) and no output written beyond what
+ *     finished kernels wrote.  Stream-ordered temporaries (those of calls
+ *     without a plan, of plan builds and of reorders) are kept after the
+ *     call in a per-device block cache of at most 8 GiB and reused by later
+ *     calls, the reusing stream waiting on an event recorded where the block
+ *     was last released; gnn_release_cached_memory gives them back.
  *     GNN_FAIL_ALLOC=k (or k:tag) in the environment makes the k-th allocation
  *     after the variable took that value fail that way, before any HIP call (a hook for
  *     testing the error paths).
@@ -296,7 +302,8 @@ int gnn_reduce_multi(const gnn_csr* csr, const void* X, gnn_dtype xtype, int32_t
  *     live in a fixed library array of GNN_NOALLOC_SCRATCH_BYTES per GPU
  *     (held from the first call on that GPU until the process ends) instead
  *     of the plan's workspace; a plan and width F that need more
- *     (n_items * F * 4, rounded up to 256, plus 16 * split rows * F bytes)
+ *     (4 * F bytes per chunk of a split row, rounded up to 256, plus
+ *     16 * F bytes per split row)
  *     return SIZE_OVERFLOW before any launch;
  *   - `stream` must belong to the calling thread's current device;
  *   - the call makes no device allocation, free or host synchronisation.
@@ -506,6 +513,12 @@ int gnn_dot_aggr(const gnn_csr* csr, const float* X, int32_t D, int64_t ldx, gnn
 /* Plain streaming copy of n bytes (device to device), used to calibrate
  * bandwidth measurements and hardware counters.  Asynchronous. */
 int gnn_copy_bytes(const void* src, void* dst, int64_t n, void* stream);
+
+/* Gives the current device's cached stream-ordered blocks (see "Device
+ * memory" above) back to the runtime.  Waits for the work that last used
+ * each block; blocks that calls still in flight on the host hold are kept.
+ * Errors: DEVICE. */
+int gnn_release_cached_memory(void);
 
 /* Text of a status code (static storage). */
 const char* gnn_status_string(int status);
