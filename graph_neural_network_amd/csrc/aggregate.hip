@@ -36,6 +36,12 @@ namespace {
 
 constexpr int WG = 256;  // 4 waves
 constexpr int U = 8;     // edges in flight per slot
+// At most this many item workgroups, each taking items blockIdx.x + k x
+// kItemBlocks: a workgroup per item spends launch slots on short items and,
+// for plans that hold only a bound of their item count, on empty ones
+// (measured on the 1M-node R-MAT reduction: 1.45 ms with one workgroup per
+// item, 1.37 ms at 4096, 1.40 ms at 1024 and 16384).
+constexpr int32_t kItemBlocks = 4096;
 
 // K_ALL: sum, mean, max and min (with source indices) of one pass.
 enum Kind { K_SUM = 0, K_MAX = 1, K_MIN = 2, K_ALL = 3 };
@@ -57,8 +63,9 @@ struct AggParams {
   int32_t n_rows;
   int32_t F;
   int32_t light_max;
-  int32_t n_item_blocks;   // item workgroups in grid.x
-  const int32_t* item_count;  // device item count (NULL: n_item_blocks is exact)
+  int32_t n_item_blocks;   // item workgroups in grid.x (each takes items blockIdx.x + k n_item_blocks)
+  int32_t n_items;         // items (an upper bound when item_count is set)
+  const int32_t* item_count;  // device item count (NULL: n_items is exact)
   const int32_t* multi_count; // device split-row count (NULL: the launch's row count is exact)
   int32_t n_light_blocks;
   int32_t rps;             // light rows per slot (LPR on large graphs)
@@ -402,93 +409,95 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
   // XCD 0 and can be remapped to per-XCD runs of consecutive row ranges.
   const int n_item_pad = (p.n_item_blocks + 7) & ~7;
   if ((int)blockIdx.x < n_item_pad) {
-    // ---------------- one workgroup per work item ----------------
-    const int lid = blockIdx.x;
-    if (lid >= p.n_item_blocks) return;
-    if (p.item_count && lid >= *p.item_count) return;
-    const int4 it = p.items[lid];
-    const int row = it.x, eb = it.y, ee = it.z, m = it.w;
-    const int len = ee - eb;
-    const int per = (len + SPB - 1) / SPB;
-    const int sb = min(ee, eb + slot * per);
-    const int se = min(ee, sb + per);
-    State<KIND, VE, ARG> st;
-    st.init();
-    scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
+    // ---------------- work items, strided over the item workgroups ----------------
+    if ((int)blockIdx.x >= p.n_item_blocks) return;
+    const int n_items = p.item_count ? min(p.n_items, *p.item_count) : p.n_items;
+    for (int lid = blockIdx.x; lid < n_items; lid += p.n_item_blocks) {
+      if (lid != (int)blockIdx.x) __syncthreads();  // the previous item's merge has read the LDS slots
+      const int4 it = p.items[lid];
+      const int row = it.x, eb = it.y, ee = it.z, m = it.w;
+      const int len = ee - eb;
+      const int per = (len + SPB - 1) / SPB;
+      const int sb = min(ee, eb + slot * per);
+      const int se = min(ee, sb + per);
+      State<KIND, VE, ARG> st;
+      st.init();
+      scan_edges<T, LPR, VE, KIND, ARG>(p, sb, se, sl, slot_base, Xf, f_ok, st);
 
-    // merge the slots in LDS, in slot order
-#pragma unroll
-    for (int v = 0; v < VE; ++v) {
-      const int t = sl * VE + v;
-      if constexpr (KIND == K_ALL) {
-        s_acc[slot * FT + t] = st.acc[v];
-        s_pk[slot * FT + t] = st.pk[v];
-        s_pk2[slot * FT + t] = st.pk2[v];
-      } else if constexpr (KIND == K_SUM) {
-        s_acc[slot * FT + t] = st.acc[v];
-      } else if constexpr (ARG) {
-        s_pk[slot * FT + t] = st.pk[v];
-      } else {
-        s_key[slot * FT + t] = st.key[v];
-      }
-    }
-    __syncthreads();
-    for (int t = threadIdx.x; t < FT; t += WG) {
-      const int f = blockIdx.y * FT + t;
-      if (f >= p.F) continue;
-      float a = 0.0f;
-      uint32_t k = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
-      unsigned long long w = State<KIND, VE, ARG>::kInit, w2 = ~0ull;
-      for (int s2 = 0; s2 < SPB; ++s2) {
+      // merge the slots in LDS, in slot order
+  #pragma unroll
+      for (int v = 0; v < VE; ++v) {
+        const int t = sl * VE + v;
         if constexpr (KIND == K_ALL) {
-          a += s_acc[s2 * FT + t];
-          const unsigned long long c = s_pk[s2 * FT + t], c2 = s_pk2[s2 * FT + t];
-          w = c > w ? c : w;
-          w2 = c2 < w2 ? c2 : w2;
+          s_acc[slot * FT + t] = st.acc[v];
+          s_pk[slot * FT + t] = st.pk[v];
+          s_pk2[slot * FT + t] = st.pk2[v];
         } else if constexpr (KIND == K_SUM) {
-          a += s_acc[s2 * FT + t];
+          s_acc[slot * FT + t] = st.acc[v];
         } else if constexpr (ARG) {
-          const unsigned long long c = s_pk[s2 * FT + t];
-          w = (KIND == K_MAX) ? (c > w ? c : w) : (c < w ? c : w);
+          s_pk[slot * FT + t] = st.pk[v];
         } else {
-          const uint32_t c = s_key[s2 * FT + t];
-          k = (KIND == K_MAX) ? max(k, c) : min(k, c);
+          s_key[slot * FT + t] = st.key[v];
         }
       }
-      if constexpr (KIND != K_SUM && !ARG) w = ((unsigned long long)k << 32) | State<KIND, VE, ARG>::tie(0);
-      if constexpr (KIND == K_ALL) {
-        const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
+      __syncthreads();
+      for (int t = threadIdx.x; t < FT; t += WG) {
+        const int f = blockIdx.y * FT + t;
+        if (f >= p.F) continue;
+        float a = 0.0f;
+        uint32_t k = (KIND == K_MIN) ? 0xFFFFFFFFu : 0u;
+        unsigned long long w = State<KIND, VE, ARG>::kInit, w2 = ~0ull;
+        for (int s2 = 0; s2 < SPB; ++s2) {
+          if constexpr (KIND == K_ALL) {
+            a += s_acc[s2 * FT + t];
+            const unsigned long long c = s_pk[s2 * FT + t], c2 = s_pk2[s2 * FT + t];
+            w = c > w ? c : w;
+            w2 = c2 < w2 ? c2 : w2;
+          } else if constexpr (KIND == K_SUM) {
+            a += s_acc[s2 * FT + t];
+          } else if constexpr (ARG) {
+            const unsigned long long c = s_pk[s2 * FT + t];
+            w = (KIND == K_MAX) ? (c > w ? c : w) : (c < w ? c : w);
+          } else {
+            const uint32_t c = s_key[s2 * FT + t];
+            k = (KIND == K_MAX) ? max(k, c) : min(k, c);
+          }
+        }
+        if constexpr (KIND != K_SUM && !ARG) w = ((unsigned long long)k << 32) | State<KIND, VE, ARG>::tie(0);
+        if constexpr (KIND == K_ALL) {
+          const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
+          if (m < 0) {
+            if (p.Y) __builtin_nontemporal_store(a, p.Y + oy);
+            if (p.Ymean) __builtin_nontemporal_store(a / (float)len, p.Ymean + oy);
+            if (p.Ymax) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Ymax + oy);
+            if (p.argmax) __builtin_nontemporal_store((int)~(uint32_t)w, p.argmax + oa);
+            if (p.Ymin) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w2 >> 32)), p.Ymin + oy);
+            if (p.argmin) __builtin_nontemporal_store((int)(uint32_t)w2, p.argmin + oa);
+          } else {
+            p.partial[(int64_t)lid * p.F + f] = a;
+            atomicMax(p.packed + (int64_t)m * p.F + f, w);
+            atomicMin(p.packed2 + (int64_t)m * p.F + f, w2);
+          }
+          continue;
+        }
         if (m < 0) {
-          if (p.Y) __builtin_nontemporal_store(a, p.Y + oy);
-          if (p.Ymean) __builtin_nontemporal_store(a / (float)len, p.Ymean + oy);
-          if (p.Ymax) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Ymax + oy);
-          if (p.argmax) __builtin_nontemporal_store((int)~(uint32_t)w, p.argmax + oa);
-          if (p.Ymin) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w2 >> 32)), p.Ymin + oy);
-          if (p.argmin) __builtin_nontemporal_store((int)(uint32_t)w2, p.argmin + oa);
+          const int deg = len;  // single item covers the whole row
+          if constexpr (KIND == K_SUM) {
+            __builtin_nontemporal_store(row_factor(p, a, deg), p.Y + (int64_t)row * p.ldy + f);
+          } else {
+            const uint32_t lo = (uint32_t)w;
+            __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Y + (int64_t)row * p.ldy + f);
+            if constexpr (ARG)
+              __builtin_nontemporal_store((int)((KIND == K_MAX) ? ~lo : lo), p.arg + (int64_t)row * p.F + f);
+          }
         } else {
-          p.partial[(int64_t)lid * p.F + f] = a;
-          atomicMax(p.packed + (int64_t)m * p.F + f, w);
-          atomicMin(p.packed2 + (int64_t)m * p.F + f, w2);
-        }
-        continue;
-      }
-      if (m < 0) {
-        const int deg = len;  // single item covers the whole row
-        if constexpr (KIND == K_SUM) {
-          __builtin_nontemporal_store(row_factor(p, a, deg), p.Y + (int64_t)row * p.ldy + f);
-        } else {
-          const uint32_t lo = (uint32_t)w;
-          __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Y + (int64_t)row * p.ldy + f);
-          if constexpr (ARG)
-            __builtin_nontemporal_store((int)((KIND == K_MAX) ? ~lo : lo), p.arg + (int64_t)row * p.F + f);
-        }
-      } else {
-        if constexpr (KIND == K_SUM) {
-          p.partial[(int64_t)lid * p.F + f] = a;
-        } else {
-          unsigned long long* dst = p.packed + (int64_t)m * p.F + f;
-          if constexpr (KIND == K_MAX) atomicMax(dst, w);
-          else atomicMin(dst, w);
+          if constexpr (KIND == K_SUM) {
+            p.partial[(int64_t)lid * p.F + f] = a;
+          } else {
+            unsigned long long* dst = p.packed + (int64_t)m * p.F + f;
+            if constexpr (KIND == K_MAX) atomicMax(dst, w);
+            else atomicMin(dst, w);
+          }
         }
       }
     }
@@ -657,7 +666,8 @@ template <typename T, int LPR, int VE, int KIND, bool ARG>
 int launch_one(gnn_plan* pl, AggParams& p, hipStream_t s) {
   constexpr int FT = LPR * VE;
   const int ftiles = (p.F + FT - 1) / FT;
-  p.n_item_blocks = (int32_t)pl->n_items;
+  p.n_items = (int32_t)pl->n_items;
+  p.n_item_blocks = std::min<int32_t>(p.n_items, kItemBlocks);
   p.item_count = pl->item_count;
   p.multi_count = pl->multi_count;
   // a light workgroup covers (WG / LPR) * rps rows: 64 / LPR slots per wave,

@@ -53,8 +53,9 @@ int debug_validate(const gnn_csr* c, hipStream_t s);
 // A plan given by the caller must be bound to this CSR (with
 // GNN_DEBUG_VALIDATE=1 also by its sampled contents); otherwise build a
 // transient one (synchronises the stream) that the caller of this helper frees.
+// transient_light: the light bound of a plan built here without a read-back
 int get_plan(const gnn_csr* csr, gnn_plan* given, hipStream_t s, gnn_plan** use, bool* transient,
-             bool need_wsb = false) {
+             bool need_wsb = false, int32_t transient_light = 32) {
   *transient = false;
   if (given) {
     GNN_TRY(check_plan(given, csr));
@@ -74,7 +75,7 @@ int get_plan(const gnn_csr* csr, gnn_plan* given, hipStream_t s, gnn_plan** use,
     GNN_TRY(debug_validate(csr, s));
     p = new (std::nothrow) gnn_plan();
     if (!p) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
-    const int rc = plan_build_async(csr, s, p);
+    const int rc = plan_build_async(csr, s, p, transient_light);
     if (rc != GNN_OK) {
       std::string keep = g_last_error;
       gnn_plan_destroy(p);
@@ -414,7 +415,7 @@ int gnn_gatv2_fused(const gnn_csr* csr, const void* xl, const void* xr, gnn_dtyp
   hipStream_t s = (hipStream_t)stream;
   gnn_plan* p = nullptr;
   bool tr = false;
-  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, false, kAttSlotRows));
   PlanGuard g{p, tr};
   return launch_gatv2(p, xl, xr, xtype, att, H, D, neg_slope, out, lse, s);
 }
@@ -450,7 +451,7 @@ int gnn_gt_fused(const gnn_csr* csr, const void* q, const void* k, const void* v
   hipStream_t s = (hipStream_t)stream;
   gnn_plan* p = nullptr;
   bool tr = false;
-  GNN_TRY(get_plan(csr, plan, s, &p, &tr, mode == GNN_GT_BLOCK16));
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, mode == GNN_GT_BLOCK16, kAttSlotRows));
   PlanGuard g{p, tr};
   if (mode == GNN_GT_BLOCK16) return launch_gt_block16(p, q, k, v, H, D, sc, out, lse, s);
   return launch_gt_csr(p, q, k, v, xtype, H, D, sc, out, lse, s);
@@ -527,7 +528,7 @@ int gnn_gatv2_backward(const gnn_csr* csr, const void* xl, const void* xr, gnn_d
   hipStream_t s = (hipStream_t)stream;
   gnn_plan* p = nullptr;
   bool tr = false;
-  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, false, kAttSlotRows));
   PlanGuard g{p, tr};
   return launch_gatv2_backward(p, xl, xr, xtype, att, H, D, neg_slope, out, lse, dout, dxl, dxr, datt, s);
 }
@@ -550,7 +551,7 @@ int gnn_gt_backward(const gnn_csr* csr, const void* q, const void* k, const void
   hipStream_t s = (hipStream_t)stream;
   gnn_plan* p = nullptr;
   bool tr = false;
-  GNN_TRY(get_plan(csr, plan, s, &p, &tr));
+  GNN_TRY(get_plan(csr, plan, s, &p, &tr, false, kAttSlotRows));
   PlanGuard g{p, tr};
   return launch_gt_backward(p, q, k, v, xtype, H, D, scale, out, lse, dout, dq, dk, dv, s);
 }

@@ -148,7 +148,8 @@ struct gnn_plan {
   // rows of at most att_lmax edges, longest first (built on the first
   // attention call): one slot per row, equal lengths side by side
   int32_t* att_rows = nullptr;   // [n_rows]
-  int32_t* att_count = nullptr;  // device: number of listed rows
+  int32_t* att_woff = nullptr;   // [windows + 1] listed rows before each window of rows
+  int32_t* att_count = nullptr;  // device: number of listed rows (att_woff's last entry)
   int32_t att_lmax = -1;
 
   // the transpose A^T (built on the first backward call): its CSR arrays,
@@ -187,7 +188,14 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
 // stream-ordered memory and no host synchronisation; its item count stays on
 // the device (item_count), n_items holds an upper bound for grid sizes.  Its
 // out-degrees are counted on first use (plan_deg_out).
-int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p);
+// Plan without a host read-back (calls given no plan): rows longer than
+// light_max are items, rows longer than one chunk are split, and the counts
+// stay on the device.
+int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p, int32_t light_max);
+// Attention kernels give one slot to each row up to this many entries; the
+// plans they build without a read-back take it as their light bound (their
+// shorter items would run on the slot path anyway).
+constexpr int32_t kAttSlotRows = 128;
 // deg_out[j] = entries with column j (columns outside [0, n_cols) are not
 // counted); enqueued on `s`, temporaries stream-ordered.
 int count_out_degrees(const int32_t* col_idx, int64_t nnz, int32_t n_cols, int32_t* deg_out, hipStream_t s);

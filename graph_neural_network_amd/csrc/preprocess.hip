@@ -157,6 +157,12 @@ __global__ __launch_bounds__(256) void k_quantile(const int32_t* hist, int32_t n
 // Row classes.  Each workgroup writes its (light, medium, heavy, max chunks)
 // totals to part[blockIdx.x]; k_stats_total folds them.  (One atomic per wave
 // on four shared counters serialises at the L2 on large graphs.)
+// Work items of a row of d entries: none up to light_max, one up to thr,
+// else one per chunk.
+__device__ __forceinline__ int row_items(int d, int32_t light_max, int32_t thr, int32_t chunk) {
+  return d <= light_max ? 0 : (d <= thr ? 1 : (d + chunk - 1) / chunk);
+}
+
 __global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max,
                                                   int32_t thr, int32_t chunk, int32_t* cnt,
                                                   int32_t* is_multi, int32_t* split_cnt,
@@ -165,10 +171,7 @@ __global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int c = 0;
   if (i < n) {
-    const int d = row_ptr[i + 1] - row_ptr[i];
-    if (d <= light_max) c = 0;
-    else if (d <= thr) c = 1;
-    else c = (d + chunk - 1) / chunk;
+    c = row_items(row_ptr[i + 1] - row_ptr[i], light_max, thr, chunk);
     cnt[i] = c;
     is_multi[i] = c > 1 ? 1 : 0;
     split_cnt[i] = c > 1 ? c : 0;
@@ -256,43 +259,147 @@ __global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, c
   multi[m] = make_int4((int)i, off, c, 0);
 }
 
-// Sort keys of the attention row list.  Rows of at most lmax edges are
-// ordered by window of 2^kAttWindowBits consecutive rows, then by decreasing
-// length, then by row: waves get rows of one length while the rows a window's
-// workgroups touch stay close (neighbourhoods of nearby rows overlap on
-// clustered graphs).  Longer rows get the top bit and sort behind.
+// The item list in two passes over the rows (for plans built without a host
+// read-back), in the layout k_fill_items writes.  Pass one: per tile of
+// kScanTile rows, the sums of items, split chunks and split rows, stored as
+// three runs of nb entries (sums[k nb + b]), which one exclusive scan over
+// all 3 nb entries turns into per-tile offsets (minus each run's first
+// entry).  Pass two: the same per-row counts, scanned inside the tile, give
+// every row its positions.
+__global__ __launch_bounds__(kScanThreads) void k_items_sums(const int32_t* row_ptr, int64_t n, int32_t light_max,
+                                                             int32_t thr, int32_t chunk, int32_t* sums) {
+  __shared__ int lw[kScanThreads / 64];
+  const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int c = 0, sc = 0, m = 0;
+  for (int k = 0; k < kScanItems; ++k) {
+    if (base + k >= n) break;
+    const int r = row_items(row_ptr[base + k + 1] - row_ptr[base + k], light_max, thr, chunk);
+    c += r;
+    sc += r > 1 ? r : 0;
+    m += r > 1 ? 1 : 0;
+  }
+  int t0, t1, t2;
+  (void)block_excl_scan(c, lw, t0);
+  (void)block_excl_scan(sc, lw, t1);
+  (void)block_excl_scan(m, lw, t2);
+  if (threadIdx.x == 0) {
+    sums[blockIdx.x] = t0;
+    sums[gridDim.x + blockIdx.x] = t1;
+    sums[2 * gridDim.x + blockIdx.x] = t2;
+  }
+}
+
+// cs: the exclusive scan of the 3 nb sums (3 nb + 1 entries).  counts[0] =
+// items, counts[1] = split rows.
+__global__ __launch_bounds__(kScanThreads) void k_items_fill(const int32_t* row_ptr, int64_t n, int32_t light_max,
+                                                             int32_t thr, int32_t chunk, const int32_t* cs,
+                                                             int4* items, int4* multi, int32_t* counts) {
+  __shared__ int lw[kScanThreads / 64];
+  const int nb = (int)gridDim.x, b = (int)blockIdx.x;
+  const int64_t base = (int64_t)b * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int r[kScanItems];
+  int c = 0, sc = 0, m = 0;
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    r[k] = base + k < n ? row_items(row_ptr[base + k + 1] - row_ptr[base + k], light_max, thr, chunk) : 0;
+    c += r[k];
+    sc += r[k] > 1 ? r[k] : 0;
+    m += r[k] > 1 ? 1 : 0;
+  }
+  int t;
+  int io = block_excl_scan(c, lw, t) + cs[b];
+  int so = block_excl_scan(sc, lw, t) + cs[nb + b] - cs[nb];
+  int mo = block_excl_scan(m, lw, t) + cs[2 * nb + b] - cs[2 * nb];
+  const int n_chunks = cs[2 * nb] - cs[nb];
+  if (b == 0 && threadIdx.x == 0) {
+    counts[0] = cs[nb];
+    counts[1] = cs[3 * nb] - cs[2 * nb];
+  }
+#pragma unroll
+  for (int k = 0; k < kScanItems; ++k) {
+    if (r[k] == 0) continue;
+    const int64_t i = base + k;
+    const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
+    if (r[k] == 1) {
+      // medium rows follow all chunks: item offset minus chunk offset counts them
+      items[n_chunks + io - so] = make_int4((int)i, e0, e1, -1);
+    } else {
+      for (int q = 0; q < r[k]; ++q) {
+        const int eb = e0 + q * chunk;
+        items[so + q] = make_int4((int)i, eb, min(e1, eb + chunk), mo);
+      }
+      multi[mo] = make_int4((int)i, so, r[k], 0);
+      so += r[k];
+      ++mo;
+    }
+    io += r[k];
+  }
+}
+
+// The attention row list.  Rows of at most lmax edges are ordered by window
+// of 2^kAttWindowBits consecutive rows, then by decreasing length, then by
+// row: waves get rows of one length while the rows a window's workgroups
+// touch stay close (neighbourhoods of nearby rows overlap on clustered
+// graphs).  Longer rows are not listed.  One workgroup per window counts its
+// listed rows; after an exclusive scan of the counts, one workgroup per
+// window sorts its rows in LDS and writes them at the window's offset.
 #ifndef GNN_ATT_WINDOW_BITS
 #define GNN_ATT_WINDOW_BITS 10
 #endif
 constexpr int kAttWindowBits = GNN_ATT_WINDOW_BITS;
+constexpr int kAttWindow = 1 << kAttWindowBits;
+static_assert(kAttWindowBits >= 8 && kAttWindowBits <= 12, "window of 256 to 4096 rows");
 
-__global__ void k_att_keys(const int32_t* row_ptr, int32_t n, int32_t lmax, int wshift, int lbits,
-                           uint64_t* keys) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
-    const int d = row_ptr[i + 1] - row_ptr[i];
-    const uint32_t hi = d <= lmax ? (((uint32_t)(i >> wshift) << lbits) | (uint32_t)(lmax - d))
-                                  : 0x80000000u;
-    keys[i] = ((uint64_t)hi << 32) | (uint64_t)i;
+__global__ __launch_bounds__(256) void k_att_win_count(const int32_t* row_ptr, int32_t n, int32_t lmax,
+                                                       int32_t* cnt) {
+  __shared__ int32_t red[4];
+  const int64_t base = (int64_t)blockIdx.x * kAttWindow;
+  int c = 0;
+  for (int k = threadIdx.x; k < kAttWindow; k += 256) {
+    const int64_t i = base + k;
+    if (i < n && row_ptr[i + 1] - row_ptr[i] <= lmax) ++c;
   }
+  for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
 }
 
-// Number of listed rows: the position of the first sorted key with the top
-// bit set (binary search by one thread).
-__global__ void k_att_count(const uint64_t* keys, int64_t n, int32_t* count) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int64_t lo = 0, hi = n;
-  while (lo < hi) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (keys[mid] >> 63) hi = mid;
-    else lo = mid + 1;
+// Sort key of a row inside its window: (lmax - length) above the row's
+// position (longer first, then by row), all ones for a row that is not
+// listed.  The length field saturates at 2^(32 - kAttWindowBits) - 1: rows
+// that much shorter than lmax keep row order among themselves.
+__global__ __launch_bounds__(256) void k_att_win_sort(const int32_t* row_ptr, int32_t n, int32_t lmax,
+                                                      const int32_t* woff, int32_t* rows) {
+  __shared__ uint32_t key[kAttWindow];
+  const int64_t base = (int64_t)blockIdx.x * kAttWindow;
+  constexpr uint32_t kLenMax = (1u << (32 - kAttWindowBits)) - 2;
+  for (int k = threadIdx.x; k < kAttWindow; k += 256) {
+    const int64_t i = base + k;
+    uint32_t v = 0xFFFFFFFFu;
+    if (i < n) {
+      const int d = row_ptr[i + 1] - row_ptr[i];
+      if (d <= lmax) v = (min((uint32_t)(lmax - d), kLenMax) << kAttWindowBits) | (uint32_t)k;
+    }
+    key[k] = v;
   }
-  *count = (int32_t)lo;
-}
-
-__global__ void k_att_rows(const uint64_t* keys, int64_t n, int32_t* rows) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) rows[i] = (int32_t)(uint32_t)keys[i];
+  __syncthreads();
+  // bitonic sorting network, ascending
+  for (int size = 2; size <= kAttWindow; size <<= 1) {
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < kAttWindow / 2; t += 256) {
+        const int a = 2 * t - (t & (j - 1)), b = a + j;
+        const uint32_t x = key[a], y = key[b];
+        if ((x > y) == ((a & size) == 0)) {
+          key[a] = y;
+          key[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int32_t off = woff[blockIdx.x], cnt = woff[blockIdx.x + 1] - off;
+  for (int k = threadIdx.x; k < cnt; k += 256) rows[off + k] = (int32_t)(base + (key[k] & (kAttWindow - 1)));
 }
 
 }  // namespace
@@ -300,33 +407,28 @@ __global__ void k_att_rows(const uint64_t* keys, int64_t n, int32_t* rows) {
 int plan_att_rows(gnn_plan* p, int32_t lmax, hipStream_t s) {
   if (p->att_lmax == lmax) return GNN_OK;
   const int32_t n = p->n_rows;
+  const int64_t nw = ((int64_t)n + kAttWindow - 1) / kAttWindow;
   if (!p->att_rows) GNN_TRY(plan_alloc(p, (void**)&p->att_rows, (size_t)std::max(n, 1) * 4));
-  if (!p->att_count) GNN_TRY(plan_alloc(p, (void**)&p->att_count, 16));
-  GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));  // stays 0 for an empty graph
-  if (n > 0) {
-    uint64_t *keys = nullptr, *tmp = nullptr;
+  if (!p->att_count) {
+    // listed rows before each window; the last entry is the count
+    int32_t* woff = nullptr;
+    GNN_TRY(plan_alloc(p, (void**)&woff, (size_t)(nw + 1) * 4));
+    p->att_woff = woff;
+    p->att_count = woff + nw;
+  }
+  if (n == 0) {
+    GNN_HIP(hipMemsetAsync(p->att_count, 0, 4, s));
+  } else {
     StreamTemps tt(s);
-    GNN_TRY(tt.get(&keys, (size_t)n * 8));
-    GNN_TRY(tt.get(&tmp, (size_t)n * 8));
-    const unsigned nb = (unsigned)((n + 255) / 256);
-    // high word: window index above lbits of (lmax - length); the top bit
-    // marks unlisted rows.  Windows widen if both fields would not fit 31 bits.
-    auto bits_of = [](int64_t v) { int b = 0; while (v >> b) ++b; return b; };
-    const int lbits = std::max(1, bits_of(lmax));
-    int wshift = kAttWindowBits;
-    while (bits_of((int64_t)(n - 1) >> wshift) + lbits > 31) ++wshift;
-    const int wbits = bits_of((int64_t)(n - 1) >> wshift);
-    hipLaunchKernelGGL(k_att_keys, dim3(nb), dim3(256), 0, s, p->row_ptr, n, lmax, wshift, lbits, keys);
-    GNN_LAUNCH_CHECK("attention row keys");
-    int rc = radix_sort_u64(keys, tmp, n, 32, 32 + lbits + wbits, s);
-    if (rc == GNN_OK) rc = radix_sort_u64(keys, tmp, n, 63, 64, s);
-    if (rc == GNN_OK) {
-      hipLaunchKernelGGL(k_att_rows, dim3(nb), dim3(256), 0, s, keys, (int64_t)n, p->att_rows);
-      hipLaunchKernelGGL(k_att_count, dim3(1), dim3(64), 0, s, keys, (int64_t)n, p->att_count);
-      if (hipGetLastError() != hipSuccess) rc = fail(GNN_ERR_DEVICE, "attention row list launch failed");
-    }
+    int32_t* cnt = nullptr;
+    GNN_TRY(tt.get(&cnt, (size_t)nw * 4));
+    hipLaunchKernelGGL(k_att_win_count, dim3((unsigned)nw), dim3(256), 0, s, p->row_ptr, n, lmax, cnt);
+    GNN_LAUNCH_CHECK("attention row counts");
+    GNN_TRY(exclusive_scan_i32(cnt, p->att_woff, nw, s));
+    hipLaunchKernelGGL(k_att_win_sort, dim3((unsigned)nw), dim3(256), 0, s, p->row_ptr, n, lmax, p->att_woff,
+                       p->att_rows);
+    GNN_LAUNCH_CHECK("attention row list");
     GNN_TRY(tt.release());
-    if (rc != GNN_OK) return rc;
   }
   p->att_lmax = lmax;
   return GNN_OK;
@@ -441,7 +543,7 @@ int plan_deg_out(gnn_plan* p, hipStream_t s) {
   return GNN_OK;
 }
 
-int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
+int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p, int32_t light_max) {
   p->n_rows = csr->n_rows;
   p->n_cols = csr->n_cols;
   p->nnz = csr->nnz;
@@ -450,8 +552,8 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
   p->stream = s;
   p->async_mem = true;
   p->opts.wsb_min_nnz = 8;
-  p->light_max = 32;
-  p->chunk_edges = 1024;
+  p->light_max = light_max;
+  p->chunk_edges = std::max(1024, 2 * (light_max + 1));  // keeps the item bound below valid
   // no degree quantile (it needs a read-back): every row longer than one
   // chunk is split
   p->heavy_thr = p->chunk_edges;
@@ -475,25 +577,16 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p) {
     return GNN_OK;
   }
   StreamTemps tt(s);
-  int32_t *cnt = nullptr, *ism = nullptr, *spl = nullptr, *ioff = nullptr, *soff = nullptr, *moff = nullptr;
-  unsigned long long* part = nullptr;
-  const size_t nn = (size_t)n;
-  const int64_t ncb = (n + 255) / 256;
-  GNN_TRY(tt.get(&cnt, nn * 4));
-  GNN_TRY(tt.get(&ism, nn * 4));
-  GNN_TRY(tt.get(&spl, nn * 4));
-  GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
-  GNN_TRY(tt.get(&soff, (nn + 1) * 4));
-  GNN_TRY(tt.get(&moff, (nn + 1) * 4));
-  GNN_TRY(tt.get(&part, (size_t)ncb * 4 * 8));
-  hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max, p->heavy_thr,
-                     p->chunk_edges, cnt, ism, spl, part);
-  GNN_LAUNCH_CHECK("classify");
-  GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
-  GNN_TRY(exclusive_scan_i32(spl, soff, n, s));
-  GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
-  hipLaunchKernelGGL(k_fill_items, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->chunk_edges, cnt, ioff,
-                     soff, moff, p->items, p->multi, p->item_count);
+  const int64_t nb = ((int64_t)n + kScanTile - 1) / kScanTile;
+  int32_t *sums = nullptr, *cs = nullptr;
+  GNN_TRY(tt.get(&sums, (size_t)nb * 3 * 4));
+  GNN_TRY(tt.get(&cs, ((size_t)nb * 3 + 1) * 4));
+  hipLaunchKernelGGL(k_items_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
+                     p->light_max, p->heavy_thr, p->chunk_edges, sums);
+  GNN_LAUNCH_CHECK("item sums");
+  GNN_TRY(exclusive_scan_i32(sums, cs, nb * 3, s));
+  hipLaunchKernelGGL(k_items_fill, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
+                     p->light_max, p->heavy_thr, p->chunk_edges, cs, p->items, p->multi, p->item_count);
   GNN_LAUNCH_CHECK("fill items");
   return tt.release();
 }

@@ -128,7 +128,7 @@ int plan_transpose(gnn_plan* p, hipStream_t s) {
   gnn_plan* tp = new (std::nothrow) gnn_plan();
   if (!tp) return fail(GNN_ERR_OUT_OF_MEMORY, "host allocation failed");
   // a transient plan's transpose is transient too: built without a host wait
-  const int rc = p->async_mem ? plan_build_async(&t, s, tp) : plan_build(&t, &o, s, tp);
+  const int rc = p->async_mem ? plan_build_async(&t, s, tp, p->light_max) : plan_build(&t, &o, s, tp);
   if (rc != GNN_OK) {
     for (int k = 0; k < tp->n_allocs; ++k)
       (void)(tp->async_mem ? dev_free_async(tp->allocs[k], s) : (int)hipFree(tp->allocs[k]));

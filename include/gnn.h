@@ -39,8 +39,9 @@
  *     launch; on an error nothing is launched and no output is touched.
  *   - plan may be NULL in the calls that take one.  The call then builds a
  *     transient plan in stream order (stream-ordered allocations, degrees
- *     and one work item per row longer than 32 entries, rows longer than
- *     1024 entries split into chunks of 1024, the counts kept on the device,
+ *     and one work item per row longer than 32 entries, 128 in the attention
+ *     calls, rows longer than 1024 entries split into chunks of 1024, the
+ *     counts kept on the device,
  *     released stream-ordered): no host synchronisation.  A plan built once
  *     by gnn_plan_create saves the per-call build and places the split
  *     threshold at a degree quantile.  Calls that need the 16x16 tiles
