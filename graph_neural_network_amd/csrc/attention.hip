@@ -417,7 +417,8 @@ template <typename T, int LPE, int VB, int KIND, int LPH>
 int launch_att_h(gnn_plan* pl, AttParams& p, int groups, hipStream_t s) {
   constexpr int UU = GNN_ATT_U;
   constexpr int SPB = (64 / LPE) * (WG / 64);
-  p.n_item_blocks = (int32_t)pl->n_items;
+  // the plan lists first the items this one-slot bound leaves to workgroups
+  p.n_item_blocks = (int32_t)(p.light_max == pl->att_item_thr ? pl->n_att_items : pl->n_items);
   p.item_count = pl->item_count;
   p.multi_count = pl->multi_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);

@@ -494,7 +494,8 @@ int launch_walk(gnn_plan* pl, BwdParams p, int groups, hipStream_t s) {
   GNN_TRY(plan_att_rows(pl, p.light_max, s));
   p.light_rows = pl->att_rows;
   p.light_count = pl->att_count;
-  p.n_item_blocks = (int32_t)pl->n_items;
+  // the plan lists first the items this one-slot bound leaves to workgroups
+  p.n_item_blocks = (int32_t)(p.light_max == pl->att_item_thr ? pl->n_att_items : pl->n_items);
   p.item_count = pl->item_count;
   p.n_light_blocks = (int32_t)((p.n_rows + SPB - 1) / SPB);
   const int64_t gx = (((int64_t)p.n_item_blocks + 7) & ~7LL) + p.n_light_blocks;

@@ -134,11 +134,15 @@ struct gnn_plan {
   int32_t heavy_thr = 0;     // rows above are split into chunks (INT32_MAX: never)
   int32_t chunk_edges = 512;
   int64_t n_light = 0, n_medium = 0, n_heavy = 0;
-  // items: the chunks of split rows first, then one per medium row; the
-  // index of a chunk item is also its partial slot in the workspace
+  // items: the chunks of split rows first, then one per medium row (those
+  // longer than att_item_thr first); the index of a chunk item is also its
+  // partial slot in the workspace
   int4* items = nullptr;     // [n_items] (row, e_begin, e_end, multi index or -1)
   int64_t n_items = 0;       // (upper bounds when item_count is set)
   int64_t n_slots = 0;       // chunk items of split rows
+  int32_t att_item_thr = 0;  // medium rows longer than this come before the others
+  int64_t n_att_items = 0;   // chunks and those rows: the items an attention call with
+                             // a one-slot bound of att_item_thr runs (a bound as n_items)
   int32_t* item_count = nullptr;   // device, plans built without a host read-back: the item count
   int32_t* multi_count = nullptr;  // device, same plans: the split-row count (item_count + 1)
   int4* multi = nullptr;     // [n_multi] (row, first chunk item, chunk count, 0)

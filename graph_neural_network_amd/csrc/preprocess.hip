@@ -163,18 +163,15 @@ __device__ __forceinline__ int row_items(int d, int32_t light_max, int32_t thr, 
   return d <= light_max ? 0 : (d <= thr ? 1 : (d + chunk - 1) / chunk);
 }
 
+// Per-block counts of light, medium and heavy rows and the largest item
+// count of a row (for the plan's statistics).
 __global__ __launch_bounds__(256) void k_classify(const int32_t* row_ptr, int32_t n, int32_t light_max,
-                                                  int32_t thr, int32_t chunk, int32_t* cnt,
-                                                  int32_t* is_multi, int32_t* split_cnt,
-                                                  unsigned long long* part) {
+                                                  int32_t thr, int32_t chunk, unsigned long long* part) {
   __shared__ unsigned long long ws[4][4];
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int c = 0;
   if (i < n) {
     c = row_items(row_ptr[i + 1] - row_ptr[i], light_max, thr, chunk);
-    cnt[i] = c;
-    is_multi[i] = c > 1 ? 1 : 0;
-    split_cnt[i] = c > 1 ? c : 0;
   }
   const unsigned long long l = __popcll(__ballot(i < n && c == 0));
   const unsigned long long m = __popcll(__ballot(i < n && c == 1));
@@ -229,110 +226,105 @@ __global__ void k_fingerprint(const int32_t* row_ptr, int32_t n, const int32_t* 
   out[K + k] = nnz > 0 ? col_idx[(int64_t)k * (nnz - 1) / (K - 1)] : 0;
 }
 
-// Work items: the chunks of split rows first (chunk k of a row at split_off[row]
-// + k, so that an item index below the chunk total is also the row's partial
-// slot), then one item per medium row in row order.  multi[m] = (row, first
-// chunk, chunk count, 0).  counts (optional, device): [0] = items, [1] =
-// split rows.
-__global__ void k_fill_items(const int32_t* row_ptr, int32_t n, int32_t chunk, const int32_t* cnt,
-                             const int32_t* item_off, const int32_t* split_off, const int32_t* multi_off,
-                             int4* items, int4* multi, int32_t* counts) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (counts && i == 0) {
-    counts[0] = item_off[n];
-    counts[1] = multi_off[n];
-  }
-  if (i >= n) return;
-  const int c = cnt[i];
-  if (c == 0) return;
-  const int b = row_ptr[i], e = row_ptr[i + 1];
-  if (c == 1) {
-    // medium rows follow all chunks: item_off - split_off counts them
-    items[split_off[n] + item_off[i] - split_off[i]] = make_int4((int)i, b, e, -1);
-    return;
-  }
-  const int off = split_off[i], m = multi_off[i];
-  for (int k = 0; k < c; ++k) {
-    const int eb = b + k * chunk;
-    items[off + k] = make_int4((int)i, eb, min(e, eb + chunk), m);
-  }
-  multi[m] = make_int4((int)i, off, c, 0);
+// The item list, built in two passes over the rows.  Layout: the chunks of
+// split rows (chunk q of a row at its split offset + q, so that an item index
+// below the chunk total is also the row's partial slot), then the medium rows
+// longer than att_thr, then the other medium rows, each group in row order.
+// multi[m] = (row, first chunk item, chunk count, 0).  The attention kernels
+// run rows of up to att_thr entries one per slot, so they launch only the
+// items before the short medium rows.
+// Pass one: per tile of kScanTile rows, the sums of items, split chunks,
+// split rows and long medium rows, stored as four runs of nb entries
+// (sums[k nb + b]); one exclusive scan over all 4 nb entries turns them into
+// per-tile offsets (minus each run's first entry).  Pass two: the same
+// per-row counts, scanned inside the tile, give every row its positions.
+struct RowCounts {
+  int c, sc, m, g;  // items, split chunks, split rows, long medium rows
+};
+
+__device__ __forceinline__ RowCounts row_counts(const int32_t* row_ptr, int64_t i, int32_t light_max, int32_t thr,
+                                                int32_t chunk, int32_t att_thr) {
+  const int d = row_ptr[i + 1] - row_ptr[i];
+  const int r = row_items(d, light_max, thr, chunk);
+  return RowCounts{r, r > 1 ? r : 0, r > 1 ? 1 : 0, (r == 1 && d > att_thr) ? 1 : 0};
 }
 
-// The item list in two passes over the rows (for plans built without a host
-// read-back), in the layout k_fill_items writes.  Pass one: per tile of
-// kScanTile rows, the sums of items, split chunks and split rows, stored as
-// three runs of nb entries (sums[k nb + b]), which one exclusive scan over
-// all 3 nb entries turns into per-tile offsets (minus each run's first
-// entry).  Pass two: the same per-row counts, scanned inside the tile, give
-// every row its positions.
 __global__ __launch_bounds__(kScanThreads) void k_items_sums(const int32_t* row_ptr, int64_t n, int32_t light_max,
-                                                             int32_t thr, int32_t chunk, int32_t* sums) {
+                                                             int32_t thr, int32_t chunk, int32_t att_thr,
+                                                             int32_t* sums) {
   __shared__ int lw[kScanThreads / 64];
   const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
-  int c = 0, sc = 0, m = 0;
+  RowCounts t{0, 0, 0, 0};
   for (int k = 0; k < kScanItems; ++k) {
     if (base + k >= n) break;
-    const int r = row_items(row_ptr[base + k + 1] - row_ptr[base + k], light_max, thr, chunk);
-    c += r;
-    sc += r > 1 ? r : 0;
-    m += r > 1 ? 1 : 0;
+    const RowCounts r = row_counts(row_ptr, base + k, light_max, thr, chunk, att_thr);
+    t.c += r.c;
+    t.sc += r.sc;
+    t.m += r.m;
+    t.g += r.g;
   }
-  int t0, t1, t2;
-  (void)block_excl_scan(c, lw, t0);
-  (void)block_excl_scan(sc, lw, t1);
-  (void)block_excl_scan(m, lw, t2);
+  int t0, t1, t2, t3;
+  (void)block_excl_scan(t.c, lw, t0);
+  (void)block_excl_scan(t.sc, lw, t1);
+  (void)block_excl_scan(t.m, lw, t2);
+  (void)block_excl_scan(t.g, lw, t3);
   if (threadIdx.x == 0) {
     sums[blockIdx.x] = t0;
     sums[gridDim.x + blockIdx.x] = t1;
     sums[2 * gridDim.x + blockIdx.x] = t2;
+    sums[3 * gridDim.x + blockIdx.x] = t3;
   }
 }
 
-// cs: the exclusive scan of the 3 nb sums (3 nb + 1 entries).  counts[0] =
-// items, counts[1] = split rows.
+// cs: the exclusive scan of the 4 nb sums (4 nb + 1 entries).  counts
+// (optional): [0] = items, [1] = split rows.
 __global__ __launch_bounds__(kScanThreads) void k_items_fill(const int32_t* row_ptr, int64_t n, int32_t light_max,
-                                                             int32_t thr, int32_t chunk, const int32_t* cs,
-                                                             int4* items, int4* multi, int32_t* counts) {
+                                                             int32_t thr, int32_t chunk, int32_t att_thr,
+                                                             const int32_t* cs, int4* items, int4* multi,
+                                                             int32_t* counts) {
   __shared__ int lw[kScanThreads / 64];
   const int nb = (int)gridDim.x, b = (int)blockIdx.x;
   const int64_t base = (int64_t)b * kScanTile + (int64_t)threadIdx.x * kScanItems;
-  int r[kScanItems];
-  int c = 0, sc = 0, m = 0;
+  RowCounts r[kScanItems];
+  RowCounts t{0, 0, 0, 0};
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    r[k] = base + k < n ? row_items(row_ptr[base + k + 1] - row_ptr[base + k], light_max, thr, chunk) : 0;
-    c += r[k];
-    sc += r[k] > 1 ? r[k] : 0;
-    m += r[k] > 1 ? 1 : 0;
+    r[k] = base + k < n ? row_counts(row_ptr, base + k, light_max, thr, chunk, att_thr) : RowCounts{0, 0, 0, 0};
+    t.c += r[k].c;
+    t.sc += r[k].sc;
+    t.m += r[k].m;
+    t.g += r[k].g;
   }
-  int t;
-  int io = block_excl_scan(c, lw, t) + cs[b];
-  int so = block_excl_scan(sc, lw, t) + cs[nb + b] - cs[nb];
-  int mo = block_excl_scan(m, lw, t) + cs[2 * nb + b] - cs[2 * nb];
-  const int n_chunks = cs[2 * nb] - cs[nb];
-  if (b == 0 && threadIdx.x == 0) {
+  int tot;
+  int io = block_excl_scan(t.c, lw, tot) + cs[b];
+  int so = block_excl_scan(t.sc, lw, tot) + cs[nb + b] - cs[nb];
+  int mo = block_excl_scan(t.m, lw, tot) + cs[2 * nb + b] - cs[2 * nb];
+  int go = block_excl_scan(t.g, lw, tot) + cs[3 * nb + b] - cs[3 * nb];
+  const int n_chunks = cs[2 * nb] - cs[nb], n_long = cs[4 * nb] - cs[3 * nb];
+  if (counts && b == 0 && threadIdx.x == 0) {
     counts[0] = cs[nb];
     counts[1] = cs[3 * nb] - cs[2 * nb];
   }
 #pragma unroll
   for (int k = 0; k < kScanItems; ++k) {
-    if (r[k] == 0) continue;
+    if (r[k].c == 0) continue;
     const int64_t i = base + k;
     const int e0 = row_ptr[i], e1 = row_ptr[i + 1];
-    if (r[k] == 1) {
-      // medium rows follow all chunks: item offset minus chunk offset counts them
-      items[n_chunks + io - so] = make_int4((int)i, e0, e1, -1);
+    if (r[k].c == 1) {
+      // medium rows before this one: io - so; long ones among them: go
+      const int pos = r[k].g ? n_chunks + go : n_chunks + n_long + (io - so - go);
+      items[pos] = make_int4((int)i, e0, e1, -1);
     } else {
-      for (int q = 0; q < r[k]; ++q) {
+      for (int q = 0; q < r[k].c; ++q) {
         const int eb = e0 + q * chunk;
         items[so + q] = make_int4((int)i, eb, min(e1, eb + chunk), mo);
       }
-      multi[mo] = make_int4((int)i, so, r[k], 0);
-      so += r[k];
-      ++mo;
+      multi[mo] = make_int4((int)i, so, r[k].c, 0);
     }
-    io += r[k];
+    io += r[k].c;
+    so += r[k].sc;
+    mo += r[k].m;
+    go += r[k].g;
   }
 }
 
@@ -568,6 +560,8 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p, int32_t lig
   p->n_items = std::min<int64_t>(nnz / (lm + 1), (int64_t)n + nnz / ch);
   p->n_multi = std::min<int64_t>(n, nnz / (ch + 1));
   p->n_slots = std::min<int64_t>(p->n_items, nnz / ch + p->n_multi);
+  p->att_item_thr = light_max;
+  p->n_att_items = p->n_items;
   GNN_TRY(plan_alloc(p, (void**)&p->item_count, 16));
   p->multi_count = p->item_count + 1;
   GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(p->n_items, 1) * sizeof(int4)));
@@ -579,14 +573,16 @@ int plan_build_async(const gnn_csr* csr, hipStream_t s, gnn_plan* p, int32_t lig
   StreamTemps tt(s);
   const int64_t nb = ((int64_t)n + kScanTile - 1) / kScanTile;
   int32_t *sums = nullptr, *cs = nullptr;
-  GNN_TRY(tt.get(&sums, (size_t)nb * 3 * 4));
-  GNN_TRY(tt.get(&cs, ((size_t)nb * 3 + 1) * 4));
+  GNN_TRY(tt.get(&sums, (size_t)nb * 4 * 4));
+  GNN_TRY(tt.get(&cs, ((size_t)nb * 4 + 1) * 4));
+  // every medium row counts as long (att_thr = light_max): row order
   hipLaunchKernelGGL(k_items_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
-                     p->light_max, p->heavy_thr, p->chunk_edges, sums);
+                     p->light_max, p->heavy_thr, p->chunk_edges, p->light_max, sums);
   GNN_LAUNCH_CHECK("item sums");
-  GNN_TRY(exclusive_scan_i32(sums, cs, nb * 3, s));
+  GNN_TRY(exclusive_scan_i32(sums, cs, nb * 4, s));
   hipLaunchKernelGGL(k_items_fill, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
-                     p->light_max, p->heavy_thr, p->chunk_edges, cs, p->items, p->multi, p->item_count);
+                     p->light_max, p->heavy_thr, p->chunk_edges, p->light_max, cs, p->items, p->multi,
+                     p->item_count);
   GNN_LAUNCH_CHECK("fill items");
   return tt.release();
 }
@@ -632,39 +628,38 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   }
   p->heavy_thr = thr_host;
 
-  // classify rows, scan counts, fill items
-  int32_t *cnt = nullptr, *ism = nullptr, *spl = nullptr, *ioff = nullptr, *soff = nullptr, *moff = nullptr;
+  // statistics, then the item list (totals read back to size it)
   unsigned long long* stats = nullptr;
-  size_t nn = (size_t)std::max(n, 1);
-  GNN_TRY(tt.get(&cnt, nn * 4));
-  GNN_TRY(tt.get(&ism, nn * 4));
-  GNN_TRY(tt.get(&spl, nn * 4));
-  GNN_TRY(tt.get(&ioff, (nn + 1) * 4));
-  GNN_TRY(tt.get(&soff, (nn + 1) * 4));
-  GNN_TRY(tt.get(&moff, (nn + 1) * 4));
   const int64_t ncb = std::max<int64_t>((n + 255) / 256, 1);
   GNN_TRY(tt.get(&stats, (4 + ncb * 4) * 8));
   GNN_HIP(hipMemsetAsync(stats, 0, (4 + ncb * 4) * 8, s));
+  // the attention kernels' one-slot bound for this plan
+  p->att_item_thr = std::max(p->light_max, std::min(p->opts.att_slot_max > 0 ? p->opts.att_slot_max : kAttSlotRows,
+                                                    p->heavy_thr));
+  const int64_t nb = std::max<int64_t>(((int64_t)n + kScanTile - 1) / kScanTile, 1);
+  int32_t *sums = nullptr, *cs = nullptr;
+  GNN_TRY(tt.get(&sums, (size_t)nb * 4 * 4));
+  GNN_TRY(tt.get(&cs, ((size_t)nb * 4 + 1) * 4));
+  int32_t tot[5] = {0, 0, 0, 0, 0};
   if (n > 0) {
     hipLaunchKernelGGL(k_classify, dim3((unsigned)ncb), dim3(256), 0, s, p->row_ptr, n, p->light_max,
-                       p->heavy_thr, p->chunk_edges, cnt, ism, spl, stats + 4);
+                       p->heavy_thr, p->chunk_edges, stats + 4);
     GNN_LAUNCH_CHECK("classify");
     hipLaunchKernelGGL(k_stats_total, dim3(1), dim3(256), 0, s, stats + 4, ncb, stats);
     GNN_LAUNCH_CHECK("classify totals");
+    hipLaunchKernelGGL(k_items_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
+                       p->light_max, p->heavy_thr, p->chunk_edges, p->att_item_thr, sums);
+    GNN_LAUNCH_CHECK("item sums");
+    GNN_TRY(exclusive_scan_i32(sums, cs, nb * 4, s));
+    for (int k = 0; k < 5; ++k) GNN_HIP(hipMemcpyAsync(&tot[k], cs + k * nb, 4, hipMemcpyDeviceToHost, s));
   }
-  GNN_TRY(exclusive_scan_i32(cnt, ioff, n, s));
-  GNN_TRY(exclusive_scan_i32(spl, soff, n, s));
-  GNN_TRY(exclusive_scan_i32(ism, moff, n, s));
-  int32_t tot[3] = {0, 0, 0};
   unsigned long long st[4] = {0, 0, 0, 0};
-  GNN_HIP(hipMemcpyAsync(&tot[0], ioff + n, 4, hipMemcpyDeviceToHost, s));
-  GNN_HIP(hipMemcpyAsync(&tot[1], moff + n, 4, hipMemcpyDeviceToHost, s));
-  GNN_HIP(hipMemcpyAsync(&tot[2], soff + n, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipMemcpyAsync(st, stats, 32, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
-  p->n_items = tot[0];
-  p->n_multi = tot[1];
-  p->n_slots = tot[2];
+  p->n_items = tot[1] - tot[0];
+  p->n_slots = tot[2] - tot[1];
+  p->n_multi = tot[3] - tot[2];
+  p->n_att_items = p->n_slots + (tot[4] - tot[3]);
   p->n_light = (int64_t)st[0];
   p->n_medium = (int64_t)st[1];
   p->n_heavy = (int64_t)st[2];
@@ -672,8 +667,9 @@ int plan_build(const gnn_csr* csr, const gnn_plan_opts* opts, hipStream_t s, gnn
   GNN_TRY(plan_alloc(p, (void**)&p->items, (size_t)std::max<int64_t>(p->n_items, 1) * sizeof(int4)));
   GNN_TRY(plan_alloc(p, (void**)&p->multi, (size_t)std::max<int64_t>(p->n_multi, 1) * sizeof(int4)));
   if (n > 0) {
-    hipLaunchKernelGGL(k_fill_items, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p->row_ptr,
-                       n, p->chunk_edges, cnt, ioff, soff, moff, p->items, p->multi, nullptr);
+    hipLaunchKernelGGL(k_items_fill, dim3((unsigned)nb), dim3(kScanThreads), 0, s, p->row_ptr, (int64_t)n,
+                       p->light_max, p->heavy_thr, p->chunk_edges, p->att_item_thr, cs, p->items, p->multi,
+                       (int32_t*)nullptr);
     GNN_LAUNCH_CHECK("fill items");
   }
   GNN_TRY(tt.release());
