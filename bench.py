@@ -121,11 +121,30 @@ class Op:
     """One timed call.  warm=True: every timed call follows an identical
     untimed one (a warm second pass over the same data)."""
 
-    def __init__(self, name, fn, edges, bytes_alg, warm=False):
+    def __init__(self, name, fn, edges, bytes_alg, warm=False, flops=0):
         self.name, self.fn, self.edges, self.bytes_alg, self.warm = name, fn, edges, bytes_alg, warm
+        self.flops = flops  # algorithmic floating-point operations per call (ALU-bound ops)
 
 
 TUNED_RMAT1M = {"heavy_quantile": 0.999, "light_max_deg": 32, "chunk_edges": 1024}
+
+# Algorithmic floating-point operations per (edge, head) of the fused attention
+# kernels, counted on the pages' formulas (an add, multiply or compare is one, a
+# multiply-add two, an exponential one):
+#   GATv2 forward: z = l_i + r_j (D), LeakyReLU (D), a . (2D), online softmax
+#     (max, difference, exponential, l update: 4), acc = acc corr + p r_j (3D);
+#   GT forward: q . k (2D), scale (1), online softmax (4), acc update (3D);
+#   GATv2 backward, each of the two walks: the score again (4D), p (4),
+#     dp = dO . r (2D), ds = p (dp - Delta) (2), and one gradient update
+#     through LeakyReLU' and a (3D);
+#   GT backward: destination walk q . k (2D), p (4), dO . v (2D), ds (2),
+#     dq += ds k (2D); source walk the same score and ds (4D + 6) plus
+#     dk += ds q and dv += p dO (4D).
+FLOPS_GATV2 = lambda D: 7 * D + 4
+FLOPS_GT = lambda D: 5 * D + 5
+FLOPS_GATV2_BWD = lambda D: 2 * (9 * D + 6)
+FLOPS_GT_BWD = lambda D: (6 * D + 6) + (8 * D + 6)
+VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, published
 TUNED_GATV2 = {"heavy_quantile": 0.999, "chunk_edges": 1024, "att_slot_max": 128}
 
 
@@ -295,7 +314,8 @@ def wl_gatv2(args):
     # projection: X read once, both weights, both outputs written (13.1 GFLOP on the matrix cores)
     b_proj = n * Fi * 2 + 2 * H * D * Fi * 2 + 2 * n * row_b
     ops = [Op("project", lambda: gnn.gnn_project(X, [Wl, Wr], out=proj_out), 0, b_proj),
-           Op("gatv2", lambda: gnn.gnn_gatv2_fused(csr, xl, xr, att, 0.2, out=out, lse=lse, plan=plan), m, b)]
+           Op("gatv2", lambda: gnn.gnn_gatv2_fused(csr, xl, xr, att, 0.2, out=out, lse=lse, plan=plan), m, b,
+              flops=m * H * FLOPS_GATV2(D))]
 
     def cpu(budget_s):
         import oracle
@@ -316,7 +336,7 @@ def wl_gatv2(args):
            "step": "gnn_project (l, r) then gnn_gatv2_fused; value = edges / (both)",
            "plan": gnn.gnn_plan_stats(plan), "plan_opts": TUNED_GATV2}
     comp = 4 * (n + 1) + 4 * m + 2 * n * row_b + H * D * 4 + n * (H * D * 4 + H * 4)
-    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 16, 0, 4, 4>",
+    return {"ops": ops, "dominant": "gatv2", "kernel": "k_attention<unsigned short, 16, 16, 0, 4, 4>", "bound": "alu",
             "config": cfg, "dtype": "bf16", "cpu": cpu, "compulsory": comp, "cpu_1thread": True,
             "keep": (w, csr, plan, X, Wl, Wr, xl, xr, att, out, lse)}
 
@@ -350,7 +370,8 @@ def wl_gt(args, mode="csr"):
         # per residual edge as in CSR; per window two offsets
         b = (st["wsb_dense_tiles"] * (2 * 16 * row_b + 96) + st["wsb_residual_edges"] * (4 + 2 * row_b)
              + st["wsb_windows"] * 8 + per_row)
-    ops = [Op("gt", lambda: gnn.gnn_gt_fused(csr, q, k, v, 0.0, mode, out=out, lse=lse, plan=plan), m, b)]
+    ops = [Op("gt", lambda: gnn.gnn_gt_fused(csr, q, k, v, 0.0, mode, out=out, lse=lse, plan=plan), m, b,
+              flops=m * H * FLOPS_GT(D))]
 
     def cpu(budget_s):
         import oracle
@@ -368,7 +389,7 @@ def wl_gt(args, mode="csr"):
         comp += (8 * st["wsb_windows"] + 48 * st["wsb_blocks"] + 4 * st["wsb_dense_tiles"]
                  + 4 * (n + 1) + 4 * st["wsb_residual_edges"])
     return {"ops": ops, "dominant": "gt", "kernel": kern, "config": cfg, "dtype": "bf16", "cpu": cpu,
-            "compulsory": comp,
+            "compulsory": comp, "bound": "alu" if mode == "csr" else "hbm",
             "keep": (w, csr, plan, q, k, v, out, lse)}
 
 
@@ -712,7 +733,8 @@ def wl_gatv2_bwd(args):
     hd, rb = H * D, H * D * 2
     b = (m * (4 + rb) + n * (rb + 12 * hd + 8 * H)              # destination walk
          + m * (4 + rb + 4 * hd + 8 * H) + n * (4 + rb + 4 * hd))  # source walk
-    ops = [Op("gatv2_bwd", lambda: gnn.gnn_gatv2_backward(csr, xl, xr, att, out, lse, dO, 0.2, plan=plan), m, b)]
+    ops = [Op("gatv2_bwd", lambda: gnn.gnn_gatv2_backward(csr, xl, xr, att, out, lse, dO, 0.2, plan=plan), m, b,
+              flops=m * H * FLOPS_GATV2_BWD(D))]
 
     def cpu(budget_s):
         import oracle
@@ -724,7 +746,7 @@ def wl_gatv2_bwd(args):
 
     cfg = {"workload": "gatv2_bwd_" + w.name, "graph": "rmat(0.57,0.19,0.19,0.05)+self-loops", "nodes": n,
            "edges": m, "heads": H, "head_dim": D, "x_dtype": "bf16"}
-    return {"ops": ops, "dominant": "gatv2_bwd", "kernel": "k_att_bwd (both walks)",
+    return {"ops": ops, "dominant": "gatv2_bwd", "kernel": "k_att_bwd (both walks)", "bound": "alu",
             "traffic_kernels": ["k_att_bwd", "k_bwd_combine", "k_da_level"], "config": cfg, "dtype": "bf16",
             "cpu": cpu, "keep": (w, csr, plan, xl, xr, att, out, lse, dO)}
 
@@ -775,7 +797,7 @@ def wl_gt_bwd(args, mode="csr"):
         extra = {"tiles_A": sa["wsb_dense_tiles"], "residual_A": sa["wsb_residual_edges"],
                  "tiles_AT": st["wsb_dense_tiles"], "residual_AT": st["wsb_residual_edges"]}
         fn = lambda: gnn.gnn_gt_backward_block16(csr, q, k, v, out, lse, dO, plan=plan)
-    ops = [Op("gt_bwd" if mode == "csr" else "gt_bwd_b16", fn, m, b)]
+    ops = [Op("gt_bwd" if mode == "csr" else "gt_bwd_b16", fn, m, b, flops=m * H * FLOPS_GT_BWD(D))]
 
     def cpu(budget_s):
         import oracle
@@ -789,7 +811,7 @@ def wl_gt_bwd(args, mode="csr"):
            "graph": "cluster(64, 0.5, 1%)+self-loops", "nodes": n, "edges": m, "heads": H, "head_dim": D,
            "x_dtype": "bf16", "mode": mode, **extra}
     if mode == "csr":
-        return {"ops": ops, "dominant": "gt_bwd", "kernel": "k_att_bwd (both walks)",
+        return {"ops": ops, "dominant": "gt_bwd", "kernel": "k_att_bwd (both walks)", "bound": "alu",
                 "traffic_kernels": ["k_att_bwd", "k_bwd_combine"], "config": cfg, "dtype": "bf16", "cpu": cpu,
                 "keep": (w, csr, plan, q, k, v, out, lse, dO)}
     return {"ops": ops, "dominant": "gt_bwd_b16", "kernel": "k_gt_b16_bwd (both walks)",
@@ -1021,6 +1043,15 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "algorithmic_bytes_per_launch": dom.bytes_alg},
     }
+    if w.get("bound") == "alu" and dom.flops:
+        # ALU-bound kernels (their gathers mostly hit in cache): algorithmic flops over the
+        # launch time against the fp32 vector peak; the byte model is kept beside it
+        tf = dom.flops / (dom_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "kernel": f"{dom.name}: {w['kernel']}", "achieved": tf,
+                           "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / VALU_PEAK_TFLOPS,
+                           "traffic": traffic, "flops_per_launch": dom.flops,
+                           "byte_model": {"algorithmic_bytes_per_launch": dom.bytes_alg, "gbps": achieved,
+                                          "frac_of_hbm_peak": achieved / HBM_PEAK_GBS}}
     if w.get("gathers"):
         # the same step as rates that compare with a one-output aggregation:
         # `value` counts every (output, edge) pair of the fused pass
