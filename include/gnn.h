@@ -66,7 +66,9 @@
  *     without a plan, of plan builds and of reorders) are kept after the
  *     call in a per-device block cache of at most 8 GiB and reused by later
  *     calls, the reusing stream waiting on an event recorded where the block
- *     was last released; gnn_release_cached_memory gives them back.
+ *     was last released; gnn_release_cached_memory gives them back.  Calls
+ *     without a plan therefore allocate, record and wait on events: they are
+ *     not for stream capture (gnn_reduce_multi_noalloc is).
  *     GNN_FAIL_ALLOC=k (or k:tag) in the environment makes the k-th allocation
  *     after the variable took that value fail that way, before any HIP call (a hook for
  *     testing the error paths).
