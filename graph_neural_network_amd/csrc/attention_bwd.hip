@@ -75,7 +75,7 @@ struct BwdParams {
   float slope;       // GATv2 LeakyReLU slope
   // bytes of the gathered arrays when each is below 2^31 (else 0): k / v
   // (rows = sources), q (rows = destinations), dO (fp32, destinations)
-  int32_t kv_bytes, q_bytes, do_bytes;
+  int32_t kv_bytes, q_bytes, do_bytes, lse_bytes;
 };
 
 template <int VEL>
@@ -121,6 +121,8 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
   const __amdgpu_buffer_rsrc_t rv = row_rsrc(p.v, p.kv_bytes);
   const __amdgpu_buffer_rsrc_t rq = row_rsrc(p.q, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rd = row_rsrc(p.dout, p.do_bytes);
+  const __amdgpu_buffer_rsrc_t rl = row_rsrc(p.lse, p.lse_bytes);
+  const __amdgpu_buffer_rsrc_t rdl = row_rsrc(p.delta, p.lse_bytes);
   for (int e0 = eb; e0 < ee; e0 += LPE) {
     const int nb = min(LPE, ee - e0);
     const int my_c = (sl < nb) ? p.col_idx[e0 + sl] : 0;
@@ -156,10 +158,10 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
                                         (uint32_t)c[u] * (uint32_t)(ld * 4), gr);
 #pragma unroll
               for (int k = 0; k < VEL; ++k) g[u][k] = __uint_as_float(gr.u[k]);
-              const float lc = p.lse[(int64_t)c[u] * p.H + head];
-              const float dc = p.delta[(int64_t)c[u] * p.H + head];
-              Lc[u] = ok ? lc * kLog2e : 0.0f;
-              Dc[u] = ok ? dc : 0.0f;
+              // the destination's (L, Delta) of this lane's head, zero past the end
+              const uint32_t ho = ok ? (uint32_t)(head * 4) : 0x80000000u, hs = (uint32_t)c[u] * (uint32_t)(p.H * 4);
+              Lc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, ho, hs, 0)) * kLog2e;
+              Dc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdl, ho, hs, 0));
             }
           }
           goto gathered;
@@ -622,6 +624,8 @@ void set_gather_bytes(const gnn_plan* pl, gnn_dtype xt, BwdParams& p) {
   p.kv_bytes = kv < lim ? (int32_t)kv : 0;
   p.q_bytes = q < lim ? (int32_t)q : 0;
   p.do_bytes = d < lim ? (int32_t)d : 0;
+  // (L, Delta) [n_rows, H] are smaller than dO: valid whenever dO's size is
+  p.lse_bytes = p.do_bytes > 0 ? (int32_t)((int64_t)pl->n_rows * p.H * 4) : 0;
 }
 
 }  // namespace
