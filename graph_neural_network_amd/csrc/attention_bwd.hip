@@ -160,7 +160,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
               for (int k = 0; k < VEL; ++k) g[u][k] = __uint_as_float(gr.u[k]);
               // the destination's (L, Delta) of this lane's head, zero past the end
               const uint32_t ho = ok ? (uint32_t)(head * 4) : 0x80000000u, hs = (uint32_t)c[u] * (uint32_t)(p.H * 4);
-              Lc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, ho, hs, 0)) * kLog2e;
+              Lc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, ho, hs, 0));
               Dc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdl, ho, hs, 0));
             }
           }
@@ -189,7 +189,7 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           if (ok) {
             load_raw<T, NV>(row_at(reinterpret_cast<const T*>(p.q) + o, c[u], rb), x[u]);
             load_f32<VEL>(row_at(p.dout + o, c[u], rb4), g[u]);
-            Lc[u] = p.lse[(int64_t)c[u] * p.H + head] * kLog2e;
+            Lc[u] = p.lse[(int64_t)c[u] * p.H + head];
             Dc[u] = p.delta[(int64_t)c[u] * p.H + head];
           } else {
 #pragma unroll
@@ -239,7 +239,10 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           for (int k = 0; k < VEL; ++k) gv = fmaf(g[u][k], R.f0[k], gv);
           dot = head_sum<LPH>(dot);
           gv = head_sum<LPH>(gv);
-          const float al = valid ? ex2(dot * sc2 - Lc[u]) : 0.0f;
+          // L in natural-log units, scaled where it is used (its load need not
+          // have arrived before the batch's first products).  An entry past the
+          // slot's end has zero q, dO, L and Delta, so it adds nothing.
+          const float al = ex2(fmaf(dot, p.scale, -Lc[u]) * kLog2e);
           const float w = p.scale * al * (gv - Dc[u]);
 #pragma unroll
           for (int k = 0; k < VEL; ++k) {
@@ -275,7 +278,8 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
           }
           e = head_sum<LPH>(e);
           gv = head_sum<LPH>(gv);
-          const float al = valid ? ex2(e * kLog2e - Lc[u]) : 0.0f;
+          // as in the GT source walk: past the slot's end every term is zero
+          const float al = ex2((e - Lc[u]) * kLog2e);
           const float de = al * (gv - Dc[u]);
           R.sde += de;
 #pragma unroll
