@@ -107,7 +107,14 @@ struct Row {
   float L2 = 0.0f;    // dst: L_i * log2 e
   float delta = 0.0f; // dst: Delta_i
   float acc0[VEL], acc1[VEL];
+  // GT destination walk with bf16 rows: dO_i split into bf16 pairs hi + lo
+  // (dO - hi - lo is below 2^-16 |dO|), so that dO_i . v_j takes dot2 steps
+  uint32_t dhi[VEL / 2], dlo[VEL / 2];
 };
+
+__device__ __forceinline__ uint32_t pack_bf16x2(__bf16 a, __bf16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
 
 // Work on entries [eb, ee) of walk row `row` for one slot (LPE lanes).
 template <typename T, int LPE, int NV, int KIND, int LPH>
@@ -216,8 +223,18 @@ __device__ __forceinline__ void scan(const BwdParams& p, int eb, int ee, int sl,
 #pragma unroll
             for (int k = 0; k < VEL; ++k) dot = fmaf(elem<T, NV>(R.own, k), elem<T, NV>(x[u], k), dot);
           }
+          if constexpr (sizeof(T) == 2) {
 #pragma unroll
-          for (int k = 0; k < VEL; ++k) gv = fmaf(R.f0[k], elem<T, NV>(y[u], k), gv);
+            for (int t = 0; t < 4 * NV; ++t) {
+              gv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, R.dhi[t]),
+                                                   __builtin_bit_cast(bf16x2_t, y[u].u[t]), gv, false);
+              gv = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, R.dlo[t]),
+                                                   __builtin_bit_cast(bf16x2_t, y[u].u[t]), gv, false);
+            }
+          } else {
+#pragma unroll
+            for (int k = 0; k < VEL; ++k) gv = fmaf(R.f0[k], elem<T, NV>(y[u], k), gv);
+          }
           dot = head_sum<LPH>(dot);
           gv = head_sum<LPH>(gv);
           const float al = valid ? ex2(dot * sc2 - R.L2) : 0.0f;
@@ -340,6 +357,8 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
 #pragma unroll
   for (int k = 0; k < VEL; ++k) R.acc0[k] = R.acc1[k] = R.av[k] = R.an[k] = R.f0[k] = R.f1[k] = 0.0f;
 #pragma unroll
+  for (int k = 0; k < VEL / 2; ++k) R.dhi[k] = R.dlo[k] = 0u;  // lanes without data join the head sums
+#pragma unroll
   for (int t = 0; t < 4 * NV; ++t) R.own.u[t] = 0u;
   const int64_t ro = row * (int64_t)p.row_elems + loff;
   if (active && d_ok) {
@@ -351,6 +370,15 @@ __global__ __launch_bounds__(WG) void k_att_bwd(BwdParams p) {
 #pragma unroll
       for (int k = 0; k < VEL; ++k) t = fmaf(R.f0[k], o[k], t);
       R.delta = t;
+      if constexpr (KIND == B_GT_DST && sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < VEL / 2; ++q) {
+          const float a = R.f0[2 * q], b = R.f0[2 * q + 1];
+          const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+          R.dhi[q] = pack_bf16x2(ha, hb);
+          R.dlo[q] = pack_bf16x2((__bf16)(a - (float)ha), (__bf16)(b - (float)hb));
+        }
+      }
       R.L2 = p.lse[row * p.H + head] * kLog2e;
       if constexpr (KIND == B_GT_DST) load_raw<T, NV>(reinterpret_cast<const T*>(p.q) + ro, R.own);
       else {
