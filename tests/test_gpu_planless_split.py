@@ -234,3 +234,39 @@ def test_block_cache_reuse_across_streams(graph):
     torch.cuda.synchronize()
     for out in outs:
         _equal([out[k] for k in sorted(ref)], [ref[k] for k in sorted(ref)])
+
+
+def test_block_cache_two_host_threads(graph):
+    """Two host threads make calls without a plan on their own streams at the
+    same time: the block cache hands a block to one call at a time, and every
+    result stays exact."""
+    import threading
+    rp, ci = graph
+    n = rp.size - 1
+    csr = dev_csr(rp, ci)
+    X = dev(gen.gauss_f32(0xFEA70906, (n, 64)))
+    ref = gnn.gnn_reduce_multi(csr, X, plan=gnn.gnn_plan_create(csr, **SAME_RULE))
+    torch.cuda.synchronize()
+    results, errors = {0: [], 1: []}, []
+
+    def work(tid):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                for _ in range(8):
+                    results[tid].append(gnn.gnn_reduce_multi(csr, X, stream=st))
+            st.synchronize()
+        except Exception as e:  # reported below, on the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in (0, 1)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for tid in (0, 1):
+        assert len(results[tid]) == 8
+        for out in results[tid]:
+            _equal([out[k] for k in sorted(ref)], [ref[k] for k in sorted(ref)])
