@@ -221,7 +221,9 @@ __device__ __forceinline__ float edge_weight(const AggParams& p, int e, int j) {
 }
 
 __device__ __forceinline__ float row_factor(const AggParams& p, float acc, int deg) {
-  if (p.norm == GNN_NORM_LEFT) return deg > 0 ? acc / (float)deg : 0.0f;
+  // the mean as a product with the rounded reciprocal of the degree (one
+  // division per row, within an ulp of the quotient), the same in every path
+  if (p.norm == GNN_NORM_LEFT) return deg > 0 ? acc * (1.0f / (float)deg) : 0.0f;
   if (p.norm == GNN_NORM_BOTH) return deg > 0 ? acc * rsqrtf((float)deg) : 0.0f;
   return acc;
 }
@@ -342,7 +344,7 @@ __device__ __forceinline__ void finish_row(const AggParams& p, int row, int deg,
     }
     if (p.Ymean) {
 #pragma unroll
-      for (int v = 0; v < VE; ++v) o[v] = deg > 0 ? st.acc[v] / (float)deg : 0.0f;
+      for (int v = 0; v < VE; ++v) o[v] = deg > 0 ? st.acc[v] * (1.0f / (float)deg) : 0.0f;
       put_tile<LPR, VE>(p.Ymean + oy, o, sl, nvalid, stage);
     }
     if (p.Ymax) {
@@ -468,7 +470,7 @@ __global__ __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(sizeof(T) ==
           const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
           if (m < 0) {
             if (p.Y) __builtin_nontemporal_store(a, p.Y + oy);
-            if (p.Ymean) __builtin_nontemporal_store(a / (float)len, p.Ymean + oy);
+            if (p.Ymean) __builtin_nontemporal_store(a * (1.0f / (float)len), p.Ymean + oy);
             if (p.Ymax) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w >> 32)), p.Ymax + oy);
             if (p.argmax) __builtin_nontemporal_store((int)~(uint32_t)w, p.argmax + oa);
             if (p.Ymin) __builtin_nontemporal_store(dev::key_to_float((uint32_t)(w2 >> 32)), p.Ymin + oy);
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(256) void k_combine_all(AggParams p, const int4* mu
     for (int c = 0; c < cnt; ++c) a += p.partial[(int64_t)(first + c) * p.F + f];
     const int64_t oy = (int64_t)row * p.ldy + f, oa = (int64_t)row * p.F + f;
     if (p.Y) p.Y[oy] = a;
-    if (p.Ymean) p.Ymean[oy] = a / (float)deg;
+    if (p.Ymean) p.Ymean[oy] = a * (1.0f / (float)deg);
     const unsigned long long w = p.packed[(int64_t)blockIdx.x * p.F + f];
     const unsigned long long w2 = p.packed2[(int64_t)blockIdx.x * p.F + f];
     if (p.Ymax) p.Ymax[oy] = dev::key_to_float((uint32_t)(w >> 32));

@@ -318,7 +318,8 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_to_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  // sign bit set: clear it; otherwise flip every bit
+  return __uint_as_float(k ^ (~(uint32_t)((int32_t)k >> 31) | 0x80000000u));
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs of an MI355X; this
