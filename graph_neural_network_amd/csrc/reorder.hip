@@ -21,8 +21,8 @@
 // Level-synchronous form computed here, which yields exactly that order:
 //   - rank(v) = position of v in the global (delta, id) order; adjacency lists
 //     sorted by rank;
-//   - component label = smallest rank in the component (min-label
-//     propagation with shortcutting);
+//   - component label = smallest rank in the component (union-find over
+//     ranks, each root hooked under the smaller one);
 //   - all components advance together, one BFS level per step: every
 //     unvisited neighbour of level L is claimed by its earliest parent
 //     (atomicMin of the parent's position in level L) and emitted in the
@@ -175,46 +175,64 @@ __global__ void k_adj_from_keys(const uint64_t* keys, const int32_t* order, int6
   adj[e] = order[keys[e] & ((1ull << idbits) - 1)];
 }
 
-// min-label propagation over edges, then shortcutting through the label's vertex
-// adj_row is sorted, so the entries of one row are consecutive lanes: a
-// segmented minimum over the wave leaves each row's smallest neighbour label
-// in the row's first lane, which alone updates the row's label (hub rows
-// would otherwise take one contended atomic per entry).  One store of the
-// `changed` flag per wave.
-__global__ void k_label_edges(const int32_t* adj, const int32_t* adj_row, int64_t m, int32_t* label,
-                              int32_t* changed) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  const bool ok = e < m;
-  const int a = ok ? adj_row[e] : -1;
-  int lb = ok ? label[adj[e]] : 0x7FFFFFFF;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int a2 = __shfl_down(a, o, 64);
-    const int l2 = __shfl_down(lb, o, 64);
-    if (lane + o < 64 && a2 == a) lb = min(lb, l2);
-  }
-  const int a_prev = __shfl_up(a, 1, 64);
-  bool ch = false;
-  if (ok && (lane == 0 || a_prev != a) && lb < label[a]) {
-    atomicMin(&label[a], lb);
-    ch = true;
-  }
-  if (__ballot(ch) && lane == 0) *changed = 1;
+// ---- component labels: union-find over ranks ----
+// P[r] is the parent of rank r, a root its own parent.  A hook only attaches
+// a root under a smaller root, so every parent is smaller than its child, a
+// tree's root is its smallest rank (the component's label) and every walk up
+// a tree ends.  Parents are read with agent-scope atomic loads (past the
+// per-CU cache); a stale read costs only a failed compare-and-swap, which
+// returns the current parent to retry from.
+__device__ __forceinline__ int uf_parent(const int32_t* P, int x) {
+  return __hip_atomic_load(P + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void k_label_jump(const int32_t* order, int32_t n, int32_t* label, int32_t* changed) {
-  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  bool ch = false;
-  if (v < n) {
-    const int l = label[v];
-    const int l2 = label[order[l]];
-    if (l2 < l) {
-      atomicMin(&label[v], l2);
-      ch = true;
-    }
+// Root of x, re-pointing each visited node to its grandparent (path halving):
+// the grandparent is an ancestor in the same tree and smaller than the
+// parent, so concurrent walks and hooks keep every tree valid.
+__device__ int uf_root(int32_t* P, int x) {
+  for (;;) {
+    const int p = uf_parent(P, x);
+    if (p == x) return x;
+    const int g = uf_parent(P, p);
+    if (g == p) return p;
+    __hip_atomic_store(P + x, g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    x = g;
   }
-  if (__ballot(ch) && (threadIdx.x & 63) == 0) *changed = 1;
+}
+
+__global__ void k_iota(int32_t* p, int32_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = (int32_t)i;
+}
+
+// One hook per undirected edge (the symmetrised pattern holds both
+// directions; the one with row < column is taken).  A failed swap means the
+// larger root was attached elsewhere meanwhile: the larger of the two roots
+// strictly decreases with every retry.
+__global__ void k_cc_hook(const int32_t* adj, const int32_t* adj_row, const int32_t* rank, int64_t m,
+                          int32_t* P) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  const int u = adj_row[e], v = adj[e];
+  if (u >= v) return;
+  int a = uf_root(P, rank[u]);
+  int b = uf_root(P, rank[v]);
+  while (a != b) {
+    if (a < b) {
+      const int t = a;
+      a = b;
+      b = t;
+    }
+    const int old = atomicCAS(P + a, a, b);
+    if (old == a) return;
+    a = uf_root(P, old);
+    b = uf_root(P, b);
+  }
+}
+
+__global__ void k_cc_label(const int32_t* rank, int32_t n, int32_t* P, int32_t* label) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < n) label[v] = uf_root(P, rank[v]);
 }
 
 __global__ void k_start_flags(const int32_t* order, const int32_t* label, int32_t n, int32_t* flag) {
@@ -337,13 +355,13 @@ int degree_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
 
 // Temporaries of rcm_perm: two flag / offset slabs of 2 nnz + 1 entries
 // (loop flags, then duplicate flags, then frontier-edge flags, each with its
-// scan), two key arrays, the symmetrised adjacency with its row ids, ten
+// scan), two key arrays, the symmetrised adjacency with its row ids, nine
 // per-vertex arrays, and scan / sort scratch.
 size_t rcm_bytes(int32_t n, int64_t nnz) {
   const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
   size_t b = 2 * Arena::round((size_t)(M2 + 1) * 4) + 2 * Arena::round((size_t)NN * 8) +
              2 * Arena::round((size_t)M2 * 4) + 3 * Arena::round((size_t)(n + 1) * 4) +
-             6 * Arena::round((size_t)n * 4) + Arena::round(4);
+             6 * Arena::round((size_t)n * 4);
   return b + std::max(scan_scratch_bytes(NN + 1), radix_scratch_bytes(NN));
 }
 
@@ -368,7 +386,6 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   int32_t* concat = ar.take<int32_t>(n);
   int32_t* visited = ar.take<int32_t>(n);
   int32_t* claim = ar.take<int32_t>(n);
-  int32_t* changed = ar.take<int32_t>(1);
   void* ws = ar.base + ar.off;  // scan and sort scratch
 
   // 1. symmetrised pattern without loops, as sorted unique (row, col) keys
@@ -422,21 +439,18 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     GNN_LAUNCH_CHECK("rcm adj sort");
   }
 
-  // 4. component labels: smallest rank in the component
-  GNN_HIP(hipMemcpyAsync(label, rank, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
-  for (int it = 0;; ++it) {
-    int32_t ch = 0;
-    GNN_HIP(hipMemsetAsync(changed, 0, 4, s));
+  // 4. component labels: smallest rank in the component, by union-find over
+  // ranks (the claim array holds the parents until the BFS)
+  {
+    int32_t* P = claim;
+    hipLaunchKernelGGL(k_iota, dim3(nb(n)), dim3(256), 0, s, P, n);
+    GNN_LAUNCH_CHECK("rcm parents");
     if (m > 0) {
-      hipLaunchKernelGGL(k_label_edges, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, m, label, changed);
-      GNN_LAUNCH_CHECK("rcm labels");
+      hipLaunchKernelGGL(k_cc_hook, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, m, P);
+      GNN_LAUNCH_CHECK("rcm hooks");
     }
-    hipLaunchKernelGGL(k_label_jump, dim3(nb(n)), dim3(256), 0, s, order, n, label, changed);
-    GNN_LAUNCH_CHECK("rcm label jump");
-    GNN_HIP(hipMemcpyAsync(&ch, changed, 4, hipMemcpyDeviceToHost, s));
-    GNN_HIP(hipStreamSynchronize(s));
-    if (!ch) break;
-    if (it > n + 2) return fail(GNN_ERR_DEVICE, "RCM: label propagation did not converge");
+    hipLaunchKernelGGL(k_cc_label, dim3(nb(n)), dim3(256), 0, s, rank, n, P, label);
+    GNN_LAUNCH_CHECK("rcm labels");
   }
 
   // 5. level-synchronous BFS of all components at once

@@ -2,7 +2,8 @@
 // the preprocessing steps (WSB column lists, degree order, RCM levels).
 //
 // One pass per digit: (1) each workgroup counts the digits of its tile of
-// 4096 keys; (2) an exclusive scan over the digit-major count table gives
+// 4096 keys (one LDS histogram per wave: plain LDS atomics measured faster
+// than matching equal digits with ballots first); (2) an exclusive scan over the digit-major count table gives
 // every (digit, tile) its output offset; (3) each workgroup sorts its tile by
 // the digit in LDS and writes every digit's keys as one contiguous run.
 // In (3) each wave ranks a contiguous quarter of the tile in rounds of 64
@@ -48,23 +49,28 @@ __device__ __forceinline__ void wave_sync_lds() {
 
 __global__ __launch_bounds__(RT) void k_rs_hist(const uint64_t* keys, int64_t n, int shift,
                                                 int32_t* hist, int32_t ntiles) {
-  __shared__ int32_t h[256];
-  h[threadIdx.x] = 0;
+  __shared__ int32_t h[NW][256];
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) h[w][threadIdx.x] = 0;
   __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const int64_t base = (int64_t)blockIdx.x * RTILE;
+  uint64_t kv[RI];
+#pragma unroll
   for (int r = 0; r < RI; ++r) {
     const int64_t i = base + (int64_t)r * RT + threadIdx.x;
-    const bool ok = i < n;
-    const int d = ok ? (int)((keys[i] >> shift) & 0xFF) : 256;
-    // one LDS atomic per distinct digit of the wave (skewed digits would
-    // otherwise serialise up to 64 atomics on one word)
-    const unsigned long long peers = digit_peers(ok, d);
-    if (ok && (peers & lt) == 0) atomicAdd(&h[d], __popcll(peers));
+    kv[r] = i < n ? keys[i] : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < RI; ++r) {
+    const int64_t i = base + (int64_t)r * RT + threadIdx.x;
+    if (i < n) atomicAdd(&h[wave][(kv[r] >> shift) & 0xFF], 1);
   }
   __syncthreads();
-  hist[(int64_t)threadIdx.x * ntiles + blockIdx.x] = h[threadIdx.x];
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) t += h[w][threadIdx.x];
+  hist[(int64_t)threadIdx.x * ntiles + blockIdx.x] = t;
 }
 
 __global__ __launch_bounds__(RT) void k_rs_scatter(const uint64_t* keys, uint64_t* out, int64_t n,
