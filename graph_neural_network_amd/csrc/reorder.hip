@@ -45,21 +45,77 @@ int bits_for(int64_t v) {
   return b;
 }
 
-__device__ __forceinline__ int row_of(const int32_t* row_ptr, int32_t n, int64_t e) {
-  int lo = 0, hi = n - 1;
+// ---- segment of an entry ----
+// Kernels over the entries of a segmented array (CSR rows, a frontier's
+// flattened adjacency) need each entry's segment: the largest k with
+// ptr[k] <= e.  A workgroup takes kSegSpan consecutive entries, finds the
+// segments of its first and last entry in global memory once, stages the
+// offsets between them in LDS and searches there (entries are not looked up
+// one by one across the whole offset array: that is ~24 dependent loads on a
+// 16M-row graph).  A span over more than kSegCap segments (many empty ones)
+// searches global memory, bounded by the same two segments.
+constexpr int kSegEPT = 8;              // entries per thread
+constexpr int kSegSpan = 256 * kSegEPT; // entries per workgroup of 256
+constexpr int kSegCap = 4096;           // staged offsets
+
+unsigned nb_seg(int64_t n) { return (unsigned)((n + kSegSpan - 1) / kSegSpan); }
+
+// largest k in [lo, hi] with ptr[k] <= e, given ptr[lo] <= e
+__device__ __forceinline__ int seg_search(const int32_t* ptr, int lo, int hi, int64_t e) {
   while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (row_ptr[mid] <= e) lo = mid;
+    const int mid = (lo + hi + 1) >> 1;
+    if (ptr[mid] <= e) lo = mid;
     else hi = mid - 1;
   }
   return lo;
 }
 
-__global__ void k_max_deg(const int32_t* row_ptr, int32_t n, int32_t* out) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  int d = i < n ? row_ptr[i + 1] - row_ptr[i] : 0;
+// This workgroup's entries [e0, e1] (of n) and their segments [r0, r1] (of
+// nseg); the offsets ptr[r0 .. r1] are staged in s_ptr when they fit.
+struct SegSpan {
+  int64_t e0, e1;
+  int r0, r1;
+};
+
+// Called by every thread of the workgroup (s_r: two words of LDS).
+__device__ __forceinline__ SegSpan seg_stage(const int32_t* ptr, int32_t nseg, int64_t n, int32_t* s_ptr,
+                                             int32_t* s_r) {
+  SegSpan sp;
+  sp.e0 = (int64_t)blockIdx.x * kSegSpan;
+  sp.e1 = min(n, sp.e0 + kSegSpan) - 1;
+  if (threadIdx.x < 2) s_r[threadIdx.x] = seg_search(ptr, 0, nseg - 1, threadIdx.x == 0 ? sp.e0 : sp.e1);
+  __syncthreads();
+  sp.r0 = s_r[0];
+  sp.r1 = s_r[1];
+  const int cnt = sp.r1 - sp.r0 + 1;
+  if (cnt <= kSegCap)
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) s_ptr[i] = ptr[sp.r0 + i];
+  __syncthreads();
+  return sp;
+}
+
+// j-th entry of this thread in the span (-1 past its end)
+__device__ __forceinline__ int64_t seg_entry(const SegSpan& sp, int j) {
+  const int64_t e = sp.e0 + (int64_t)j * blockDim.x + threadIdx.x;
+  return e <= sp.e1 ? e : -1;
+}
+
+__device__ __forceinline__ int seg_find(const int32_t* ptr, const int32_t* s_ptr, const SegSpan& sp, int64_t e) {
+  if (sp.r1 - sp.r0 + 1 > kSegCap) return seg_search(ptr, sp.r0, sp.r1, e);
+  return sp.r0 + seg_search(s_ptr, 0, sp.r1 - sp.r0, e);
+}
+
+// Largest row length: a grid-stride walk, one atomic per workgroup (one per
+// wave serialises 250k atomics on one word for a 16M-row graph).
+__global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t n, int32_t* out) {
+  __shared__ int32_t s_m[4];
+  int d = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    d = max(d, row_ptr[i + 1] - row_ptr[i]);
   for (int o = 32; o >= 1; o >>= 1) d = max(d, __shfl_xor(d, o));
-  if ((threadIdx.x & 63) == 0) atomicMax(out, d);
+  if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = d;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(out, max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3])));
 }
 
 __global__ void k_deg_keys(const int32_t* row_ptr, int32_t n, int32_t maxdeg, int idbits,
@@ -89,33 +145,51 @@ __global__ void k_new_deg(const int32_t* row_ptr, const int32_t* perm, int32_t n
 }
 
 // key = (new row << colbits) | new column, for every entry of P A P^T
-__global__ void k_perm_keys(const int32_t* row_ptr, const int32_t* col_idx, const int32_t* perm,
-                            const int32_t* inv, const int32_t* new_ptr, int32_t n, int64_t nnz,
-                            int colbits, uint64_t* keys) {
-  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= nnz) return;
-  const int p = row_of(new_ptr, n, q);
-  const int64_t old_e = row_ptr[perm[p]] + (q - new_ptr[p]);
-  keys[q] = ((uint64_t)p << colbits) | (uint32_t)inv[col_idx[old_e]];
+__global__ __launch_bounds__(256) void k_perm_keys(const int32_t* row_ptr, const int32_t* col_idx,
+                                                   const int32_t* perm, const int32_t* inv,
+                                                   const int32_t* new_ptr, int32_t n, int64_t nnz,
+                                                   int colbits, uint64_t* keys) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(new_ptr, n, nnz, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t q = seg_entry(sp, j);
+    if (q < 0) break;
+    const int p = seg_find(new_ptr, s_ptr, sp, q);
+    const int64_t old_e = row_ptr[perm[p]] + (q - new_ptr[p]);
+    keys[q] = ((uint64_t)p << colbits) | (uint32_t)inv[col_idx[old_e]];
+  }
 }
 
 // ---- RCM ----
 
 // both directions of every non-loop edge (compacted by a scan of flags)
-__global__ void k_loop_flags(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
-                             int32_t* flag) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz) return;
-  flag[e] = (col_idx[e] != row_of(row_ptr, n, e)) ? 1 : 0;
+__global__ __launch_bounds__(256) void k_loop_flags(const int32_t* row_ptr, const int32_t* col_idx,
+                                                    int32_t n, int64_t nnz, int32_t* flag) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t e = seg_entry(sp, j);
+    if (e < 0) break;
+    flag[e] = (col_idx[e] != seg_find(row_ptr, s_ptr, sp, e)) ? 1 : 0;
+  }
 }
 
-__global__ void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx, int32_t n, int64_t nnz,
-                           const int32_t* flag, const int32_t* pos, int idbits, uint64_t* keys) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nnz || !flag[e]) return;
-  const uint64_t i = (uint64_t)row_of(row_ptr, n, e), j = (uint64_t)col_idx[e];
-  keys[2 * (int64_t)pos[e]] = (i << idbits) | j;
-  keys[2 * (int64_t)pos[e] + 1] = (j << idbits) | i;
+__global__ __launch_bounds__(256) void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx,
+                                                  int32_t n, int64_t nnz, const int32_t* flag,
+                                                  const int32_t* pos, int idbits, uint64_t* keys) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t e = seg_entry(sp, j);
+    if (e < 0) break;
+    if (!flag[e]) continue;
+    const uint64_t i = (uint64_t)seg_find(row_ptr, s_ptr, sp, e), c = (uint64_t)col_idx[e];
+    keys[2 * (int64_t)pos[e]] = (i << idbits) | c;
+    keys[2 * (int64_t)pos[e] + 1] = (c << idbits) | i;
+  }
 }
 
 __global__ void k_uniq_flags(const uint64_t* keys, int64_t m, int32_t* flag) {
@@ -261,43 +335,50 @@ __global__ void k_front_deg(const int32_t* front, int32_t f, const int32_t* sym_
   if (k < f) deg[k] = sym_ptr[front[k] + 1] - sym_ptr[front[k]];
 }
 
-__device__ __forceinline__ int front_of(const int32_t* eoff, int32_t f, int64_t q) {
-  int lo = 0, hi = f - 1;  // largest k with eoff[k] <= q
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (eoff[mid] <= q) lo = mid;
-    else hi = mid - 1;
+__global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, const int32_t* eoff,
+                                               int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
+                                               const int32_t* visited, int32_t* claim) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t q = seg_entry(sp, j);
+    if (q < 0) break;
+    const int k = seg_find(eoff, s_ptr, sp, q);
+    const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
+    if (!visited[w]) atomicMin(&claim[w], k);
   }
-  return lo;
 }
 
-__global__ void k_claim(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
-                        const int32_t* sym_ptr, const int32_t* adj, const int32_t* visited,
-                        int32_t* claim) {
-  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= ef) return;
-  const int k = front_of(eoff, f, q);
-  const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
-  if (!visited[w]) atomicMin(&claim[w], k);
+__global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32_t f, const int32_t* eoff,
+                                                     int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
+                                                     const int32_t* visited, const int32_t* claim,
+                                                     int32_t* flag) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t q = seg_entry(sp, j);
+    if (q < 0) break;
+    const int k = seg_find(eoff, s_ptr, sp, q);
+    const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
+    flag[q] = (!visited[w] && claim[w] == k) ? 1 : 0;
+  }
 }
 
-__global__ void k_child_flags(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
-                              const int32_t* sym_ptr, const int32_t* adj, const int32_t* visited,
-                              const int32_t* claim, int32_t* flag) {
-  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= ef) return;
-  const int k = front_of(eoff, f, q);
-  const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
-  flag[q] = (!visited[w] && claim[w] == k) ? 1 : 0;
-}
-
-__global__ void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff, int64_t ef,
-                             const int32_t* sym_ptr, const int32_t* adj, const int32_t* flag,
-                             const int32_t* pos, int32_t* next) {
-  int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= ef || !flag[q]) return;
-  const int k = front_of(eoff, f, q);
-  next[pos[q]] = adj[sym_ptr[front[k]] + (q - eoff[k])];
+__global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff,
+                                                    int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
+                                                    const int32_t* flag, const int32_t* pos, int32_t* next) {
+  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t q = seg_entry(sp, j);
+    if (q < 0) break;
+    if (!flag[q]) continue;
+    const int k = seg_find(eoff, s_ptr, sp, q);
+    next[pos[q]] = adj[sym_ptr[front[k]] + (q - eoff[k])];
+  }
 }
 
 __global__ void k_mark(const int32_t* next, int32_t f, int32_t* visited) {
@@ -337,7 +418,7 @@ int degree_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   uint64_t* tmp = ar.take<uint64_t>(n);
   void* ws = ar.base + ar.off;
   GNN_HIP(hipMemsetAsync(mx, 0, 4, s));
-  hipLaunchKernelGGL(k_max_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, n, mx);
+  hipLaunchKernelGGL(k_max_deg, dim3(std::min<unsigned>(nb(n), 2048)), dim3(256), 0, s, c->row_ptr, n, mx);
   GNN_LAUNCH_CHECK("max degree");
   int32_t maxdeg = 0;
   GNN_HIP(hipMemcpyAsync(&maxdeg, mx, 4, hipMemcpyDeviceToHost, s));
@@ -391,7 +472,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   // 1. symmetrised pattern without loops, as sorted unique (row, col) keys
   int32_t *flag = slab0, *pos = slab1;
   if (nnz > 0) {
-    hipLaunchKernelGGL(k_loop_flags, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag);
+    hipLaunchKernelGGL(k_loop_flags, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag);
     GNN_LAUNCH_CHECK("rcm loop flags");
   }
   GNN_TRY(exclusive_scan_i32(flag, pos, nnz, s, ws));
@@ -401,7 +482,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   const int64_t m2 = 2 * (int64_t)nl;
   if (m2 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM: symmetrised pattern too large");
   if (nnz > 0) {
-    hipLaunchKernelGGL(k_sym_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag,
+    hipLaunchKernelGGL(k_sym_keys, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag,
                        pos, idbits, keys);
     GNN_LAUNCH_CHECK("rcm sym keys");
   }
@@ -482,9 +563,9 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     if (ef < 0 || ef > m) return fail(GNN_ERR_DEVICE, "RCM: frontier adjacency larger than the graph");
     int32_t nf = 0;
     if (ef > 0) {
-      hipLaunchKernelGGL(k_claim, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
+      hipLaunchKernelGGL(k_claim, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
                          adj, visited, claim);
-      hipLaunchKernelGGL(k_child_flags, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
+      hipLaunchKernelGGL(k_child_flags, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
                          sym_ptr, adj, visited, claim, qflag);
       GNN_LAUNCH_CHECK("rcm level flags");
       GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s, ws));
@@ -493,7 +574,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     }
     if (nf < 0 || base + f + nf > n) return fail(GNN_ERR_DEVICE, "RCM: level larger than the graph");
     if (nf > 0) {
-      hipLaunchKernelGGL(k_child_emit, dim3(nb(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
+      hipLaunchKernelGGL(k_child_emit, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
                          sym_ptr, adj, qflag, qpos, next);
       GNN_LAUNCH_CHECK("rcm level emit");
       hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, visited);
@@ -534,7 +615,7 @@ int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t*
   GNN_TRY(exclusive_scan_i32(deg, rp_out, n, s, ws));
   if (nnz > 0) {
     const int colbits = bits_for(n);
-    hipLaunchKernelGGL(k_perm_keys, dim3(nb(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
+    hipLaunchKernelGGL(k_perm_keys, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
                        rp_out, n, nnz, colbits, keys);
     GNN_LAUNCH_CHECK("permute keys");
     GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, 2 * colbits, s, ws));
