@@ -71,7 +71,8 @@ __device__ __forceinline__ int seg_search(const int32_t* ptr, int lo, int hi, in
 }
 
 // This workgroup's entries [e0, e1] (of n) and their segments [r0, r1] (of
-// nseg); the offsets ptr[r0 .. r1] are staged in s_ptr when they fit.
+// nseg); the offsets ptr[r0 .. r1 + 1] are staged in s_ptr (kSegCap + 1
+// words) when r1 - r0 < kSegCap.
 struct SegSpan {
   int64_t e0, e1;
   int r0, r1;
@@ -89,7 +90,7 @@ __device__ __forceinline__ SegSpan seg_stage(const int32_t* ptr, int32_t nseg, i
   sp.r1 = s_r[1];
   const int cnt = sp.r1 - sp.r0 + 1;
   if (cnt <= kSegCap)
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) s_ptr[i] = ptr[sp.r0 + i];
+    for (int i = threadIdx.x; i <= cnt; i += blockDim.x) s_ptr[i] = ptr[sp.r0 + i];
   __syncthreads();
   return sp;
 }
@@ -105,6 +106,11 @@ __device__ __forceinline__ int seg_find(const int32_t* ptr, const int32_t* s_ptr
   return sp.r0 + seg_search(s_ptr, 0, sp.r1 - sp.r0, e);
 }
 
+// ptr[k] for k in [r0, r1 + 1]
+__device__ __forceinline__ int seg_at(const int32_t* ptr, const int32_t* s_ptr, const SegSpan& sp, int k) {
+  return sp.r1 - sp.r0 + 1 > kSegCap ? ptr[k] : s_ptr[k - sp.r0];
+}
+
 // Largest row length: a grid-stride walk, one atomic per workgroup (one per
 // wave serialises 250k atomics on one word for a 16M-row graph).
 __global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t n, int32_t* out) {
@@ -116,6 +122,225 @@ __global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t
   if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = d;
   __syncthreads();
   if (threadIdx.x == 0) atomicMax(out, max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3])));
+}
+
+// ---- segmented sort of 32-bit values ----
+// Sorts every segment [ptr[k], ptr[k+1]) of `in` ascending into the same
+// positions of `out` (equal values are interchangeable: their order is not
+// kept).  Four tiers by segment length L:
+//   L <= kSortSmall: each value counts the smaller values of its segment and
+//     the equal ones before it, which is its place;
+//   L <= kSortWave: one wave per segment, bitonic sort in LDS (the four waves
+//     of a workgroup sort four segments, without workgroup barriers);
+//   L <= kSortBlock: one workgroup per segment, bitonic sort in LDS;
+//   longer: (long-segment index, value) keys through the global radix sort,
+//     written back segment by segment.
+// The rows of a CSR or an adjacency are already grouped, so this replaces a
+// radix sort of (row, value) keys over all entries.
+constexpr int kSortSmall = 64;
+constexpr int kSortWave = 1024;
+constexpr int kSortBlock = 4096;
+constexpr int kSortBlocks = 4096;  // workgroups striding over the medium segments
+constexpr int kClassPer = 8;       // segments per thread when classifying
+
+__global__ __launch_bounds__(256) void k_sseg_small(const uint32_t* in, uint32_t* out, const int32_t* ptr,
+                                                    int32_t nseg, int64_t n) {
+  __shared__ int32_t s_ptr[kSegCap + 1];
+  __shared__ int32_t s_r[2];
+  const SegSpan sp = seg_stage(ptr, nseg, n, s_ptr, s_r);
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t e = seg_entry(sp, j);
+    if (e < 0) break;
+    const int k = seg_find(ptr, s_ptr, sp, e);
+    const int b = seg_at(ptr, s_ptr, sp, k);
+    const int len = seg_at(ptr, s_ptr, sp, k + 1) - b;
+    if (len > kSortSmall) continue;
+    const uint32_t x = in[e];
+    const int me = (int)(e - b);
+    int rank = 0;
+    for (int t = 0; t < len; ++t) {
+      const uint32_t y = in[b + t];
+      rank += (y < x || (y == x && t < me)) ? 1 : 0;
+    }
+    out[b + rank] = x;
+  }
+}
+
+// Lists the wave-sorted segments (wmid), the workgroup-sorted ones (mid) and
+// the long ones (big, with lengths); cnt = {mid count, long count, entries of
+// long segments, wmid count}.  Positions in the lists are reserved with one
+// global atomic per list and workgroup.
+__global__ __launch_bounds__(256) void k_sseg_classify(const int32_t* ptr, int32_t nseg, int32_t* mid,
+                                                       int32_t* big, int32_t* big_len, int32_t* wmid,
+                                                       int32_t* cnt) {
+  __shared__ int32_t s_n[3], s_base[3], s_tot;
+  if (threadIdx.x < 3) s_n[threadIdx.x] = 0;
+  if (threadIdx.x == 0) s_tot = 0;
+  __syncthreads();
+  int cls[kClassPer], pos[kClassPer], len[kClassPer];
+  const int64_t k0 = (int64_t)blockIdx.x * 256 * kClassPer + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kClassPer; ++j) {
+    const int64_t k = k0 + (int64_t)j * 256;
+    len[j] = k < nseg ? ptr[k + 1] - ptr[k] : 0;
+    cls[j] = len[j] > kSortBlock ? 2 : (len[j] > kSortWave ? 1 : (len[j] > kSortSmall ? 3 : 0));
+    pos[j] = cls[j] ? atomicAdd(&s_n[cls[j] - 1], 1) : 0;
+    if (cls[j] == 2) atomicAdd(&s_tot, len[j]);
+  }
+  __syncthreads();
+  if (threadIdx.x < 3 && s_n[threadIdx.x] > 0)
+    s_base[threadIdx.x] = atomicAdd(&cnt[threadIdx.x == 2 ? 3 : threadIdx.x], s_n[threadIdx.x]);
+  if (threadIdx.x == 0 && s_tot > 0) atomicAdd(&cnt[2], s_tot);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kClassPer; ++j) {
+    const int k = (int)(k0 + (int64_t)j * 256);
+    if (cls[j] == 1) mid[s_base[0] + pos[j]] = k;
+    if (cls[j] == 2) {
+      big[s_base[1] + pos[j]] = k;
+      big_len[s_base[1] + pos[j]] = len[j];
+    }
+    if (cls[j] == 3) wmid[s_base[2] + pos[j]] = k;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sseg_mid(const uint32_t* in, uint32_t* out, const int32_t* ptr,
+                                                  const int32_t* mid, const int32_t* cnt) {
+  __shared__ uint32_t sv[kSortBlock];
+  const int nmid = cnt[0];
+  for (int i = blockIdx.x; i < nmid; i += gridDim.x) {
+    if (i != (int)blockIdx.x) __syncthreads();  // the previous segment has left LDS
+    const int k = mid[i];
+    const int b = ptr[k], len = ptr[k + 1] - b;
+    int P = 1;
+    while (P < len) P <<= 1;
+    for (int t = threadIdx.x; t < P; t += blockDim.x) sv[t] = t < len ? in[b + t] : 0xFFFFFFFFu;
+    __syncthreads();
+    for (int kk = 2; kk <= P; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int t = threadIdx.x; t < P; t += blockDim.x) {
+          const int u = t ^ jj;
+          if (u > t) {
+            const uint32_t x = sv[t], y = sv[u];
+            if ((x > y) == ((t & kk) == 0)) {
+              sv[t] = y;
+              sv[u] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int t = threadIdx.x; t < len; t += blockDim.x) out[b + t] = sv[t];
+  }
+}
+
+// One segment per wave, waves striding over the list (wave-level
+// synchronisation only: each wave owns its quarter of LDS).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(256) void k_sseg_wave(const uint32_t* in, uint32_t* out, const int32_t* ptr,
+                                                   const int32_t* wmid, const int32_t* cnt) {
+  __shared__ uint32_t sv_all[4][kSortWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t* sv = sv_all[wave];
+  const int nw = cnt[3];
+  for (int i = blockIdx.x * 4 + wave; i < nw; i += gridDim.x * 4) {
+    const int k = wmid[i];
+    const int b = ptr[k], len = ptr[k + 1] - b;
+    int P = 1;
+    while (P < len) P <<= 1;
+    wave_lds_sync();  // the previous segment's values have been read
+    for (int t = lane; t < P; t += 64) sv[t] = t < len ? in[b + t] : 0xFFFFFFFFu;
+    wave_lds_sync();
+    for (int kk = 2; kk <= P; kk <<= 1) {
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+        for (int t = lane; t < P; t += 64) {
+          const int u = t ^ jj;
+          if (u > t) {
+            const uint32_t x = sv[t], y = sv[u];
+            if ((x > y) == ((t & kk) == 0)) {
+              sv[t] = y;
+              sv[u] = x;
+            }
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    for (int t = lane; t < len; t += 64) out[b + t] = sv[t];
+  }
+}
+
+// keys of long segment i (one workgroup per segment): (i << vbits) | value
+__global__ __launch_bounds__(256) void k_sseg_big_keys(const uint32_t* in, const int32_t* ptr, const int32_t* big,
+                                                       const int32_t* big_off, int vbits, uint64_t* keys) {
+  const int i = blockIdx.x;
+  const int b = ptr[big[i]], o = big_off[i], len = big_off[i + 1] - o;
+  for (int t = threadIdx.x; t < len; t += blockDim.x)
+    keys[(int64_t)o + t] = ((uint64_t)i << vbits) | in[b + t];
+}
+
+__global__ void k_sseg_big_out(const uint64_t* keys, int64_t nk, const int32_t* ptr, const int32_t* big,
+                               const int32_t* big_off, int vbits, uint32_t* out) {
+  const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= nk) return;
+  const uint64_t key = keys[q];
+  const int i = (int)(key >> vbits);
+  out[ptr[big[i]] + (q - big_off[i])] = (uint32_t)(key & ((1ull << vbits) - 1));
+}
+
+// Values are below vmax.  One host synchronisation (the long segments' entry
+// count); temporaries are stream-ordered.
+int segmented_sort_u32(const uint32_t* in, uint32_t* out, const int32_t* ptr, int32_t nseg, int64_t n,
+                       uint32_t vmax, hipStream_t s) {
+  if (n <= 0 || nseg <= 0) return GNN_OK;
+  const int64_t big_max = std::min<int64_t>(nseg, n / (kSortBlock + 1) + 1);
+  StreamTemps own(s);
+  int32_t *cnt = nullptr, *mid = nullptr, *wmid = nullptr, *big = nullptr, *big_len = nullptr, *big_off = nullptr;
+  GNN_TRY(own.get(&cnt, 16));
+  GNN_TRY(own.get(&mid, (size_t)std::min<int64_t>(nseg, n / (kSortWave + 1) + 1) * 4));
+  GNN_TRY(own.get(&wmid, (size_t)std::min<int64_t>(nseg, n / (kSortSmall + 1) + 1) * 4));
+  GNN_TRY(own.get(&big, (size_t)big_max * 4));
+  GNN_TRY(own.get(&big_len, (size_t)big_max * 4));
+  GNN_TRY(own.get(&big_off, (size_t)(big_max + 1) * 4));
+  GNN_HIP(hipMemsetAsync(cnt, 0, 16, s));
+  const unsigned ncls = (unsigned)((nseg + 256 * kClassPer - 1) / (256 * kClassPer));
+  hipLaunchKernelGGL(k_sseg_classify, dim3(ncls), dim3(256), 0, s, ptr, nseg, mid, big, big_len, wmid, cnt);
+  GNN_LAUNCH_CHECK("segment classes");
+  hipLaunchKernelGGL(k_sseg_small, dim3(nb_seg(n)), dim3(256), 0, s, in, out, ptr, nseg, n);
+  GNN_LAUNCH_CHECK("short segments");
+  hipLaunchKernelGGL(k_sseg_mid, dim3((unsigned)std::min<int64_t>(nseg, kSortBlocks)), dim3(256), 0, s, in, out,
+                     ptr, mid, cnt);
+  GNN_LAUNCH_CHECK("medium segments");
+  hipLaunchKernelGGL(k_sseg_wave, dim3((unsigned)std::min<int64_t>((nseg + 3) / 4, 4 * kSortBlocks)), dim3(256), 0, s,
+                     in, out, ptr, wmid, cnt);
+  GNN_LAUNCH_CHECK("wave segments");
+  int32_t hc[3] = {0, 0, 0};
+  GNN_HIP(hipMemcpyAsync(hc, cnt, 12, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipStreamSynchronize(s));
+  const int32_t nbig = hc[1];
+  const int64_t nk = hc[2];
+  if (nbig < 0 || nbig > big_max || nk < 0 || nk > n) return fail(GNN_ERR_DEVICE, "segmented sort: bad counts");
+  if (nbig > 0) {
+    GNN_TRY(exclusive_scan_i32(big_len, big_off, nbig, s));
+    const int vbits = bits_for((int64_t)std::max<uint32_t>(vmax, 1) - 1);
+    const int ibits = bits_for(nbig - 1);
+    if (vbits + ibits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "segmented sort keys exceed 64 bits");
+    uint64_t *keys = nullptr, *tmp = nullptr;
+    GNN_TRY(own.get(&keys, (size_t)nk * 8));
+    GNN_TRY(own.get(&tmp, (size_t)nk * 8));
+    hipLaunchKernelGGL(k_sseg_big_keys, dim3((unsigned)nbig), dim3(256), 0, s, in, ptr, big, big_off, vbits, keys);
+    GNN_LAUNCH_CHECK("long segment keys");
+    GNN_TRY(radix_sort_u64(keys, tmp, nk, 0, vbits + ibits, s));
+    hipLaunchKernelGGL(k_sseg_big_out, dim3(nb(nk)), dim3(256), 0, s, keys, nk, ptr, big, big_off, vbits, out);
+    GNN_LAUNCH_CHECK("long segments");
+  }
+  return own.release();
 }
 
 __global__ void k_deg_keys(const int32_t* row_ptr, int32_t n, int32_t maxdeg, int idbits,
@@ -144,12 +369,13 @@ __global__ void k_new_deg(const int32_t* row_ptr, const int32_t* perm, int32_t n
   if (p < n) deg[p] = row_ptr[perm[p] + 1] - row_ptr[perm[p]];
 }
 
-// key = (new row << colbits) | new column, for every entry of P A P^T
-__global__ __launch_bounds__(256) void k_perm_keys(const int32_t* row_ptr, const int32_t* col_idx,
+// new column of every entry of P A P^T, rows in their new places (the
+// entries of new row p are those of old row perm[p], in their old order)
+__global__ __launch_bounds__(256) void k_perm_cols(const int32_t* row_ptr, const int32_t* col_idx,
                                                    const int32_t* perm, const int32_t* inv,
                                                    const int32_t* new_ptr, int32_t n, int64_t nnz,
-                                                   int colbits, uint64_t* keys) {
-  __shared__ int32_t s_ptr[kSegCap];
+                                                   uint32_t* cols) {
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(new_ptr, n, nnz, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -157,7 +383,7 @@ __global__ __launch_bounds__(256) void k_perm_keys(const int32_t* row_ptr, const
     if (q < 0) break;
     const int p = seg_find(new_ptr, s_ptr, sp, q);
     const int64_t old_e = row_ptr[perm[p]] + (q - new_ptr[p]);
-    keys[q] = ((uint64_t)p << colbits) | (uint32_t)inv[col_idx[old_e]];
+    cols[q] = (uint32_t)inv[col_idx[old_e]];
   }
 }
 
@@ -166,7 +392,7 @@ __global__ __launch_bounds__(256) void k_perm_keys(const int32_t* row_ptr, const
 // both directions of every non-loop edge (compacted by a scan of flags)
 __global__ __launch_bounds__(256) void k_loop_flags(const int32_t* row_ptr, const int32_t* col_idx,
                                                     int32_t n, int64_t nnz, int32_t* flag) {
-  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -179,7 +405,7 @@ __global__ __launch_bounds__(256) void k_loop_flags(const int32_t* row_ptr, cons
 __global__ __launch_bounds__(256) void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx,
                                                   int32_t n, int64_t nnz, const int32_t* flag,
                                                   const int32_t* pos, int idbits, uint64_t* keys) {
-  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -235,18 +461,16 @@ __global__ void k_rank(const uint64_t* keys, int32_t n, int idbits, int32_t* ord
   rank[v] = (int32_t)r;
 }
 
-__global__ void k_adj_keys(const int32_t* adj, const int32_t* adj_row, const int32_t* rank, int64_t m,
-                           int idbits, uint64_t* keys) {
+__global__ void k_adj_ranks(const int32_t* adj, const int32_t* rank, int64_t m, uint32_t* rk) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= m) return;
-  keys[e] = ((uint64_t)adj_row[e] << idbits) | (uint64_t)rank[adj[e]];
+  rk[e] = (uint32_t)rank[adj[e]];
 }
 
-__global__ void k_adj_from_keys(const uint64_t* keys, const int32_t* order, int64_t m, int idbits,
-                                int32_t* adj) {
+__global__ void k_adj_from_ranks(const uint32_t* rk, const int32_t* order, int64_t m, int32_t* adj) {
   int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= m) return;
-  adj[e] = order[keys[e] & ((1ull << idbits) - 1)];
+  adj[e] = order[rk[e]];
 }
 
 // ---- component labels: union-find over ranks ----
@@ -338,7 +562,7 @@ __global__ void k_front_deg(const int32_t* front, int32_t f, const int32_t* sym_
 __global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, const int32_t* eoff,
                                                int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
                                                const int32_t* visited, int32_t* claim) {
-  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -354,7 +578,7 @@ __global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32
                                                      int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
                                                      const int32_t* visited, const int32_t* claim,
                                                      int32_t* flag) {
-  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -369,7 +593,7 @@ __global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32
 __global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff,
                                                     int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
                                                     const int32_t* flag, const int32_t* pos, int32_t* next) {
-  __shared__ int32_t s_ptr[kSegCap];
+  __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
   for (int j = 0; j < kSegEPT; ++j) {
@@ -511,12 +735,14 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   hipLaunchKernelGGL(k_rank, dim3(nb(n)), dim3(256), 0, s, keys, n, idbits, order, rank);
   GNN_LAUNCH_CHECK("rcm rank");
 
-  // 3. adjacency lists in rank order
+  // 3. adjacency lists in rank order: each row's neighbour ranks sorted
   if (m > 0) {
-    hipLaunchKernelGGL(k_adj_keys, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, m, idbits, keys);
-    GNN_LAUNCH_CHECK("rcm adj keys");
-    GNN_TRY(radix_sort_u64(keys, tmp, m, 0, 2 * idbits, s, ws));
-    hipLaunchKernelGGL(k_adj_from_keys, dim3(nb(m)), dim3(256), 0, s, keys, order, m, idbits, adj);
+    uint32_t* rk = reinterpret_cast<uint32_t*>(keys);
+    uint32_t* rk_sorted = reinterpret_cast<uint32_t*>(tmp);
+    hipLaunchKernelGGL(k_adj_ranks, dim3(nb(m)), dim3(256), 0, s, adj, rank, m, rk);
+    GNN_LAUNCH_CHECK("rcm adj ranks");
+    GNN_TRY(segmented_sort_u32(rk, rk_sorted, sym_ptr, n, m, (uint32_t)n, s));
+    hipLaunchKernelGGL(k_adj_from_ranks, dim3(nb(m)), dim3(256), 0, s, rk_sorted, order, m, adj);
     GNN_LAUNCH_CHECK("rcm adj sort");
   }
 
@@ -596,8 +822,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
 
 size_t permute_bytes(int32_t n, int64_t nnz) {
   const int64_t m = std::max<int64_t>(nnz, 1);
-  return 2 * Arena::round((size_t)n * 4) + 2 * Arena::round((size_t)m * 8) +
-         std::max(scan_scratch_bytes(n), radix_scratch_bytes(m));
+  return 2 * Arena::round((size_t)n * 4) + Arena::round((size_t)m * 4) + scan_scratch_bytes(n);
 }
 
 int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t* ci_out, Arena& ar,
@@ -606,21 +831,17 @@ int permute_csr(const gnn_csr* c, const int32_t* perm, int32_t* rp_out, int32_t*
   const int64_t nnz = c->nnz;
   int32_t* inv = ar.take<int32_t>(n);
   int32_t* deg = ar.take<int32_t>(n);
-  uint64_t* keys = ar.take<uint64_t>(std::max<int64_t>(nnz, 1));
-  uint64_t* tmp = ar.take<uint64_t>(std::max<int64_t>(nnz, 1));
+  uint32_t* cols = ar.take<uint32_t>(std::max<int64_t>(nnz, 1));
   void* ws = ar.base + ar.off;
   hipLaunchKernelGGL(k_inverse, dim3(nb(n)), dim3(256), 0, s, perm, n, inv);
   hipLaunchKernelGGL(k_new_deg, dim3(nb(n)), dim3(256), 0, s, c->row_ptr, perm, n, deg);
   GNN_LAUNCH_CHECK("permute degrees");
   GNN_TRY(exclusive_scan_i32(deg, rp_out, n, s, ws));
   if (nnz > 0) {
-    const int colbits = bits_for(n);
-    hipLaunchKernelGGL(k_perm_keys, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
-                       rp_out, n, nnz, colbits, keys);
-    GNN_LAUNCH_CHECK("permute keys");
-    GNN_TRY(radix_sort_u64(keys, tmp, nnz, 0, 2 * colbits, s, ws));
-    hipLaunchKernelGGL(k_low_bits, dim3(nb(nnz)), dim3(256), 0, s, keys, nnz, colbits, ci_out);
+    hipLaunchKernelGGL(k_perm_cols, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, perm, inv,
+                       rp_out, n, nnz, cols);
     GNN_LAUNCH_CHECK("permute cols");
+    GNN_TRY(segmented_sort_u32(cols, reinterpret_cast<uint32_t*>(ci_out), rp_out, n, nnz, (uint32_t)n, s));
   }
   return GNN_OK;
 }
