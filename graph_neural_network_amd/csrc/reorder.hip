@@ -503,18 +503,12 @@ __global__ void k_iota(int32_t* p, int32_t n) {
   if (i < n) p[i] = (int32_t)i;
 }
 
-// One hook per undirected edge (the symmetrised pattern holds both
-// directions; the one with row < column is taken).  A failed swap means the
-// larger root was attached elsewhere meanwhile: the larger of the two roots
-// strictly decreases with every retry.
-__global__ void k_cc_hook(const int32_t* adj, const int32_t* adj_row, const int32_t* rank, int64_t m,
-                          int32_t* P) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= m) return;
-  const int u = adj_row[e], v = adj[e];
-  if (u >= v) return;
-  int a = uf_root(P, rank[u]);
-  int b = uf_root(P, rank[v]);
+// Joins the trees of ranks a and b: attaches the larger root under the
+// smaller one.  A failed swap means that root was attached elsewhere
+// meanwhile: the larger of the two roots strictly decreases with every retry.
+__device__ void uf_hook(int32_t* P, int a, int b) {
+  a = uf_root(P, a);
+  b = uf_root(P, b);
   while (a != b) {
     if (a < b) {
       const int t = a;
@@ -526,6 +520,61 @@ __global__ void k_cc_hook(const int32_t* adj, const int32_t* adj_row, const int3
     a = uf_root(P, old);
     b = uf_root(P, b);
   }
+}
+
+// Neighbour sampling (the components of most graphs are found from a few
+// edges per vertex): every vertex with more than j neighbours is joined to
+// its j-th one.
+__global__ void k_cc_link_nth(const int32_t* sym_ptr, const int32_t* adj, const int32_t* rank, int32_t n, int j,
+                              int32_t* P) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  const int b = sym_ptr[v];
+  if (sym_ptr[v + 1] - b > j) uf_hook(P, rank[v], rank[adj[b + j]]);
+}
+
+// Every rank points at its root (no hooks run meanwhile; concurrent walks
+// may leave a few entries one step short, which only costs later walks).
+__global__ void k_cc_compress(int32_t n, int32_t* P) {
+  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < n) __hip_atomic_store(P + r, uf_root(P, (int)r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The most frequent root among 1024 spread sample ranks (one workgroup of
+// 256): the component whose vertices skip the full pass.
+__global__ __launch_bounds__(256) void k_cc_giant(int32_t n, int32_t* P, int32_t* giant) {
+  __shared__ int32_t s_root[1024];
+  __shared__ unsigned long long s_best;
+  if (threadIdx.x == 0) s_best = 0;
+  for (int i = threadIdx.x; i < 1024; i += 256)
+    s_root[i] = uf_root(P, (int)(((uint64_t)i * 2654435761u) % (uint64_t)n));
+  __syncthreads();
+  for (int i = threadIdx.x; i < 1024; i += 256) {
+    int c = 0;
+    for (int t = 0; t < 1024; ++t) c += s_root[t] == s_root[i];
+    atomicMax(&s_best, ((unsigned long long)c << 32) | (uint32_t)s_root[i]);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *giant = (int32_t)(uint32_t)s_best;
+}
+
+// skip[v] = v's tree is the sampled giant one
+__global__ void k_cc_skip(const int32_t* rank, int32_t n, int32_t* P, const int32_t* giant, int32_t* skip) {
+  const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < n) skip[v] = uf_root(P, rank[v]) == *giant ? 1 : 0;
+}
+
+// Every entry (u, v) of a vertex outside the giant tree is hooked.  An edge
+// between two giant-tree vertices joins vertices already in one tree; an
+// edge with one end outside is hooked from that end (the pattern holds both
+// directions).
+__global__ void k_cc_hook(const int32_t* adj, const int32_t* adj_row, const int32_t* rank, const int32_t* skip,
+                          int64_t m, int32_t* P) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= m) return;
+  const int u = adj_row[e];
+  if (skip[u]) return;
+  uf_hook(P, rank[u], rank[adj[e]]);
 }
 
 __global__ void k_cc_label(const int32_t* rank, int32_t n, int32_t* P, int32_t* label) {
@@ -747,13 +796,23 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   }
 
   // 4. component labels: smallest rank in the component, by union-find over
-  // ranks (the claim array holds the parents until the BFS)
+  // ranks: two rounds of neighbour sampling, then every entry of the
+  // vertices outside the sampled giant tree (the claim array holds the
+  // parents and the visited array the skip flags until the BFS)
   {
     int32_t* P = claim;
     hipLaunchKernelGGL(k_iota, dim3(nb(n)), dim3(256), 0, s, P, n);
     GNN_LAUNCH_CHECK("rcm parents");
     if (m > 0) {
-      hipLaunchKernelGGL(k_cc_hook, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, m, P);
+      for (int j = 0; j < 2; ++j) {
+        hipLaunchKernelGGL(k_cc_link_nth, dim3(nb(n)), dim3(256), 0, s, sym_ptr, adj, rank, n, j, P);
+        hipLaunchKernelGGL(k_cc_compress, dim3(nb(n)), dim3(256), 0, s, n, P);
+        GNN_LAUNCH_CHECK("rcm sampled links");
+      }
+      int32_t* giant = ccnt;  // one word, free until the BFS
+      hipLaunchKernelGGL(k_cc_giant, dim3(1), dim3(256), 0, s, n, P, giant);
+      hipLaunchKernelGGL(k_cc_skip, dim3(nb(n)), dim3(256), 0, s, rank, n, P, giant, visited);
+      hipLaunchKernelGGL(k_cc_hook, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, visited, m, P);
       GNN_LAUNCH_CHECK("rcm hooks");
     }
     hipLaunchKernelGGL(k_cc_label, dim3(nb(n)), dim3(256), 0, s, rank, n, P, label);

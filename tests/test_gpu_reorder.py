@@ -40,7 +40,40 @@ def graphs():
     out["rmat_loops"] = gen.rmat(0x5EED0401, 7001, 50000, self_loops=True)
     out["cluster"] = gen.cluster(0x5EED0402, 64 * 50, 64, 0.5, 0.01, self_loops=True)
     out["empty"] = gen.from_edges(37, [], [])
+    out["components"] = components(rng)
     return out
+
+
+def components(rng):
+    """Disjoint pieces under shuffled labels: a 5001-vertex star (the largest
+    component, its centre's row past 4096 entries), three hubs with 100, 2000
+    and 4500 neighbours among 4600 vertices (rows in each sort tier), a
+    3000-vertex path, a small R-MAT graph, cliques of 5-12 and isolated
+    vertices; every edge in both directions."""
+    pieces, n = [], 0
+
+    def add(k, s, d):
+        nonlocal n
+        pieces.append((np.asarray(s, np.int64) + n, np.asarray(d, np.int64) + n))
+        n += k
+
+    add(5001, np.zeros(5000), np.arange(1, 5001))
+    hub_s, hub_d = [], []
+    for h, deg in enumerate((100, 2000, 4500)):
+        nb = 3 + rng.choice(4597, size=deg, replace=False)
+        hub_s.append(np.full(deg, h)); hub_d.append(nb)
+    add(4600, np.concatenate(hub_s + [[0, 1]]), np.concatenate(hub_d + [[1, 2]]))
+    add(3000, np.arange(2999), np.arange(1, 3000))
+    rrp, rci = gen.rmat(0x5EED0403, 1500, 6000)
+    add(1500, np.repeat(np.arange(1500), np.diff(rrp)), rci)
+    for size in rng.integers(5, 13, size=40):
+        i, j = np.triu_indices(int(size), 1)
+        add(int(size), i, j)
+    add(200, [], [])
+    s = np.concatenate([p[0] for p in pieces])
+    d = np.concatenate([p[1] for p in pieces])
+    lab = rng.permutation(n)
+    return gen.from_edges(n, np.r_[lab[s], lab[d]], np.r_[lab[d], lab[s]])
 
 
 GRAPHS = graphs()
