@@ -589,19 +589,21 @@ __global__ void k_start_flags(const int32_t* order, const int32_t* label, int32_
 }
 
 __global__ void k_start_fill(const int32_t* order, const int32_t* flag, const int32_t* pos, int32_t n,
-                             int32_t* level, int32_t* visited) {
+                             int32_t* level, int32_t* claim) {
   int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (r >= n || !flag[r]) return;
   const int v = order[r];
   level[pos[r]] = v;
-  visited[v] = 1;
+  claim[v] = -1;
 }
 
 // ---- one BFS level over the frontier's flattened adjacency ----
 // Frontier edge q (0 <= q < E_f) belongs to frontier position k with
 // eoff[k] <= q < eoff[k+1]; its target is adj[sym_ptr[front[k]] + q - eoff[k]].
 // Edges are numbered in (frontier position, adjacency order), so emitting
-// them in q order keeps the queue order.
+// them in q order keeps the queue order.  claim[w] is -1 once w is visited,
+// else the smallest frontier position claiming it (INT_MAX: none), so one
+// word per vertex serves both tests.
 
 __global__ void k_front_deg(const int32_t* front, int32_t f, const int32_t* sym_ptr, int32_t* deg) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -610,7 +612,7 @@ __global__ void k_front_deg(const int32_t* front, int32_t f, const int32_t* sym_
 
 __global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, const int32_t* eoff,
                                                int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
-                                               const int32_t* visited, int32_t* claim) {
+                                               int32_t* claim) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
@@ -619,14 +621,13 @@ __global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, 
     if (q < 0) break;
     const int k = seg_find(eoff, s_ptr, sp, q);
     const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
-    if (!visited[w]) atomicMin(&claim[w], k);
+    if (claim[w] > k) atomicMin(&claim[w], k);
   }
 }
 
 __global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32_t f, const int32_t* eoff,
                                                      int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
-                                                     const int32_t* visited, const int32_t* claim,
-                                                     int32_t* flag) {
+                                                     const int32_t* claim, int32_t* flag) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32
     if (q < 0) break;
     const int k = seg_find(eoff, s_ptr, sp, q);
     const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
-    flag[q] = (!visited[w] && claim[w] == k) ? 1 : 0;
+    flag[q] = claim[w] == k ? 1 : 0;
   }
 }
 
@@ -654,9 +655,9 @@ __global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_
   }
 }
 
-__global__ void k_mark(const int32_t* next, int32_t f, int32_t* visited) {
+__global__ void k_mark(const int32_t* next, int32_t f, int32_t* claim) {
   int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (k < f) visited[next[k]] = 1;
+  if (k < f) claim[next[k]] = -1;
 }
 
 __global__ void k_final_keys(const int32_t* concat, const int32_t* label, int32_t n, int idbits,
@@ -738,7 +739,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   int32_t* rank = ar.take<int32_t>(n);
   int32_t* label = ar.take<int32_t>(n);
   int32_t* concat = ar.take<int32_t>(n);
-  int32_t* visited = ar.take<int32_t>(n);
+  int32_t* skip = ar.take<int32_t>(n);
   int32_t* claim = ar.take<int32_t>(n);
   void* ws = ar.base + ar.off;  // scan and sort scratch
 
@@ -798,7 +799,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   // 4. component labels: smallest rank in the component, by union-find over
   // ranks: two rounds of neighbour sampling, then every entry of the
   // vertices outside the sampled giant tree (the claim array holds the
-  // parents and the visited array the skip flags until the BFS)
+  // parents)
   {
     int32_t* P = claim;
     hipLaunchKernelGGL(k_iota, dim3(nb(n)), dim3(256), 0, s, P, n);
@@ -811,8 +812,8 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
       }
       int32_t* giant = ccnt;  // one word, free until the BFS
       hipLaunchKernelGGL(k_cc_giant, dim3(1), dim3(256), 0, s, n, P, giant);
-      hipLaunchKernelGGL(k_cc_skip, dim3(nb(n)), dim3(256), 0, s, rank, n, P, giant, visited);
-      hipLaunchKernelGGL(k_cc_hook, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, visited, m, P);
+      hipLaunchKernelGGL(k_cc_skip, dim3(nb(n)), dim3(256), 0, s, rank, n, P, giant, skip);
+      hipLaunchKernelGGL(k_cc_hook, dim3(nb(m)), dim3(256), 0, s, adj, adj_row, rank, skip, m, P);
       GNN_LAUNCH_CHECK("rcm hooks");
     }
     hipLaunchKernelGGL(k_cc_label, dim3(nb(n)), dim3(256), 0, s, rank, n, P, label);
@@ -823,13 +824,12 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   // frontier-edge flags and positions (a level touches at most every entry
   // once) in the slabs, whose duplicate flags are no longer needed
   int32_t *qflag = slab0, *qpos = slab1;
-  GNN_HIP(hipMemsetAsync(visited, 0, (size_t)n * 4, s));
   hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
   GNN_LAUNCH_CHECK("rcm claim init");
   hipLaunchKernelGGL(k_start_flags, dim3(nb(n)), dim3(256), 0, s, order, label, n, ccnt);
   GNN_LAUNCH_CHECK("rcm starts");
   GNN_TRY(exclusive_scan_i32(ccnt, coff, n, s, ws));
-  hipLaunchKernelGGL(k_start_fill, dim3(nb(n)), dim3(256), 0, s, order, ccnt, coff, n, concat, visited);
+  hipLaunchKernelGGL(k_start_fill, dim3(nb(n)), dim3(256), 0, s, order, ccnt, coff, n, concat, claim);
   GNN_LAUNCH_CHECK("rcm level 0");
   int32_t f = 0;
   GNN_HIP(hipMemcpyAsync(&f, coff + n, 4, hipMemcpyDeviceToHost, s));
@@ -849,9 +849,9 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     int32_t nf = 0;
     if (ef > 0) {
       hipLaunchKernelGGL(k_claim, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
-                         adj, visited, claim);
+                         adj, claim);
       hipLaunchKernelGGL(k_child_flags, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
-                         sym_ptr, adj, visited, claim, qflag);
+                         sym_ptr, adj, claim, qflag);
       GNN_LAUNCH_CHECK("rcm level flags");
       GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s, ws));
       GNN_HIP(hipMemcpyAsync(&nf, qpos + ef, 4, hipMemcpyDeviceToHost, s));
@@ -862,7 +862,7 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
       hipLaunchKernelGGL(k_child_emit, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
                          sym_ptr, adj, qflag, qpos, next);
       GNN_LAUNCH_CHECK("rcm level emit");
-      hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, visited);
+      hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, claim);
       GNN_LAUNCH_CHECK("rcm mark");
     }
     base += f;
