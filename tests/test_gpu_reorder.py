@@ -103,6 +103,18 @@ def test_rcm_bandwidth_on_relabelled_path_and_grid():
         assert np.abs(inv[rows] - inv[ci]).max() <= bound
 
 
+@pytest.mark.parametrize("n", [7, 20001])
+@pytest.mark.parametrize("F", [33, 64, 100, 128, 256])
+def test_permute_rows_widths(n, F):
+    """Rows that are whole 16-byte units take the 16-byte copy, 132 B rows
+    the element copy; row counts that do not fill the last workgroup."""
+    rng = np.random.default_rng(F * 1000 + n)
+    P = rng.permutation(n).astype(np.int32)
+    X = gen.gauss_f32(F + n, (n, F))
+    Xp = gnn.gnn_permute_rows(dev(P), dev(X))
+    assert np.array_equal(host(Xp), X[P])
+
+
 def test_permute_rows_and_reordered_spmm():
     rp, ci = GRAPHS["rmat"]
     n = rp.size - 1
