@@ -55,37 +55,75 @@ __device__ int block_excl_scan(int v, int* lds_waves, int& total) {
   return off + inc - v;
 }
 
+// A thread's kScanItems consecutive inputs; a tile inside the array with
+// 16-byte aligned arrays (VEC) is read with four 16-byte loads per thread.
+template <bool VEC>
+__device__ __forceinline__ void scan_load(const int32_t* in, int64_t n, int64_t base, int (&v)[kScanItems]) {
+  if (VEC && (int64_t)(blockIdx.x + 1) * kScanTile <= n) {
+    const int4* p = reinterpret_cast<const int4*>(in + base);
+#pragma unroll
+    for (int q = 0; q < kScanItems / 4; ++q) {
+      const int4 t = p[q];
+      v[4 * q] = t.x;
+      v[4 * q + 1] = t.y;
+      v[4 * q + 2] = t.z;
+      v[4 * q + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) v[k] = (base + k < n) ? in[base + k] : 0;
+  }
+}
+
+template <bool VEC>
 __global__ __launch_bounds__(kScanThreads) void k_scan_block_sums(const int32_t* in, int64_t n,
                                                                   int32_t* sums) {
   __shared__ int lw[kScanThreads / 64];
   int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+  int v[kScanItems];
+  scan_load<VEC>(in, n, base, v);
   int s = 0;
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k)
-    if (base + k < n) s += in[base + k];
+  for (int k = 0; k < kScanItems; ++k) s += v[k];
   int total;
   block_excl_scan(s, lw, total);
   if (threadIdx.x == 0) sums[blockIdx.x] = total;
 }
 
+template <bool VEC>
 __global__ __launch_bounds__(kScanThreads) void k_scan_tiles(const int32_t* in, int64_t n,
                                                              const int32_t* block_off,
                                                              int32_t* out) {
   __shared__ int lw[kScanThreads / 64];
   int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
   int v[kScanItems];
+  scan_load<VEC>(in, n, base, v);
   int s = 0;
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    v[k] = (base + k < n) ? in[base + k] : 0;
-    s += v[k];
-  }
+  for (int k = 0; k < kScanItems; ++k) s += v[k];
   int total;
   int run = block_excl_scan(s, lw, total) + (block_off ? block_off[blockIdx.x] : 0);
+  if (VEC && (int64_t)(blockIdx.x + 1) * kScanTile <= n) {
+    int4* p = reinterpret_cast<int4*>(out + base);
 #pragma unroll
-  for (int k = 0; k < kScanItems; ++k) {
-    if (base + k < n) out[base + k] = run;
-    run += v[k];
+    for (int q = 0; q < kScanItems / 4; ++q) {
+      int4 t;
+      t.x = run;
+      run += v[4 * q];
+      t.y = run;
+      run += v[4 * q + 1];
+      t.z = run;
+      run += v[4 * q + 2];
+      t.w = run;
+      run += v[4 * q + 3];
+      p[q] = t;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < kScanItems; ++k) {
+      if (base + k < n) out[base + k] = run;
+      run += v[k];
+    }
   }
   // the last element's successor: out[n] = grand total
   if (base + kScanItems >= n && base < n) out[n] = run;
@@ -434,8 +472,10 @@ size_t scan_scratch_bytes(int64_t n) {
 
 int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s, void* scratch) {
   int64_t nb = (n + kScanTile - 1) / kScanTile;
+  const bool in16 = (uintptr_t)in % 16 == 0, vec = in16 && (uintptr_t)out % 16 == 0;
   if (nb <= 1) {
-    hipLaunchKernelGGL(k_scan_tiles, dim3(1), dim3(kScanThreads), 0, s, in, n, nullptr, out);
+    if (vec) hipLaunchKernelGGL(k_scan_tiles<true>, dim3(1), dim3(kScanThreads), 0, s, in, n, nullptr, out);
+    else hipLaunchKernelGGL(k_scan_tiles<false>, dim3(1), dim3(kScanThreads), 0, s, in, n, nullptr, out);
     GNN_LAUNCH_CHECK("scan");
     return GNN_OK;
   }
@@ -444,12 +484,15 @@ int exclusive_scan_i32(const int32_t* in, int32_t* out, int64_t n, hipStream_t s
   Arena a{static_cast<char*>(scratch), scan_scratch_bytes(n), 0};
   int32_t* sums = a.take<int32_t>(nb);
   int32_t* offs = a.take<int32_t>(nb + 1);
-  hipLaunchKernelGGL(k_scan_block_sums, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, sums);
+  if (in16) hipLaunchKernelGGL(k_scan_block_sums<true>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, sums);
+  else hipLaunchKernelGGL(k_scan_block_sums<false>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, sums);
   GNN_LAUNCH_CHECK("scan sums");
   int rc = exclusive_scan_i32(sums, offs, nb, s, a.base + a.off);
   if (rc == GNN_OK) {
-    hipLaunchKernelGGL(k_scan_tiles, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, offs,
-                       out);
+    if (vec)
+      hipLaunchKernelGGL(k_scan_tiles<true>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, offs, out);
+    else
+      hipLaunchKernelGGL(k_scan_tiles<false>, dim3((unsigned)nb), dim3(kScanThreads), 0, s, in, n, offs, out);
     GNN_LAUNCH_CHECK("scan tiles");
   }
   if (rc != GNN_OK) return rc;
