@@ -625,33 +625,70 @@ __global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, 
   }
 }
 
-__global__ __launch_bounds__(256) void k_child_flags(const int32_t* front, int32_t f, const int32_t* eoff,
+// Children of the level: frontier edge q keeps its target w when its
+// frontier position k won w's claim.  k_child_count stores, per wave and
+// round of its span, the ballot of kept edges (words in q order) and the
+// span's count; k_child_emit writes every kept target at the span's offset
+// plus the kept edges before it.
+constexpr int kSpanWords = kSegEPT * 4;  // ballot words per span (4 waves)
+
+__global__ __launch_bounds__(256) void k_child_count(const int32_t* front, int32_t f, const int32_t* eoff,
                                                      int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
-                                                     const int32_t* claim, int32_t* flag) {
+                                                     const int32_t* claim, unsigned long long* keep,
+                                                     int32_t* cnt) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
+  __shared__ int32_t s_c[4];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int c = 0;
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t q = seg_entry(sp, j);
-    if (q < 0) break;
-    const int k = seg_find(eoff, s_ptr, sp, q);
-    const int w = adj[sym_ptr[front[k]] + (q - eoff[k])];
-    flag[q] = claim[w] == k ? 1 : 0;
+    bool kept = false;
+    if (q >= 0) {
+      const int k = seg_find(eoff, s_ptr, sp, q);
+      kept = claim[adj[sym_ptr[front[k]] + (q - eoff[k])]] == k;
+    }
+    const unsigned long long b = __ballot(kept);
+    if (lane == 0) keep[(int64_t)blockIdx.x * kSpanWords + j * 4 + wave] = b;
+    c += __popcll(b);
   }
+  if (lane == 0) s_c[wave] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[blockIdx.x] = s_c[0] + s_c[1] + s_c[2] + s_c[3];
 }
 
 __global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff,
                                                     int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
-                                                    const int32_t* flag, const int32_t* pos, int32_t* next) {
+                                                    const unsigned long long* keep, const int32_t* off,
+                                                    int32_t* next) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
+  __shared__ int32_t s_pre[kSpanWords];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
+  const unsigned long long* kw = keep + (int64_t)blockIdx.x * kSpanWords;
+  if (threadIdx.x < 64) {  // kept edges before each ballot word of the span
+    const int t = threadIdx.x;
+    const int c = t < kSpanWords ? __popcll(kw[t]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (t >= o) incl += v;
+    }
+    if (t < kSpanWords) s_pre[t] = incl - c;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int base = off[blockIdx.x];
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t q = seg_entry(sp, j);
     if (q < 0) break;
-    if (!flag[q]) continue;
+    const unsigned long long b = kw[j * 4 + wave];
+    if (!((b >> lane) & 1ull)) continue;
     const int k = seg_find(eoff, s_ptr, sp, q);
-    next[pos[q]] = adj[sym_ptr[front[k]] + (q - eoff[k])];
+    next[base + s_pre[j * 4 + wave] + __popcll(b & lt)] = adj[sym_ptr[front[k]] + (q - eoff[k])];
   }
 }
 
@@ -820,10 +857,11 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     GNN_LAUNCH_CHECK("rcm labels");
   }
 
-  // 5. level-synchronous BFS of all components at once
-  // frontier-edge flags and positions (a level touches at most every entry
-  // once) in the slabs, whose duplicate flags are no longer needed
-  int32_t *qflag = slab0, *qpos = slab1;
+  // 5. level-synchronous BFS of all components at once; per-span counts of
+  // kept frontier edges and their offsets in the slabs, the spans' ballot
+  // words in the key array (both free until step 6)
+  int32_t *tcnt = slab0, *toff = slab1;
+  unsigned long long* keep = reinterpret_cast<unsigned long long*>(keys);
   hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
   GNN_LAUNCH_CHECK("rcm claim init");
   hipLaunchKernelGGL(k_start_flags, dim3(nb(n)), dim3(256), 0, s, order, label, n, ccnt);
@@ -850,17 +888,17 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     if (ef > 0) {
       hipLaunchKernelGGL(k_claim, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
                          adj, claim);
-      hipLaunchKernelGGL(k_child_flags, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
-                         sym_ptr, adj, claim, qflag);
-      GNN_LAUNCH_CHECK("rcm level flags");
-      GNN_TRY(exclusive_scan_i32(qflag, qpos, ef, s, ws));
-      GNN_HIP(hipMemcpyAsync(&nf, qpos + ef, 4, hipMemcpyDeviceToHost, s));
+      hipLaunchKernelGGL(k_child_count, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
+                         sym_ptr, adj, claim, keep, tcnt);
+      GNN_LAUNCH_CHECK("rcm level counts");
+      GNN_TRY(exclusive_scan_i32(tcnt, toff, nb_seg(ef), s, ws));
+      GNN_HIP(hipMemcpyAsync(&nf, toff + nb_seg(ef), 4, hipMemcpyDeviceToHost, s));
       GNN_HIP(hipStreamSynchronize(s));
     }
     if (nf < 0 || base + f + nf > n) return fail(GNN_ERR_DEVICE, "RCM: level larger than the graph");
     if (nf > 0) {
       hipLaunchKernelGGL(k_child_emit, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
-                         sym_ptr, adj, qflag, qpos, next);
+                         sym_ptr, adj, keep, toff, next);
       GNN_LAUNCH_CHECK("rcm level emit");
       hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, claim);
       GNN_LAUNCH_CHECK("rcm mark");
