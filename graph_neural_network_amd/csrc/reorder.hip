@@ -111,6 +111,54 @@ __device__ __forceinline__ int seg_at(const int32_t* ptr, const int32_t* s_ptr, 
   return sp.r1 - sp.r0 + 1 > kSegCap ? ptr[k] : s_ptr[k - sp.r0];
 }
 
+// ---- compaction of a span's kept entries ----
+// A counting pass stores, per wave and round of its span, the ballot of kept
+// entries (words in entry order) and the span's count; after a scan of the
+// counts, a writing pass places each kept entry at its span's offset plus
+// the kept entries before it.  No flag or position per entry goes through
+// memory.
+constexpr int kSpanWords = kSegEPT * 4;  // ballot words per span (4 waves)
+
+// this wave's ballot of round j into the span's words kw; c counts them
+__device__ __forceinline__ void span_keep(bool kept, unsigned long long* kw, int j, int& c) {
+  const unsigned long long b = __ballot(kept);
+  if ((threadIdx.x & 63) == 0) kw[j * 4 + (threadIdx.x >> 6)] = b;
+  c += __popcll(b);
+}
+
+// the span's count; every thread calls (s_c: four words of LDS)
+__device__ __forceinline__ void span_count(int c, int32_t* s_c, int32_t* cnt) {
+  if ((threadIdx.x & 63) == 0) s_c[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) cnt[blockIdx.x] = s_c[0] + s_c[1] + s_c[2] + s_c[3];
+}
+
+// s_pre[w] = kept entries before ballot word w of the span; every thread calls
+__device__ __forceinline__ void span_prefix(const unsigned long long* kw, int32_t* s_pre) {
+  if (threadIdx.x < 64) {
+    const int t = threadIdx.x;
+    const int c = t < kSpanWords ? __popcll(kw[t]) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (t >= o) incl += v;
+    }
+    if (t < kSpanWords) s_pre[t] = incl - c;
+  }
+  __syncthreads();
+}
+
+// whether this lane's entry of round j is kept, and if so its output position
+__device__ __forceinline__ bool span_pos(const unsigned long long* kw, const int32_t* s_pre, int j, int base,
+                                         int& pos) {
+  const int lane = threadIdx.x & 63, w = j * 4 + (threadIdx.x >> 6);
+  const unsigned long long b = kw[w];
+  if (!((b >> lane) & 1ull)) return false;
+  pos = base + s_pre[w] + __popcll(b & (lane ? (~0ull >> (64 - lane)) : 0ull));
+  return true;
+}
+
 // Largest row length: a grid-stride walk, one atomic per workgroup (one per
 // wave serialises 250k atomics on one word for a 16M-row graph).
 __global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t n, int32_t* out) {
@@ -389,47 +437,73 @@ __global__ __launch_bounds__(256) void k_perm_cols(const int32_t* row_ptr, const
 
 // ---- RCM ----
 
-// both directions of every non-loop edge (compacted by a scan of flags)
-__global__ __launch_bounds__(256) void k_loop_flags(const int32_t* row_ptr, const int32_t* col_idx,
-                                                    int32_t n, int64_t nnz, int32_t* flag) {
+// both directions of every non-loop edge, compacted: the counting pass keeps
+// entries whose column is not their row, the writing pass emits the keys
+__global__ __launch_bounds__(256) void k_loop_count(const int32_t* row_ptr, const int32_t* col_idx, int32_t n,
+                                                    int64_t nnz, unsigned long long* keep, int32_t* cnt) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
+  __shared__ int32_t s_c[4];
   const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
+  int c = 0;
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t e = seg_entry(sp, j);
-    if (e < 0) break;
-    flag[e] = (col_idx[e] != seg_find(row_ptr, s_ptr, sp, e)) ? 1 : 0;
+    const bool kept = e >= 0 && col_idx[e] != seg_find(row_ptr, s_ptr, sp, e);
+    span_keep(kept, keep + (int64_t)blockIdx.x * kSpanWords, j, c);
   }
+  span_count(c, s_c, cnt);
 }
 
-__global__ __launch_bounds__(256) void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx,
-                                                  int32_t n, int64_t nnz, const int32_t* flag,
-                                                  const int32_t* pos, int idbits, uint64_t* keys) {
+__global__ __launch_bounds__(256) void k_sym_keys(const int32_t* row_ptr, const int32_t* col_idx, int32_t n,
+                                                  int64_t nnz, const unsigned long long* keep, const int32_t* off,
+                                                  int idbits, uint64_t* keys) {
   __shared__ int32_t s_ptr[kSegCap + 1];
   __shared__ int32_t s_r[2];
+  __shared__ int32_t s_pre[kSpanWords];
   const SegSpan sp = seg_stage(row_ptr, n, nnz, s_ptr, s_r);
+  const unsigned long long* kw = keep + (int64_t)blockIdx.x * kSpanWords;
+  span_prefix(kw, s_pre);
+  const int base = off[blockIdx.x];
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t e = seg_entry(sp, j);
+    int p;
     if (e < 0) break;
-    if (!flag[e]) continue;
+    if (!span_pos(kw, s_pre, j, base, p)) continue;
     const uint64_t i = (uint64_t)seg_find(row_ptr, s_ptr, sp, e), c = (uint64_t)col_idx[e];
-    keys[2 * (int64_t)pos[e]] = (i << idbits) | c;
-    keys[2 * (int64_t)pos[e] + 1] = (c << idbits) | i;
+    keys[2 * (int64_t)p] = (i << idbits) | c;
+    keys[2 * (int64_t)p + 1] = (c << idbits) | i;
   }
 }
 
-__global__ void k_uniq_flags(const uint64_t* keys, int64_t m, int32_t* flag) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= m) return;
-  flag[e] = (e == 0 || keys[e] != keys[e - 1]) ? 1 : 0;
+// sorted keys: keep the first of each run of equal keys
+__global__ __launch_bounds__(256) void k_uniq_count(const uint64_t* keys, int64_t m2, unsigned long long* keep,
+                                                    int32_t* cnt) {
+  __shared__ int32_t s_c[4];
+  const int64_t e0 = (int64_t)blockIdx.x * kSegSpan;
+  int c = 0;
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t e = e0 + (int64_t)j * blockDim.x + threadIdx.x;
+    const bool kept = e < m2 && (e == 0 || keys[e] != keys[e - 1]);
+    span_keep(kept, keep + (int64_t)blockIdx.x * kSpanWords, j, c);
+  }
+  span_count(c, s_c, cnt);
 }
 
-__global__ void k_sym_fill(const uint64_t* keys, const int32_t* flag, const int32_t* pos, int64_t m,
-                           int idbits, int32_t* adj, int32_t* adj_row) {
-  int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= m || !flag[e]) return;
-  adj[pos[e]] = (int32_t)(keys[e] & ((1ull << idbits) - 1));
-  adj_row[pos[e]] = (int32_t)(keys[e] >> idbits);
+__global__ __launch_bounds__(256) void k_sym_fill(const uint64_t* keys, int64_t m2, const unsigned long long* keep,
+                                                  const int32_t* off, int idbits, int32_t* adj, int32_t* adj_row) {
+  __shared__ int32_t s_pre[kSpanWords];
+  const unsigned long long* kw = keep + (int64_t)blockIdx.x * kSpanWords;
+  span_prefix(kw, s_pre);
+  const int64_t e0 = (int64_t)blockIdx.x * kSegSpan;
+  const int base = off[blockIdx.x];
+  for (int j = 0; j < kSegEPT; ++j) {
+    const int64_t e = e0 + (int64_t)j * blockDim.x + threadIdx.x;
+    int p;
+    if (e >= m2) break;
+    if (!span_pos(kw, s_pre, j, base, p)) continue;
+    adj[p] = (int32_t)(keys[e] & ((1ull << idbits) - 1));
+    adj_row[p] = (int32_t)(keys[e] >> idbits);
+  }
 }
 
 // Row pointers of the symmetrised pattern: adj_row is sorted, so row r starts
@@ -626,12 +700,7 @@ __global__ __launch_bounds__(256) void k_claim(const int32_t* front, int32_t f, 
 }
 
 // Children of the level: frontier edge q keeps its target w when its
-// frontier position k won w's claim.  k_child_count stores, per wave and
-// round of its span, the ballot of kept edges (words in q order) and the
-// span's count; k_child_emit writes every kept target at the span's offset
-// plus the kept edges before it.
-constexpr int kSpanWords = kSegEPT * 4;  // ballot words per span (4 waves)
-
+// frontier position k won w's claim; kept targets are compacted in q order.
 __global__ __launch_bounds__(256) void k_child_count(const int32_t* front, int32_t f, const int32_t* eoff,
                                                      int64_t ef, const int32_t* sym_ptr, const int32_t* adj,
                                                      const int32_t* claim, unsigned long long* keep,
@@ -640,7 +709,6 @@ __global__ __launch_bounds__(256) void k_child_count(const int32_t* front, int32
   __shared__ int32_t s_r[2];
   __shared__ int32_t s_c[4];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int c = 0;
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t q = seg_entry(sp, j);
@@ -649,13 +717,9 @@ __global__ __launch_bounds__(256) void k_child_count(const int32_t* front, int32
       const int k = seg_find(eoff, s_ptr, sp, q);
       kept = claim[adj[sym_ptr[front[k]] + (q - eoff[k])]] == k;
     }
-    const unsigned long long b = __ballot(kept);
-    if (lane == 0) keep[(int64_t)blockIdx.x * kSpanWords + j * 4 + wave] = b;
-    c += __popcll(b);
+    span_keep(kept, keep + (int64_t)blockIdx.x * kSpanWords, j, c);
   }
-  if (lane == 0) s_c[wave] = c;
-  __syncthreads();
-  if (threadIdx.x == 0) cnt[blockIdx.x] = s_c[0] + s_c[1] + s_c[2] + s_c[3];
+  span_count(c, s_c, cnt);
 }
 
 __global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_t f, const int32_t* eoff,
@@ -667,28 +731,15 @@ __global__ __launch_bounds__(256) void k_child_emit(const int32_t* front, int32_
   __shared__ int32_t s_pre[kSpanWords];
   const SegSpan sp = seg_stage(eoff, f, ef, s_ptr, s_r);
   const unsigned long long* kw = keep + (int64_t)blockIdx.x * kSpanWords;
-  if (threadIdx.x < 64) {  // kept edges before each ballot word of the span
-    const int t = threadIdx.x;
-    const int c = t < kSpanWords ? __popcll(kw[t]) : 0;
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(incl, o, 64);
-      if (t >= o) incl += v;
-    }
-    if (t < kSpanWords) s_pre[t] = incl - c;
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  span_prefix(kw, s_pre);
   const int base = off[blockIdx.x];
   for (int j = 0; j < kSegEPT; ++j) {
     const int64_t q = seg_entry(sp, j);
+    int p;
     if (q < 0) break;
-    const unsigned long long b = kw[j * 4 + wave];
-    if (!((b >> lane) & 1ull)) continue;
+    if (!span_pos(kw, s_pre, j, base, p)) continue;
     const int k = seg_find(eoff, s_ptr, sp, q);
-    next[base + s_pre[j * 4 + wave] + __popcll(b & lt)] = adj[sym_ptr[front[k]] + (q - eoff[k])];
+    next[p] = adj[sym_ptr[front[k]] + (q - eoff[k])];
   }
 }
 
@@ -745,13 +796,15 @@ int degree_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   return GNN_OK;
 }
 
-// Temporaries of rcm_perm: two flag / offset slabs of 2 nnz + 1 entries
-// (loop flags, then duplicate flags, then frontier-edge flags, each with its
-// scan), two key arrays, the symmetrised adjacency with its row ids, nine
+// Temporaries of rcm_perm: two small slabs (per-span counts of kept entries
+// and their offsets, one word per span of the 2 nnz symmetric entries), two
+// key arrays, the symmetrised adjacency with its row ids, nine
 // per-vertex arrays, and scan / sort scratch.
 size_t rcm_bytes(int32_t n, int64_t nnz) {
-  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
-  size_t b = 2 * Arena::round((size_t)(M2 + 1) * 4) + 2 * Arena::round((size_t)NN * 8) +
+  // key arrays: 2 nnz symmetric keys, n rank keys, the BFS's ballot words
+  // (kSpanWords per span of frontier edges: at most 1/64 of them plus one span's)
+  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>({M2, (int64_t)n, 2 * kSpanWords});
+  size_t b = 2 * Arena::round((size_t)(M2 / kSegSpan + 2) * 4) + 2 * Arena::round((size_t)NN * 8) +
              2 * Arena::round((size_t)M2 * 4) + 3 * Arena::round((size_t)(n + 1) * 4) +
              6 * Arena::round((size_t)n * 4);
   return b + std::max(scan_scratch_bytes(NN + 1), radix_scratch_bytes(NN));
@@ -762,9 +815,11 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   const int64_t nnz = c->nnz;
   const int idbits = bits_for(n);
   if (2 * idbits > 64) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM keys exceed 64 bits");
-  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>(M2, std::max<int32_t>(n, 1));
-  int32_t* slab0 = ar.take<int32_t>(M2 + 1);
-  int32_t* slab1 = ar.take<int32_t>(M2 + 1);
+  // key arrays: 2 nnz symmetric keys, n rank keys, the BFS's ballot words
+  // (kSpanWords per span of frontier edges: at most 1/64 of them plus one span's)
+  const int64_t M2 = std::max<int64_t>(2 * nnz, 1), NN = std::max<int64_t>({M2, (int64_t)n, 2 * kSpanWords});
+  int32_t* slab0 = ar.take<int32_t>(M2 / kSegSpan + 2);
+  int32_t* slab1 = ar.take<int32_t>(M2 / kSegSpan + 2);
   uint64_t* keys = ar.take<uint64_t>(NN);
   uint64_t* tmp = ar.take<uint64_t>(NN);
   int32_t* adj = ar.take<int32_t>(M2);
@@ -780,36 +835,40 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
   int32_t* claim = ar.take<int32_t>(n);
   void* ws = ar.base + ar.off;  // scan and sort scratch
 
-  // 1. symmetrised pattern without loops, as sorted unique (row, col) keys
-  int32_t *flag = slab0, *pos = slab1;
+  // 1. symmetrised pattern without loops, as sorted unique (row, col) keys;
+  // span counts and their offsets in the slabs, the spans' ballot words in
+  // the second key array (free outside the sort)
+  int32_t *cnt = slab0, *off = slab1;
+  unsigned long long* keep = reinterpret_cast<unsigned long long*>(tmp);
+  const unsigned nsp1 = nb_seg(nnz);
   if (nnz > 0) {
-    hipLaunchKernelGGL(k_loop_flags, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag);
-    GNN_LAUNCH_CHECK("rcm loop flags");
+    hipLaunchKernelGGL(k_loop_count, dim3(nsp1), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, keep, cnt);
+    GNN_LAUNCH_CHECK("rcm loop counts");
   }
-  GNN_TRY(exclusive_scan_i32(flag, pos, nnz, s, ws));
+  GNN_TRY(exclusive_scan_i32(cnt, off, nsp1, s, ws));
   int32_t nl = 0;
-  GNN_HIP(hipMemcpyAsync(&nl, pos + nnz, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipMemcpyAsync(&nl, off + nsp1, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   const int64_t m2 = 2 * (int64_t)nl;
   if (m2 >= 0x7FFFFFFF) return fail(GNN_ERR_SIZE_OVERFLOW, "RCM: symmetrised pattern too large");
   if (nnz > 0) {
-    hipLaunchKernelGGL(k_sym_keys, dim3(nb_seg(nnz)), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, flag,
-                       pos, idbits, keys);
+    hipLaunchKernelGGL(k_sym_keys, dim3(nsp1), dim3(256), 0, s, c->row_ptr, c->col_idx, n, nnz, keep, off,
+                       idbits, keys);
     GNN_LAUNCH_CHECK("rcm sym keys");
   }
   GNN_TRY(radix_sort_u64(keys, tmp, m2, 0, 2 * idbits, s, ws));
-  int32_t *uf = slab0, *up = slab1;  // the loop flags are no longer needed
+  const unsigned nsp2 = nb_seg(m2);
   if (m2 > 0) {
-    hipLaunchKernelGGL(k_uniq_flags, dim3(nb(m2)), dim3(256), 0, s, keys, m2, uf);
+    hipLaunchKernelGGL(k_uniq_count, dim3(nsp2), dim3(256), 0, s, keys, m2, keep, cnt);
     GNN_LAUNCH_CHECK("rcm unique");
   }
-  GNN_TRY(exclusive_scan_i32(uf, up, m2, s, ws));
+  GNN_TRY(exclusive_scan_i32(cnt, off, nsp2, s, ws));
   int32_t m32 = 0;
-  GNN_HIP(hipMemcpyAsync(&m32, up + m2, 4, hipMemcpyDeviceToHost, s));
+  GNN_HIP(hipMemcpyAsync(&m32, off + nsp2, 4, hipMemcpyDeviceToHost, s));
   GNN_HIP(hipStreamSynchronize(s));
   const int64_t m = m32;  // entries of the symmetrised pattern
   if (m2 > 0) {
-    hipLaunchKernelGGL(k_sym_fill, dim3(nb(m2)), dim3(256), 0, s, keys, uf, up, m2, idbits, adj, adj_row);
+    hipLaunchKernelGGL(k_sym_fill, dim3(nsp2), dim3(256), 0, s, keys, m2, keep, off, idbits, adj, adj_row);
     GNN_LAUNCH_CHECK("rcm sym fill");
   }
   hipLaunchKernelGGL(k_row_bounds, dim3(nb((int64_t)n + 1)), dim3(256), 0, s, adj_row, m, n, sym_ptr);
@@ -857,11 +916,8 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
     GNN_LAUNCH_CHECK("rcm labels");
   }
 
-  // 5. level-synchronous BFS of all components at once; per-span counts of
-  // kept frontier edges and their offsets in the slabs, the spans' ballot
-  // words in the key array (both free until step 6)
-  int32_t *tcnt = slab0, *toff = slab1;
-  unsigned long long* keep = reinterpret_cast<unsigned long long*>(keys);
+  // 5. level-synchronous BFS of all components at once (kept frontier edges
+  // compacted through cnt, off and keep as in step 1)
   hipLaunchKernelGGL(k_fill_i32, dim3(nb(n)), dim3(256), 0, s, claim, (int64_t)n, 0x7FFFFFFF);
   GNN_LAUNCH_CHECK("rcm claim init");
   hipLaunchKernelGGL(k_start_flags, dim3(nb(n)), dim3(256), 0, s, order, label, n, ccnt);
@@ -889,16 +945,16 @@ int rcm_perm(const gnn_csr* c, int32_t* perm, Arena& ar, hipStream_t s) {
       hipLaunchKernelGGL(k_claim, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef, sym_ptr,
                          adj, claim);
       hipLaunchKernelGGL(k_child_count, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
-                         sym_ptr, adj, claim, keep, tcnt);
+                         sym_ptr, adj, claim, keep, cnt);
       GNN_LAUNCH_CHECK("rcm level counts");
-      GNN_TRY(exclusive_scan_i32(tcnt, toff, nb_seg(ef), s, ws));
-      GNN_HIP(hipMemcpyAsync(&nf, toff + nb_seg(ef), 4, hipMemcpyDeviceToHost, s));
+      GNN_TRY(exclusive_scan_i32(cnt, off, nb_seg(ef), s, ws));
+      GNN_HIP(hipMemcpyAsync(&nf, off + nb_seg(ef), 4, hipMemcpyDeviceToHost, s));
       GNN_HIP(hipStreamSynchronize(s));
     }
     if (nf < 0 || base + f + nf > n) return fail(GNN_ERR_DEVICE, "RCM: level larger than the graph");
     if (nf > 0) {
       hipLaunchKernelGGL(k_child_emit, dim3(nb_seg(ef)), dim3(256), 0, s, front, f, coff, (int64_t)ef,
-                         sym_ptr, adj, keep, toff, next);
+                         sym_ptr, adj, keep, off, next);
       GNN_LAUNCH_CHECK("rcm level emit");
       hipLaunchKernelGGL(k_mark, dim3(nb(nf)), dim3(256), 0, s, next, nf, claim);
       GNN_LAUNCH_CHECK("rcm mark");
