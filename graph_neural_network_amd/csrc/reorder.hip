@@ -178,8 +178,8 @@ __global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t
 // kept).  Four tiers by segment length L:
 //   L <= kSortSmall: each value counts the smaller values of its segment and
 //     the equal ones before it, which is its place;
-//   L <= kSortWave: one wave per segment, bitonic sort in LDS (the four waves
-//     of a workgroup sort four segments, without workgroup barriers);
+//   L <= kSortWave: one wave per segment, bitonic sort in registers (the
+//     four waves of a workgroup sort four segments, without LDS or barriers);
 //   L <= kSortBlock: one workgroup per segment, bitonic sort in LDS;
 //   longer: (long-segment index, value) keys through the global radix sort,
 //     written back segment by segment.
@@ -283,44 +283,69 @@ __global__ __launch_bounds__(256) void k_sseg_mid(const uint32_t* in, uint32_t* 
   }
 }
 
-// One segment per wave, waves striding over the list (wave-level
-// synchronisation only: each wave owns its quarter of LDS).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Bitonic sort of 64 R values held in registers by one wave: value t is
+// slot t / 64 of lane t % 64.  A compare-exchange of t with t ^ j pairs two
+// slots of one lane when j >= 64 and two lanes' equal slots otherwise (one
+// lane swap), so no stage touches LDS.  Fully unrolled: slots are registers.
+template <int R>
+__device__ __forceinline__ void wave_sort_regs(uint32_t (&v)[R], int lane) {
+  constexpr int P = 64 * R;
+#pragma unroll
+  for (int k = 2; k <= P; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int r2 = r ^ (j >> 6);
+          if (r2 > r) {
+            const bool up = ((r * 64) & k) == 0;  // k > j >= 64: the same for every lane
+            const uint32_t x = v[r], y = v[r2];
+            v[r] = up ? min(x, y) : max(x, y);
+            v[r2] = up ? max(x, y) : min(x, y);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const uint32_t y = __shfl_xor(v[r], j, 64);
+          const bool up = ((r * 64 + lane) & k) == 0;
+          const bool lower = (lane & j) == 0;
+          v[r] = (lower == up) ? min(v[r], y) : max(v[r], y);
+        }
+      }
+    }
+  }
 }
 
+template <int R>
+__device__ __forceinline__ void wave_sort_segment(const uint32_t* in, uint32_t* out, int b, int len, int lane) {
+  uint32_t v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = r * 64 + lane;
+    v[r] = t < len ? in[b + t] : 0xFFFFFFFFu;
+  }
+  wave_sort_regs<R>(v, lane);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = r * 64 + lane;
+    if (t < len) out[b + t] = v[r];
+  }
+}
+
+// One segment per wave, waves striding over the list.
 __global__ __launch_bounds__(256) void k_sseg_wave(const uint32_t* in, uint32_t* out, const int32_t* ptr,
                                                    const int32_t* wmid, const int32_t* cnt) {
-  __shared__ uint32_t sv_all[4][kSortWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t* sv = sv_all[wave];
   const int nw = cnt[3];
   for (int i = blockIdx.x * 4 + wave; i < nw; i += gridDim.x * 4) {
     const int k = wmid[i];
     const int b = ptr[k], len = ptr[k + 1] - b;
-    int P = 1;
-    while (P < len) P <<= 1;
-    wave_lds_sync();  // the previous segment's values have been read
-    for (int t = lane; t < P; t += 64) sv[t] = t < len ? in[b + t] : 0xFFFFFFFFu;
-    wave_lds_sync();
-    for (int kk = 2; kk <= P; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int t = lane; t < P; t += 64) {
-          const int u = t ^ jj;
-          if (u > t) {
-            const uint32_t x = sv[t], y = sv[u];
-            if ((x > y) == ((t & kk) == 0)) {
-              sv[t] = y;
-              sv[u] = x;
-            }
-          }
-        }
-        wave_lds_sync();
-      }
-    }
-    for (int t = lane; t < len; t += 64) out[b + t] = sv[t];
+    if (len <= 128) wave_sort_segment<2>(in, out, b, len, lane);
+    else if (len <= 256) wave_sort_segment<4>(in, out, b, len, lane);
+    else if (len <= 512) wave_sort_segment<8>(in, out, b, len, lane);
+    else wave_sort_segment<16>(in, out, b, len, lane);
   }
 }
 
