@@ -252,70 +252,54 @@ __global__ __launch_bounds__(256) void k_sseg_classify(const int32_t* ptr, int32
   }
 }
 
-__global__ __launch_bounds__(256) void k_sseg_mid(const uint32_t* in, uint32_t* out, const int32_t* ptr,
-                                                  const int32_t* mid, const int32_t* cnt) {
-  __shared__ uint32_t sv[kSortBlock];
-  const int nmid = cnt[0];
-  for (int i = blockIdx.x; i < nmid; i += gridDim.x) {
-    if (i != (int)blockIdx.x) __syncthreads();  // the previous segment has left LDS
-    const int k = mid[i];
-    const int b = ptr[k], len = ptr[k + 1] - b;
-    int P = 1;
-    while (P < len) P <<= 1;
-    for (int t = threadIdx.x; t < P; t += blockDim.x) sv[t] = t < len ? in[b + t] : 0xFFFFFFFFu;
-    __syncthreads();
-    for (int kk = 2; kk <= P; kk <<= 1) {
-      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-        for (int t = threadIdx.x; t < P; t += blockDim.x) {
-          const int u = t ^ jj;
-          if (u > t) {
-            const uint32_t x = sv[t], y = sv[u];
-            if ((x > y) == ((t & kk) == 0)) {
-              sv[t] = y;
-              sv[u] = x;
-            }
-          }
-        }
-        __syncthreads();
+// Bitonic sorting network over values held in registers by one wave: the
+// wave holds positions t0 .. t0 + 64 R - 1, position t0 + t in slot t / 64
+// of lane t % 64.  A compare-exchange of positions t and t ^ j (j < 64 R)
+// pairs two slots of one lane when j >= 64 and two lanes' equal slots
+// otherwise (one lane swap), so no stage touches LDS.  Each stage sorts
+// ascending where position & k is 0.  Fully unrolled: slots are registers.
+template <int R, int J>
+__device__ __forceinline__ void regs_stage(uint32_t (&v)[R], int lane, int t0, int k) {
+  if constexpr (J >= 64) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      constexpr int dr = J >> 6;
+      if ((r ^ dr) > r) {
+        const bool up = ((t0 + r * 64) & k) == 0;  // k > J >= 64: the same for every lane
+        const uint32_t x = v[r], y = v[r ^ dr];
+        v[r] = up ? min(x, y) : max(x, y);
+        v[r ^ dr] = up ? max(x, y) : min(x, y);
       }
     }
-    for (int t = threadIdx.x; t < len; t += blockDim.x) out[b + t] = sv[t];
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t y = __shfl_xor(v[r], J, 64);
+      const bool up = ((t0 + r * 64 + lane) & k) == 0;
+      const bool lower = (lane & J) == 0;
+      v[r] = (lower == up) ? min(v[r], y) : max(v[r], y);
+    }
   }
 }
 
-// Bitonic sort of 64 R values held in registers by one wave: value t is
-// slot t / 64 of lane t % 64.  A compare-exchange of t with t ^ j pairs two
-// slots of one lane when j >= 64 and two lanes' equal slots otherwise (one
-// lane swap), so no stage touches LDS.  Fully unrolled: slots are registers.
+// stages J, J / 2, ..., 1 of merge step k
+template <int R, int J>
+__device__ __forceinline__ void regs_merge(uint32_t (&v)[R], int lane, int t0, int k) {
+  regs_stage<R, J>(v, lane, t0, k);
+  if constexpr (J > 1) regs_merge<R, J / 2>(v, lane, t0, k);
+}
+
+// merge steps K, 2 K, ..., 64 R: the wave's positions end sorted (ascending
+// or descending by bit 64 R of t0, as the network needs)
+template <int R, int K>
+__device__ __forceinline__ void regs_sort_from(uint32_t (&v)[R], int lane, int t0) {
+  regs_merge<R, K / 2>(v, lane, t0, K);
+  if constexpr (K < 64 * R) regs_sort_from<R, 2 * K>(v, lane, t0);
+}
+
 template <int R>
-__device__ __forceinline__ void wave_sort_regs(uint32_t (&v)[R], int lane) {
-  constexpr int P = 64 * R;
-#pragma unroll
-  for (int k = 2; k <= P; k <<= 1) {
-#pragma unroll
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const int r2 = r ^ (j >> 6);
-          if (r2 > r) {
-            const bool up = ((r * 64) & k) == 0;  // k > j >= 64: the same for every lane
-            const uint32_t x = v[r], y = v[r2];
-            v[r] = up ? min(x, y) : max(x, y);
-            v[r2] = up ? max(x, y) : min(x, y);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint32_t y = __shfl_xor(v[r], j, 64);
-          const bool up = ((r * 64 + lane) & k) == 0;
-          const bool lower = (lane & j) == 0;
-          v[r] = (lower == up) ? min(v[r], y) : max(v[r], y);
-        }
-      }
-    }
-  }
+__device__ __forceinline__ void wave_sort_regs(uint32_t (&v)[R], int lane, int t0 = 0) {
+  regs_sort_from<R, 2>(v, lane, t0);
 }
 
 template <int R>
@@ -326,7 +310,7 @@ __device__ __forceinline__ void wave_sort_segment(const uint32_t* in, uint32_t* 
     const int t = r * 64 + lane;
     v[r] = t < len ? in[b + t] : 0xFFFFFFFFu;
   }
-  wave_sort_regs<R>(v, lane);
+  wave_sort_regs<R>(v, lane, 0);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int t = r * 64 + lane;
@@ -346,6 +330,56 @@ __global__ __launch_bounds__(256) void k_sseg_wave(const uint32_t* in, uint32_t*
     else if (len <= 256) wave_sort_segment<4>(in, out, b, len, lane);
     else if (len <= 512) wave_sort_segment<8>(in, out, b, len, lane);
     else wave_sort_segment<16>(in, out, b, len, lane);
+  }
+}
+
+// One segment of up to 4 x 64 R values per workgroup: each wave sorts its
+// quarter in registers (directions from the positions in the whole segment),
+// then every merge step of the whole runs its stages across quarters through
+// LDS and the rest in registers.
+template <int R>
+__device__ __forceinline__ void block_sort_segment(const uint32_t* in, uint32_t* out, int b, int len,
+                                                   uint32_t* sv) {
+  constexpr int Q = 64 * R, P = 4 * Q;
+  const int lane = threadIdx.x & 63, t0 = (threadIdx.x >> 6) * Q;
+  uint32_t v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r * 64 + lane;
+    v[r] = t < len ? in[b + t] : 0xFFFFFFFFu;
+  }
+  wave_sort_regs<R>(v, lane, t0);
+  for (int k = 2 * Q; k <= P; k <<= 1) {
+    for (int j = k >> 1; j >= Q; j >>= 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) sv[t0 + r * 64 + lane] = v[r];
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int t = t0 + r * 64 + lane;
+        const uint32_t y = sv[t ^ j];
+        v[r] = (((t & j) == 0) == ((t & k) == 0)) ? min(v[r], y) : max(v[r], y);
+      }
+      __syncthreads();
+    }
+    regs_merge<R, Q / 2>(v, lane, t0, k);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int t = t0 + r * 64 + lane;
+    if (t < len) out[b + t] = v[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sseg_mid(const uint32_t* in, uint32_t* out, const int32_t* ptr,
+                                                  const int32_t* mid, const int32_t* cnt) {
+  __shared__ uint32_t sv[kSortBlock];
+  const int nmid = cnt[0];
+  for (int i = blockIdx.x; i < nmid; i += gridDim.x) {
+    const int k = mid[i];
+    const int b = ptr[k], len = ptr[k + 1] - b;
+    if (len <= 2048) block_sort_segment<8>(in, out, b, len, sv);
+    else block_sort_segment<16>(in, out, b, len, sv);
   }
 }
 
