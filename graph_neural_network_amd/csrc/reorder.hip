@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void k_max_deg(const int32_t* row_ptr, int32_t
 //     written back segment by segment.
 // The rows of a CSR or an adjacency are already grouped, so this replaces a
 // radix sort of (row, value) keys over all entries.
-constexpr int kSortSmall = 64;
+constexpr int kSortSmall = 16;
 constexpr int kSortWave = 1024;
 constexpr int kSortBlock = 4096;
 constexpr int kSortBlocks = 4096;  // workgroups striding over the medium segments
@@ -326,7 +326,8 @@ __global__ __launch_bounds__(256) void k_sseg_wave(const uint32_t* in, uint32_t*
   for (int i = blockIdx.x * 4 + wave; i < nw; i += gridDim.x * 4) {
     const int k = wmid[i];
     const int b = ptr[k], len = ptr[k + 1] - b;
-    if (len <= 128) wave_sort_segment<2>(in, out, b, len, lane);
+    if (len <= 64) wave_sort_segment<1>(in, out, b, len, lane);
+    else if (len <= 128) wave_sort_segment<2>(in, out, b, len, lane);
     else if (len <= 256) wave_sort_segment<4>(in, out, b, len, lane);
     else if (len <= 512) wave_sort_segment<8>(in, out, b, len, lane);
     else wave_sort_segment<16>(in, out, b, len, lane);
